@@ -1,0 +1,249 @@
+"""Benchmark of the CPR Gated DeltaNet layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the layer's hot path over synthetic inputs already
+resident in HBM:
+  - prefill of 5 packed sequences x 2,048 tokens (H=16, d_k=d_v=128, C=64,
+    bf16 q/k/v/g/beta, fp32 state): varlen plan, chunk products, boundary
+    chain, in-chunk scan;
+  - one decode step for 256 sequences whose state holds a 2,048-token prefix
+    (per-token step on the running state; the resynchronisation pass runs
+    every call and does the chunk computation when a tail fills).
+Prints one JSON line.  `value` is tokens per second over the whole step
+(5*2048 + 256 tokens).  The dominant kernel is the in-chunk scan; its
+duration is measured with HIP events recorded by the library on its own
+stream (gdn_cpr_set_stage_events).  The CPU baseline is the float64 oracle
+on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN layer tokens/s (prefill 5x2048, decode 256x1) + bitwise prefill/decode parity"
+# MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2 flop (fp32 FMA, one per lane per
+# clock without packed math) x 2.4 GHz.
+PEAK_VALU_F32 = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+PEAK_VALU_F32_PACKED = 157.3
+PEAK_HBM = 8000.0  # GB/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this layer's work is sharded by sequence/head with "
+              "no exchange, so there is no multi-GPU step to time (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import bitwise_invariant_gated_amd as gdn
+    from gdn_synth import make_batch, workload
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    H, D, C = 16, 128, 64
+    shape = gdn.LayerShape(H, D, D, C, torch.bfloat16)
+
+    def to_dev(b):
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+        return dict(q=t(b.q), k=t(b.k), v=t(b.v), g=t(b.g), beta=t(b.beta),
+                    cu=torch.from_numpy(b.cu_seqlens).to(dev))
+
+    # ---- prefill inputs: three draws of the 5 x 2,048 workload, rotated so
+    # that repeats are not served from the 256 MB last-level cache
+    log("generating prefill inputs")
+    b_pre, _, _, _ = workload("prefill_5x2048")
+    sets = [to_dev(b_pre)] + [to_dev(make_batch(200 + r, [2048] * 5, H, D, D, "bf16")) for r in range(2)]
+    T = b_pre.total_tokens
+    N_pre = b_pre.num_seqs
+    caches = [gdn.alloc_cache(shape, N_pre, dev) for _ in sets]
+    outs = [torch.empty((T, H, D), dtype=torch.bfloat16, device=dev) for _ in sets]
+    ws_pre = gdn.alloc_workspace(shape, N_pre, T, gdn.GDN_OP_PREFILL, dev)
+
+    # ---- decode: 256 sequences with a 2,048-token prefix, then decode tokens
+    log("generating decode inputs (256 x 2,048-token prefixes)")
+    n_dec_tok = args.warmup + args.steps + 64
+    b_dec = make_batch(3, [2048 + n_dec_tok] * 256, H, D, D, "bf16")
+    dd = to_dev(b_dec)
+    N_dec = 256
+    rows_all = (torch.from_numpy(b_dec.cu_seqlens[:-1].astype(np.int64)).to(dev)[None, :]
+                + torch.arange(2048, 2048 + n_dec_tok, device=dev)[:, None])  # [steps, N]
+    dec_in = {n: dd[n][rows_all].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    b_prefix = b_dec.truncate([2048] * 256)
+    dp = to_dev(b_prefix)
+    cache_dec = gdn.alloc_cache(shape, N_dec, dev)
+    o_prefix = torch.empty((b_prefix.total_tokens, H, D), dtype=torch.bfloat16, device=dev)
+    ws_big = gdn.alloc_workspace(shape, N_dec, b_prefix.total_tokens, gdn.GDN_OP_PREFILL, dev)
+    log("prefilling the decode prefix")
+    gdn.gdn_cpr_prefill(shape, dp["q"], dp["k"], dp["v"], dp["g"], dp["beta"], dp["cu"], None,
+                        cache_dec, o_prefix, ws_big)
+    del ws_big, o_prefix, dp
+    ws_dec = gdn.alloc_workspace(shape, N_dec, 0, gdn.GDN_OP_DECODE, dev)
+    o_dec = torch.empty((N_dec, H, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    pre_ev = gdn.StageEvents(5)
+    dec_ev = gdn.StageEvents(3)
+    scan_ms, chain_ms, local_ms, prefill_ms, decode_ms = [], [], [], [], []
+    dstep = [0]
+
+    def step(timed):
+        r = dstep[0] % len(sets)
+        s = sets[r]
+        with pre_ev:
+            gdn.gdn_cpr_prefill(shape, s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], None,
+                                caches[r], outs[r], ws_pre)
+        i = dstep[0]
+        with dec_ev:
+            gdn.gdn_cpr_decode_step(shape, dec_in["q"][i], dec_in["k"][i], dec_in["v"][i],
+                                    dec_in["g"][i], dec_in["beta"][i], cache_dec, o_dec, ws_dec)
+        dstep[0] += 1
+        if timed:
+            torch.cuda.synchronize()  # per-step event readout; the step total is timed separately
+            local_ms.append(pre_ev.stage_ms(2))
+            chain_ms.append(pre_ev.stage_ms(3))
+            scan_ms.append(pre_ev.stage_ms(4))
+            prefill_ms.append(pre_ev.events[0].elapsed_time(pre_ev.events[4]))
+            decode_ms.append(dec_ev.events[0].elapsed_time(dec_ev.events[2]))
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # timed region 1: K steps back to back (whole-step wall time)
+    start_step = dstep[0]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        r = dstep[0] % len(sets)
+        s = sets[r]
+        gdn.gdn_cpr_prefill(shape, s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], None,
+                            caches[r], outs[r], ws_pre)
+        i = dstep[0]
+        gdn.gdn_cpr_decode_step(shape, dec_in["q"][i], dec_in["k"][i], dec_in["v"][i],
+                                dec_in["g"][i], dec_in["beta"][i], cache_dec, o_dec, ws_dec)
+        dstep[0] += 1
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms (host wall {wall * 1e3:.3f} ms)")
+    # timed region 2: per-stage events (same work, one step at a time)
+    dstep[0] = start_step  # decode tokens advance regardless; keep rows in range
+    dstep[0] = args.warmup + args.steps
+    for _ in range(min(args.steps, 8)):
+        if dstep[0] >= n_dec_tok:
+            break
+        step(True)
+    ms_per_step = total_ms / args.steps
+    toks = T + N_dec
+    value = toks / (ms_per_step / 1e3)
+
+    # ---- parity: decode the last token of every prefill sequence == prefill output
+    log("parity check: prefill vs decode on the 5 x 2,048 workload")
+    s = sets[0]
+    bpre_1 = b_pre.truncate([2047] * 5)
+    p1 = to_dev(bpre_1)
+    cache_p = gdn.alloc_cache(shape, N_pre, dev)
+    o_p = torch.empty((bpre_1.total_tokens, H, D), dtype=torch.bfloat16, device=dev)
+    gdn.gdn_cpr_prefill(shape, p1["q"], p1["k"], p1["v"], p1["g"], p1["beta"], p1["cu"], None,
+                        cache_p, o_p, ws_pre)
+    last = torch.from_numpy(b_pre.cu_seqlens[1:].astype(np.int64) - 1).to(dev)
+    ws_d5 = gdn.alloc_workspace(shape, N_pre, 0, gdn.GDN_OP_DECODE, dev)
+    o_d5 = torch.empty((N_pre, H, D), dtype=torch.bfloat16, device=dev)
+    gdn.gdn_cpr_decode_step(shape, s["q"][last].contiguous(), s["k"][last].contiguous(),
+                            s["v"][last].contiguous(), s["g"][last].contiguous(),
+                            s["beta"][last].contiguous(), cache_p, o_d5, ws_d5)
+    c_full = gdn.alloc_cache(shape, N_pre, dev)
+    o_full = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    gdn.gdn_cpr_prefill(shape, s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], None,
+                        c_full, o_full, ws_pre)
+    torch.cuda.synchronize()
+    parity_o = bool(torch.equal(o_d5.view(torch.int16), o_full[last].contiguous().view(torch.int16)))
+    parity_s = bool(torch.equal(cache_p.s_run.view(torch.int32), c_full.s_run.view(torch.int32)))
+
+    scan_avg = float(np.mean(scan_ms))
+    flops_scan = 7.0 * D * D * T * H  # algorithmic: 7 flop per state entry per token-head
+    achieved = flops_scan / (scan_avg / 1e3) / 1e12
+    roofline = {
+        "kernel": "k_scan (in-chunk recurrent scan)",
+        "bound": "alu",
+        "achieved": round(achieved, 3),
+        "peak": round(PEAK_VALU_F32, 1),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_VALU_F32, 4),
+        "frac_vs_packed_peak": round(achieved / PEAK_VALU_F32_PACKED, 4),
+        "traffic": None,
+        "algorithmic_flop_per_launch": flops_scan,
+        "avg_launch_ms": round(scan_avg, 5),
+    }
+    dec_avg = float(np.mean(decode_ms))
+    dec_bytes = N_dec * H * (2 * D * D * 4 + 3 * D * 2 + 2 * 2 + D * 2 + (2 * D + 2) * 2)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic (seeded GDN-shaped inputs; see gdn_synth)",
+        "config": {"workload": "prefill 5x2048 tokens + decode 256 seqs x 1 token (2048-token prefix)",
+                   "heads": H, "d_k": D, "d_v": D, "chunk": C, "state": "fp32"},
+        "prefill": {"ms": round(float(np.mean(prefill_ms)), 5),
+                    "tokens_per_s": round(T / (float(np.mean(prefill_ms)) / 1e3), 1),
+                    "stage_ms": {"chunk_products": round(float(np.mean(local_ms)), 5),
+                                 "boundary_chain": round(float(np.mean(chain_ms)), 5),
+                                 "scan": round(scan_avg, 5)}},
+        "decode": {"ms": round(dec_avg, 5), "tokens_per_s": round(N_dec / (dec_avg / 1e3), 1),
+                   "algorithmic_bytes": dec_bytes,
+                   "achieved_GBps": round(dec_bytes / (dec_avg / 1e3) / 1e9, 1),
+                   "hbm_frac": round(dec_bytes / (dec_avg / 1e3) / 1e9 / PEAK_HBM, 4)},
+        "parity": {"decode_o_equals_prefill_o_bitwise": parity_o,
+                   "decode_state_equals_prefill_state_bitwise": parity_s},
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        log("CPU baseline: fp64 oracle on one 2,048-token sequence (16 heads)")
+        import oracle
+        b1 = b_pre.select([0]).truncate([512])
+        t0 = time.perf_counter()
+        oracle.recurrent_forward(b1.q, b1.k, b1.v, b1.g, b1.beta, b1.cu_seqlens, None)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(b1.total_tokens / dt, 2), "unit": "tokens/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"fp64 token recurrence, 1 sequence x {b1.total_tokens} tokens "
+                                            f"x 16 heads of the prefill workload ({dt:.1f} s)"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,728 @@
+// CPR Gated DeltaNet layer: HIP kernels for gfx950 and the C ABI (gdn_cpr.h).
+//
+// Prefill (per call, all on the caller's stream):
+//   k_plan            per-sequence chunk counts -> prefix sums (varlen plan)
+//   k_chunk_local     chunk products of every full chunk, all in parallel
+//   k_chain           boundary states: sequential over each sequence's full
+//                     chunks, parallel over sequences x heads x column blocks
+//   k_scan            per-token recurrence inside every chunk, all chunks in
+//                     parallel, each from its boundary state; writes o, the
+//                     final state and the decode tail
+// Decode step:
+//   k_decode          per-token step on the running state (one work item per
+//                     sequence x head), tail append, resync flag
+//   k_chunk_local_resync / k_chain_resync
+//                     for the (sequence, head) pairs whose tail just filled:
+//                     the same chunk products and boundary advance as prefill
+//                     over the C tail tokens, from the boundary state
+// The structure follows the pages (IsoExec, "Chunkwise-Parallel Recurrent
+// (CPR) Gated DeltaNet"; Chinese page, third-way section): boundary states
+// first, then a parallel in-chunk recurrent scan; decode resynchronises every
+// C tokens.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gdn_cpr.h"
+#include "cpr_device.hpp"
+
+using namespace cpr;
+
+namespace {
+
+constexpr int C = kChunk;
+constexpr int kChainCols = 32;  // state columns per boundary-chain work item
+
+// ---------------------------------------------------------------------------
+// kernel arguments
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const int32_t* cu;
+  const float* h0;
+  float* s_bnd;
+  float* s_run;
+  void* tail_k;
+  void* tail_v;
+  void* tail_g;
+  void* tail_beta;
+  int32_t* tail_len;
+  void* o;
+  int32_t* full_base;  // [N+1] prefix sums of full chunks per sequence
+  int32_t* all_base;   // [N+1] prefix sums of all chunks (full + partial)
+  float* prod;         // [F_max*H] chunk-product slots
+  float* gamn;         // [F_max*H]
+  float* bnd;          // [A_max*H][DK][DV] state at the start of every chunk
+  int32_t N;
+  int32_t H;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  float* s_bnd;
+  float* s_run;
+  void* tail_k;
+  void* tail_v;
+  void* tail_g;
+  void* tail_beta;
+  int32_t* tail_len;
+  void* o;
+  int32_t* flag;  // [N*H] 1 = this pair resynchronises in this step
+  float* prod;    // [N*H] chunk-product slots
+  float* gamn;    // [N*H]
+  int32_t N;
+  int32_t H;
+};
+
+template <int DK, int DV>
+__host__ __device__ constexpr size_t prod_floats() {
+  return (size_t)C * DK + (size_t)C * DV + (size_t)DK * C;
+}
+
+// largest i in [0, N) with base[i] <= slot (slot < base[N] assumed)
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ base, int N, int slot) {
+  int lo = 0, hi = N;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (base[mid] <= slot)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// varlen plan: exclusive prefix sums of full and of all chunks per sequence
+
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ cu, int32_t N,
+                                               int32_t* __restrict__ full_base,
+                                               int32_t* __restrict__ all_base) {
+  __shared__ int32_t sf[1024];
+  __shared__ int32_t sa[1024];
+  __shared__ int32_t carry[2];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    carry[0] = 0;
+    carry[1] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int i = base + tid;
+    int nf = 0, na = 0;
+    if (i < N) {
+      const int L = cu[i + 1] - cu[i];
+      nf = L / C;
+      na = (L + C - 1) / C;
+    }
+    sf[tid] = nf;
+    sa[tid] = na;
+    __syncthreads();
+    // Hillis-Steele inclusive scan (integers: order does not matter)
+    for (int off = 1; off < 1024; off <<= 1) {
+      int xf = 0, xa = 0;
+      if (tid >= off) {
+        xf = sf[tid - off];
+        xa = sa[tid - off];
+      }
+      __syncthreads();
+      sf[tid] += xf;
+      sa[tid] += xa;
+      __syncthreads();
+    }
+    if (i < N) {
+      full_base[i] = carry[0] + sf[tid] - nf;
+      all_base[i] = carry[1] + sa[tid] - na;
+    }
+    __syncthreads();
+    if (tid == 1023) {
+      carry[0] += sf[1023];
+      carry[1] += sa[1023];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    full_base[N] = carry[0];
+    all_base[N] = carry[1];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk products
+
+template <class D, int DK, int DV>
+__device__ __forceinline__ void stage_chunk(ChunkLds<DK, DV>& sm, const typename D::T* __restrict__ k,
+                                            size_t k_row0, size_t k_stride,
+                                            const typename D::T* __restrict__ v, size_t v_row0,
+                                            size_t v_stride, const typename D::T* __restrict__ g,
+                                            const typename D::T* __restrict__ beta, size_t gb0,
+                                            size_t gb_stride) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int idx = tid; idx < C * DK; idx += nt) {
+    const int t = idx / DK, i = idx % DK;
+    sm.K[t][i] = D::load(k, (k_row0 + (size_t)t * k_stride) * DK + i);
+  }
+  for (int idx = tid; idx < C * DV; idx += nt) {
+    const int t = idx / DV, j = idx % DV;
+    sm.V[t][j] = D::load(v, (v_row0 + (size_t)t * v_stride) * DV + j);
+  }
+  for (int t = tid; t < C; t += nt) {
+    sm.g[t] = D::load(g, gb0 + (size_t)t * gb_stride);
+    sm.beta[t] = D::load(beta, gb0 + (size_t)t * gb_stride);
+  }
+  __syncthreads();
+}
+
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(256) void k_chunk_local_prefill(const PrefillArgs a) {
+  using T = typename D::T;
+  __shared__ ChunkLds<DK, DV> sm;
+  const int f = blockIdx.x, h = blockIdx.y;
+  const int N = a.N, H = a.H;
+  if (f >= a.full_base[N]) return;
+  const int i = find_seq(a.full_base, N, f);
+  const int c = f - a.full_base[i];
+  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  const size_t row0 = tok0 * H + h;  // row index into [T, H, ...]
+  stage_chunk<D, DK, DV>(sm, (const T*)a.k, row0, H, (const T*)a.v, row0, H, (const T*)a.g,
+                         (const T*)a.beta, row0, H);
+  const size_t slot = (size_t)f * H + h;
+  float* P = a.prod + slot * prod_floats<DK, DV>();
+  chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + slot);
+}
+
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(256) void k_chunk_local_resync(const DecodeArgs a) {
+  using T = typename D::T;
+  __shared__ ChunkLds<DK, DV> sm;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  if (a.flag[sh] == 0) return;
+  // tail rows of this (sequence, head): [C, DK], [C, DV], [C]
+  stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, sh * C, 1, (const T*)a.tail_v, sh * C, 1,
+                         (const T*)a.tail_g, (const T*)a.tail_beta, sh * C, 1);
+  float* P = a.prod + sh * prod_floats<DK, DV>();
+  chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + sh);
+}
+
+// ---------------------------------------------------------------------------
+// boundary chain
+
+template <int DK, int DV, int NB>
+__device__ __forceinline__ void stage_products(ChainLds<DK, NB>& sm, const float* __restrict__ P,
+                                               const float* __restrict__ gamn, int col0) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const float* W = P;
+  const float* U = P + C * DK;
+  const float* KtT = P + C * DK + C * DV;
+  for (int idx = tid; idx < C * DK; idx += nt) (&sm.W[0][0])[idx] = W[idx];
+  for (int idx = tid; idx < DK * C; idx += nt) (&sm.KtT[0][0])[idx] = KtT[idx];
+  for (int idx = tid; idx < C * NB; idx += nt) {
+    const int t = idx / NB, j = idx % NB;
+    sm.U[t][j] = U[t * DV + col0 + j];
+  }
+  if (tid == 0) sm.gamn = *gamn;
+  __syncthreads();
+}
+
+template <int DK, int DV, int NB>
+__device__ __forceinline__ void put_block(float* __restrict__ dst, const ChainLds<DK, NB>& sm, int col0) {
+  for (int idx = threadIdx.x; idx < DK * NB; idx += blockDim.x) {
+    const int i = idx / NB, j = idx % NB;
+    dst[(size_t)i * DV + col0 + j] = sm.S[i][j];
+  }
+}
+
+template <int DK, int DV, int NB>
+__device__ __forceinline__ void get_block(ChainLds<DK, NB>& sm, const float* __restrict__ src, int col0) {
+  for (int idx = threadIdx.x; idx < DK * NB; idx += blockDim.x) {
+    const int i = idx / NB, j = idx % NB;
+    sm.S[i][j] = src ? src[(size_t)i * DV + col0 + j] : 0.f;
+  }
+  __syncthreads();
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
+  constexpr int NB = kChainCols;
+  __shared__ ChainLds<DK, NB> sm;
+  const int i = blockIdx.x, h = blockIdx.y, col0 = blockIdx.z * NB;
+  const int H = a.H;
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int nfull = L / C, nall = (L + C - 1) / C;
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  get_block<DK, DV, NB>(sm, a.h0 ? a.h0 + sh * SS : nullptr, col0);
+  const int abase = a.all_base[i], fbase = a.full_base[i];
+  if (nall > 0) put_block<DK, DV, NB>(a.bnd + ((size_t)abase * H + h) * SS, sm, col0);
+  for (int c = 0; c < nfull; ++c) {
+    const size_t slot = (size_t)(fbase + c) * H + h;
+    stage_products<DK, DV, NB>(sm, a.prod + slot * prod_floats<DK, DV>(), a.gamn + slot, col0);
+    chain_step_f32<DK, NB>(sm);
+    if (c + 1 < nall) put_block<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
+  }
+  put_block<DK, DV, NB>(a.s_bnd + sh * SS, sm, col0);
+  if (L % C == 0) put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
+  if (blockIdx.z == 0 && threadIdx.x == 0) a.tail_len[sh] = L % C;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
+  constexpr int NB = kChainCols;
+  __shared__ ChainLds<DK, NB> sm;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  if (a.flag[sh] == 0) return;
+  const int col0 = blockIdx.z * NB;
+  const size_t SS = (size_t)DK * DV;
+  get_block<DK, DV, NB>(sm, a.s_bnd + sh * SS, col0);
+  stage_products<DK, DV, NB>(sm, a.prod + sh * prod_floats<DK, DV>(), a.gamn + sh, col0);
+  chain_step_f32<DK, NB>(sm);
+  put_block<DK, DV, NB>(a.s_bnd + sh * SS, sm, col0);
+  put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
+}
+
+// ---------------------------------------------------------------------------
+// in-chunk scan (prefill): one wave per (chunk, head, 64 state columns)
+
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(64) void k_scan(const PrefillArgs a) {
+  using T = typename D::T;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const int N = a.N, H = a.H;
+  if (slot >= a.all_base[N]) return;
+  const int i = find_seq(a.all_base, N, slot);
+  const int c = slot - a.all_base[i];
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int n = min(C, L - c * C);
+  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  const int lane = threadIdx.x;
+  const int col = blockIdx.z * kWave + lane;
+  const size_t SS = (size_t)DK * DV;
+
+  const float* B = a.bnd + ((size_t)slot * H + h) * SS;
+  float s[DK];
+#pragma unroll
+  for (int ii = 0; ii < DK; ++ii) s[ii] = B[(size_t)ii * DV + col];
+
+  const T* gp = (const T*)a.g;
+  const T* bp = (const T*)a.beta;
+  float alpha_l = 1.f, beta_l = 0.f;
+  if (lane < n) {
+    const size_t r = (tok0 + lane) * H + h;
+    alpha_l = decay_of(D::load(gp, r));
+    beta_l = D::load(bp, r);
+  }
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const T* vp = (const T*)a.v;
+  T* op = (T*)a.o;
+  for (int t = 0; t < n; ++t) {
+    const size_t row = (tok0 + t) * H + h;
+    const UniformRow kr = (UniformRow)(kp + row * DK);
+    const UniformRow qr = (UniformRow)(qp + row * DK);
+    const float vv = D::load(vp, row * DV + col);
+    const float out = token_step<D, DK>(s, kr, qr, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vv);
+    D::store(op, row * DV + col, out);
+  }
+  const int nall = (L + C - 1) / C;
+  if (c == nall - 1 && (L % C) != 0) {
+    // last, partial chunk: its end state is the running state, its tokens the tail
+    const size_t sh = (size_t)i * H + h;
+    float* R = a.s_run + sh * SS;
+#pragma unroll
+    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+    T* tv = (T*)a.tail_v + sh * C * DV;
+    for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
+    if (blockIdx.z == 0) {
+      T* tk = (T*)a.tail_k + sh * C * DK;
+      for (int idx = lane; idx < n * DK; idx += kWave) {
+        const int t = idx / DK, e = idx % DK;
+        tk[idx] = kp[((tok0 + t) * H + h) * DK + e];
+      }
+      if (lane < n) {
+        ((T*)a.tail_g)[sh * C + lane] = gp[(tok0 + lane) * H + h];
+        ((T*)a.tail_beta)[sh * C + lane] = bp[(tok0 + lane) * H + h];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode: one work item per (sequence, head); DV threads, lane = state column
+
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
+  using T = typename D::T;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const int col = threadIdx.x;
+  const size_t SS = (size_t)DK * DV;
+  const int tl = a.tail_len[sh];
+  __syncthreads();  // every wave has read tail_len before it is rewritten below
+  if ((unsigned)tl >= (unsigned)C) return;  // not a valid cache: touch nothing
+  float* R = a.s_run + sh * SS;
+  float s[DK];
+#pragma unroll
+  for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const float alpha = decay_of(D::load((const T*)a.g, sh));
+  const float bt = D::load((const T*)a.beta, sh);
+  const float vv = D::load((const T*)a.v, sh * DV + col);
+  const float out = token_step<D, DK>(s, (UniformRow)(kp + sh * DK), (UniformRow)(qp + sh * DK), alpha, bt, vv);
+  D::store((T*)a.o, sh * DV + col, out);
+  // append the token to the tail
+  T* tk = (T*)a.tail_k + (sh * C + tl) * DK;
+  for (int e = col; e < DK; e += DV) tk[e] = kp[sh * DK + e];
+  ((T*)a.tail_v)[(sh * C + tl) * DV + col] = ((const T*)a.v)[sh * DV + col];
+  if (col == 0) {
+    ((T*)a.tail_g)[sh * C + tl] = ((const T*)a.g)[sh];
+    ((T*)a.tail_beta)[sh * C + tl] = ((const T*)a.beta)[sh];
+  }
+  const bool full = (tl + 1 == C);
+  if (!full) {
+#pragma unroll
+    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+  }
+  if (col == 0) {
+    a.tail_len[sh] = full ? 0 : tl + 1;
+    a.flag[sh] = full ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+thread_local std::string g_last_error;
+thread_local void* const* g_events = nullptr;
+thread_local int32_t g_n_events = 0;
+
+// records stage event i (instrumentation hook; no-op unless set)
+inline void mark(int i, hipStream_t st) {
+  if (g_events && i < g_n_events && g_events[i]) (void)hipEventRecord((hipEvent_t)g_events[i], st);
+}
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool shape_ok(const gdn_cpr_shape* s, std::string* why) {
+  if (!s) {
+    *why = "shape is NULL";
+    return false;
+  }
+  if (s->num_heads < 1) {
+    *why = "num_heads must be >= 1";
+    return false;
+  }
+  if (!((s->head_dim_k == 64 || s->head_dim_k == 128) && (s->head_dim_v == 64 || s->head_dim_v == 128))) {
+    *why = "head dims must be 64 or 128";
+    return false;
+  }
+  if (s->chunk != C) {
+    *why = "chunk must be 64";
+    return false;
+  }
+  if (s->dtype != GDN_DTYPE_F32 && s->dtype != GDN_DTYPE_BF16) {
+    *why = "dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16";
+    return false;
+  }
+  return true;
+}
+
+struct PrefillLayout {
+  size_t full_base, all_base, prod, gamn, bnd, total;
+};
+
+PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
+  const size_t H = s.num_heads, DK = s.head_dim_k, DV = s.head_dim_v;
+  const size_t Fmax = (size_t)(T / C);
+  const size_t Amax = Fmax + (size_t)N;
+  PrefillLayout L;
+  size_t off = 0;
+  L.full_base = off;
+  off = align_up(off + sizeof(int32_t) * (N + 1));
+  L.all_base = off;
+  off = align_up(off + sizeof(int32_t) * (N + 1));
+  L.prod = off;
+  off = align_up(off + sizeof(float) * Fmax * H * ((size_t)C * DK + (size_t)C * DV + DK * C));
+  L.gamn = off;
+  off = align_up(off + sizeof(float) * Fmax * H);
+  L.bnd = off;
+  off = align_up(off + sizeof(float) * Amax * H * DK * DV);
+  L.total = off;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t flag, prod, gamn, total;
+};
+
+DecodeLayout decode_layout(const gdn_cpr_shape& s, int32_t N) {
+  const size_t H = s.num_heads, DK = s.head_dim_k, DV = s.head_dim_v;
+  DecodeLayout L;
+  size_t off = 0;
+  L.flag = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)N * H);
+  L.prod = off;
+  off = align_up(off + sizeof(float) * (size_t)N * H * ((size_t)C * DK + (size_t)C * DV + DK * C));
+  L.gamn = off;
+  off = align_up(off + sizeof(float) * (size_t)N * H);
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define CHECK_PTR(p, name)                                                                 \
+  do {                                                                                     \
+    if (!(p)) return fail(GDN_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);                \
+    if (!aligned16(p)) return fail(GDN_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name); \
+  } while (0)
+
+#define CHECK_OPT_PTR(p, name)                                                             \
+  do {                                                                                     \
+    if ((p) && !aligned16(p))                                                              \
+      return fail(GDN_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);         \
+  } while (0)
+
+gdn_status launch_status(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+template <class D, int DK, int DV>
+gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const char* fn) {
+  const int Fmax = (int)(T / C);
+  const int Amax = Fmax + a.N;
+  mark(0, st);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.cu, a.N, a.full_base, a.all_base);
+  mark(1, st);
+  if (Fmax > 0)
+    hipLaunchKernelGGL((k_chunk_local_prefill<D, DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
+  mark(2, st);
+  if (a.N > 0)
+    hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+  mark(3, st);
+  if (Amax > 0 && T > 0)
+    hipLaunchKernelGGL((k_scan<D, DK, DV>), dim3(Amax, a.H, DV / kWave), dim3(kWave), 0, st, a);
+  mark(4, st);
+  return launch_status(fn);
+}
+
+template <class D, int DK, int DV>
+gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
+  mark(0, st);
+  hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(DV), 0, st, a);
+  mark(1, st);
+  hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+  mark(2, st);
+  return launch_status(fn);
+}
+
+template <template <class, int, int> class Fn, class... Args>
+gdn_status dispatch(const gdn_cpr_shape& s, Args&&... args) {
+  const bool bf = s.dtype == GDN_DTYPE_BF16;
+  const int dk = s.head_dim_k, dv = s.head_dim_v;
+#define GDN_CASE(DKv, DVv)                                                         \
+  if (dk == DKv && dv == DVv)                                                      \
+    return bf ? Fn<Bf16, DKv, DVv>::run(std::forward<Args>(args)...)               \
+              : Fn<F32, DKv, DVv>::run(std::forward<Args>(args)...);
+  GDN_CASE(64, 64)
+  GDN_CASE(64, 128)
+  GDN_CASE(128, 64)
+  GDN_CASE(128, 128)
+#undef GDN_CASE
+  return fail(GDN_ERR_UNSUPPORTED, "unsupported head dims");
+}
+
+template <class D, int DK, int DV>
+struct PrefillFn {
+  static gdn_status run(const PrefillArgs& a, int64_t T, hipStream_t st, const char* fn) {
+    return run_prefill<D, DK, DV>(a, T, st, fn);
+  }
+};
+
+template <class D, int DK, int DV>
+struct DecodeFn {
+  static gdn_status run(const DecodeArgs& a, hipStream_t st, const char* fn) {
+    return run_decode<D, DK, DV>(a, st, fn);
+  }
+};
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+
+extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num_seqs,
+                                         int64_t total_tokens, int32_t op) {
+  std::string why;
+  if (!shape_ok(shape, &why) || num_seqs < 0 || total_tokens < 0) return 0;
+  if (op == GDN_OP_PREFILL || op == GDN_OP_FWD_BWD) return prefill_layout(*shape, num_seqs, total_tokens).total;
+  if (op == GDN_OP_DECODE) return decode_layout(*shape, num_seqs).total;
+  return 0;
+}
+
+extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                                      const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta, const int32_t* cu_seqlens, const float* h0,
+                                      const gdn_cpr_cache* cache_out, void* o, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_cpr_prefill";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (total_tokens > (int64_t)INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+  if (!cache_out) return fail(GDN_ERR_INVALID_ARG, "%s: cache_out is NULL", fn);
+  CHECK_PTR(cu_seqlens, "cu_seqlens");
+  CHECK_OPT_PTR(h0, "h0");
+  CHECK_PTR(cache_out->s_bnd, "cache.s_bnd");
+  CHECK_PTR(cache_out->s_run, "cache.s_run");
+  CHECK_PTR(cache_out->tail_k, "cache.tail_k");
+  CHECK_PTR(cache_out->tail_v, "cache.tail_v");
+  CHECK_PTR(cache_out->tail_g, "cache.tail_g");
+  CHECK_PTR(cache_out->tail_beta, "cache.tail_beta");
+  CHECK_PTR(cache_out->tail_len, "cache.tail_len");
+  if (total_tokens > 0) {
+    CHECK_PTR(q, "q");
+    CHECK_PTR(k, "k");
+    CHECK_PTR(v, "v");
+    CHECK_PTR(g, "g");
+    CHECK_PTR(beta, "beta");
+    CHECK_PTR(o, "o");
+  }
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  const PrefillLayout L = prefill_layout(*shape, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  char* ws = (char*)workspace;
+  PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.h0 = h0;
+  a.s_bnd = cache_out->s_bnd;
+  a.s_run = cache_out->s_run;
+  a.tail_k = cache_out->tail_k;
+  a.tail_v = cache_out->tail_v;
+  a.tail_g = cache_out->tail_g;
+  a.tail_beta = cache_out->tail_beta;
+  a.tail_len = cache_out->tail_len;
+  a.o = o;
+  a.full_base = (int32_t*)(ws + L.full_base);
+  a.all_base = (int32_t*)(ws + L.all_base);
+  a.prod = (float*)(ws + L.prod);
+  a.gamn = (float*)(ws + L.gamn);
+  a.bnd = (float*)(ws + L.bnd);
+  a.N = num_seqs;
+  a.H = shape->num_heads;
+  return dispatch<PrefillFn>(*shape, a, total_tokens, (hipStream_t)stream, fn);
+}
+
+extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                                          const void* k, const void* v, const void* g, const void* beta,
+                                          const gdn_cpr_cache* cache, void* o, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_cpr_decode_step";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(g, "g");
+  CHECK_PTR(beta, "beta");
+  CHECK_PTR(o, "o");
+  CHECK_PTR(cache->s_bnd, "cache.s_bnd");
+  CHECK_PTR(cache->s_run, "cache.s_run");
+  CHECK_PTR(cache->tail_k, "cache.tail_k");
+  CHECK_PTR(cache->tail_v, "cache.tail_v");
+  CHECK_PTR(cache->tail_g, "cache.tail_g");
+  CHECK_PTR(cache->tail_beta, "cache.tail_beta");
+  CHECK_PTR(cache->tail_len, "cache.tail_len");
+  const DecodeLayout L = decode_layout(*shape, num_seqs);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  char* ws = (char*)workspace;
+  DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.s_bnd = cache->s_bnd;
+  a.s_run = cache->s_run;
+  a.tail_k = cache->tail_k;
+  a.tail_v = cache->tail_v;
+  a.tail_g = cache->tail_g;
+  a.tail_beta = cache->tail_beta;
+  a.tail_len = cache->tail_len;
+  a.o = o;
+  a.flag = (int32_t*)(ws + L.flag);
+  a.prod = (float*)(ws + L.prod);
+  a.gamn = (float*)(ws + L.gamn);
+  a.N = num_seqs;
+  a.H = shape->num_heads;
+  return dispatch<DecodeFn>(*shape, a, (hipStream_t)stream, fn);
+}
+
+extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                                      const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta, const int32_t* cu_seqlens, const float* h0,
+                                      const void* d_o, const float* d_hT, void* o, float* hT, void* dq,
+                                      void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  (void)shape; (void)num_seqs; (void)total_tokens; (void)q; (void)k; (void)v; (void)g; (void)beta;
+  (void)cu_seqlens; (void)h0; (void)d_o; (void)d_hT; (void)o; (void)hT; (void)dq; (void)dk; (void)dv;
+  (void)dg; (void)dbeta; (void)dh0; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(GDN_ERR_UNSUPPORTED, "gdn_cpr_fwd_bwd: not built yet");
+}
+
+extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) {
+  g_events = (events && n_events > 0) ? events : nullptr;
+  g_n_events = g_events ? n_events : 0;
+}
+
+extern "C" const char* gdn_cpr_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* gdn_cpr_numerics_id(void) {
+  return "gdn_cpr numerics v1: token_step fp32 (decay mul, 2-way even/odd fma dot for k and q, "
+         "explicit fma rank-1 update); chunk products and boundary chain fp32 VALU with ascending "
+         "explicit-fma sums; exp = ocml expf; bf16 outputs round-to-nearest-even; C = 64";
+}

@@ -130,7 +130,7 @@ class Batch:
         """Keep the first lengths[i] tokens of every sequence i."""
         lens = [int(x) for x in lengths]
         own = self.lengths
-        if len(lens) != self.num_seqs or any(a > b for a, b in zip(lens, own)):
+        if len(lens) != self.num_seqs or any(a > b or a < 0 for a, b in zip(lens, own)):
             raise ValueError("bad truncation lengths")
         idx = np.concatenate([np.arange(int(self.cu_seqlens[i]), int(self.cu_seqlens[i]) + n)
                               for i, n in enumerate(lens)]) if lens else np.zeros(0, np.int64)

@@ -1,0 +1,201 @@
+/*
+ * gdn_cpr.h -- C ABI of the chunkwise-parallel recurrent (CPR) Gated DeltaNet
+ * layer for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For each head the layer carries a state S (d_k x d_v,
+ * fp32; S = M^T for the d_v x d_k matrix M of the update rule) and, token by
+ * token,
+ *     M_t = alpha_t M_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = M_t q_t,        alpha_t = exp(g_t).
+ * CPR (IsoExec pages, "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet";
+ * Chinese page, the section on a third way for Gated DeltaNet) evaluates this
+ * recurrence so that training, prefill and decode round identically:
+ *   - prefill / training first compute the state at every chunk boundary
+ *     (every C tokens from each sequence's start) with the chunk (WY/UT) form,
+ *     then run the per-token recurrence inside every chunk, all chunks in
+ *     parallel, each starting from its boundary state;
+ *   - decode runs the same per-token step and, every C tokens, replaces its
+ *     running state by the chunk-boundary computation over the last C tokens.
+ * Every output of this library is therefore bit-identical between prefill
+ * and decode, and between a sequence run alone and the same sequence packed
+ * with others.  The results match the exact recurrence within fp32 rounding
+ * (fp32 inputs) or within the rounding of bf16 chunk operands (bf16 inputs).
+ *
+ * Conventions (all calls):
+ *   - Pointers are DEVICE pointers owned by the caller unless marked host.
+ *     The library allocates no device memory and keeps none between calls;
+ *     scratch lives in the caller's workspace (size from
+ *     gdn_cpr_workspace_size).  Calls only enqueue work on `stream` (a
+ *     hipStream_t; NULL = the legacy default stream) and return; results are
+ *     ready when the stream reaches them.  No call synchronises the host.
+ *   - Token-major packed layouts: q, k [T, H, d_k]; v, o [T, H, d_v];
+ *     g, beta [T, H]; all rows contiguous.  cu_seqlens int32 [N + 1] with
+ *     cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T.
+ *   - States [N, H, d_k, d_v] fp32, key dimension first (S layout).
+ *   - dtype GDN_DTYPE_F32: q, k, v, g, beta, o (and d_o, dq, dk, dv) are fp32.
+ *     dtype GDN_DTYPE_BF16: they are bf16 (raw 16-bit patterns); outputs are
+ *     rounded to nearest even.  States, dg, dbeta are always fp32.
+ *   - g must be <= 0 (alpha in (0, 1]); beta is used as given.  Values are
+ *     not checked on the device.
+ *   - Supported shapes: d_k, d_v in {64, 128}; C = 64; H >= 1.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Errors detectable on the host (null or misaligned pointer, unsupported
+ *     shape, workspace too small, negative sizes) return a status before any
+ *     work is enqueued; gdn_cpr_last_error() then describes it.  Launch
+ *     failures return GDN_ERR_HIP.  A malformed cu_seqlens (not
+ *     non-decreasing, or not ending at T) is the caller's error and is not
+ *     detected.
+ */
+#ifndef GDN_CPR_H
+#define GDN_CPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1,
+  GDN_ERR_UNSUPPORTED = 2,
+  GDN_ERR_WORKSPACE = 3,
+  GDN_ERR_HIP = 4
+} gdn_status;
+
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+
+typedef enum { GDN_OP_PREFILL = 0, GDN_OP_DECODE = 1, GDN_OP_FWD_BWD = 2 } gdn_op;
+
+/* Layer shape (host struct). */
+typedef struct {
+  int32_t num_heads;  /* H */
+  int32_t head_dim_k; /* d_k */
+  int32_t head_dim_v; /* d_v */
+  int32_t chunk;      /* C, the boundary / resynchronisation period */
+  int32_t dtype;      /* gdn_dtype of q, k, v, g, beta, o and the tail buffers */
+} gdn_cpr_shape;
+
+/*
+ * Per-sequence CPR cache (host struct of device pointers), N sequences.
+ * This is everything decode needs to continue a sequence bit-exactly, and it
+ * is position independent: copying it elsewhere (or to the host and back)
+ * and continuing gives the same bits.
+ *   s_bnd     [N, H, d_k, d_v] fp32  state at the last chunk boundary
+ *   s_run     [N, H, d_k, d_v] fp32  state after the last token (the final
+ *                                    state); equals s_bnd when tail_len = 0
+ *   tail_k    [N, H, C, d_k] dtype   tokens since that boundary
+ *   tail_v    [N, H, C, d_v] dtype
+ *   tail_g    [N, H, C]      dtype
+ *   tail_beta [N, H, C]      dtype
+ *   tail_len  [N, H] int32 in [0, C-1]; equal across the heads of a sequence
+ *                                    (one counter per head so that each head's
+ *                                    work item owns its own counter)
+ */
+typedef struct {
+  float* s_bnd;
+  float* s_run;
+  void* tail_k;
+  void* tail_v;
+  void* tail_g;
+  void* tail_beta;
+  int32_t* tail_len;
+} gdn_cpr_cache;
+
+/*
+ * Bytes of workspace a call needs (host only; never fails, returns 0 for an
+ * invalid or unsupported shape).  op is a gdn_op.  For GDN_OP_DECODE,
+ * total_tokens is ignored (one token per sequence).
+ */
+size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num_seqs,
+                              int64_t total_tokens, int32_t op);
+
+/*
+ * Prefill (the engine_prefill case): run N packed sequences from their
+ * initial states and fill the cache so that decode can continue them.
+ * Chunks start at each sequence's first token.  The chain of boundary
+ * states covers a sequence's full chunks; the tokens after its last full
+ * chunk (L mod C of them) become the cache's tail.
+ *   q, k, v, g, beta  inputs, layouts above (T = total_tokens rows)
+ *   cu_seqlens        [N + 1] int32
+ *   h0                [N, H, d_k, d_v] fp32 initial states, or NULL for zero
+ *                     states.  May alias cache_out->s_bnd or ->s_run.
+ *   cache_out         host struct; every field required; written in full
+ *   o                 [T, H, d_v] outputs
+ * Zero-length sequences are allowed: their cache becomes h0 and no output
+ * rows exist for them.
+ */
+gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                           const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const int32_t* cu_seqlens, const float* h0,
+                           const gdn_cpr_cache* cache_out, void* o, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Decode (the engine_decode case): one token for each of N sequences.
+ *   q, k, v, g, beta  [N, H, ...] one token per sequence
+ *   cache             read-modify-write in place
+ *   o                 [N, H, d_v]
+ * The token's output comes from the per-token step on s_run.  When the step
+ * completes a chunk (tail_len reaches C), s_bnd and s_run are both replaced
+ * by the chunk-boundary computation from s_bnd over the C tail tokens, and
+ * tail_len returns to 0.
+ */
+gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                               const void* k, const void* v, const void* g, const void* beta,
+                               const gdn_cpr_cache* cache, void* o, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Training forward + backward (the trainer_fwd case plus its gradient).
+ * The forward is the prefill computation (o is bit-identical to
+ * gdn_cpr_prefill on the same inputs).  The backward is the exact gradient
+ * of the recurrence for the loss sum(o * d_o) + sum(hT * d_hT), evaluated
+ * per chunk from the boundary states.
+ *   d_o               [T, H, d_v] dtype, upstream gradient of o
+ *   d_hT              [N, H, d_k, d_v] fp32 upstream gradient of the final
+ *                     states, or NULL (zero)
+ *   o                 [T, H, d_v] forward output
+ *   hT                [N, H, d_k, d_v] fp32 final states, or NULL
+ *   dq, dk, dv        dtype, shaped like q, k, v
+ *   dg, dbeta         [T, H] fp32
+ *   dh0               [N, H, d_k, d_v] fp32, or NULL
+ */
+gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                           const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const int32_t* cu_seqlens, const float* h0,
+                           const void* d_o, const float* d_hT, void* o, float* hT, void* dq,
+                           void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement hook (the pages report per-stage timings of the layer, English
+ * page, CPR table).  events points to an array of hipEvent_t handles owned by
+ * the caller, or NULL to switch the hook off (the default).  While set, on
+ * the calling thread, each call records events[0] before its first kernel
+ * and events[i] after its stage i, on the call's stream:
+ *   prefill / fwd_bwd forward: 1 plan, 2 chunk products, 3 boundary chain,
+ *                              4 in-chunk scan
+ *   decode:                    1 per-token step, 2 resynchronisation
+ *   fwd_bwd backward:          5 reverse boundary chain, 6 per-chunk gradients
+ * n_events is the array length; stages beyond it are not recorded.  Nothing
+ * is allocated and nothing else changes.
+ */
+void gdn_cpr_set_stage_events(void* const* events, int32_t n_events);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* gdn_cpr_last_error(void);
+
+/*
+ * Text naming every choice that fixes the library's rounding (routine
+ * versions, accumulation orders, operand precisions).  Two builds with the
+ * same text produce the same bits.
+ */
+const char* gdn_cpr_numerics_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_CPR_H */

@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments on the host
+before enqueueing anything (no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bitwise_invariant_gated_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    return _lib.load()
+
+
+def test_header_declares_exactly_the_bound_symbols():
+    with open(os.path.join(ROOT, "include", "gdn_cpr.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"\b(gdn_cpr_[a-z_]+)\s*\(", text))
+    assert declared == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib_or_skip()
+    for name in _lib.EXPORTED:
+        assert hasattr(lib, name), name
+
+
+def _shape(H=2, dk=64, dv=64, C=64, dtype=_lib.GDN_DTYPE_BF16):
+    return _lib.Shape(H, dk, dv, C, dtype)
+
+
+def test_workspace_size_shapes():
+    lib = _lib_or_skip()
+    s = _shape(16, 128, 128)
+    n_pre = lib.gdn_cpr_workspace_size(ctypes.byref(s), 5, 10240, _lib.GDN_OP_PREFILL)
+    n_dec = lib.gdn_cpr_workspace_size(ctypes.byref(s), 256, 0, _lib.GDN_OP_DECODE)
+    assert n_pre > 5 * 16 * 32 * 128 * 128 * 4  # at least one fp32 boundary state per chunk
+    assert n_dec > 256 * 16 * 4
+    assert n_pre % 256 == 0 and n_dec % 256 == 0
+    bad = _shape(16, 96, 128)
+    assert lib.gdn_cpr_workspace_size(ctypes.byref(bad), 5, 10240, _lib.GDN_OP_PREFILL) == 0
+    assert lib.gdn_cpr_workspace_size(ctypes.byref(s), -1, 10240, _lib.GDN_OP_PREFILL) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _cache(ptr=FAKE):
+    return _lib.Cache(ptr, ptr, ptr, ptr, ptr, ptr, ptr)
+
+
+def _prefill(lib, shape, N=2, T=128, cache=None, cu=FAKE, q=FAKE, ws=FAKE, ws_bytes=0, h0=None):
+    cache = cache if cache is not None else _cache()
+    return lib.gdn_cpr_prefill(ctypes.byref(shape), N, T, q, FAKE, FAKE, FAKE, FAKE, cu, h0,
+                               ctypes.byref(cache), FAKE, ws, ws_bytes, None)
+
+
+def test_prefill_rejects_unsupported_shapes():
+    lib = _lib_or_skip()
+    for s in (_shape(dk=96), _shape(dv=32), _shape(C=32), _shape(H=0), _shape(dtype=7)):
+        assert _prefill(lib, s) == _lib.GDN_ERR_UNSUPPORTED
+        assert lib.gdn_cpr_last_error()
+
+
+def test_prefill_rejects_null_and_misaligned_pointers():
+    lib = _lib_or_skip()
+    s = _shape()
+    assert _prefill(lib, s, cu=None) == _lib.GDN_ERR_INVALID_ARG
+    assert b"cu_seqlens" in lib.gdn_cpr_last_error()
+    assert _prefill(lib, s, q=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(lib, s, q=FAKE + 4) == _lib.GDN_ERR_INVALID_ARG
+    assert b"aligned" in lib.gdn_cpr_last_error()
+    assert _prefill(lib, s, h0=FAKE + 8) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(lib, s, cache=_cache(0)) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(lib, s, N=-1) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_small_workspace():
+    lib = _lib_or_skip()
+    s = _shape()
+    need = lib.gdn_cpr_workspace_size(ctypes.byref(s), 2, 128, _lib.GDN_OP_PREFILL)
+    assert _prefill(lib, s, ws_bytes=need - 1) == _lib.GDN_ERR_WORKSPACE
+    assert _prefill(lib, s, ws=None, ws_bytes=need) == _lib.GDN_ERR_WORKSPACE
+    assert b"workspace" in lib.gdn_cpr_last_error()
+
+
+def test_prefill_empty_batch_is_a_no_op():
+    lib = _lib_or_skip()
+    assert _prefill(lib, _shape(), N=0, T=0) == _lib.GDN_OK
+    assert lib.gdn_cpr_last_error() == b""
+
+
+def test_decode_rejects_bad_arguments():
+    lib = _lib_or_skip()
+    s = _shape()
+    cache = _cache()
+
+    def dec(shape=s, N=4, q=FAKE, ws=FAKE, ws_bytes=0, c=cache):
+        return lib.gdn_cpr_decode_step(ctypes.byref(shape), N, q, FAKE, FAKE, FAKE, FAKE,
+                                       ctypes.byref(c), FAKE, ws, ws_bytes, None)
+
+    assert dec(shape=_shape(dk=32)) == _lib.GDN_ERR_UNSUPPORTED
+    assert dec(q=None) == _lib.GDN_ERR_INVALID_ARG
+    assert dec(c=_cache(FAKE + 2)) == _lib.GDN_ERR_INVALID_ARG
+    assert dec(ws_bytes=16) == _lib.GDN_ERR_WORKSPACE
+    assert dec(N=0) == _lib.GDN_OK
+
+
+def test_numerics_id_is_stable_text():
+    lib = _lib_or_skip()
+    a = lib.gdn_cpr_numerics_id()
+    assert a and a == lib.gdn_cpr_numerics_id()

@@ -259,4 +259,257 @@ __device__ void chain_step_f32(ChainLds<DK, NB>& sm) {
   __syncthreads();
 }
 
+// ===========================================================================
+// bf16 inputs: chunk products and boundary advance on MFMA
+// (v_mfma_f32_16x16x32_bf16: bf16 operands, fp32 accumulation).
+//
+// Operand layout (16x16 output tiles, 64 lanes, lane = 16 g + c):
+//   accumulator: lane holds D[4g + r][c], r = 0..3
+//   A fragment:  lane holds A[c][k slots of group g], 8 bf16
+//   B fragment:  lane holds B[k slots of group g][c], 8 bf16
+// The k slots of group g for a 32-wide k step starting at k0 are
+//   k0 + 4g + {0,1,2,3}  and  k0 + 16 + 4g + {0,1,2,3}
+// (the same mapping for A and B, so every product pairs matching k).  With
+// this mapping two accumulator tiles that cover rows k0..k0+31 ARE a B
+// fragment, so the boundary state and the corrections Delta feed the next
+// product straight from registers.
+namespace mfma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)Bf16::round(lo) | ((uint32_t)Bf16::round(hi) << 16);
+}
+
+// B fragment from the accumulator tiles holding rows k0..k0+15 (a) and k0+16..k0+31 (b)
+__device__ __forceinline__ u32x4 frag_from_acc(const f32x4& a, const f32x4& b) {
+  return u32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3])};
+}
+
+// fragment from one row of a row-major bf16 matrix (8-byte aligned rows)
+__device__ __forceinline__ u32x4 frag_row(const uint16_t* row, int k0, int g) {
+  const u32x2 x = *reinterpret_cast<const u32x2*>(row + k0 + 4 * g);
+  const u32x2 y = *reinterpret_cast<const u32x2*>(row + k0 + 16 + 4 * g);
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
+}  // namespace mfma
+
+// Chunk products, bf16 path (one full chunk, one head, 256 threads = 4 waves).
+//   gamma = left-to-right fp32 cumsum of g; Gamma_t = exp(gamma_t);
+//   e_t = exp(gamma_{C-1} - gamma_t)
+//   G = K K^T                             (MFMA, bf16 K exact, fp32 sums)
+//   L[t][s] = (beta_t * exp(gamma_t - gamma_s)) * G[t][s], s < t   (fp32)
+//   T = (I + L)^{-1} diag(beta)           (fp32 forward substitution: lane =
+//                                          column s, rows t ascending, each row
+//                                          acc = (t == s ? beta_t : 0), then
+//                                          acc = fma(-L[t][r], T[r][s], acc), r < t)
+//   Wneg = -( bf16(T diag(Gamma)) K )     (MFMA; stored bf16, row-major [C][DK])
+//   U    = bf16(T) V                      (MFMA; stored fp32, accumulator tiles)
+//   KtT  = bf16(e_r * K[r][i])            (stored bf16, row-major [DK][C])
+//   Gamma_n = Gamma_{C-1}
+template <int DK, int DV>
+struct alignas(16) ChunkLdsB {
+  union {
+    uint16_t K[kChunk][DK + 8];  // row-major K, needed only for G
+    struct {
+      uint16_t TG[kChunk][kChunk + 8];
+      uint16_t TB[kChunk][kChunk + 8];
+    } t;  // written after G is done
+  } u;
+  uint16_t KT[DK][kChunk + 8];
+  uint16_t VT[DV][kChunk + 8];
+  float L[kChunk][kChunk + 1];  // L, then T in place
+  float g[kChunk], beta[kChunk], gam[kChunk], Gam[kChunk], e[kChunk];
+};
+
+// Workspace bytes of one chunk-product slot on the bf16 path.
+template <int DK, int DV>
+__host__ __device__ constexpr size_t prod_bytes_bf16() {
+  return (size_t)kChunk * DK * 2 + (size_t)DK * kChunk * 2 + (size_t)kChunk * DV * 4;
+}
+
+// Stage one chunk (bf16 rows) into LDS: K row-major, K^T, V^T, g, beta.
+// Row t of k starts at k + (k_row0 + t * k_stride) * DK (likewise v); g and
+// beta at gb0 + t * gb_stride.
+template <int DK, int DV>
+__device__ __forceinline__ void stage_chunk_bf16(ChunkLdsB<DK, DV>& sm, const uint16_t* __restrict__ k,
+                                                 size_t k_row0, size_t k_stride,
+                                                 const uint16_t* __restrict__ v, size_t v_row0,
+                                                 size_t v_stride, const uint16_t* __restrict__ g,
+                                                 const uint16_t* __restrict__ beta, size_t gb0,
+                                                 size_t gb_stride) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  for (int idx = tid; idx < kChunk * DK / 8; idx += nt) {
+    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
+    const u32x4v w = *reinterpret_cast<const u32x4v*>(k + (k_row0 + (size_t)t * k_stride) * DK + i0);
+    *reinterpret_cast<u32x4v*>(&sm.u.K[t][i0]) = w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.KT[i0 + e][t] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+  for (int idx = tid; idx < kChunk * DV / 8; idx += nt) {
+    const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+    const u32x4v w = *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.VT[j0 + e][t] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+  for (int t = tid; t < kChunk; t += nt) {
+    sm.g[t] = Bf16::load(g, gb0 + (size_t)t * gb_stride);
+    sm.beta[t] = Bf16::load(beta, gb0 + (size_t)t * gb_stride);
+  }
+  __syncthreads();
+}
+
+// Caller staged the chunk and synchronised; 256 threads.  Writes the slot:
+// Wneg [C][DK] bf16, KtT [DK][C] bf16, U [C*DV] fp32 in accumulator tiles
+// (tile (tm, jt) = 16 rows x 16 columns at ((tm * DV/16 + jt) * 64 + lane) * 4).
+template <int DK, int DV>
+__device__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ slot, float* __restrict__ gamn) {
+  using namespace mfma;
+  constexpr int C = kChunk;
+  uint16_t* Wneg = reinterpret_cast<uint16_t*>(slot);
+  uint16_t* KtT = Wneg + C * DK;
+  float* U = reinterpret_cast<float*>(KtT + DK * C);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  if (tid == 0) {
+    float acc = sm.g[0];
+    sm.gam[0] = acc;
+    for (int t = 1; t < C; ++t) {
+      acc = acc + sm.g[t];
+      sm.gam[t] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    sm.Gam[tid] = expf(sm.gam[tid]);
+    sm.e[tid] = expf(sm.gam[C - 1] - sm.gam[tid]);
+  }
+  // G = K K^T, 16 tiles, 4 per wave; L from G
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int tile = wave * 4 + q, tm = tile >> 2, tn = tile & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      acc = mma(frag_row(&sm.u.K[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.u.K[16 * tn + lr][0], 32 * kb, g), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
+      sm.L[t][s] = (s < t) ? (sm.beta[t] * expf(sm.gam[t] - sm.gam[s])) * acc[r] : 0.f;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // Forward substitution, lane = column s of T, one wave.  T overwrites L
+    // in place: row t of L is read by every lane before any lane stores its
+    // T[t][s] (one wave, program order), and rows r < t already hold T.
+    for (int t = 0; t < C; ++t) {
+      float acc = (t == lane) ? sm.beta[t] : 0.f;
+      for (int r = 0; r < t; ++r) acc = __builtin_fmaf(-sm.L[t][r], sm.L[r][lane], acc);
+      sm.L[t][lane] = acc;
+    }
+    const float gs = sm.Gam[lane];
+    for (int t = 0; t < C; ++t) {
+      const float x = sm.L[t][lane];
+      sm.u.t.TG[t][lane] = Bf16::round(x * gs);
+      sm.u.t.TB[t][lane] = Bf16::round(x);
+    }
+  } else {
+    // KtT = bf16(e_r K[r][i]) while wave 0 solves
+    for (int idx = tid - 64; idx < DK * C; idx += 192) {
+      const int i = idx / C, r = idx % C;
+      KtT[idx] = Bf16::round(sm.e[r] * Bf16::load(&sm.KT[i][0], r));
+    }
+  }
+  __syncthreads();
+  // W and U tiles
+  constexpr int nW = 4 * (DK / 16), nU = 4 * (DV / 16);
+  for (int tile = wave; tile < nW + nU; tile += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tile < nW) {
+      const int tm = tile / (DK / 16), it = tile % (DK / 16);
+#pragma unroll
+      for (int kb = 0; kb < C / 32; ++kb)
+        acc = mma(frag_row(&sm.u.t.TG[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.KT[16 * it + lr][0], 32 * kb, g), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Wneg[(16 * tm + 4 * g + r) * DK + 16 * it + lr] = Bf16::round(-acc[r]);
+    } else {
+      const int u = tile - nW, tm = u / (DV / 16), jt = u % (DV / 16);
+#pragma unroll
+      for (int kb = 0; kb < C / 32; ++kb)
+        acc = mma(frag_row(&sm.u.t.TB[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.VT[16 * jt + lr][0], 32 * kb, g), acc);
+      *reinterpret_cast<f32x4*>(U + ((size_t)(tm * (DV / 16) + jt) * 64 + lane) * 4) = acc;
+    }
+  }
+  if (tid == 0) *gamn = sm.Gam[C - 1];
+}
+
+// Boundary advance on the bf16 path for one 16-column block of the state,
+// one wave.  S[im] is the accumulator tile of state rows 16 im .. 16 im + 15.
+//   Sb    = bf16(S)                            (B fragments)
+//   Delta = U + Wneg Sb                        (acc starts at U, k ascending)
+//   S'    = Gamma_n * S + KtT bf16(Delta)      (acc starts at Gamma_n * S)
+template <int DK, int DV>
+__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16], const uint8_t* __restrict__ slot,
+                                                float gn, int jb, int lane) {
+  using namespace mfma;
+  constexpr int C = kChunk;
+  const uint16_t* Wneg = reinterpret_cast<const uint16_t*>(slot);
+  const uint16_t* KtT = Wneg + C * DK;
+  const float* U = reinterpret_cast<const float*>(KtT + DK * C);
+  const int lr = lane & 15, g = lane >> 4;
+  u32x4 Sb[DK / 32];
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb) Sb[kb] = frag_from_acc(S[2 * kb], S[2 * kb + 1]);
+  f32x4 D[C / 16];
+#pragma unroll
+  for (int tm = 0; tm < C / 16; ++tm) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(U + ((size_t)(tm * (DV / 16) + jb) * 64 + lane) * 4);
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) acc = mma(frag_row(Wneg + (16 * tm + lr) * DK, 32 * kb, g), Sb[kb], acc);
+    D[tm] = acc;
+  }
+  u32x4 Db[C / 32];
+#pragma unroll
+  for (int kb = 0; kb < C / 32; ++kb) Db[kb] = frag_from_acc(D[2 * kb], D[2 * kb + 1]);
+#pragma unroll
+  for (int im = 0; im < DK / 16; ++im) {
+    f32x4 acc = {gn * S[im][0], gn * S[im][1], gn * S[im][2], gn * S[im][3]};
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) acc = mma(frag_row(KtT + (16 * im + lr) * C, 32 * kb, g), Db[kb], acc);
+    S[im] = acc;
+  }
+}
+
+// State tile I/O for one 16-column block: rows 16 im + 4 g + r, column 16 jb + c.
+template <int DK, int DV>
+__device__ __forceinline__ void load_state_tiles(mfma::f32x4 (&S)[DK / 16], const float* __restrict__ src, int jb,
+                                                 int lane) {
+  const int lr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int im = 0; im < DK / 16; ++im)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[im][r] = src ? src[(size_t)(16 * im + 4 * g + r) * DV + 16 * jb + lr] : 0.f;
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void store_state_tiles(float* __restrict__ dst, const mfma::f32x4 (&S)[DK / 16], int jb,
+                                                  int lane) {
+  const int lr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int im = 0; im < DK / 16; ++im)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(size_t)(16 * im + 4 * g + r) * DV + 16 * jb + lr] = S[im][r];
+}
+
 }  // namespace cpr

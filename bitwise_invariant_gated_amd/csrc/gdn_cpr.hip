@@ -25,6 +25,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <type_traits>
 
 #include "../../include/gdn_cpr.h"
 #include "cpr_device.hpp"
@@ -57,7 +58,7 @@ struct PrefillArgs {
   void* o;
   int32_t* full_base;  // [N+1] prefix sums of full chunks per sequence
   int32_t* all_base;   // [N+1] prefix sums of all chunks (full + partial)
-  float* prod;         // [F_max*H] chunk-product slots
+  uint8_t* prod;       // [F_max*H] chunk-product slots of prod_slot_bytes
   float* gamn;         // [F_max*H]
   float* bnd;          // [A_max*H][DK][DV] state at the start of every chunk
   int32_t N;
@@ -79,7 +80,7 @@ struct DecodeArgs {
   int32_t* tail_len;
   void* o;
   int32_t* flag;  // [N*H] 1 = this pair resynchronises in this step
-  float* prod;    // [N*H] chunk-product slots
+  uint8_t* prod;  // [N*H] chunk-product slots of prod_slot_bytes
   float* gamn;    // [N*H]
   int32_t N;
   int32_t H;
@@ -88,6 +89,13 @@ struct DecodeArgs {
 template <int DK, int DV>
 __host__ __device__ constexpr size_t prod_floats() {
   return (size_t)C * DK + (size_t)C * DV + (size_t)DK * C;
+}
+
+// bytes of one chunk-product slot: fp32 W, U, K~^T on the fp32 path; bf16
+// Wneg and K~^T plus fp32 U on the bf16 (MFMA) path
+__host__ __device__ constexpr size_t prod_slot_bytes(bool bf16, int DK, int DV) {
+  return bf16 ? (size_t)C * DK * 2 + (size_t)DK * C * 2 + (size_t)C * DV * 4
+              : ((size_t)C * DK + (size_t)C * DV + (size_t)DK * C) * 4;
 }
 
 // largest i in [0, N) with base[i] <= slot (slot < base[N] assumed)
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256) void k_chunk_local_prefill(const PrefillArgs a
   stage_chunk<D, DK, DV>(sm, (const T*)a.k, row0, H, (const T*)a.v, row0, H, (const T*)a.g,
                          (const T*)a.beta, row0, H);
   const size_t slot = (size_t)f * H + h;
-  float* P = a.prod + slot * prod_floats<DK, DV>();
+  float* P = (float*)(a.prod + slot * prod_slot_bytes(false, DK, DV));
   chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + slot);
 }
 
@@ -211,8 +219,34 @@ __global__ __launch_bounds__(256) void k_chunk_local_resync(const DecodeArgs a) 
   // tail rows of this (sequence, head): [C, DK], [C, DV], [C]
   stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, sh * C, 1, (const T*)a.tail_v, sh * C, 1,
                          (const T*)a.tail_g, (const T*)a.tail_beta, sh * C, 1);
-  float* P = a.prod + sh * prod_floats<DK, DV>();
+  float* P = (float*)(a.prod + sh * prod_slot_bytes(false, DK, DV));
   chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + sh);
+}
+
+// bf16 path: MFMA chunk products
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_chunk_local_prefill_bf16(const PrefillArgs a) {
+  __shared__ ChunkLdsB<DK, DV> sm;
+  const int f = blockIdx.x, h = blockIdx.y;
+  const int N = a.N, H = a.H;
+  if (f >= a.full_base[N]) return;
+  const int i = find_seq(a.full_base, N, f);
+  const int c = f - a.full_base[i];
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, row0, H, (const uint16_t*)a.v, row0, H,
+                           (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H);
+  const size_t slot = (size_t)f * H + h;
+  chunk_local_bf16<DK, DV>(sm, a.prod + slot * prod_slot_bytes(true, DK, DV), a.gamn + slot);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_chunk_local_resync_bf16(const DecodeArgs a) {
+  __shared__ ChunkLdsB<DK, DV> sm;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  if (a.flag[sh] == 0) return;
+  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, sh * C, 1, (const uint16_t*)a.tail_v, sh * C, 1,
+                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, sh * C, 1);
+  chunk_local_bf16<DK, DV>(sm, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn + sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -267,7 +301,8 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
   if (nall > 0) put_block<DK, DV, NB>(a.bnd + ((size_t)abase * H + h) * SS, sm, col0);
   for (int c = 0; c < nfull; ++c) {
     const size_t slot = (size_t)(fbase + c) * H + h;
-    stage_products<DK, DV, NB>(sm, a.prod + slot * prod_floats<DK, DV>(), a.gamn + slot, col0);
+    stage_products<DK, DV, NB>(sm, (const float*)(a.prod + slot * prod_slot_bytes(false, DK, DV)), a.gamn + slot,
+                               col0);
     chain_step_f32<DK, NB>(sm);
     if (c + 1 < nall) put_block<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
   }
@@ -285,10 +320,47 @@ __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   const int col0 = blockIdx.z * NB;
   const size_t SS = (size_t)DK * DV;
   get_block<DK, DV, NB>(sm, a.s_bnd + sh * SS, col0);
-  stage_products<DK, DV, NB>(sm, a.prod + sh * prod_floats<DK, DV>(), a.gamn + sh, col0);
+  stage_products<DK, DV, NB>(sm, (const float*)(a.prod + sh * prod_slot_bytes(false, DK, DV)), a.gamn + sh, col0);
   chain_step_f32<DK, NB>(sm);
   put_block<DK, DV, NB>(a.s_bnd + sh * SS, sm, col0);
   put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
+}
+
+// bf16 path: one wave per (sequence, head, 16 state columns); the state block
+// lives in MFMA accumulator tiles for the whole chain
+template <int DK, int DV>
+__global__ __launch_bounds__(64) void k_chain_prefill_bf16(const PrefillArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y, jb = blockIdx.z, lane = threadIdx.x;
+  const int H = a.H;
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int nfull = L / C, nall = (L + C - 1) / C;
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  mfma::f32x4 S[DK / 16];
+  load_state_tiles<DK, DV>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb, lane);
+  const int abase = a.all_base[i], fbase = a.full_base[i];
+  if (nall > 0) store_state_tiles<DK, DV>(a.bnd + ((size_t)abase * H + h) * SS, S, jb, lane);
+  for (int c = 0; c < nfull; ++c) {
+    const size_t slot = (size_t)(fbase + c) * H + h;
+    chain_step_bf16<DK, DV>(S, a.prod + slot * prod_slot_bytes(true, DK, DV), a.gamn[slot], jb, lane);
+    if (c + 1 < nall) store_state_tiles<DK, DV>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb, lane);
+  }
+  store_state_tiles<DK, DV>(a.s_bnd + sh * SS, S, jb, lane);
+  if (L % C == 0) store_state_tiles<DK, DV>(a.s_run + sh * SS, S, jb, lane);
+  if (jb == 0 && lane == 0) a.tail_len[sh] = L % C;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  if (a.flag[sh] == 0) return;
+  const int jb = blockIdx.z, lane = threadIdx.x;
+  const size_t SS = (size_t)DK * DV;
+  mfma::f32x4 S[DK / 16];
+  load_state_tiles<DK, DV>(S, a.s_bnd + sh * SS, jb, lane);
+  chain_step_bf16<DK, DV>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb, lane);
+  store_state_tiles<DK, DV>(a.s_bnd + sh * SS, S, jb, lane);
+  store_state_tiles<DK, DV>(a.s_run + sh * SS, S, jb, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +520,7 @@ bool shape_ok(const gdn_cpr_shape* s, std::string* why) {
 }
 
 struct PrefillLayout {
-  size_t full_base, all_base, prod, gamn, bnd, total;
+  size_t full_base, all_base, prod, slot, gamn, bnd, total;
 };
 
 PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
@@ -462,7 +534,8 @@ PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   L.all_base = off;
   off = align_up(off + sizeof(int32_t) * (N + 1));
   L.prod = off;
-  off = align_up(off + sizeof(float) * Fmax * H * ((size_t)C * DK + (size_t)C * DV + DK * C));
+  L.slot = prod_slot_bytes(s.dtype == GDN_DTYPE_BF16, (int)DK, (int)DV);
+  off = align_up(off + Fmax * H * L.slot);
   L.gamn = off;
   off = align_up(off + sizeof(float) * Fmax * H);
   L.bnd = off;
@@ -472,7 +545,7 @@ PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
 }
 
 struct DecodeLayout {
-  size_t flag, prod, gamn, total;
+  size_t flag, prod, slot, gamn, total;
 };
 
 DecodeLayout decode_layout(const gdn_cpr_shape& s, int32_t N) {
@@ -482,7 +555,8 @@ DecodeLayout decode_layout(const gdn_cpr_shape& s, int32_t N) {
   L.flag = off;
   off = align_up(off + sizeof(int32_t) * (size_t)N * H);
   L.prod = off;
-  off = align_up(off + sizeof(float) * (size_t)N * H * ((size_t)C * DK + (size_t)C * DV + DK * C));
+  L.slot = prod_slot_bytes(s.dtype == GDN_DTYPE_BF16, (int)DK, (int)DV);
+  off = align_up(off + (size_t)N * H * L.slot);
   L.gamn = off;
   off = align_up(off + sizeof(float) * (size_t)N * H);
   L.total = off;
@@ -517,11 +591,20 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   mark(0, st);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.cu, a.N, a.full_base, a.all_base);
   mark(1, st);
-  if (Fmax > 0)
-    hipLaunchKernelGGL((k_chunk_local_prefill<D, DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
+  constexpr bool kBf16 = std::is_same<D, Bf16>::value;
+  if (Fmax > 0) {
+    if constexpr (kBf16)
+      hipLaunchKernelGGL((k_chunk_local_prefill_bf16<DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_chunk_local_prefill<D, DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
+  }
   mark(2, st);
-  if (a.N > 0)
-    hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+  if (a.N > 0) {
+    if constexpr (kBf16)
+      hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV>), dim3(a.N, a.H, DV / 16), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+  }
   mark(3, st);
   if (Amax > 0 && T > 0)
     hipLaunchKernelGGL((k_scan<D, DK, DV>), dim3(Amax, a.H, DV / kWave), dim3(kWave), 0, st, a);
@@ -534,8 +617,13 @@ gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
   mark(0, st);
   hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(DV), 0, st, a);
   mark(1, st);
-  hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+  if constexpr (std::is_same<D, Bf16>::value) {
+    hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / 16), dim3(64), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+  }
   mark(2, st);
   return launch_status(fn);
 }
@@ -640,7 +728,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.o = o;
   a.full_base = (int32_t*)(ws + L.full_base);
   a.all_base = (int32_t*)(ws + L.all_base);
-  a.prod = (float*)(ws + L.prod);
+  a.prod = (uint8_t*)(ws + L.prod);
   a.gamn = (float*)(ws + L.gamn);
   a.bnd = (float*)(ws + L.bnd);
   a.N = num_seqs;
@@ -695,7 +783,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   a.tail_len = cache->tail_len;
   a.o = o;
   a.flag = (int32_t*)(ws + L.flag);
-  a.prod = (float*)(ws + L.prod);
+  a.prod = (uint8_t*)(ws + L.prod);
   a.gamn = (float*)(ws + L.gamn);
   a.N = num_seqs;
   a.H = shape->num_heads;

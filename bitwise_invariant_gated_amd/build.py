@@ -31,6 +31,80 @@ FLAGS = [
 ]
 
 
+def check_dpp_hazards(asm_text: str) -> list:
+    """Every v_fmac_f32_dpp must not read, as its DPP source, a VGPR that a
+    VALU instruction wrote within the two preceding wait states (the gfx9
+    VALU-write -> DPP-read hazard; s_nop N provides N + 1 wait states).
+    Returns a list of violations (function, line number, text)."""
+    import re
+    bad = []
+    func = "?"
+    recent = []  # (wait states it provides, set of VGPRs it wrote)
+    vreg = re.compile(r"^v(\d+)$|^v\[(\d+):(\d+)\]$")
+
+    def regs(tok):
+        m = vreg.match(tok.strip())
+        if not m:
+            return set()
+        if m.group(1) is not None:
+            return {int(m.group(1))}
+        return set(range(int(m.group(2)), int(m.group(3)) + 1))
+
+    for no, line in enumerate(asm_text.splitlines(), 1):
+        t = line.strip()
+        if not t or t.startswith(";") or t.startswith("."):
+            continue
+        if t.endswith(":"):
+            if not t.startswith(".L"):
+                func = t[:-1]
+                recent = []
+            continue
+        parts = t.split(None, 1)
+        op = parts[0]
+        args = [a.strip() for a in parts[1].split(",")] if len(parts) > 1 else []
+        if op.startswith("v_fmac_f32_dpp") and len(args) >= 2:
+            src = regs(args[1].split()[0])
+            waits = 0
+            for ws, wrote in reversed(recent):
+                if waits >= 2:
+                    break
+                if wrote & src:
+                    bad.append((func, no, t))
+                    break
+                waits += ws
+        if op == "s_nop":
+            ws = int(args[0], 0) + 1 if args else 1
+            recent.append((ws, set()))
+        elif op.startswith("v_") and args:
+            first = args[0].split()[0]
+            recent.append((1, regs(first) if not first.startswith("s") else set()))
+        else:
+            recent.append((1, set()))
+        recent = recent[-4:]
+    return bad
+
+
+def check_isa(verbose: bool = True) -> None:
+    """Compile the device code to assembly and check the DPP hazard rule."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "gdn_cpr.s")
+        cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only", "-S",
+               "-o", out, SRC]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("device assembly failed:\n" + res.stderr[-2000:])
+        with open(out) as f:
+            text = f.read()
+    n_dpp = text.count("v_fmac_f32_dpp")
+    bad = check_dpp_hazards(text)
+    if bad:
+        raise RuntimeError(f"DPP hazard in generated code ({len(bad)}): " + "; ".join(
+            f"{fn} line {no}: {t}" for fn, no, t in bad[:5]))
+    if verbose:
+        print(f"ISA check: {n_dpp} v_fmac_f32_dpp instructions, no VALU-write -> DPP-read hazard")
+
+
 def build(verbose: bool = True) -> str:
     tmp = OUT + ".tmp"
     cmd = [HIPCC, *FLAGS, "-o", tmp, SRC]
@@ -46,6 +120,7 @@ def build(verbose: bool = True) -> str:
     if verbose and lines:
         print("\n".join(lines))
     os.replace(tmp, OUT)
+    check_isa(verbose)
     return OUT
 
 

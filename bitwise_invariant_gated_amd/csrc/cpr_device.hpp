@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace cpr {
 
 constexpr int kChunk = 64;  // C
@@ -119,6 +121,125 @@ __device__ __forceinline__ float token_step(float (&s)[DK], UniformRow krow, Uni
 
 // alpha = exp(g); one definition for the scan and for decode.
 __device__ __forceinline__ float decay_of(float g) { return expf(g); }
+
+// ---------------------------------------------------------------------------
+// The same per-token step with k and q delivered by DPP row broadcast.
+//
+// Used by the prefill scan.  Instead of scalar loads (whose cache misses
+// stall the wave), every lane 16 r + c vector-loads elements 8c .. 8c+7 of
+// the token's k and q rows (each 16-lane row holds a full copy) and
+// v_fmac_f32_dpp with row_newbcast:c reads element 8c + e from lane c of the
+// lane's own row.  The arithmetic is token_step's, operation for operation
+// and accumulator for accumulator (fma(a, b, c) = fma(b, a, c) exactly), so
+// both routines produce identical bits; the GPU tests compare prefill (this
+// routine) with decode (token_step) bit for bit.
+//
+// Hazard: a DPP instruction must not read a VGPR written by a VALU
+// instruction in the two preceding cycles.  The converted k and q values are
+// passed through an s_nop 1 before each pass, and the build checks the ISA
+// for any remaining DPP-source write within two instructions.
+#define CPR_FMAC_BCAST_CASE(N)                                                                  \
+  if constexpr (I == N)                                                                          \
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"      \
+                 : "+v"(acc)                                                                     \
+                 : "v"(src), "v"(x));
+// acc += src[lane 16 r + I of this lane's row] * x
+template <int I>
+__device__ __forceinline__ void fmac_bcast(float& acc, float src, float x) {
+  static_assert(I >= 0 && I < 16, "row_newbcast selects one of 16 lanes");
+  CPR_FMAC_BCAST_CASE(0) CPR_FMAC_BCAST_CASE(1) CPR_FMAC_BCAST_CASE(2) CPR_FMAC_BCAST_CASE(3)
+  CPR_FMAC_BCAST_CASE(4) CPR_FMAC_BCAST_CASE(5) CPR_FMAC_BCAST_CASE(6) CPR_FMAC_BCAST_CASE(7)
+  CPR_FMAC_BCAST_CASE(8) CPR_FMAC_BCAST_CASE(9) CPR_FMAC_BCAST_CASE(10) CPR_FMAC_BCAST_CASE(11)
+  CPR_FMAC_BCAST_CASE(12) CPR_FMAC_BCAST_CASE(13) CPR_FMAC_BCAST_CASE(14) CPR_FMAC_BCAST_CASE(15)
+}
+#undef CPR_FMAC_BCAST_CASE
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Raw k and q elements 8c .. 8c+7 of one token (c = lane mod 16).
+template <class D>
+struct KQRaw {
+  uint32_t w[D::kRowGroup == 16 ? 8 : 16];  // k then q: 4 + 4 dwords (bf16) or 8 + 8 (fp32)
+};
+
+template <class D, int DK>
+__device__ __forceinline__ void load_kq(KQRaw<D>& r, const typename D::T* krow, const typename D::T* qrow, int lane) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const int c = (lane & 15) & (DK / 8 - 1);  // lanes past the row repeat an in-bounds slot
+  constexpr int n = sizeof(typename D::T) == 2 ? 1 : 2;  // 16-byte loads per 8 elements
+#pragma unroll
+  for (int m = 0; m < n; ++m) {
+    const u32x4v a = *reinterpret_cast<const u32x4v*>(krow + 8 * c + 4 * m);
+    const u32x4v b = *reinterpret_cast<const u32x4v*>(qrow + 8 * c + 4 * m);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r.w[4 * m + e] = a[e];
+      r.w[4 * n + 4 * m + e] = b[e];
+    }
+  }
+}
+
+template <class D>
+__device__ __forceinline__ void unpack_kq(const KQRaw<D>& r, float (&kf)[8], float (&qf)[8]) {
+  if constexpr (sizeof(typename D::T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wk = r.w[e >> 1], wq = r.w[4 + (e >> 1)];
+      kf[e] = (e & 1) ? __uint_as_float(wk & 0xffff0000u) : __uint_as_float(wk << 16);
+      qf[e] = (e & 1) ? __uint_as_float(wq & 0xffff0000u) : __uint_as_float(wq << 16);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = __uint_as_float(r.w[e]);
+      qf[e] = __uint_as_float(r.w[8 + e]);
+    }
+  }
+}
+
+template <int DK>
+__device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf)[8], const float (&qf)[8],
+                                                float alpha, float beta, float v) {
+  static_assert(DK % 16 == 0 && DK <= 128, "one 16-lane row holds the key row");
+  asm volatile("s_nop 1" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
+               "v"(kf[7]));
+  float p0 = 0.f, p1 = 0.f;
+  static_for<0, DK / 8>([&](auto nc) {
+    constexpr int n = decltype(nc)::value;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int i = 8 * n + e;
+      s[i] = alpha * s[i];
+      fmac_bcast<n>(p0, kf[e], s[i]);
+      s[i + 1] = alpha * s[i + 1];
+      fmac_bcast<n>(p1, kf[e + 1], s[i + 1]);
+    }
+  });
+  const float u = beta * (v - (p0 + p1));
+  asm volatile("s_nop 1" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
+               "v"(qf[7]));
+  float o0 = 0.f, o1 = 0.f;
+  static_for<0, DK / 8>([&](auto nc) {
+    constexpr int n = decltype(nc)::value;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int i = 8 * n + e;
+      // both updates first: a state register is never read by the very next
+      // instruction that follows its write (the per-accumulator order is unchanged)
+      fmac_bcast<n>(s[i], kf[e], u);
+      fmac_bcast<n>(s[i + 1], kf[e + 1], u);
+      fmac_bcast<n>(o0, qf[e], s[i]);
+      fmac_bcast<n>(o1, qf[e + 1], s[i + 1]);
+    }
+  });
+  return o0 + o1;
+}
 
 // ---------------------------------------------------------------------------
 // Chunk-local products, fp32 VALU (one full chunk of C tokens, one head).

@@ -398,13 +398,23 @@ __global__ __launch_bounds__(64) void k_scan(const PrefillArgs a) {
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
   T* op = (T*)a.o;
+  // k, q and v of token t+1 are loaded while token t computes
+  KQRaw<D> raw;
+  size_t row = tok0 * H + h;
+  load_kq<D, DK>(raw, kp + row * DK, qp + row * DK, lane);
+  float vv = D::load(vp, row * DV + col);
   for (int t = 0; t < n; ++t) {
-    const size_t row = (tok0 + t) * H + h;
-    const UniformRow kr = (UniformRow)(kp + row * DK);
-    const UniformRow qr = (UniformRow)(qp + row * DK);
-    const float vv = D::load(vp, row * DV + col);
-    const float out = token_step<D, DK>(s, kr, qr, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vv);
+    float kf[8], qf[8];
+    unpack_kq<D>(raw, kf, qf);
+    const float vcur = vv;
+    const size_t next = row + H;
+    if (t + 1 < n) {
+      load_kq<D, DK>(raw, kp + next * DK, qp + next * DK, lane);
+      vv = D::load(vp, next * DV + col);
+    }
+    const float out = token_step_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
     D::store(op, row * DV + col, out);
+    row = next;
   }
   const int nall = (L + C - 1) / C;
   if (c == nall - 1 && (L % C) != 0) {

@@ -1,0 +1,50 @@
+"""CPU checks of the build's ISA hazard checker (it must flag a DPP source
+written by a VALU instruction fewer than two wait states earlier)."""
+
+from bitwise_invariant_gated_amd.build import check_dpp_hazards
+
+
+def test_flags_valu_write_right_before_dpp_read():
+    asm = """k:
+    v_lshlrev_b32_e32 v5, 16, v4
+    v_fmac_f32_dpp v1, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf
+"""
+    assert len(check_dpp_hazards(asm)) == 1
+
+
+def test_flags_write_two_instructions_back_without_nop():
+    asm = """k:
+    v_and_b32_e32 v5, 0xffff0000, v4
+    v_mul_f32_e32 v9, s2, v9
+    v_fmac_f32_dpp v1, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf
+"""
+    assert len(check_dpp_hazards(asm)) == 1
+
+
+def test_accepts_nop_or_distance():
+    ok1 = """k:
+    v_lshlrev_b32_e32 v5, 16, v4
+    s_nop 1
+    v_fmac_f32_dpp v1, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf
+"""
+    ok2 = """k:
+    v_lshlrev_b32_e32 v5, 16, v4
+    v_mul_f32_e32 v9, s2, v9
+    v_mul_f32_e32 v8, s2, v8
+    v_fmac_f32_dpp v1, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf
+"""
+    ok3 = """k:
+    v_lshlrev_b32_e32 v6, 16, v4
+    v_fmac_f32_dpp v1, v5, v6 row_newbcast:3 row_mask:0xf bank_mask:0xf
+"""
+    for a in (ok1, ok2, ok3):
+        assert check_dpp_hazards(a) == []
+
+
+def test_register_ranges_count_as_writes():
+    asm = """k:
+    global_load_dwordx4 v[4:7], v0, s[0:1]
+    v_mov_b64 v[4:5], 0
+    v_fmac_f32_dpp v1, v5, v2 row_newbcast:0 row_mask:0xf bank_mask:0xf
+"""
+    assert len(check_dpp_hazards(asm)) == 1

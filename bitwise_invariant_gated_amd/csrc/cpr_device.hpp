@@ -265,7 +265,7 @@ struct ChunkLds {
 // Caller has staged K, V, g, beta into sm and synchronised.  Writes W [C][DK],
 // U [C][DV], KtT [DK][C] and *gamn (global memory).
 template <int DK, int DV>
-__device__ void chunk_local_f32(ChunkLds<DK, DV>& sm, float* __restrict__ W, float* __restrict__ U,
+__device__ __forceinline__ void chunk_local_f32(ChunkLds<DK, DV>& sm, float* __restrict__ W, float* __restrict__ U,
                                 float* __restrict__ KtT, float* __restrict__ gamn) {
   constexpr int C = kChunk;
   const int tid = threadIdx.x;
@@ -347,7 +347,7 @@ struct ChainLds {
 
 // Caller has staged W, KtT, U (columns of this block), gamn and S; synchronised.
 template <int DK, int NB>
-__device__ void chain_step_f32(ChainLds<DK, NB>& sm) {
+__device__ __forceinline__ void chain_step_f32(ChainLds<DK, NB>& sm) {
   constexpr int C = kChunk;
   constexpr int kPer = (DK * NB + 255) / 256;
   const int tid = threadIdx.x;
@@ -448,7 +448,7 @@ struct alignas(16) ChunkLdsB {
   } u;
   uint16_t KT[DK][kChunk + 8];
   uint16_t VT[DV][kChunk + 8];
-  float L[kChunk][kChunk + 1];  // L, then T in place
+  float LT[kChunk][kChunk + 4];  // LT[s][t] = L[t][s]
   float g[kChunk], beta[kChunk], gam[kChunk], Gam[kChunk], e[kChunk];
 };
 
@@ -494,7 +494,7 @@ __device__ __forceinline__ void stage_chunk_bf16(ChunkLdsB<DK, DV>& sm, const ui
 // Wneg [C][DK] bf16, KtT [DK][C] bf16, U [C*DV] fp32 in accumulator tiles
 // (tile (tm, jt) = 16 rows x 16 columns at ((tm * DV/16 + jt) * 64 + lane) * 4).
 template <int DK, int DV>
-__device__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ slot, float* __restrict__ gamn) {
+__device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ slot, float* __restrict__ gamn) {
   using namespace mfma;
   constexpr int C = kChunk;
   uint16_t* Wneg = reinterpret_cast<uint16_t*>(slot);
@@ -526,24 +526,43 @@ __device__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ sl
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
-      sm.L[t][s] = (s < t) ? (sm.beta[t] * expf(sm.gam[t] - sm.gam[s])) * acc[r] : 0.f;
+      sm.LT[s][t] = (s < t) ? (sm.beta[t] * expf(sm.gam[t] - sm.gam[s])) * acc[r] : 0.f;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    // Forward substitution, lane = column s of T, one wave.  T overwrites L
-    // in place: row t of L is read by every lane before any lane stores its
-    // T[t][s] (one wave, program order), and rows r < t already hold T.
-    for (int t = 0; t < C; ++t) {
-      float acc = (t == lane) ? sm.beta[t] : 0.f;
-      for (int r = 0; r < t; ++r) acc = __builtin_fmaf(-sm.L[t][r], sm.L[r][lane], acc);
-      sm.L[t][lane] = acc;
-    }
-    const float gs = sm.Gam[lane];
-    for (int t = 0; t < C; ++t) {
-      const float x = sm.L[t][lane];
-      sm.u.t.TG[t][lane] = Bf16::round(x * gs);
-      sm.u.t.TB[t][lane] = Bf16::round(x);
+    // Forward substitution, one wave, lane = column s of T.  Rows are solved
+    // in blocks of 16 held in registers; each T[t][s] accumulates
+    // fma(-L[t][r], T[r][s], .) over r = 0 .. t-1 in ascending order from the
+    // initial value (t == s ? beta_t : 0) -- first the finished rows r < 16 B,
+    // read back from LDS, then the rows of its own block (right-looking).
+    // Finished T[r][s] (s <= r) are stored in the lower triangle of LT, which
+    // holds no L entries (LT[r][s] = L[s][r] is zero for s <= r).
+    const int s = lane;
+#pragma unroll
+    for (int B = 0; B < C / 16; ++B) {
+      float x[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) x[q] = (16 * B + q == s) ? sm.beta[16 * B + q] : 0.f;
+#pragma unroll 2
+      for (int r = 0; r < 16 * B; ++r) {
+        const float xr = (s <= r) ? sm.LT[r][s] : 0.f;  // T[r][s]
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = __builtin_fmaf(-sm.LT[r][16 * B + q], xr, x[q]);
+      }
+#pragma unroll
+      for (int r = 0; r < 15; ++r) {
+#pragma unroll
+        for (int q = r + 1; q < 16; ++q) x[q] = __builtin_fmaf(-sm.LT[16 * B + r][16 * B + q], x[r], x[q]);
+      }
+      const float gs = sm.Gam[s];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int t = 16 * B + q;
+        if (s <= t) sm.LT[t][s] = x[q];
+        sm.u.t.TG[t][s] = Bf16::round(x[q] * gs);
+        sm.u.t.TB[t][s] = Bf16::round(x[q]);
+      }
     }
   } else {
     // KtT = bf16(e_r K[r][i]) while wave 0 solves
@@ -580,14 +599,25 @@ __device__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ sl
 //   Sb    = bf16(S)                            (B fragments)
 //   Delta = U + Wneg Sb                        (acc starts at U, k ascending)
 //   S'    = Gamma_n * S + KtT bf16(Delta)      (acc starts at Gamma_n * S)
-template <int DK, int DV>
-__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16], const uint8_t* __restrict__ slot,
-                                                float gn, int jb, int lane) {
+// U tiles of one 16-column block (4 accumulator tiles, rows 16 tm .. 16 tm + 15).
+template <int DV>
+__device__ __forceinline__ void load_u_tiles(mfma::f32x4 (&Ut)[kChunk / 16], const uint8_t* __restrict__ slot,
+                                             int DK, int jb, int lane) {
+  const float* U = reinterpret_cast<const float*>(slot + (size_t)kChunk * DK * 4);
+#pragma unroll
+  for (int tm = 0; tm < kChunk / 16; ++tm)
+    Ut[tm] = *reinterpret_cast<const mfma::f32x4*>(U + ((size_t)(tm * (DV / 16) + jb) * 64 + lane) * 4);
+}
+
+// Wneg rows are w_stride elements apart and KtT rows kt_stride apart (the
+// global slot layout is unpadded; LDS copies are padded).  The arithmetic
+// does not depend on where the operands come from.
+template <int DK>
+__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16], const uint16_t* Wneg, int w_stride,
+                                                const uint16_t* KtT, int kt_stride,
+                                                const mfma::f32x4 (&Ut)[kChunk / 16], float gn, int lane) {
   using namespace mfma;
   constexpr int C = kChunk;
-  const uint16_t* Wneg = reinterpret_cast<const uint16_t*>(slot);
-  const uint16_t* KtT = Wneg + C * DK;
-  const float* U = reinterpret_cast<const float*>(KtT + DK * C);
   const int lr = lane & 15, g = lane >> 4;
   u32x4 Sb[DK / 32];
 #pragma unroll
@@ -595,9 +625,10 @@ __device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16], const
   f32x4 D[C / 16];
 #pragma unroll
   for (int tm = 0; tm < C / 16; ++tm) {
-    f32x4 acc = *reinterpret_cast<const f32x4*>(U + ((size_t)(tm * (DV / 16) + jb) * 64 + lane) * 4);
+    f32x4 acc = Ut[tm];
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) acc = mma(frag_row(Wneg + (16 * tm + lr) * DK, 32 * kb, g), Sb[kb], acc);
+    for (int kb = 0; kb < DK / 32; ++kb)
+      acc = mma(frag_row(Wneg + (16 * tm + lr) * w_stride, 32 * kb, g), Sb[kb], acc);
     D[tm] = acc;
   }
   u32x4 Db[C / 32];
@@ -607,9 +638,21 @@ __device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16], const
   for (int im = 0; im < DK / 16; ++im) {
     f32x4 acc = {gn * S[im][0], gn * S[im][1], gn * S[im][2], gn * S[im][3]};
 #pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb) acc = mma(frag_row(KtT + (16 * im + lr) * C, 32 * kb, g), Db[kb], acc);
+    for (int kb = 0; kb < C / 32; ++kb)
+      acc = mma(frag_row(KtT + (16 * im + lr) * kt_stride, 32 * kb, g), Db[kb], acc);
     S[im] = acc;
   }
+}
+
+// One step straight from a global chunk-product slot (decode resync).
+template <int DK, int DV>
+__device__ __forceinline__ void chain_step_bf16_global(mfma::f32x4 (&S)[DK / 16], const uint8_t* __restrict__ slot,
+                                                       float gn, int jb, int lane) {
+  const uint16_t* Wneg = reinterpret_cast<const uint16_t*>(slot);
+  const uint16_t* KtT = Wneg + kChunk * DK;
+  mfma::f32x4 Ut[kChunk / 16];
+  load_u_tiles<DV>(Ut, slot, DK, jb, lane);
+  chain_step_bf16<DK>(S, Wneg, DK, KtT, kChunk, Ut, gn, lane);
 }
 
 // State tile I/O for one 16-column block: rows 16 im + 4 g + r, column 16 jb + c.

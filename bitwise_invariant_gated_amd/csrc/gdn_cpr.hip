@@ -326,28 +326,88 @@ __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
 }
 
-// bf16 path: one wave per (sequence, head, 16 state columns); the state block
-// lives in MFMA accumulator tiles for the whole chain
+// bf16 path: one work-group per (sequence, head), one wave per 16 state
+// columns; each wave keeps its block of the state in MFMA accumulator tiles
+// for the whole chain.  The next chunk's Wneg and KtT (shared by all column
+// blocks) are staged into LDS while the current step runs; each wave
+// prefetches its own U tiles.
+template <int DK>
+struct ChainStage {
+  static constexpr int kW = DK + 8, kK = C + 8;  // padded LDS row strides (elements)
+  uint16_t W[2][C][kW];
+  uint16_t K[2][DK][kK];
+};
+
 template <int DK, int DV>
-__global__ __launch_bounds__(64) void k_chain_prefill_bf16(const PrefillArgs a) {
-  const int i = blockIdx.x, h = blockIdx.y, jb = blockIdx.z, lane = threadIdx.x;
+__global__ __launch_bounds__(DV * 4) void k_chain_prefill_bf16(const PrefillArgs a) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  constexpr int kThreads = DV * 4;                       // DV / 16 waves
+  constexpr int kPieces = (C * DK + DK * C) / 8;          // 16-byte pieces of Wneg + KtT
+  constexpr int kPer = kPieces / kThreads;
+  static_assert(kPieces % kThreads == 0, "staging split");
+  __shared__ ChainStage<DK> st;
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, jb = tid >> 6, lane = tid & 63;
   const int H = a.H;
   const int L = a.cu[i + 1] - a.cu[i];
   const int nfull = L / C, nall = (L + C - 1) / C;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
+  const size_t sbytes = prod_slot_bytes(true, DK, DV);
+  const int abase = a.all_base[i], fbase = a.full_base[i];
+
+  // piece p of a slot: p < C*DK/8 -> Wneg row p / (DK/8); else KtT row
+  auto fetch = [&](int c, u32x4v (&r)[kPer]) {
+    const u32x4v* src = reinterpret_cast<const u32x4v*>(a.prod + ((size_t)(fbase + c) * H + h) * sbytes);
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) r[m] = src[tid + m * kThreads];
+  };
+  auto put = [&](int buf, const u32x4v (&r)[kPer]) {
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int p = tid + m * kThreads;
+      if (p < C * DK / 8) {
+        const int row = p / (DK / 8), c8 = (p % (DK / 8)) * 8;
+        *reinterpret_cast<u32x4v*>(&st.W[buf][row][c8]) = r[m];
+      } else {
+        const int q = p - C * DK / 8, row = q / (C / 8), c8 = (q % (C / 8)) * 8;
+        *reinterpret_cast<u32x4v*>(&st.K[buf][row][c8]) = r[m];
+      }
+    }
+  };
+
   mfma::f32x4 S[DK / 16];
   load_state_tiles<DK, DV>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb, lane);
-  const int abase = a.all_base[i], fbase = a.full_base[i];
   if (nall > 0) store_state_tiles<DK, DV>(a.bnd + ((size_t)abase * H + h) * SS, S, jb, lane);
+  mfma::f32x4 Ut[C / 16], Un[C / 16];
+  u32x4v r[kPer];
+  if (nfull > 0) {
+    fetch(0, r);
+    put(0, r);
+    load_u_tiles<DV>(Ut, a.prod + ((size_t)fbase * H + h) * sbytes, DK, jb, lane);
+  }
+  __syncthreads();
   for (int c = 0; c < nfull; ++c) {
-    const size_t slot = (size_t)(fbase + c) * H + h;
-    chain_step_bf16<DK, DV>(S, a.prod + slot * prod_slot_bytes(true, DK, DV), a.gamn[slot], jb, lane);
+    const int buf = c & 1;
+    const bool more = c + 1 < nfull;
+    if (more) {
+      fetch(c + 1, r);
+      load_u_tiles<DV>(Un, a.prod + ((size_t)(fbase + c + 1) * H + h) * sbytes, DK, jb, lane);
+    }
+    const float gn = a.gamn[(size_t)(fbase + c) * H + h];
+    chain_step_bf16<DK>(S, &st.W[buf][0][0], ChainStage<DK>::kW, &st.K[buf][0][0], ChainStage<DK>::kK, Ut, gn,
+                        lane);
     if (c + 1 < nall) store_state_tiles<DK, DV>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb, lane);
+    if (more) {
+      put(buf ^ 1, r);
+#pragma unroll
+      for (int tm = 0; tm < C / 16; ++tm) Ut[tm] = Un[tm];
+    }
+    __syncthreads();
   }
   store_state_tiles<DK, DV>(a.s_bnd + sh * SS, S, jb, lane);
   if (L % C == 0) store_state_tiles<DK, DV>(a.s_run + sh * SS, S, jb, lane);
-  if (jb == 0 && lane == 0) a.tail_len[sh] = L % C;
+  if (tid == 0) a.tail_len[sh] = L % C;
 }
 
 template <int DK, int DV>
@@ -358,7 +418,7 @@ __global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
   const size_t SS = (size_t)DK * DV;
   mfma::f32x4 S[DK / 16];
   load_state_tiles<DK, DV>(S, a.s_bnd + sh * SS, jb, lane);
-  chain_step_bf16<DK, DV>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb, lane);
+  chain_step_bf16_global<DK, DV>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb, lane);
   store_state_tiles<DK, DV>(a.s_bnd + sh * SS, S, jb, lane);
   store_state_tiles<DK, DV>(a.s_run + sh * SS, S, jb, lane);
 }
@@ -611,7 +671,7 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   mark(2, st);
   if (a.N > 0) {
     if constexpr (kBf16)
-      hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV>), dim3(a.N, a.H, DV / 16), dim3(64), 0, st, a);
+      hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV>), dim3(a.N, a.H), dim3(DV * 4), 0, st, a);
     else
       hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
   }

@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "../../include/gdn_cpr.h"
+#include "cpr_backward.hpp"
 #include "cpr_device.hpp"
 
 using namespace cpr;
@@ -379,29 +380,40 @@ __global__ __launch_bounds__(DV * 4) void k_chain_prefill_bf16(const PrefillArgs
   mfma::f32x4 S[DK / 16];
   load_state_tiles<DK, DV>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb, lane);
   if (nall > 0) store_state_tiles<DK, DV>(a.bnd + ((size_t)abase * H + h) * SS, S, jb, lane);
-  mfma::f32x4 Ut[C / 16], Un[C / 16];
-  u32x4v r[kPer];
+  // chunk c's products are in LDS buffer c & 1 during step c; chunk c + 1's
+  // sit in registers (r1, Un1) and chunk c + 2's are being fetched, so each
+  // global load has two steps to arrive
+  mfma::f32x4 Ut[C / 16], Un1[C / 16], Un2[C / 16];
+  u32x4v r1[kPer], r2[kPer];
+  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * sbytes; };
   if (nfull > 0) {
-    fetch(0, r);
-    put(0, r);
-    load_u_tiles<DV>(Ut, a.prod + ((size_t)fbase * H + h) * sbytes, DK, jb, lane);
+    fetch(0, r1);
+    put(0, r1);
+    load_u_tiles<DV>(Ut, slot_of(0), DK, jb, lane);
+  }
+  if (nfull > 1) {
+    fetch(1, r1);
+    load_u_tiles<DV>(Un1, slot_of(1), DK, jb, lane);
   }
   __syncthreads();
   for (int c = 0; c < nfull; ++c) {
     const int buf = c & 1;
-    const bool more = c + 1 < nfull;
-    if (more) {
-      fetch(c + 1, r);
-      load_u_tiles<DV>(Un, a.prod + ((size_t)(fbase + c + 1) * H + h) * sbytes, DK, jb, lane);
+    if (c + 2 < nfull) {
+      fetch(c + 2, r2);
+      load_u_tiles<DV>(Un2, slot_of(c + 2), DK, jb, lane);
     }
     const float gn = a.gamn[(size_t)(fbase + c) * H + h];
     chain_step_bf16<DK>(S, &st.W[buf][0][0], ChainStage<DK>::kW, &st.K[buf][0][0], ChainStage<DK>::kK, Ut, gn,
                         lane);
     if (c + 1 < nall) store_state_tiles<DK, DV>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb, lane);
-    if (more) {
-      put(buf ^ 1, r);
+    if (c + 1 < nfull) {
+      put(buf ^ 1, r1);
 #pragma unroll
-      for (int tm = 0; tm < C / 16; ++tm) Ut[tm] = Un[tm];
+      for (int tm = 0; tm < C / 16; ++tm) Ut[tm] = Un1[tm];
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) r1[m] = r2[m];
+#pragma unroll
+      for (int tm = 0; tm < C / 16; ++tm) Un1[tm] = Un2[tm];
     }
     __syncthreads();
   }
@@ -538,6 +550,529 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   if (col == 0) {
     a.tail_len[sh] = full ? 0 : tl + 1;
     a.flag[sh] = full ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward (fwd_bwd): per-chunk local terms, reverse boundary chain, gradients
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const void* d_o;
+  const int32_t* cu;
+  const int32_t* all_base;
+  const float* bnd;   // forward state at the start of every chunk slot
+  const float* d_hT;  // [N,H,DK,DV] or null
+  uint8_t* ws;        // [A_max*H] backward slots
+  float* gamn;        // [A_max*H]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;
+  int32_t N;
+  int32_t H;
+};
+
+template <int DK, int DV>
+struct BwdLocalLds {
+  float At[C][C + 1];  // At[s][t] = A[t][s]
+  float X[C][C + 1];
+  float Pt[C][C + 1];  // Pt[s][t] = P[t][s]
+  float W[C][DK + 1];
+  float Dd[C][DV + 1];
+  bwd::ChunkScalars cs;
+};
+
+// B1: per chunk slot (full or partial) and head: X, W, Kt, -W^T, dDelta_local
+// = P^T dO and R = (diag(Gamma) Q)^T dO - W^T dDelta_local.
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
+  using namespace bwd;
+  using T = typename D::T;
+  typedef BwdSlot<DK, DV, sizeof(T)> Slot;
+  __shared__ BwdLocalLds<DK, DV> sm;
+  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
+  if (slot >= a.all_base[a.N]) return;
+  const int i = find_seq(a.all_base, a.N, slot);
+  const int c = slot - a.all_base[i];
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int n = min(C, L - c * C);
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const T* dop = (const T*)a.d_o;
+  chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
+  const ChunkScalars& cs = sm.cs;
+  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
+  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
+  auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
+  uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
+
+  // A = strict lower(beta_t D G) and P = lower(QK^T .* D): 16 + 16 tiles
+  for (int q = 0; q < 8; ++q) {
+    const int id = wave * 8 + q, tl = id & 15, tm = tl >> 2, tn = tl & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (id < 16) {
+      acc = tile<DK>([&](int m, int k) { return Kx(m, k); }, [&](int k, int nn) { return Kx(nn, k); }, 16 * tm,
+                     16 * tn, acc);
+      tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) {
+        sm.At[s][t] = (s < t) ? (cs.beta[t] * expf(cs.gam[t] - cs.gam[s])) * v : 0.f;
+      });
+    } else {
+      acc = tile<DK>([&](int m, int k) { return Qx(m, k); }, [&](int k, int nn) { return Kx(nn, k); }, 16 * tm,
+                     16 * tn, acc);
+      tile_each(acc, 16 * tm, 16 * tn,
+                [&](int t, int s, float v) { sm.Pt[s][t] = (s <= t) ? v * expf(cs.gam[t] - cs.gam[s]) : 0.f; });
+    }
+  }
+  __syncthreads();
+  if (wave == 0) unit_lower_inverse<C + 1, C + 1>(sm.At, sm.X);
+  __syncthreads();
+  float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
+  constexpr int nW = 4 * (DK / 16), nD = 4 * (DV / 16);
+  for (int id = wave; id < nW + nD; id += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (id < nW) {
+      const int tm = id / (DK / 16), it = id % (DK / 16);
+      acc = tile<C>([&](int t, int r) { return sm.X[t][r] * (cs.beta[r] * cs.Gam[r]); },
+                    [&](int r, int e) { return Kx(r, e); }, 16 * tm, 16 * it, acc);
+      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.W[t][e] = v; });
+    } else {
+      const int u = id - nW, tm = u / (DV / 16), jt = u % (DV / 16);
+      acc = tile<C>([&](int t, int s) { return sm.Pt[t][s]; }, [&](int s, int j) { return dOx(s, j); }, 16 * tm,
+                    16 * jt, acc);
+      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.Dd[t][j] = v; });
+      *reinterpret_cast<f32x4*>(Dd + ((size_t)(jt * (C / 16) + tm) * 64 + (tid & 63)) * 4) = acc;
+    }
+  }
+  __syncthreads();
+  T* Kt = reinterpret_cast<T*>(ws + Slot::oKt);
+  T* WnT = reinterpret_cast<T*>(ws + Slot::oWnT);
+  float* Xs = reinterpret_cast<float*>(ws + Slot::oX);
+  for (int idx = tid; idx < C * DK; idx += 256) {
+    const int t = idx / DK, e = idx % DK;
+    D::store(Kt, idx, cs.e[t] * Kx(t, e));
+    D::store(WnT, (size_t)e * C + t, -sm.W[t][e]);
+  }
+  for (int idx = tid; idx < C * C; idx += 256) Xs[idx] = sm.X[idx / C][idx % C];
+  float* R = reinterpret_cast<float*>(ws + Slot::oR);
+  constexpr int nR = (DK / 16) * (DV / 16);
+  for (int id = wave; id < nR; id += 4) {
+    const int im = id / (DV / 16), jt = id % (DV / 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<C>([&](int e, int t) { return cs.Gam[t] * Qx(t, e); }, [&](int t, int j) { return dOx(t, j); },
+                  16 * im, 16 * jt, acc);
+    acc = tile<C>([&](int e, int t) { return -sm.W[t][e]; }, [&](int t, int j) { return sm.Dd[t][j]; }, 16 * im,
+                  16 * jt, acc);
+    *reinterpret_cast<f32x4*>(R + ((size_t)(jt * (DK / 16) + im) * 64 + (tid & 63)) * 4) = acc;
+  }
+  if (tid == 0) a.gamn[(size_t)slot * H + h] = cs.Gam[C - 1];
+}
+
+// B2: reverse boundary chain per (sequence, head), one wave per 16 columns:
+//   dS <- Gamma_n dS + R - W^T (Kt dS), last chunk first, from dhT.
+// Stores, per chunk, dB' (the adjoint of the chunk's end state) and the full
+// dDelta = dDelta_local + Kt dB'.
+template <int DK, int DV>
+__global__ __launch_bounds__(DV * 4) void k_bwd_chain(const BwdArgs a) {
+  using namespace mfma;
+  typedef bwd::BwdSlot<DK, DV, 2> Slot;
+  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
+  const int tid = threadIdx.x, jb = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int nall = (L + C - 1) / C;
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  const int abase = a.all_base[i];
+  f32x4 S[DK / 16];
+  load_state_tiles<DK, DV>(S, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  for (int c = nall - 1; c >= 0; --c) {
+    const size_t sl = (size_t)(abase + c) * H + h;
+    uint8_t* ws = a.ws + sl * Slot::bytes;
+    store_state_tiles<DK, DV>(reinterpret_cast<float*>(ws + Slot::oDbp), S, jb, lane);
+    const uint16_t* Kt = reinterpret_cast<const uint16_t*>(ws + Slot::oKt);
+    const uint16_t* WnT = reinterpret_cast<const uint16_t*>(ws + Slot::oWnT);
+    const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
+    float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
+    u32x4 Sb[DK / 32];
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) Sb[kb] = frag_from_acc(S[2 * kb], S[2 * kb + 1]);
+    f32x4 E[C / 16];
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) acc = mma(frag_row(Kt + (16 * tm + lr) * DK, 32 * kb, g), Sb[kb], acc);
+      E[tm] = acc;
+      f32x4* dd = reinterpret_cast<f32x4*>(Dd + ((size_t)(jb * (C / 16) + tm) * 64 + lane) * 4);
+      *dd = *dd + acc;
+    }
+    u32x4 Eb[C / 32];
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) Eb[kb] = frag_from_acc(E[2 * kb], E[2 * kb + 1]);
+    const float gn = a.gamn[sl];
+#pragma unroll
+    for (int im = 0; im < DK / 16; ++im) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(R + ((size_t)(jb * (DK / 16) + im) * 64 + lane) * 4);
+      f32x4 acc = {gn * S[im][0] + r[0], gn * S[im][1] + r[1], gn * S[im][2] + r[2], gn * S[im][3] + r[3]};
+#pragma unroll
+      for (int kb = 0; kb < C / 32; ++kb) acc = mma(frag_row(WnT + (16 * im + lr) * C, 32 * kb, g), Eb[kb], acc);
+      S[im] = acc;
+    }
+  }
+  if (a.dh0) store_state_tiles<DK, DV>(a.dh0 + sh * SS, S, jb, lane);
+}
+
+// B2 for fp32 inputs: the same reverse chain with fp32 operands on
+// v_mfma_f32_16x16x4_f32.  The k index of step m in a 16-row tile is
+// 16 tile + 4 g + m, so accumulator tiles (lane group g holds rows 4 g .. 4 g
+// + 3) are B operands as they stand.
+template <int DK, int DV>
+__global__ __launch_bounds__(DV * 4) void k_bwd_chain_f32(const BwdArgs a) {
+  using namespace bwd;
+  typedef BwdSlot<DK, DV, 4> Slot;
+  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
+  const int tid = threadIdx.x, jb = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int nall = (L + C - 1) / C;
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  const int abase = a.all_base[i];
+  f32x4 S[DK / 16];
+  load_state_tiles<DK, DV>(S, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  for (int c = nall - 1; c >= 0; --c) {
+    const size_t sl = (size_t)(abase + c) * H + h;
+    uint8_t* ws = a.ws + sl * Slot::bytes;
+    store_state_tiles<DK, DV>(reinterpret_cast<float*>(ws + Slot::oDbp), S, jb, lane);
+    const float* Kt = reinterpret_cast<const float*>(ws + Slot::oKt);
+    const float* WnT = reinterpret_cast<const float*>(ws + Slot::oWnT);
+    const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
+    float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
+    f32x4 E[C / 16];
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mma4(Kt[(16 * tm + lr) * DK + 16 * it + 4 * g + m], S[it][m], acc);
+      E[tm] = acc;
+      f32x4* dd = reinterpret_cast<f32x4*>(Dd + ((size_t)(jb * (C / 16) + tm) * 64 + lane) * 4);
+      *dd = *dd + acc;
+    }
+    const float gn = a.gamn[sl];
+#pragma unroll
+    for (int im = 0; im < DK / 16; ++im) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(R + ((size_t)(jb * (DK / 16) + im) * 64 + lane) * 4);
+      f32x4 acc = {gn * S[im][0] + r[0], gn * S[im][1] + r[1], gn * S[im][2] + r[2], gn * S[im][3] + r[3]};
+#pragma unroll
+      for (int tm = 0; tm < C / 16; ++tm)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mma4(WnT[(16 * im + lr) * C + 16 * tm + 4 * g + m], E[tm][m], acc);
+      S[im] = acc;
+    }
+  }
+  if (a.dh0) store_state_tiles<DK, DV>(a.dh0 + sh * SS, S, jb, lane);
+}
+
+template <int DK, int DV>
+struct BwdGradLds {
+  static constexpr int DM = DK > DV ? DK : DV;
+  float N1[C][C + 1];   // G
+  float N2[C][C + 1];   // dT -> dX -> dA -> dG
+  float N3[C][C + 1];   // X
+  float N4[C][C + 1];   // dPD = (dO Delta^T) .* D, lower incl.
+  float N5[C][C + 1];   // Z_P, then Y, then dA D G
+  float M1[C][DM + 1];  // W -> dO B^T -> dW -> T^T dW
+  float M2[C][DM + 1];  // U -> Delta -> dKt
+  bwd::ChunkScalars cs;
+  float rzP[C], czP[C], dGamO[C], dGamW[C], de[C], dbc[C], dbr[C], rzA[C], czA[C];
+  float red[256];
+};
+
+// B3: per chunk slot and head: dq, dk, dv, dg, dbeta of the chunk's tokens.
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
+  using namespace bwd;
+  using T = typename D::T;
+  typedef BwdSlot<DK, DV, sizeof(T)> Slot;
+  __shared__ BwdGradLds<DK, DV> sm;
+  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
+  if (slot >= a.all_base[a.N]) return;
+  const int i = find_seq(a.all_base, a.N, slot);
+  const int c = slot - a.all_base[i];
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int n = min(C, L - c * C);
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const T* vp = (const T*)a.v;
+  const T* dop = (const T*)a.d_o;
+  chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
+  const ChunkScalars& cs = sm.cs;
+  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
+  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
+  auto Vx = [&](int t, int j) { return t < n ? D::load(vp, (row0 + (size_t)t * H) * DV + j) : 0.f; };
+  auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
+  const uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
+  const float* Bst = a.bnd + ((size_t)slot * H + h) * DK * DV;
+  const float* dBp = reinterpret_cast<const float*>(ws + Slot::oDbp);
+  const float* Ddg = reinterpret_cast<const float*>(ws + Slot::oDd);
+  const float* Xs = reinterpret_cast<const float*>(ws + Slot::oX);
+  auto dDx = [&](int t, int j) { return Ddg[tile_index<C>(t, j)]; };
+  constexpr int nK = 4 * (DK / 16), nV = 4 * (DV / 16);
+
+  // G and X
+  for (int q = 0; q < 4; ++q) {
+    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<DK>([&](int m, int k) { return Kx(m, k); }, [&](int k, int nn) { return Kx(nn, k); }, 16 * tm, 16 * tn,
+                   acc);
+    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N1[t][s] = v; });
+  }
+  for (int idx = tid; idx < C * C; idx += 256) sm.N3[idx / C][idx % C] = Xs[idx];
+  __syncthreads();
+  // W = X diag(beta Gamma) K -> M1,  U = X diag(beta) V -> M2
+  for (int id = wave; id < nK + nV; id += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (id < nK) {
+      const int tm = id / (DK / 16), it = id % (DK / 16);
+      acc = tile<C>([&](int t, int r) { return sm.N3[t][r] * (cs.beta[r] * cs.Gam[r]); },
+                    [&](int r, int e) { return Kx(r, e); }, 16 * tm, 16 * it, acc);
+      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
+    } else {
+      const int u = id - nK, tm = u / (DV / 16), jt = u % (DV / 16);
+      acc = tile<C>([&](int t, int r) { return sm.N3[t][r] * cs.beta[r]; }, [&](int r, int j) { return Vx(r, j); },
+                    16 * tm, 16 * jt, acc);
+      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.M2[t][j] = v; });
+    }
+  }
+  __syncthreads();
+  // Delta = U - W B (in place in M2; every tile is read and written by one wave)
+  for (int id = wave; id < nV; id += 4) {
+    const int tm = id / (DV / 16), jt = id % (DV / 16);
+    f32x4 acc;
+    {
+      const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = sm.M2[16 * tm + 4 * g + r][16 * jt + lr];
+    }
+    acc = tile<DK>([&](int t, int e) { return -sm.M1[t][e]; }, [&](int e, int j) { return Bst[(size_t)e * DV + j]; },
+                   16 * tm, 16 * jt, acc);
+    tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.M2[t][j] = v; });
+  }
+  __syncthreads();
+  // dP .* D (N4), Z_P = dPD .* QK (N5); dV = T^T dDelta
+  for (int q = 0; q < 4; ++q) {
+    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
+    f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+    accP = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int s) { return sm.M2[s][j]; }, 16 * tm,
+                    16 * tn, accP);
+    accQ = tile<DK>([&](int t, int e) { return Qx(t, e); }, [&](int e, int s) { return Kx(s, e); }, 16 * tm, 16 * tn,
+                    accQ);
+    const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
+      const float dpd = (s <= t) ? accP[r] * expf(cs.gam[t] - cs.gam[s]) : 0.f;
+      sm.N4[t][s] = dpd;
+      sm.N5[t][s] = dpd * accQ[r];
+    }
+  }
+  T* dvp = (T*)a.dv;
+  for (int id = wave; id < nV; id += 4) {
+    const int tm = id / (DV / 16), jt = id % (DV / 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<C>([&](int t, int s) { return sm.N3[s][t]; }, [&](int s, int j) { return dDx(s, j); }, 16 * tm,
+                  16 * jt, acc);
+    tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) {
+      if (t < n) D::store(dvp, (row0 + (size_t)t * H) * DV + j, cs.beta[t] * v);
+    });
+  }
+  __syncthreads();
+  // row / column sums of Z_P; dO B^T -> M1
+  if (tid < C) {
+    float acc = 0.f;
+    for (int s = 0; s < C; ++s) acc += sm.N5[tid][s];
+    sm.rzP[tid] = acc;
+  } else if (tid < 2 * C) {
+    const int s = tid - C;
+    float acc = 0.f;
+    for (int t = 0; t < C; ++t) acc += sm.N5[t][s];
+    sm.czP[s] = acc;
+  }
+  for (int id = wave; id < nK; id += 4) {
+    const int tm = id / (DK / 16), it = id % (DK / 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int e) { return Bst[(size_t)e * DV + j]; },
+                   16 * tm, 16 * it, acc);
+    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
+  }
+  __syncthreads();
+  // dQ = diag(Gamma) dO B^T + dPD K;  dGamma (output part) = <dO B^T, Q> per row
+  T* dqp = (T*)a.dq;
+  for (int id = wave; id < nK; id += 4) {
+    const int tm = id / (DK / 16), it = id % (DK / 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<C>([&](int t, int s) { return sm.N4[t][s]; }, [&](int s, int e) { return Kx(s, e); }, 16 * tm, 16 * it,
+                  acc);
+    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
+      if (t < n) D::store(dqp, (row0 + (size_t)t * H) * DK + e, cs.Gam[t] * sm.M1[t][e] + v);
+    });
+  }
+  if (tid < C) {
+    float acc = 0.f;
+    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M1[tid][e], Qx(tid, e), acc);
+    sm.dGamO[tid] = acc;
+  }
+  __syncthreads();
+  // dW = -dDelta B^T -> M1
+  for (int id = wave; id < nK; id += 4) {
+    const int tm = id / (DK / 16), it = id % (DK / 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int e) { return Bst[(size_t)e * DV + j]; },
+                   16 * tm, 16 * it, acc);
+    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = -v; });
+  }
+  __syncthreads();
+  // T^T dW and dKt = Delta dB'^T (kept in registers), dT -> N2
+  f32x4 TW[(nK + 3) / 4], KW[(nK + 3) / 4];
+  for (int q = 0, id = wave; id < nK; id += 4, ++q) {
+    const int tm = id / (DK / 16), it = id % (DK / 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    TW[q] = tile<C>([&](int t, int s) { return cs.beta[t] * sm.N3[s][t]; }, [&](int s, int e) { return sm.M1[s][e]; },
+                    16 * tm, 16 * it, acc);
+    KW[q] = tile<DV>([&](int t, int j) { return sm.M2[t][j]; }, [&](int j, int e) { return dBp[(size_t)e * DV + j]; },
+                     16 * tm, 16 * it, acc);
+  }
+  for (int q = 0; q < 4; ++q) {
+    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int s) { return Vx(s, j); }, 16 * tm, 16 * tn,
+                   acc);
+    acc = tile<DK>([&](int t, int e) { return sm.M1[t][e]; }, [&](int e, int s) { return cs.Gam[s] * Kx(s, e); },
+                   16 * tm, 16 * tn, acc);
+    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N2[t][s] = v; });
+  }
+  __syncthreads();
+  for (int q = 0, id = wave; id < nK; id += 4, ++q) {
+    const int tm = id / (DK / 16), it = id % (DK / 16);
+    tile_each(TW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
+    tile_each(KW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M2[t][e] = v; });
+  }
+  __syncthreads();
+  // dGamma (W part), de, dbeta (column part)
+  if (tid < C) {
+    float acc = 0.f;
+    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M1[tid][e], Kx(tid, e), acc);
+    sm.dGamW[tid] = acc;
+  } else if (tid < 2 * C) {
+    const int t = tid - C;
+    float acc = 0.f;
+    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M2[t][e], Kx(t, e), acc);
+    sm.de[t] = acc;
+  } else if (tid < 3 * C) {
+    const int s = tid - 2 * C;
+    float acc = 0.f;
+    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(sm.N3[t][s], sm.N2[t][s], acc);
+    sm.dbc[s] = acc;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * C; idx += 256) sm.N2[idx / C][idx % C] *= sm.cs.beta[idx % C];  // dX
+  __syncthreads();
+  // Y = dX X^T -> N5
+  for (int q = 0; q < 4; ++q) {
+    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<C>([&](int t, int r) { return sm.N2[t][r]; }, [&](int r, int s) { return sm.N3[s][r]; }, 16 * tm,
+                  16 * tn, acc);
+    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N5[t][s] = v; });
+  }
+  __syncthreads();
+  // dA = -X^T Y, strict lower -> N2
+  {
+    f32x4 accs[4];
+    for (int q = 0; q < 4; ++q) {
+      const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      accs[q] = tile<C>([&](int t, int r) { return sm.N3[r][t]; }, [&](int r, int s) { return sm.N5[r][s]; }, 16 * tm,
+                        16 * tn, acc);
+    }
+    __syncthreads();
+    for (int q = 0; q < 4; ++q) {
+      const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
+      tile_each(accs[q], 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N2[t][s] = (s < t) ? -v : 0.f; });
+    }
+  }
+  __syncthreads();
+  // dA D G -> N5, dG = dA beta_t D -> N2
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, s = idx % C;
+    const float dA = sm.N2[t][s];
+    float zb = 0.f, dG = 0.f;
+    if (s < t) {
+      const float Dv = expf(cs.gam[t] - cs.gam[s]);
+      zb = dA * Dv * sm.N1[t][s];
+      dG = dA * cs.beta[t] * Dv;
+    }
+    sm.N5[t][s] = zb;
+    sm.N2[t][s] = dG;
+  }
+  __syncthreads();
+  if (tid < C) {
+    float acc = 0.f;
+    for (int s = 0; s < C; ++s) acc += sm.N5[tid][s];
+    sm.dbr[tid] = acc;
+    sm.rzA[tid] = cs.beta[tid] * acc;
+  } else if (tid < 2 * C) {
+    const int s = tid - C;
+    float acc = 0.f;
+    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(cs.beta[t], sm.N5[t][s], acc);
+    sm.czA[s] = acc;
+  }
+  {
+    float acc = 0.f;
+    for (int idx = tid; idx < DK * DV; idx += 256) acc = __builtin_fmaf(dBp[idx], Bst[idx], acc);
+    sm.red[tid] = acc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float dGn = 0.f;
+    for (int r = 0; r < 256; ++r) dGn += sm.red[r];
+    float sum_de = 0.f;
+    for (int t = 0; t < C; ++t) sum_de = __builtin_fmaf(sm.de[t], cs.e[t], sum_de);
+    float acc = 0.f;
+    for (int t = C - 1; t >= 0; --t) {
+      float dgam = (sm.rzP[t] + sm.rzA[t]) - (sm.czP[t] + sm.czA[t]) + (sm.dGamO[t] + sm.dGamW[t]) * cs.Gam[t] -
+                   sm.de[t] * cs.e[t];
+      if (t == C - 1) dgam += dGn * cs.Gam[C - 1] + sum_de;
+      acc += dgam;
+      if (t < n) {
+        a.dg[row0 + (size_t)t * H] = acc;
+        a.dbeta[row0 + (size_t)t * H] = sm.dbc[t] + sm.dbr[t];
+      }
+    }
+  }
+  // dK = dPD^T Q + (dG + dG^T) K + diag(e) dKt + diag(Gamma) T^T dW
+  T* dkp = (T*)a.dk;
+  for (int id = wave; id < nK; id += 4) {
+    const int tm = id / (DK / 16), it = id % (DK / 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile<C>([&](int t, int s) { return sm.N4[s][t]; }, [&](int s, int e) { return Qx(s, e); }, 16 * tm, 16 * it,
+                  acc);
+    acc = tile<C>([&](int t, int s) { return sm.N2[t][s] + sm.N2[s][t]; }, [&](int s, int e) { return Kx(s, e); },
+                  16 * tm, 16 * it, acc);
+    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
+      if (t < n) D::store(dkp, (row0 + (size_t)t * H) * DK + e, v + cs.e[t] * sm.M2[t][e] + cs.Gam[t] * sm.M1[t][e]);
+    });
   }
 }
 
@@ -728,6 +1263,64 @@ struct DecodeFn {
   }
 };
 
+struct FwdBwdLayout {
+  PrefillLayout pre;
+  size_t s_bnd, s_run, tail_k, tail_v, tail_g, tail_b, tail_len, bgamn, bslots, slot, total;
+};
+
+FwdBwdLayout fwd_bwd_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
+  const size_t H = s.num_heads, DK = s.head_dim_k, DV = s.head_dim_v;
+  const size_t esz = s.dtype == GDN_DTYPE_BF16 ? 2 : 4;
+  const size_t Amax = (size_t)(T / C) + (size_t)N;
+  FwdBwdLayout L;
+  L.pre = prefill_layout(s, N, T);
+  size_t off = L.pre.total;
+  const size_t NH = (size_t)N * H;
+  L.s_bnd = off;
+  off = align_up(off + NH * DK * DV * 4);
+  L.s_run = off;
+  off = align_up(off + NH * DK * DV * 4);
+  L.tail_k = off;
+  off = align_up(off + NH * C * DK * esz);
+  L.tail_v = off;
+  off = align_up(off + NH * C * DV * esz);
+  L.tail_g = off;
+  off = align_up(off + NH * C * esz);
+  L.tail_b = off;
+  off = align_up(off + NH * C * esz);
+  L.tail_len = off;
+  off = align_up(off + NH * 4);
+  L.bgamn = off;
+  off = align_up(off + Amax * H * 4);
+  L.slot = (size_t)C * DK * esz + DK * (size_t)C * esz + DK * DV * 4 + (size_t)C * DV * 4 + (size_t)C * C * 4 +
+           DK * DV * 4;
+  L.bslots = off;
+  off = align_up(off + Amax * H * L.slot);
+  L.total = off;
+  return L;
+}
+
+template <class D, int DK, int DV>
+struct FwdBwdFn {
+  static gdn_status run(const PrefillArgs& pa, const BwdArgs& ba, int64_t T, size_t slot_bytes, hipStream_t st,
+                        const char* fn) {
+    typedef bwd::BwdSlot<DK, DV, sizeof(typename D::T)> Slot;
+    if (slot_bytes != Slot::bytes) return fail(GDN_ERR_HIP, "%s: internal slot size mismatch", fn);
+    gdn_status r = run_prefill<D, DK, DV>(pa, T, st, fn);
+    if (r != GDN_OK) return r;
+    const int Amax = (int)(T / C) + pa.N;
+    if (T > 0) hipLaunchKernelGGL((k_bwd_local<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+    if constexpr (std::is_same<D, Bf16>::value)
+      hipLaunchKernelGGL((k_bwd_chain<DK, DV>), dim3(pa.N, pa.H), dim3(DV * 4), 0, st, ba);
+    else
+      hipLaunchKernelGGL((k_bwd_chain_f32<DK, DV>), dim3(pa.N, pa.H), dim3(DV * 4), 0, st, ba);
+    mark(5, st);
+    if (T > 0) hipLaunchKernelGGL((k_bwd_grads<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+    mark(6, st);
+    return launch_status(fn);
+  }
+};
+
 }  // namespace
 
 // ===========================================================================
@@ -737,7 +1330,8 @@ extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num
                                          int64_t total_tokens, int32_t op) {
   std::string why;
   if (!shape_ok(shape, &why) || num_seqs < 0 || total_tokens < 0) return 0;
-  if (op == GDN_OP_PREFILL || op == GDN_OP_FWD_BWD) return prefill_layout(*shape, num_seqs, total_tokens).total;
+  if (op == GDN_OP_PREFILL) return prefill_layout(*shape, num_seqs, total_tokens).total;
+  if (op == GDN_OP_FWD_BWD) return fwd_bwd_layout(*shape, num_seqs, total_tokens).total;
   if (op == GDN_OP_DECODE) return decode_layout(*shape, num_seqs).total;
   return 0;
 }
@@ -866,10 +1460,85 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
                                       const void* d_o, const float* d_hT, void* o, float* hT, void* dq,
                                       void* dk, void* dv, float* dg, float* dbeta, float* dh0,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-  (void)shape; (void)num_seqs; (void)total_tokens; (void)q; (void)k; (void)v; (void)g; (void)beta;
-  (void)cu_seqlens; (void)h0; (void)d_o; (void)d_hT; (void)o; (void)hT; (void)dq; (void)dk; (void)dv;
-  (void)dg; (void)dbeta; (void)dh0; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(GDN_ERR_UNSUPPORTED, "gdn_cpr_fwd_bwd: not built yet");
+  const char* fn = "gdn_cpr_fwd_bwd";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (total_tokens > (int64_t)INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+  CHECK_PTR(cu_seqlens, "cu_seqlens");
+  CHECK_OPT_PTR(h0, "h0");
+  CHECK_OPT_PTR(d_hT, "d_hT");
+  CHECK_OPT_PTR(hT, "hT");
+  CHECK_OPT_PTR(dh0, "dh0");
+  if (total_tokens > 0) {
+    CHECK_PTR(q, "q");
+    CHECK_PTR(k, "k");
+    CHECK_PTR(v, "v");
+    CHECK_PTR(g, "g");
+    CHECK_PTR(beta, "beta");
+    CHECK_PTR(d_o, "d_o");
+    CHECK_PTR(o, "o");
+    CHECK_PTR(dq, "dq");
+    CHECK_PTR(dk, "dk");
+    CHECK_PTR(dv, "dv");
+    CHECK_PTR(dg, "dg");
+    CHECK_PTR(dbeta, "dbeta");
+  }
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  const FwdBwdLayout L = fwd_bwd_layout(*shape, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  char* ws = (char*)workspace;
+  PrefillArgs pa;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.g = g;
+  pa.beta = beta;
+  pa.cu = cu_seqlens;
+  pa.h0 = h0;
+  pa.s_bnd = (float*)(ws + L.s_bnd);
+  pa.s_run = hT ? hT : (float*)(ws + L.s_run);
+  pa.tail_k = ws + L.tail_k;
+  pa.tail_v = ws + L.tail_v;
+  pa.tail_g = ws + L.tail_g;
+  pa.tail_beta = ws + L.tail_b;
+  pa.tail_len = (int32_t*)(ws + L.tail_len);
+  pa.o = o;
+  pa.full_base = (int32_t*)(ws + L.pre.full_base);
+  pa.all_base = (int32_t*)(ws + L.pre.all_base);
+  pa.prod = (uint8_t*)(ws + L.pre.prod);
+  pa.gamn = (float*)(ws + L.pre.gamn);
+  pa.bnd = (float*)(ws + L.pre.bnd);
+  pa.N = num_seqs;
+  pa.H = shape->num_heads;
+  BwdArgs ba;
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.g = g;
+  ba.beta = beta;
+  ba.d_o = d_o;
+  ba.cu = cu_seqlens;
+  ba.all_base = pa.all_base;
+  ba.bnd = pa.bnd;
+  ba.d_hT = d_hT;
+  ba.ws = (uint8_t*)(ws + L.bslots);
+  ba.gamn = (float*)(ws + L.bgamn);
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dg = dg;
+  ba.dbeta = dbeta;
+  ba.dh0 = dh0;
+  ba.N = num_seqs;
+  ba.H = shape->num_heads;
+  return dispatch<FwdBwdFn>(*shape, pa, ba, total_tokens, L.slot, (hipStream_t)stream, fn);
 }
 
 extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) {
@@ -880,7 +1549,9 @@ extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) 
 extern "C" const char* gdn_cpr_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" const char* gdn_cpr_numerics_id(void) {
-  return "gdn_cpr numerics v1: token_step fp32 (decay mul, 2-way even/odd fma dot for k and q, "
-         "explicit fma rank-1 update); chunk products and boundary chain fp32 VALU with ascending "
-         "explicit-fma sums; exp = ocml expf; bf16 outputs round-to-nearest-even; C = 64";
+  return "gdn_cpr numerics v2: token step fp32 (decay mul; k and q dots as 2-way even/odd explicit-fma "
+         "chains; explicit-fma rank-1 update); fp32 inputs: chunk products and boundary chain fp32 VALU with "
+         "ascending explicit-fma sums; bf16 inputs: G, W, U and the boundary chain on "
+         "v_mfma_f32_16x16x32_bf16 with bf16 T, W, K~, S, Delta operands and fp32 accumulation, forward "
+         "substitution fp32 (ascending pivots); exp = ocml expf; bf16 outputs round-to-nearest-even; C = 64";
 }

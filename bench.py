@@ -104,6 +104,7 @@ def main():
     pre_ev = gdn.StageEvents(5)
     dec_ev = gdn.StageEvents(3)
     scan_ms, chain_ms, local_ms, prefill_ms, decode_ms = [], [], [], [], []
+    dstep_ms, dres_ms = [], []
     dstep = [0]
 
     def step(timed):
@@ -124,6 +125,8 @@ def main():
             scan_ms.append(pre_ev.stage_ms(4))
             prefill_ms.append(pre_ev.events[0].elapsed_time(pre_ev.events[4]))
             decode_ms.append(dec_ev.events[0].elapsed_time(dec_ev.events[2]))
+            dstep_ms.append(dec_ev.stage_ms(1))
+            dres_ms.append(dec_ev.stage_ms(2))
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -159,6 +162,64 @@ def main():
     ms_per_step = total_ms / args.steps
     toks = T + N_dec
     value = toks / (ms_per_step / 1e3)
+
+    # ---- decode over 64 consecutive steps (one chunk: exactly one resync per
+    # sequence) on a fresh copy of the 2,048-token-prefix cache
+    log("decode: 64 consecutive steps (one resynchronisation)")
+    b_dec64 = make_batch(3, [2048 + 64] * 256, H, D, D, "bf16")
+    d64 = to_dev(b_dec64)
+    rows64 = (torch.from_numpy(b_dec64.cu_seqlens[:-1].astype(np.int64)).to(dev)[None, :]
+              + torch.arange(2048, 2048 + 64, device=dev)[:, None])
+    dec64 = {n: d64[n][rows64].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    c64 = gdn.alloc_cache(shape, N_dec, dev)
+    bp64 = b_dec64.truncate([2048] * 256)
+    dp64 = to_dev(bp64)
+    ws_big = gdn.alloc_workspace(shape, N_dec, bp64.total_tokens, gdn.GDN_OP_PREFILL, dev)
+    o_big = torch.empty((bp64.total_tokens, H, D), dtype=torch.bfloat16, device=dev)
+    gdn.gdn_cpr_prefill(shape, dp64["q"], dp64["k"], dp64["v"], dp64["g"], dp64["beta"], dp64["cu"], None,
+                        c64, o_big, ws_big)
+    del ws_big, o_big, dp64, d64
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for i in range(64):
+        gdn.gdn_cpr_decode_step(shape, dec64["q"][i], dec64["k"][i], dec64["v"][i], dec64["g"][i],
+                                dec64["beta"][i], c64, o_dec, ws_dec)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    dec64_ms = e2.elapsed_time(e3) / 64
+
+    # ---- trainer forward + backward, 1 x 10,240 tokens
+    log("fwd_bwd: 1 x 10,240 tokens")
+    b_tr, _, _, _ = workload("train_1x10240")
+    tr = to_dev(b_tr)
+    tr_do = torch.from_numpy(b_tr.d_o).to(dev).to(torch.bfloat16)
+    T4 = b_tr.total_tokens
+    ws_tr = gdn.alloc_workspace(shape, 1, T4, gdn.GDN_OP_FWD_BWD, dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    o4 = torch.empty((T4, H, D), **bf)
+    dq4, dk4, dv4 = (torch.empty((T4, H, D), **bf) for _ in range(3))
+    dg4 = torch.empty((T4, H), dtype=torch.float32, device=dev)
+    db4 = torch.empty((T4, H), dtype=torch.float32, device=dev)
+    fb_ev = gdn.StageEvents(7)
+
+    def fwd_bwd():
+        gdn.gdn_cpr_fwd_bwd(shape, tr["q"], tr["k"], tr["v"], tr["g"], tr["beta"], tr["cu"], None, tr_do,
+                            None, o4, None, dq4, dk4, dv4, dg4, db4, None, ws_tr)
+
+    for _ in range(2):
+        fwd_bwd()
+    torch.cuda.synchronize()
+    fb_ms, fb_fwd, fb_bchain, fb_grads = [], [], [], []
+    for _ in range(5):
+        with fb_ev:
+            fwd_bwd()
+        torch.cuda.synchronize()
+        fb_ms.append(fb_ev.events[0].elapsed_time(fb_ev.events[6]))
+        fb_fwd.append(fb_ev.events[0].elapsed_time(fb_ev.events[4]))
+        fb_bchain.append(fb_ev.stage_ms(5))
+        fb_grads.append(fb_ev.stage_ms(6))
+    del ws_tr
 
     # ---- parity: decode the last token of every prefill sequence == prefill output
     log("parity check: prefill vs decode on the 5 x 2,048 workload")
@@ -222,25 +283,39 @@ def main():
                                  "boundary_chain": round(float(np.mean(chain_ms)), 5),
                                  "scan": round(scan_avg, 5)}},
         "decode": {"ms": round(dec_avg, 5), "tokens_per_s": round(N_dec / (dec_avg / 1e3), 1),
-                   "algorithmic_bytes": dec_bytes,
-                   "achieved_GBps": round(dec_bytes / (dec_avg / 1e3) / 1e9, 1),
-                   "hbm_frac": round(dec_bytes / (dec_avg / 1e3) / 1e9 / PEAK_HBM, 4)},
+                   "stage_ms": {"token_step": round(float(np.mean(dstep_ms)), 5),
+                                "resync_pass": round(float(np.mean(dres_ms)), 5)},
+                   "roofline": {"kernel": "k_decode (per-token step, state read-modify-write)",
+                                "bound": "hbm", "algorithmic_bytes_per_launch": dec_bytes,
+                                "achieved": round(dec_bytes / (float(np.mean(dstep_ms)) / 1e3) / 1e9, 1),
+                                "peak": PEAK_HBM, "unit": "GB/s",
+                                "frac": round(dec_bytes / (float(np.mean(dstep_ms)) / 1e3) / 1e9 / PEAK_HBM, 4)},
+                   "whole_call_GBps": round(dec_bytes / (dec_avg / 1e3) / 1e9, 1),
+                   "mean_over_64_steps_ms": round(dec64_ms, 5),
+                   "mean_over_64_steps_tokens_per_s": round(N_dec / (dec64_ms / 1e3), 1)},
+        "fwd_bwd": {"workload": "1 x 10240 tokens", "ms": round(float(np.median(fb_ms)), 4),
+                    "tokens_per_s": round(T4 / (float(np.median(fb_ms)) / 1e3), 1),
+                    "stage_ms": {"forward": round(float(np.median(fb_fwd)), 4),
+                                 "bwd_local_and_reverse_chain": round(float(np.median(fb_bchain)), 4),
+                                 "bwd_grads": round(float(np.median(fb_grads)), 4)}},
         "parity": {"decode_o_equals_prefill_o_bitwise": parity_o,
                    "decode_state_equals_prefill_state_bitwise": parity_s},
         "roofline": roofline,
     }
 
     if not args.no_cpu_baseline:
-        log("CPU baseline: fp64 oracle on one 2,048-token sequence (16 heads)")
+        log("CPU baseline: fp64 oracle over the 5 x 2,048 prefill batch (16 heads)")
         import oracle
-        b1 = b_pre.select([0]).truncate([512])
-        t0 = time.perf_counter()
-        oracle.recurrent_forward(b1.q, b1.k, b1.v, b1.g, b1.beta, b1.cu_seqlens, None)
-        dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": round(b1.total_tokens / dt, 2), "unit": "tokens/s",
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):  # the baseline's core count is then exactly one
+            t0 = time.perf_counter()
+            oracle.recurrent_forward(b_pre.q, b_pre.k, b_pre.v, b_pre.g, b_pre.beta, b_pre.cu_seqlens, None)
+            dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(b_pre.total_tokens / dt, 2), "unit": "tokens/s",
                                   "cores": 1, "kind": "oracle",
-                                  "sample": f"fp64 token recurrence, 1 sequence x {b1.total_tokens} tokens "
-                                            f"x 16 heads of the prefill workload ({dt:.1f} s)"}
+                                  "sample": f"fp64 token recurrence (NumPy, one thread) over the whole 5 x 2048 "
+                                            f"prefill batch, 16 heads, d=128: {dt:.1f} s; host has "
+                                            f"{len(os.sched_getaffinity(0))} cores available"}
     print(json.dumps(result), flush=True)
     return 0
 

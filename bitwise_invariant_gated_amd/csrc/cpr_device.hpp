@@ -42,13 +42,9 @@ struct Bf16 {
     return __uint_as_float((uint32_t)p[i] << 16);
   }
   __device__ static __forceinline__ void store(T* p, size_t i, float x) { p[i] = round(x); }
-  // fp32 -> bf16, round to nearest even; NaN stays NaN.
-  __device__ static __forceinline__ uint16_t round(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-  }
+  // fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32: branch
+  // free, IEEE RNE for every non-NaN input; NaN stays NaN).
+  __device__ static __forceinline__ uint16_t round(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
   __device__ static __forceinline__ float elem(const u32x8& w, int e) {
     return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
   }
@@ -406,8 +402,12 @@ __device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)Bf16::round(lo) | ((uint32_t)Bf16::round(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 // B fragment from the accumulator tiles holding rows k0..k0+15 (a) and k0+16..k0+31 (b)

@@ -599,81 +599,138 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
 //   Sb    = bf16(S)                            (B fragments)
 //   Delta = U + Wneg Sb                        (acc starts at U, k ascending)
 //   S'    = Gamma_n * S + KtT bf16(Delta)      (acc starts at Gamma_n * S)
-// U tiles of one 16-column block (4 accumulator tiles, rows 16 tm .. 16 tm + 15).
-template <int DV>
-__device__ __forceinline__ void load_u_tiles(mfma::f32x4 (&Ut)[kChunk / 16], const uint8_t* __restrict__ slot,
-                                             int DK, int jb, int lane) {
-  const float* U = reinterpret_cast<const float*>(slot + (size_t)kChunk * DK * 4);
-#pragma unroll
-  for (int tm = 0; tm < kChunk / 16; ++tm)
-    Ut[tm] = *reinterpret_cast<const mfma::f32x4*>(U + ((size_t)(tm * (DV / 16) + jb) * 64 + lane) * 4);
-}
-
 // Wneg rows are w_stride elements apart and KtT rows kt_stride apart (the
-// global slot layout is unpadded; LDS copies are padded).  The arithmetic
-// does not depend on where the operands come from.
-template <int DK>
-__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16], const uint16_t* Wneg, int w_stride,
+// global slot layout is unpadded; LDS copies are padded).  NT 16-column tiles
+// per wave: every A fragment read feeds NT MFMAs.  All A fragments of a k
+// step are read before its MFMAs, and k steps run outermost so consecutive
+// MFMAs are independent; each tile accumulates its k steps in ascending order
+// from its initial value, so the result does not depend on NT or on where
+// the operands come from.
+template <int DK, int NT>
+__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], const uint16_t* Wneg, int w_stride,
                                                 const uint16_t* KtT, int kt_stride,
-                                                const mfma::f32x4 (&Ut)[kChunk / 16], float gn, int lane) {
+                                                const mfma::f32x4 (&Ut)[kChunk / 16][NT], float gn, int lane) {
   using namespace mfma;
   constexpr int C = kChunk;
   const int lr = lane & 15, g = lane >> 4;
-  u32x4 Sb[DK / 32];
+  u32x4 Sb[DK / 32][NT];
 #pragma unroll
-  for (int kb = 0; kb < DK / 32; ++kb) Sb[kb] = frag_from_acc(S[2 * kb], S[2 * kb + 1]);
-  f32x4 D[C / 16];
+  for (int kb = 0; kb < DK / 32; ++kb)
 #pragma unroll
-  for (int tm = 0; tm < C / 16; ++tm) {
-    f32x4 acc = Ut[tm];
+    for (int nt = 0; nt < NT; ++nt) Sb[kb][nt] = frag_from_acc(S[2 * kb][nt], S[2 * kb + 1][nt]);
+  f32x4 D[C / 16][NT];
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      acc = mma(frag_row(Wneg + (16 * tm + lr) * w_stride, 32 * kb, g), Sb[kb], acc);
-    D[tm] = acc;
+  for (int tm = 0; tm < C / 16; ++tm)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) D[tm][nt] = Ut[tm][nt];
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb) {
+    u32x4 Wf[C / 16];
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) Wf[tm] = frag_row(Wneg + (16 * tm + lr) * w_stride, 32 * kb, g);
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) D[tm][nt] = mma(Wf[tm], Sb[kb][nt], D[tm][nt]);
   }
-  u32x4 Db[C / 32];
+  u32x4 Db[C / 32][NT];
 #pragma unroll
-  for (int kb = 0; kb < C / 32; ++kb) Db[kb] = frag_from_acc(D[2 * kb], D[2 * kb + 1]);
+  for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
-  for (int im = 0; im < DK / 16; ++im) {
-    f32x4 acc = {gn * S[im][0], gn * S[im][1], gn * S[im][2], gn * S[im][3]};
+    for (int nt = 0; nt < NT; ++nt) Db[kb][nt] = frag_from_acc(D[2 * kb][nt], D[2 * kb + 1][nt]);
 #pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb)
-      acc = mma(frag_row(KtT + (16 * im + lr) * kt_stride, 32 * kb, g), Db[kb], acc);
-    S[im] = acc;
+  for (int im = 0; im < DK / 16; ++im)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      S[im][nt] = f32x4{gn * S[im][nt][0], gn * S[im][nt][1], gn * S[im][nt][2], gn * S[im][nt][3]};
+#pragma unroll
+  for (int kb = 0; kb < C / 32; ++kb) {
+#pragma unroll
+    for (int im = 0; im < DK / 16; ++im) {
+      const u32x4 Kf = frag_row(KtT + (16 * im + lr) * kt_stride, 32 * kb, g);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) S[im][nt] = mma(Kf, Db[kb][nt], S[im][nt]);
+    }
   }
+}
+
+// U tiles of NT 16-column blocks starting at block jb0.
+template <int DV, int NT>
+__device__ __forceinline__ void load_u_tiles(mfma::f32x4 (&Ut)[kChunk / 16][NT], const uint8_t* __restrict__ slot,
+                                             int DK, int jb0, int lane) {
+  const float* U = reinterpret_cast<const float*>(slot + (size_t)kChunk * DK * 4);
+#pragma unroll
+  for (int tm = 0; tm < kChunk / 16; ++tm)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      Ut[tm][nt] = *reinterpret_cast<const mfma::f32x4*>(U + ((size_t)(tm * (DV / 16) + jb0 + nt) * 64 + lane) * 4);
 }
 
 // One step straight from a global chunk-product slot (decode resync).
-template <int DK, int DV>
-__device__ __forceinline__ void chain_step_bf16_global(mfma::f32x4 (&S)[DK / 16], const uint8_t* __restrict__ slot,
-                                                       float gn, int jb, int lane) {
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void chain_step_bf16_global(mfma::f32x4 (&S)[DK / 16][NT],
+                                                       const uint8_t* __restrict__ slot, float gn, int jb0, int lane) {
   const uint16_t* Wneg = reinterpret_cast<const uint16_t*>(slot);
   const uint16_t* KtT = Wneg + kChunk * DK;
-  mfma::f32x4 Ut[kChunk / 16];
-  load_u_tiles<DV>(Ut, slot, DK, jb, lane);
-  chain_step_bf16<DK>(S, Wneg, DK, KtT, kChunk, Ut, gn, lane);
+  mfma::f32x4 Ut[kChunk / 16][NT];
+  load_u_tiles<DV, NT>(Ut, slot, DK, jb0, lane);
+  chain_step_bf16<DK, NT>(S, Wneg, DK, KtT, kChunk, Ut, gn, lane);
 }
 
-// State tile I/O for one 16-column block: rows 16 im + 4 g + r, column 16 jb + c.
-template <int DK, int DV>
-__device__ __forceinline__ void load_state_tiles(mfma::f32x4 (&S)[DK / 16], const float* __restrict__ src, int jb,
-                                                 int lane) {
+// State tile I/O for NT 16-column blocks from block jb0 (row-major [DK][DV]
+// states): rows 16 im + 4 g + r, column 16 (jb0 + nt) + c.
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void load_state_tiles(mfma::f32x4 (&S)[DK / 16][NT], const float* __restrict__ src,
+                                                 int jb0, int lane) {
   const int lr = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int im = 0; im < DK / 16; ++im)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[im][r] = src ? src[(size_t)(16 * im + 4 * g + r) * DV + 16 * jb + lr] : 0.f;
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[im][nt][r] = src ? src[(size_t)(16 * im + 4 * g + r) * DV + 16 * (jb0 + nt) + lr] : 0.f;
 }
 
-template <int DK, int DV>
-__device__ __forceinline__ void store_state_tiles(float* __restrict__ dst, const mfma::f32x4 (&S)[DK / 16], int jb,
-                                                  int lane) {
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void store_state_tiles(float* __restrict__ dst, const mfma::f32x4 (&S)[DK / 16][NT],
+                                                  int jb0, int lane) {
   const int lr = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int im = 0; im < DK / 16; ++im)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(size_t)(16 * im + 4 * g + r) * DV + 16 * jb + lr] = S[im][r];
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * im + 4 * g + r) * DV + 16 * (jb0 + nt) + lr] = S[im][nt][r];
+}
+
+// Boundary states inside the workspace are kept in accumulator-tile order:
+// element (row, col) of a [DK][DV] state at
+//   (((col / 16) * (DK / 16) + row / 16) * 64 + 16 ((row % 16) / 4) + col % 16) * 4 + row % 4,
+// so the chain writes one 16-byte store per tile and the scan reads each
+// lane's column with 16-byte loads.
+template <int DK>
+__host__ __device__ __forceinline__ size_t bnd_index(int row, int col) {
+  return ((size_t)((col >> 4) * (DK / 16) + (row >> 4)) * 64 + 16 * ((row & 15) >> 2) + (col & 15)) * 4 + (row & 3);
+}
+
+template <int DK, int NT>
+__device__ __forceinline__ void store_bnd_tiles(float* __restrict__ dst, const mfma::f32x4 (&S)[DK / 16][NT], int jb0,
+                                                int lane) {
+#pragma unroll
+  for (int im = 0; im < DK / 16; ++im)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<mfma::f32x4*>(dst + ((size_t)((jb0 + nt) * (DK / 16) + im) * 64 + lane) * 4) = S[im][nt];
+}
+
+// the same layout from a row-major [DK][DV] state (or zeros), for chunk 0
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void store_bnd_tiles_from_rows(float* __restrict__ dst, const float* __restrict__ src,
+                                                          int jb0, int lane) {
+  mfma::f32x4 S[DK / 16][NT];
+  load_state_tiles<DK, DV, NT>(S, src, jb0, lane);
+  store_bnd_tiles<DK, NT>(dst, S, jb0, lane);
 }
 
 }  // namespace cpr

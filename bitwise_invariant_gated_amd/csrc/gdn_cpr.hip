@@ -278,6 +278,15 @@ __device__ __forceinline__ void put_block(float* __restrict__ dst, const ChainLd
   }
 }
 
+// the same block into a boundary slot (accumulator-tile order, bnd_index)
+template <int DK, int DV, int NB>
+__device__ __forceinline__ void put_block_bnd(float* __restrict__ dst, const ChainLds<DK, NB>& sm, int col0) {
+  for (int idx = threadIdx.x; idx < DK * NB; idx += blockDim.x) {
+    const int i = idx / NB, j = idx % NB;
+    dst[bnd_index<DK>(i, col0 + j)] = sm.S[i][j];
+  }
+}
+
 template <int DK, int DV, int NB>
 __device__ __forceinline__ void get_block(ChainLds<DK, NB>& sm, const float* __restrict__ src, int col0) {
   for (int idx = threadIdx.x; idx < DK * NB; idx += blockDim.x) {
@@ -299,13 +308,13 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
   const size_t SS = (size_t)DK * DV;
   get_block<DK, DV, NB>(sm, a.h0 ? a.h0 + sh * SS : nullptr, col0);
   const int abase = a.all_base[i], fbase = a.full_base[i];
-  if (nall > 0) put_block<DK, DV, NB>(a.bnd + ((size_t)abase * H + h) * SS, sm, col0);
+  if (nall > 0) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)abase * H + h) * SS, sm, col0);
   for (int c = 0; c < nfull; ++c) {
     const size_t slot = (size_t)(fbase + c) * H + h;
     stage_products<DK, DV, NB>(sm, (const float*)(a.prod + slot * prod_slot_bytes(false, DK, DV)), a.gamn + slot,
                                col0);
     chain_step_f32<DK, NB>(sm);
-    if (c + 1 < nall) put_block<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
+    if (c + 1 < nall) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
   }
   put_block<DK, DV, NB>(a.s_bnd + sh * SS, sm, col0);
   if (L % C == 0) put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
@@ -327,11 +336,13 @@ __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
 }
 
-// bf16 path: one work-group per (sequence, head), one wave per 16 state
-// columns; each wave keeps its block of the state in MFMA accumulator tiles
-// for the whole chain.  The next chunk's Wneg and KtT (shared by all column
-// blocks) are staged into LDS while the current step runs; each wave
-// prefetches its own U tiles.
+// bf16 path: one work-group per (sequence, head), one wave per 32 state
+// columns (two 16-column tiles); each wave keeps its block of the state in
+// MFMA accumulator tiles for the whole chain.  The next chunk's Wneg and KtT
+// (shared by all waves) are staged into LDS while the current step runs;
+// each wave prefetches its own U tiles.
+constexpr int kChainNT = 2;  // 16-column tiles per wave
+
 template <int DK>
 struct ChainStage {
   static constexpr int kW = DK + 8, kK = C + 8;  // padded LDS row strides (elements)
@@ -340,15 +351,16 @@ struct ChainStage {
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(DV * 4) void k_chain_prefill_bf16(const PrefillArgs a) {
+__global__ __launch_bounds__(DV * 2) void k_chain_prefill_bf16(const PrefillArgs a) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  constexpr int kThreads = DV * 4;                       // DV / 16 waves
+  constexpr int NT = kChainNT;
+  constexpr int kThreads = DV * 2;                        // DV / 32 waves
   constexpr int kPieces = (C * DK + DK * C) / 8;          // 16-byte pieces of Wneg + KtT
   constexpr int kPer = kPieces / kThreads;
   static_assert(kPieces % kThreads == 0, "staging split");
   __shared__ ChainStage<DK> st;
   const int i = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, jb = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, jb0 = (tid >> 6) * NT, lane = tid & 63;
   const int H = a.H;
   const int L = a.cu[i + 1] - a.cu[i];
   const int nfull = L / C, nall = (L + C - 1) / C;
@@ -356,10 +368,11 @@ __global__ __launch_bounds__(DV * 4) void k_chain_prefill_bf16(const PrefillArgs
   const size_t SS = (size_t)DK * DV;
   const size_t sbytes = prod_slot_bytes(true, DK, DV);
   const int abase = a.all_base[i], fbase = a.full_base[i];
+  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * sbytes; };
 
   // piece p of a slot: p < C*DK/8 -> Wneg row p / (DK/8); else KtT row
   auto fetch = [&](int c, u32x4v (&r)[kPer]) {
-    const u32x4v* src = reinterpret_cast<const u32x4v*>(a.prod + ((size_t)(fbase + c) * H + h) * sbytes);
+    const u32x4v* src = reinterpret_cast<const u32x4v*>(slot_of(c));
 #pragma unroll
     for (int m = 0; m < kPer; ++m) r[m] = src[tid + m * kThreads];
   };
@@ -377,69 +390,63 @@ __global__ __launch_bounds__(DV * 4) void k_chain_prefill_bf16(const PrefillArgs
     }
   };
 
-  mfma::f32x4 S[DK / 16];
-  load_state_tiles<DK, DV>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb, lane);
-  if (nall > 0) store_state_tiles<DK, DV>(a.bnd + ((size_t)abase * H + h) * SS, S, jb, lane);
+  mfma::f32x4 S[DK / 16][NT];
+  load_state_tiles<DK, DV, NT>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb0, lane);
+  if (nall > 0) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)abase * H + h) * SS, S, jb0, lane);
   // chunk c's products are in LDS buffer c & 1 during step c; chunk c + 1's
-  // sit in registers (r1, Un1) and chunk c + 2's are being fetched, so each
-  // global load has two steps to arrive
-  mfma::f32x4 Ut[C / 16], Un1[C / 16], Un2[C / 16];
-  u32x4v r1[kPer], r2[kPer];
-  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * sbytes; };
+  // arrive in registers (r, Un) meanwhile
+  mfma::f32x4 Ut[C / 16][NT], Un[C / 16][NT];
+  u32x4v r[kPer];
   if (nfull > 0) {
-    fetch(0, r1);
-    put(0, r1);
-    load_u_tiles<DV>(Ut, slot_of(0), DK, jb, lane);
-  }
-  if (nfull > 1) {
-    fetch(1, r1);
-    load_u_tiles<DV>(Un1, slot_of(1), DK, jb, lane);
+    fetch(0, r);
+    put(0, r);
+    load_u_tiles<DV, NT>(Ut, slot_of(0), DK, jb0, lane);
   }
   __syncthreads();
   for (int c = 0; c < nfull; ++c) {
     const int buf = c & 1;
-    if (c + 2 < nfull) {
-      fetch(c + 2, r2);
-      load_u_tiles<DV>(Un2, slot_of(c + 2), DK, jb, lane);
+    const bool more = c + 1 < nfull;
+    if (more) {
+      fetch(c + 1, r);
+      load_u_tiles<DV, NT>(Un, slot_of(c + 1), DK, jb0, lane);
     }
     const float gn = a.gamn[(size_t)(fbase + c) * H + h];
-    chain_step_bf16<DK>(S, &st.W[buf][0][0], ChainStage<DK>::kW, &st.K[buf][0][0], ChainStage<DK>::kK, Ut, gn,
-                        lane);
-    if (c + 1 < nall) store_state_tiles<DK, DV>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb, lane);
-    if (c + 1 < nfull) {
-      put(buf ^ 1, r1);
+    chain_step_bf16<DK, NT>(S, &st.W[buf][0][0], ChainStage<DK>::kW, &st.K[buf][0][0], ChainStage<DK>::kK, Ut, gn,
+                            lane);
+    if (c + 1 < nall) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb0, lane);
+    if (more) {
+      put(buf ^ 1, r);
 #pragma unroll
-      for (int tm = 0; tm < C / 16; ++tm) Ut[tm] = Un1[tm];
+      for (int tm = 0; tm < C / 16; ++tm)
 #pragma unroll
-      for (int m = 0; m < kPer; ++m) r1[m] = r2[m];
-#pragma unroll
-      for (int tm = 0; tm < C / 16; ++tm) Un1[tm] = Un2[tm];
+        for (int nt = 0; nt < NT; ++nt) Ut[tm][nt] = Un[tm][nt];
     }
     __syncthreads();
   }
-  store_state_tiles<DK, DV>(a.s_bnd + sh * SS, S, jb, lane);
-  if (L % C == 0) store_state_tiles<DK, DV>(a.s_run + sh * SS, S, jb, lane);
+  store_state_tiles<DK, DV, NT>(a.s_bnd + sh * SS, S, jb0, lane);
+  if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + sh * SS, S, jb0, lane);
   if (tid == 0) a.tail_len[sh] = L % C;
 }
 
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
+  constexpr int NT = kChainNT;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
-  const int jb = blockIdx.z, lane = threadIdx.x;
+  const int jb0 = blockIdx.z * NT, lane = threadIdx.x;
   const size_t SS = (size_t)DK * DV;
-  mfma::f32x4 S[DK / 16];
-  load_state_tiles<DK, DV>(S, a.s_bnd + sh * SS, jb, lane);
-  chain_step_bf16_global<DK, DV>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb, lane);
-  store_state_tiles<DK, DV>(a.s_bnd + sh * SS, S, jb, lane);
-  store_state_tiles<DK, DV>(a.s_run + sh * SS, S, jb, lane);
+  mfma::f32x4 S[DK / 16][NT];
+  load_state_tiles<DK, DV, NT>(S, a.s_bnd + sh * SS, jb0, lane);
+  chain_step_bf16_global<DK, DV, NT>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb0, lane);
+  store_state_tiles<DK, DV, NT>(a.s_bnd + sh * SS, S, jb0, lane);
+  store_state_tiles<DK, DV, NT>(a.s_run + sh * SS, S, jb0, lane);
 }
 
 // ---------------------------------------------------------------------------
 // in-chunk scan (prefill): one wave per (chunk, head, 64 state columns)
 
 template <class D, int DK, int DV>
-__global__ __launch_bounds__(64) void k_scan(const PrefillArgs a) {
+__global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   using T = typename D::T;
   const int slot = blockIdx.x, h = blockIdx.y;
   const int N = a.N, H = a.H;
@@ -456,7 +463,13 @@ __global__ __launch_bounds__(64) void k_scan(const PrefillArgs a) {
   const float* B = a.bnd + ((size_t)slot * H + h) * SS;
   float s[DK];
 #pragma unroll
-  for (int ii = 0; ii < DK; ++ii) s[ii] = B[(size_t)ii * DV + col];
+  for (int q = 0; q < DK / 4; ++q) {  // rows 4q .. 4q+3 of column col: one 16-byte load
+    const mfma::f32x4 x = *reinterpret_cast<const mfma::f32x4*>(B + bnd_index<DK>(4 * q, col));
+    s[4 * q] = x[0];
+    s[4 * q + 1] = x[1];
+    s[4 * q + 2] = x[2];
+    s[4 * q + 3] = x[3];
+  }
 
   const T* gp = (const T*)a.g;
   const T* bp = (const T*)a.beta;
@@ -691,12 +704,13 @@ __global__ __launch_bounds__(DV * 4) void k_bwd_chain(const BwdArgs a) {
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
   const int abase = a.all_base[i];
-  f32x4 S[DK / 16];
-  load_state_tiles<DK, DV>(S, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  f32x4 S1[DK / 16][1];
+  load_state_tiles<DK, DV, 1>(S1, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  f32x4(&S)[DK / 16] = *reinterpret_cast<f32x4(*)[DK / 16]>(&S1);
   for (int c = nall - 1; c >= 0; --c) {
     const size_t sl = (size_t)(abase + c) * H + h;
     uint8_t* ws = a.ws + sl * Slot::bytes;
-    store_state_tiles<DK, DV>(reinterpret_cast<float*>(ws + Slot::oDbp), S, jb, lane);
+    store_state_tiles<DK, DV, 1>(reinterpret_cast<float*>(ws + Slot::oDbp), S1, jb, lane);
     const uint16_t* Kt = reinterpret_cast<const uint16_t*>(ws + Slot::oKt);
     const uint16_t* WnT = reinterpret_cast<const uint16_t*>(ws + Slot::oWnT);
     const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
@@ -727,7 +741,7 @@ __global__ __launch_bounds__(DV * 4) void k_bwd_chain(const BwdArgs a) {
       S[im] = acc;
     }
   }
-  if (a.dh0) store_state_tiles<DK, DV>(a.dh0 + sh * SS, S, jb, lane);
+  if (a.dh0) store_state_tiles<DK, DV, 1>(a.dh0 + sh * SS, S1, jb, lane);
 }
 
 // B2 for fp32 inputs: the same reverse chain with fp32 operands on
@@ -745,12 +759,13 @@ __global__ __launch_bounds__(DV * 4) void k_bwd_chain_f32(const BwdArgs a) {
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
   const int abase = a.all_base[i];
-  f32x4 S[DK / 16];
-  load_state_tiles<DK, DV>(S, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  f32x4 S1[DK / 16][1];
+  load_state_tiles<DK, DV, 1>(S1, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  f32x4(&S)[DK / 16] = *reinterpret_cast<f32x4(*)[DK / 16]>(&S1);
   for (int c = nall - 1; c >= 0; --c) {
     const size_t sl = (size_t)(abase + c) * H + h;
     uint8_t* ws = a.ws + sl * Slot::bytes;
-    store_state_tiles<DK, DV>(reinterpret_cast<float*>(ws + Slot::oDbp), S, jb, lane);
+    store_state_tiles<DK, DV, 1>(reinterpret_cast<float*>(ws + Slot::oDbp), S1, jb, lane);
     const float* Kt = reinterpret_cast<const float*>(ws + Slot::oKt);
     const float* WnT = reinterpret_cast<const float*>(ws + Slot::oWnT);
     const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
@@ -779,7 +794,7 @@ __global__ __launch_bounds__(DV * 4) void k_bwd_chain_f32(const BwdArgs a) {
       S[im] = acc;
     }
   }
-  if (a.dh0) store_state_tiles<DK, DV>(a.dh0 + sh * SS, S, jb, lane);
+  if (a.dh0) store_state_tiles<DK, DV, 1>(a.dh0 + sh * SS, S1, jb, lane);
 }
 
 template <int DK, int DV>
@@ -865,7 +880,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = sm.M2[16 * tm + 4 * g + r][16 * jt + lr];
     }
-    acc = tile<DK>([&](int t, int e) { return -sm.M1[t][e]; }, [&](int e, int j) { return Bst[(size_t)e * DV + j]; },
+    acc = tile<DK>([&](int t, int e) { return -sm.M1[t][e]; }, [&](int e, int j) { return Bst[bnd_index<DK>(e, j)]; },
                    16 * tm, 16 * jt, acc);
     tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.M2[t][j] = v; });
   }
@@ -912,7 +927,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   for (int id = wave; id < nK; id += 4) {
     const int tm = id / (DK / 16), it = id % (DK / 16);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int e) { return Bst[(size_t)e * DV + j]; },
+    acc = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int e) { return Bst[bnd_index<DK>(e, j)]; },
                    16 * tm, 16 * it, acc);
     tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
   }
@@ -938,7 +953,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   for (int id = wave; id < nK; id += 4) {
     const int tm = id / (DK / 16), it = id % (DK / 16);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int e) { return Bst[(size_t)e * DV + j]; },
+    acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int e) { return Bst[bnd_index<DK>(e, j)]; },
                    16 * tm, 16 * it, acc);
     tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = -v; });
   }
@@ -1040,7 +1055,8 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   }
   {
     float acc = 0.f;
-    for (int idx = tid; idx < DK * DV; idx += 256) acc = __builtin_fmaf(dBp[idx], Bst[idx], acc);
+    for (int idx = tid; idx < DK * DV; idx += 256)
+      acc = __builtin_fmaf(dBp[idx], Bst[bnd_index<DK>(idx / DV, idx % DV)], acc);
     sm.red[tid] = acc;
   }
   __syncthreads();
@@ -1206,7 +1222,7 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   mark(2, st);
   if (a.N > 0) {
     if constexpr (kBf16)
-      hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV>), dim3(a.N, a.H), dim3(DV * 4), 0, st, a);
+      hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV>), dim3(a.N, a.H), dim3(DV * 2), 0, st, a);
     else
       hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
   }
@@ -1224,7 +1240,7 @@ gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
   mark(1, st);
   if constexpr (std::is_same<D, Bf16>::value) {
     hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / 16), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / 32), dim3(64), 0, st, a);
   } else {
     hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
     hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);

@@ -397,10 +397,12 @@ __global__ __launch_bounds__(DV * 2) void k_chain_prefill_bf16(const PrefillArgs
   // arrive in registers (r, Un) meanwhile
   mfma::f32x4 Ut[C / 16][NT], Un[C / 16][NT];
   u32x4v r[kPer];
+  float gn = 1.f, gn_next = 1.f;
   if (nfull > 0) {
     fetch(0, r);
     put(0, r);
     load_u_tiles<DV, NT>(Ut, slot_of(0), DK, jb0, lane);
+    gn = a.gamn[(size_t)fbase * H + h];
   }
   __syncthreads();
   for (int c = 0; c < nfull; ++c) {
@@ -409,8 +411,8 @@ __global__ __launch_bounds__(DV * 2) void k_chain_prefill_bf16(const PrefillArgs
     if (more) {
       fetch(c + 1, r);
       load_u_tiles<DV, NT>(Un, slot_of(c + 1), DK, jb0, lane);
+      gn_next = a.gamn[(size_t)(fbase + c + 1) * H + h];
     }
-    const float gn = a.gamn[(size_t)(fbase + c) * H + h];
     chain_step_bf16<DK, NT>(S, &st.W[buf][0][0], ChainStage<DK>::kW, &st.K[buf][0][0], ChainStage<DK>::kK, Ut, gn,
                             lane);
     if (c + 1 < nall) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb0, lane);
@@ -420,6 +422,7 @@ __global__ __launch_bounds__(DV * 2) void k_chain_prefill_bf16(const PrefillArgs
       for (int tm = 0; tm < C / 16; ++tm)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) Ut[tm][nt] = Un[tm][nt];
+      gn = gn_next;
     }
     __syncthreads();
   }

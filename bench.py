@@ -36,6 +36,35 @@ PEAK_VALU_F32_PACKED = 157.3
 PEAK_HBM = 8000.0  # GB/s
 
 
+def kernel_source_digest():
+    """sha256 over the HIP sources and the C header (the code the counters were taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bitwise_invariant_gated_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "gdn_cpr.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM-side bytes per launch of `kernel` from the committed PMC summary, or None when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -46,6 +75,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this layer's work is sharded by sequence/head with "
@@ -99,6 +131,15 @@ def main():
     ws_dec = gdn.alloc_workspace(shape, N_dec, 0, gdn.GDN_OP_DECODE, dev)
     o_dec = torch.empty((N_dec, H, D), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_probe_mib MiB
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.current_stream()
     pre_ev = gdn.StageEvents(5)
@@ -255,7 +296,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_VALU_F32, 4),
         "frac_vs_packed_peak": round(achieved / PEAK_VALU_F32_PACKED, 4),
-        "traffic": None,
+        "traffic": measured_traffic("k_scan"),
         "algorithmic_flop_per_launch": flops_scan,
         "avg_launch_ms": round(scan_avg, 5),
     }
@@ -289,6 +330,7 @@ def main():
                                 "bound": "hbm", "algorithmic_bytes_per_launch": dec_bytes,
                                 "achieved": round(dec_bytes / (float(np.mean(dstep_ms)) / 1e3) / 1e9, 1),
                                 "peak": PEAK_HBM, "unit": "GB/s",
+                                "traffic": measured_traffic("k_decode"),
                                 "frac": round(dec_bytes / (float(np.mean(dstep_ms)) / 1e3) / 1e9 / PEAK_HBM, 4)},
                    "whole_call_GBps": round(dec_bytes / (dec_avg / 1e3) / 1e9, 1),
                    "mean_over_64_steps_ms": round(dec64_ms, 5),

@@ -42,9 +42,7 @@ namespace bwd {
 using mfma::f32x4;
 constexpr int C = kChunk;
 
-__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
+using mfma::mma4;
 
 // 16 x 16 output tile at (m0, n0) of sum_k A(m, k) B(k, n), k < K (K % 4 == 0).
 // fp32 operand layout: lane holds A[m0 + c][k0 + g] and B[k0 + g][n0 + c].

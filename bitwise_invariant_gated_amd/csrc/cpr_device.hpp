@@ -424,41 +424,55 @@ __device__ __forceinline__ u32x4 frag_row(const uint16_t* row, int k0, int g) {
 
 }  // namespace mfma
 
+// Chunk-product slot of the bf16 path.  It is written in the order the
+// boundary chain consumes it: every 1 KB block is one wave-wide MFMA operand
+// with lane l's 16 bytes at byte 16 l, so the chain reads it with contiguous
+// 16-byte loads.  Lane l = 16 g + c:
+//   WF  A fragments of Wneg = -W (C x DK); fragment (kb, tm) is block
+//       kb * C/16 + tm; lane holds Wneg[16 tm + c][32 kb + 4 g + {0..3}] and
+//       Wneg[16 tm + c][32 kb + 16 + 4 g + {0..3}]
+//   KF  A fragments of K~^T (DK x C); fragment (kb, im) is block kb * DK/16 + im;
+//       lane holds KtT[16 im + c][32 kb + 4 g + {0..3}] and [32 kb + 16 + 4 g + {0..3}]
+//   UT  U (C x DV) fp32 in accumulator tiles; tile (jt, tm) is block
+//       jt * C/16 + tm; lane holds U[16 tm + 4 g + r][16 jt + c], r = 0..3
+template <int DK, int DV>
+struct SlotB {
+  static constexpr size_t oWF = 0;
+  static constexpr size_t oKF = (size_t)kChunk * DK * 2;
+  static constexpr size_t oU = oKF + (size_t)DK * kChunk * 2;
+  static constexpr size_t bytes = oU + (size_t)kChunk * DV * 4;
+};
+
 // Chunk products, bf16 path (one full chunk, one head, 256 threads = 4 waves).
 //   gamma = left-to-right fp32 cumsum of g; Gamma_t = exp(gamma_t);
 //   e_t = exp(gamma_{C-1} - gamma_t)
 //   G = K K^T                             (MFMA, bf16 K exact, fp32 sums)
 //   L[t][s] = (beta_t * exp(gamma_t - gamma_s)) * G[t][s], s < t   (fp32)
-//   T = (I + L)^{-1} diag(beta)           (fp32 forward substitution: lane =
-//                                          column s, rows t ascending, each row
-//                                          acc = (t == s ? beta_t : 0), then
-//                                          acc = fma(-L[t][r], T[r][s], acc), r < t)
-//   Wneg = -( bf16(T diag(Gamma)) K )     (MFMA; stored bf16, row-major [C][DK])
-//   U    = bf16(T) V                      (MFMA; stored fp32, accumulator tiles)
-//   KtT  = bf16(e_r * K[r][i])            (stored bf16, row-major [DK][C])
+//   X = (I + L)^{-1} by 16 x 16 blocks (fp32):
+//     diagonal blocks X_BB = (I + L_BB)^{-1} by forward substitution: lane =
+//       column s, rows q ascending, acc = (q == s), then
+//       acc = fma(-L[q][r], X[r][s], acc) for r = 0 .. q-1 ascending;
+//     below the diagonal, block rows B = 1, 2, 3 in turn, for j < B:
+//       Y = sum_{k=j}^{B-1} L_Bk X_kj,  X_Bj = -X_BB Y
+//       (v_mfma_f32_16x16x4_f32, blocks k ascending; step m of a 16-wide
+//       block contracts index 4 g + m in lane group g)
+//   T = X diag(beta);  TB = bf16(T);  TG = bf16(T diag(Gamma))
+//   W^T = K^T TG^T  -> Wneg fragments (MFMA bf16; W rounded to bf16, negated)
+//   U   = TB V                         (MFMA bf16; fp32 tiles)
+//   KtT = bf16(e_r * K[r][i])
 //   Gamma_n = Gamma_{C-1}
 template <int DK, int DV>
 struct alignas(16) ChunkLdsB {
-  union {
-    uint16_t K[kChunk][DK + 8];  // row-major K, needed only for G
-    struct {
-      uint16_t TG[kChunk][kChunk + 8];
-      uint16_t TB[kChunk][kChunk + 8];
-    } t;  // written after G is done
-  } u;
-  uint16_t KT[DK][kChunk + 8];
-  uint16_t VT[DV][kChunk + 8];
-  float LT[kChunk][kChunk + 4];  // LT[s][t] = L[t][s]
+  static constexpr int kLK = DK + 8, kLV = DV + 8, kLA = kChunk + 4, kLT = kChunk + 8;
+  uint16_t K[kChunk][kLK];   // row-major K
+  uint16_t V[kChunk][kLV];   // row-major V
+  float A[kChunk][kLA];      // A[t][s] = L[t][s] (s < t); A[s][t] = X[t][s] (s <= t)
+  uint16_t TG[kChunk][kLT];  // bf16(T diag(Gamma)), row-major
+  uint16_t TB[kChunk][kLT];  // bf16(T), row-major
   float g[kChunk], beta[kChunk], gam[kChunk], Gam[kChunk], e[kChunk];
 };
 
-// Workspace bytes of one chunk-product slot on the bf16 path.
-template <int DK, int DV>
-__host__ __device__ constexpr size_t prod_bytes_bf16() {
-  return (size_t)kChunk * DK * 2 + (size_t)DK * kChunk * 2 + (size_t)kChunk * DV * 4;
-}
-
-// Stage one chunk (bf16 rows) into LDS: K row-major, K^T, V^T, g, beta.
+// Stage one chunk (bf16 rows) into LDS: K and V row-major, g, beta.
 // Row t of k starts at k + (k_row0 + t * k_stride) * DK (likewise v); g and
 // beta at gb0 + t * gb_stride.
 template <int DK, int DV>
@@ -472,16 +486,13 @@ __device__ __forceinline__ void stage_chunk_bf16(ChunkLdsB<DK, DV>& sm, const ui
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   for (int idx = tid; idx < kChunk * DK / 8; idx += nt) {
     const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    const u32x4v w = *reinterpret_cast<const u32x4v*>(k + (k_row0 + (size_t)t * k_stride) * DK + i0);
-    *reinterpret_cast<u32x4v*>(&sm.u.K[t][i0]) = w;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm.KT[i0 + e][t] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) =
+        *reinterpret_cast<const u32x4v*>(k + (k_row0 + (size_t)t * k_stride) * DK + i0);
   }
   for (int idx = tid; idx < kChunk * DV / 8; idx += nt) {
     const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-    const u32x4v w = *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm.VT[j0 + e][t] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) =
+        *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
   }
   for (int t = tid; t < kChunk; t += nt) {
     sm.g[t] = Bf16::load(g, gb0 + (size_t)t * gb_stride);
@@ -490,16 +501,31 @@ __device__ __forceinline__ void stage_chunk_bf16(ChunkLdsB<DK, DV>& sm, const ui
   __syncthreads();
 }
 
-// Caller staged the chunk and synchronised; 256 threads.  Writes the slot:
-// Wneg [C][DK] bf16, KtT [DK][C] bf16, U [C*DV] fp32 in accumulator tiles
-// (tile (tm, jt) = 16 rows x 16 columns at ((tm * DV/16 + jt) * 64 + lane) * 4).
+namespace mfma {
+// Fragment whose k index runs down the rows of a row-major bf16 matrix M
+// (leading dimension ld): lane 16 g + c gets M[k0 + 4 g + e][col] and
+// M[k0 + 16 + 4 g + e][col], e = 0..3 (col already includes c).
+__device__ __forceinline__ u32x4 frag_col(const uint16_t* M, int ld, int k0, int col, int g) {
+  const uint16_t* p = M + (k0 + 4 * g) * ld + col;
+  const uint16_t* q = p + 16 * ld;
+  return u32x4{(uint32_t)p[0] | ((uint32_t)p[ld] << 16), (uint32_t)p[2 * ld] | ((uint32_t)p[3 * ld] << 16),
+               (uint32_t)q[0] | ((uint32_t)q[ld] << 16), (uint32_t)q[2 * ld] | ((uint32_t)q[3 * ld] << 16)};
+}
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+}  // namespace mfma
+
+// Caller staged the chunk and synchronised; 256 threads.  Writes the slot
+// (SlotB layout) and *gamn.
 template <int DK, int DV>
-__device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ slot, float* __restrict__ gamn) {
+__device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ slot,
+                                                 float* __restrict__ gamn) {
   using namespace mfma;
   constexpr int C = kChunk;
-  uint16_t* Wneg = reinterpret_cast<uint16_t*>(slot);
-  uint16_t* KtT = Wneg + C * DK;
-  float* U = reinterpret_cast<float*>(KtT + DK * C);
+  typedef SlotB<DK, DV> Sl;
+  static_assert(DK % 32 == 0 && DV % 32 == 0, "head dims are multiples of 32");
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   if (tid == 0) {
@@ -515,104 +541,147 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
     sm.Gam[tid] = expf(sm.gam[tid]);
     sm.e[tid] = expf(sm.gam[C - 1] - sm.gam[tid]);
   }
-  // G = K K^T, 16 tiles, 4 per wave; L from G
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tile = wave * 4 + q, tm = tile >> 2, tn = tile & 3;
+  // L from G = K K^T: the 10 tiles on or below the diagonal
+  for (int q = wave; q < 10; q += 4) {
+    const int tm = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+    const int tn = q - tm * (tm + 1) / 2;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb)
-      acc = mma(frag_row(&sm.u.K[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.u.K[16 * tn + lr][0], 32 * kb, g), acc);
+      acc = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
-      sm.LT[s][t] = (s < t) ? (sm.beta[t] * expf(sm.gam[t] - sm.gam[s])) * acc[r] : 0.f;
+      if (s < t) sm.A[t][s] = (sm.beta[t] * expf(sm.gam[t] - sm.gam[s])) * acc[r];
     }
   }
   __syncthreads();
   if (wave == 0) {
-    // Forward substitution, one wave, lane = column s of T.  Rows are solved
-    // in blocks of 16 held in registers; each T[t][s] accumulates
-    // fma(-L[t][r], T[r][s], .) over r = 0 .. t-1 in ascending order from the
-    // initial value (t == s ? beta_t : 0) -- first the finished rows r < 16 B,
-    // read back from LDS, then the rows of its own block (right-looking).
-    // Finished T[r][s] (s <= r) are stored in the lower triangle of LT, which
-    // holds no L entries (LT[r][s] = L[s][r] is zero for s <= r).
-    const int s = lane;
+    // diagonal blocks, all four at once: lane 16 B + s solves column s of block B
+    const int B = lane >> 4, s = lane & 15, o = 16 * B;
+    float x[16];
 #pragma unroll
-    for (int B = 0; B < C / 16; ++B) {
-      float x[16];
+    for (int q = 0; q < 16; ++q) {
+      float acc = (q == s) ? 1.f : 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) x[q] = (16 * B + q == s) ? sm.beta[16 * B + q] : 0.f;
-#pragma unroll 2
-      for (int r = 0; r < 16 * B; ++r) {
-        const float xr = (s <= r) ? sm.LT[r][s] : 0.f;  // T[r][s]
-#pragma unroll
-        for (int q = 0; q < 16; ++q) x[q] = __builtin_fmaf(-sm.LT[r][16 * B + q], xr, x[q]);
-      }
-#pragma unroll
-      for (int r = 0; r < 15; ++r) {
-#pragma unroll
-        for (int q = r + 1; q < 16; ++q) x[q] = __builtin_fmaf(-sm.LT[16 * B + r][16 * B + q], x[r], x[q]);
-      }
-      const float gs = sm.Gam[s];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int t = 16 * B + q;
-        if (s <= t) sm.LT[t][s] = x[q];
-        sm.u.t.TG[t][s] = Bf16::round(x[q] * gs);
-        sm.u.t.TB[t][s] = Bf16::round(x[q]);
-      }
+      for (int r = 0; r < q; ++r) acc = __builtin_fmaf(-sm.A[o + q][o + r], x[r], acc);
+      x[q] = acc;  // exactly +0 for q < s
     }
+    // X[o + q][o + s] -> A[o + s][o + q] (the zeros land on L_BB, which is no longer read)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<f32x4*>(&sm.A[o + s][o + 4 * q4]) = f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
   } else {
-    // KtT = bf16(e_r K[r][i]) while wave 0 solves
-    for (int idx = tid - 64; idx < DK * C; idx += 192) {
-      const int i = idx / C, r = idx % C;
-      KtT[idx] = Bf16::round(sm.e[r] * Bf16::load(&sm.KT[i][0], r));
+    // K~^T fragments meanwhile
+    for (int f = wave - 1; f < (C / 32) * (DK / 16); f += 3) {
+      const int kb = f / (DK / 16), im = f % (DK / 16);
+      const u32x4 raw = frag_col(&sm.K[0][0], ChunkLdsB<DK, DV>::kLK, 32 * kb, 16 * im + lr, g);
+      u32x4 out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int r = 32 * kb + 16 * (w >> 1) + 4 * g + 2 * (w & 1);
+        out[w] = pack2(sm.e[r] * __uint_as_float(raw[w] << 16), sm.e[r + 1] * __uint_as_float(raw[w] & 0xffff0000u));
+      }
+      *reinterpret_cast<u32x4*>(slot + Sl::oKF + ((size_t)f * 64 + lane) * 16) = out;
     }
   }
   __syncthreads();
-  // W and U tiles
-  constexpr int nW = 4 * (DK / 16), nU = 4 * (DV / 16);
-  for (int tile = wave; tile < nW + nU; tile += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (tile < nW) {
-      const int tm = tile / (DK / 16), it = tile % (DK / 16);
+  // blocks below the diagonal, one block row at a time
+#pragma unroll
+  for (int B = 1; B < C / 16; ++B) {
+    if (wave < B) {
+      const int j = wave;
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = j; kk < B; ++kk)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          Y = mma4(sm.A[16 * B + lr][16 * kk + 4 * g + m], sm.A[16 * j + lr][16 * kk + 4 * g + m], Y);
+      f32x4 Xb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Xb = mma4(-sm.A[16 * B + 4 * g + m][16 * B + lr], Y[m], Xb);
+      *reinterpret_cast<f32x4*>(&sm.A[16 * j + lr][16 * B + 4 * g]) = Xb;
+    }
+    __syncthreads();
+  }
+  // T = X diag(beta) -> TB, TG
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int r = idx / C, t = idx % C;
+    const float T = (r <= t) ? sm.A[r][t] * sm.beta[r] : 0.f;
+    sm.TB[t][r] = Bf16::round(T);
+    sm.TG[t][r] = Bf16::round(T * sm.Gam[r]);
+  }
+  __syncthreads();
+  // Wneg fragments: W^T tiles (2 p, tm) and (2 p + 1, tm) form fragment (p, tm)
+  for (int p = wave; p < DK / 32; p += 4) {
+    u32x4 Kt[2][C / 32];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb)
-        acc = mma(frag_row(&sm.u.t.TG[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.KT[16 * it + lr][0], 32 * kb, g), acc);
+        Kt[h][kb] = frag_col(&sm.K[0][0], ChunkLdsB<DK, DV>::kLK, 32 * kb, 32 * p + 16 * h + lr, g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Wneg[(16 * tm + 4 * g + r) * DK + 16 * it + lr] = Bf16::round(-acc[r]);
-    } else {
-      const int u = tile - nW, tm = u / (DV / 16), jt = u % (DV / 16);
+    for (int tm = 0; tm < C / 16; ++tm) {
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kb = 0; kb < C / 32; ++kb) {
+        const u32x4 tg = frag_row(&sm.TG[16 * tm + lr][0], 32 * kb, g);
+        acc[0] = mma(Kt[0][kb], tg, acc[0]);
+        acc[1] = mma(Kt[1][kb], tg, acc[1]);
+      }
+      const u32x4 out = {pack2(-acc[0][0], -acc[0][1]), pack2(-acc[0][2], -acc[0][3]), pack2(-acc[1][0], -acc[1][1]),
+                         pack2(-acc[1][2], -acc[1][3])};
+      *reinterpret_cast<u32x4*>(slot + Sl::oWF + ((size_t)(p * (C / 16) + tm) * 64 + lane) * 16) = out;
+    }
+  }
+  // U tiles (tm, jt), jt = 2 p, 2 p + 1
+  for (int p = wave; p < DV / 32; p += 4) {
+    u32x4 Vt[2][C / 32];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb)
-        acc = mma(frag_row(&sm.u.t.TB[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.VT[16 * jt + lr][0], 32 * kb, g), acc);
-      *reinterpret_cast<f32x4*>(U + ((size_t)(tm * (DV / 16) + jt) * 64 + lane) * 4) = acc;
+        Vt[h][kb] = frag_col(&sm.V[0][0], ChunkLdsB<DK, DV>::kLV, 32 * kb, 32 * p + 16 * h + lr, g);
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kb = 0; kb < C / 32; ++kb) {
+        const u32x4 tb = frag_row(&sm.TB[16 * tm + lr][0], 32 * kb, g);
+        acc[0] = mma(tb, Vt[0][kb], acc[0]);
+        acc[1] = mma(tb, Vt[1][kb], acc[1]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<f32x4*>(slot + Sl::oU + ((size_t)((2 * p + h) * (C / 16) + tm) * 64 + lane) * 16) = acc[h];
     }
   }
   if (tid == 0) *gamn = sm.Gam[C - 1];
 }
 
-// Boundary advance on the bf16 path for one 16-column block of the state,
-// one wave.  S[im] is the accumulator tile of state rows 16 im .. 16 im + 15.
+// Boundary advance on the bf16 path for NT 16-column blocks of the state,
+// one wave.  S[im][nt] is the accumulator tile of state rows 16 im .. 16 im + 15.
 //   Sb    = bf16(S)                            (B fragments)
 //   Delta = U + Wneg Sb                        (acc starts at U, k ascending)
 //   S'    = Gamma_n * S + KtT bf16(Delta)      (acc starts at Gamma_n * S)
-// Wneg rows are w_stride elements apart and KtT rows kt_stride apart (the
-// global slot layout is unpadded; LDS copies are padded).  NT 16-column tiles
-// per wave: every A fragment read feeds NT MFMAs.  All A fragments of a k
-// step are read before its MFMAs, and k steps run outermost so consecutive
-// MFMAs are independent; each tile accumulates its k steps in ascending order
-// from its initial value, so the result does not depend on NT or on where
-// the operands come from.
-template <int DK, int NT>
-__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], const uint16_t* Wneg, int w_stride,
-                                                const uint16_t* KtT, int kt_stride,
-                                                const mfma::f32x4 (&Ut)[kChunk / 16][NT], float gn, int lane) {
+// wf(kb, tm) and kf(kb, im) return the slot's WF / KF fragments (from LDS or
+// global memory).  k steps run outermost so consecutive MFMAs are
+// independent; each tile accumulates its k steps in ascending order from its
+// initial value, so the result depends neither on NT nor on where the
+// operands come from.
+template <int DK, int NT, class FW, class FK>
+__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], FW&& wf, FK&& kf,
+                                                const mfma::f32x4 (&Ut)[kChunk / 16][NT], float gn) {
   using namespace mfma;
   constexpr int C = kChunk;
-  const int lr = lane & 15, g = lane >> 4;
+  u32x4 Wf[DK / 32][C / 16], Kf[C / 32][DK / 16];
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb)
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) Wf[kb][tm] = wf(kb, tm);
+#pragma unroll
+  for (int kb = 0; kb < C / 32; ++kb)
+#pragma unroll
+    for (int im = 0; im < DK / 16; ++im) Kf[kb][im] = kf(kb, im);
   u32x4 Sb[DK / 32][NT];
 #pragma unroll
   for (int kb = 0; kb < DK / 32; ++kb)
@@ -624,15 +693,11 @@ __device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], c
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) D[tm][nt] = Ut[tm][nt];
 #pragma unroll
-  for (int kb = 0; kb < DK / 32; ++kb) {
-    u32x4 Wf[C / 16];
-#pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) Wf[tm] = frag_row(Wneg + (16 * tm + lr) * w_stride, 32 * kb, g);
+  for (int kb = 0; kb < DK / 32; ++kb)
 #pragma unroll
     for (int tm = 0; tm < C / 16; ++tm)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) D[tm][nt] = mma(Wf[tm], Sb[kb][nt], D[tm][nt]);
-  }
+      for (int nt = 0; nt < NT; ++nt) D[tm][nt] = mma(Wf[kb][tm], Sb[kb][nt], D[tm][nt]);
   u32x4 Db[C / 32][NT];
 #pragma unroll
   for (int kb = 0; kb < C / 32; ++kb)
@@ -644,37 +709,31 @@ __device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], c
     for (int nt = 0; nt < NT; ++nt)
       S[im][nt] = f32x4{gn * S[im][nt][0], gn * S[im][nt][1], gn * S[im][nt][2], gn * S[im][nt][3]};
 #pragma unroll
-  for (int kb = 0; kb < C / 32; ++kb) {
+  for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
-    for (int im = 0; im < DK / 16; ++im) {
-      const u32x4 Kf = frag_row(KtT + (16 * im + lr) * kt_stride, 32 * kb, g);
+    for (int im = 0; im < DK / 16; ++im)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S[im][nt] = mma(Kf, Db[kb][nt], S[im][nt]);
-    }
-  }
+      for (int nt = 0; nt < NT; ++nt) S[im][nt] = mma(Kf[kb][im], Db[kb][nt], S[im][nt]);
 }
 
-// U tiles of NT 16-column blocks starting at block jb0.
-template <int DV, int NT>
-__device__ __forceinline__ void load_u_tiles(mfma::f32x4 (&Ut)[kChunk / 16][NT], const uint8_t* __restrict__ slot,
-                                             int DK, int jb0, int lane) {
-  const float* U = reinterpret_cast<const float*>(slot + (size_t)kChunk * DK * 4);
-#pragma unroll
-  for (int tm = 0; tm < kChunk / 16; ++tm)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      Ut[tm][nt] = *reinterpret_cast<const mfma::f32x4*>(U + ((size_t)(tm * (DV / 16) + jb0 + nt) * 64 + lane) * 4);
-}
-
-// One step straight from a global chunk-product slot (decode resync).
+// One step straight from a global chunk-product slot (decode resync), for
+// the NT 16-column blocks starting at block jb0.
 template <int DK, int DV, int NT>
 __device__ __forceinline__ void chain_step_bf16_global(mfma::f32x4 (&S)[DK / 16][NT],
                                                        const uint8_t* __restrict__ slot, float gn, int jb0, int lane) {
-  const uint16_t* Wneg = reinterpret_cast<const uint16_t*>(slot);
-  const uint16_t* KtT = Wneg + kChunk * DK;
+  typedef SlotB<DK, DV> Sl;
+  typedef mfma::u32x4 F;
+  const F* W = reinterpret_cast<const F*>(slot + Sl::oWF);
+  const F* K = reinterpret_cast<const F*>(slot + Sl::oKF);
+  const mfma::f32x4* U = reinterpret_cast<const mfma::f32x4*>(slot + Sl::oU);
   mfma::f32x4 Ut[kChunk / 16][NT];
-  load_u_tiles<DV, NT>(Ut, slot, DK, jb0, lane);
-  chain_step_bf16<DK, NT>(S, Wneg, DK, KtT, kChunk, Ut, gn, lane);
+#pragma unroll
+  for (int tm = 0; tm < kChunk / 16; ++tm)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) Ut[tm][nt] = U[((jb0 + nt) * (kChunk / 16) + tm) * 64 + lane];
+  chain_step_bf16<DK, NT>(
+      S, [&](int kb, int tm) { return W[(kb * (kChunk / 16) + tm) * 64 + lane]; },
+      [&](int kb, int im) { return K[(kb * (DK / 16) + im) * 64 + lane]; }, Ut, gn);
 }
 
 // State tile I/O for NT 16-column blocks from block jb0 (row-major [DK][DV]

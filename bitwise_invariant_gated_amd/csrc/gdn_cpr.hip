@@ -336,104 +336,116 @@ __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
 }
 
-// bf16 path: one work-group per (sequence, head), one wave per 32 state
-// columns (two 16-column tiles); each wave keeps its block of the state in
-// MFMA accumulator tiles for the whole chain.  The next chunk's Wneg and KtT
-// (shared by all waves) are staged into LDS while the current step runs;
-// each wave prefetches its own U tiles.
-constexpr int kChainNT = 2;  // 16-column tiles per wave
-
-template <int DK>
-struct ChainStage {
-  static constexpr int kW = DK + 8, kK = C + 8;  // padded LDS row strides (elements)
-  uint16_t W[2][C][kW];
-  uint16_t K[2][DK][kK];
-};
-
-template <int DK, int DV>
-__global__ __launch_bounds__(DV * 2) void k_chain_prefill_bf16(const PrefillArgs a) {
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  constexpr int NT = kChainNT;
-  constexpr int kThreads = DV * 2;                        // DV / 32 waves
-  constexpr int kPieces = (C * DK + DK * C) / 8;          // 16-byte pieces of Wneg + KtT
+// bf16 path: one work-group per (sequence, head, block of CB = WAVES * NT * 16
+// state columns); each wave keeps NT 16-column tiles of the state in MFMA
+// accumulator tiles for the whole chain.  A chunk's WF / KF fragments (shared
+// by the work-group) and the U tiles of its columns go through a two-buffer
+// LDS stage; the loads run two chunks ahead in registers, so each step only
+// waits on loads issued a full step earlier.  The column split is bit-neutral
+// (every state column's arithmetic depends only on that column), so the
+// launch picks WAVES and NT by the number of (sequence, head) pairs.
+template <int DK, int DV, int WAVES, int NT>
+__global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const PrefillArgs a) {
+  using namespace mfma;
+  typedef SlotB<DK, DV> Sl;
+  constexpr int kThreads = WAVES * 64;
+  constexpr int CB = WAVES * NT * 16;
+  constexpr int kFragPieces = (int)(Sl::oU / 16);  // WF + KF, 16-byte pieces
+  constexpr int kUPieces = C * CB * 4 / 16;        // U tiles of this block's columns
+  constexpr int kPieces = kFragPieces + kUPieces;
   constexpr int kPer = kPieces / kThreads;
-  static_assert(kPieces % kThreads == 0, "staging split");
-  __shared__ ChainStage<DK> st;
+  constexpr int kPerFrag = kFragPieces / kThreads;
+  static_assert(kPieces % kThreads == 0 && kFragPieces % kThreads == 0, "staging split");
+  static_assert(DV % CB == 0, "column blocks tile d_v");
+  __shared__ u32x4 stage[2][kPieces];
   const int i = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, jb0 = (tid >> 6) * NT, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int jbg = blockIdx.z * (CB / 16), jb0 = jbg + wave * NT;
   const int H = a.H;
   const int L = a.cu[i + 1] - a.cu[i];
   const int nfull = L / C, nall = (L + C - 1) / C;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
-  const size_t sbytes = prod_slot_bytes(true, DK, DV);
   const int abase = a.all_base[i], fbase = a.full_base[i];
-  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * sbytes; };
-
-  // piece p of a slot: p < C*DK/8 -> Wneg row p / (DK/8); else KtT row
-  auto fetch = [&](int c, u32x4v (&r)[kPer]) {
-    const u32x4v* src = reinterpret_cast<const u32x4v*>(slot_of(c));
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) r[m] = src[tid + m * kThreads];
-  };
-  auto put = [&](int buf, const u32x4v (&r)[kPer]) {
+  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * Sl::bytes; };
+  auto gamn_of = [&](int c) { return a.gamn[(size_t)(fbase + c) * H + h]; };
+  // piece p of chunk c: WF/KF piece p, or U piece p - kFragPieces of this block's tiles
+  auto fetch = [&](int c, u32x4 (&r)[kPer]) {
+    const uint8_t* s = slot_of(c);
+    const u32x4* f = reinterpret_cast<const u32x4*>(s);
+    const u32x4* u = reinterpret_cast<const u32x4*>(s + Sl::oU) + (size_t)jbg * (C / 16) * 64;
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
       const int p = tid + m * kThreads;
-      if (p < C * DK / 8) {
-        const int row = p / (DK / 8), c8 = (p % (DK / 8)) * 8;
-        *reinterpret_cast<u32x4v*>(&st.W[buf][row][c8]) = r[m];
-      } else {
-        const int q = p - C * DK / 8, row = q / (C / 8), c8 = (q % (C / 8)) * 8;
-        *reinterpret_cast<u32x4v*>(&st.K[buf][row][c8]) = r[m];
-      }
+      r[m] = m < kPerFrag ? f[p] : u[p - kFragPieces];
     }
   };
+  auto put = [&](int buf, const u32x4 (&r)[kPer]) {
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) stage[buf][tid + m * kThreads] = r[m];
+  };
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  mfma::f32x4 S[DK / 16][NT];
+  f32x4 S[DK / 16][NT];
   load_state_tiles<DK, DV, NT>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb0, lane);
   if (nall > 0) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)abase * H + h) * SS, S, jb0, lane);
-  // chunk c's products are in LDS buffer c & 1 during step c; chunk c + 1's
-  // arrive in registers (r, Un) meanwhile
-  mfma::f32x4 Ut[C / 16][NT], Un[C / 16][NT];
-  u32x4v r[kPer];
-  float gn = 1.f, gn_next = 1.f;
+  u32x4 R0[kPer], R1[kPer];
+  float G0 = 1.f, G1 = 1.f;  // Gamma_n of the chunk in stage buffer 0 / 1
   if (nfull > 0) {
-    fetch(0, r);
-    put(0, r);
-    load_u_tiles<DV, NT>(Ut, slot_of(0), DK, jb0, lane);
-    gn = a.gamn[(size_t)fbase * H + h];
+    fetch(0, R0);
+    put(0, R0);
+    G0 = gamn_of(0);
+  }
+  if (nfull > 1) {
+    fetch(1, R1);
+    G1 = gamn_of(1);
   }
   __syncthreads();
-  for (int c = 0; c < nfull; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nfull;
-    if (more) {
-      fetch(c + 1, r);
-      load_u_tiles<DV, NT>(Un, slot_of(c + 1), DK, jb0, lane);
-      gn_next = a.gamn[(size_t)(fbase + c + 1) * H + h];
+  // step c: chunk c is in stage buffer P = c & 1 and its registers RP are
+  // free; chunk c + 1 sits in the other registers RQ
+  auto step = [&](auto par, int c) {
+    constexpr int P = decltype(par)::value;
+    u32x4(&RP)[kPer] = P ? R1 : R0;
+    u32x4(&RQ)[kPer] = P ? R0 : R1;
+    float& GP = P ? G1 : G0;
+    float gnext = 1.f;
+    if (c + 2 < nfull) {
+      fetch(c + 2, RP);
+      gnext = gamn_of(c + 2);
     }
-    chain_step_bf16<DK, NT>(S, &st.W[buf][0][0], ChainStage<DK>::kW, &st.K[buf][0][0], ChainStage<DK>::kK, Ut, gn,
-                            lane);
+    const u32x4* st = stage[P];
+    f32x4 Ut[C / 16][NT];
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        Ut[tm][nt] = __builtin_bit_cast(f32x4, st[kFragPieces + ((wave * NT + nt) * (C / 16) + tm) * 64 + lane]);
+    chain_step_bf16<DK, NT>(
+        S, [&](int kb, int tm) { return st[(kb * (C / 16) + tm) * 64 + lane]; },
+        [&](int kb, int im) { return st[(int)(Sl::oKF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut, GP);
     if (c + 1 < nall) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb0, lane);
-    if (more) {
-      put(buf ^ 1, r);
-#pragma unroll
-      for (int tm = 0; tm < C / 16; ++tm)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) Ut[tm][nt] = Un[tm][nt];
-      gn = gn_next;
-    }
-    __syncthreads();
+    if (c + 1 < nfull) put(P ^ 1, RQ);
+    GP = gnext;
+    barrier();
+  };
+  int c = 0;
+  for (; c + 1 < nfull; c += 2) {
+    step(std::integral_constant<int, 0>{}, c);
+    step(std::integral_constant<int, 1>{}, c + 1);
   }
+  if (c < nfull) step(std::integral_constant<int, 0>{}, c);
   store_state_tiles<DK, DV, NT>(a.s_bnd + sh * SS, S, jb0, lane);
   if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + sh * SS, S, jb0, lane);
-  if (tid == 0) a.tail_len[sh] = L % C;
+  if (blockIdx.z == 0 && tid == 0) a.tail_len[sh] = L % C;
 }
+
+// decode resync, bf16 path: one wave per (sequence, head, 32 state columns),
+// operands straight from the decode workspace's product slot
+constexpr int kResyncNT = 2;
 
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
-  constexpr int NT = kChainNT;
+  constexpr int NT = kResyncNT;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
   const int jb0 = blockIdx.z * NT, lane = threadIdx.x;
@@ -1224,9 +1236,22 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   }
   mark(2, st);
   if (a.N > 0) {
-    if constexpr (kBf16)
-      hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV>), dim3(a.N, a.H), dim3(DV * 2), 0, st, a);
-    else
+    if constexpr (kBf16) {
+      // the fewer (sequence, head) pairs, the more work-groups per pair
+      const long pairs = (long)a.N * a.H;
+      bool done = false;
+      if constexpr (DV >= 128) {
+        if (pairs * (DV / 128) >= 128) {
+          hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 4, 2>), dim3(a.N, a.H, DV / 128), dim3(256), 0, st, a);
+          done = true;
+        }
+      }
+      if (done) {
+      } else if (pairs * (DV / 64) >= 96)
+        hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 4, 1>), dim3(a.N, a.H, DV / 64), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 2, 1>), dim3(a.N, a.H, DV / 32), dim3(128), 0, st, a);
+    } else
       hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
   }
   mark(3, st);
@@ -1243,7 +1268,7 @@ gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
   mark(1, st);
   if constexpr (std::is_same<D, Bf16>::value) {
     hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / 32), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / (16 * kResyncNT)), dim3(64), 0, st, a);
   } else {
     hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
     hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);

@@ -389,31 +389,39 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   f32x4 S[DK / 16][NT];
   load_state_tiles<DK, DV, NT>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb0, lane);
   if (nall > 0) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)abase * H + h) * SS, S, jb0, lane);
+  // Gamma_n travels with its chunk: every thread loads it, thread 0 stages it
+  __shared__ float gn_stage[2];
   u32x4 R0[kPer], R1[kPer];
-  float G0 = 1.f, G1 = 1.f;  // Gamma_n of the chunk in stage buffer 0 / 1
+  float G0 = 1.f, G1 = 1.f;
   if (nfull > 0) {
     fetch(0, R0);
-    put(0, R0);
     G0 = gamn_of(0);
-  }
-  if (nfull > 1) {
-    fetch(1, R1);
-    G1 = gamn_of(1);
+    put(0, R0);
+    if (tid == 0) gn_stage[0] = G0;
+    const int c1 = min(1, nfull - 1);
+    fetch(c1, R1);
+    G1 = gamn_of(c1);
   }
   __syncthreads();
-  // step c: chunk c is in stage buffer P = c & 1 and its registers RP are
-  // free; chunk c + 1 sits in the other registers RQ
-  auto step = [&](auto par, int c) {
+  // Step c: chunk c is in stage buffer P = c & 1; its registers RP are free
+  // and receive chunk c + 2 (clamped: the loads stay unconditional, so the
+  // compiler's wait counts cover exactly the loads a put needs); chunk c + 1
+  // sits in the other registers RQ and goes to the other buffer.  All steps
+  // but the last store their boundary unconditionally, for the same reason.
+  auto step = [&](auto par, auto is_last, int c) {
     constexpr int P = decltype(par)::value;
+    constexpr bool kLast = decltype(is_last)::value;
     u32x4(&RP)[kPer] = P ? R1 : R0;
     u32x4(&RQ)[kPer] = P ? R0 : R1;
     float& GP = P ? G1 : G0;
-    float gnext = 1.f;
-    if (c + 2 < nfull) {
-      fetch(c + 2, RP);
-      gnext = gamn_of(c + 2);
+    float& GQ = P ? G0 : G1;
+    if constexpr (!kLast) {
+      const int cf = min(c + 2, nfull - 1);
+      fetch(cf, RP);
+      GP = gamn_of(cf);
     }
     const u32x4* st = stage[P];
+    const float gn = gn_stage[P];
     f32x4 Ut[C / 16][NT];
 #pragma unroll
     for (int tm = 0; tm < C / 16; ++tm)
@@ -422,18 +430,32 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
         Ut[tm][nt] = __builtin_bit_cast(f32x4, st[kFragPieces + ((wave * NT + nt) * (C / 16) + tm) * 64 + lane]);
     chain_step_bf16<DK, NT>(
         S, [&](int kb, int tm) { return st[(kb * (C / 16) + tm) * 64 + lane]; },
-        [&](int kb, int im) { return st[(int)(Sl::oKF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut, GP);
-    if (c + 1 < nall) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, S, jb0, lane);
-    if (c + 1 < nfull) put(P ^ 1, RQ);
-    GP = gnext;
-    barrier();
+        [&](int kb, int im) { return st[(int)(Sl::oKF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut, gn);
+    float* bnd_next = a.bnd + ((size_t)(abase + c + 1) * H + h) * SS;
+    if constexpr (kLast) {
+      if (c + 1 < nall) store_bnd_tiles<DK, NT>(bnd_next, S, jb0, lane);
+    } else {
+      store_bnd_tiles<DK, NT>(bnd_next, S, jb0, lane);
+      put(P ^ 1, RQ);
+      if (tid == 0) gn_stage[P ^ 1] = GQ;
+      barrier();
+    }
   };
+  typedef std::integral_constant<int, 0> P0;
+  typedef std::integral_constant<int, 1> P1;
+  typedef std::integral_constant<bool, false> Mid;
+  typedef std::integral_constant<bool, true> Last;
   int c = 0;
-  for (; c + 1 < nfull; c += 2) {
-    step(std::integral_constant<int, 0>{}, c);
-    step(std::integral_constant<int, 1>{}, c + 1);
+  for (; c + 2 < nfull; c += 2) {
+    step(P0{}, Mid{}, c);
+    step(P1{}, Mid{}, c + 1);
   }
-  if (c < nfull) step(std::integral_constant<int, 0>{}, c);
+  if (c + 1 < nfull) {
+    step(P0{}, Mid{}, c);
+    step(P1{}, Last{}, c + 1);
+  } else if (c < nfull) {
+    step(P0{}, Last{}, c);
+  }
   store_state_tiles<DK, DV, NT>(a.s_bnd + sh * SS, S, jb0, lane);
   if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + sh * SS, S, jb0, lane);
   if (blockIdx.z == 0 && tid == 0) a.tail_len[sh] = L % C;

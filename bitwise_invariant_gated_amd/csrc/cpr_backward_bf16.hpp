@@ -1,0 +1,755 @@
+// Backward of the CPR Gated DeltaNet layer for bf16 inputs: per-chunk stages
+// with every operand staged in LDS or read as 16-byte lane vectors.
+//
+// The gradient is the one written out in cpr_backward.hpp (chunk / WY form,
+// exact in exact arithmetic).  For a chunk of n <= C tokens (padded to C with
+// k = q = v = dO = 0, g = beta = 0), start state B (d_k x d_v) and end-state
+// adjoint dB':
+//   local     (before the reverse chain)
+//     L = strict lower(beta_t D G), X = (I + L)^{-1}, P = (Q K^T) .* D
+//     W = X diag(beta Gamma) K,  Kt = diag(e) K
+//     Ddl = P^T dO,  R = (diag(Gamma) Q)^T dO - W^T Ddl
+//   reverse chain   dB = Gamma_n dB' + R + (-W^T) Kt dB'   (bf16 operands)
+//   state     (after it)
+//     Dd = Ddl + Kt dB',  Delta = X diag(beta) V - W B
+//     QB = dO B^T,  dWn = Dd B^T (= -dW),  dKt = Delta dB'^T,  dGamma_n = <dB', B>
+//   local gradients
+//     dPD = (dO Delta^T) .* D,  dQ = diag(Gamma) QB + dPD K
+//     dV = diag(beta) X^T Dd,  TW = T^T dW = -diag(beta) X^T dWn
+//     dT = Dd V^T - dWn (diag(Gamma) K)^T,  dX = dT diag(beta)
+//     dA = -X^T (dX X^T) (strict lower),  dG = dA .* beta_t D
+//     dK = dPD^T Q + (dG + dG^T) K + diag(e) dKt + diag(Gamma) TW
+//     dbeta = colsum(X .* dT) + rowsum(dA .* D .* G)
+//     dgamma = rowsum(Z) - colsum(Z) + (dGamma_out + dGamma_W) Gamma - de e
+//              (+ dGamma_n Gamma_n + sum(de e) at t = C - 1),
+//       Z = dPD .* QK + beta_t dA .* D .* G,  dGamma_out = <QB, Q> per row,
+//       dGamma_W = <TW, K> per row,  de = <dKt, K> per row
+//     dg = reverse cumsum of dgamma.
+// Products run on v_mfma_f32_16x16x4_f32 (fp32 operands; step m of a
+// 16-wide k block contracts index 4 g + m in lane group g) except G and
+// Q K^T (exact bf16 operands, v_mfma_f32_16x16x32_bf16) and the reverse
+// chain (bf16 operands, as the forward chain).  Every reduction has a fixed
+// order, so reruns give identical bits.
+#pragma once
+
+#include "cpr_backward.hpp"
+#include "cpr_device.hpp"
+
+namespace cpr {
+namespace bwdb {
+
+using namespace mfma;
+constexpr int C = kChunk;
+
+// Per (chunk slot, head) workspace.  TL = accumulator-tile order (element
+// (r, c) of a matrix with NR rows at (((c/16) (NR/16) + r/16) 64 + 16 ((r%16)/4)
+// + c%16) 4 + r%4); RM = row-major.
+template <int DK, int DV>
+struct Slot {
+  static constexpr size_t oKTF = 0;                                 // Kt fragments (chain phase 1)
+  static constexpr size_t oWNF = oKTF + (size_t)C * DK * 2;         // -W^T fragments (chain phase 2)
+  static constexpr size_t oR = oWNF + (size_t)DK * C * 2;           // R, TL (DK rows)
+  static constexpr size_t oDbp = oR + (size_t)DK * DV * 4;          // dB', TL (DK rows)
+  static constexpr size_t oX = oDbp + (size_t)DK * DV * 4;          // X, RM
+  static constexpr size_t oW = oX + (size_t)C * C * 4;              // W, RM
+  static constexpr size_t oDdl = oW + (size_t)C * DK * 4;           // Ddl, TL (C rows)
+  static constexpr size_t oDd = oDdl + (size_t)C * DV * 4;          // Dd, RM
+  static constexpr size_t oDe = oDd + (size_t)C * DV * 4;           // Delta, RM
+  static constexpr size_t oQB = oDe + (size_t)C * DV * 4;           // QB, RM
+  static constexpr size_t oDWn = oQB + (size_t)C * DK * 4;          // dWn, RM
+  static constexpr size_t oDKt = oDWn + (size_t)C * DK * 4;         // dKt, RM
+  static constexpr size_t oDGn = oDKt + (size_t)C * DK * 4;         // dGamma_n
+  static constexpr size_t bytes = oDGn + 256;
+};
+
+// ---------------------------------------------------------------------------
+// operand helpers (lane l = 16 g + c)
+
+__device__ __forceinline__ f32x4 mma16(const f32x4& a, const f32x4& b, f32x4 acc) {
+  acc = mma4(a[0], b[0], acc);
+  acc = mma4(a[1], b[1], acc);
+  acc = mma4(a[2], b[2], acc);
+  return mma4(a[3], b[3], acc);
+}
+
+__device__ __forceinline__ float bfv(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// M[r][k0 + 4 g + {0..3}] of a row-major bf16 matrix (8-byte aligned rows)
+__device__ __forceinline__ f32x4 row4_bf(const uint16_t* M, int ld, int r, int k0, int g) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(M + (size_t)r * ld + k0 + 4 * g);
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+               __uint_as_float(w[1] & 0xffff0000u)};
+}
+
+// M[k0 + 4 g + {0..3}][col] of a row-major bf16 matrix
+__device__ __forceinline__ f32x4 col4_bf(const uint16_t* M, int ld, int k0, int col, int g) {
+  const uint16_t* p = M + (size_t)(k0 + 4 * g) * ld + col;
+  return f32x4{bfv(p[0]), bfv(p[ld]), bfv(p[2 * ld]), bfv(p[3 * ld])};
+}
+
+// M[r][k0 + 4 g + {0..3}] of a row-major fp32 matrix (16-byte aligned rows)
+__device__ __forceinline__ f32x4 row4_f(const float* M, int ld, int r, int k0, int g) {
+  return *reinterpret_cast<const f32x4*>(M + (size_t)r * ld + k0 + 4 * g);
+}
+
+// M[k0 + 4 g + {0..3}][col] of a row-major fp32 matrix
+__device__ __forceinline__ f32x4 col4_f(const float* M, int ld, int k0, int col, int g) {
+  const float* p = M + (size_t)(k0 + 4 * g) * ld + col;
+  return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+
+// this lane's 16 bytes of TL tile (row block rb, column block cb) of a matrix with NR rows
+template <int NR>
+__device__ __forceinline__ f32x4 tl4(const float* T, int rb, int cb, int lane) {
+  return *reinterpret_cast<const f32x4*>(T + ((size_t)(cb * (NR / 16) + rb) * 64 + lane) * 4);
+}
+
+template <int NR>
+__device__ __forceinline__ void st_tl(float* T, int rb, int cb, const f32x4& acc, int lane) {
+  *reinterpret_cast<f32x4*>(T + ((size_t)(cb * (NR / 16) + rb) * 64 + lane) * 4) = acc;
+}
+
+// accumulator tile (rows r0 + 4 g + i, column c0 + c) into a row-major fp32 matrix
+__device__ __forceinline__ void st_rm(float* M, int ld, int r0, int c0, const f32x4& acc, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) M[(size_t)(r0 + 4 * g + i) * ld + c0 + c] = acc[i];
+}
+
+// sum over the 16 lanes of a lane group (result valid in lane c = 0 of each group)
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 8, 16);
+  x += __shfl_xor(x, 4, 16);
+  x += __shfl_xor(x, 2, 16);
+  x += __shfl_xor(x, 1, 16);
+  return x;
+}
+
+// rows t < n of a [T, H, D] bf16 tensor (row t at src + (row0 + t H) D) into
+// LDS; rows t >= n are zero
+template <int D, int LD>
+__device__ __forceinline__ void stage_rows(uint16_t (*dst)[LD], const uint16_t* __restrict__ src, size_t row0,
+                                           int H, int n) {
+  for (int idx = threadIdx.x; idx < C * D / 8; idx += blockDim.x) {
+    const int t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (t < n) w = *reinterpret_cast<const u32x4*>(src + (row0 + (size_t)t * H) * D + c8);
+    *reinterpret_cast<u32x4*>(&dst[t][c8]) = w;
+  }
+}
+
+// tiles on or below the diagonal of a C x C matrix: index q in [0, 10)
+__device__ __forceinline__ void lower_tile(int q, int& tm, int& tn) {
+  tm = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+  tn = q - tm * (tm + 1) / 2;
+}
+
+// ===========================================================================
+// local stage (256 threads): L, X, P, W, Kt and -W^T fragments, Ddl, R
+template <int DK, int DV>
+struct LocalLds {
+  static constexpr int kLK = DK + 8, kLV = DV + 8, kLA = C + 4;
+  uint16_t K[C][kLK];
+  uint16_t Q[C][kLK];
+  uint16_t dO[C][kLV];
+  float A[C][kLA];  // L, then X^T on and above the diagonal
+  float P[C][kLA];  // P[t][s]
+  float Ddl[C * DV];  // TL
+  bwd::ChunkScalars cs;
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t* q, const uint16_t* k,
+                                            const uint16_t* d_o, const uint16_t* gp, const uint16_t* bp,
+                                            size_t row0, int H, int n, uint8_t* __restrict__ slot,
+                                            float* __restrict__ gamn) {
+  typedef Slot<DK, DV> Sl;
+  typedef LocalLds<DK, DV> Lds;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  stage_rows<DK>(sm.K, k, row0, H, n);
+  stage_rows<DK>(sm.Q, q, row0, H, n);
+  stage_rows<DV>(sm.dO, d_o, row0, H, n);
+  bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
+  const bwd::ChunkScalars& cs = sm.cs;
+  // L (strictly lower) and P (lower, diagonal included) from the 10 lower tiles each
+  for (int q2 = wave; q2 < 20; q2 += 4) {
+    int tm, tn;
+    lower_tile(q2 % 10, tm, tn);
+    const bool isP = q2 >= 10;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      acc = mma(frag_row(isP ? &sm.Q[16 * tm + lr][0] : &sm.K[16 * tm + lr][0], 32 * kb, g),
+                frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
+      if (!isP) {
+        if (s < t) sm.A[t][s] = (cs.beta[t] * expf(cs.gam[t] - cs.gam[s])) * acc[r];
+      } else {
+        sm.P[t][s] = (s <= t) ? acc[r] * expf(cs.gam[t] - cs.gam[s]) : 0.f;
+      }
+    }
+  }
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, s = idx % C;
+    if ((s >> 4) > (t >> 4)) sm.P[t][s] = 0.f;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    inverse_diag_blocks(sm.A, lane);
+  } else {
+    // Kt fragments (chain phase 1, the slot's first 16 KB): fragment (kb, tm)
+    for (int f = wave - 1; f < (DK / 32) * (C / 16); f += 3) {
+      const int kb = f / (C / 16), tm = f % (C / 16), t = 16 * tm + lr;
+      const u32x4 raw = frag_row(&sm.K[t][0], 32 * kb, g);
+      const float et = cs.e[t];
+      u32x4 out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        out[w] = pack2(et * __uint_as_float(raw[w] << 16), et * __uint_as_float(raw[w] & 0xffff0000u));
+      *reinterpret_cast<u32x4*>(slot + Sl::oKTF + ((size_t)f * 64 + lane) * 16) = out;
+    }
+  }
+  __syncthreads();
+  inverse_below_diag(sm.A, wave, lane);
+  // W tiles (tm, it), it = wave + 4 p; X[t][s] = A[s][t] for s <= t
+  constexpr int NI = DK / 64, NJ = DV / 64;
+  f32x4 Wt[NI][C / 16];
+  float* Wg = reinterpret_cast<float*>(slot + Sl::oW);
+#pragma unroll
+  for (int p = 0; p < NI; ++p) {
+    const int it = wave + 4 * p;
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int t = 16 * tm + lr;
+      for (int sb = 0; sb <= tm; ++sb) {
+        f32x4 a;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int s = 16 * sb + 4 * g + m;
+          a[m] = (s <= t) ? sm.A[s][t] * (cs.beta[s] * cs.Gam[s]) : 0.f;
+        }
+        acc = mma16(a, col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, 16 * it + lr, g), acc);
+      }
+      Wt[p][tm] = acc;
+      st_rm(Wg, DK, 16 * tm, 16 * it, acc, lane);
+    }
+    // -W^T fragments (chain phase 2): fragment (kb, it)
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      const f32x4& x = Wt[p][2 * kb];
+      const f32x4& y = Wt[p][2 * kb + 1];
+      const u32x4 out = {pack2(-x[0], -x[1]), pack2(-x[2], -x[3]), pack2(-y[0], -y[1]), pack2(-y[2], -y[3])};
+      *reinterpret_cast<u32x4*>(slot + Sl::oWNF + ((size_t)(kb * (DK / 16) + it) * 64 + lane) * 16) = out;
+    }
+  }
+  // Ddl = P^T dO, tiles (sb, jt), jt = wave + 4 p; P[t][s] = 0 for t < s
+  float* Ddlg = reinterpret_cast<float*>(slot + Sl::oDdl);
+#pragma unroll
+  for (int p = 0; p < NJ; ++p) {
+    const int jt = wave + 4 * p;
+#pragma unroll
+    for (int sb = 0; sb < C / 16; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int tb = sb; tb < C / 16; ++tb) {
+        f32x4 a;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = sm.P[16 * tb + 4 * g + m][16 * sb + lr];
+        acc = mma16(a, col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g), acc);
+      }
+      st_tl<C>(sm.Ddl, sb, jt, acc, lane);
+      st_tl<C>(Ddlg, sb, jt, acc, lane);
+    }
+  }
+  __syncthreads();
+  // R = (diag(Gamma) Q)^T dO - W^T Ddl, tiles (it, jt) with this wave's it
+  float* Rg = reinterpret_cast<float*>(slot + Sl::oR);
+#pragma unroll
+  for (int p = 0; p < NI; ++p) {
+    const int it = wave + 4 * p;
+    for (int jt = 0; jt < DV / 16; ++jt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tb = 0; tb < C / 16; ++tb) {
+        f32x4 a = col4_bf(&sm.Q[0][0], Lds::kLK, 16 * tb, 16 * it + lr, g);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] *= cs.Gam[16 * tb + 4 * g + m];
+        acc = mma16(a, col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g), acc);
+      }
+#pragma unroll
+      for (int tb = 0; tb < C / 16; ++tb) {
+        const f32x4& w = Wt[p][tb];
+        acc = mma16(f32x4{-w[0], -w[1], -w[2], -w[3]}, tl4<C>(sm.Ddl, tb, jt, lane), acc);
+      }
+      st_tl<DK>(Rg, it, jt, acc, lane);
+    }
+  }
+  // X (row-major, zero above the diagonal) and Gamma_n
+  float* Xg = reinterpret_cast<float*>(slot + Sl::oX);
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, s = idx % C;
+    Xg[idx] = (s <= t) ? sm.A[s][t] : 0.f;
+  }
+  if (tid == 0) *gamn = cs.Gam[C - 1];
+}
+
+// ===========================================================================
+// state stage (256 threads): Dd, Delta, QB, dWn, dKt, dGamma_n
+template <int DK, int DV>
+struct StateLds {
+  static constexpr int kLK = DK + 8, kLV = DV + 8, kLX = C + 4, kLD = DV + 4, kLB = 32 + 4;
+  uint16_t K[C][kLK];
+  uint16_t V[C][kLV];
+  uint16_t dO[C][kLV];
+  float X[C][kLX];
+  float Dd[C][kLD];
+  float De[C][kLD];
+  float Bs[DK][kLB];  // 32 columns of B or dB', row-major
+  bwd::ChunkScalars cs;
+  float red[256];
+};
+
+// stage columns 32 jb .. 32 jb + 31 of a TL state (DK rows) into Bs
+template <int DK, int LB>
+__device__ __forceinline__ void stage_cols(float (*Bs)[LB], const float* __restrict__ T, int jb) {
+  for (int pc = threadIdx.x; pc < 2 * (DK / 16) * 64; pc += blockDim.x) {
+    const int tt = pc >> 6, l = pc & 63;
+    const int jt = 2 * jb + tt / (DK / 16), im = tt % (DK / 16);
+    const f32x4 v = tl4<DK>(T, im, jt, l);
+    const int c = l & 15, g = l >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Bs[16 * im + 4 * g + r][16 * (jt - 2 * jb) + c] = v[r];
+  }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t* k, const uint16_t* v,
+                                            const uint16_t* d_o, const uint16_t* gp, const uint16_t* bp,
+                                            size_t row0, int H, int n, const float* __restrict__ B,
+                                            uint8_t* __restrict__ slot) {
+  typedef Slot<DK, DV> Sl;
+  typedef StateLds<DK, DV> Lds;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  constexpr int NI = DK / 64, NJ = DV / 64;
+  const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
+  const float* Wg = reinterpret_cast<const float*>(slot + Sl::oW);
+  const float* Ddlg = reinterpret_cast<const float*>(slot + Sl::oDdl);
+  const float* dBp = reinterpret_cast<const float*>(slot + Sl::oDbp);
+  stage_rows<DK>(sm.K, k, row0, H, n);
+  stage_rows<DV>(sm.V, v, row0, H, n);
+  stage_rows<DV>(sm.dO, d_o, row0, H, n);
+  for (int idx = tid; idx < C * C / 4; idx += 256) {
+    const int t = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
+    *reinterpret_cast<f32x4*>(&sm.X[t][s4]) = *reinterpret_cast<const f32x4*>(Xg + (size_t)t * C + s4);
+  }
+  bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
+  const bwd::ChunkScalars& cs = sm.cs;
+  float* Ddg = reinterpret_cast<float*>(slot + Sl::oDd);
+  float* Deg = reinterpret_cast<float*>(slot + Sl::oDe);
+#pragma unroll
+  for (int p = 0; p < NJ; ++p) {
+    const int jt = wave + 4 * p;
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      const int t = 16 * tm + lr;
+      // Dd = Ddl + Kt dB'
+      f32x4 acc = tl4<C>(Ddlg, tm, jt, lane);
+      const float et = cs.e[t];
+      for (int ib = 0; ib < DK / 16; ++ib) {
+        f32x4 a = row4_bf(&sm.K[0][0], Lds::kLK, t, 16 * ib, g);
+        a = f32x4{et * a[0], et * a[1], et * a[2], et * a[3]};
+        acc = mma16(a, tl4<DK>(dBp, ib, jt, lane), acc);
+      }
+      st_rm(&sm.Dd[0][0], Lds::kLD, 16 * tm, 16 * jt, acc, lane);
+      st_rm(Ddg, DV, 16 * tm, 16 * jt, acc, lane);
+      // Delta = X diag(beta) V - W B
+      f32x4 de = {0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb <= tm; ++sb) {
+        f32x4 a = row4_f(&sm.X[0][0], Lds::kLX, t, 16 * sb, g);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] *= cs.beta[16 * sb + 4 * g + m];
+        de = mma16(a, col4_bf(&sm.V[0][0], Lds::kLV, 16 * sb, 16 * jt + lr, g), de);
+      }
+      for (int ib = 0; ib < DK / 16; ++ib) {
+        const f32x4 w = row4_f(Wg, DK, t, 16 * ib, g);
+        de = mma16(f32x4{-w[0], -w[1], -w[2], -w[3]}, tl4<DK>(B, ib, jt, lane), de);
+      }
+      st_rm(&sm.De[0][0], Lds::kLD, 16 * tm, 16 * jt, de, lane);
+      st_rm(Deg, DV, 16 * tm, 16 * jt, de, lane);
+    }
+  }
+  __syncthreads();
+  // QB = dO B^T and dWn = Dd B^T, then dKt = Delta dB'^T, 32 columns of B / dB' at a time
+  f32x4 QB[NI][C / 16], DW[NI][C / 16];
+#pragma unroll
+  for (int p = 0; p < NI; ++p)
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) QB[p][tm] = DW[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int jb = 0; jb < DV / 32; ++jb) {
+    stage_cols<DK>(sm.Bs, B, jb);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NI; ++p) {
+      const int it = wave + 4 * p;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const f32x4 b = row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g);
+#pragma unroll
+        for (int tm = 0; tm < C / 16; ++tm) {
+          QB[p][tm] = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 32 * jb + 16 * kk, g), b, QB[p][tm]);
+          DW[p][tm] = mma16(row4_f(&sm.Dd[0][0], Lds::kLD, 16 * tm + lr, 32 * jb + 16 * kk, g), b, DW[p][tm]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* QBg = reinterpret_cast<float*>(slot + Sl::oQB);
+  float* DWg = reinterpret_cast<float*>(slot + Sl::oDWn);
+#pragma unroll
+  for (int p = 0; p < NI; ++p)
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      st_rm(QBg, DK, 16 * tm, 16 * (wave + 4 * p), QB[p][tm], lane);
+      st_rm(DWg, DK, 16 * tm, 16 * (wave + 4 * p), DW[p][tm], lane);
+      QB[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};  // reused for dKt
+    }
+  for (int jb = 0; jb < DV / 32; ++jb) {
+    stage_cols<DK>(sm.Bs, dBp, jb);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NI; ++p) {
+      const int it = wave + 4 * p;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const f32x4 b = row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g);
+#pragma unroll
+        for (int tm = 0; tm < C / 16; ++tm)
+          QB[p][tm] = mma16(row4_f(&sm.De[0][0], Lds::kLD, 16 * tm + lr, 32 * jb + 16 * kk, g), b, QB[p][tm]);
+      }
+    }
+    __syncthreads();
+  }
+  float* KTg = reinterpret_cast<float*>(slot + Sl::oDKt);
+#pragma unroll
+  for (int p = 0; p < NI; ++p)
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) st_rm(KTg, DK, 16 * tm, 16 * (wave + 4 * p), QB[p][tm], lane);
+  // dGamma_n = <dB', B> (both in TL order), fixed order
+  {
+    float acc = 0.f;
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(B);
+    const f32x4* d4 = reinterpret_cast<const f32x4*>(dBp);
+    for (int idx = tid; idx < DK * DV / 4; idx += 256) {
+      const f32x4 x = b4[idx], y = d4[idx];
+      acc = __builtin_fmaf(x[0], y[0], acc);
+      acc = __builtin_fmaf(x[1], y[1], acc);
+      acc = __builtin_fmaf(x[2], y[2], acc);
+      acc = __builtin_fmaf(x[3], y[3], acc);
+    }
+    sm.red[tid] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.f;
+      for (int r = 0; r < 256; ++r) s += sm.red[r];
+      *reinterpret_cast<float*>(slot + Sl::oDGn) = s;
+    }
+  }
+}
+
+// ===========================================================================
+// local gradients (256 threads): dq, dk, dv, dg, dbeta of the chunk's tokens
+template <int DK, int DV>
+struct GradLds {
+  static constexpr int kLK = DK + 8, kLV = DV + 8, kLX = C + 4;
+  uint16_t K[C][kLK];
+  uint16_t Q[C][kLK];
+  uint16_t V[C][kLV];
+  uint16_t dO[C][kLV];
+  float X[C][kLX];
+  float dPD[C][kLX];
+  float M2[C][kLX];  // Z_P, then dT -> dX, then dA .* D
+  float M3[C][kLX];  // Y, then Z_A
+  bwd::ChunkScalars cs;
+  float pGO[C][DK / 16], pGW[C][DK / 16], pDE[C][DK / 16];  // per-row partial dot products
+  float rzP[C], czP[C], dbc[C], dbr[C], rzA[C], czA[C], dgo[C], de[C];
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* v, const uint16_t* d_o, const uint16_t* gp,
+                                           const uint16_t* bp, size_t row0, int H, int n,
+                                           const uint8_t* __restrict__ slot, uint16_t* __restrict__ dq,
+                                           uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dg,
+                                           float* __restrict__ dbeta) {
+  typedef Slot<DK, DV> Sl;
+  typedef GradLds<DK, DV> Lds;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  constexpr int NI = DK / 64, NJ = DV / 64;
+  const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
+  const float* Ddg = reinterpret_cast<const float*>(slot + Sl::oDd);
+  const float* Deg = reinterpret_cast<const float*>(slot + Sl::oDe);
+  const float* QBg = reinterpret_cast<const float*>(slot + Sl::oQB);
+  const float* DWg = reinterpret_cast<const float*>(slot + Sl::oDWn);
+  const float* KTg = reinterpret_cast<const float*>(slot + Sl::oDKt);
+  stage_rows<DK>(sm.K, k, row0, H, n);
+  stage_rows<DK>(sm.Q, q, row0, H, n);
+  stage_rows<DV>(sm.V, v, row0, H, n);
+  stage_rows<DV>(sm.dO, d_o, row0, H, n);
+  for (int idx = tid; idx < C * C / 4; idx += 256) {
+    const int t = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
+    *reinterpret_cast<f32x4*>(&sm.X[t][s4]) = *reinterpret_cast<const f32x4*>(Xg + (size_t)t * C + s4);
+  }
+  bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
+  const bwd::ChunkScalars& cs = sm.cs;
+
+  // dPD = (dO Delta^T) .* D (lower, diagonal included), Z_P = dPD .* QK^T
+  for (int q2 = wave; q2 < 10; q2 += 4) {
+    int tm, tn;
+    lower_tile(q2, tm, tn);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < DV / 16; ++jb)
+      acc = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 16 * jb, g), row4_f(Deg, DV, 16 * tn + lr, 16 * jb, g),
+                  acc);
+    f32x4 qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      qk = mma(frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), qk);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
+      const float dpd = (s <= t) ? acc[r] * expf(cs.gam[t] - cs.gam[s]) : 0.f;
+      sm.dPD[t][s] = dpd;
+      sm.M2[t][s] = dpd * qk[r];
+    }
+  }
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, s = idx % C;
+    if ((s >> 4) > (t >> 4)) sm.dPD[t][s] = sm.M2[t][s] = 0.f;
+  }
+  __syncthreads();
+  if (tid < C) {
+    float acc = 0.f;
+    for (int s = 0; s < C; ++s) acc += sm.M2[tid][s];
+    sm.rzP[tid] = acc;
+  } else if (tid < 2 * C) {
+    const int s = tid - C;
+    float acc = 0.f;
+    for (int t = 0; t < C; ++t) acc += sm.M2[t][s];
+    sm.czP[s] = acc;
+  }
+  // dQ = diag(Gamma) QB + dPD K;  <QB, Q> per row
+#pragma unroll
+  for (int p = 0; p < NI; ++p) {
+    const int it = wave + 4 * p;
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb <= tm; ++sb)
+        acc = mma16(row4_f(&sm.dPD[0][0], Lds::kLX, 16 * tm + lr, 16 * sb, g),
+                    col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, 16 * it + lr, g), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tm + 4 * g + r, i = 16 * it + lr;
+        const float qb = QBg[(size_t)t * DK + i];
+        const float part = sum16(qb * bfv(sm.Q[t][i]));
+        if (lr == 0) sm.pGO[t][it] = part;
+        if (t < n) Bf16::store(dq, (row0 + (size_t)t * H) * DK + i, __builtin_fmaf(cs.Gam[t], qb, acc[r]));
+      }
+    }
+  }
+  // dV = diag(beta) X^T Dd
+#pragma unroll
+  for (int p = 0; p < NJ; ++p) {
+    const int jt = wave + 4 * p;
+#pragma unroll
+    for (int sb = 0; sb < C / 16; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int tb = sb; tb < C / 16; ++tb)
+        acc = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), col4_f(Ddg, DV, 16 * tb, 16 * jt + lr, g),
+                    acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * sb + 4 * g + r;
+        if (s < n) Bf16::store(dv, (row0 + (size_t)s * H) * DV + 16 * jt + lr, cs.beta[s] * acc[r]);
+      }
+    }
+  }
+  // TW = T^T dW = -diag(beta) X^T dWn (kept for dK)
+  f32x4 TW[NI][C / 16];
+#pragma unroll
+  for (int p = 0; p < NI; ++p) {
+    const int it = wave + 4 * p;
+#pragma unroll
+    for (int sb = 0; sb < C / 16; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int tb = sb; tb < C / 16; ++tb)
+        acc = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), col4_f(DWg, DK, 16 * tb, 16 * it + lr, g),
+                    acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = -cs.beta[16 * sb + 4 * g + r] * acc[r];
+      TW[p][sb] = acc;
+    }
+  }
+  __syncthreads();  // Z_P sums done: M2 is free
+  // dT = Dd V^T - dWn (diag(Gamma) K)^T, all 16 tiles
+  for (int q2 = wave; q2 < 16; q2 += 4) {
+    const int tm = q2 >> 2, tn = q2 & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < DV / 16; ++jb)
+      acc = mma16(row4_f(Ddg, DV, 16 * tm + lr, 16 * jb, g), row4_bf(&sm.V[0][0], Lds::kLV, 16 * tn + lr, 16 * jb, g),
+                  acc);
+    const float gs = cs.Gam[16 * tn + lr];
+    for (int ib = 0; ib < DK / 16; ++ib) {
+      const f32x4 w = row4_f(DWg, DK, 16 * tm + lr, 16 * ib, g);
+      const f32x4 kk = row4_bf(&sm.K[0][0], Lds::kLK, 16 * tn + lr, 16 * ib, g);
+      acc = mma16(f32x4{-w[0], -w[1], -w[2], -w[3]}, f32x4{gs * kk[0], gs * kk[1], gs * kk[2], gs * kk[3]}, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.M2[16 * tm + 4 * g + r][16 * tn + lr] = acc[r];
+  }
+  __syncthreads();
+  if (tid < C) {  // dbeta, column part: sum_t X[t][s] dT[t][s]
+    float acc = 0.f;
+    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(sm.X[t][tid], sm.M2[t][tid], acc);
+    sm.dbc[tid] = acc;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * C; idx += 256) sm.M2[idx / C][idx % C] *= cs.beta[idx % C];  // dX
+  __syncthreads();
+  // Y = dX X^T -> M3
+  for (int q2 = wave; q2 < 16; q2 += 4) {
+    const int tm = q2 >> 2, tn = q2 & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb <= tn; ++rb)
+      acc = mma16(row4_f(&sm.M2[0][0], Lds::kLX, 16 * tm + lr, 16 * rb, g),
+                  row4_f(&sm.X[0][0], Lds::kLX, 16 * tn + lr, 16 * rb, g), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * tn + lr] = acc[r];
+  }
+  __syncthreads();
+  // dA = -X^T Y (strict lower); dA .* D -> M2, Z_A = beta_t dA .* D .* G -> M3 (after a barrier)
+  f32x4 ZA[3];
+#pragma unroll
+  for (int nz = 0; nz < 3; ++nz) {
+    const int q2 = wave + 4 * nz;
+    if (q2 >= 10) break;
+    int tm, tn;
+    lower_tile(q2, tm, tn);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = tm; rb < C / 16; ++rb)
+      acc = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * rb, 16 * tm + lr, g),
+                  col4_f(&sm.M3[0][0], Lds::kLX, 16 * rb, 16 * tn + lr, g), acc);
+    f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      gk = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), gk);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
+      float dad = 0.f, z = 0.f;
+      if (s < t) {
+        dad = -acc[r] * expf(cs.gam[t] - cs.gam[s]);
+        z = dad * gk[r];
+      }
+      sm.M2[t][s] = dad;
+      ZA[nz][r] = z;
+    }
+  }
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, s = idx % C;
+    if ((s >> 4) > (t >> 4)) sm.M2[t][s] = 0.f;
+  }
+  __syncthreads();  // Y no longer read
+#pragma unroll
+  for (int nz = 0; nz < 3; ++nz) {
+    const int q2 = wave + 4 * nz;
+    if (q2 >= 10) break;
+    int tm, tn;
+    lower_tile(q2, tm, tn);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * tn + lr] = ZA[nz][r];
+  }
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, s = idx % C;
+    if ((s >> 4) > (t >> 4)) sm.M3[t][s] = 0.f;
+  }
+  __syncthreads();
+  if (tid < C) {
+    float acc = 0.f;
+    for (int s = 0; s < C; ++s) acc += sm.M3[tid][s];
+    sm.dbr[tid] = acc;
+    sm.rzA[tid] = cs.beta[tid] * acc;
+  } else if (tid < 2 * C) {
+    const int s = tid - C;
+    float acc = 0.f;
+    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(cs.beta[t], sm.M3[t][s], acc);
+    sm.czA[s] = acc;
+  }
+  // dK = dPD^T Q + (dG + dG^T) K + diag(e) dKt + diag(Gamma) TW, dG = beta_t (dA .* D)
+#pragma unroll
+  for (int p = 0; p < NI; ++p) {
+    const int it = wave + 4 * p;
+#pragma unroll
+    for (int sb = 0; sb < C / 16; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int tb = sb; tb < C / 16; ++tb)
+        acc = mma16(col4_f(&sm.dPD[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g),
+                    col4_bf(&sm.Q[0][0], Lds::kLK, 16 * tb, 16 * it + lr, g), acc);
+      for (int tb = 0; tb < C / 16; ++tb) {
+        const f32x4 lo = row4_f(&sm.M2[0][0], Lds::kLX, 16 * sb + lr, 16 * tb, g);   // dA D [s][t]
+        const f32x4 hi = col4_f(&sm.M2[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g);  // dA D [t][s]
+        const float bs = cs.beta[16 * sb + lr];
+        f32x4 a;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = __builtin_fmaf(bs, lo[m], cs.beta[16 * tb + 4 * g + m] * hi[m]);
+        acc = mma16(a, col4_bf(&sm.K[0][0], Lds::kLK, 16 * tb, 16 * it + lr, g), acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * sb + 4 * g + r, i = 16 * it + lr;
+        const float kt = KTg[(size_t)s * DK + i];
+        const float ks = bfv(sm.K[s][i]);
+        const float tw = TW[p][sb][r];
+        const float pw = sum16(tw * ks), pe = sum16(kt * ks);
+        if (lr == 0) {
+          sm.pGW[s][it] = pw;
+          sm.pDE[s][it] = pe;
+        }
+        const float val = acc[r] + cs.e[s] * kt + cs.Gam[s] * tw;
+        if (s < n) Bf16::store(dk, (row0 + (size_t)s * H) * DK + i, val);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    float a = 0.f, b = 0.f, c = 0.f;
+    for (int it = 0; it < DK / 16; ++it) {
+      a += sm.pGO[tid][it];
+      b += sm.pGW[tid][it];
+      c += sm.pDE[tid][it];
+    }
+    sm.dgo[tid] = a + b;
+    sm.de[tid] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float dGn = *reinterpret_cast<const float*>(slot + Sl::oDGn);
+    float sum_de = 0.f;
+    for (int t = 0; t < C; ++t) sum_de = __builtin_fmaf(sm.de[t], cs.e[t], sum_de);
+    float acc = 0.f;
+    for (int t = C - 1; t >= 0; --t) {
+      float dgam = (sm.rzP[t] + sm.rzA[t]) - (sm.czP[t] + sm.czA[t]) + sm.dgo[t] * cs.Gam[t] - sm.de[t] * cs.e[t];
+      if (t == C - 1) dgam += dGn * cs.Gam[C - 1] + sum_de;
+      acc += dgam;
+      if (t < n) {
+        dg[row0 + (size_t)t * H] = acc;
+        dbeta[row0 + (size_t)t * H] = sm.dbc[t] + sm.dbr[t];
+      }
+    }
+  }
+}
+
+}  // namespace bwdb
+}  // namespace cpr

@@ -517,6 +517,58 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, const f32x4& c) {
 }
 }  // namespace mfma
 
+// X = (I + L)^{-1} for a strictly lower C x C matrix L, by 16 x 16 blocks.
+// A holds L below the diagonal (A[t][s] = L[t][s], s < t); the routines
+// write X^T into the diagonal and upper triangle (A[s][t] = X[t][s], s <= t,
+// the diagonal blocks' lower halves receiving X's zeros).
+//   diagonal blocks (inverse_diag_blocks, one wave, lane 16 B + s solves
+//   column s of block B): rows q ascending, acc = (q == s), then
+//   acc = fma(-L[q][r], X[r][s], acc) for r = 0 .. q-1 ascending;
+//   below the diagonal (inverse_below_diag, all 4 waves of the work-group,
+//   block rows B = 1, 2, 3 in turn, wave j < B makes block (B, j)):
+//   Y = sum_{k=j}^{B-1} L_Bk X_kj (k ascending), X_Bj = -X_BB Y
+//   (v_mfma_f32_16x16x4_f32; step m of a 16-wide block contracts index
+//   4 g + m in lane group g).
+template <int LDA>
+__device__ __forceinline__ void inverse_diag_blocks(float (*A)[LDA], int lane) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int o = 16 * (lane >> 4), s = lane & 15;
+  float x[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    float acc = (q == s) ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 0; r < q; ++r) acc = __builtin_fmaf(-A[o + q][o + r], x[r], acc);
+    x[q] = acc;  // exactly +0 for q < s
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    *reinterpret_cast<f4*>(&A[o + s][o + 4 * q4]) = f4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+}
+
+// Caller synchronised after inverse_diag_blocks; ends synchronised.
+template <int LDA>
+__device__ __forceinline__ void inverse_below_diag(float (*A)[LDA], int wave, int lane) {
+  using namespace mfma;
+  const int lr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int B = 1; B < kChunk / 16; ++B) {
+    if (wave < B) {
+      const int j = wave;
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = j; kk < B; ++kk)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          Y = mma4(A[16 * B + lr][16 * kk + 4 * g + m], A[16 * j + lr][16 * kk + 4 * g + m], Y);
+      f32x4 Xb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Xb = mma4(-A[16 * B + 4 * g + m][16 * B + lr], Y[m], Xb);
+      *reinterpret_cast<f32x4*>(&A[16 * j + lr][16 * B + 4 * g]) = Xb;
+    }
+    __syncthreads();
+  }
+}
+
 // Caller staged the chunk and synchronised; 256 threads.  Writes the slot
 // (SlotB layout) and *gamn.
 template <int DK, int DV>
@@ -557,20 +609,7 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
   }
   __syncthreads();
   if (wave == 0) {
-    // diagonal blocks, all four at once: lane 16 B + s solves column s of block B
-    const int B = lane >> 4, s = lane & 15, o = 16 * B;
-    float x[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      float acc = (q == s) ? 1.f : 0.f;
-#pragma unroll
-      for (int r = 0; r < q; ++r) acc = __builtin_fmaf(-sm.A[o + q][o + r], x[r], acc);
-      x[q] = acc;  // exactly +0 for q < s
-    }
-    // X[o + q][o + s] -> A[o + s][o + q] (the zeros land on L_BB, which is no longer read)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<f32x4*>(&sm.A[o + s][o + 4 * q4]) = f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+    inverse_diag_blocks(sm.A, lane);
   } else {
     // K~^T fragments meanwhile
     for (int f = wave - 1; f < (C / 32) * (DK / 16); f += 3) {
@@ -586,23 +625,7 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
     }
   }
   __syncthreads();
-  // blocks below the diagonal, one block row at a time
-#pragma unroll
-  for (int B = 1; B < C / 16; ++B) {
-    if (wave < B) {
-      const int j = wave;
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      for (int kk = j; kk < B; ++kk)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          Y = mma4(sm.A[16 * B + lr][16 * kk + 4 * g + m], sm.A[16 * j + lr][16 * kk + 4 * g + m], Y);
-      f32x4 Xb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) Xb = mma4(-sm.A[16 * B + 4 * g + m][16 * B + lr], Y[m], Xb);
-      *reinterpret_cast<f32x4*>(&sm.A[16 * j + lr][16 * B + 4 * g]) = Xb;
-    }
-    __syncthreads();
-  }
+  inverse_below_diag(sm.A, wave, lane);
   // T = X diag(beta) -> TB, TG
   for (int idx = tid; idx < C * C; idx += 256) {
     const int r = idx / C, t = idx % C;
@@ -668,9 +691,11 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
 // independent; each tile accumulates its k steps in ascending order from its
 // initial value, so the result depends neither on NT nor on where the
 // operands come from.
-template <int DK, int NT, class FW, class FK>
-__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], FW&& wf, FK&& kf,
-                                                const mfma::f32x4 (&Ut)[kChunk / 16][NT], float gn) {
+// The general form: init2(im, nt, S[im][nt]) gives phase 2's initial tile
+// (Gamma_n * S for the forward; the reverse chain adds its R term).
+template <int DK, int NT, class FW, class FK, class FI>
+__device__ __forceinline__ void chain_step_bf16_init(mfma::f32x4 (&S)[DK / 16][NT], FW&& wf, FK&& kf,
+                                                     const mfma::f32x4 (&Ut)[kChunk / 16][NT], FI&& init2) {
   using namespace mfma;
   constexpr int C = kChunk;
   u32x4 Wf[DK / 32][C / 16], Kf[C / 32][DK / 16];
@@ -706,14 +731,21 @@ __device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], F
 #pragma unroll
   for (int im = 0; im < DK / 16; ++im)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      S[im][nt] = f32x4{gn * S[im][nt][0], gn * S[im][nt][1], gn * S[im][nt][2], gn * S[im][nt][3]};
+    for (int nt = 0; nt < NT; ++nt) S[im][nt] = init2(im, nt, S[im][nt]);
 #pragma unroll
   for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
     for (int im = 0; im < DK / 16; ++im)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) S[im][nt] = mma(Kf[kb][im], Db[kb][nt], S[im][nt]);
+}
+
+template <int DK, int NT, class FW, class FK>
+__device__ __forceinline__ void chain_step_bf16(mfma::f32x4 (&S)[DK / 16][NT], FW&& wf, FK&& kf,
+                                                const mfma::f32x4 (&Ut)[kChunk / 16][NT], float gn) {
+  chain_step_bf16_init<DK, NT>(S, wf, kf, Ut, [gn](int, int, const mfma::f32x4& x) {
+    return mfma::f32x4{gn * x[0], gn * x[1], gn * x[2], gn * x[3]};
+  });
 }
 
 // One step straight from a global chunk-product slot (decode resync), for

@@ -29,6 +29,7 @@
 
 #include "../../include/gdn_cpr.h"
 #include "cpr_backward.hpp"
+#include "cpr_backward_bf16.hpp"
 #include "cpr_device.hpp"
 
 using namespace cpr;
@@ -726,61 +727,6 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
   if (tid == 0) a.gamn[(size_t)slot * H + h] = cs.Gam[C - 1];
 }
 
-// B2: reverse boundary chain per (sequence, head), one wave per 16 columns:
-//   dS <- Gamma_n dS + R - W^T (Kt dS), last chunk first, from dhT.
-// Stores, per chunk, dB' (the adjoint of the chunk's end state) and the full
-// dDelta = dDelta_local + Kt dB'.
-template <int DK, int DV>
-__global__ __launch_bounds__(DV * 4) void k_bwd_chain(const BwdArgs a) {
-  using namespace mfma;
-  typedef bwd::BwdSlot<DK, DV, 2> Slot;
-  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
-  const int tid = threadIdx.x, jb = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int L = a.cu[i + 1] - a.cu[i];
-  const int nall = (L + C - 1) / C;
-  const size_t sh = (size_t)i * H + h;
-  const size_t SS = (size_t)DK * DV;
-  const int abase = a.all_base[i];
-  f32x4 S1[DK / 16][1];
-  load_state_tiles<DK, DV, 1>(S1, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
-  f32x4(&S)[DK / 16] = *reinterpret_cast<f32x4(*)[DK / 16]>(&S1);
-  for (int c = nall - 1; c >= 0; --c) {
-    const size_t sl = (size_t)(abase + c) * H + h;
-    uint8_t* ws = a.ws + sl * Slot::bytes;
-    store_state_tiles<DK, DV, 1>(reinterpret_cast<float*>(ws + Slot::oDbp), S1, jb, lane);
-    const uint16_t* Kt = reinterpret_cast<const uint16_t*>(ws + Slot::oKt);
-    const uint16_t* WnT = reinterpret_cast<const uint16_t*>(ws + Slot::oWnT);
-    const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
-    float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
-    u32x4 Sb[DK / 32];
-#pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) Sb[kb] = frag_from_acc(S[2 * kb], S[2 * kb + 1]);
-    f32x4 E[C / 16];
-#pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) acc = mma(frag_row(Kt + (16 * tm + lr) * DK, 32 * kb, g), Sb[kb], acc);
-      E[tm] = acc;
-      f32x4* dd = reinterpret_cast<f32x4*>(Dd + ((size_t)(jb * (C / 16) + tm) * 64 + lane) * 4);
-      *dd = *dd + acc;
-    }
-    u32x4 Eb[C / 32];
-#pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb) Eb[kb] = frag_from_acc(E[2 * kb], E[2 * kb + 1]);
-    const float gn = a.gamn[sl];
-#pragma unroll
-    for (int im = 0; im < DK / 16; ++im) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(R + ((size_t)(jb * (DK / 16) + im) * 64 + lane) * 4);
-      f32x4 acc = {gn * S[im][0] + r[0], gn * S[im][1] + r[1], gn * S[im][2] + r[2], gn * S[im][3] + r[3]};
-#pragma unroll
-      for (int kb = 0; kb < C / 32; ++kb) acc = mma(frag_row(WnT + (16 * im + lr) * C, 32 * kb, g), Eb[kb], acc);
-      S[im] = acc;
-    }
-  }
-  if (a.dh0) store_state_tiles<DK, DV, 1>(a.dh0 + sh * SS, S1, jb, lane);
-}
-
 // B2 for fp32 inputs: the same reverse chain with fp32 operands on
 // v_mfma_f32_16x16x4_f32.  The k index of step m in a 16-row tile is
 // 16 tile + 4 g + m, so accumulator tiles (lane group g holds rows 4 g .. 4 g
@@ -1130,6 +1076,178 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// backward, bf16 path: local stage, reverse chain, state stage, gradients
+// (cpr_backward_bf16.hpp); one work-group per (chunk slot, head) except the chain
+
+struct SlotPos {
+  int n;        // real tokens of the chunk
+  size_t row0;  // row of its first token in [T, H, ...]
+  size_t sl;    // slot * H + h
+};
+
+__device__ __forceinline__ bool slot_pos(const BwdArgs& a, SlotPos& p) {
+  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
+  if (slot >= a.all_base[a.N]) return false;
+  const int i = find_seq(a.all_base, a.N, slot);
+  const int c = slot - a.all_base[i];
+  const int L = a.cu[i + 1] - a.cu[i];
+  p.n = min(C, L - c * C);
+  p.row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  p.sl = (size_t)slot * H + h;
+  return true;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_bwd_local_bf16(const BwdArgs a) {
+  typedef bwdb::Slot<DK, DV> Sl;
+  __shared__ bwdb::LocalLds<DK, DV> sm;
+  SlotPos p;
+  if (!slot_pos(a, p)) return;
+  bwdb::local_stage<DK, DV>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.d_o,
+                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.n, a.ws + p.sl * Sl::bytes,
+                            a.gamn + p.sl);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_bwd_state_bf16(const BwdArgs a) {
+  typedef bwdb::Slot<DK, DV> Sl;
+  __shared__ bwdb::StateLds<DK, DV> sm;
+  SlotPos p;
+  if (!slot_pos(a, p)) return;
+  bwdb::state_stage<DK, DV>(sm, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
+                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.n,
+                            a.bnd + p.sl * DK * DV, a.ws + p.sl * Sl::bytes);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_bwd_grads_bf16(const BwdArgs a) {
+  typedef bwdb::Slot<DK, DV> Sl;
+  __shared__ bwdb::GradLds<DK, DV> sm;
+  SlotPos p;
+  if (!slot_pos(a, p)) return;
+  bwdb::grad_stage<DK, DV>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.d_o, (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.n,
+                           a.ws + p.sl * Sl::bytes, (uint16_t*)a.dq, (uint16_t*)a.dk, (uint16_t*)a.dv, a.dg,
+                           a.dbeta);
+}
+
+// Reverse chain, bf16 path: the forward chain's structure run from the last
+// chunk to the first.  Per chunk (dS = adjoint of the chunk's end state):
+//   store dB' = dS;  E = Kt bf16(dS);  dS = fma(Gamma_n, dS, R) + (-W^T) bf16(E)
+// Work-groups own CB = WAVES * NT * 16 state columns; the chunk's Kt / -W^T
+// fragments and its R tiles for those columns go through a two-buffer LDS
+// stage with loads two chunks ahead.
+template <int DK, int DV, int WAVES, int NT>
+__global__ __launch_bounds__(WAVES * 64) void k_bwd_chain_bf16(const BwdArgs a) {
+  using namespace mfma;
+  typedef bwdb::Slot<DK, DV> Sl;
+  constexpr int kThreads = WAVES * 64;
+  constexpr int CB = WAVES * NT * 16;
+  constexpr int kFragPieces = (int)(Sl::oR / 16);
+  constexpr int kRPieces = DK * CB * 4 / 16;
+  constexpr int kPieces = kFragPieces + kRPieces;
+  constexpr int kPer = kPieces / kThreads;
+  constexpr int kPerFrag = kFragPieces / kThreads;
+  static_assert(kPieces % kThreads == 0 && kFragPieces % kThreads == 0, "staging split");
+  static_assert(DV % CB == 0, "column blocks tile d_v");
+  __shared__ u32x4 stage[2][kPieces];
+  __shared__ float gn_stage[2];
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int jbg = blockIdx.z * (CB / 16), jb0 = jbg + wave * NT;
+  const int H = a.H;
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int nall = (L + C - 1) / C;
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  const int abase = a.all_base[i];
+  // step u visits chunk nall - 1 - u
+  auto slot_of = [&](int u) { return a.ws + ((size_t)(abase + nall - 1 - u) * H + h) * Sl::bytes; };
+  auto gamn_of = [&](int u) { return a.gamn[(size_t)(abase + nall - 1 - u) * H + h]; };
+  auto fetch = [&](int u, u32x4 (&r)[kPer]) {
+    const uint8_t* s = slot_of(u);
+    const u32x4* f = reinterpret_cast<const u32x4*>(s);
+    const u32x4* rr = reinterpret_cast<const u32x4*>(s + Sl::oR) + (size_t)jbg * (DK / 16) * 64;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int p = tid + m * kThreads;
+      r[m] = m < kPerFrag ? f[p] : rr[p - kFragPieces];
+    }
+  };
+  auto put = [&](int buf, const u32x4 (&r)[kPer]) {
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) stage[buf][tid + m * kThreads] = r[m];
+  };
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  f32x4 S[DK / 16][NT];
+  load_state_tiles<DK, DV, NT>(S, a.d_hT ? a.d_hT + sh * SS : nullptr, jb0, lane);
+  u32x4 R0[kPer], R1[kPer];
+  float G0 = 1.f, G1 = 1.f;
+  if (nall > 0) {
+    fetch(0, R0);
+    G0 = gamn_of(0);
+    put(0, R0);
+    if (tid == 0) gn_stage[0] = G0;
+    const int u1 = min(1, nall - 1);
+    fetch(u1, R1);
+    G1 = gamn_of(u1);
+  }
+  __syncthreads();
+  auto step = [&](auto par, auto is_last, int u) {
+    constexpr int P = decltype(par)::value;
+    constexpr bool kLast = decltype(is_last)::value;
+    u32x4(&RP)[kPer] = P ? R1 : R0;
+    u32x4(&RQ)[kPer] = P ? R0 : R1;
+    float& GP = P ? G1 : G0;
+    float& GQ = P ? G0 : G1;
+    if constexpr (!kLast) {
+      const int uf = min(u + 2, nall - 1);
+      fetch(uf, RP);
+      GP = gamn_of(uf);
+    }
+    const u32x4* st = stage[P];
+    const float gn = gn_stage[P];
+    store_bnd_tiles<DK, NT>(reinterpret_cast<float*>(slot_of(u) + Sl::oDbp), S, jb0, lane);
+    f32x4 Ut[C / 16][NT];
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) Ut[tm][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    chain_step_bf16_init<DK, NT>(
+        S, [&](int kb, int tm) { return st[(kb * (C / 16) + tm) * 64 + lane]; },
+        [&](int kb, int im) { return st[(int)(Sl::oWNF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut,
+        [&](int im, int nt, const f32x4& x) {
+          const f32x4 r =
+              __builtin_bit_cast(f32x4, st[kFragPieces + ((wave * NT + nt) * (DK / 16) + im) * 64 + lane]);
+          return f32x4{__builtin_fmaf(gn, x[0], r[0]), __builtin_fmaf(gn, x[1], r[1]), __builtin_fmaf(gn, x[2], r[2]),
+                       __builtin_fmaf(gn, x[3], r[3])};
+        });
+    if constexpr (!kLast) {
+      put(P ^ 1, RQ);
+      if (tid == 0) gn_stage[P ^ 1] = GQ;
+      barrier();
+    }
+  };
+  typedef std::integral_constant<int, 0> P0;
+  typedef std::integral_constant<int, 1> P1;
+  typedef std::integral_constant<bool, false> Mid;
+  typedef std::integral_constant<bool, true> Last;
+  int u = 0;
+  for (; u + 2 < nall; u += 2) {
+    step(P0{}, Mid{}, u);
+    step(P1{}, Mid{}, u + 1);
+  }
+  if (u + 1 < nall) {
+    step(P0{}, Mid{}, u);
+    step(P1{}, Last{}, u + 1);
+  } else if (u < nall) {
+    step(P0{}, Last{}, u);
+  }
+  if (a.dh0) store_state_tiles<DK, DV, NT>(a.dh0 + sh * SS, S, jb0, lane);
+}
+
+// ---------------------------------------------------------------------------
 // host side
 
 thread_local std::string g_last_error;
@@ -1358,8 +1476,12 @@ FwdBwdLayout fwd_bwd_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   off = align_up(off + NH * 4);
   L.bgamn = off;
   off = align_up(off + Amax * H * 4);
-  L.slot = (size_t)C * DK * esz + DK * (size_t)C * esz + DK * DV * 4 + (size_t)C * DV * 4 + (size_t)C * C * 4 +
-           DK * DV * 4;
+  if (s.dtype == GDN_DTYPE_BF16)  // bwdb::Slot
+    L.slot = 2 * (size_t)C * DK * 2 + 2 * DK * DV * 4 + (size_t)C * C * 4 + 4 * (size_t)C * DK * 4 +
+             3 * (size_t)C * DV * 4 + 256;
+  else
+    L.slot = (size_t)C * DK * esz + DK * (size_t)C * esz + DK * DV * 4 + (size_t)C * DV * 4 + (size_t)C * C * 4 +
+             DK * DV * 4;
   L.bslots = off;
   off = align_up(off + Amax * H * L.slot);
   L.total = off;
@@ -1370,19 +1492,33 @@ template <class D, int DK, int DV>
 struct FwdBwdFn {
   static gdn_status run(const PrefillArgs& pa, const BwdArgs& ba, int64_t T, size_t slot_bytes, hipStream_t st,
                         const char* fn) {
-    typedef bwd::BwdSlot<DK, DV, sizeof(typename D::T)> Slot;
-    if (slot_bytes != Slot::bytes) return fail(GDN_ERR_HIP, "%s: internal slot size mismatch", fn);
+    constexpr bool kBf16 = std::is_same<D, Bf16>::value;
+    const size_t want = kBf16 ? bwdb::Slot<DK, DV>::bytes : bwd::BwdSlot<DK, DV, sizeof(typename D::T)>::bytes;
+    if (slot_bytes != want) return fail(GDN_ERR_HIP, "%s: internal slot size mismatch", fn);
     gdn_status r = run_prefill<D, DK, DV>(pa, T, st, fn);
     if (r != GDN_OK) return r;
     const int Amax = (int)(T / C) + pa.N;
-    if (T > 0) hipLaunchKernelGGL((k_bwd_local<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
-    if constexpr (std::is_same<D, Bf16>::value)
-      hipLaunchKernelGGL((k_bwd_chain<DK, DV>), dim3(pa.N, pa.H), dim3(DV * 4), 0, st, ba);
-    else
+    if constexpr (kBf16) {
+      if (T > 0) hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+      const long pairs = (long)pa.N * pa.H;
+      if (pairs * (DV / 64) >= 96)
+        hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 4, 1>), dim3(pa.N, pa.H, DV / 64), dim3(256), 0, st, ba);
+      else
+        hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 2, 1>), dim3(pa.N, pa.H, DV / 32), dim3(128), 0, st, ba);
+      mark(5, st);
+      if (T > 0) {
+        hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+        hipLaunchKernelGGL((k_bwd_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+      }
+      mark(6, st);
+    } else {
+      // fp32 inputs: local terms, reverse chain and gradients on fp32 operands
+      if (T > 0) hipLaunchKernelGGL((k_bwd_local<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
       hipLaunchKernelGGL((k_bwd_chain_f32<DK, DV>), dim3(pa.N, pa.H), dim3(DV * 4), 0, st, ba);
-    mark(5, st);
-    if (T > 0) hipLaunchKernelGGL((k_bwd_grads<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
-    mark(6, st);
+      mark(5, st);
+      if (T > 0) hipLaunchKernelGGL((k_bwd_grads<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+      mark(6, st);
+    }
     return launch_status(fn);
   }
 };

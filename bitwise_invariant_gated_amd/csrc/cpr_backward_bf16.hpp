@@ -11,7 +11,7 @@
 //     Ddl = P^T dO,  R = (diag(Gamma) Q)^T dO - W^T Ddl
 //   reverse chain   dB = Gamma_n dB' + R + (-W^T) Kt dB'   (bf16 operands)
 //   state     (after it)
-//     Dd = Ddl + Kt dB',  Delta = X diag(beta) V - W B
+//     Dd = Ddl + Kt dB',  Delta = X diag(beta) (V - diag(Gamma) K B)  (= X diag(beta) V - W B)
 //     QB = dO B^T,  dWn = Dd B^T (= -dW),  dKt = Delta dB'^T,  dGamma_n = <dB', B>
 //   local gradients
 //     dPD = (dO Delta^T) .* D,  dQ = diag(Gamma) QB + dPD K
@@ -51,8 +51,7 @@ struct Slot {
   static constexpr size_t oR = oWNF + (size_t)DK * C * 2;           // R, TL (DK rows)
   static constexpr size_t oDbp = oR + (size_t)DK * DV * 4;          // dB', TL (DK rows)
   static constexpr size_t oX = oDbp + (size_t)DK * DV * 4;          // X, RM
-  static constexpr size_t oW = oX + (size_t)C * C * 4;              // W, RM
-  static constexpr size_t oDdl = oW + (size_t)C * DK * 4;           // Ddl, TL (C rows)
+  static constexpr size_t oDdl = oX + (size_t)C * C * 4;            // Ddl, TL (C rows)
   static constexpr size_t oDd = oDdl + (size_t)C * DV * 4;          // Dd, RM
   static constexpr size_t oDe = oDd + (size_t)C * DV * 4;           // Delta, RM
   static constexpr size_t oQB = oDe + (size_t)C * DV * 4;           // QB, RM
@@ -213,28 +212,33 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
   }
   __syncthreads();
   inverse_below_diag(sm.A, wave, lane);
-  // W tiles (tm, it), it = wave + 4 p; X[t][s] = A[s][t] for s <= t
-  constexpr int NI = DK / 64, NJ = DV / 64;
-  f32x4 Wt[NI][C / 16];
-  float* Wg = reinterpret_cast<float*>(slot + Sl::oW);
+  // W tiles (tm, it), it = wave + 4 p; X[t][s] = A[s][t] for s <= t.  The
+  // K column block is shared by the four row tiles, whose accumulations
+  // interleave.
+  constexpr int NI = DK / 64, NJ = DV / 64, NB = C / 16;
+  f32x4 Wt[NI][NB];
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
     const int it = wave + 4 * p;
 #pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int t = 16 * tm + lr;
-      for (int sb = 0; sb <= tm; ++sb) {
+    for (int tm = 0; tm < NB; ++tm) Wt[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb) {
+      const f32x4 b = col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, 16 * it + lr, g);
+      f32x4 bg;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) bg[m] = cs.beta[16 * sb + 4 * g + m] * cs.Gam[16 * sb + 4 * g + m];
+#pragma unroll
+      for (int tm = sb; tm < NB; ++tm) {
+        const int t = 16 * tm + lr;
         f32x4 a;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int s = 16 * sb + 4 * g + m;
-          a[m] = (s <= t) ? sm.A[s][t] * (cs.beta[s] * cs.Gam[s]) : 0.f;
+          a[m] = (s <= t) ? sm.A[s][t] * bg[m] : 0.f;
         }
-        acc = mma16(a, col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, 16 * it + lr, g), acc);
+        Wt[p][tm] = mma16(a, b, Wt[p][tm]);
       }
-      Wt[p][tm] = acc;
-      st_rm(Wg, DK, 16 * tm, 16 * it, acc, lane);
     }
     // -W^T fragments (chain phase 2): fragment (kb, it)
 #pragma unroll
@@ -250,41 +254,51 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
     const int jt = wave + 4 * p;
+    f32x4 acc[NB];
 #pragma unroll
-    for (int sb = 0; sb < C / 16; ++sb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int tb = sb; tb < C / 16; ++tb) {
+    for (int sb = 0; sb < NB; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      const f32x4 b = col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g);
+#pragma unroll
+      for (int sb = 0; sb <= tb; ++sb) {
         f32x4 a;
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[m] = sm.P[16 * tb + 4 * g + m][16 * sb + lr];
-        acc = mma16(a, col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g), acc);
+        acc[sb] = mma16(a, b, acc[sb]);
       }
-      st_tl<C>(sm.Ddl, sb, jt, acc, lane);
-      st_tl<C>(Ddlg, sb, jt, acc, lane);
+    }
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb) {
+      st_tl<C>(sm.Ddl, sb, jt, acc[sb], lane);
+      st_tl<C>(Ddlg, sb, jt, acc[sb], lane);
     }
   }
   __syncthreads();
-  // R = (diag(Gamma) Q)^T dO - W^T Ddl, tiles (it, jt) with this wave's it
+  // R = (diag(Gamma) Q)^T dO - W^T Ddl, tiles (it, jt) with this wave's it;
+  // the eight column tiles accumulate together
   float* Rg = reinterpret_cast<float*>(slot + Sl::oR);
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
     const int it = wave + 4 * p;
-    for (int jt = 0; jt < DV / 16; ++jt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[DV / 16];
 #pragma unroll
-      for (int tb = 0; tb < C / 16; ++tb) {
-        f32x4 a = col4_bf(&sm.Q[0][0], Lds::kLK, 16 * tb, 16 * it + lr, g);
+    for (int jt = 0; jt < DV / 16; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] *= cs.Gam[16 * tb + 4 * g + m];
-        acc = mma16(a, col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g), acc);
+    for (int tb = 0; tb < NB; ++tb) {
+      f32x4 a = col4_bf(&sm.Q[0][0], Lds::kLK, 16 * tb, 16 * it + lr, g);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] *= cs.Gam[16 * tb + 4 * g + m];
+      const f32x4& w = Wt[p][tb];
+      const f32x4 wn = {-w[0], -w[1], -w[2], -w[3]};
+#pragma unroll
+      for (int jt = 0; jt < DV / 16; ++jt) {
+        acc[jt] = mma16(a, col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g), acc[jt]);
+        acc[jt] = mma16(wn, tl4<C>(sm.Ddl, tb, jt, lane), acc[jt]);
       }
-#pragma unroll
-      for (int tb = 0; tb < C / 16; ++tb) {
-        const f32x4& w = Wt[p][tb];
-        acc = mma16(f32x4{-w[0], -w[1], -w[2], -w[3]}, tl4<C>(sm.Ddl, tb, jt, lane), acc);
-      }
-      st_tl<DK>(Rg, it, jt, acc, lane);
     }
+#pragma unroll
+    for (int jt = 0; jt < DV / 16; ++jt) st_tl<DK>(Rg, it, jt, acc[jt], lane);
   }
   // X (row-major, zero above the diagonal) and Gamma_n
   float* Xg = reinterpret_cast<float*>(slot + Sl::oX);
@@ -334,7 +348,6 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   constexpr int NI = DK / 64, NJ = DV / 64;
   const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
-  const float* Wg = reinterpret_cast<const float*>(slot + Sl::oW);
   const float* Ddlg = reinterpret_cast<const float*>(slot + Sl::oDdl);
   const float* dBp = reinterpret_cast<const float*>(slot + Sl::oDbp);
   stage_rows<DK>(sm.K, k, row0, H, n);
@@ -348,36 +361,63 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
   const bwd::ChunkScalars& cs = sm.cs;
   float* Ddg = reinterpret_cast<float*>(slot + Sl::oDd);
   float* Deg = reinterpret_cast<float*>(slot + Sl::oDe);
+  constexpr int NB = C / 16;
+  // Column tile jt = wave + 4 p: the dB' and B tiles of the column block are
+  // loaded once; the four row tiles accumulate together.
+  //   Dd    = Ddl + Kt dB'
+  //   KB    = K B                                   (kept in registers)
+  //   Delta = X diag(beta) (V - diag(Gamma) KB)     (= X diag(beta) V - W B)
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
     const int jt = wave + 4 * p;
+    f32x4 bD[DK / 16], bB[DK / 16];
 #pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) {
-      const int t = 16 * tm + lr;
-      // Dd = Ddl + Kt dB'
-      f32x4 acc = tl4<C>(Ddlg, tm, jt, lane);
-      const float et = cs.e[t];
-      for (int ib = 0; ib < DK / 16; ++ib) {
-        f32x4 a = row4_bf(&sm.K[0][0], Lds::kLK, t, 16 * ib, g);
-        a = f32x4{et * a[0], et * a[1], et * a[2], et * a[3]};
-        acc = mma16(a, tl4<DK>(dBp, ib, jt, lane), acc);
+    for (int ib = 0; ib < DK / 16; ++ib) {
+      bD[ib] = tl4<DK>(dBp, ib, jt, lane);
+      bB[ib] = tl4<DK>(B, ib, jt, lane);
+    }
+    f32x4 dd[NB], kb[NB];
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) {
+      dd[tm] = tl4<C>(Ddlg, tm, jt, lane);
+      kb[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ib = 0; ib < DK / 16; ++ib)
+#pragma unroll
+      for (int tm = 0; tm < NB; ++tm) {
+        const f32x4 a = row4_bf(&sm.K[0][0], Lds::kLK, 16 * tm + lr, 16 * ib, g);
+        const float et = cs.e[16 * tm + lr];
+        dd[tm] = mma16(f32x4{et * a[0], et * a[1], et * a[2], et * a[3]}, bD[ib], dd[tm]);
+        kb[tm] = mma16(a, bB[ib], kb[tm]);
       }
-      st_rm(&sm.Dd[0][0], Lds::kLD, 16 * tm, 16 * jt, acc, lane);
-      st_rm(Ddg, DV, 16 * tm, 16 * jt, acc, lane);
-      // Delta = X diag(beta) V - W B
-      f32x4 de = {0.f, 0.f, 0.f, 0.f};
-      for (int sb = 0; sb <= tm; ++sb) {
-        f32x4 a = row4_f(&sm.X[0][0], Lds::kLX, t, 16 * sb, g);
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) {
+      st_rm(&sm.Dd[0][0], Lds::kLD, 16 * tm, 16 * jt, dd[tm], lane);
+      st_rm(Ddg, DV, 16 * tm, 16 * jt, dd[tm], lane);
+    }
+    f32x4 de[NB];
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) de[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb) {
+      // B operand: rows s = 16 sb + 4 g + m of V - diag(Gamma) KB, column 16 jt + c
+      const f32x4 v = col4_bf(&sm.V[0][0], Lds::kLV, 16 * sb, 16 * jt + lr, g);
+      f32x4 b;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) b[m] = __builtin_fmaf(-cs.Gam[16 * sb + 4 * g + m], kb[sb][m], v[m]);
+#pragma unroll
+      for (int tm = sb; tm < NB; ++tm) {
+        f32x4 a = row4_f(&sm.X[0][0], Lds::kLX, 16 * tm + lr, 16 * sb, g);
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[m] *= cs.beta[16 * sb + 4 * g + m];
-        de = mma16(a, col4_bf(&sm.V[0][0], Lds::kLV, 16 * sb, 16 * jt + lr, g), de);
+        de[tm] = mma16(a, b, de[tm]);
       }
-      for (int ib = 0; ib < DK / 16; ++ib) {
-        const f32x4 w = row4_f(Wg, DK, t, 16 * ib, g);
-        de = mma16(f32x4{-w[0], -w[1], -w[2], -w[3]}, tl4<DK>(B, ib, jt, lane), de);
-      }
-      st_rm(&sm.De[0][0], Lds::kLD, 16 * tm, 16 * jt, de, lane);
-      st_rm(Deg, DV, 16 * tm, 16 * jt, de, lane);
+    }
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) {
+      st_rm(&sm.De[0][0], Lds::kLD, 16 * tm, 16 * jt, de[tm], lane);
+      st_rm(Deg, DV, 16 * tm, 16 * jt, de[tm], lane);
     }
   }
   __syncthreads();
@@ -504,110 +544,155 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
   const bwd::ChunkScalars& cs = sm.cs;
 
-  // dPD = (dO Delta^T) .* D (lower, diagonal included), Z_P = dPD .* QK^T
-  for (int q2 = wave; q2 < 10; q2 += 4) {
-    int tm, tn;
-    lower_tile(q2, tm, tn);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NB = C / 16;
+  // dPD = (dO Delta^T) .* D (lower, diagonal included), Z_P = dPD .* QK^T;
+  // wave w makes the tiles of column block w (rows tm >= w)
+  {
+    const int tn = wave;
+    f32x4 bde[DV / 16];
+#pragma unroll
+    for (int jb = 0; jb < DV / 16; ++jb) bde[jb] = row4_f(Deg, DV, 16 * tn + lr, 16 * jb, g);
+    f32x4 acc[NB], qk[NB];
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) acc[tm] = qk[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int jb = 0; jb < DV / 16; ++jb)
-      acc = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 16 * jb, g), row4_f(Deg, DV, 16 * tn + lr, 16 * jb, g),
-                  acc);
-    f32x4 qk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      qk = mma(frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), qk);
+      for (int tm = 0; tm < NB; ++tm)
+        if (tm >= tn) acc[tm] = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 16 * jb, g), bde[jb], acc[tm]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
-      const float dpd = (s <= t) ? acc[r] * expf(cs.gam[t] - cs.gam[s]) : 0.f;
-      sm.dPD[t][s] = dpd;
-      sm.M2[t][s] = dpd * qk[r];
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const u32x4 kf = frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g);
+#pragma unroll
+      for (int tm = 0; tm < NB; ++tm)
+        if (tm >= tn) qk[tm] = mma(frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g), kf, qk[tm]);
     }
-  }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int t = idx / C, s = idx % C;
-    if ((s >> 4) > (t >> 4)) sm.dPD[t][s] = sm.M2[t][s] = 0.f;
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tm + 4 * g + r, s2 = 16 * tn + lr;
+        const float dpd = (tm >= tn && s2 <= t) ? acc[tm][r] * expf(cs.gam[t] - cs.gam[s2]) : 0.f;
+        sm.dPD[t][s2] = dpd;
+        sm.M2[t][s2] = dpd * qk[tm][r];
+      }
   }
   __syncthreads();
   if (tid < C) {
     float acc = 0.f;
-    for (int s = 0; s < C; ++s) acc += sm.M2[tid][s];
+    for (int s2 = 0; s2 < C; ++s2) acc += sm.M2[tid][s2];
     sm.rzP[tid] = acc;
   } else if (tid < 2 * C) {
-    const int s = tid - C;
+    const int s2 = tid - C;
     float acc = 0.f;
-    for (int t = 0; t < C; ++t) acc += sm.M2[t][s];
-    sm.czP[s] = acc;
+    for (int t = 0; t < C; ++t) acc += sm.M2[t][s2];
+    sm.czP[s2] = acc;
   }
   // dQ = diag(Gamma) QB + dPD K;  <QB, Q> per row
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
-    const int it = wave + 4 * p;
+    const int it = wave + 4 * p, i = 16 * it + lr;
+    float qb[NB][4];
 #pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int sb = 0; sb <= tm; ++sb)
-        acc = mma16(row4_f(&sm.dPD[0][0], Lds::kLX, 16 * tm + lr, 16 * sb, g),
-                    col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, 16 * it + lr, g), acc);
+    for (int tm = 0; tm < NB; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qb[tm][r] = QBg[(size_t)(16 * tm + 4 * g + r) * DK + i];
+    f32x4 acc[NB];
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) acc[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb) {
+      const f32x4 b = col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, i, g);
+#pragma unroll
+      for (int tm = sb; tm < NB; ++tm)
+        acc[tm] = mma16(row4_f(&sm.dPD[0][0], Lds::kLX, 16 * tm + lr, 16 * sb, g), b, acc[tm]);
+    }
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tm + 4 * g + r, i = 16 * it + lr;
-        const float qb = QBg[(size_t)t * DK + i];
-        const float part = sum16(qb * bfv(sm.Q[t][i]));
+        const int t = 16 * tm + 4 * g + r;
+        const float part = sum16(qb[tm][r] * bfv(sm.Q[t][i]));
         if (lr == 0) sm.pGO[t][it] = part;
-        if (t < n) Bf16::store(dq, (row0 + (size_t)t * H) * DK + i, __builtin_fmaf(cs.Gam[t], qb, acc[r]));
+        if (t < n) Bf16::store(dq, (row0 + (size_t)t * H) * DK + i, __builtin_fmaf(cs.Gam[t], qb[tm][r], acc[tm][r]));
       }
-    }
   }
   // dV = diag(beta) X^T Dd
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
     const int jt = wave + 4 * p;
+    f32x4 bd[NB], acc[NB];
 #pragma unroll
-    for (int sb = 0; sb < C / 16; ++sb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int tb = sb; tb < C / 16; ++tb)
-        acc = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), col4_f(Ddg, DV, 16 * tb, 16 * jt + lr, g),
-                    acc);
+    for (int tb = 0; tb < NB; ++tb) {
+      bd[tb] = col4_f(Ddg, DV, 16 * tb, 16 * jt + lr, g);
+      acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+      for (int sb = 0; sb <= tb; ++sb)
+        acc[sb] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), bd[tb], acc[sb]);
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = 16 * sb + 4 * g + r;
-        if (s < n) Bf16::store(dv, (row0 + (size_t)s * H) * DV + 16 * jt + lr, cs.beta[s] * acc[r]);
+        const int s2 = 16 * sb + 4 * g + r;
+        if (s2 < n) Bf16::store(dv, (row0 + (size_t)s2 * H) * DV + 16 * jt + lr, cs.beta[s2] * acc[sb][r]);
       }
-    }
   }
   // TW = T^T dW = -diag(beta) X^T dWn (kept for dK)
-  f32x4 TW[NI][C / 16];
+  f32x4 TW[NI][NB];
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
     const int it = wave + 4 * p;
+    f32x4 bw[NB];
 #pragma unroll
-    for (int sb = 0; sb < C / 16; ++sb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int tb = sb; tb < C / 16; ++tb)
-        acc = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), col4_f(DWg, DK, 16 * tb, 16 * it + lr, g),
-                    acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = -cs.beta[16 * sb + 4 * g + r] * acc[r];
-      TW[p][sb] = acc;
+    for (int tb = 0; tb < NB; ++tb) {
+      bw[tb] = col4_f(DWg, DK, 16 * tb, 16 * it + lr, g);
+      TW[p][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+      for (int sb = 0; sb <= tb; ++sb)
+        TW[p][sb] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), bw[tb], TW[p][sb]);
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) TW[p][sb][r] = -cs.beta[16 * sb + 4 * g + r] * TW[p][sb][r];
   }
   __syncthreads();  // Z_P sums done: M2 is free
-  // dT = Dd V^T - dWn (diag(Gamma) K)^T, all 16 tiles
-  for (int q2 = wave; q2 < 16; q2 += 4) {
-    const int tm = q2 >> 2, tn = q2 & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int jb = 0; jb < DV / 16; ++jb)
-      acc = mma16(row4_f(Ddg, DV, 16 * tm + lr, 16 * jb, g), row4_bf(&sm.V[0][0], Lds::kLV, 16 * tn + lr, 16 * jb, g),
-                  acc);
-    const float gs = cs.Gam[16 * tn + lr];
+  // dT = Dd V^T - dWn (diag(Gamma) K)^T; wave w makes row block w
+  {
+    const int tm = wave;
+    f32x4 ad[DV / 16], aw[DK / 16];
+#pragma unroll
+    for (int jb = 0; jb < DV / 16; ++jb) ad[jb] = row4_f(Ddg, DV, 16 * tm + lr, 16 * jb, g);
+#pragma unroll
     for (int ib = 0; ib < DK / 16; ++ib) {
       const f32x4 w = row4_f(DWg, DK, 16 * tm + lr, 16 * ib, g);
-      const f32x4 kk = row4_bf(&sm.K[0][0], Lds::kLK, 16 * tn + lr, 16 * ib, g);
-      acc = mma16(f32x4{-w[0], -w[1], -w[2], -w[3]}, f32x4{gs * kk[0], gs * kk[1], gs * kk[2], gs * kk[3]}, acc);
+      aw[ib] = f32x4{-w[0], -w[1], -w[2], -w[3]};
     }
+    f32x4 acc[NB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.M2[16 * tm + 4 * g + r][16 * tn + lr] = acc[r];
+    for (int tn = 0; tn < NB; ++tn) acc[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < DV / 16; ++jb)
+#pragma unroll
+      for (int tn = 0; tn < NB; ++tn)
+        acc[tn] = mma16(ad[jb], row4_bf(&sm.V[0][0], Lds::kLV, 16 * tn + lr, 16 * jb, g), acc[tn]);
+#pragma unroll
+    for (int ib = 0; ib < DK / 16; ++ib)
+#pragma unroll
+      for (int tn = 0; tn < NB; ++tn) {
+        const float gs = cs.Gam[16 * tn + lr];
+        const f32x4 kk = row4_bf(&sm.K[0][0], Lds::kLK, 16 * tn + lr, 16 * ib, g);
+        acc[tn] = mma16(aw[ib], f32x4{gs * kk[0], gs * kk[1], gs * kk[2], gs * kk[3]}, acc[tn]);
+      }
+#pragma unroll
+    for (int tn = 0; tn < NB; ++tn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.M2[16 * tm + 4 * g + r][16 * tn + lr] = acc[tn][r];
   }
   __syncthreads();
   if (tid < C) {  // dbeta, column part: sum_t X[t][s] dT[t][s]
@@ -618,109 +703,121 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   __syncthreads();
   for (int idx = tid; idx < C * C; idx += 256) sm.M2[idx / C][idx % C] *= cs.beta[idx % C];  // dX
   __syncthreads();
-  // Y = dX X^T -> M3
-  for (int q2 = wave; q2 < 16; q2 += 4) {
-    const int tm = q2 >> 2, tn = q2 & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int rb = 0; rb <= tn; ++rb)
-      acc = mma16(row4_f(&sm.M2[0][0], Lds::kLX, 16 * tm + lr, 16 * rb, g),
-                  row4_f(&sm.X[0][0], Lds::kLX, 16 * tn + lr, 16 * rb, g), acc);
+  // Y = dX X^T -> M3; wave w makes row block w
+  {
+    const int tm = wave;
+    f32x4 acc[NB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * tn + lr] = acc[r];
+    for (int tn = 0; tn < NB; ++tn) acc[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const f32x4 a = row4_f(&sm.M2[0][0], Lds::kLX, 16 * tm + lr, 16 * rb, g);
+#pragma unroll
+      for (int tn = rb; tn < NB; ++tn)
+        acc[tn] = mma16(a, row4_f(&sm.X[0][0], Lds::kLX, 16 * tn + lr, 16 * rb, g), acc[tn]);
+    }
+#pragma unroll
+    for (int tn = 0; tn < NB; ++tn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * tn + lr] = acc[tn][r];
   }
   __syncthreads();
-  // dA = -X^T Y (strict lower); dA .* D -> M2, Z_A = beta_t dA .* D .* G -> M3 (after a barrier)
-  f32x4 ZA[3];
+  // dA = -X^T Y (strict lower); dA .* D -> M2, Z_A = dA .* D .* G -> M3 after a
+  // barrier; wave w makes the tiles of column block w
+  f32x4 ZA[NB];
+  {
+    const int tn = wave;
+    f32x4 acc[NB], gk[NB];
 #pragma unroll
-  for (int nz = 0; nz < 3; ++nz) {
-    const int q2 = wave + 4 * nz;
-    if (q2 >= 10) break;
-    int tm, tn;
-    lower_tile(q2, tm, tn);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int rb = tm; rb < C / 16; ++rb)
-      acc = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * rb, 16 * tm + lr, g),
-                  col4_f(&sm.M3[0][0], Lds::kLX, 16 * rb, 16 * tn + lr, g), acc);
-    f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+    for (int tm = 0; tm < NB; ++tm) acc[tm] = gk[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      gk = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), gk);
+    for (int rb = 0; rb < NB; ++rb) {
+      const f32x4 b = col4_f(&sm.M3[0][0], Lds::kLX, 16 * rb, 16 * tn + lr, g);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
-      float dad = 0.f, z = 0.f;
-      if (s < t) {
-        dad = -acc[r] * expf(cs.gam[t] - cs.gam[s]);
-        z = dad * gk[r];
-      }
-      sm.M2[t][s] = dad;
-      ZA[nz][r] = z;
+      for (int tm = 0; tm <= rb; ++tm)
+        if (tm >= tn) acc[tm] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * rb, 16 * tm + lr, g), b, acc[tm]);
     }
-  }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int t = idx / C, s = idx % C;
-    if ((s >> 4) > (t >> 4)) sm.M2[t][s] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const u32x4 kf = frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g);
+#pragma unroll
+      for (int tm = 0; tm < NB; ++tm)
+        if (tm >= tn) gk[tm] = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), kf, gk[tm]);
+    }
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tm + 4 * g + r, s2 = 16 * tn + lr;
+        float dad = 0.f, z = 0.f;
+        if (tm >= tn && s2 < t) {
+          dad = -acc[tm][r] * expf(cs.gam[t] - cs.gam[s2]);
+          z = dad * gk[tm][r];
+        }
+        sm.M2[t][s2] = dad;
+        ZA[tm][r] = z;
+      }
   }
   __syncthreads();  // Y no longer read
 #pragma unroll
-  for (int nz = 0; nz < 3; ++nz) {
-    const int q2 = wave + 4 * nz;
-    if (q2 >= 10) break;
-    int tm, tn;
-    lower_tile(q2, tm, tn);
+  for (int tm = 0; tm < NB; ++tm)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * tn + lr] = ZA[nz][r];
-  }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int t = idx / C, s = idx % C;
-    if ((s >> 4) > (t >> 4)) sm.M3[t][s] = 0.f;
-  }
+    for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * wave + lr] = ZA[tm][r];
   __syncthreads();
   if (tid < C) {
     float acc = 0.f;
-    for (int s = 0; s < C; ++s) acc += sm.M3[tid][s];
+    for (int s2 = 0; s2 < C; ++s2) acc += sm.M3[tid][s2];
     sm.dbr[tid] = acc;
     sm.rzA[tid] = cs.beta[tid] * acc;
   } else if (tid < 2 * C) {
-    const int s = tid - C;
+    const int s2 = tid - C;
     float acc = 0.f;
-    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(cs.beta[t], sm.M3[t][s], acc);
-    sm.czA[s] = acc;
+    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(cs.beta[t], sm.M3[t][s2], acc);
+    sm.czA[s2] = acc;
   }
   // dK = dPD^T Q + (dG + dG^T) K + diag(e) dKt + diag(Gamma) TW, dG = beta_t (dA .* D)
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
-    const int it = wave + 4 * p;
+    const int it = wave + 4 * p, i = 16 * it + lr;
+    float kt[NB][4];
 #pragma unroll
-    for (int sb = 0; sb < C / 16; ++sb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int tb = sb; tb < C / 16; ++tb)
-        acc = mma16(col4_f(&sm.dPD[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g),
-                    col4_bf(&sm.Q[0][0], Lds::kLK, 16 * tb, 16 * it + lr, g), acc);
-      for (int tb = 0; tb < C / 16; ++tb) {
+    for (int sb = 0; sb < NB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kt[sb][r] = KTg[(size_t)(16 * sb + 4 * g + r) * DK + i];
+    f32x4 acc[NB];
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      const f32x4 bq = col4_bf(&sm.Q[0][0], Lds::kLK, 16 * tb, i, g);
+      const f32x4 bk = col4_bf(&sm.K[0][0], Lds::kLK, 16 * tb, i, g);
+#pragma unroll
+      for (int sb = 0; sb < NB; ++sb) {
+        if (sb <= tb) acc[sb] = mma16(col4_f(&sm.dPD[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), bq, acc[sb]);
         const f32x4 lo = row4_f(&sm.M2[0][0], Lds::kLX, 16 * sb + lr, 16 * tb, g);   // dA D [s][t]
         const f32x4 hi = col4_f(&sm.M2[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g);  // dA D [t][s]
         const float bs = cs.beta[16 * sb + lr];
         f32x4 a;
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[m] = __builtin_fmaf(bs, lo[m], cs.beta[16 * tb + 4 * g + m] * hi[m]);
-        acc = mma16(a, col4_bf(&sm.K[0][0], Lds::kLK, 16 * tb, 16 * it + lr, g), acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = 16 * sb + 4 * g + r, i = 16 * it + lr;
-        const float kt = KTg[(size_t)s * DK + i];
-        const float ks = bfv(sm.K[s][i]);
-        const float tw = TW[p][sb][r];
-        const float pw = sum16(tw * ks), pe = sum16(kt * ks);
-        if (lr == 0) {
-          sm.pGW[s][it] = pw;
-          sm.pDE[s][it] = pe;
-        }
-        const float val = acc[r] + cs.e[s] * kt + cs.Gam[s] * tw;
-        if (s < n) Bf16::store(dk, (row0 + (size_t)s * H) * DK + i, val);
+        acc[sb] = mma16(a, bk, acc[sb]);
       }
     }
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s2 = 16 * sb + 4 * g + r;
+        const float ks = bfv(sm.K[s2][i]);
+        const float tw = TW[p][sb][r];
+        const float pw = sum16(tw * ks), pe = sum16(kt[sb][r] * ks);
+        if (lr == 0) {
+          sm.pGW[s2][it] = pw;
+          sm.pDE[s2][it] = pe;
+        }
+        const float val = acc[sb][r] + cs.e[s2] * kt[sb][r] + cs.Gam[s2] * tw;
+        if (s2 < n) Bf16::store(dk, (row0 + (size_t)s2 * H) * DK + i, val);
+      }
   }
   __syncthreads();
   if (tid < C) {

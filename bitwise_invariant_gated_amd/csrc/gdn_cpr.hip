@@ -1477,7 +1477,7 @@ FwdBwdLayout fwd_bwd_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   L.bgamn = off;
   off = align_up(off + Amax * H * 4);
   if (s.dtype == GDN_DTYPE_BF16)  // bwdb::Slot
-    L.slot = 2 * (size_t)C * DK * 2 + 2 * DK * DV * 4 + (size_t)C * C * 4 + 4 * (size_t)C * DK * 4 +
+    L.slot = 2 * (size_t)C * DK * 2 + 2 * DK * DV * 4 + (size_t)C * C * 4 + 3 * (size_t)C * DK * 4 +
              3 * (size_t)C * DV * 4 + 256;
   else
     L.slot = (size_t)C * DK * esz + DK * (size_t)C * esz + DK * DV * 4 + (size_t)C * DV * 4 + (size_t)C * C * 4 +

@@ -115,12 +115,17 @@ __device__ __forceinline__ void st_rm(float* M, int ld, int r0, int c0, const f3
   for (int i = 0; i < 4; ++i) M[(size_t)(r0 + 4 * g + i) * ld + c0 + c] = acc[i];
 }
 
-// sum over the 16 lanes of a lane group (result valid in lane c = 0 of each group)
+// sum over the 16 lanes of a lane group by DPP row rotations (8, 4, 2, 1);
+// callers use the value in lane c = 0, whose addition order is fixed
+template <int R>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + R, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 8, 16);
-  x += __shfl_xor(x, 4, 16);
-  x += __shfl_xor(x, 2, 16);
-  x += __shfl_xor(x, 1, 16);
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
   return x;
 }
 

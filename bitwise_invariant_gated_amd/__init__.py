@@ -15,6 +15,13 @@ from .api import (  # noqa: F401
     gdn_cpr_last_error,
     gdn_cpr_numerics_id,
     gdn_cpr_prefill,
+    gdn_cpr_prefill_continue,
     gdn_cpr_workspace_size,
 )
-from ._lib import GDN_OP_DECODE, GDN_OP_FWD_BWD, GDN_OP_PREFILL, GdnError  # noqa: F401
+from ._lib import (  # noqa: F401
+    GDN_OP_DECODE,
+    GDN_OP_FWD_BWD,
+    GDN_OP_PREFILL,
+    GDN_OP_PREFILL_CONTINUE,
+    GdnError,
+)

@@ -24,12 +24,14 @@ GDN_DTYPE_BF16 = 1
 GDN_OP_PREFILL = 0
 GDN_OP_DECODE = 1
 GDN_OP_FWD_BWD = 2
+GDN_OP_PREFILL_CONTINUE = 3
 
 # every symbol the header declares
 EXPORTED = (
     "gdn_cpr_workspace_size",
     "gdn_cpr_prefill",
     "gdn_cpr_decode_step",
+    "gdn_cpr_prefill_continue",
     "gdn_cpr_fwd_bwd",
     "gdn_cpr_set_stage_events",
     "gdn_cpr_last_error",
@@ -83,6 +85,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_cpr_decode_step.restype = ctypes.c_int
     lib.gdn_cpr_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, _vp, _vp, _vp, _vp,
                                         _vp, ctypes.POINTER(Cache), _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdn_cpr_prefill_continue.restype = ctypes.c_int
+    lib.gdn_cpr_prefill_continue.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cache), _vp,
+                                             _vp, ctypes.c_size_t, _vp]
     lib.gdn_cpr_fwd_bwd.restype = ctypes.c_int
     lib.gdn_cpr_fwd_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -111,6 +111,18 @@ def gdn_cpr_decode_step(shape: LayerShape, q, k, v, g, beta, cache: CprCache, o,
                                        workspace.numel(), _stream(stream)))
 
 
+def gdn_cpr_prefill_continue(shape: LayerShape, q, k, v, g, beta, cu_seqlens, cache: CprCache, o,
+                             workspace: torch.Tensor, stream=None) -> None:
+    lib = _lib.load()
+    N = int(cu_seqlens.numel()) - 1
+    T = int(q.shape[0])
+    cc = cache.c()
+    _lib.check(lib.gdn_cpr_prefill_continue(ctypes.byref(shape.c()), N, T, _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(g), _ptr(beta), _ptr(cu_seqlens), ctypes.byref(cc),
+                                            _ptr(o), _ptr(workspace), workspace.numel(),
+                                            _stream(stream)))
+
+
 def gdn_cpr_fwd_bwd(shape: LayerShape, q, k, v, g, beta, cu_seqlens, h0, d_o, d_hT, o, hT, dq, dk,
                     dv, dg, dbeta, dh0, workspace: torch.Tensor, stream=None) -> None:
     lib = _lib.load()

@@ -48,7 +48,9 @@ struct PrefillArgs {
   const void* v;
   const void* g;
   const void* beta;
-  const int32_t* cu;
+  const int32_t* start;  // [N] first token row of each sequence
+  const int32_t* end;    // [N] one past its last token row (cu_seqlens + 1 for a plain prefill)
+  int32_t skip_empty;    // 1: a sequence with no tokens leaves its cache untouched
   const float* h0;
   float* s_bnd;
   float* s_run;
@@ -116,8 +118,8 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ base, int N,
 // ---------------------------------------------------------------------------
 // varlen plan: exclusive prefix sums of full and of all chunks per sequence
 
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ cu, int32_t N,
-                                               int32_t* __restrict__ full_base,
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start, const int32_t* __restrict__ end,
+                                               int32_t N, int32_t* __restrict__ full_base,
                                                int32_t* __restrict__ all_base) {
   __shared__ int32_t sf[1024];
   __shared__ int32_t sa[1024];
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ cu, i
     const int i = base + tid;
     int nf = 0, na = 0;
     if (i < N) {
-      const int L = cu[i + 1] - cu[i];
+      const int L = end[i] - start[i];
       nf = L / C;
       na = (L + C - 1) / C;
     }
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(256) void k_chunk_local_prefill(const PrefillArgs a
   if (f >= a.full_base[N]) return;
   const int i = find_seq(a.full_base, N, f);
   const int c = f - a.full_base[i];
-  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  const size_t tok0 = (size_t)a.start[i] + (size_t)c * C;
   const size_t row0 = tok0 * H + h;  // row index into [T, H, ...]
   stage_chunk<D, DK, DV>(sm, (const T*)a.k, row0, H, (const T*)a.v, row0, H, (const T*)a.g,
                          (const T*)a.beta, row0, H);
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) void k_chunk_local_prefill_bf16(const PrefillA
   if (f >= a.full_base[N]) return;
   const int i = find_seq(a.full_base, N, f);
   const int c = f - a.full_base[i];
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const size_t row0 = ((size_t)a.start[i] + (size_t)c * C) * H + h;
   stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, row0, H, (const uint16_t*)a.v, row0, H,
                            (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H);
   const size_t slot = (size_t)f * H + h;
@@ -303,7 +305,8 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
   __shared__ ChainLds<DK, NB> sm;
   const int i = blockIdx.x, h = blockIdx.y, col0 = blockIdx.z * NB;
   const int H = a.H;
-  const int L = a.cu[i + 1] - a.cu[i];
+  const int L = a.end[i] - a.start[i];
+  if (a.skip_empty && L == 0) return;
   const int nfull = L / C, nall = (L + C - 1) / C;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
@@ -363,7 +366,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int jbg = blockIdx.z * (CB / 16), jb0 = jbg + wave * NT;
   const int H = a.H;
-  const int L = a.cu[i + 1] - a.cu[i];
+  const int L = a.end[i] - a.start[i];
+  if (a.skip_empty && L == 0) return;
   const int nfull = L / C, nall = (L + C - 1) / C;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
@@ -491,9 +495,9 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   if (slot >= a.all_base[N]) return;
   const int i = find_seq(a.all_base, N, slot);
   const int c = slot - a.all_base[i];
-  const int L = a.cu[i + 1] - a.cu[i];
+  const int L = a.end[i] - a.start[i];
   const int n = min(C, L - c * C);
-  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  const size_t tok0 = (size_t)a.start[i] + (size_t)c * C;
   const int lane = threadIdx.x;
   const int col = blockIdx.z * kWave + lane;
   const size_t SS = (size_t)DK * DV;
@@ -600,6 +604,83 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   }
   if (col == 0) {
     a.tail_len[sh] = full ? 0 : tl + 1;
+    a.flag[sh] = full ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill continued from a cache: the head of each sequence (the tokens that
+// complete the cache's partial chunk) runs the decode step token by token;
+// the resynchronisation kernels then close that chunk, and the rest of the
+// sequence (which starts on a chunk boundary) goes through the prefill
+// kernels from the new boundary state.
+
+struct ContArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const int32_t* cu;
+  float* s_run;
+  void* tail_k;
+  void* tail_v;
+  void* tail_g;
+  void* tail_beta;
+  int32_t* tail_len;
+  void* o;
+  int32_t* flag;        // [N*H] 1 = this pair closes its chunk in the head
+  int32_t* body_start;  // [N] first token row after the head
+  int32_t N;
+  int32_t H;
+};
+
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
+  using T = typename D::T;
+  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
+  const size_t sh = (size_t)i * H + h;
+  const int col = threadIdx.x;
+  const size_t SS = (size_t)DK * DV;
+  const int tl = a.tail_len[sh];
+  __syncthreads();  // every wave has read tail_len before it is rewritten below
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int nh = ((unsigned)tl < (unsigned)C && tl > 0) ? min(C - tl, L) : 0;
+  if (h == 0 && col == 0) a.body_start[i] = a.cu[i] + nh;
+  if (col == 0) a.flag[sh] = 0;
+  if (nh == 0) return;
+  float* R = a.s_run + sh * SS;
+  float s[DK];
+#pragma unroll
+  for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const T* vp = (const T*)a.v;
+  const T* gp = (const T*)a.g;
+  const T* bp = (const T*)a.beta;
+  for (int t = 0; t < nh; ++t) {
+    const size_t row = (size_t)(a.cu[i] + t) * H + h;
+    const float alpha = decay_of(D::load(gp, row));
+    const float bt = D::load(bp, row);
+    const float vv = D::load(vp, row * DV + col);
+    const float out = token_step<D, DK>(s, (UniformRow)(kp + row * DK), (UniformRow)(qp + row * DK), alpha, bt, vv);
+    D::store((T*)a.o, row * DV + col, out);
+    const size_t tr = sh * C + tl + t;  // tail row
+    T* tk = (T*)a.tail_k + tr * DK;
+    for (int e = col; e < DK; e += DV) tk[e] = kp[row * DK + e];
+    ((T*)a.tail_v)[tr * DV + col] = vp[row * DV + col];
+    if (col == 0) {
+      ((T*)a.tail_g)[tr] = gp[row];
+      ((T*)a.tail_beta)[tr] = bp[row];
+    }
+  }
+  const bool full = (tl + nh == C);
+  if (!full) {
+#pragma unroll
+    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+  }
+  if (col == 0) {
+    a.tail_len[sh] = full ? 0 : tl + nh;
     a.flag[sh] = full ? 1 : 0;
   }
 }
@@ -1365,7 +1446,7 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   const int Fmax = (int)(T / C);
   const int Amax = Fmax + a.N;
   mark(0, st);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.cu, a.N, a.full_base, a.all_base);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.full_base, a.all_base);
   mark(1, st);
   constexpr bool kBf16 = std::is_same<D, Bf16>::value;
   if (Fmax > 0) {
@@ -1444,6 +1525,41 @@ template <class D, int DK, int DV>
 struct DecodeFn {
   static gdn_status run(const DecodeArgs& a, hipStream_t st, const char* fn) {
     return run_decode<D, DK, DV>(a, st, fn);
+  }
+};
+
+struct ContLayout {
+  PrefillLayout pre;
+  DecodeLayout dec;
+  size_t dec_off, body_start, total;
+};
+
+ContLayout cont_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
+  ContLayout L;
+  L.pre = prefill_layout(s, N, T);
+  L.dec = decode_layout(s, N);
+  L.dec_off = L.pre.total;
+  L.body_start = align_up(L.dec_off + L.dec.total);
+  L.total = align_up(L.body_start + sizeof(int32_t) * (size_t)N);
+  return L;
+}
+
+template <class D, int DK, int DV>
+struct ContFn {
+  static gdn_status run(const ContArgs& ca, const DecodeArgs& da, const PrefillArgs& pa, int64_t T, hipStream_t st,
+                        const char* fn) {
+    hipLaunchKernelGGL((k_cont_head<D, DK, DV>), dim3(ca.N, ca.H), dim3(DV), 0, st, ca);
+    if constexpr (std::is_same<D, Bf16>::value) {
+      hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
+      hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(da.N, da.H, DV / (16 * kResyncNT)), dim3(64), 0, st,
+                         da);
+    } else {
+      hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
+      hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(da.N, da.H, DV / kChainCols), dim3(256), 0, st, da);
+    }
+    gdn_status r = launch_status(fn);
+    if (r != GDN_OK) return r;
+    return run_prefill<D, DK, DV>(pa, T, st, fn);
   }
 };
 
@@ -1535,6 +1651,7 @@ extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num
   if (op == GDN_OP_PREFILL) return prefill_layout(*shape, num_seqs, total_tokens).total;
   if (op == GDN_OP_FWD_BWD) return fwd_bwd_layout(*shape, num_seqs, total_tokens).total;
   if (op == GDN_OP_DECODE) return decode_layout(*shape, num_seqs).total;
+  if (op == GDN_OP_PREFILL_CONTINUE) return cont_layout(*shape, num_seqs, total_tokens).total;
   return 0;
 }
 
@@ -1582,7 +1699,9 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.v = v;
   a.g = g;
   a.beta = beta;
-  a.cu = cu_seqlens;
+  a.start = cu_seqlens;
+  a.end = cu_seqlens + 1;
+  a.skip_empty = 0;
   a.h0 = h0;
   a.s_bnd = cache_out->s_bnd;
   a.s_run = cache_out->s_run;
@@ -1656,6 +1775,104 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   return dispatch<DecodeFn>(*shape, a, (hipStream_t)stream, fn);
 }
 
+extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                                               const void* q, const void* k, const void* v, const void* g,
+                                               const void* beta, const int32_t* cu_seqlens, const gdn_cpr_cache* cache,
+                                               void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_cpr_prefill_continue";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (total_tokens > (int64_t)INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+  if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  CHECK_PTR(cu_seqlens, "cu_seqlens");
+  CHECK_PTR(cache->s_bnd, "cache.s_bnd");
+  CHECK_PTR(cache->s_run, "cache.s_run");
+  CHECK_PTR(cache->tail_k, "cache.tail_k");
+  CHECK_PTR(cache->tail_v, "cache.tail_v");
+  CHECK_PTR(cache->tail_g, "cache.tail_g");
+  CHECK_PTR(cache->tail_beta, "cache.tail_beta");
+  CHECK_PTR(cache->tail_len, "cache.tail_len");
+  if (total_tokens > 0) {
+    CHECK_PTR(q, "q");
+    CHECK_PTR(k, "k");
+    CHECK_PTR(v, "v");
+    CHECK_PTR(g, "g");
+    CHECK_PTR(beta, "beta");
+    CHECK_PTR(o, "o");
+  }
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  const ContLayout L = cont_layout(*shape, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  char* ws = (char*)workspace;
+  char* wd = ws + L.dec_off;
+  int32_t* body_start = (int32_t*)(ws + L.body_start);
+  ContArgs ca;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.g = g;
+  ca.beta = beta;
+  ca.cu = cu_seqlens;
+  ca.s_run = cache->s_run;
+  ca.tail_k = cache->tail_k;
+  ca.tail_v = cache->tail_v;
+  ca.tail_g = cache->tail_g;
+  ca.tail_beta = cache->tail_beta;
+  ca.tail_len = cache->tail_len;
+  ca.o = o;
+  ca.flag = (int32_t*)(wd + L.dec.flag);
+  ca.body_start = body_start;
+  ca.N = num_seqs;
+  ca.H = shape->num_heads;
+  DecodeArgs da;
+  memset(&da, 0, sizeof(da));
+  da.s_bnd = cache->s_bnd;
+  da.s_run = cache->s_run;
+  da.tail_k = cache->tail_k;
+  da.tail_v = cache->tail_v;
+  da.tail_g = cache->tail_g;
+  da.tail_beta = cache->tail_beta;
+  da.tail_len = cache->tail_len;
+  da.flag = ca.flag;
+  da.prod = (uint8_t*)(wd + L.dec.prod);
+  da.gamn = (float*)(wd + L.dec.gamn);
+  da.N = num_seqs;
+  da.H = shape->num_heads;
+  PrefillArgs pa;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.g = g;
+  pa.beta = beta;
+  pa.start = body_start;
+  pa.end = cu_seqlens + 1;
+  pa.skip_empty = 1;
+  pa.h0 = cache->s_bnd;  // the boundary the body starts from (aliases the output, as allowed)
+  pa.s_bnd = cache->s_bnd;
+  pa.s_run = cache->s_run;
+  pa.tail_k = cache->tail_k;
+  pa.tail_v = cache->tail_v;
+  pa.tail_g = cache->tail_g;
+  pa.tail_beta = cache->tail_beta;
+  pa.tail_len = cache->tail_len;
+  pa.o = o;
+  pa.full_base = (int32_t*)(ws + L.pre.full_base);
+  pa.all_base = (int32_t*)(ws + L.pre.all_base);
+  pa.prod = (uint8_t*)(ws + L.pre.prod);
+  pa.gamn = (float*)(ws + L.pre.gamn);
+  pa.bnd = (float*)(ws + L.pre.bnd);
+  pa.N = num_seqs;
+  pa.H = shape->num_heads;
+  return dispatch<ContFn>(*shape, ca, da, pa, total_tokens, (hipStream_t)stream, fn);
+}
+
 extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                                       const void* q, const void* k, const void* v, const void* g,
                                       const void* beta, const int32_t* cu_seqlens, const float* h0,
@@ -1702,7 +1919,9 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.v = v;
   pa.g = g;
   pa.beta = beta;
-  pa.cu = cu_seqlens;
+  pa.start = cu_seqlens;
+  pa.end = cu_seqlens + 1;
+  pa.skip_empty = 0;
   pa.h0 = h0;
   pa.s_bnd = (float*)(ws + L.s_bnd);
   pa.s_run = hT ? hT : (float*)(ws + L.s_run);

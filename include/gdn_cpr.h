@@ -66,7 +66,12 @@ typedef enum {
 
 typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
 
-typedef enum { GDN_OP_PREFILL = 0, GDN_OP_DECODE = 1, GDN_OP_FWD_BWD = 2 } gdn_op;
+typedef enum {
+  GDN_OP_PREFILL = 0,
+  GDN_OP_DECODE = 1,
+  GDN_OP_FWD_BWD = 2,
+  GDN_OP_PREFILL_CONTINUE = 3
+} gdn_op;
 
 /* Layer shape (host struct). */
 typedef struct {
@@ -146,6 +151,35 @@ gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, con
                                const void* k, const void* v, const void* g, const void* beta,
                                const gdn_cpr_cache* cache, void* o, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill continued from a cache (serving: a further prompt segment, or
+ * several decode tokens at once, for sequences whose state is in `cache`).
+ * The pages state that the serving engine's scheduler, KV-cache management
+ * and graph capture keep working under the method (Chinese page, opening
+ * summary and the section on its two parts, the execution contract and the
+ * unified model); this call extends a cached sequence by any number of tokens
+ * with the bits that one prefill of the whole sequence (or decode token by
+ * token) would give, with no host synchronisation.
+ *   q, k, v, g, beta  the new tokens of the N sequences, packed, layouts
+ *                     above (T = total_tokens rows)
+ *   cu_seqlens        [N + 1] int32 over the new tokens
+ *   cache             read-modify-write in place; cache i continues with
+ *                     sequence i's new tokens
+ *   o                 [T, H, d_v] outputs of the new tokens
+ * Per sequence with tail_len = r and L new tokens: the first min(C - r, L)
+ * tokens (none when r = 0) take the decode step from s_run and join the
+ * tail; if they complete the chunk, s_bnd = s_run = the chunk-boundary
+ * computation over the C tail tokens.  The remaining tokens, which start on a
+ * chunk boundary, are prefilled from s_bnd.  L = 0 leaves the cache as it is.
+ * So gdn_cpr_prefill(A + B) equals gdn_cpr_prefill(A) followed by this call
+ * on B, bit for bit, and one token per sequence equals gdn_cpr_decode_step.
+ * Workspace: gdn_cpr_workspace_size(..., GDN_OP_PREFILL_CONTINUE).
+ */
+gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                                    const void* q, const void* k, const void* v, const void* g,
+                                    const void* beta, const int32_t* cu_seqlens, const gdn_cpr_cache* cache,
+                                    void* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Training forward + backward (the trainer_fwd case plus its gradient).

@@ -113,6 +113,24 @@ def test_decode_rejects_bad_arguments():
     assert dec(N=0) == _lib.GDN_OK
 
 
+def test_prefill_continue_rejects_bad_arguments():
+    lib = _lib_or_skip()
+    s = _shape()
+
+    def cont(shape=s, N=2, T=128, q=FAKE, cu=FAKE, ws=FAKE, ws_bytes=0, c=_cache()):
+        return lib.gdn_cpr_prefill_continue(ctypes.byref(shape), N, T, q, FAKE, FAKE, FAKE, FAKE, cu,
+                                            ctypes.byref(c), FAKE, ws, ws_bytes, None)
+
+    assert cont(shape=_shape(C=16)) == _lib.GDN_ERR_UNSUPPORTED
+    assert cont(cu=None) == _lib.GDN_ERR_INVALID_ARG
+    assert cont(q=FAKE + 2) == _lib.GDN_ERR_INVALID_ARG
+    assert cont(c=_cache(0)) == _lib.GDN_ERR_INVALID_ARG
+    need = lib.gdn_cpr_workspace_size(ctypes.byref(s), 2, 128, _lib.GDN_OP_PREFILL_CONTINUE)
+    assert need >= lib.gdn_cpr_workspace_size(ctypes.byref(s), 2, 128, _lib.GDN_OP_PREFILL)
+    assert cont(ws_bytes=need - 1) == _lib.GDN_ERR_WORKSPACE
+    assert cont(N=0, T=0) == _lib.GDN_OK
+
+
 def test_numerics_id_is_stable_text():
     lib = _lib_or_skip()
     a = lib.gdn_cpr_numerics_id()

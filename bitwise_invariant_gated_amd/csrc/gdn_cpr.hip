@@ -1970,9 +1970,13 @@ extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) 
 extern "C" const char* gdn_cpr_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" const char* gdn_cpr_numerics_id(void) {
-  return "gdn_cpr numerics v2: token step fp32 (decay mul; k and q dots as 2-way even/odd explicit-fma "
-         "chains; explicit-fma rank-1 update); fp32 inputs: chunk products and boundary chain fp32 VALU with "
-         "ascending explicit-fma sums; bf16 inputs: G, W, U and the boundary chain on "
-         "v_mfma_f32_16x16x32_bf16 with bf16 T, W, K~, S, Delta operands and fp32 accumulation, forward "
-         "substitution fp32 (ascending pivots); exp = ocml expf; bf16 outputs round-to-nearest-even; C = 64";
+  return "gdn_cpr numerics v3: token step fp32 (decay mul; k and q dots as 2-way even/odd explicit-fma "
+         "chains; explicit-fma rank-1 update); exp = ocml expf; gamma = left-to-right fp32 cumsum; "
+         "fp32 inputs: chunk products and boundary chain fp32 VALU with ascending explicit-fma sums and "
+         "column-wise forward substitution; bf16 inputs: G, W^T, U and the boundary chain on "
+         "v_mfma_f32_16x16x32_bf16 (k slots k0+4g+{0..3}, k0+16+4g+{0..3}; k steps ascending) with bf16 "
+         "T diag(Gamma), T, K~, S, Delta operands and fp32 accumulation; (I+L)^-1 by 16x16 blocks: "
+         "diagonal blocks by fp32 forward substitution (ascending pivots), blocks below by "
+         "v_mfma_f32_16x16x4_f32 (Y = sum_k L_Bk X_kj, k ascending; X_Bj = -X_BB Y); T = X diag(beta) "
+         "rounded once per product; bf16 outputs round-to-nearest-even; C = 64";
 }

@@ -58,6 +58,7 @@ class Cache(ctypes.Structure):
         ("tail_g", ctypes.c_void_p),
         ("tail_beta", ctypes.c_void_p),
         ("tail_len", ctypes.c_void_p),
+        ("slot_index", ctypes.c_void_p),
     ]
 
 

@@ -35,7 +35,8 @@ class LayerShape:
 
 @dataclasses.dataclass
 class CprCache:
-    """Device tensors of a gdn_cpr_cache (layouts in gdn_cpr.h)."""
+    """Device tensors of a gdn_cpr_cache (layouts in gdn_cpr.h).  slot_index
+    (int32 [N] or None) selects the cache rows of a call's batch entries."""
 
     s_bnd: torch.Tensor
     s_run: torch.Tensor
@@ -44,16 +45,21 @@ class CprCache:
     tail_g: torch.Tensor
     tail_beta: torch.Tensor
     tail_len: torch.Tensor
+    slot_index: Optional[torch.Tensor] = None
 
     def c(self) -> _lib.Cache:
-        return _lib.Cache(*(t.data_ptr() for t in (self.s_bnd, self.s_run, self.tail_k, self.tail_v,
-                                                   self.tail_g, self.tail_beta, self.tail_len)))
+        si = None if self.slot_index is None else _ptr(self.slot_index)
+        return _lib.Cache(*(t.data_ptr() for t in self.tensors()), si)
 
     def clone(self) -> "CprCache":
-        return CprCache(*(t.clone() for t in dataclasses.astuple(self)))
+        return CprCache(*(t.clone() for t in self.tensors()), self.slot_index)
+
+    def with_slots(self, slot_index: Optional[torch.Tensor]) -> "CprCache":
+        """The same cache arrays addressed through another row map."""
+        return CprCache(*self.tensors(), slot_index)
 
     def tensors(self):
-        return dataclasses.astuple(self)
+        return (self.s_bnd, self.s_run, self.tail_k, self.tail_v, self.tail_g, self.tail_beta, self.tail_len)
 
 
 def alloc_cache(shape: LayerShape, num_seqs: int, device="cuda") -> CprCache:

@@ -51,6 +51,8 @@ struct PrefillArgs {
   const int32_t* start;  // [N] first token row of each sequence
   const int32_t* end;    // [N] one past its last token row (cu_seqlens + 1 for a plain prefill)
   int32_t skip_empty;    // 1: a sequence with no tokens leaves its cache untouched
+  const int32_t* slot;   // [N] cache row of sequence i, or null (row i)
+  int32_t h0_slotted;    // 1: h0 is indexed by cache row (h0 = the cache's s_bnd)
   const float* h0;
   float* s_bnd;
   float* s_run;
@@ -70,6 +72,7 @@ struct PrefillArgs {
 };
 
 struct DecodeArgs {
+  const int32_t* slot;  // [N] cache row of sequence i, or null (row i)
   const void* q;
   const void* k;
   const void* v;
@@ -113,6 +116,11 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ base, int N,
       hi = mid;
   }
   return lo;
+}
+
+// cache row of batch entry i (slot-indexed caches)
+__device__ __forceinline__ size_t cache_row(const int32_t* __restrict__ slot, int i) {
+  return slot ? (size_t)slot[i] : (size_t)i;
 }
 
 // ---------------------------------------------------------------------------
@@ -220,9 +228,10 @@ __global__ __launch_bounds__(256) void k_chunk_local_resync(const DecodeArgs a) 
   __shared__ ChunkLds<DK, DV> sm;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
   // tail rows of this (sequence, head): [C, DK], [C, DV], [C]
-  stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, sh * C, 1, (const T*)a.tail_v, sh * C, 1,
-                         (const T*)a.tail_g, (const T*)a.tail_beta, sh * C, 1);
+  stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, ch * C, 1, (const T*)a.tail_v, ch * C, 1,
+                         (const T*)a.tail_g, (const T*)a.tail_beta, ch * C, 1);
   float* P = (float*)(a.prod + sh * prod_slot_bytes(false, DK, DV));
   chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + sh);
 }
@@ -248,8 +257,9 @@ __global__ __launch_bounds__(256) void k_chunk_local_resync_bf16(const DecodeArg
   __shared__ ChunkLdsB<DK, DV> sm;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
-  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, sh * C, 1, (const uint16_t*)a.tail_v, sh * C, 1,
-                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, sh * C, 1);
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, ch * C, 1, (const uint16_t*)a.tail_v, ch * C, 1,
+                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, ch * C, 1);
   chunk_local_bf16<DK, DV>(sm, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn + sh);
 }
 
@@ -310,7 +320,8 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
   const int nfull = L / C, nall = (L + C - 1) / C;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
-  get_block<DK, DV, NB>(sm, a.h0 ? a.h0 + sh * SS : nullptr, col0);
+  const size_t ch = cache_row(a.slot, i) * H + h;
+  get_block<DK, DV, NB>(sm, a.h0 ? a.h0 + (a.h0_slotted ? ch : sh) * SS : nullptr, col0);
   const int abase = a.all_base[i], fbase = a.full_base[i];
   if (nall > 0) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)abase * H + h) * SS, sm, col0);
   for (int c = 0; c < nfull; ++c) {
@@ -320,9 +331,9 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
     chain_step_f32<DK, NB>(sm);
     if (c + 1 < nall) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
   }
-  put_block<DK, DV, NB>(a.s_bnd + sh * SS, sm, col0);
-  if (L % C == 0) put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
-  if (blockIdx.z == 0 && threadIdx.x == 0) a.tail_len[sh] = L % C;
+  put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
+  if (L % C == 0) put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
+  if (blockIdx.z == 0 && threadIdx.x == 0) a.tail_len[ch] = L % C;
 }
 
 template <int DK, int DV>
@@ -333,11 +344,12 @@ __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   if (a.flag[sh] == 0) return;
   const int col0 = blockIdx.z * NB;
   const size_t SS = (size_t)DK * DV;
-  get_block<DK, DV, NB>(sm, a.s_bnd + sh * SS, col0);
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  get_block<DK, DV, NB>(sm, a.s_bnd + ch * SS, col0);
   stage_products<DK, DV, NB>(sm, (const float*)(a.prod + sh * prod_slot_bytes(false, DK, DV)), a.gamn + sh, col0);
   chain_step_f32<DK, NB>(sm);
-  put_block<DK, DV, NB>(a.s_bnd + sh * SS, sm, col0);
-  put_block<DK, DV, NB>(a.s_run + sh * SS, sm, col0);
+  put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
+  put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
 }
 
 // bf16 path: one work-group per (sequence, head, block of CB = WAVES * NT * 16
@@ -392,7 +404,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   f32x4 S[DK / 16][NT];
-  load_state_tiles<DK, DV, NT>(S, a.h0 ? a.h0 + sh * SS : nullptr, jb0, lane);
+  const size_t ch = cache_row(a.slot, i) * H + h;
+  load_state_tiles<DK, DV, NT>(S, a.h0 ? a.h0 + (a.h0_slotted ? ch : sh) * SS : nullptr, jb0, lane);
   if (nall > 0) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)abase * H + h) * SS, S, jb0, lane);
   // Gamma_n travels with its chunk: every thread loads it, thread 0 stages it
   __shared__ float gn_stage[2];
@@ -461,9 +474,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   } else if (c < nfull) {
     step(P0{}, Last{}, c);
   }
-  store_state_tiles<DK, DV, NT>(a.s_bnd + sh * SS, S, jb0, lane);
-  if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + sh * SS, S, jb0, lane);
-  if (blockIdx.z == 0 && tid == 0) a.tail_len[sh] = L % C;
+  store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
+  if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
+  if (blockIdx.z == 0 && tid == 0) a.tail_len[ch] = L % C;
 }
 
 // decode resync, bf16 path: one wave per (sequence, head, 32 state columns),
@@ -478,10 +491,11 @@ __global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
   const int jb0 = blockIdx.z * NT, lane = threadIdx.x;
   const size_t SS = (size_t)DK * DV;
   mfma::f32x4 S[DK / 16][NT];
-  load_state_tiles<DK, DV, NT>(S, a.s_bnd + sh * SS, jb0, lane);
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * SS, jb0, lane);
   chain_step_bf16_global<DK, DV, NT>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb0, lane);
-  store_state_tiles<DK, DV, NT>(a.s_bnd + sh * SS, S, jb0, lane);
-  store_state_tiles<DK, DV, NT>(a.s_run + sh * SS, S, jb0, lane);
+  store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
+  store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,21 +560,21 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   const int nall = (L + C - 1) / C;
   if (c == nall - 1 && (L % C) != 0) {
     // last, partial chunk: its end state is the running state, its tokens the tail
-    const size_t sh = (size_t)i * H + h;
-    float* R = a.s_run + sh * SS;
+    const size_t ch = cache_row(a.slot, i) * H + h;
+    float* R = a.s_run + ch * SS;
 #pragma unroll
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
-    T* tv = (T*)a.tail_v + sh * C * DV;
+    T* tv = (T*)a.tail_v + ch * C * DV;
     for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
     if (blockIdx.z == 0) {
-      T* tk = (T*)a.tail_k + sh * C * DK;
+      T* tk = (T*)a.tail_k + ch * C * DK;
       for (int idx = lane; idx < n * DK; idx += kWave) {
         const int t = idx / DK, e = idx % DK;
         tk[idx] = kp[((tok0 + t) * H + h) * DK + e];
       }
       if (lane < n) {
-        ((T*)a.tail_g)[sh * C + lane] = gp[(tok0 + lane) * H + h];
-        ((T*)a.tail_beta)[sh * C + lane] = bp[(tok0 + lane) * H + h];
+        ((T*)a.tail_g)[ch * C + lane] = gp[(tok0 + lane) * H + h];
+        ((T*)a.tail_beta)[ch * C + lane] = bp[(tok0 + lane) * H + h];
       }
     }
   }
@@ -573,12 +587,13 @@ template <class D, int DK, int DV>
 __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   using T = typename D::T;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
   const int col = threadIdx.x;
   const size_t SS = (size_t)DK * DV;
-  const int tl = a.tail_len[sh];
+  const int tl = a.tail_len[ch];
   __syncthreads();  // every wave has read tail_len before it is rewritten below
   if ((unsigned)tl >= (unsigned)C) return;  // not a valid cache: touch nothing
-  float* R = a.s_run + sh * SS;
+  float* R = a.s_run + ch * SS;
   float s[DK];
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
@@ -590,12 +605,12 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   const float out = token_step<D, DK>(s, (UniformRow)(kp + sh * DK), (UniformRow)(qp + sh * DK), alpha, bt, vv);
   D::store((T*)a.o, sh * DV + col, out);
   // append the token to the tail
-  T* tk = (T*)a.tail_k + (sh * C + tl) * DK;
+  T* tk = (T*)a.tail_k + (ch * C + tl) * DK;
   for (int e = col; e < DK; e += DV) tk[e] = kp[sh * DK + e];
-  ((T*)a.tail_v)[(sh * C + tl) * DV + col] = ((const T*)a.v)[sh * DV + col];
+  ((T*)a.tail_v)[(ch * C + tl) * DV + col] = ((const T*)a.v)[sh * DV + col];
   if (col == 0) {
-    ((T*)a.tail_g)[sh * C + tl] = ((const T*)a.g)[sh];
-    ((T*)a.tail_beta)[sh * C + tl] = ((const T*)a.beta)[sh];
+    ((T*)a.tail_g)[ch * C + tl] = ((const T*)a.g)[sh];
+    ((T*)a.tail_beta)[ch * C + tl] = ((const T*)a.beta)[sh];
   }
   const bool full = (tl + 1 == C);
   if (!full) {
@@ -603,7 +618,7 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
   }
   if (col == 0) {
-    a.tail_len[sh] = full ? 0 : tl + 1;
+    a.tail_len[ch] = full ? 0 : tl + 1;
     a.flag[sh] = full ? 1 : 0;
   }
 }
@@ -616,6 +631,7 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
 // kernels from the new boundary state.
 
 struct ContArgs {
+  const int32_t* slot;  // [N] cache row of sequence i, or null (row i)
   const void* q;
   const void* k;
   const void* v;
@@ -640,16 +656,17 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   using T = typename D::T;
   const int i = blockIdx.x, h = blockIdx.y, H = a.H;
   const size_t sh = (size_t)i * H + h;
+  const size_t ch = cache_row(a.slot, i) * H + h;
   const int col = threadIdx.x;
   const size_t SS = (size_t)DK * DV;
-  const int tl = a.tail_len[sh];
+  const int tl = a.tail_len[ch];
   __syncthreads();  // every wave has read tail_len before it is rewritten below
   const int L = a.cu[i + 1] - a.cu[i];
   const int nh = ((unsigned)tl < (unsigned)C && tl > 0) ? min(C - tl, L) : 0;
   if (h == 0 && col == 0) a.body_start[i] = a.cu[i] + nh;
   if (col == 0) a.flag[sh] = 0;
   if (nh == 0) return;
-  float* R = a.s_run + sh * SS;
+  float* R = a.s_run + ch * SS;
   float s[DK];
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
@@ -665,7 +682,7 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
     const float vv = D::load(vp, row * DV + col);
     const float out = token_step<D, DK>(s, (UniformRow)(kp + row * DK), (UniformRow)(qp + row * DK), alpha, bt, vv);
     D::store((T*)a.o, row * DV + col, out);
-    const size_t tr = sh * C + tl + t;  // tail row
+    const size_t tr = ch * C + tl + t;  // tail row
     T* tk = (T*)a.tail_k + tr * DK;
     for (int e = col; e < DK; e += DV) tk[e] = kp[row * DK + e];
     ((T*)a.tail_v)[tr * DV + col] = vp[row * DV + col];
@@ -680,7 +697,7 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
   }
   if (col == 0) {
-    a.tail_len[sh] = full ? 0 : tl + nh;
+    a.tail_len[ch] = full ? 0 : tl + nh;
     a.flag[sh] = full ? 1 : 0;
   }
 }
@@ -1675,6 +1692,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   CHECK_PTR(cache_out->tail_g, "cache.tail_g");
   CHECK_PTR(cache_out->tail_beta, "cache.tail_beta");
   CHECK_PTR(cache_out->tail_len, "cache.tail_len");
+  CHECK_OPT_PTR(cache_out->slot_index, "cache.slot_index");
   if (total_tokens > 0) {
     CHECK_PTR(q, "q");
     CHECK_PTR(k, "k");
@@ -1702,6 +1720,8 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.start = cu_seqlens;
   a.end = cu_seqlens + 1;
   a.skip_empty = 0;
+  a.slot = cache_out->slot_index;
+  a.h0_slotted = 0;
   a.h0 = h0;
   a.s_bnd = cache_out->s_bnd;
   a.s_run = cache_out->s_run;
@@ -1747,6 +1767,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   CHECK_PTR(cache->tail_g, "cache.tail_g");
   CHECK_PTR(cache->tail_beta, "cache.tail_beta");
   CHECK_PTR(cache->tail_len, "cache.tail_len");
+  CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
   const DecodeLayout L = decode_layout(*shape, num_seqs);
   if (!workspace || workspace_bytes < L.total)
     return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
@@ -1754,6 +1775,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
   char* ws = (char*)workspace;
   DecodeArgs a;
+  a.slot = cache->slot_index;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -1793,6 +1815,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   CHECK_PTR(cache->tail_g, "cache.tail_g");
   CHECK_PTR(cache->tail_beta, "cache.tail_beta");
   CHECK_PTR(cache->tail_len, "cache.tail_len");
+  CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
   if (total_tokens > 0) {
     CHECK_PTR(q, "q");
     CHECK_PTR(k, "k");
@@ -1814,6 +1837,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   char* wd = ws + L.dec_off;
   int32_t* body_start = (int32_t*)(ws + L.body_start);
   ContArgs ca;
+  ca.slot = cache->slot_index;
   ca.q = q;
   ca.k = k;
   ca.v = v;
@@ -1845,6 +1869,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   da.gamn = (float*)(wd + L.dec.gamn);
   da.N = num_seqs;
   da.H = shape->num_heads;
+  da.slot = cache->slot_index;
   PrefillArgs pa;
   pa.q = q;
   pa.k = k;
@@ -1854,6 +1879,8 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   pa.start = body_start;
   pa.end = cu_seqlens + 1;
   pa.skip_empty = 1;
+  pa.slot = cache->slot_index;
+  pa.h0_slotted = 1;
   pa.h0 = cache->s_bnd;  // the boundary the body starts from (aliases the output, as allowed)
   pa.s_bnd = cache->s_bnd;
   pa.s_run = cache->s_run;
@@ -1922,6 +1949,8 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.start = cu_seqlens;
   pa.end = cu_seqlens + 1;
   pa.skip_empty = 0;
+  pa.slot = nullptr;
+  pa.h0_slotted = 0;
   pa.h0 = h0;
   pa.s_bnd = (float*)(ws + L.s_bnd);
   pa.s_run = hT ? hT : (float*)(ws + L.s_run);

@@ -97,6 +97,15 @@ typedef struct {
  *   tail_len  [N, H] int32 in [0, C-1]; equal across the heads of a sequence
  *                                    (one counter per head so that each head's
  *                                    work item owns its own counter)
+ *   slot_index [N] int32, or NULL    slot-indexed caches: batch entry i uses
+ *                                    row slot_index[i] of every array above
+ *                                    (which then have at least
+ *                                    max(slot_index) + 1 rows in place of N);
+ *                                    rows must be distinct within a call.
+ *                                    NULL: row i.  Rows not named are not
+ *                                    touched, so a serving engine can keep a
+ *                                    pool of cache rows and pass each step's
+ *                                    batch by row number.
  */
 typedef struct {
   float* s_bnd;
@@ -106,6 +115,7 @@ typedef struct {
   void* tail_g;
   void* tail_beta;
   int32_t* tail_len;
+  const int32_t* slot_index;
 } gdn_cpr_cache;
 
 /*
@@ -124,8 +134,10 @@ size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num_seqs,
  * chunk (L mod C of them) become the cache's tail.
  *   q, k, v, g, beta  inputs, layouts above (T = total_tokens rows)
  *   cu_seqlens        [N + 1] int32
- *   h0                [N, H, d_k, d_v] fp32 initial states, or NULL for zero
- *                     states.  May alias cache_out->s_bnd or ->s_run.
+ *   h0                [N, H, d_k, d_v] fp32 initial states indexed by batch
+ *                     entry (not by cache row), or NULL for zero states.
+ *                     May alias cache_out->s_bnd or ->s_run when the cache
+ *                     has no slot_index.
  *   cache_out         host struct; every field required; written in full
  *   o                 [T, H, d_v] outputs
  * Zero-length sequences are allowed: their cache becomes h0 and no output

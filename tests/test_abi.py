@@ -52,8 +52,8 @@ def test_workspace_size_shapes():
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
 
 
-def _cache(ptr=FAKE):
-    return _lib.Cache(ptr, ptr, ptr, ptr, ptr, ptr, ptr)
+def _cache(ptr=FAKE, slots=None):
+    return _lib.Cache(ptr, ptr, ptr, ptr, ptr, ptr, ptr, slots)
 
 
 def _prefill(lib, shape, N=2, T=128, cache=None, cu=FAKE, q=FAKE, ws=FAKE, ws_bytes=0, h0=None):
@@ -109,6 +109,8 @@ def test_decode_rejects_bad_arguments():
     assert dec(shape=_shape(dk=32)) == _lib.GDN_ERR_UNSUPPORTED
     assert dec(q=None) == _lib.GDN_ERR_INVALID_ARG
     assert dec(c=_cache(FAKE + 2)) == _lib.GDN_ERR_INVALID_ARG
+    assert dec(c=_cache(FAKE, FAKE + 4)) == _lib.GDN_ERR_INVALID_ARG
+    assert b"slot_index" in lib.gdn_cpr_last_error()
     assert dec(ws_bytes=16) == _lib.GDN_ERR_WORKSPACE
     assert dec(N=0) == _lib.GDN_OK
 

@@ -230,6 +230,41 @@ def main():
     torch.cuda.synchronize()
     dec64_ms = e2.elapsed_time(e3) / 64
 
+    # ---- multi-token decode through the continuation call: 4 tokens for each
+    # of the 256 cached sequences per call (from the cache after the 64-step
+    # series), against 4 single-token decode steps on a copy of that cache
+    log("continuation: 256 sequences x 4 tokens per call")
+    n_tok = 4
+    c_cont = c64.clone()
+    c_dec = c64.clone()
+    b_c = make_batch(3, [2048 + 64 + n_tok] * 256, H, D, D, "bf16")
+    dc = to_dev(b_c)
+    rows_c = (torch.from_numpy(b_c.cu_seqlens[:-1].astype(np.int64)).to(dev)[:, None]
+              + torch.arange(2048 + 64, 2048 + 64 + n_tok, device=dev)[None, :]).reshape(-1)
+    cont_in = {n: dc[n][rows_c].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    dec_in4 = {n: cont_in[n].view(256, n_tok, *cont_in[n].shape[1:]).transpose(0, 1).contiguous()
+               for n in cont_in}
+    cu_c = torch.arange(0, 256 * n_tok + 1, n_tok, dtype=torch.int32, device=dev)
+    ws_c = gdn.alloc_workspace(shape, N_dec, 256 * n_tok, gdn.GDN_OP_PREFILL_CONTINUE, dev)
+    o_c = torch.empty((256 * n_tok, H, D), dtype=torch.bfloat16, device=dev)
+    o_d4 = torch.empty((n_tok, N_dec, H, D), dtype=torch.bfloat16, device=dev)
+    del dc
+    e4, e5, e6 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    torch.cuda.synchronize()
+    e4.record(stream)
+    gdn.gdn_cpr_prefill_continue(shape, cont_in["q"], cont_in["k"], cont_in["v"], cont_in["g"],
+                                 cont_in["beta"], cu_c, c_cont, o_c, ws_c)
+    e5.record(stream)
+    for j in range(n_tok):
+        gdn.gdn_cpr_decode_step(shape, dec_in4["q"][j], dec_in4["k"][j], dec_in4["v"][j], dec_in4["g"][j],
+                                dec_in4["beta"][j], c_dec, o_d4[j], ws_dec)
+    e6.record(stream)
+    torch.cuda.synchronize()
+    cont_ms, dec4_ms = e4.elapsed_time(e5), e5.elapsed_time(e6)
+    cont_bitwise = bool(torch.equal(o_c.view(256, n_tok, H, D).transpose(0, 1).contiguous().view(torch.int16),
+                                    o_d4.view(torch.int16))
+                        and torch.equal(c_cont.s_run.view(torch.int32), c_dec.s_run.view(torch.int32)))
+
     # ---- trainer forward + backward, 1 x 10,240 tokens
     log("fwd_bwd: 1 x 10,240 tokens")
     b_tr, _, _, _ = workload("train_1x10240")
@@ -340,6 +375,10 @@ def main():
                     "stage_ms": {"forward": round(float(np.median(fb_fwd)), 4),
                                  "bwd_local_and_reverse_chain": round(float(np.median(fb_bchain)), 4),
                                  "bwd_grads": round(float(np.median(fb_grads)), 4)}},
+        "continuation": {"workload": "256 cached sequences x 4 tokens in one gdn_cpr_prefill_continue call",
+                         "ms": round(cont_ms, 5), "tokens_per_s": round(256 * n_tok / (cont_ms / 1e3), 1),
+                         "four_decode_steps_ms": round(dec4_ms, 5),
+                         "equals_four_decode_steps_bitwise": cont_bitwise},
         "parity": {"decode_o_equals_prefill_o_bitwise": parity_o,
                    "decode_state_equals_prefill_state_bitwise": parity_s},
         "roofline": roofline,

@@ -297,6 +297,63 @@ def main():
         fb_grads.append(fb_ev.stage_ms(6))
     del ws_tr
 
+    # ---- comparators (not CPR) on the same inputs: prefill 5 x 2,048 and the
+    # 256-sequence decode step, plus the prefill/decode agreement on the last
+    # token of each prefill sequence
+    log("comparators: recurrent-everywhere and chunkwise (native) prefill, recurrent decode")
+    s0 = sets[0]
+    cmp_res = {}
+    st_cmp = torch.empty((N_pre, H, D, D), dtype=torch.float32, device=dev)
+    o_cmp = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    last = torch.from_numpy(b_pre.cu_seqlens[1:].astype(np.int64) - 1).to(dev)
+    bpre_1 = b_pre.truncate([2047] * 5)
+    p1 = to_dev(bpre_1)
+    x_last = {n: s0[n][last].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    for name, mode in (("recurrent_everywhere", gdn.GDN_CMP_RECURRENT), ("chunkwise_native", gdn.GDN_CMP_CHUNKWISE)):
+        ws_cmp = gdn.gdn_cmp_workspace(shape, mode, N_pre, T, dev)
+        run = lambda: gdn.gdn_cmp_prefill(shape, mode, s0["q"], s0["k"], s0["v"], s0["g"], s0["beta"], s0["cu"],
+                                          None, st_cmp, o_cmp, ws_cmp)
+        run()
+        torch.cuda.synchronize()
+        ta, tb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        ta.record(stream)
+        for _ in range(reps):
+            run()
+        tb.record(stream)
+        torch.cuda.synchronize()
+        pre_ms = ta.elapsed_time(tb) / reps
+        o_full = o_cmp[last].clone()
+        st1 = torch.empty_like(st_cmp)
+        o1 = torch.empty((bpre_1.total_tokens, H, D), dtype=torch.bfloat16, device=dev)
+        gdn.gdn_cmp_prefill(shape, mode, p1["q"], p1["k"], p1["v"], p1["g"], p1["beta"], p1["cu"], None, st1, o1,
+                            gdn.gdn_cmp_workspace(shape, mode, N_pre, bpre_1.total_tokens, dev))
+        o_dl = torch.empty((N_pre, H, D), dtype=torch.bfloat16, device=dev)
+        gdn.gdn_cmp_decode_step(shape, x_last["q"], x_last["k"], x_last["v"], x_last["g"], x_last["beta"], st1, o_dl)
+        torch.cuda.synchronize()
+        cmp_res[name] = {"prefill_ms": round(pre_ms, 5),
+                         "prefill_tokens_per_s": round(T / (pre_ms / 1e3), 1),
+                         "decode_after_prefill_equals_prefill_bitwise":
+                             bool(torch.equal(o_dl.view(torch.int16), o_full.view(torch.int16))),
+                         "max_abs_decode_minus_prefill": float(torch.max(torch.abs(o_dl.float() - o_full.float())))}
+        del ws_cmp
+    # recurrent decode step (no tail, no resync) on the 256-sequence state
+    st_dec = cache_dec.s_run.clone()
+    o_rd = torch.empty((N_dec, H, D), dtype=torch.bfloat16, device=dev)
+    i0 = 0
+    gdn.gdn_cmp_decode_step(shape, dec_in["q"][i0], dec_in["k"][i0], dec_in["v"][i0], dec_in["g"][i0],
+                            dec_in["beta"][i0], st_dec, o_rd)
+    torch.cuda.synchronize()
+    ta, tb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ta.record(stream)
+    for j in range(8):
+        gdn.gdn_cmp_decode_step(shape, dec_in["q"][j], dec_in["k"][j], dec_in["v"][j], dec_in["g"][j],
+                                dec_in["beta"][j], st_dec, o_rd)
+    tb.record(stream)
+    torch.cuda.synchronize()
+    cmp_res["recurrent_decode_step_ms"] = round(ta.elapsed_time(tb) / 8, 5)
+    del st_dec, p1
+
     # ---- parity: decode the last token of every prefill sequence == prefill output
     log("parity check: prefill vs decode on the 5 x 2,048 workload")
     s = sets[0]
@@ -379,6 +436,7 @@ def main():
                          "ms": round(cont_ms, 5), "tokens_per_s": round(256 * n_tok / (cont_ms / 1e3), 1),
                          "four_decode_steps_ms": round(dec4_ms, 5),
                          "equals_four_decode_steps_bitwise": cont_bitwise},
+        "comparators": cmp_res,
         "parity": {"decode_o_equals_prefill_o_bitwise": parity_o,
                    "decode_state_equals_prefill_state_bitwise": parity_s},
         "roofline": roofline,

@@ -10,6 +10,9 @@ from .api import (  # noqa: F401
     StageEvents,
     alloc_cache,
     alloc_workspace,
+    gdn_cmp_decode_step,
+    gdn_cmp_prefill,
+    gdn_cmp_workspace,
     gdn_cpr_decode_step,
     gdn_cpr_fwd_bwd,
     gdn_cpr_last_error,
@@ -23,5 +26,7 @@ from ._lib import (  # noqa: F401
     GDN_OP_FWD_BWD,
     GDN_OP_PREFILL,
     GDN_OP_PREFILL_CONTINUE,
+    GDN_CMP_CHUNKWISE,
+    GDN_CMP_RECURRENT,
     GdnError,
 )

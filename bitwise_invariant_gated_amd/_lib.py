@@ -26,6 +26,9 @@ GDN_OP_DECODE = 1
 GDN_OP_FWD_BWD = 2
 GDN_OP_PREFILL_CONTINUE = 3
 
+GDN_CMP_RECURRENT = 0
+GDN_CMP_CHUNKWISE = 1
+
 # every symbol the header declares
 EXPORTED = (
     "gdn_cpr_workspace_size",
@@ -36,6 +39,9 @@ EXPORTED = (
     "gdn_cpr_set_stage_events",
     "gdn_cpr_last_error",
     "gdn_cpr_numerics_id",
+    "gdn_cmp_workspace_size",
+    "gdn_cmp_prefill",
+    "gdn_cmp_decode_step",
 )
 
 
@@ -94,6 +100,14 @@ def load() -> ctypes.CDLL:
     lib.gdn_cpr_fwd_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdn_cmp_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_cmp_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+    lib.gdn_cmp_prefill.restype = ctypes.c_int
+    lib.gdn_cmp_prefill.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdn_cmp_decode_step.restype = ctypes.c_int
+    lib.gdn_cmp_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp]
     lib.gdn_cpr_set_stage_events.restype = None
     lib.gdn_cpr_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
     lib.gdn_cpr_last_error.restype = ctypes.c_char_p

@@ -141,6 +141,31 @@ def gdn_cpr_fwd_bwd(shape: LayerShape, q, k, v, g, beta, cu_seqlens, h0, d_o, d_
                                    _stream(stream)))
 
 
+def gdn_cmp_workspace(shape: LayerShape, mode: int, num_seqs: int, total_tokens: int,
+                      device="cuda") -> torch.Tensor:
+    n = int(_lib.load().gdn_cmp_workspace_size(ctypes.byref(shape.c()), mode, num_seqs, total_tokens))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def gdn_cmp_prefill(shape: LayerShape, mode: int, q, k, v, g, beta, cu_seqlens, h0, state_out, o,
+                    workspace: torch.Tensor, stream=None) -> None:
+    """Comparator prefill (GDN_CMP_RECURRENT or GDN_CMP_CHUNKWISE), not CPR."""
+    lib = _lib.load()
+    N = int(cu_seqlens.numel()) - 1
+    T = int(q.shape[0])
+    _lib.check(lib.gdn_cmp_prefill(ctypes.byref(shape.c()), mode, N, T, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(state_out), _ptr(o),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def gdn_cmp_decode_step(shape: LayerShape, q, k, v, g, beta, state, o, stream=None) -> None:
+    """Comparator decode: the per-token step on `state`, no tail, no resynchronisation."""
+    lib = _lib.load()
+    N = int(q.shape[0])
+    _lib.check(lib.gdn_cmp_decode_step(ctypes.byref(shape.c()), N, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta), _ptr(state), _ptr(o), _stream(stream)))
+
+
 class StageEvents:
     """Per-stage HIP events recorded by the library's measurement hook
     (gdn_cpr_set_stage_events), as torch events on the call's stream."""

@@ -53,6 +53,8 @@ struct PrefillArgs {
   int32_t skip_empty;    // 1: a sequence with no tokens leaves its cache untouched
   const int32_t* slot;   // [N] cache row of sequence i, or null (row i)
   int32_t h0_slotted;    // 1: h0 is indexed by cache row (h0 = the cache's s_bnd)
+  int32_t all_chunks;    // 1 (comparator): products exist for every chunk slot, partial ones zero-padded;
+                         // the chain runs over all of them and writes only the final state to s_bnd
   const float* h0;
   float* s_bnd;
   float* s_run;
@@ -380,10 +382,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   const int H = a.H;
   const int L = a.end[i] - a.start[i];
   if (a.skip_empty && L == 0) return;
-  const int nfull = L / C, nall = (L + C - 1) / C;
+  int nfull = L / C;
+  const int nall = (L + C - 1) / C;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
-  const int abase = a.all_base[i], fbase = a.full_base[i];
+  const int abase = a.all_base[i];
+  const int fbase = a.all_chunks ? abase : a.full_base[i];
+  if (a.all_chunks) nfull = nall;
   auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * Sl::bytes; };
   auto gamn_of = [&](int c) { return a.gamn[(size_t)(fbase + c) * H + h]; };
   // piece p of chunk c: WF/KF piece p, or U piece p - kFragPieces of this block's tiles
@@ -475,6 +480,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
     step(P0{}, Last{}, c);
   }
   store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
+  if (a.all_chunks) return;
   if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
   if (blockIdx.z == 0 && tid == 0) a.tail_len[ch] = L % C;
 }
@@ -699,6 +705,277 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   if (col == 0) {
     a.tail_len[ch] = full ? 0 : tl + nh;
     a.flag[sh] = full ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// comparators (not CPR): the two evaluation orders whose mismatch the pages
+// describe, built from this library's routines (English page, CPR section
+// and its table; Chinese page, third-way section):
+//   recurrent everywhere   the token step over each whole sequence, and the
+//                          same step for decode (no chunk boundaries)
+//   chunkwise everywhere   boundary states over every chunk (the last,
+//                          partial chunk zero-padded) and the outputs from the
+//                          chunk form O = diag(Gamma) Q B + (Q K^T .* D) Delta,
+//                          with no per-token scan
+// "Native mixed" serving is the chunkwise prefill followed by the recurrent
+// decode: both are exact in exact arithmetic, but they round differently.
+
+struct CmpArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const int32_t* cu;
+  const float* h0;
+  float* state;  // [N, H, DK, DV] final state (prefill) / running state (decode)
+  void* o;
+  int32_t* all_base;
+  uint8_t* prod;
+  float* gamn;
+  float* bnd;
+  int32_t N;
+  int32_t H;
+};
+
+// recurrent prefill: one wave per (sequence, head, 64 state columns), the
+// scan's operand delivery (DPP row broadcast) over every token in order
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(64, 3) void k_cmp_rec_prefill(const CmpArgs a) {
+  using T = typename D::T;
+  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
+  const int lane = threadIdx.x, col = blockIdx.z * kWave + lane;
+  const int L = a.cu[i + 1] - a.cu[i];
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  float s[DK];
+#pragma unroll
+  for (int ii = 0; ii < DK; ++ii) s[ii] = a.h0 ? a.h0[sh * SS + (size_t)ii * DV + col] : 0.f;
+  const T* gp = (const T*)a.g;
+  const T* bp = (const T*)a.beta;
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const T* vp = (const T*)a.v;
+  T* op = (T*)a.o;
+  for (int c0 = 0; c0 < L; c0 += kWave) {
+    const int n = min(kWave, L - c0);
+    const size_t tok0 = (size_t)a.cu[i] + c0;
+    float alpha_l = 1.f, beta_l = 0.f;
+    if (lane < n) {
+      const size_t r = (tok0 + lane) * H + h;
+      alpha_l = decay_of(D::load(gp, r));
+      beta_l = D::load(bp, r);
+    }
+    KQRaw<D> raw;
+    size_t row = tok0 * H + h;
+    load_kq<D, DK>(raw, kp + row * DK, qp + row * DK, lane);
+    float vv = D::load(vp, row * DV + col);
+    for (int t = 0; t < n; ++t) {
+      float kf[8], qf[8];
+      unpack_kq<D>(raw, kf, qf);
+      const float vcur = vv;
+      const size_t next = row + H;
+      if (t + 1 < n) {
+        load_kq<D, DK>(raw, kp + next * DK, qp + next * DK, lane);
+        vv = D::load(vp, next * DV + col);
+      }
+      const float out = token_step_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
+      D::store(op, row * DV + col, out);
+      row = next;
+    }
+  }
+#pragma unroll
+  for (int ii = 0; ii < DK; ++ii) a.state[sh * SS + (size_t)ii * DV + col] = s[ii];
+}
+
+// recurrent decode: the per-token step on the running state, nothing else
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(DV) void k_cmp_rec_decode(const CmpArgs a) {
+  using T = typename D::T;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const int col = threadIdx.x;
+  float* R = a.state + sh * (size_t)DK * DV;
+  float s[DK];
+#pragma unroll
+  for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const float alpha = decay_of(D::load((const T*)a.g, sh));
+  const float bt = D::load((const T*)a.beta, sh);
+  const float vv = D::load((const T*)a.v, sh * DV + col);
+  const float out = token_step<D, DK>(s, (UniformRow)(kp + sh * DK), (UniformRow)(qp + sh * DK), alpha, bt, vv);
+  D::store((T*)a.o, sh * DV + col, out);
+#pragma unroll
+  for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+}
+
+// chunkwise: chunk products of every chunk slot, a partial chunk padded with
+// k = v = 0, g = beta = 0 (identity steps)
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_cmp_chunk_local_bf16(const CmpArgs a) {
+  typedef SlotB<DK, DV> Sl;
+  __shared__ ChunkLdsB<DK, DV> sm;
+  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
+  if (slot >= a.all_base[a.N]) return;
+  const int i = find_seq(a.all_base, a.N, slot);
+  const int c = slot - a.all_base[i];
+  const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const uint16_t* kp = (const uint16_t*)a.k;
+  const uint16_t* vp = (const uint16_t*)a.v;
+  const int tid = threadIdx.x;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  for (int idx = tid; idx < C * DK / 8; idx += 256) {
+    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
+    u32x4v w = {0u, 0u, 0u, 0u};
+    if (t < n) w = *reinterpret_cast<const u32x4v*>(kp + (row0 + (size_t)t * H) * DK + i0);
+    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
+  }
+  for (int idx = tid; idx < C * DV / 8; idx += 256) {
+    const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+    u32x4v w = {0u, 0u, 0u, 0u};
+    if (t < n) w = *reinterpret_cast<const u32x4v*>(vp + (row0 + (size_t)t * H) * DV + j0);
+    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) = w;
+  }
+  if (tid < C) {
+    sm.g[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
+    sm.beta[tid] = tid < n ? Bf16::load((const uint16_t*)a.beta, row0 + (size_t)tid * H) : 0.f;
+  }
+  __syncthreads();
+  const size_t ps = (size_t)slot * H + h;
+  chunk_local_bf16<DK, DV>(sm, a.prod + ps * Sl::bytes, a.gamn + ps);
+}
+
+// chunkwise outputs: per (chunk slot, head), 4 waves x 32 state columns
+//   Delta = U + Wneg bf16(B)                       (as the chain's first phase)
+//   O     = diag(Gamma) (Q bf16(B)) + bf16(P) bf16(Delta),  P = (Q K^T) .* D
+template <int DK, int DV>
+struct CmpOutLds {
+  uint16_t Q[C][DK + 8];
+  uint16_t K[C][DK + 8];
+  uint16_t P[C][C + 8];
+  float g[C], gam[C], Gam[C];
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
+  using namespace mfma;
+  typedef SlotB<DK, DV> Sl;
+  constexpr int NT = DV / 64;  // 16-column tiles per wave
+  __shared__ CmpOutLds<DK, DV> sm;
+  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
+  if (slot >= a.all_base[a.N]) return;
+  const int i = find_seq(a.all_base, a.N, slot);
+  const int c = slot - a.all_base[i];
+  const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const uint16_t* qp = (const uint16_t*)a.q;
+  const uint16_t* kp = (const uint16_t*)a.k;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  for (int idx = tid; idx < C * DK / 8; idx += 256) {
+    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
+    u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
+    if (t < n) {
+      wq = *reinterpret_cast<const u32x4v*>(qp + (row0 + (size_t)t * H) * DK + i0);
+      wk = *reinterpret_cast<const u32x4v*>(kp + (row0 + (size_t)t * H) * DK + i0);
+    }
+    *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
+    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
+  }
+  if (tid < C) sm.g[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = sm.g[0];
+    sm.gam[0] = acc;
+    for (int t = 1; t < C; ++t) {
+      acc = acc + sm.g[t];
+      sm.gam[t] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < C) sm.Gam[tid] = expf(sm.gam[tid]);
+  // P = (Q K^T) .* D (lower, diagonal included), rounded to bf16
+  for (int q2 = wave; q2 < 16; q2 += 4) {
+    const int tm = q2 >> 2, tn = q2 & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tn <= tm) {
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb)
+        acc = mma(frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tm + 4 * g + r, s2 = 16 * tn + lr;
+      sm.P[t][s2] = Bf16::round(s2 <= t ? acc[r] * expf(sm.gam[t] - sm.gam[s2]) : 0.f);
+    }
+  }
+  __syncthreads();
+  const size_t ps = (size_t)slot * H + h;
+  const uint8_t* sl = a.prod + ps * Sl::bytes;
+  const u32x4* WF = reinterpret_cast<const u32x4*>(sl + Sl::oWF);
+  const f32x4* UT = reinterpret_cast<const f32x4*>(sl + Sl::oU);
+  const float* B = a.bnd + ps * (size_t)DK * DV;
+  const int jb0 = wave * NT;
+  f32x4 S[DK / 16][NT];
+#pragma unroll
+  for (int im = 0; im < DK / 16; ++im)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      S[im][nt] = *reinterpret_cast<const f32x4*>(B + ((size_t)((jb0 + nt) * (DK / 16) + im) * 64 + lane) * 4);
+  u32x4 Sb[DK / 32][NT];
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) Sb[kb][nt] = frag_from_acc(S[2 * kb][nt], S[2 * kb + 1][nt]);
+  f32x4 Dl[C / 16][NT];
+#pragma unroll
+  for (int tm = 0; tm < C / 16; ++tm)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) Dl[tm][nt] = UT[((jb0 + nt) * (C / 16) + tm) * 64 + lane];
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb)
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      const u32x4 w = WF[(kb * (C / 16) + tm) * 64 + lane];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) Dl[tm][nt] = mma(w, Sb[kb][nt], Dl[tm][nt]);
+    }
+  u32x4 Db[C / 32][NT];
+#pragma unroll
+  for (int kb = 0; kb < C / 32; ++kb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) Db[kb][nt] = frag_from_acc(Dl[2 * kb][nt], Dl[2 * kb + 1][nt]);
+  uint16_t* op = (uint16_t*)a.o;
+#pragma unroll
+  for (int tm = 0; tm < C / 16; ++tm) {
+    f32x4 O[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const u32x4 qf = frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) O[nt] = mma(qf, Sb[kb][nt], O[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[nt][r] *= sm.Gam[16 * tm + 4 * g + r];
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      const u32x4 pf = frag_row(&sm.P[16 * tm + lr][0], 32 * kb, g);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) O[nt] = mma(pf, Db[kb][nt], O[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tm + 4 * g + r;
+        if (t < n) op[(row0 + (size_t)t * H) * DV + 16 * (jb0 + nt) + lr] = Bf16::round(O[nt][r]);
+      }
   }
 }
 
@@ -1458,6 +1735,23 @@ gdn_status launch_status(const char* fn) {
   return GDN_OK;
 }
 
+// bf16 boundary chain: the fewer (sequence, head) pairs, the more work-groups
+// per pair (the column split is bit-neutral)
+template <int DK, int DV>
+void launch_chain_bf16(const PrefillArgs& a, hipStream_t st) {
+  const long pairs = (long)a.N * a.H;
+  if constexpr (DV >= 128) {
+    if (pairs * (DV / 128) >= 128) {
+      hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 4, 2>), dim3(a.N, a.H, DV / 128), dim3(256), 0, st, a);
+      return;
+    }
+  }
+  if (pairs * (DV / 64) >= 96)
+    hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 4, 1>), dim3(a.N, a.H, DV / 64), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 2, 1>), dim3(a.N, a.H, DV / 32), dim3(128), 0, st, a);
+}
+
 template <class D, int DK, int DV>
 gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const char* fn) {
   const int Fmax = (int)(T / C);
@@ -1474,22 +1768,9 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   }
   mark(2, st);
   if (a.N > 0) {
-    if constexpr (kBf16) {
-      // the fewer (sequence, head) pairs, the more work-groups per pair
-      const long pairs = (long)a.N * a.H;
-      bool done = false;
-      if constexpr (DV >= 128) {
-        if (pairs * (DV / 128) >= 128) {
-          hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 4, 2>), dim3(a.N, a.H, DV / 128), dim3(256), 0, st, a);
-          done = true;
-        }
-      }
-      if (done) {
-      } else if (pairs * (DV / 64) >= 96)
-        hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 4, 1>), dim3(a.N, a.H, DV / 64), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 2, 1>), dim3(a.N, a.H, DV / 32), dim3(128), 0, st, a);
-    } else
+    if constexpr (kBf16)
+      launch_chain_bf16<DK, DV>(a, st);
+    else
       hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
   }
   mark(3, st);
@@ -1577,6 +1858,60 @@ struct ContFn {
     gdn_status r = launch_status(fn);
     if (r != GDN_OK) return r;
     return run_prefill<D, DK, DV>(pa, T, st, fn);
+  }
+};
+
+// comparators: chunkwise layout = plan, one product slot and one boundary
+// state per (chunk slot incl. partial, head)
+struct CmpLayout {
+  size_t full_base, all_base, prod, gamn, bnd, total;
+};
+
+CmpLayout cmp_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
+  const size_t H = s.num_heads, DK = s.head_dim_k, DV = s.head_dim_v;
+  const size_t Amax = (size_t)(T / C) + (size_t)N;
+  CmpLayout L;
+  size_t off = 0;
+  L.full_base = off;
+  off = align_up(off + sizeof(int32_t) * (N + 1));
+  L.all_base = off;
+  off = align_up(off + sizeof(int32_t) * (N + 1));
+  L.prod = off;
+  off = align_up(off + Amax * H * prod_slot_bytes(true, (int)DK, (int)DV));
+  L.gamn = off;
+  off = align_up(off + sizeof(float) * Amax * H);
+  L.bnd = off;
+  off = align_up(off + sizeof(float) * Amax * H * DK * DV);
+  L.total = off;
+  return L;
+}
+
+template <class D, int DK, int DV>
+struct CmpPrefillFn {
+  static gdn_status run(int mode, const CmpArgs& ca, const PrefillArgs& pa, int64_t T, hipStream_t st,
+                        const char* fn) {
+    if constexpr (!std::is_same<D, Bf16>::value) {
+      return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take bf16 inputs", fn);
+    } else {
+      const int Amax = (int)(T / C) + ca.N;
+      if (mode == GDN_CMP_RECURRENT) {
+        hipLaunchKernelGGL((k_cmp_rec_prefill<D, DK, DV>), dim3(ca.N, ca.H, DV / kWave), dim3(kWave), 0, st, ca);
+        return launch_status(fn);
+      }
+      hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.full_base, pa.all_base);
+      if (T > 0) hipLaunchKernelGGL((k_cmp_chunk_local_bf16<DK, DV>), dim3(Amax, ca.H), dim3(256), 0, st, ca);
+      launch_chain_bf16<DK, DV>(pa, st);
+      if (T > 0) hipLaunchKernelGGL((k_cmp_chunk_out_bf16<DK, DV>), dim3(Amax, ca.H), dim3(256), 0, st, ca);
+      return launch_status(fn);
+    }
+  }
+};
+
+template <class D, int DK, int DV>
+struct CmpDecodeFn {
+  static gdn_status run(const CmpArgs& ca, hipStream_t st, const char* fn) {
+    hipLaunchKernelGGL((k_cmp_rec_decode<D, DK, DV>), dim3(ca.N, ca.H), dim3(DV), 0, st, ca);
+    return launch_status(fn);
   }
 };
 
@@ -1722,6 +2057,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.skip_empty = 0;
   a.slot = cache_out->slot_index;
   a.h0_slotted = 0;
+  a.all_chunks = 0;
   a.h0 = h0;
   a.s_bnd = cache_out->s_bnd;
   a.s_run = cache_out->s_run;
@@ -1881,6 +2217,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   pa.skip_empty = 1;
   pa.slot = cache->slot_index;
   pa.h0_slotted = 1;
+  pa.all_chunks = 0;
   pa.h0 = cache->s_bnd;  // the boundary the body starts from (aliases the output, as allowed)
   pa.s_bnd = cache->s_bnd;
   pa.s_run = cache->s_run;
@@ -1951,6 +2288,7 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.skip_empty = 0;
   pa.slot = nullptr;
   pa.h0_slotted = 0;
+  pa.all_chunks = 0;
   pa.h0 = h0;
   pa.s_bnd = (float*)(ws + L.s_bnd);
   pa.s_run = hT ? hT : (float*)(ws + L.s_run);
@@ -1989,6 +2327,116 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   ba.N = num_seqs;
   ba.H = shape->num_heads;
   return dispatch<FwdBwdFn>(*shape, pa, ba, total_tokens, L.slot, (hipStream_t)stream, fn);
+}
+
+extern "C" size_t gdn_cmp_workspace_size(const gdn_cpr_shape* shape, int32_t mode, int32_t num_seqs,
+                                         int64_t total_tokens) {
+  std::string why;
+  if (!shape_ok(shape, &why) || num_seqs < 0 || total_tokens < 0) return 0;
+  if (mode == GDN_CMP_RECURRENT) return 256;
+  if (mode == GDN_CMP_CHUNKWISE) return cmp_layout(*shape, num_seqs, total_tokens).total;
+  return 0;
+}
+
+extern "C" gdn_status gdn_cmp_prefill(const gdn_cpr_shape* shape, int32_t mode, int32_t num_seqs, int64_t total_tokens,
+                                      const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const int32_t* cu_seqlens, const float* h0, float* state_out, void* o,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_cmp_prefill";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (shape->dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take bf16 inputs", fn);
+  if (mode != GDN_CMP_RECURRENT && mode != GDN_CMP_CHUNKWISE) return fail(GDN_ERR_INVALID_ARG, "%s: mode", fn);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (total_tokens > (int64_t)INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+  CHECK_PTR(cu_seqlens, "cu_seqlens");
+  CHECK_OPT_PTR(h0, "h0");
+  CHECK_PTR(state_out, "state_out");
+  if (total_tokens > 0) {
+    CHECK_PTR(q, "q");
+    CHECK_PTR(k, "k");
+    CHECK_PTR(v, "v");
+    CHECK_PTR(g, "g");
+    CHECK_PTR(beta, "beta");
+    CHECK_PTR(o, "o");
+  }
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  const size_t need = gdn_cmp_workspace_size(shape, mode, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  char* ws = (char*)workspace;
+  const CmpLayout L = cmp_layout(*shape, num_seqs, total_tokens);
+  CmpArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.g = g;
+  ca.beta = beta;
+  ca.cu = cu_seqlens;
+  ca.h0 = h0;
+  ca.state = state_out;
+  ca.o = o;
+  ca.N = num_seqs;
+  ca.H = shape->num_heads;
+  PrefillArgs pa;
+  memset(&pa, 0, sizeof(pa));
+  if (mode == GDN_CMP_CHUNKWISE) {
+    ca.all_base = (int32_t*)(ws + L.all_base);
+    ca.prod = (uint8_t*)(ws + L.prod);
+    ca.gamn = (float*)(ws + L.gamn);
+    ca.bnd = (float*)(ws + L.bnd);
+    pa.start = cu_seqlens;
+    pa.end = cu_seqlens + 1;
+    pa.all_chunks = 1;
+    pa.h0 = h0;
+    pa.s_bnd = state_out;
+    pa.full_base = (int32_t*)(ws + L.full_base);
+    pa.all_base = ca.all_base;
+    pa.prod = ca.prod;
+    pa.gamn = ca.gamn;
+    pa.bnd = ca.bnd;
+    pa.N = num_seqs;
+    pa.H = shape->num_heads;
+  }
+  return dispatch<CmpPrefillFn>(*shape, (int)mode, ca, pa, total_tokens, (hipStream_t)stream, fn);
+}
+
+extern "C" gdn_status gdn_cmp_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                                          const void* k, const void* v, const void* g, const void* beta,
+                                          float* state, void* o, void* stream) {
+  const char* fn = "gdn_cmp_decode_step";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(g, "g");
+  CHECK_PTR(beta, "beta");
+  CHECK_PTR(o, "o");
+  CHECK_PTR(state, "state");
+  CmpArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.g = g;
+  ca.beta = beta;
+  ca.state = state;
+  ca.o = o;
+  ca.N = num_seqs;
+  ca.H = shape->num_heads;
+  return dispatch<CmpDecodeFn>(*shape, ca, (hipStream_t)stream, fn);
 }
 
 extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) {

@@ -216,6 +216,44 @@ gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Comparators (not CPR).  The pages measure CPR against the evaluation orders
+ * it replaces: chunkwise-parallel prefill and training with a recurrent
+ * decode, whose outputs disagree (English page, CPR section and its table;
+ * Chinese page, third-way section).  These calls build those orders from
+ * this library's routines so that the disagreement and the cost of each
+ * order can be measured on the same inputs; bf16 inputs only.
+ *   GDN_CMP_RECURRENT  prefill = the per-token step over each whole sequence
+ *                      (no chunk boundaries); decode = the same step.  Prefill
+ *                      and decode agree bitwise, but prefill is sequential
+ *                      along the sequence.
+ *   GDN_CMP_CHUNKWISE  prefill = boundary states over every chunk (the last,
+ *                      partial chunk zero-padded) and outputs from the chunk
+ *                      form O = diag(Gamma) Q B + (Q K^T .* D) Delta with bf16
+ *                      B, Delta and (Q K^T .* D) operands, no per-token scan.
+ *                      Followed by gdn_cmp_decode_step it is the "native
+ *                      mixed" serving path: prefill and decode round
+ *                      differently.
+ * gdn_cmp_prefill: h0 [N, H, d_k, d_v] or NULL (zeros); state_out
+ * [N, H, d_k, d_v] receives each sequence's final state; o [T, H, d_v].
+ * gdn_cmp_decode_step: the per-token step on state [N, H, d_k, d_v] (read-
+ * modify-write), one token per sequence, no tail and no resynchronisation.
+ * Workspace: gdn_cmp_workspace_size (the recurrent mode needs none beyond
+ * 256 bytes; the decode step needs none).
+ */
+typedef enum { GDN_CMP_RECURRENT = 0, GDN_CMP_CHUNKWISE = 1 } gdn_cmp_mode;
+
+size_t gdn_cmp_workspace_size(const gdn_cpr_shape* shape, int32_t mode, int32_t num_seqs, int64_t total_tokens);
+
+gdn_status gdn_cmp_prefill(const gdn_cpr_shape* shape, int32_t mode, int32_t num_seqs, int64_t total_tokens,
+                           const void* q, const void* k, const void* v, const void* g, const void* beta,
+                           const int32_t* cu_seqlens, const float* h0, float* state_out, void* o,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+gdn_status gdn_cmp_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q, const void* k,
+                               const void* v, const void* g, const void* beta, float* state, void* o,
+                               void* stream);
+
+/*
  * Measurement hook (the pages report per-stage timings of the layer, English
  * page, CPR table).  events points to an array of hipEvent_t handles owned by
  * the caller, or NULL to switch the hook off (the default).  While set, on

@@ -22,7 +22,7 @@ def _lib_or_skip():
 def test_header_declares_exactly_the_bound_symbols():
     with open(os.path.join(ROOT, "include", "gdn_cpr.h")) as f:
         text = f.read()
-    declared = set(re.findall(r"\b(gdn_cpr_[a-z_]+)\s*\(", text))
+    declared = set(re.findall(r"\b(gdn_(?:cpr|cmp)_[a-z_]+)\s*\(", text))
     assert declared == set(_lib.EXPORTED)
 
 

@@ -353,6 +353,20 @@ def main():
     torch.cuda.synchronize()
     cmp_res["recurrent_decode_step_ms"] = round(ta.elapsed_time(tb) / 8, 5)
     del st_dec, p1
+    # chunkwise-everywhere decode: 64 consecutive steps (one chunk, one boundary
+    # move per sequence) from the 2,112-token cache, beside CPR's 64-step mean
+    c_cd = c64.clone()
+    o_cd = torch.empty((N_dec, H, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    ta.record(stream)
+    for i in range(64):
+        gdn.gdn_cmp_chunk_decode_step(shape, dec64["q"][i], dec64["k"][i], dec64["v"][i], dec64["g"][i],
+                                      dec64["beta"][i], c_cd, o_cd, ws_dec)
+    tb.record(stream)
+    torch.cuda.synchronize()
+    cmp_res["chunkwise_decode_mean_over_64_steps_ms"] = round(ta.elapsed_time(tb) / 64, 5)
+    cmp_res["cpr_decode_mean_over_64_steps_ms"] = round(dec64_ms, 5)
+    del c_cd
 
     # ---- parity: decode the last token of every prefill sequence == prefill output
     log("parity check: prefill vs decode on the 5 x 2,048 workload")

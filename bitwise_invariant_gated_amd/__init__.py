@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     StageEvents,
     alloc_cache,
     alloc_workspace,
+    gdn_cmp_chunk_decode_step,
     gdn_cmp_decode_step,
     gdn_cmp_prefill,
     gdn_cmp_workspace,

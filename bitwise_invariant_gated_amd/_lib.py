@@ -42,6 +42,7 @@ EXPORTED = (
     "gdn_cmp_workspace_size",
     "gdn_cmp_prefill",
     "gdn_cmp_decode_step",
+    "gdn_cmp_chunk_decode_step",
 )
 
 
@@ -108,6 +109,9 @@ def load() -> ctypes.CDLL:
     lib.gdn_cmp_decode_step.restype = ctypes.c_int
     lib.gdn_cmp_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp]
+    lib.gdn_cmp_chunk_decode_step.restype = ctypes.c_int
+    lib.gdn_cmp_chunk_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                              _vp, ctypes.POINTER(Cache), _vp, _vp, ctypes.c_size_t, _vp]
     lib.gdn_cpr_set_stage_events.restype = None
     lib.gdn_cpr_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
     lib.gdn_cpr_last_error.restype = ctypes.c_char_p

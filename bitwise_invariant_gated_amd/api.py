@@ -166,6 +166,18 @@ def gdn_cmp_decode_step(shape: LayerShape, q, k, v, g, beta, state, o, stream=No
                                        _ptr(beta), _ptr(state), _ptr(o), _stream(stream)))
 
 
+def gdn_cmp_chunk_decode_step(shape: LayerShape, q, k, v, g, beta, cache: CprCache, o,
+                              workspace: torch.Tensor, stream=None) -> None:
+    """Comparator decode, chunkwise everywhere: the token's output from the chunk
+    form over its partial chunk (cache tail + the token) on cache.s_bnd."""
+    lib = _lib.load()
+    N = int(q.shape[0])
+    cc = cache.c()
+    _lib.check(lib.gdn_cmp_chunk_decode_step(ctypes.byref(shape.c()), N, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                             _ptr(beta), ctypes.byref(cc), _ptr(o), _ptr(workspace),
+                                             workspace.numel(), _stream(stream)))
+
+
 class StageEvents:
     """Per-stage HIP events recorded by the library's measurement hook
     (gdn_cpr_set_stage_events), as torch events on the call's stream."""

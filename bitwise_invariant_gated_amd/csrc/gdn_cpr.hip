@@ -598,7 +598,10 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   const size_t SS = (size_t)DK * DV;
   const int tl = a.tail_len[ch];
   __syncthreads();  // every wave has read tail_len before it is rewritten below
-  if ((unsigned)tl >= (unsigned)C) return;  // not a valid cache: touch nothing
+  if ((unsigned)tl >= (unsigned)C) {  // not a valid cache: touch nothing
+    if (col == 0) a.flag[sh] = 0;
+    return;
+  }
   float* R = a.s_run + ch * SS;
   float s[DK];
 #pragma unroll
@@ -858,34 +861,11 @@ struct CmpOutLds {
   float g[C], gam[C], Gam[C];
 };
 
+// gamma, Gamma and P = bf16((Q K^T) .* D) of a chunk staged in sm (Q, K, g)
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
+__device__ __forceinline__ void cmp_out_prepare(CmpOutLds<DK, DV>& sm) {
   using namespace mfma;
-  typedef SlotB<DK, DV> Sl;
-  constexpr int NT = DV / 64;  // 16-column tiles per wave
-  __shared__ CmpOutLds<DK, DV> sm;
-  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
-  if (slot >= a.all_base[a.N]) return;
-  const int i = find_seq(a.all_base, a.N, slot);
-  const int c = slot - a.all_base[i];
-  const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const uint16_t* qp = (const uint16_t*)a.q;
-  const uint16_t* kp = (const uint16_t*)a.k;
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  for (int idx = tid; idx < C * DK / 8; idx += 256) {
-    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
-    if (t < n) {
-      wq = *reinterpret_cast<const u32x4v*>(qp + (row0 + (size_t)t * H) * DK + i0);
-      wk = *reinterpret_cast<const u32x4v*>(kp + (row0 + (size_t)t * H) * DK + i0);
-    }
-    *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
-    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
-  }
-  if (tid < C) sm.g[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
-  __syncthreads();
   if (tid == 0) {
     float acc = sm.g[0];
     sm.gam[0] = acc;
@@ -896,7 +876,6 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
   }
   __syncthreads();
   if (tid < C) sm.Gam[tid] = expf(sm.gam[tid]);
-  // P = (Q K^T) .* D (lower, diagonal included), rounded to bf16
   for (int q2 = wave; q2 < 16; q2 += 4) {
     const int tm = q2 >> 2, tn = q2 & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -912,18 +891,21 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
     }
   }
   __syncthreads();
-  const size_t ps = (size_t)slot * H + h;
-  const uint8_t* sl = a.prod + ps * Sl::bytes;
+}
+
+// Chunkwise outputs of the 16-row tiles tm0 <= tm < tm1 of one chunk, this
+// wave's DV / 4 state columns: S = the chunk's start state (accumulator
+// tiles), sl = its product slot.  out(row, column, value) receives each.
+template <int DK, int DV, class Out>
+__device__ __forceinline__ void cmp_out_rows(const CmpOutLds<DK, DV>& sm, const mfma::f32x4 (&S)[DK / 16][DV / 64],
+                                             const uint8_t* sl, int tm0, int tm1, Out&& out) {
+  using namespace mfma;
+  typedef SlotB<DK, DV> Sl;
+  constexpr int NT = DV / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4;
+  const int jb0 = wave * NT;
   const u32x4* WF = reinterpret_cast<const u32x4*>(sl + Sl::oWF);
   const f32x4* UT = reinterpret_cast<const f32x4*>(sl + Sl::oU);
-  const float* B = a.bnd + ps * (size_t)DK * DV;
-  const int jb0 = wave * NT;
-  f32x4 S[DK / 16][NT];
-#pragma unroll
-  for (int im = 0; im < DK / 16; ++im)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      S[im][nt] = *reinterpret_cast<const f32x4*>(B + ((size_t)((jb0 + nt) * (DK / 16) + im) * 64 + lane) * 4);
   u32x4 Sb[DK / 32][NT];
 #pragma unroll
   for (int kb = 0; kb < DK / 32; ++kb)
@@ -947,9 +929,9 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
   for (int kb = 0; kb < C / 32; ++kb)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) Db[kb][nt] = frag_from_acc(Dl[2 * kb][nt], Dl[2 * kb + 1][nt]);
-  uint16_t* op = (uint16_t*)a.o;
 #pragma unroll
   for (int tm = 0; tm < C / 16; ++tm) {
+    if (tm < tm0 || tm >= tm1) continue;
     f32x4 O[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -972,10 +954,151 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tm + 4 * g + r;
-        if (t < n) op[(row0 + (size_t)t * H) * DV + 16 * (jb0 + nt) + lr] = Bf16::round(O[nt][r]);
-      }
+      for (int r = 0; r < 4; ++r) out(16 * tm + 4 * g + r, 16 * (jb0 + nt) + lr, O[nt][r]);
+  }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
+  typedef SlotB<DK, DV> Sl;
+  constexpr int NT = DV / 64;  // 16-column tiles per wave
+  __shared__ CmpOutLds<DK, DV> sm;
+  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
+  if (slot >= a.all_base[a.N]) return;
+  const int i = find_seq(a.all_base, a.N, slot);
+  const int c = slot - a.all_base[i];
+  const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint16_t* qp = (const uint16_t*)a.q;
+  const uint16_t* kp = (const uint16_t*)a.k;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  for (int idx = tid; idx < C * DK / 8; idx += 256) {
+    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
+    u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
+    if (t < n) {
+      wq = *reinterpret_cast<const u32x4v*>(qp + (row0 + (size_t)t * H) * DK + i0);
+      wk = *reinterpret_cast<const u32x4v*>(kp + (row0 + (size_t)t * H) * DK + i0);
+    }
+    *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
+    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
+  }
+  if (tid < C) sm.g[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
+  __syncthreads();
+  cmp_out_prepare(sm);
+  const size_t ps = (size_t)slot * H + h;
+  const float* B = a.bnd + ps * (size_t)DK * DV;
+  const int jb0 = wave * NT;
+  mfma::f32x4 S[DK / 16][NT];
+#pragma unroll
+  for (int im = 0; im < DK / 16; ++im)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      S[im][nt] = *reinterpret_cast<const mfma::f32x4*>(B + ((size_t)((jb0 + nt) * (DK / 16) + im) * 64 + lane) * 4);
+  uint16_t* op = (uint16_t*)a.o;
+  cmp_out_rows(sm, S, a.prod + ps * Sl::bytes, 0, C / 16, [&](int t, int col, float val) {
+    if (t < n) op[(row0 + (size_t)t * H) * DV + col] = Bf16::round(val);
+  });
+}
+
+// chunkwise-everywhere decode (comparator): every token recomputes the chunk
+// products of its partial chunk -- the cached tail, then the token, then zero
+// padding -- and takes its output from the chunk form on the cache's boundary
+// state, as the chunkwise prefill does for the same token.  When the token
+// completes the chunk, k_chain_resync_bf16 moves the boundary (s_run follows
+// it then; between boundaries this comparator leaves s_run alone).
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_cmp_cdec_local_bf16(const DecodeArgs a) {
+  __shared__ ChunkLdsB<DK, DV> sm;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  const int tl = a.tail_len[ch];
+  if ((unsigned)tl >= (unsigned)C) return;
+  const int tid = threadIdx.x;
+  const uint16_t* tk = (const uint16_t*)a.tail_k;
+  const uint16_t* tv = (const uint16_t*)a.tail_v;
+  const uint16_t* kp = (const uint16_t*)a.k;
+  const uint16_t* vp = (const uint16_t*)a.v;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  for (int idx = tid; idx < C * DK / 8; idx += 256) {
+    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
+    u32x4v w = {0u, 0u, 0u, 0u};
+    if (t < tl) w = *reinterpret_cast<const u32x4v*>(tk + (ch * C + t) * DK + i0);
+    if (t == tl) w = *reinterpret_cast<const u32x4v*>(kp + sh * DK + i0);
+    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
+  }
+  for (int idx = tid; idx < C * DV / 8; idx += 256) {
+    const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+    u32x4v w = {0u, 0u, 0u, 0u};
+    if (t < tl) w = *reinterpret_cast<const u32x4v*>(tv + (ch * C + t) * DV + j0);
+    if (t == tl) w = *reinterpret_cast<const u32x4v*>(vp + sh * DV + j0);
+    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) = w;
+  }
+  if (tid < C) {
+    const uint16_t* gs = tid < tl ? (const uint16_t*)a.tail_g : (const uint16_t*)a.g;
+    const uint16_t* bs = tid < tl ? (const uint16_t*)a.tail_beta : (const uint16_t*)a.beta;
+    const size_t r = tid < tl ? ch * C + tid : sh;
+    sm.g[tid] = tid <= tl ? Bf16::load(gs, r) : 0.f;
+    sm.beta[tid] = tid <= tl ? Bf16::load(bs, r) : 0.f;
+  }
+  __syncthreads();
+  chunk_local_bf16<DK, DV>(sm, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn + sh);
+  // append the token to the tail (row tl of the tail is read by no kernel of this step)
+  uint16_t* wk = (uint16_t*)a.tail_k + (ch * C + tl) * DK;
+  uint16_t* wv = (uint16_t*)a.tail_v + (ch * C + tl) * DV;
+  for (int e = tid; e < DK; e += 256) wk[e] = kp[sh * DK + e];
+  for (int e = tid; e < DV; e += 256) wv[e] = vp[sh * DV + e];
+  if (tid == 0) {
+    ((uint16_t*)a.tail_g)[ch * C + tl] = ((const uint16_t*)a.g)[sh];
+    ((uint16_t*)a.tail_beta)[ch * C + tl] = ((const uint16_t*)a.beta)[sh];
+  }
+}
+
+// its output row, then tail_len and the resynchronisation flag
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_cmp_cdec_out_bf16(const DecodeArgs a) {
+  constexpr int NT = DV / 64;
+  __shared__ CmpOutLds<DK, DV> sm;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  const int tl = a.tail_len[ch];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __syncthreads();  // every wave has read tail_len before it is rewritten below
+  if ((unsigned)tl >= (unsigned)C) {
+    if (tid == 0) a.flag[sh] = 0;
+    return;
+  }
+  const uint16_t* tk = (const uint16_t*)a.tail_k;
+  const uint16_t* qp = (const uint16_t*)a.q;
+  const uint16_t* kp = (const uint16_t*)a.k;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  for (int idx = tid; idx < C * DK / 8; idx += 256) {
+    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
+    u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
+    if (t < tl) wk = *reinterpret_cast<const u32x4v*>(tk + (ch * C + t) * DK + i0);
+    if (t == tl) {
+      wq = *reinterpret_cast<const u32x4v*>(qp + sh * DK + i0);
+      wk = *reinterpret_cast<const u32x4v*>(kp + sh * DK + i0);
+    }
+    *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
+    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
+  }
+  if (tid < C)
+    sm.g[tid] = tid < tl ? Bf16::load((const uint16_t*)a.tail_g, ch * C + tid)
+                         : (tid == tl ? Bf16::load((const uint16_t*)a.g, sh) : 0.f);
+  __syncthreads();
+  cmp_out_prepare(sm);
+  mfma::f32x4 S[DK / 16][NT];
+  load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * (size_t)DK * DV, wave * NT, lane);
+  uint16_t* op = (uint16_t*)a.o;
+  cmp_out_rows(sm, S, a.prod + sh * prod_slot_bytes(true, DK, DV), tl / 16, tl / 16 + 1,
+               [&](int t, int col, float val) {
+                 if (t == tl) op[sh * DV + col] = Bf16::round(val);
+               });
+  if (tid == 0) {
+    const bool full = (tl + 1 == C);
+    a.tail_len[ch] = full ? 0 : tl + 1;
+    a.flag[sh] = full ? 1 : 0;
   }
 }
 
@@ -1915,6 +2038,20 @@ struct CmpDecodeFn {
   }
 };
 
+template <class D, int DK, int DV>
+struct CmpChunkDecodeFn {
+  static gdn_status run(const DecodeArgs& a, hipStream_t st, const char* fn) {
+    if constexpr (!std::is_same<D, Bf16>::value) {
+      return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take bf16 inputs", fn);
+    } else {
+      hipLaunchKernelGGL((k_cmp_cdec_local_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_cmp_cdec_out_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / (16 * kResyncNT)), dim3(64), 0, st, a);
+      return launch_status(fn);
+    }
+  }
+};
+
 struct FwdBwdLayout {
   PrefillLayout pre;
   size_t s_bnd, s_run, tail_k, tail_v, tail_g, tail_b, tail_len, bgamn, bslots, slot, total;
@@ -2437,6 +2574,63 @@ extern "C" gdn_status gdn_cmp_decode_step(const gdn_cpr_shape* shape, int32_t nu
   ca.N = num_seqs;
   ca.H = shape->num_heads;
   return dispatch<CmpDecodeFn>(*shape, ca, (hipStream_t)stream, fn);
+}
+
+extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                                                const void* k, const void* v, const void* g, const void* beta,
+                                                const gdn_cpr_cache* cache, void* o, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_cmp_chunk_decode_step";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (shape->dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take bf16 inputs", fn);
+  if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(g, "g");
+  CHECK_PTR(beta, "beta");
+  CHECK_PTR(o, "o");
+  CHECK_PTR(cache->s_bnd, "cache.s_bnd");
+  CHECK_PTR(cache->s_run, "cache.s_run");
+  CHECK_PTR(cache->tail_k, "cache.tail_k");
+  CHECK_PTR(cache->tail_v, "cache.tail_v");
+  CHECK_PTR(cache->tail_g, "cache.tail_g");
+  CHECK_PTR(cache->tail_beta, "cache.tail_beta");
+  CHECK_PTR(cache->tail_len, "cache.tail_len");
+  CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
+  const DecodeLayout L = decode_layout(*shape, num_seqs);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  char* ws = (char*)workspace;
+  DecodeArgs a;
+  a.slot = cache->slot_index;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.s_bnd = cache->s_bnd;
+  a.s_run = cache->s_run;
+  a.tail_k = cache->tail_k;
+  a.tail_v = cache->tail_v;
+  a.tail_g = cache->tail_g;
+  a.tail_beta = cache->tail_beta;
+  a.tail_len = cache->tail_len;
+  a.o = o;
+  a.flag = (int32_t*)(ws + L.flag);
+  a.prod = (uint8_t*)(ws + L.prod);
+  a.gamn = (float*)(ws + L.gamn);
+  a.N = num_seqs;
+  a.H = shape->num_heads;
+  return dispatch<CmpChunkDecodeFn>(*shape, a, (hipStream_t)stream, fn);
 }
 
 extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) {

@@ -254,6 +254,27 @@ gdn_status gdn_cmp_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, con
                                void* stream);
 
 /*
+ * gdn_cmp_chunk_decode_step: the chunkwise-everywhere decode (the pages'
+ * chunkwise decode column, English page, CPR table).  Each token recomputes
+ * the chunk products of its partial chunk -- the cached tail, the token, zero
+ * padding -- and takes its output from the chunk form on cache->s_bnd, so it
+ * equals, bit for bit, the output gdn_cmp_prefill(GDN_CMP_CHUNKWISE) gives
+ * the same token; the token is appended to the tail.  A token that completes
+ * its chunk moves s_bnd (and s_run) to the next boundary by the same chain
+ * step as the prefill, and empties the tail.  The cache is the CPR cache of
+ * gdn_cpr_prefill, whose s_bnd and tail are what the chunkwise prefill
+ * computes for the same tokens (the chunk products and the chain are shared);
+ * between boundaries this call leaves s_run as it is, so the cache must not
+ * then go on through gdn_cpr_decode_step.  Arguments, layouts, slot_index
+ * and workspace (gdn_cpr_workspace_size with GDN_OP_DECODE) as
+ * gdn_cpr_decode_step; a row with tail_len outside 0..C-1 is left untouched.
+ */
+gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                                     const void* k, const void* v, const void* g, const void* beta,
+                                     const gdn_cpr_cache* cache, void* o, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * Measurement hook (the pages report per-stage timings of the layer, English
  * page, CPR table).  events points to an array of hipEvent_t handles owned by
  * the caller, or NULL to switch the hook off (the default).  While set, on

@@ -109,3 +109,44 @@ def test_cpr_agrees_where_native_mixed_does_not():
                             gdn.alloc_workspace(db.shape, N, 0, gdn.GDN_OP_DECODE))
     torch.cuda.synchronize()
     assert np.array_equal(bits(o_dec), bits(o_full[rows]))
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64)])
+def test_chunkwise_decode_equals_chunkwise_prefill(dk, dv):
+    """Chunkwise everywhere: each decoded token's output is the chunkwise
+    prefill's output for it, bit for bit, across chunk boundaries; at a
+    length that is a multiple of C the boundary state equals the prefill's
+    final state.  Starts from the CPR prefill's cache (same boundary and tail)."""
+    note(f"chunkwise-everywhere decode dk={dk} dv={dv}")
+    pre = np.array([62, 0, 63, 64, 126, 190])
+    m = 66
+    full = pre + m  # 128, 66, 129, 130, 192, 256
+    b = make_batch(732, list(full), 2, dk, dv, dtype="bf16", h0_std=0.1)
+    db = DevBatch(b)
+    N = b.num_seqs
+    o_full, st_full = cmp_prefill(db, gdn.GDN_CMP_CHUNKWISE)
+    dbp = DevBatch(b.truncate(list(pre)))
+    cache = gdn.alloc_cache(db.shape, N)
+    o_p = torch.empty((max(dbp.b.total_tokens, 1), 2, dv), dtype=torch.bfloat16, device=DEV)
+    gdn.gdn_cpr_prefill(db.shape, dbp.q, dbp.k, dbp.v, dbp.g, dbp.beta, dbp.cu, db.h0, cache, o_p,
+                        gdn.alloc_workspace(db.shape, N, dbp.b.total_tokens, gdn.GDN_OP_PREFILL))
+    ws = gdn.alloc_workspace(db.shape, N, 0, gdn.GDN_OP_DECODE)
+    base = b.cu_seqlens[:-1].astype(np.int64) + pre
+    o_dec = torch.empty((m, N, 2, dv), dtype=torch.bfloat16, device=DEV)
+    for s in range(m):
+        rows = torch.from_numpy(base + s).to(DEV)
+        x = {n: getattr(db, n)[rows].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        gdn.gdn_cmp_chunk_decode_step(db.shape, x["q"], x["k"], x["v"], x["g"], x["beta"], cache, o_dec[s], ws)
+    torch.cuda.synchronize()
+    rows_all = torch.from_numpy((base[None, :] + np.arange(m)[:, None]).reshape(-1)).to(DEV)
+    ref = o_full[rows_all].view(m, N, 2, dv)
+    assert np.array_equal(bits(o_dec), bits(ref))
+    for i in range(N):
+        if full[i] % 64 == 0:
+            assert np.array_equal(bits(cache.s_bnd[i]), bits(st_full[i])), i
+            assert int(cache.tail_len[i, 0]) == 0
+        else:
+            assert int(cache.tail_len[i, 0]) == full[i] % 64
+    o_ref, _ = oracle.recurrent_forward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0)
+    dec_rows = (base[None, :] + np.arange(m)[:, None]).reshape(-1)
+    assert float(np.max(np.abs(as_f64(o_dec).reshape(m * N, 2, dv) - o_ref[dec_rows]))) <= 2e-2

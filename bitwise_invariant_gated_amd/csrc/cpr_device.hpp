@@ -48,6 +48,9 @@ struct Bf16 {
   __device__ static __forceinline__ float elem(const u32x8& w, int e) {
     return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
   }
+  // the element's bits as loaded, decoded later (load() = from_bits(load_bits()))
+  __device__ static __forceinline__ uint32_t load_bits(const T* p, size_t i) { return p[i]; }
+  __device__ static __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
 };
 
 struct F32 {
@@ -56,6 +59,8 @@ struct F32 {
   __device__ static __forceinline__ float load(const T* p, size_t i) { return p[i]; }
   __device__ static __forceinline__ void store(T* p, size_t i, float x) { p[i] = x; }
   __device__ static __forceinline__ float elem(const u32x8& w, int e) { return __uint_as_float(w[e]); }
+  __device__ static __forceinline__ uint32_t load_bits(const T* p, size_t i) { return __float_as_uint(p[i]); }
+  __device__ static __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b); }
 };
 
 // Hides a pointer's value from the optimiser so that each use issues its own
@@ -221,20 +226,64 @@ __device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf
   asm volatile("s_nop 1" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
                "v"(qf[7]));
   float o0 = 0.f, o1 = 0.f;
-  static_for<0, DK / 8>([&](auto nc) {
-    constexpr int n = decltype(nc)::value;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int i = 8 * n + e;
-      // both updates first: a state register is never read by the very next
-      // instruction that follows its write (the per-accumulator order is unchanged)
+  // software-pipelined: the updates of elements 2j, 2j+1 are followed by the
+  // output terms of elements 2j-2, 2j-1, so every state register and output
+  // accumulator is read at least four instructions after its last write and
+  // the DPP hazard needs no wait (each accumulator still takes its terms in
+  // ascending order)
+  static_for<0, DK / 2 + 1>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < DK / 2) {
+      constexpr int i = 2 * j, n = i / 8, e = i % 8;
       fmac_bcast<n>(s[i], kf[e], u);
       fmac_bcast<n>(s[i + 1], kf[e + 1], u);
+    }
+    if constexpr (j >= 1) {
+      constexpr int i = 2 * j - 2, n = i / 8, e = i % 8;
       fmac_bcast<n>(o0, qf[e], s[i]);
       fmac_bcast<n>(o1, qf[e + 1], s[i + 1]);
     }
   });
   return o0 + o1;
+}
+
+// The scan's loop over tokens t = 0 .. n-1 (n >= 1) of one stretch of a
+// sequence, token t at row row0 + t * H: output o_t to column col of row
+// (row0 + t * H) of o, state s updated in place; alpha_l / beta_l hold token
+// t's decay and beta in lane t.  k, q and v of token t+1 are fetched into the
+// other of two register buffers as token t starts (no copies between them).
+// Every fetch is issued (its index is clamped to token n-1), so the wait
+// before a token's first use of its operands covers that token's loads only,
+// and v stays undecoded until then.
+template <class D, int DK, int DV>
+__device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T* __restrict__ kp,
+                                            const typename D::T* __restrict__ qp, const typename D::T* __restrict__ vp,
+                                            typename D::T* __restrict__ op, size_t row0, int H, int n, int col,
+                                            int lane, float alpha_l, float beta_l) {
+  KQRaw<D> r0, r1;
+  uint32_t v0, v1;
+  auto fetch = [&](KQRaw<D>& r, uint32_t& vb, int t) {
+    const size_t row = row0 + (size_t)min(t, n - 1) * H;
+    load_kq<D, DK>(r, kp + row * DK, qp + row * DK, lane);
+    vb = D::load_bits(vp + row * DV, col);
+  };
+  auto step = [&](KQRaw<D>& r, uint32_t& vb, KQRaw<D>& rn, uint32_t& vn, int t) {
+    float kf[8], qf[8];
+    unpack_kq<D>(r, kf, qf);
+    uint32_t vbits = vb;
+    asm volatile("" : "+v"(vbits));  // decode v here, not next to its load
+    const float vcur = D::from_bits(vbits);
+    fetch(rn, vn, t + 1);
+    const float out = token_step_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
+    D::store(op + (row0 + (size_t)t * H) * DV, col, out);
+  };
+  fetch(r0, v0, 0);
+  int t = 0;
+  for (; t + 1 < n; t += 2) {
+    step(r0, v0, r1, v1, t);
+    step(r1, v1, r0, v0, t + 1);
+  }
+  if (t < n) step(r0, v0, r1, v1, t);
 }
 
 // ---------------------------------------------------------------------------

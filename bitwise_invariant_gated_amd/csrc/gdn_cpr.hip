@@ -544,25 +544,7 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
-  T* op = (T*)a.o;
-  // k, q and v of token t+1 are loaded while token t computes
-  KQRaw<D> raw;
-  size_t row = tok0 * H + h;
-  load_kq<D, DK>(raw, kp + row * DK, qp + row * DK, lane);
-  float vv = D::load(vp, row * DV + col);
-  for (int t = 0; t < n; ++t) {
-    float kf[8], qf[8];
-    unpack_kq<D>(raw, kf, qf);
-    const float vcur = vv;
-    const size_t next = row + H;
-    if (t + 1 < n) {
-      load_kq<D, DK>(raw, kp + next * DK, qp + next * DK, lane);
-      vv = D::load(vp, next * DV + col);
-    }
-    const float out = token_step_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
-    D::store(op, row * DV + col, out);
-    row = next;
-  }
+  scan_tokens<D, DK, DV>(s, kp, qp, vp, (T*)a.o, tok0 * H + h, H, n, col, lane, alpha_l, beta_l);
   const int nall = (L + C - 1) / C;
   if (c == nall - 1 && (L % C) != 0) {
     // last, partial chunk: its end state is the running state, its tokens the tail
@@ -770,23 +752,7 @@ __global__ __launch_bounds__(64, 3) void k_cmp_rec_prefill(const CmpArgs a) {
       alpha_l = decay_of(D::load(gp, r));
       beta_l = D::load(bp, r);
     }
-    KQRaw<D> raw;
-    size_t row = tok0 * H + h;
-    load_kq<D, DK>(raw, kp + row * DK, qp + row * DK, lane);
-    float vv = D::load(vp, row * DV + col);
-    for (int t = 0; t < n; ++t) {
-      float kf[8], qf[8];
-      unpack_kq<D>(raw, kf, qf);
-      const float vcur = vv;
-      const size_t next = row + H;
-      if (t + 1 < n) {
-        load_kq<D, DK>(raw, kp + next * DK, qp + next * DK, lane);
-        vv = D::load(vp, next * DV + col);
-      }
-      const float out = token_step_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
-      D::store(op, row * DV + col, out);
-      row = next;
-    }
+    scan_tokens<D, DK, DV>(s, kp, qp, vp, op, tok0 * H + h, H, n, col, lane, alpha_l, beta_l);
   }
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) a.state[sh * SS + (size_t)ii * DV + col] = s[ii];

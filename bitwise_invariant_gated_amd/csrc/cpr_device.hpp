@@ -510,18 +510,22 @@ struct SlotB {
 //   U   = TB V                         (MFMA bf16; fp32 tiles)
 //   KtT = bf16(e_r * K[r][i])
 //   Gamma_n = Gamma_{C-1}
+// 53,248 bytes for d_k = d_v = 128: three work-groups fit in one CU's LDS.
 template <int DK, int DV>
 struct alignas(16) ChunkLdsB {
-  static constexpr int kLK = DK + 8, kLV = DV + 8, kLA = kChunk + 4, kLT = kChunk + 8;
-  uint16_t K[kChunk][kLK];   // row-major K
-  uint16_t V[kChunk][kLV];   // row-major V
-  float A[kChunk][kLA];      // A[t][s] = L[t][s] (s < t); A[s][t] = X[t][s] (s <= t)
-  uint16_t TG[kChunk][kLT];  // bf16(T diag(Gamma)), row-major
-  uint16_t TB[kChunk][kLT];  // bf16(T), row-major
-  float g[kChunk], beta[kChunk], gam[kChunk], Gam[kChunk], e[kChunk];
+  static constexpr int kLK = DK + 8, kLV = DV + 8, kLA = kChunk + 4, kLT = kChunk + 4;
+  uint16_t K[kChunk][kLK];  // row-major K
+  uint16_t V[kChunk][kLV];  // row-major V
+  // A[t][s] = L[t][s] (s < t); A[s][t] = X[t][s] (s <= t).  Once X is read,
+  // the same bytes hold bf16(T diag(Gamma)) and bf16(T), row-major (TG, TB).
+  float A[kChunk][kLA];
+  float beta[kChunk], gam[kChunk], Gam[kChunk], e[kChunk];  // gam holds g until the cumsum
+  __device__ uint16_t (*TG())[kLT] { return reinterpret_cast<uint16_t (*)[kLT]>(&A[0][0]); }
+  __device__ uint16_t (*TB())[kLT] { return reinterpret_cast<uint16_t (*)[kLT]>(&A[0][0]) + kChunk; }
+  static_assert(2 * kChunk * kLT * 2 <= kChunk * kLA * 4, "TG and TB fit in A's bytes");
 };
 
-// Stage one chunk (bf16 rows) into LDS: K and V row-major, g, beta.
+// Stage one chunk (bf16 rows) into LDS: K and V row-major, g (into gam), beta.
 // Row t of k starts at k + (k_row0 + t * k_stride) * DK (likewise v); g and
 // beta at gb0 + t * gb_stride.
 template <int DK, int DV>
@@ -544,7 +548,7 @@ __device__ __forceinline__ void stage_chunk_bf16(ChunkLdsB<DK, DV>& sm, const ui
         *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
   }
   for (int t = tid; t < kChunk; t += nt) {
-    sm.g[t] = Bf16::load(g, gb0 + (size_t)t * gb_stride);
+    sm.gam[t] = Bf16::load(g, gb0 + (size_t)t * gb_stride);
     sm.beta[t] = Bf16::load(beta, gb0 + (size_t)t * gb_stride);
   }
   __syncthreads();
@@ -629,31 +633,50 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
   static_assert(DK % 32 == 0 && DV % 32 == 0, "head dims are multiples of 32");
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  if (tid == 0) {
-    float acc = sm.g[0];
-    sm.gam[0] = acc;
+  // gamma = left-to-right fp32 cumsum of g (wave 0, in registers), while
+  // waves 1-3 form the 10 tiles of G = K K^T on or below the diagonal
+  // (wave w: tiles w - 1, w + 2, w + 5, w + 8 of the row-major order)
+  f32x4 Gt[4];
+  if (wave == 0) {
+    const float gl = sm.gam[lane];
+    float acc = lane_bcast(gl, 0), mine = acc;
     for (int t = 1; t < C; ++t) {
-      acc = acc + sm.g[t];
-      sm.gam[t] = acc;
+      acc = acc + lane_bcast(gl, t);
+      if (lane == t) mine = acc;
+    }
+    sm.gam[lane] = mine;
+    sm.Gam[lane] = expf(mine);
+    sm.e[lane] = expf(acc - mine);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave - 1 + 3 * j;
+      Gt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (q < 10) {
+        const int tm = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+        const int tn = q - tm * (tm + 1) / 2;
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+          Gt[j] = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g),
+                      Gt[j]);
+      }
     }
   }
   __syncthreads();
-  if (tid < C) {
-    sm.Gam[tid] = expf(sm.gam[tid]);
-    sm.e[tid] = expf(sm.gam[C - 1] - sm.gam[tid]);
-  }
-  // L from G = K K^T: the 10 tiles on or below the diagonal
-  for (int q = wave; q < 10; q += 4) {
-    const int tm = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
-    const int tn = q - tm * (tm + 1) / 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // L[t][s] = (beta_t exp(gamma_t - gamma_s)) G[t][s], s < t
+  if (wave > 0) {
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      acc = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), acc);
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave - 1 + 3 * j;
+      if (q < 10) {
+        const int tm = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+        const int tn = q - tm * (tm + 1) / 2;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
-      if (s < t) sm.A[t][s] = (sm.beta[t] * expf(sm.gam[t] - sm.gam[s])) * acc[r];
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
+          if (s < t) sm.A[t][s] = (sm.beta[t] * expf(sm.gam[t] - sm.gam[s])) * Gt[j][r];
+        }
+      }
     }
   }
   __syncthreads();
@@ -675,12 +698,32 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
   }
   __syncthreads();
   inverse_below_diag(sm.A, wave, lane);
-  // T = X diag(beta) -> TB, TG
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int r = idx / C, t = idx % C;
-    const float T = (r <= t) ? sm.A[r][t] * sm.beta[r] : 0.f;
-    sm.TB[t][r] = Bf16::round(T);
-    sm.TG[t][r] = Bf16::round(T * sm.Gam[r]);
+  // T = X diag(beta) -> TB = bf16(T), TG = bf16(T diag(Gamma)), written over
+  // A once every thread holds its part of X: thread items (t, 8 columns r0..)
+  float Tv[C * C / 8 / 256][8];
+#pragma unroll
+  for (int m = 0; m < C * C / 8 / 256; ++m) {
+    const int item = tid + 256 * m, t = item >> 3, r0 = (item & 7) * 8;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) {
+      const int r = r0 + e2;
+      Tv[m][e2] = (r <= t) ? sm.A[r][t] * sm.beta[r] : 0.f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < C * C / 8 / 256; ++m) {
+    const int item = tid + 256 * m, t = item >> 3, r0 = (item & 7) * 8;
+    u32x2 b[2], gg[2];
+#pragma unroll
+    for (int e2 = 0; e2 < 8; e2 += 2) {
+      b[e2 >> 2][(e2 >> 1) & 1] = pack2(Tv[m][e2], Tv[m][e2 + 1]);
+      gg[e2 >> 2][(e2 >> 1) & 1] = pack2(Tv[m][e2] * sm.Gam[r0 + e2], Tv[m][e2 + 1] * sm.Gam[r0 + e2 + 1]);
+    }
+    *reinterpret_cast<u32x2*>(&sm.TB()[t][r0]) = b[0];
+    *reinterpret_cast<u32x2*>(&sm.TB()[t][r0 + 4]) = b[1];
+    *reinterpret_cast<u32x2*>(&sm.TG()[t][r0]) = gg[0];
+    *reinterpret_cast<u32x2*>(&sm.TG()[t][r0 + 4]) = gg[1];
   }
   __syncthreads();
   // Wneg fragments: W^T tiles (2 p, tm) and (2 p + 1, tm) form fragment (p, tm)
@@ -696,7 +739,7 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb) {
-        const u32x4 tg = frag_row(&sm.TG[16 * tm + lr][0], 32 * kb, g);
+        const u32x4 tg = frag_row(&sm.TG()[16 * tm + lr][0], 32 * kb, g);
         acc[0] = mma(Kt[0][kb], tg, acc[0]);
         acc[1] = mma(Kt[1][kb], tg, acc[1]);
       }
@@ -718,7 +761,7 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb) {
-        const u32x4 tb = frag_row(&sm.TB[16 * tm + lr][0], 32 * kb, g);
+        const u32x4 tb = frag_row(&sm.TB()[16 * tm + lr][0], 32 * kb, g);
         acc[0] = mma(tb, Vt[0][kb], acc[0]);
         acc[1] = mma(tb, Vt[1][kb], acc[1]);
       }

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void k_chunk_local_resync(const DecodeArgs a) 
 
 // bf16 path: MFMA chunk products
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_chunk_local_prefill_bf16(const PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void k_chunk_local_prefill_bf16(const PrefillArgs a) {
   __shared__ ChunkLdsB<DK, DV> sm;
   const int f = blockIdx.x, h = blockIdx.y;
   const int N = a.N, H = a.H;
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void k_chunk_local_prefill_bf16(const PrefillA
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_chunk_local_resync_bf16(const DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void k_chunk_local_resync_bf16(const DecodeArgs a) {
   __shared__ ChunkLdsB<DK, DV> sm;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
@@ -782,7 +782,7 @@ __global__ __launch_bounds__(DV) void k_cmp_rec_decode(const CmpArgs a) {
 // chunkwise: chunk products of every chunk slot, a partial chunk padded with
 // k = v = 0, g = beta = 0 (identity steps)
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_cmp_chunk_local_bf16(const CmpArgs a) {
+__global__ __launch_bounds__(256, 3) void k_cmp_chunk_local_bf16(const CmpArgs a) {
   typedef SlotB<DK, DV> Sl;
   __shared__ ChunkLdsB<DK, DV> sm;
   const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
@@ -808,7 +808,7 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_local_bf16(const CmpArgs a) {
     *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) = w;
   }
   if (tid < C) {
-    sm.g[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
+    sm.gam[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
     sm.beta[tid] = tid < n ? Bf16::load((const uint16_t*)a.beta, row0 + (size_t)tid * H) : 0.f;
   }
   __syncthreads();
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
 // completes the chunk, k_chain_resync_bf16 moves the boundary (s_run follows
 // it then; between boundaries this comparator leaves s_run alone).
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_cmp_cdec_local_bf16(const DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void k_cmp_cdec_local_bf16(const DecodeArgs a) {
   __shared__ ChunkLdsB<DK, DV> sm;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
@@ -1004,7 +1004,7 @@ __global__ __launch_bounds__(256) void k_cmp_cdec_local_bf16(const DecodeArgs a)
     const uint16_t* gs = tid < tl ? (const uint16_t*)a.tail_g : (const uint16_t*)a.g;
     const uint16_t* bs = tid < tl ? (const uint16_t*)a.tail_beta : (const uint16_t*)a.beta;
     const size_t r = tid < tl ? ch * C + tid : sh;
-    sm.g[tid] = tid <= tl ? Bf16::load(gs, r) : 0.f;
+    sm.gam[tid] = tid <= tl ? Bf16::load(gs, r) : 0.f;
     sm.beta[tid] = tid <= tl ? Bf16::load(bs, r) : 0.f;
   }
   __syncthreads();

@@ -23,7 +23,8 @@ Reproducibility: sequence lengths come from a generator seeded with
 sequence's values do not depend on which other sequences share its batch.
 
 Layouts (packed varlen batch of N sequences, T tokens in total):
-  q, k [T, H, d_k]; v, dO [T, H, d_v]; g, beta [T, H];
+  q, k [T, H_k, d_k] (H_k = H unless fewer key heads are asked for; H_k
+  divides H); v, dO [T, H, d_v]; g, beta [T, H];
   cu_seqlens int32 [N + 1]; h0 [N, H, d_k, d_v] (the state S = M^T, key
   dimension first).
 """
@@ -90,6 +91,11 @@ class Batch:
     beta: np.ndarray
     h0: Optional[np.ndarray] = None  # fp32 [N,H,d_k,d_v] or None (zero state)
     d_o: Optional[np.ndarray] = None  # [T,H,d_v] or None
+    num_key_heads: int = 0  # heads of q and k (0: num_heads)
+
+    def __post_init__(self):
+        if self.num_key_heads == 0:
+            self.num_key_heads = self.num_heads
 
     @property
     def num_seqs(self) -> int:
@@ -124,7 +130,7 @@ class Batch:
         h0 = None if self.h0 is None else np.ascontiguousarray(self.h0[seqs])
         return Batch(self.dtype, self.num_heads, self.d_k, self.d_v, cu,
                      cat(self.q), cat(self.k), cat(self.v), cat(self.g), cat(self.beta),
-                     h0, cat(self.d_o))
+                     h0, cat(self.d_o), self.num_key_heads)
 
     def truncate(self, lengths: Sequence[int]) -> "Batch":
         """Keep the first lengths[i] tokens of every sequence i."""
@@ -142,7 +148,7 @@ class Batch:
 
         return Batch(self.dtype, self.num_heads, self.d_k, self.d_v, cu,
                      take(self.q), take(self.k), take(self.v), take(self.g), take(self.beta),
-                     None if self.h0 is None else self.h0.copy(), take(self.d_o))
+                     None if self.h0 is None else self.h0.copy(), take(self.d_o), self.num_key_heads)
 
 
 def draw_lengths(seed: int, num_seqs: int, low: int, high: int) -> np.ndarray:
@@ -158,15 +164,20 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
 
 def make_batch(seed: int, lengths: Sequence[int], num_heads: int, d_k: int, d_v: int,
                dtype: str = "bf16", h0_std: Optional[float] = None,
-               with_do: bool = False) -> Batch:
-    """Draw a packed batch; sequence i uses the (seed, i + 1) stream."""
+               with_do: bool = False, num_key_heads: Optional[int] = None) -> Batch:
+    """Draw a packed batch; sequence i uses the (seed, i + 1) stream.
+
+    num_key_heads: heads of q and k (default num_heads; must divide it)."""
     if dtype not in ("f32", "bf16"):
         raise ValueError(dtype)
     lengths = [int(n) for n in lengths]
     H = num_heads
+    Hk = H if num_key_heads is None else int(num_key_heads)
+    if Hk <= 0 or H % Hk != 0:
+        raise ValueError("num_key_heads must divide num_heads")
     T = int(sum(lengths))
-    q = np.empty((T, H, d_k), np.float32)
-    k = np.empty((T, H, d_k), np.float32)
+    q = np.empty((T, Hk, d_k), np.float32)
+    k = np.empty((T, Hk, d_k), np.float32)
     v = np.empty((T, H, d_v), np.float32)
     g = np.empty((T, H), np.float32)
     beta = np.empty((T, H), np.float32)
@@ -177,8 +188,8 @@ def make_batch(seed: int, lengths: Sequence[int], num_heads: int, d_k: int, d_v:
     for i, n in enumerate(lengths):
         rng = np.random.default_rng([seed, i + 1])
         sl = slice(pos, pos + n)
-        q[sl] = rnd(_unit_rows(rng.standard_normal((n, H, d_k), dtype=np.float32)))
-        k[sl] = rnd(_unit_rows(rng.standard_normal((n, H, d_k), dtype=np.float32)))
+        q[sl] = rnd(_unit_rows(rng.standard_normal((n, Hk, d_k), dtype=np.float32)))
+        k[sl] = rnd(_unit_rows(rng.standard_normal((n, Hk, d_k), dtype=np.float32)))
         v[sl] = rnd(rng.standard_normal((n, H, d_v), dtype=np.float32))
         zb = rng.standard_normal((n, H), dtype=np.float32)
         beta[sl] = rnd((1.0 / (1.0 + np.exp(-zb.astype(np.float64)))).astype(np.float32))
@@ -191,7 +202,7 @@ def make_batch(seed: int, lengths: Sequence[int], num_heads: int, d_k: int, d_v:
         pos += n
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
-    return Batch(dtype, H, d_k, d_v, cu, q, k, v, g, beta, h0, d_o)
+    return Batch(dtype, H, d_k, d_v, cu, q, k, v, g, beta, h0, d_o, Hk)
 
 
 # The five workloads the layer is exercised on.  Each entry: seed, sequence

@@ -17,6 +17,7 @@ Modules:
   chunkwise  -- the chunk (WY/UT) form, written separately, same results
   backward   -- analytic reverse-mode gradient of the recurrence
   fd         -- central finite differences of a scalar loss, for pinning
+  heads      -- key/query heads shared by groups of value heads
 
 Notation (one head): state M (d_v x d_k), key/query k, q (d_k), value v (d_v),
 log-decay g <= 0 with alpha = exp(g), write strength beta in (0, 1).
@@ -33,6 +34,7 @@ from .recurrent import recurrent_forward, token_step
 from .chunkwise import chunkwise_forward, chunk_products
 from .backward import recurrent_backward
 from .fd import fd_gradients, loss_value
+from .heads import expand_key_heads, sum_key_heads
 
 __all__ = [
     "recurrent_forward",
@@ -42,4 +44,6 @@ __all__ = [
     "recurrent_backward",
     "fd_gradients",
     "loss_value",
+    "expand_key_heads",
+    "sum_key_heads",
 ]

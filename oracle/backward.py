@@ -26,6 +26,7 @@ from typing import Optional
 
 import numpy as np
 
+from .heads import expand_key_heads, sum_key_heads
 from .recurrent import token_step
 
 
@@ -34,12 +35,15 @@ def recurrent_backward(q, k, v, g, beta, cu_seqlens, h0: Optional[np.ndarray],
                        checkpoint: int = 64):
     """Gradients of L w.r.t. (q, k, v, g, beta, h0).
 
-    Returns dict with dq, dk [T,H,d_k]; dv [T,H,d_v]; dg, dbeta [T,H];
-    dh0 [N,H,d_k,d_v] (S layout); all float64.
+    Returns dict with dq, dk [T,H_k,d_k] (the shapes of q, k; a key head
+    shared by several value heads receives the sum of their gradients, see
+    heads.py); dv [T,H,d_v]; dg, dbeta [T,H]; dh0 [N,H,d_k,d_v] (S layout);
+    all float64.
     """
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
+    num_key_heads = np.asarray(q).shape[1]
+    q = expand_key_heads(q, v.shape[1])
+    k = expand_key_heads(k, v.shape[1])
     g = np.asarray(g, np.float64)
     beta = np.asarray(beta, np.float64)
     d_o = np.asarray(d_o, np.float64)
@@ -99,4 +103,5 @@ def recurrent_backward(q, k, v, g, beta, cu_seqlens, h0: Optional[np.ndarray],
                 dg[r] = a * np.sum(dMp * Mprev, axis=(1, 2))
                 dM = a[:, None, None] * dMp
         dh0[i] = np.swapaxes(dM, -1, -2)
-    return dict(dq=dq, dk=dkk, dv=dvv, dg=dg, dbeta=db, dh0=dh0)
+    return dict(dq=sum_key_heads(dq, num_key_heads), dk=sum_key_heads(dkk, num_key_heads), dv=dvv, dg=dg,
+                dbeta=db, dh0=dh0)

@@ -33,6 +33,8 @@ from typing import Optional
 
 import numpy as np
 
+from .heads import expand_key_heads
+
 
 def chunk_products(K: np.ndarray, V: np.ndarray, g: np.ndarray, beta: np.ndarray):
     """Chunk-local products for one head: (W, U, Ktilde, Gamma_n, T, D, Gamma).
@@ -66,9 +68,9 @@ def chunkwise_forward(q, k, v, g, beta, cu_seqlens, h0: Optional[np.ndarray] = N
     return_boundaries also a list (per sequence) of [n_chunks+1, H, d_k, d_v]
     boundary states (S layout), index 0 = initial state.
     """
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
+    q = expand_key_heads(q, v.shape[1])  # q, k may have fewer heads (heads.py)
+    k = expand_key_heads(k, v.shape[1])
     g = np.asarray(g, np.float64)
     beta = np.asarray(beta, np.float64)
     cu = np.asarray(cu_seqlens, np.int64)

@@ -23,6 +23,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
+from .heads import expand_key_heads
+
 
 def token_step(M: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
                g: np.ndarray, beta: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
@@ -44,15 +46,15 @@ def recurrent_forward(q, k, v, g, beta, cu_seqlens, h0: Optional[np.ndarray] = N
                       return_all_states: bool = False):
     """Run the recurrence over a packed varlen batch in float64.
 
-    q, k [T, H, d_k]; v [T, H, d_v]; g, beta [T, H]; cu_seqlens [N+1];
-    h0 [N, H, d_k, d_v] or None.
+    q, k [T, H_k, d_k] (H_k divides H; see heads.py); v [T, H, d_v];
+    g, beta [T, H]; cu_seqlens [N+1]; h0 [N, H, d_k, d_v] or None.
     Returns (o [T, H, d_v] float64, hT [N, H, d_k, d_v] float64).
     If return_all_states, also a list (per sequence) of [L+1, H, d_v, d_k]
     M-form states (index 0 = initial state).
     """
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
+    q = expand_key_heads(q, v.shape[1])
+    k = expand_key_heads(k, v.shape[1])
     g = np.asarray(g, np.float64)
     beta = np.asarray(beta, np.float64)
     cu = np.asarray(cu_seqlens, np.int64)

@@ -341,6 +341,60 @@ def test_backward_matches_finite_differences():
 
 
 # ----------------------------------------------------------------------------
+# key and query heads shared by groups of value heads (oracle/heads.py)
+def test_shared_key_heads_equal_one_head_runs():
+    """Value head h of a grouped batch equals a one-head run on its own v, g,
+    beta and state with key head h // G's query and key rows; the chunk form
+    agrees with the token form on the grouped batch."""
+    b = make_batch(51, [13, 40, 7], 6, 5, 3, dtype="f32", h0_std=0.5, num_key_heads=2)  # G = 3
+    assert b.q.shape[1] == 2 and b.v.shape[1] == 6
+    o, hT = oracle.recurrent_forward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0)
+    oc, hc = oracle.chunkwise_forward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0, chunk=8)
+    assert np.max(np.abs(oc - o)) < 1e-12 and np.max(np.abs(hc - hT)) < 1e-12
+    for h in range(6):
+        j = h // 3
+        oh, hh = oracle.recurrent_forward(b.q[:, j:j + 1], b.k[:, j:j + 1], b.v[:, h:h + 1], b.g[:, h:h + 1],
+                                          b.beta[:, h:h + 1], b.cu_seqlens, b.h0[:, h:h + 1])
+        assert np.max(np.abs(oh[:, 0] - o[:, h])) < 1e-13, h
+        assert np.max(np.abs(hh[:, 0] - hT[:, h])) < 1e-13, h
+
+
+def test_shared_key_head_gradients_sum_over_the_group():
+    """dq and dk of a shared key head are the sums of the one-head gradients
+    of its value heads; every per-value-head gradient is that head's own."""
+    b = make_batch(52, [9, 12], 4, 4, 3, dtype="f32", h0_std=0.5, with_do=True, num_key_heads=2)
+    d_hT = np.random.default_rng(6).standard_normal(b.h0.shape)
+    ref = oracle.recurrent_backward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0, b.d_o, d_hT, checkpoint=4)
+    assert ref["dq"].shape == b.q.shape and ref["dk"].shape == b.k.shape
+    for j in range(2):
+        dq_sum = np.zeros_like(ref["dq"][:, j])
+        dk_sum = np.zeros_like(ref["dk"][:, j])
+        for h in (2 * j, 2 * j + 1):
+            r = oracle.recurrent_backward(b.q[:, j:j + 1], b.k[:, j:j + 1], b.v[:, h:h + 1], b.g[:, h:h + 1],
+                                          b.beta[:, h:h + 1], b.cu_seqlens, b.h0[:, h:h + 1], b.d_o[:, h:h + 1],
+                                          d_hT[:, h:h + 1], checkpoint=4)
+            dq_sum += r["dq"][:, 0]
+            dk_sum += r["dk"][:, 0]
+            for key in ("dv", "dg", "dbeta", "dh0"):
+                assert np.max(np.abs(r[key][:, 0] - ref[key][:, h])) < 1e-12, (key, h)
+        assert np.max(np.abs(dq_sum - ref["dq"][:, j])) < 1e-12
+        assert np.max(np.abs(dk_sum - ref["dk"][:, j])) < 1e-12
+
+
+def test_shared_key_head_gradients_match_finite_differences():
+    """One key head shared by two value heads: central differences of the
+    loss agree with the analytic dq and dk (h = 1e-6, 1e-6 * max|grad|)."""
+    b = make_batch(53, [10], 2, 3, 3, dtype="f32", h0_std=0.3, with_do=True, num_key_heads=1)
+    d_hT = np.random.default_rng(7).standard_normal(b.h0.shape)
+    ref = oracle.recurrent_backward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0, b.d_o, d_hT)
+    inputs = {n: np.asarray(getattr(b, n), np.float64) for n in ("q", "k", "v", "g", "beta", "h0")}
+    fd = oracle.fd_gradients(inputs, b.cu_seqlens, b.d_o, d_hT, names=("q", "k"))
+    for n, key in (("q", "dq"), ("k", "dk")):
+        scale = np.max(np.abs(ref[key]))
+        assert np.max(np.abs(fd[n] - ref[key])) <= 1e-6 * scale, n
+
+
+# ----------------------------------------------------------------------------
 # planted mistakes: each must be caught by at least one pin above
 
 

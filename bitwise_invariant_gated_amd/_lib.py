@@ -53,6 +53,7 @@ class Shape(ctypes.Structure):
         ("head_dim_v", ctypes.c_int32),
         ("chunk", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("num_key_heads", ctypes.c_int32),
     ]
 
 

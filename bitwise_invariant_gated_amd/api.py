@@ -25,12 +25,13 @@ class LayerShape:
     head_dim_v: int
     chunk: int = 64
     dtype: torch.dtype = torch.bfloat16
+    num_key_heads: int = 0  # heads of q and k; 0 = num_heads
 
     def c(self) -> _lib.Shape:
         if self.dtype not in _DTYPES:
             raise ValueError(f"unsupported dtype {self.dtype}")
         return _lib.Shape(self.num_heads, self.head_dim_k, self.head_dim_v, self.chunk,
-                          _DTYPES[self.dtype])
+                          _DTYPES[self.dtype], self.num_key_heads)
 
 
 @dataclasses.dataclass

@@ -165,13 +165,13 @@ struct LocalLds {
 template <int DK, int DV>
 __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t* q, const uint16_t* k,
                                             const uint16_t* d_o, const uint16_t* gp, const uint16_t* bp,
-                                            size_t row0, int H, int n, uint8_t* __restrict__ slot,
-                                            float* __restrict__ gamn) {
+                                            size_t row0, int H, size_t kq0, int Hk, int n,
+                                            uint8_t* __restrict__ slot, float* __restrict__ gamn) {
   typedef Slot<DK, DV> Sl;
   typedef LocalLds<DK, DV> Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  stage_rows<DK>(sm.K, k, row0, H, n);
-  stage_rows<DK>(sm.Q, q, row0, H, n);
+  stage_rows<DK>(sm.K, k, kq0, Hk, n);
+  stage_rows<DK>(sm.Q, q, kq0, Hk, n);
   stage_rows<DV>(sm.dO, d_o, row0, H, n);
   bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
   const bwd::ChunkScalars& cs = sm.cs;
@@ -346,8 +346,8 @@ __device__ __forceinline__ void stage_cols(float (*Bs)[LB], const float* __restr
 template <int DK, int DV>
 __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t* k, const uint16_t* v,
                                             const uint16_t* d_o, const uint16_t* gp, const uint16_t* bp,
-                                            size_t row0, int H, int n, const float* __restrict__ B,
-                                            uint8_t* __restrict__ slot) {
+                                            size_t row0, int H, size_t kq0, int Hk, int n,
+                                            const float* __restrict__ B, uint8_t* __restrict__ slot) {
   typedef Slot<DK, DV> Sl;
   typedef StateLds<DK, DV> Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
@@ -355,7 +355,7 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
   const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
   const float* Ddlg = reinterpret_cast<const float*>(slot + Sl::oDdl);
   const float* dBp = reinterpret_cast<const float*>(slot + Sl::oDbp);
-  stage_rows<DK>(sm.K, k, row0, H, n);
+  stage_rows<DK>(sm.K, k, kq0, Hk, n);
   stage_rows<DV>(sm.V, v, row0, H, n);
   stage_rows<DV>(sm.dO, d_o, row0, H, n);
   for (int idx = tid; idx < C * C / 4; idx += 256) {
@@ -522,12 +522,16 @@ struct GradLds {
 };
 
 template <int DK, int DV>
+// dq and dk go to rows kq0 + t Hk of [T, Hk, DK] in bf16 or, when the key
+// heads are shared (dq_part non-null), to the value head's rows row0 + t H of
+// fp32 [T, H, DK] partials that a later pass sums over the group.
 __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* q, const uint16_t* k,
                                            const uint16_t* v, const uint16_t* d_o, const uint16_t* gp,
-                                           const uint16_t* bp, size_t row0, int H, int n,
+                                           const uint16_t* bp, size_t row0, int H, size_t kq0, int Hk, int n,
                                            const uint8_t* __restrict__ slot, uint16_t* __restrict__ dq,
-                                           uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dg,
-                                           float* __restrict__ dbeta) {
+                                           uint16_t* __restrict__ dk, float* __restrict__ dq_part,
+                                           float* __restrict__ dk_part, uint16_t* __restrict__ dv,
+                                           float* __restrict__ dg, float* __restrict__ dbeta) {
   typedef Slot<DK, DV> Sl;
   typedef GradLds<DK, DV> Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
@@ -538,8 +542,8 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   const float* QBg = reinterpret_cast<const float*>(slot + Sl::oQB);
   const float* DWg = reinterpret_cast<const float*>(slot + Sl::oDWn);
   const float* KTg = reinterpret_cast<const float*>(slot + Sl::oDKt);
-  stage_rows<DK>(sm.K, k, row0, H, n);
-  stage_rows<DK>(sm.Q, q, row0, H, n);
+  stage_rows<DK>(sm.K, k, kq0, Hk, n);
+  stage_rows<DK>(sm.Q, q, kq0, Hk, n);
   stage_rows<DV>(sm.V, v, row0, H, n);
   stage_rows<DV>(sm.dO, d_o, row0, H, n);
   for (int idx = tid; idx < C * C / 4; idx += 256) {
@@ -619,7 +623,13 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
         const int t = 16 * tm + 4 * g + r;
         const float part = sum16(qb[tm][r] * bfv(sm.Q[t][i]));
         if (lr == 0) sm.pGO[t][it] = part;
-        if (t < n) Bf16::store(dq, (row0 + (size_t)t * H) * DK + i, __builtin_fmaf(cs.Gam[t], qb[tm][r], acc[tm][r]));
+        if (t < n) {
+          const float val = __builtin_fmaf(cs.Gam[t], qb[tm][r], acc[tm][r]);
+          if (dq_part)
+            dq_part[(row0 + (size_t)t * H) * DK + i] = val;
+          else
+            Bf16::store(dq, (kq0 + (size_t)t * Hk) * DK + i, val);
+        }
       }
   }
   // dV = diag(beta) X^T Dd
@@ -821,7 +831,12 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
           sm.pDE[s2][it] = pe;
         }
         const float val = acc[sb][r] + cs.e[s2] * kt[sb][r] + cs.Gam[s2] * tw;
-        if (s2 < n) Bf16::store(dk, (row0 + (size_t)s2 * H) * DK + i, val);
+        if (s2 < n) {
+          if (dk_part)
+            dk_part[(row0 + (size_t)s2 * H) * DK + i] = val;
+          else
+            Bf16::store(dk, (kq0 + (size_t)s2 * Hk) * DK + i, val);
+        }
       }
   }
   __syncthreads();

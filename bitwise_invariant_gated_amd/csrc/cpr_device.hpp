@@ -248,9 +248,9 @@ __device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf
 }
 
 // The scan's loop over tokens t = 0 .. n-1 (n >= 1) of one stretch of a
-// sequence, token t at row row0 + t * H: output o_t to column col of row
-// (row0 + t * H) of o, state s updated in place; alpha_l / beta_l hold token
-// t's decay and beta in lane t.  k, q and v of token t+1 are fetched into the
+// sequence, token t at row row0 + t * H of v and o and at row
+// kq0 + t * Hk of q and k: output o_t to column col of its row of o, state s
+// updated in place; alpha_l / beta_l hold token t's decay and beta in lane t.  k, q and v of token t+1 are fetched into the
 // other of two register buffers as token t starts (no copies between them).
 // Every fetch is issued (its index is clamped to token n-1), so the wait
 // before a token's first use of its operands covers that token's loads only,
@@ -258,13 +258,14 @@ __device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf
 template <class D, int DK, int DV>
 __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T* __restrict__ kp,
                                             const typename D::T* __restrict__ qp, const typename D::T* __restrict__ vp,
-                                            typename D::T* __restrict__ op, size_t row0, int H, int n, int col,
-                                            int lane, float alpha_l, float beta_l) {
+                                            typename D::T* __restrict__ op, size_t row0, int H, size_t kq0,
+                                            int Hk, int n, int col, int lane, float alpha_l, float beta_l) {
   KQRaw<D> r0, r1;
   uint32_t v0, v1;
   auto fetch = [&](KQRaw<D>& r, uint32_t& vb, int t) {
-    const size_t row = row0 + (size_t)min(t, n - 1) * H;
-    load_kq<D, DK>(r, kp + row * DK, qp + row * DK, lane);
+    const size_t tt = (size_t)min(t, n - 1);
+    const size_t row = row0 + tt * H, kr = kq0 + tt * Hk;
+    load_kq<D, DK>(r, kp + kr * DK, qp + kr * DK, lane);
     vb = D::load_bits(vp + row * DV, col);
   };
   auto step = [&](KQRaw<D>& r, uint32_t& vb, KQRaw<D>& rn, uint32_t& vn, int t) {

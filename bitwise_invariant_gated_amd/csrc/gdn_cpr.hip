@@ -71,6 +71,8 @@ struct PrefillArgs {
   float* bnd;          // [A_max*H][DK][DV] state at the start of every chunk
   int32_t N;
   int32_t H;
+  int32_t Hk;  // heads of q and k
+  int32_t G;   // value heads per key head, H / Hk
 };
 
 struct DecodeArgs {
@@ -93,6 +95,8 @@ struct DecodeArgs {
   float* gamn;    // [N*H]
   int32_t N;
   int32_t H;
+  int32_t Hk;  // heads of q and k
+  int32_t G;   // value heads per key head, H / Hk
 };
 
 template <int DK, int DV>
@@ -124,6 +128,10 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ base, int N,
 __device__ __forceinline__ size_t cache_row(const int32_t* __restrict__ slot, int i) {
   return slot ? (size_t)slot[i] : (size_t)i;
 }
+
+// row of q and k ([rows, Hk, d_k]) that value head h of token row tok reads:
+// key head h / G (value heads jG .. jG + G - 1 share key head j)
+__device__ __forceinline__ size_t kq_row(size_t tok, int h, int Hk, int G) { return tok * Hk + h / G; }
 
 // ---------------------------------------------------------------------------
 // varlen plan: exclusive prefix sums of full and of all chunks per sequence
@@ -217,8 +225,8 @@ __global__ __launch_bounds__(256) void k_chunk_local_prefill(const PrefillArgs a
   const int c = f - a.full_base[i];
   const size_t tok0 = (size_t)a.start[i] + (size_t)c * C;
   const size_t row0 = tok0 * H + h;  // row index into [T, H, ...]
-  stage_chunk<D, DK, DV>(sm, (const T*)a.k, row0, H, (const T*)a.v, row0, H, (const T*)a.g,
-                         (const T*)a.beta, row0, H);
+  stage_chunk<D, DK, DV>(sm, (const T*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const T*)a.v, row0, H,
+                         (const T*)a.g, (const T*)a.beta, row0, H);
   const size_t slot = (size_t)f * H + h;
   float* P = (float*)(a.prod + slot * prod_slot_bytes(false, DK, DV));
   chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + slot);
@@ -247,9 +255,10 @@ __global__ __launch_bounds__(256, 3) void k_chunk_local_prefill_bf16(const Prefi
   if (f >= a.full_base[N]) return;
   const int i = find_seq(a.full_base, N, f);
   const int c = f - a.full_base[i];
-  const size_t row0 = ((size_t)a.start[i] + (size_t)c * C) * H + h;
-  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, row0, H, (const uint16_t*)a.v, row0, H,
-                           (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H);
+  const size_t tok0 = (size_t)a.start[i] + (size_t)c * C;
+  const size_t row0 = tok0 * H + h;
+  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const uint16_t*)a.v, row0,
+                           H, (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H);
   const size_t slot = (size_t)f * H + h;
   chunk_local_bf16<DK, DV>(sm, a.prod + slot * prod_slot_bytes(true, DK, DV), a.gamn + slot);
 }
@@ -544,7 +553,8 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
-  scan_tokens<D, DK, DV>(s, kp, qp, vp, (T*)a.o, tok0 * H + h, H, n, col, lane, alpha_l, beta_l);
+  scan_tokens<D, DK, DV>(s, kp, qp, vp, (T*)a.o, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col, lane,
+                         alpha_l, beta_l);
   const int nall = (L + C - 1) / C;
   if (c == nall - 1 && (L % C) != 0) {
     // last, partial chunk: its end state is the running state, its tokens the tail
@@ -558,7 +568,7 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
       T* tk = (T*)a.tail_k + ch * C * DK;
       for (int idx = lane; idx < n * DK; idx += kWave) {
         const int t = idx / DK, e = idx % DK;
-        tk[idx] = kp[((tok0 + t) * H + h) * DK + e];
+        tk[idx] = kp[kq_row(tok0 + t, h, a.Hk, a.G) * DK + e];
       }
       if (lane < n) {
         ((T*)a.tail_g)[ch * C + lane] = gp[(tok0 + lane) * H + h];
@@ -593,11 +603,12 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   const float alpha = decay_of(D::load((const T*)a.g, sh));
   const float bt = D::load((const T*)a.beta, sh);
   const float vv = D::load((const T*)a.v, sh * DV + col);
-  const float out = token_step<D, DK>(s, (UniformRow)(kp + sh * DK), (UniformRow)(qp + sh * DK), alpha, bt, vv);
+  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
+  const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
   D::store((T*)a.o, sh * DV + col, out);
   // append the token to the tail
   T* tk = (T*)a.tail_k + (ch * C + tl) * DK;
-  for (int e = col; e < DK; e += DV) tk[e] = kp[sh * DK + e];
+  for (int e = col; e < DK; e += DV) tk[e] = kp[kr * DK + e];
   ((T*)a.tail_v)[(ch * C + tl) * DV + col] = ((const T*)a.v)[sh * DV + col];
   if (col == 0) {
     ((T*)a.tail_g)[ch * C + tl] = ((const T*)a.g)[sh];
@@ -640,6 +651,8 @@ struct ContArgs {
   int32_t* body_start;  // [N] first token row after the head
   int32_t N;
   int32_t H;
+  int32_t Hk;  // heads of q and k
+  int32_t G;   // value heads per key head, H / Hk
 };
 
 template <class D, int DK, int DV>
@@ -671,11 +684,12 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
     const float alpha = decay_of(D::load(gp, row));
     const float bt = D::load(bp, row);
     const float vv = D::load(vp, row * DV + col);
-    const float out = token_step<D, DK>(s, (UniformRow)(kp + row * DK), (UniformRow)(qp + row * DK), alpha, bt, vv);
+    const size_t kr = kq_row((size_t)(a.cu[i] + t), h, a.Hk, a.G);
+    const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
     D::store((T*)a.o, row * DV + col, out);
     const size_t tr = ch * C + tl + t;  // tail row
     T* tk = (T*)a.tail_k + tr * DK;
-    for (int e = col; e < DK; e += DV) tk[e] = kp[row * DK + e];
+    for (int e = col; e < DK; e += DV) tk[e] = kp[kr * DK + e];
     ((T*)a.tail_v)[tr * DV + col] = vp[row * DV + col];
     if (col == 0) {
       ((T*)a.tail_g)[tr] = gp[row];
@@ -722,6 +736,8 @@ struct CmpArgs {
   float* bnd;
   int32_t N;
   int32_t H;
+  int32_t Hk;  // heads of q and k
+  int32_t G;   // value heads per key head, H / Hk
 };
 
 // recurrent prefill: one wave per (sequence, head, 64 state columns), the
@@ -752,7 +768,8 @@ __global__ __launch_bounds__(64, 3) void k_cmp_rec_prefill(const CmpArgs a) {
       alpha_l = decay_of(D::load(gp, r));
       beta_l = D::load(bp, r);
     }
-    scan_tokens<D, DK, DV>(s, kp, qp, vp, op, tok0 * H + h, H, n, col, lane, alpha_l, beta_l);
+    scan_tokens<D, DK, DV>(s, kp, qp, vp, op, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col, lane,
+                           alpha_l, beta_l);
   }
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) a.state[sh * SS + (size_t)ii * DV + col] = s[ii];
@@ -773,7 +790,8 @@ __global__ __launch_bounds__(DV) void k_cmp_rec_decode(const CmpArgs a) {
   const float alpha = decay_of(D::load((const T*)a.g, sh));
   const float bt = D::load((const T*)a.beta, sh);
   const float vv = D::load((const T*)a.v, sh * DV + col);
-  const float out = token_step<D, DK>(s, (UniformRow)(kp + sh * DK), (UniformRow)(qp + sh * DK), alpha, bt, vv);
+  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
+  const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
   D::store((T*)a.o, sh * DV + col, out);
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
@@ -790,7 +808,8 @@ __global__ __launch_bounds__(256, 3) void k_cmp_chunk_local_bf16(const CmpArgs a
   const int i = find_seq(a.all_base, a.N, slot);
   const int c = slot - a.all_base[i];
   const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  const size_t row0 = tok0 * H + h, kq0 = kq_row(tok0, h, a.Hk, a.G);
   const uint16_t* kp = (const uint16_t*)a.k;
   const uint16_t* vp = (const uint16_t*)a.v;
   const int tid = threadIdx.x;
@@ -798,7 +817,7 @@ __global__ __launch_bounds__(256, 3) void k_cmp_chunk_local_bf16(const CmpArgs a
   for (int idx = tid; idx < C * DK / 8; idx += 256) {
     const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
     u32x4v w = {0u, 0u, 0u, 0u};
-    if (t < n) w = *reinterpret_cast<const u32x4v*>(kp + (row0 + (size_t)t * H) * DK + i0);
+    if (t < n) w = *reinterpret_cast<const u32x4v*>(kp + (kq0 + (size_t)t * a.Hk) * DK + i0);
     *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
   }
   for (int idx = tid; idx < C * DV / 8; idx += 256) {
@@ -934,7 +953,8 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
   const int i = find_seq(a.all_base, a.N, slot);
   const int c = slot - a.all_base[i];
   const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  const size_t row0 = tok0 * H + h, kq0 = kq_row(tok0, h, a.Hk, a.G);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint16_t* qp = (const uint16_t*)a.q;
   const uint16_t* kp = (const uint16_t*)a.k;
@@ -943,8 +963,8 @@ __global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
     const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
     u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
     if (t < n) {
-      wq = *reinterpret_cast<const u32x4v*>(qp + (row0 + (size_t)t * H) * DK + i0);
-      wk = *reinterpret_cast<const u32x4v*>(kp + (row0 + (size_t)t * H) * DK + i0);
+      wq = *reinterpret_cast<const u32x4v*>(qp + (kq0 + (size_t)t * a.Hk) * DK + i0);
+      wk = *reinterpret_cast<const u32x4v*>(kp + (kq0 + (size_t)t * a.Hk) * DK + i0);
     }
     *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
     *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
@@ -981,6 +1001,7 @@ __global__ __launch_bounds__(256, 3) void k_cmp_cdec_local_bf16(const DecodeArgs
   const int tl = a.tail_len[ch];
   if ((unsigned)tl >= (unsigned)C) return;
   const int tid = threadIdx.x;
+  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
   const uint16_t* tk = (const uint16_t*)a.tail_k;
   const uint16_t* tv = (const uint16_t*)a.tail_v;
   const uint16_t* kp = (const uint16_t*)a.k;
@@ -990,7 +1011,7 @@ __global__ __launch_bounds__(256, 3) void k_cmp_cdec_local_bf16(const DecodeArgs
     const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
     u32x4v w = {0u, 0u, 0u, 0u};
     if (t < tl) w = *reinterpret_cast<const u32x4v*>(tk + (ch * C + t) * DK + i0);
-    if (t == tl) w = *reinterpret_cast<const u32x4v*>(kp + sh * DK + i0);
+    if (t == tl) w = *reinterpret_cast<const u32x4v*>(kp + kr * DK + i0);
     *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
   }
   for (int idx = tid; idx < C * DV / 8; idx += 256) {
@@ -1012,7 +1033,7 @@ __global__ __launch_bounds__(256, 3) void k_cmp_cdec_local_bf16(const DecodeArgs
   // append the token to the tail (row tl of the tail is read by no kernel of this step)
   uint16_t* wk = (uint16_t*)a.tail_k + (ch * C + tl) * DK;
   uint16_t* wv = (uint16_t*)a.tail_v + (ch * C + tl) * DV;
-  for (int e = tid; e < DK; e += 256) wk[e] = kp[sh * DK + e];
+  for (int e = tid; e < DK; e += 256) wk[e] = kp[kr * DK + e];
   for (int e = tid; e < DV; e += 256) wv[e] = vp[sh * DV + e];
   if (tid == 0) {
     ((uint16_t*)a.tail_g)[ch * C + tl] = ((const uint16_t*)a.g)[sh];
@@ -1043,8 +1064,8 @@ __global__ __launch_bounds__(256) void k_cmp_cdec_out_bf16(const DecodeArgs a) {
     u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
     if (t < tl) wk = *reinterpret_cast<const u32x4v*>(tk + (ch * C + t) * DK + i0);
     if (t == tl) {
-      wq = *reinterpret_cast<const u32x4v*>(qp + sh * DK + i0);
-      wk = *reinterpret_cast<const u32x4v*>(kp + sh * DK + i0);
+      wq = *reinterpret_cast<const u32x4v*>(qp + kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G) * DK + i0);
+      wk = *reinterpret_cast<const u32x4v*>(kp + kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G) * DK + i0);
     }
     *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
     *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
@@ -1090,8 +1111,12 @@ struct BwdArgs {
   float* dg;
   float* dbeta;
   float* dh0;
+  float* dq_part;  // [T, H, DK] fp32 per value head when key heads are shared, else null
+  float* dk_part;
   int32_t N;
   int32_t H;
+  int32_t Hk;  // heads of q and k
+  int32_t G;   // value heads per key head, H / Hk
 };
 
 template <int DK, int DV>
@@ -1125,8 +1150,9 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
   const T* dop = (const T*)a.d_o;
   chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
   const ChunkScalars& cs = sm.cs;
-  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
-  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
+  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * C, h, a.Hk, a.G);
+  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
+  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
   auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
   uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
 
@@ -1280,8 +1306,9 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   const T* dop = (const T*)a.d_o;
   chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
   const ChunkScalars& cs = sm.cs;
-  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
-  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (row0 + (size_t)t * H) * DK + e) : 0.f; };
+  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * C, h, a.Hk, a.G);
+  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
+  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
   auto Vx = [&](int t, int j) { return t < n ? D::load(vp, (row0 + (size_t)t * H) * DV + j) : 0.f; };
   auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
   const uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
@@ -1387,7 +1414,13 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     acc = tile<C>([&](int t, int s) { return sm.N4[t][s]; }, [&](int s, int e) { return Kx(s, e); }, 16 * tm, 16 * it,
                   acc);
     tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
-      if (t < n) D::store(dqp, (row0 + (size_t)t * H) * DK + e, cs.Gam[t] * sm.M1[t][e] + v);
+      if (t < n) {
+        const float val = cs.Gam[t] * sm.M1[t][e] + v;
+        if (a.dq_part)
+          a.dq_part[(row0 + (size_t)t * H) * DK + e] = val;
+        else
+          D::store(dqp, (kq0 + (size_t)t * a.Hk) * DK + e, val);
+      }
     });
   }
   if (tid < C) {
@@ -1534,7 +1567,13 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     acc = tile<C>([&](int t, int s) { return sm.N2[t][s] + sm.N2[s][t]; }, [&](int s, int e) { return Kx(s, e); },
                   16 * tm, 16 * it, acc);
     tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
-      if (t < n) D::store(dkp, (row0 + (size_t)t * H) * DK + e, v + cs.e[t] * sm.M2[t][e] + cs.Gam[t] * sm.M1[t][e]);
+      if (t < n) {
+        const float val = v + cs.e[t] * sm.M2[t][e] + cs.Gam[t] * sm.M1[t][e];
+        if (a.dk_part)
+          a.dk_part[(row0 + (size_t)t * H) * DK + e] = val;
+        else
+          D::store(dkp, (kq0 + (size_t)t * a.Hk) * DK + e, val);
+      }
     });
   }
 }
@@ -1546,6 +1585,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
 struct SlotPos {
   int n;        // real tokens of the chunk
   size_t row0;  // row of its first token in [T, H, ...]
+  size_t kq0;   // its row in [T, Hk, DK] (q, k)
   size_t sl;    // slot * H + h
 };
 
@@ -1556,7 +1596,9 @@ __device__ __forceinline__ bool slot_pos(const BwdArgs& a, SlotPos& p) {
   const int c = slot - a.all_base[i];
   const int L = a.cu[i + 1] - a.cu[i];
   p.n = min(C, L - c * C);
-  p.row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  p.row0 = tok0 * H + h;
+  p.kq0 = kq_row(tok0, h, a.Hk, a.G);
   p.sl = (size_t)slot * H + h;
   return true;
 }
@@ -1568,8 +1610,8 @@ __global__ __launch_bounds__(256) void k_bwd_local_bf16(const BwdArgs a) {
   SlotPos p;
   if (!slot_pos(a, p)) return;
   bwdb::local_stage<DK, DV>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.d_o,
-                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.n, a.ws + p.sl * Sl::bytes,
-                            a.gamn + p.sl);
+                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
+                            a.ws + p.sl * Sl::bytes, a.gamn + p.sl);
 }
 
 template <int DK, int DV>
@@ -1579,7 +1621,7 @@ __global__ __launch_bounds__(256) void k_bwd_state_bf16(const BwdArgs a) {
   SlotPos p;
   if (!slot_pos(a, p)) return;
   bwdb::state_stage<DK, DV>(sm, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
-                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.n,
+                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
                             a.bnd + p.sl * DK * DV, a.ws + p.sl * Sl::bytes);
 }
 
@@ -1590,9 +1632,9 @@ __global__ __launch_bounds__(256) void k_bwd_grads_bf16(const BwdArgs a) {
   SlotPos p;
   if (!slot_pos(a, p)) return;
   bwdb::grad_stage<DK, DV>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.d_o, (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.n,
-                           a.ws + p.sl * Sl::bytes, (uint16_t*)a.dq, (uint16_t*)a.dk, (uint16_t*)a.dv, a.dg,
-                           a.dbeta);
+                           (const uint16_t*)a.d_o, (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0,
+                           a.Hk, p.n, a.ws + p.sl * Sl::bytes, (uint16_t*)a.dq, (uint16_t*)a.dk, a.dq_part,
+                           a.dk_part, (uint16_t*)a.dv, a.dg, a.dbeta);
 }
 
 // Reverse chain, bf16 path: the forward chain's structure run from the last
@@ -1756,8 +1798,16 @@ bool shape_ok(const gdn_cpr_shape* s, std::string* why) {
     *why = "dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16";
     return false;
   }
+  if (s->num_key_heads < 0 || s->num_key_heads > s->num_heads ||
+      (s->num_key_heads > 0 && s->num_heads % s->num_key_heads != 0)) {
+    *why = "num_key_heads must be 0 or divide num_heads";
+    return false;
+  }
   return true;
 }
+
+// heads of q and k (0 in the shape means one per value head)
+int key_heads(const gdn_cpr_shape& s) { return s.num_key_heads > 0 ? s.num_key_heads : s.num_heads; }
 
 struct PrefillLayout {
   size_t full_base, all_base, prod, slot, gamn, bnd, total;
@@ -2018,9 +2068,24 @@ struct CmpChunkDecodeFn {
   }
 };
 
+// dq, dk of key heads shared by G value heads: out[tok][j][e] = sum over
+// g = 0 .. G-1 (ascending) of part[tok][j G + g][e], rounded once to dtype.
+// One work-group of DK threads per (token, key head).
+template <class D, int DK>
+__global__ __launch_bounds__(DK) void k_key_head_sum(const float* __restrict__ part, typename D::T* __restrict__ out,
+                                                     int Hk, int G) {
+  const size_t r = blockIdx.x;  // token * Hk + j
+  const int e = threadIdx.x;
+  const size_t tok = r / Hk, j = r % Hk;
+  const float* p = part + ((tok * Hk + j) * G) * DK + e;  // rows tok * H + j G + g, H = Hk G
+  float acc = p[0];
+  for (int g = 1; g < G; ++g) acc = acc + p[(size_t)g * DK];
+  D::store(out, r * DK + e, acc);
+}
+
 struct FwdBwdLayout {
   PrefillLayout pre;
-  size_t s_bnd, s_run, tail_k, tail_v, tail_g, tail_b, tail_len, bgamn, bslots, slot, total;
+  size_t s_bnd, s_run, tail_k, tail_v, tail_g, tail_b, tail_len, bgamn, bslots, slot, dq_part, dk_part, total;
 };
 
 FwdBwdLayout fwd_bwd_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
@@ -2055,12 +2120,27 @@ FwdBwdLayout fwd_bwd_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
              DK * DV * 4;
   L.bslots = off;
   off = align_up(off + Amax * H * L.slot);
+  L.dq_part = L.dk_part = 0;
+  if (key_heads(s) != (int)H) {  // per-value-head dq, dk partials
+    L.dq_part = off;
+    off = align_up(off + (size_t)T * H * DK * 4);
+    L.dk_part = off;
+    off = align_up(off + (size_t)T * H * DK * 4);
+  }
   L.total = off;
   return L;
 }
 
 template <class D, int DK, int DV>
 struct FwdBwdFn {
+  static void launch_key_head_sums(const BwdArgs& ba, int64_t T, hipStream_t st) {
+    if (!ba.dq_part) return;
+    const unsigned rows = (unsigned)(T * ba.Hk);
+    hipLaunchKernelGGL((k_key_head_sum<D, DK>), dim3(rows), dim3(DK), 0, st, ba.dq_part, (typename D::T*)ba.dq, ba.Hk,
+                       ba.G);
+    hipLaunchKernelGGL((k_key_head_sum<D, DK>), dim3(rows), dim3(DK), 0, st, ba.dk_part, (typename D::T*)ba.dk, ba.Hk,
+                       ba.G);
+  }
   static gdn_status run(const PrefillArgs& pa, const BwdArgs& ba, int64_t T, size_t slot_bytes, hipStream_t st,
                         const char* fn) {
     constexpr bool kBf16 = std::is_same<D, Bf16>::value;
@@ -2080,6 +2160,7 @@ struct FwdBwdFn {
       if (T > 0) {
         hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
         hipLaunchKernelGGL((k_bwd_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+        launch_key_head_sums(ba, T, st);
       }
       mark(6, st);
     } else {
@@ -2087,7 +2168,10 @@ struct FwdBwdFn {
       if (T > 0) hipLaunchKernelGGL((k_bwd_local<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
       hipLaunchKernelGGL((k_bwd_chain_f32<DK, DV>), dim3(pa.N, pa.H), dim3(DV * 4), 0, st, ba);
       mark(5, st);
-      if (T > 0) hipLaunchKernelGGL((k_bwd_grads<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+      if (T > 0) {
+        hipLaunchKernelGGL((k_bwd_grads<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+        launch_key_head_sums(ba, T, st);
+      }
       mark(6, st);
     }
     return launch_status(fn);
@@ -2177,6 +2261,8 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.bnd = (float*)(ws + L.bnd);
   a.N = num_seqs;
   a.H = shape->num_heads;
+  a.Hk = key_heads(*shape);
+  a.G = a.H / a.Hk;
   return dispatch<PrefillFn>(*shape, a, total_tokens, (hipStream_t)stream, fn);
 }
 
@@ -2233,6 +2319,8 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   a.gamn = (float*)(ws + L.gamn);
   a.N = num_seqs;
   a.H = shape->num_heads;
+  a.Hk = key_heads(*shape);
+  a.G = a.H / a.Hk;
   return dispatch<DecodeFn>(*shape, a, (hipStream_t)stream, fn);
 }
 
@@ -2294,6 +2382,8 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   ca.body_start = body_start;
   ca.N = num_seqs;
   ca.H = shape->num_heads;
+  ca.Hk = key_heads(*shape);
+  ca.G = ca.H / ca.Hk;
   DecodeArgs da;
   memset(&da, 0, sizeof(da));
   da.s_bnd = cache->s_bnd;
@@ -2308,6 +2398,8 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   da.gamn = (float*)(wd + L.dec.gamn);
   da.N = num_seqs;
   da.H = shape->num_heads;
+  da.Hk = key_heads(*shape);
+  da.G = da.H / da.Hk;
   da.slot = cache->slot_index;
   PrefillArgs pa;
   pa.q = q;
@@ -2337,6 +2429,8 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   pa.bnd = (float*)(ws + L.pre.bnd);
   pa.N = num_seqs;
   pa.H = shape->num_heads;
+  pa.Hk = key_heads(*shape);
+  pa.G = pa.H / pa.Hk;
   return dispatch<ContFn>(*shape, ca, da, pa, total_tokens, (hipStream_t)stream, fn);
 }
 
@@ -2408,6 +2502,8 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.bnd = (float*)(ws + L.pre.bnd);
   pa.N = num_seqs;
   pa.H = shape->num_heads;
+  pa.Hk = key_heads(*shape);
+  pa.G = pa.H / pa.Hk;
   BwdArgs ba;
   ba.q = q;
   ba.k = k;
@@ -2427,8 +2523,12 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   ba.dg = dg;
   ba.dbeta = dbeta;
   ba.dh0 = dh0;
+  ba.dq_part = L.dq_part ? (float*)(ws + L.dq_part) : nullptr;
+  ba.dk_part = L.dk_part ? (float*)(ws + L.dk_part) : nullptr;
   ba.N = num_seqs;
   ba.H = shape->num_heads;
+  ba.Hk = key_heads(*shape);
+  ba.G = ba.H / ba.Hk;
   return dispatch<FwdBwdFn>(*shape, pa, ba, total_tokens, L.slot, (hipStream_t)stream, fn);
 }
 
@@ -2487,6 +2587,8 @@ extern "C" gdn_status gdn_cmp_prefill(const gdn_cpr_shape* shape, int32_t mode, 
   ca.o = o;
   ca.N = num_seqs;
   ca.H = shape->num_heads;
+  ca.Hk = key_heads(*shape);
+  ca.G = ca.H / ca.Hk;
   PrefillArgs pa;
   memset(&pa, 0, sizeof(pa));
   if (mode == GDN_CMP_CHUNKWISE) {
@@ -2506,6 +2608,8 @@ extern "C" gdn_status gdn_cmp_prefill(const gdn_cpr_shape* shape, int32_t mode, 
     pa.bnd = ca.bnd;
     pa.N = num_seqs;
     pa.H = shape->num_heads;
+    pa.Hk = key_heads(*shape);
+    pa.G = pa.H / pa.Hk;
   }
   return dispatch<CmpPrefillFn>(*shape, (int)mode, ca, pa, total_tokens, (hipStream_t)stream, fn);
 }
@@ -2539,6 +2643,8 @@ extern "C" gdn_status gdn_cmp_decode_step(const gdn_cpr_shape* shape, int32_t nu
   ca.o = o;
   ca.N = num_seqs;
   ca.H = shape->num_heads;
+  ca.Hk = key_heads(*shape);
+  ca.G = ca.H / ca.Hk;
   return dispatch<CmpDecodeFn>(*shape, ca, (hipStream_t)stream, fn);
 }
 
@@ -2596,6 +2702,8 @@ extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int3
   a.gamn = (float*)(ws + L.gamn);
   a.N = num_seqs;
   a.H = shape->num_heads;
+  a.Hk = key_heads(*shape);
+  a.G = a.H / a.Hk;
   return dispatch<CmpChunkDecodeFn>(*shape, a, (hipStream_t)stream, fn);
 }
 

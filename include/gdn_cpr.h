@@ -28,8 +28,13 @@
  *     gdn_cpr_workspace_size).  Calls only enqueue work on `stream` (a
  *     hipStream_t; NULL = the legacy default stream) and return; results are
  *     ready when the stream reaches them.  No call synchronises the host.
- *   - Token-major packed layouts: q, k [T, H, d_k]; v, o [T, H, d_v];
- *     g, beta [T, H]; all rows contiguous.  cu_seqlens int32 [N + 1] with
+ *   - Token-major packed layouts: q, k [T, H_k, d_k]; v, o [T, H, d_v];
+ *     g, beta [T, H]; all rows contiguous.  H_k = H unless the shape asks
+ *     for fewer key heads.  The pages name hybrid Gated DeltaNet models
+ *     (Chinese page, the paragraph on the released code and the model
+ *     classes it supports) without their layer dimensions; layers of that
+ *     kind may give q and k fewer heads than v, so the library takes H_k
+ *     key heads, each serving H / H_k consecutive value heads.  cu_seqlens int32 [N + 1] with
  *     cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T.
  *   - States [N, H, d_k, d_v] fp32, key dimension first (S layout).
  *   - dtype GDN_DTYPE_F32: q, k, v, g, beta, o (and d_o, dq, dk, dv) are fp32.
@@ -37,7 +42,7 @@
  *     rounded to nearest even.  States, dg, dbeta are always fp32.
  *   - g must be <= 0 (alpha in (0, 1]); beta is used as given.  Values are
  *     not checked on the device.
- *   - Supported shapes: d_k, d_v in {64, 128}; C = 64; H >= 1.
+ *   - Supported shapes: d_k, d_v in {64, 128}; C = 64; H >= 1; H_k divides H.
  *   - Every pointer must be 16-byte aligned.
  *   - Errors detectable on the host (null or misaligned pointer, unsupported
  *     shape, workspace too small, negative sizes) return a status before any
@@ -75,11 +80,13 @@ typedef enum {
 
 /* Layer shape (host struct). */
 typedef struct {
-  int32_t num_heads;  /* H */
-  int32_t head_dim_k; /* d_k */
-  int32_t head_dim_v; /* d_v */
-  int32_t chunk;      /* C, the boundary / resynchronisation period */
-  int32_t dtype;      /* gdn_dtype of q, k, v, g, beta, o and the tail buffers */
+  int32_t num_heads;     /* H: value heads (v, g, beta, o, states, caches) */
+  int32_t head_dim_k;    /* d_k */
+  int32_t head_dim_v;    /* d_v */
+  int32_t chunk;         /* C, the boundary / resynchronisation period */
+  int32_t dtype;         /* gdn_dtype of q, k, v, g, beta, o and the tail buffers */
+  int32_t num_key_heads; /* H_k: heads of q and k; 0 means H.  H_k divides H and
+                            value head h reads key head h / (H / H_k) */
 } gdn_cpr_shape;
 
 /*
@@ -151,7 +158,8 @@ gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t
 
 /*
  * Decode (the engine_decode case): one token for each of N sequences.
- *   q, k, v, g, beta  [N, H, ...] one token per sequence
+ *   q, k, v, g, beta  one token per sequence: q, k [N, H_k, d_k]; v [N, H, d_v];
+ *                     g, beta [N, H]
  *   cache             read-modify-write in place
  *   o                 [N, H, d_v]
  * The token's output comes from the per-token step on s_run.  When the step

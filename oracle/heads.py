@@ -2,8 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
-Some Gated DeltaNet layers in the hybrid model families the pages discuss
-give the queries and keys fewer heads than the values.  Reading used here:
+The pages name hybrid Gated DeltaNet models (Chinese page, the paragraph
+on the released code and the model classes it supports) but not their layer
+dimensions; layers of that kind may give the queries and keys fewer heads
+than the values.  Reading used here:
 with H value heads and H_k key heads (H a multiple of H_k, G = H / H_k),
 value head h reads the query and key of key head floor(h / G), so heads
 jG .. jG + G - 1 share key head j; everything else (state, decay, beta,

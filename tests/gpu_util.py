@@ -25,7 +25,7 @@ def torch_dtype(b: Batch):
 
 
 def shape_of(b: Batch, C: int = 64) -> gdn.LayerShape:
-    return gdn.LayerShape(b.num_heads, b.d_k, b.d_v, C, torch_dtype(b))
+    return gdn.LayerShape(b.num_heads, b.d_k, b.d_v, C, torch_dtype(b), b.num_key_heads)
 
 
 class DevBatch:

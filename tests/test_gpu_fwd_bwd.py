@@ -29,8 +29,8 @@ def run_fwd_bwd(db, d_hT=None):
     out = dict(
         o=torch.empty((T, H, b.d_v), dtype=dt, device=DEV),
         hT=torch.empty((N, H, b.d_k, b.d_v), dtype=torch.float32, device=DEV),
-        dq=torch.empty((T, H, b.d_k), dtype=dt, device=DEV),
-        dk=torch.empty((T, H, b.d_k), dtype=dt, device=DEV),
+        dq=torch.empty((T, b.num_key_heads, b.d_k), dtype=dt, device=DEV),
+        dk=torch.empty((T, b.num_key_heads, b.d_k), dtype=dt, device=DEV),
         dv=torch.empty((T, H, b.d_v), dtype=dt, device=DEV),
         dg=torch.empty((T, H), dtype=torch.float32, device=DEV),
         dbeta=torch.empty((T, H), dtype=torch.float32, device=DEV),

@@ -263,7 +263,8 @@ def main():
     cont_ms, dec4_ms = e4.elapsed_time(e5), e5.elapsed_time(e6)
     cont_bitwise = bool(torch.equal(o_c.view(256, n_tok, H, D).transpose(0, 1).contiguous().view(torch.int16),
                                     o_d4.view(torch.int16))
-                        and torch.equal(c_cont.s_run.view(torch.int32), c_dec.s_run.view(torch.int32)))
+                        and torch.equal(c_cont.s_run.view(torch.int32), c_dec.s_run.view(torch.int32))
+                        and torch.equal(c_cont.run_log_scale.view(torch.int32), c_dec.run_log_scale.view(torch.int32)))
 
     # ---- trainer forward + backward, 1 x 10,240 tokens
     log("fwd_bwd: 1 x 10,240 tokens")
@@ -389,7 +390,8 @@ def main():
                         c_full, o_full, ws_pre)
     torch.cuda.synchronize()
     parity_o = bool(torch.equal(o_d5.view(torch.int16), o_full[last].contiguous().view(torch.int16)))
-    parity_s = bool(torch.equal(cache_p.s_run.view(torch.int32), c_full.s_run.view(torch.int32)))
+    parity_s = bool(torch.equal(cache_p.s_run.view(torch.int32), c_full.s_run.view(torch.int32))
+                    and torch.equal(cache_p.run_log_scale.view(torch.int32), c_full.run_log_scale.view(torch.int32)))
 
     scan_avg = float(np.mean(scan_ms))
     flops_scan = 7.0 * D * D * T * H  # algorithmic: 7 flop per state entry per token-head
@@ -407,7 +409,8 @@ def main():
         "avg_launch_ms": round(scan_avg, 5),
     }
     dec_avg = float(np.mean(decode_ms))
-    dec_bytes = N_dec * H * (2 * D * D * 4 + 3 * D * 2 + 2 * 2 + D * 2 + (2 * D + 2) * 2)
+    # per (sequence, head): state read + write, log-scale read + write, q/k/v, g/beta, o, tail append
+    dec_bytes = N_dec * H * (2 * D * D * 4 + 2 * 4 + 3 * D * 2 + 2 * 2 + D * 2 + (2 * D + 2) * 2)
     result = {
         "metric": METRIC,
         "value": round(value, 1),

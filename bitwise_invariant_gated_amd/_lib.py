@@ -36,6 +36,7 @@ EXPORTED = (
     "gdn_cpr_decode_step",
     "gdn_cpr_prefill_continue",
     "gdn_cpr_fwd_bwd",
+    "gdn_cpr_cache_state",
     "gdn_cpr_set_stage_events",
     "gdn_cpr_last_error",
     "gdn_cpr_numerics_id",
@@ -67,6 +68,7 @@ class Cache(ctypes.Structure):
         ("tail_beta", ctypes.c_void_p),
         ("tail_len", ctypes.c_void_p),
         ("slot_index", ctypes.c_void_p),
+        ("run_log_scale", ctypes.c_void_p),
     ]
 
 
@@ -102,6 +104,8 @@ def load() -> ctypes.CDLL:
     lib.gdn_cpr_fwd_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdn_cpr_cache_state.restype = ctypes.c_int
+    lib.gdn_cpr_cache_state.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.POINTER(Cache), _vp, _vp]
     lib.gdn_cmp_workspace_size.restype = ctypes.c_size_t
     lib.gdn_cmp_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     lib.gdn_cmp_prefill.restype = ctypes.c_int

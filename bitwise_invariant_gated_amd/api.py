@@ -36,8 +36,10 @@ class LayerShape:
 
 @dataclasses.dataclass
 class CprCache:
-    """Device tensors of a gdn_cpr_cache (layouts in gdn_cpr.h).  slot_index
-    (int32 [N] or None) selects the cache rows of a call's batch entries."""
+    """Device tensors of a gdn_cpr_cache (layouts in gdn_cpr.h).  s_run holds
+    the running state in scaled form (the state is exp(run_log_scale) * s_run;
+    gdn_cpr_cache_state writes it out).  slot_index (int32 [N] or None)
+    selects the cache rows of a call's batch entries."""
 
     s_bnd: torch.Tensor
     s_run: torch.Tensor
@@ -46,11 +48,14 @@ class CprCache:
     tail_g: torch.Tensor
     tail_beta: torch.Tensor
     tail_len: torch.Tensor
+    run_log_scale: torch.Tensor
     slot_index: Optional[torch.Tensor] = None
 
     def c(self) -> _lib.Cache:
         si = None if self.slot_index is None else _ptr(self.slot_index)
-        return _lib.Cache(*(t.data_ptr() for t in self.tensors()), si)
+        return _lib.Cache(_ptr(self.s_bnd), _ptr(self.s_run), _ptr(self.tail_k), _ptr(self.tail_v),
+                          _ptr(self.tail_g), _ptr(self.tail_beta), _ptr(self.tail_len), si,
+                          _ptr(self.run_log_scale))
 
     def clone(self) -> "CprCache":
         return CprCache(*(t.clone() for t in self.tensors()), self.slot_index)
@@ -60,7 +65,9 @@ class CprCache:
         return CprCache(*self.tensors(), slot_index)
 
     def tensors(self):
-        return (self.s_bnd, self.s_run, self.tail_k, self.tail_v, self.tail_g, self.tail_beta, self.tail_len)
+        """Every array of the cache (slot_index aside), in field order."""
+        return (self.s_bnd, self.s_run, self.tail_k, self.tail_v, self.tail_g, self.tail_beta, self.tail_len,
+                self.run_log_scale)
 
 
 def alloc_cache(shape: LayerShape, num_seqs: int, device="cuda") -> CprCache:
@@ -70,7 +77,23 @@ def alloc_cache(shape: LayerShape, num_seqs: int, device="cuda") -> CprCache:
     return CprCache(torch.zeros((N, H, dk, dv), **f32), torch.zeros((N, H, dk, dv), **f32),
                     torch.zeros((N, H, C, dk), **dt), torch.zeros((N, H, C, dv), **dt),
                     torch.zeros((N, H, C), **dt), torch.zeros((N, H, C), **dt),
-                    torch.zeros((N, H), dtype=torch.int32, device=device))
+                    torch.zeros((N, H), dtype=torch.int32, device=device), torch.zeros((N, H), **f32))
+
+
+def gdn_cpr_cache_state(shape: LayerShape, cache: CprCache, num_seqs: Optional[int] = None, out=None,
+                        stream=None) -> torch.Tensor:
+    """The state after each cached sequence's last token, exp(run_log_scale) * s_run,
+    as a new [N, H, d_k, d_v] fp32 tensor (or into `out`)."""
+    lib = _lib.load()
+    if num_seqs is None:
+        num_seqs = int(cache.slot_index.numel()) if cache.slot_index is not None else int(cache.s_run.shape[0])
+    if out is None:
+        out = torch.empty((num_seqs, shape.num_heads, shape.head_dim_k, shape.head_dim_v), dtype=torch.float32,
+                          device=cache.s_run.device)
+    cc = cache.c()
+    _lib.check(lib.gdn_cpr_cache_state(ctypes.byref(shape.c()), num_seqs, ctypes.byref(cc), _ptr(out),
+                                       _stream(stream)))
+    return out
 
 
 def gdn_cpr_workspace_size(shape: LayerShape, num_seqs: int, total_tokens: int, op: int) -> int:

@@ -2,8 +2,10 @@
 //
 // Every quantity that must round identically in prefill and decode is
 // computed by exactly one routine in this file:
-//   token_step        the per-token recurrence on one state column
-//                     (prefill's in-chunk scan and decode both call it)
+//   token_step        the per-token recurrence on one state column, on a
+//                     scaled running state (prefill's in-chunk scan and
+//                     decode both call it; token_step_dpp is the same
+//                     arithmetic with another operand delivery)
 //   chunk_local_f32   chunk products W, U, K~^T, Gamma_n of one chunk
 //                     (prefill's chunk pass and decode's resync call it)
 //   chain_step_f32    boundary advance S' = Gamma_n S + K~^T (U - W S)
@@ -70,12 +72,25 @@ __device__ __forceinline__ UniformRow fresh(UniformRow p) {
   return p;
 }
 
+// Buffer resource over [base, base + bytes) for raw (unformatted) buffer
+// loads and stores: the address is the wave-uniform base plus a 32-bit
+// scalar offset plus a 32-bit lane offset, so a per-lane access pattern
+// costs one VGPR, and the hardware drops any access past `bytes`.
+// Dword 3 is the gfx9 raw-buffer format word.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float lane_bcast(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
 // ---------------------------------------------------------------------------
-// The per-token step (one state column per lane).
+// The plain per-token step (one state column per lane), used only by the
+// comparators that stand for the orders CPR replaces (recurrent everywhere,
+// and the recurrent decode of "native mixed" serving): the state is decayed
+// element by element at every token.  The CPR path uses token_step below.
 //
 // Lane j holds column j of S (S[i][j] = M[j][i], i = 0..DK-1) in s[].  With
 // k, q wave-uniform (scalar registers), the step is, in this exact order:
@@ -85,7 +100,7 @@ __device__ __forceinline__ float lane_bcast(float x, int lane) {
 //   return o_0 + o_1
 // which is M' = alpha M, p = M' k, u = beta (v - p), M = M' + u k^T, o = M q.
 template <class D, int DK>
-__device__ __forceinline__ float token_step(float (&s)[DK], UniformRow krow, UniformRow qrow,
+__device__ __forceinline__ float token_step_plain(float (&s)[DK], UniformRow krow, UniformRow qrow,
                                             float alpha, float beta, float v) {
   constexpr int G = D::kRowGroup;
   static_assert(DK % G == 0, "key dim must be a multiple of the scalar load group");
@@ -124,16 +139,110 @@ __device__ __forceinline__ float token_step(float (&s)[DK], UniformRow krow, Uni
 __device__ __forceinline__ float decay_of(float g) { return expf(g); }
 
 // ---------------------------------------------------------------------------
-// The same per-token step with k and q delivered by DPP row broadcast.
+// The CPR per-token step, on a scaled running state.
 //
-// Used by the prefill scan.  Instead of scalar loads (whose cache misses
+// Between chunk boundaries the running state is held as M = exp(lg) N: the
+// state registers (and the cache's s_run) hold N, and lg, one fp32 per
+// sequence and head, is the log of its scale.  A boundary state has lg = 0
+// and N = M.  Token t, with log-decay g, first advances the scale:
+//   x = lg + g                                        (one fp32 add)
+//   x >= kRenormLog:  c = exp(x), r = exp(-x), lg' = x
+//   x <  kRenormLog:  N = exp(x) N element by element, c = r = 1, lg' = 0
+// and then steps N with the scalars c and b = beta r:
+//   p = c (N k)      w = b (v - p)      (= u r with u = beta (v - p))
+//   N = N + w k^T    o = c (N q)
+// In exact arithmetic this is M' = alpha M = c N, p = M' k,
+// M = M' + u k^T = exp(lg') N and o = M q: the update of the pages'
+// recurrence.  The per-element decay multiply of the plain step becomes the
+// scalar c, so a state element costs three FMAs per token (N k, the update,
+// N q) instead of a multiply and three FMAs.  Renormalising keeps |N| within
+// a factor exp(-kRenormLog) of the state's scale, far inside fp32's range;
+// the decision depends only on the sequence's own log-decays since the last
+// boundary, so prefill and decode renormalise at the same tokens.
+//
+// Order (pinned): with k, q wave-uniform, lane j (state column j),
+//   b = beta * r   (per token)
+//   pass A, i ascending:  p_(i mod 4) = fma(N[i], k[i], p_(i mod 4))
+//   w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3)))
+//   pass B, i ascending:  N[i] = fma(k[i], w, N[i]);  o_(i mod 2) = fma(N[i], q[i], o_(i mod 2))
+//   o = c * (o_0 + o_1)
+constexpr float kRenormLog = -32.f;
+
+// log-scale after a token with log-decay g; renorm is set when it falls
+// below kRenormLog (the token then renormalises and the scale becomes 1)
+__device__ __forceinline__ float scale_advance(float lg, float g, bool& renorm) {
+  const float x = lg + g;
+  renorm = x < kRenormLog;
+  return x;
+}
+
+// the step's scalars for log-scale x: c = exp(x) (for a renormalising token,
+// the factor applied to N before a step with c = 1) and r = exp(-x) (1 when
+// renormalising)
+__device__ __forceinline__ void scale_factors(float x, bool renorm, float& c, float& r) {
+  c = expf(x);
+  r = renorm ? 1.f : expf(-x);
+}
+
+// N = c N before a renormalising token's step
+template <int DK>
+__device__ __forceinline__ void renormalise(float (&s)[DK], float c) {
+#pragma unroll
+  for (int i = 0; i < DK; ++i) s[i] = c * s[i];
+}
+
+// state element of a scaled running state: exp(lg) * n (exactly n when lg = 0)
+__device__ __forceinline__ float scale_of_log(float lg) { return expf(lg); }
+
+template <class D, int DK>
+__device__ __forceinline__ float token_step(float (&s)[DK], UniformRow krow, UniformRow qrow, float c, float b,
+                                            float v) {
+  constexpr int G = D::kRowGroup;
+  static_assert(DK % G == 0 && G % 4 == 0, "key dim must be a multiple of the scalar load group");
+  float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < DK / G; ++gi) {
+    const u32x8 kw = *fresh(krow + gi);
+#pragma unroll
+    for (int e = 0; e < G; e += 4) {
+      const int i = gi * G + e;
+      p0 = __builtin_fmaf(s[i], D::elem(kw, e), p0);
+      p1 = __builtin_fmaf(s[i + 1], D::elem(kw, e + 1), p1);
+      p2 = __builtin_fmaf(s[i + 2], D::elem(kw, e + 2), p2);
+      p3 = __builtin_fmaf(s[i + 3], D::elem(kw, e + 3), p3);
+    }
+  }
+  const float w = b * (v - c * ((p0 + p1) + (p2 + p3)));
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < DK / G; ++gi) {
+    const u32x8 kw = *fresh(krow + gi);
+    const u32x8 qw = *fresh(qrow + gi);
+#pragma unroll
+    for (int e = 0; e < G; e += 2) {
+      const int i = gi * G + e;
+      s[i] = __builtin_fmaf(D::elem(kw, e), w, s[i]);
+      o0 = __builtin_fmaf(s[i], D::elem(qw, e), o0);
+      s[i + 1] = __builtin_fmaf(D::elem(kw, e + 1), w, s[i + 1]);
+      o1 = __builtin_fmaf(s[i + 1], D::elem(qw, e + 1), o1);
+    }
+  }
+  return c * (o0 + o1);
+}
+
+// ---------------------------------------------------------------------------
+// The per-token steps with k and q delivered by DPP row broadcast.
+//
+// Used by the prefill scan (token_step_dpp) and the recurrent comparator
+// (token_step_plain_dpp).  Instead of scalar loads (whose cache misses
 // stall the wave), every lane 16 r + c vector-loads elements 8c .. 8c+7 of
 // the token's k and q rows (each 16-lane row holds a full copy) and
 // v_fmac_f32_dpp with row_newbcast:c reads element 8c + e from lane c of the
 // lane's own row.  The arithmetic is token_step's, operation for operation
 // and accumulator for accumulator (fma(a, b, c) = fma(b, a, c) exactly), so
 // both routines produce identical bits; the GPU tests compare prefill (this
-// routine) with decode (token_step) bit for bit.
+// routine) with decode (token_step) bit for bit.  The same holds for the
+// plain pair (token_step_plain_dpp / token_step_plain).
 //
 // Hazard: a DPP instruction must not read a VGPR written by a VALU
 // instruction in the two preceding cycles.  The converted k and q values are
@@ -205,8 +314,8 @@ __device__ __forceinline__ void unpack_kq(const KQRaw<D>& r, float (&kf)[8], flo
 }
 
 template <int DK>
-__device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf)[8], const float (&qf)[8],
-                                                float alpha, float beta, float v) {
+__device__ __forceinline__ float token_step_plain_dpp(float (&s)[DK], const float (&kf)[8], const float (&qf)[8],
+                                                      float alpha, float beta, float v) {
   static_assert(DK % 16 == 0 && DK <= 128, "one 16-lane row holds the key row");
   asm volatile("s_nop 1" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
                "v"(kf[7]));
@@ -247,19 +356,126 @@ __device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf
   return o0 + o1;
 }
 
-// The scan's loop over tokens t = 0 .. n-1 (n >= 1) of one stretch of a
-// sequence, token t at row row0 + t * H of v and o and at row
-// kq0 + t * Hk of q and k: output o_t to column col of its row of o, state s
-// updated in place; alpha_l / beta_l hold token t's decay and beta in lane t.  k, q and v of token t+1 are fetched into the
-// other of two register buffers as token t starts (no copies between them).
-// Every fetch is issued (its index is clamped to token n-1), so the wait
-// before a token's first use of its operands covers that token's loads only,
-// and v stays undecoded until then.
+// token_step with k and q from DPP row broadcast (the prefill scan's delivery)
+template <int DK>
+__device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf)[8], const float (&qf)[8], float c,
+                                                float b, float v) {
+  static_assert(DK % 16 == 0 && DK <= 128, "one 16-lane row holds the key row");
+  asm volatile("s_nop 1" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
+               "v"(kf[7]));
+  float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+  static_for<0, DK / 8>([&](auto nc) {
+    constexpr int n = decltype(nc)::value;
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      const int i = 8 * n + e;
+      fmac_bcast<n>(p0, kf[e], s[i]);
+      fmac_bcast<n>(p1, kf[e + 1], s[i + 1]);
+      fmac_bcast<n>(p2, kf[e + 2], s[i + 2]);
+      fmac_bcast<n>(p3, kf[e + 3], s[i + 3]);
+    }
+  });
+  const float w = b * (v - c * ((p0 + p1) + (p2 + p3)));
+  asm volatile("s_nop 1" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
+               "v"(qf[7]));
+  float o0 = 0.f, o1 = 0.f;
+  // software-pipelined as in token_step_plain_dpp: the updates of elements
+  // 2j, 2j+1 are followed by the output terms of elements 2j-2, 2j-1
+  static_for<0, DK / 2 + 1>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < DK / 2) {
+      constexpr int i = 2 * j, n = i / 8, e = i % 8;
+      fmac_bcast<n>(s[i], kf[e], w);
+      fmac_bcast<n>(s[i + 1], kf[e + 1], w);
+    }
+    if constexpr (j >= 1) {
+      constexpr int i = 2 * j - 2, n = i / 8, e = i % 8;
+      fmac_bcast<n>(o0, qf[e], s[i]);
+      fmac_bcast<n>(o1, qf[e + 1], s[i + 1]);
+    }
+  });
+  return c * (o0 + o1);
+}
+
+// The CPR scan's loop over tokens t = 0 .. n-1 (n >= 1) of one stretch of a
+// sequence that starts on a chunk boundary: token t at row row0 + t * H of v
+// and o and at row kq0 + t * Hk of q and k; output o_t to column col of its
+// row of o; the state (N, from scale 1) updated in place.  Lane t holds token
+// t's step scalars c_l and b_l = beta r (scale_factors); bit t of renorm is
+// set when token t renormalises.  k, q and v of token t+1 are fetched as soon
+// as token t's have been unpacked; every fetch is issued (its index is
+// clamped to token n-1), so the wait before a token's first use of its
+// operands covers that token's loads only.  Rows are addressed as a
+// wave-uniform base plus a 32-bit lane offset (one VGPR per operand kind).
 template <class D, int DK, int DV>
 __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T* __restrict__ kp,
                                             const typename D::T* __restrict__ qp, const typename D::T* __restrict__ vp,
-                                            typename D::T* __restrict__ op, size_t row0, int H, size_t kq0,
-                                            int Hk, int n, int col, int lane, float alpha_l, float beta_l) {
+                                            typename D::T* __restrict__ op, size_t row0, int H, size_t kq0, int Hk,
+                                            int n, int col, int lane, float c_l, float b_l, uint64_t renorm) {
+  typedef typename D::T T;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  constexpr int nq = sizeof(T) == 2 ? 1 : 2;  // 16-byte loads per 8 elements
+  const uint32_t kq_stride = (uint32_t)(Hk * DK * sizeof(T)), v_stride = (uint32_t)(H * DV * sizeof(T));
+  const BufRsrc rk = buf_rsrc(kp + kq0 * DK, (uint32_t)(n - 1) * kq_stride + DK * sizeof(T));
+  const BufRsrc rq = buf_rsrc(qp + kq0 * DK, (uint32_t)(n - 1) * kq_stride + DK * sizeof(T));
+  const BufRsrc rv = buf_rsrc(vp + row0 * DV, (uint32_t)(n - 1) * v_stride + DV * sizeof(T));
+  const BufRsrc ro = buf_rsrc(op + row0 * DV, (uint32_t)(n - 1) * v_stride + DV * sizeof(T));
+  // lanes past the row repeat an in-bounds slot
+  const uint32_t kq_off = (uint32_t)(((lane & 15) & (DK / 8 - 1)) * 8 * sizeof(T));
+  const uint32_t v_off = (uint32_t)(col * sizeof(T));
+  KQRaw<D> raw;
+  uint32_t vb;
+  auto fetch = [&](int t) {
+    const uint32_t tt = (uint32_t)min(t, n - 1);
+#pragma unroll
+    for (int m = 0; m < nq; ++m) {
+      const u32x4v a =
+          __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rk, kq_off + 16 * m, tt * kq_stride, 0));
+      const u32x4v b =
+          __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, kq_off + 16 * m, tt * kq_stride, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        raw.w[4 * m + e] = a[e];
+        raw.w[4 * nq + 4 * m + e] = b[e];
+      }
+    }
+    if constexpr (sizeof(T) == 2)
+      vb = __builtin_amdgcn_raw_buffer_load_b16(rv, v_off, tt * v_stride, 0);
+    else
+      vb = __builtin_amdgcn_raw_buffer_load_b32(rv, v_off, tt * v_stride, 0);
+  };
+  fetch(0);
+  for (int t = 0; t < n; ++t) {
+    float kf[8], qf[8];
+    unpack_kq<D>(raw, kf, qf);
+    uint32_t vbits = vb;
+    asm volatile("" : "+v"(vbits));  // decode v here, not next to its load
+    const float vcur = D::from_bits(vbits);
+    fetch(t + 1);
+    float cs = lane_bcast(c_l, t);
+    if ((renorm >> t) & 1) {
+      renormalise<DK>(s, cs);
+      cs = 1.f;
+    }
+    const float out = token_step_dpp<DK>(s, kf, qf, cs, lane_bcast(b_l, t), vcur);
+    if constexpr (sizeof(T) == 2)
+      __builtin_amdgcn_raw_buffer_store_b16(D::round(out), ro, v_off, (uint32_t)t * v_stride, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ro, v_off, (uint32_t)t * v_stride, 0);
+  }
+}
+
+// The plain scan loop (comparators): tokens t = 0 .. n-1 (n >= 1) of one
+// stretch of a sequence, laid out as for scan_tokens, with the plain step;
+// alpha_l / beta_l hold token t's decay and beta in lane t.  k, q and v of
+// token t+1 are fetched into the other of two register buffers as token t
+// starts.
+template <class D, int DK, int DV>
+__device__ __forceinline__ void scan_tokens_plain(float (&s)[DK], const typename D::T* __restrict__ kp,
+                                                  const typename D::T* __restrict__ qp,
+                                                  const typename D::T* __restrict__ vp, typename D::T* __restrict__ op,
+                                                  size_t row0, int H, size_t kq0, int Hk, int n, int col, int lane,
+                                                  float alpha_l, float beta_l) {
   KQRaw<D> r0, r1;
   uint32_t v0, v1;
   auto fetch = [&](KQRaw<D>& r, uint32_t& vb, int t) {
@@ -275,7 +491,7 @@ __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T*
     asm volatile("" : "+v"(vbits));  // decode v here, not next to its load
     const float vcur = D::from_bits(vbits);
     fetch(rn, vn, t + 1);
-    const float out = token_step_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
+    const float out = token_step_plain_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
     D::store(op + (row0 + (size_t)t * H) * DV, col, out);
   };
   fetch(r0, v0, 0);

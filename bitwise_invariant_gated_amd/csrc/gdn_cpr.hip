@@ -63,6 +63,8 @@ struct PrefillArgs {
   void* tail_g;
   void* tail_beta;
   int32_t* tail_len;
+  float* lgs;               // [rows, H] log-scale of s_run (the cache's run_log_scale), or null
+  int32_t run_materialize;  // 1: the partial last chunk writes the state exp(lg) N to s_run (no lgs)
   void* o;
   int32_t* full_base;  // [N+1] prefix sums of full chunks per sequence
   int32_t* all_base;   // [N+1] prefix sums of all chunks (full + partial)
@@ -89,6 +91,7 @@ struct DecodeArgs {
   void* tail_g;
   void* tail_beta;
   int32_t* tail_len;
+  float* lgs;  // [rows, H] log-scale of s_run, or null (written 0 when s_run becomes a boundary)
   void* o;
   int32_t* flag;  // [N*H] 1 = this pair resynchronises in this step
   uint8_t* prod;  // [N*H] chunk-product slots of prod_slot_bytes
@@ -344,7 +347,10 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
   }
   put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
   if (L % C == 0) put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
-  if (blockIdx.z == 0 && threadIdx.x == 0) a.tail_len[ch] = L % C;
+  if (blockIdx.z == 0 && threadIdx.x == 0) {
+    a.tail_len[ch] = L % C;
+    if (L % C == 0 && a.lgs) a.lgs[ch] = 0.f;
+  }
 }
 
 template <int DK, int DV>
@@ -361,6 +367,7 @@ __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   chain_step_f32<DK, NB>(sm);
   put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
   put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
+  if (blockIdx.z == 0 && threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
 }
 
 // bf16 path: one work-group per (sequence, head, block of CB = WAVES * NT * 16
@@ -491,7 +498,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
   if (a.all_chunks) return;
   if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
-  if (blockIdx.z == 0 && tid == 0) a.tail_len[ch] = L % C;
+  if (blockIdx.z == 0 && tid == 0) {
+    a.tail_len[ch] = L % C;
+    if (L % C == 0 && a.lgs) a.lgs[ch] = 0.f;
+  }
 }
 
 // decode resync, bf16 path: one wave per (sequence, head, 32 state columns),
@@ -511,6 +521,7 @@ __global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
   chain_step_bf16_global<DK, DV, NT>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb0, lane);
   store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
   store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
+  if (blockIdx.z == 0 && lane == 0 && a.lgs) a.lgs[ch] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -544,24 +555,49 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
 
   const T* gp = (const T*)a.g;
   const T* bp = (const T*)a.beta;
-  float alpha_l = 1.f, beta_l = 0.f;
+  float g_l = 0.f, beta_l = 0.f;
   if (lane < n) {
     const size_t r = (tok0 + lane) * H + h;
-    alpha_l = decay_of(D::load(gp, r));
+    g_l = D::load(gp, r);
     beta_l = D::load(bp, r);
   }
+  // log-scale of the running state after every token, in token order from
+  // the boundary (lg = 0); lane t keeps token t's
+  float lg = 0.f, x_l = 0.f;
+  bool ren_l = false;
+  for (int t = 0; t < n; ++t) {
+    bool ren;
+    const float x = scale_advance(lg, lane_bcast(g_l, t), ren);
+    if (lane == t) {
+      x_l = x;
+      ren_l = ren;
+    }
+    lg = ren ? 0.f : x;
+  }
+  float c_l, r_l;
+  scale_factors(x_l, ren_l, c_l, r_l);
+  const float b_l = beta_l * r_l;
+  const uint64_t renorm = __ballot(ren_l && lane < n);
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
   scan_tokens<D, DK, DV>(s, kp, qp, vp, (T*)a.o, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col, lane,
-                         alpha_l, beta_l);
+                         c_l, b_l, renorm);
   const int nall = (L + C - 1) / C;
   if (c == nall - 1 && (L % C) != 0) {
-    // last, partial chunk: its end state is the running state, its tokens the tail
+    // last, partial chunk: its end state is the running state (N with
+    // log-scale lg, or the state itself when materialised), its tokens the tail
     const size_t ch = cache_row(a.slot, i) * H + h;
     float* R = a.s_run + ch * SS;
+    if (a.run_materialize) {
+      const float e = scale_of_log(lg);
 #pragma unroll
-    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+      for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = e * s[ii];
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+      if (blockIdx.z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
+    }
     T* tv = (T*)a.tail_v + ch * C * DV;
     for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
     if (blockIdx.z == 0) {
@@ -589,7 +625,8 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   const int col = threadIdx.x;
   const size_t SS = (size_t)DK * DV;
   const int tl = a.tail_len[ch];
-  __syncthreads();  // every wave has read tail_len before it is rewritten below
+  const float lg = a.lgs[ch];
+  __syncthreads();  // every wave has read tail_len and lgs before they are rewritten below
   if ((unsigned)tl >= (unsigned)C) {  // not a valid cache: touch nothing
     if (col == 0) a.flag[sh] = 0;
     return;
@@ -600,11 +637,18 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
-  const float alpha = decay_of(D::load((const T*)a.g, sh));
+  bool ren;
+  const float x = scale_advance(lg, D::load((const T*)a.g, sh), ren);
+  float cs, rs;
+  scale_factors(x, ren, cs, rs);
+  if (ren) {
+    renormalise<DK>(s, cs);
+    cs = 1.f;
+  }
   const float bt = D::load((const T*)a.beta, sh);
   const float vv = D::load((const T*)a.v, sh * DV + col);
   const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
-  const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
+  const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
   D::store((T*)a.o, sh * DV + col, out);
   // append the token to the tail
   T* tk = (T*)a.tail_k + (ch * C + tl) * DK;
@@ -621,7 +665,27 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   }
   if (col == 0) {
     a.tail_len[ch] = full ? 0 : tl + 1;
+    a.lgs[ch] = (full || ren) ? 0.f : x;  // a full tail resynchronises to a boundary (scale 1)
     a.flag[sh] = full ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the running state of every (sequence, head) from its scaled form:
+// out = exp(lg) * s_run, row-major [d_k][d_v] (the same product the scan
+// uses when it writes a final state itself)
+
+__global__ __launch_bounds__(256) void k_cache_state(const float* __restrict__ s_run, const float* __restrict__ lgs,
+                                                    const int32_t* __restrict__ slot, float* __restrict__ out,
+                                                    int H, int SS4) {
+  const size_t sh = (size_t)blockIdx.x * H + blockIdx.y;
+  const size_t ch = cache_row(slot, blockIdx.x) * H + blockIdx.y;
+  const float e = scale_of_log(lgs[ch]);
+  const float4* src = reinterpret_cast<const float4*>(s_run) + ch * SS4;
+  float4* dst = reinterpret_cast<float4*>(out) + sh * SS4;
+  for (int i = threadIdx.x; i < SS4; i += 256) {
+    const float4 x = src[i];
+    dst[i] = make_float4(e * x.x, e * x.y, e * x.z, e * x.w);
   }
 }
 
@@ -646,6 +710,7 @@ struct ContArgs {
   void* tail_g;
   void* tail_beta;
   int32_t* tail_len;
+  float* lgs;  // [rows, H] log-scale of s_run
   void* o;
   int32_t* flag;        // [N*H] 1 = this pair closes its chunk in the head
   int32_t* body_start;  // [N] first token row after the head
@@ -664,7 +729,8 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   const int col = threadIdx.x;
   const size_t SS = (size_t)DK * DV;
   const int tl = a.tail_len[ch];
-  __syncthreads();  // every wave has read tail_len before it is rewritten below
+  float lg = a.lgs[ch];
+  __syncthreads();  // every wave has read tail_len and lgs before they are rewritten below
   const int L = a.cu[i + 1] - a.cu[i];
   const int nh = ((unsigned)tl < (unsigned)C && tl > 0) ? min(C - tl, L) : 0;
   if (h == 0 && col == 0) a.body_start[i] = a.cu[i] + nh;
@@ -681,11 +747,19 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   const T* bp = (const T*)a.beta;
   for (int t = 0; t < nh; ++t) {
     const size_t row = (size_t)(a.cu[i] + t) * H + h;
-    const float alpha = decay_of(D::load(gp, row));
+    bool ren;
+    const float x = scale_advance(lg, D::load(gp, row), ren);
+    float cs, rs;
+    scale_factors(x, ren, cs, rs);
+    if (ren) {
+      renormalise<DK>(s, cs);
+      cs = 1.f;
+    }
+    lg = ren ? 0.f : x;
     const float bt = D::load(bp, row);
     const float vv = D::load(vp, row * DV + col);
     const size_t kr = kq_row((size_t)(a.cu[i] + t), h, a.Hk, a.G);
-    const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
+    const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
     D::store((T*)a.o, row * DV + col, out);
     const size_t tr = ch * C + tl + t;  // tail row
     T* tk = (T*)a.tail_k + tr * DK;
@@ -703,6 +777,7 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   }
   if (col == 0) {
     a.tail_len[ch] = full ? 0 : tl + nh;
+    a.lgs[ch] = full ? 0.f : lg;
     a.flag[sh] = full ? 1 : 0;
   }
 }
@@ -768,8 +843,8 @@ __global__ __launch_bounds__(64, 3) void k_cmp_rec_prefill(const CmpArgs a) {
       alpha_l = decay_of(D::load(gp, r));
       beta_l = D::load(bp, r);
     }
-    scan_tokens<D, DK, DV>(s, kp, qp, vp, op, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col, lane,
-                           alpha_l, beta_l);
+    scan_tokens_plain<D, DK, DV>(s, kp, qp, vp, op, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col,
+                                 lane, alpha_l, beta_l);
   }
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) a.state[sh * SS + (size_t)ii * DV + col] = s[ii];
@@ -791,7 +866,7 @@ __global__ __launch_bounds__(DV) void k_cmp_rec_decode(const CmpArgs a) {
   const float bt = D::load((const T*)a.beta, sh);
   const float vv = D::load((const T*)a.v, sh * DV + col);
   const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
-  const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
+  const float out = token_step_plain<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
   D::store((T*)a.o, sh * DV + col, out);
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
@@ -2214,6 +2289,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   CHECK_PTR(cache_out->tail_g, "cache.tail_g");
   CHECK_PTR(cache_out->tail_beta, "cache.tail_beta");
   CHECK_PTR(cache_out->tail_len, "cache.tail_len");
+  CHECK_PTR(cache_out->run_log_scale, "cache.run_log_scale");
   CHECK_OPT_PTR(cache_out->slot_index, "cache.slot_index");
   if (total_tokens > 0) {
     CHECK_PTR(q, "q");
@@ -2253,6 +2329,8 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.tail_g = cache_out->tail_g;
   a.tail_beta = cache_out->tail_beta;
   a.tail_len = cache_out->tail_len;
+  a.lgs = cache_out->run_log_scale;
+  a.run_materialize = 0;
   a.o = o;
   a.full_base = (int32_t*)(ws + L.full_base);
   a.all_base = (int32_t*)(ws + L.all_base);
@@ -2292,6 +2370,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   CHECK_PTR(cache->tail_g, "cache.tail_g");
   CHECK_PTR(cache->tail_beta, "cache.tail_beta");
   CHECK_PTR(cache->tail_len, "cache.tail_len");
+  CHECK_PTR(cache->run_log_scale, "cache.run_log_scale");
   CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
   const DecodeLayout L = decode_layout(*shape, num_seqs);
   if (!workspace || workspace_bytes < L.total)
@@ -2313,6 +2392,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   a.tail_g = cache->tail_g;
   a.tail_beta = cache->tail_beta;
   a.tail_len = cache->tail_len;
+  a.lgs = cache->run_log_scale;
   a.o = o;
   a.flag = (int32_t*)(ws + L.flag);
   a.prod = (uint8_t*)(ws + L.prod);
@@ -2342,6 +2422,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   CHECK_PTR(cache->tail_g, "cache.tail_g");
   CHECK_PTR(cache->tail_beta, "cache.tail_beta");
   CHECK_PTR(cache->tail_len, "cache.tail_len");
+  CHECK_PTR(cache->run_log_scale, "cache.run_log_scale");
   CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
   if (total_tokens > 0) {
     CHECK_PTR(q, "q");
@@ -2377,6 +2458,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   ca.tail_g = cache->tail_g;
   ca.tail_beta = cache->tail_beta;
   ca.tail_len = cache->tail_len;
+  ca.lgs = cache->run_log_scale;
   ca.o = o;
   ca.flag = (int32_t*)(wd + L.dec.flag);
   ca.body_start = body_start;
@@ -2393,6 +2475,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   da.tail_g = cache->tail_g;
   da.tail_beta = cache->tail_beta;
   da.tail_len = cache->tail_len;
+  da.lgs = cache->run_log_scale;
   da.flag = ca.flag;
   da.prod = (uint8_t*)(wd + L.dec.prod);
   da.gamn = (float*)(wd + L.dec.gamn);
@@ -2421,6 +2504,8 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   pa.tail_g = cache->tail_g;
   pa.tail_beta = cache->tail_beta;
   pa.tail_len = cache->tail_len;
+  pa.lgs = cache->run_log_scale;
+  pa.run_materialize = 0;
   pa.o = o;
   pa.full_base = (int32_t*)(ws + L.pre.full_base);
   pa.all_base = (int32_t*)(ws + L.pre.all_base);
@@ -2494,6 +2579,8 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.tail_g = ws + L.tail_g;
   pa.tail_beta = ws + L.tail_b;
   pa.tail_len = (int32_t*)(ws + L.tail_len);
+  pa.lgs = nullptr;
+  pa.run_materialize = 1;  // hT is the final state itself
   pa.o = o;
   pa.full_base = (int32_t*)(ws + L.pre.full_base);
   pa.all_base = (int32_t*)(ws + L.pre.all_base);
@@ -2675,6 +2762,7 @@ extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int3
   CHECK_PTR(cache->tail_g, "cache.tail_g");
   CHECK_PTR(cache->tail_beta, "cache.tail_beta");
   CHECK_PTR(cache->tail_len, "cache.tail_len");
+  CHECK_PTR(cache->run_log_scale, "cache.run_log_scale");
   CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
   const DecodeLayout L = decode_layout(*shape, num_seqs);
   if (!workspace || workspace_bytes < L.total)
@@ -2696,6 +2784,7 @@ extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int3
   a.tail_g = cache->tail_g;
   a.tail_beta = cache->tail_beta;
   a.tail_len = cache->tail_len;
+  a.lgs = cache->run_log_scale;
   a.o = o;
   a.flag = (int32_t*)(ws + L.flag);
   a.prod = (uint8_t*)(ws + L.prod);
@@ -2707,6 +2796,28 @@ extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int3
   return dispatch<CmpChunkDecodeFn>(*shape, a, (hipStream_t)stream, fn);
 }
 
+extern "C" gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t num_seqs, const gdn_cpr_cache* cache,
+                                          float* state_out, void* stream) {
+  const char* fn = "gdn_cpr_cache_state";
+  std::string why;
+  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  if (num_seqs == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  CHECK_PTR(cache->s_run, "cache.s_run");
+  CHECK_PTR(cache->run_log_scale, "cache.run_log_scale");
+  CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
+  CHECK_PTR(state_out, "state_out");
+  if (state_out == cache->s_run) return fail(GDN_ERR_INVALID_ARG, "%s: state_out aliases cache.s_run", fn);
+  const int SS4 = shape->head_dim_k * shape->head_dim_v / 4;
+  hipLaunchKernelGGL(k_cache_state, dim3(num_seqs, shape->num_heads), dim3(256), 0, (hipStream_t)stream,
+                     cache->s_run, cache->run_log_scale, cache->slot_index, state_out, shape->num_heads, SS4);
+  return launch_status(fn);
+}
+
 extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) {
   g_events = (events && n_events > 0) ? events : nullptr;
   g_n_events = g_events ? n_events : 0;
@@ -2715,8 +2826,10 @@ extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) 
 extern "C" const char* gdn_cpr_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" const char* gdn_cpr_numerics_id(void) {
-  return "gdn_cpr numerics v3: token step fp32 (decay mul; k and q dots as 2-way even/odd explicit-fma "
-         "chains; explicit-fma rank-1 update); exp = ocml expf; gamma = left-to-right fp32 cumsum; "
+  return "gdn_cpr numerics v4: token step fp32 on a scaled running state M = exp(lg) N (lg += g, fp32; "
+         "lg < -32: N = exp(lg) N, lg = 0; c = exp(lg), r = exp(-lg); k dot as 4-way i mod 4 explicit-fma "
+         "chains summed (p0+p1)+(p2+p3), p = c dot; u = beta (v - p); w = u r; explicit-fma rank-1 update "
+         "N += w k^T; q dot 2-way even/odd, o = c dot); exp = ocml expf; gamma = left-to-right fp32 cumsum; "
          "fp32 inputs: chunk products and boundary chain fp32 VALU with ascending explicit-fma sums and "
          "column-wise forward substitution; bf16 inputs: G, W^T, U and the boundary chain on "
          "v_mfma_f32_16x16x32_bf16 (k slots k0+4g+{0..3}, k0+16+4g+{0..3}; k steps ascending) with bf16 "

@@ -16,6 +16,11 @@
  *     parallel, each starting from its boundary state;
  *   - decode runs the same per-token step and, every C tokens, replaces its
  *     running state by the chunk-boundary computation over the last C tokens.
+ * Between boundaries the per-token step keeps the running state as
+ * exp(lg) N: the decay accumulates in one scalar lg per head instead of
+ * being applied to every state element at every token (gdn_cpr_cache,
+ * run_log_scale).  The per-token step is the same routine in prefill and
+ * decode.
  * Every output of this library is therefore bit-identical between prefill
  * and decode, and between a sequence run alone and the same sequence packed
  * with others.  The results match the exact recurrence within fp32 rounding
@@ -95,8 +100,11 @@ typedef struct {
  * is position independent: copying it elsewhere (or to the host and back)
  * and continuing gives the same bits.
  *   s_bnd     [N, H, d_k, d_v] fp32  state at the last chunk boundary
- *   s_run     [N, H, d_k, d_v] fp32  state after the last token (the final
- *                                    state); equals s_bnd when tail_len = 0
+ *   s_run     [N, H, d_k, d_v] fp32  state after the last token in scaled
+ *                                    form: the state is exp(run_log_scale) *
+ *                                    s_run (gdn_cpr_cache_state writes it
+ *                                    out); when tail_len = 0, s_run = s_bnd
+ *                                    and run_log_scale = 0
  *   tail_k    [N, H, C, d_k] dtype   tokens since that boundary
  *   tail_v    [N, H, C, d_v] dtype
  *   tail_g    [N, H, C]      dtype
@@ -113,6 +121,14 @@ typedef struct {
  *                                    touched, so a serving engine can keep a
  *                                    pool of cache rows and pass each step's
  *                                    batch by row number.
+ *   run_log_scale [N, H] fp32        log of s_run's scale: the cumulative
+ *                                    log-decay since the last boundary (or
+ *                                    since the last renormalisation, which
+ *                                    sets it to 0 when it would fall below
+ *                                    -32).  Keeping the decay in this scalar
+ *                                    rather than in every state element is
+ *                                    part of the pinned per-token step that
+ *                                    prefill and decode share.
  */
 typedef struct {
   float* s_bnd;
@@ -123,6 +139,7 @@ typedef struct {
   void* tail_beta;
   int32_t* tail_len;
   const int32_t* slot_index;
+  float* run_log_scale;
 } gdn_cpr_cache;
 
 /*
@@ -200,6 +217,17 @@ gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32_t num_seqs
                                     const void* q, const void* k, const void* v, const void* g,
                                     const void* beta, const int32_t* cu_seqlens, const gdn_cpr_cache* cache,
                                     void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The state after each cached sequence's last token (the final state of
+ * prefill, decode or continuation), written out from the cache's scaled form:
+ *   state_out[i, h] = exp(run_log_scale[row, h]) * s_run[row, h]
+ * with row = slot_index[i] (or i).  state_out is [N, H, d_k, d_v] fp32 and
+ * must not alias the cache.  When tail_len = 0 the result equals s_bnd bit
+ * for bit.  gdn_cpr_fwd_bwd's hT is this same product.
+ */
+gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t num_seqs, const gdn_cpr_cache* cache,
+                               float* state_out, void* stream);
 
 /*
  * Training forward + backward (the trainer_fwd case plus its gradient).

@@ -72,6 +72,12 @@ def decode_rows(db: DevBatch, start: np.ndarray, steps: int, cache):
     return outs
 
 
+def state_of(shape: gdn.LayerShape, cache) -> torch.Tensor:
+    """The state after each cached sequence's last token, exp(run_log_scale) * s_run,
+    written out by the library (gdn_cpr_cache_state)."""
+    return gdn.gdn_cpr_cache_state(shape, cache)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw bit patterns (for bit-exact comparisons; -0.0 != +0.0, NaN == NaN)."""
     t = t.detach().contiguous().cpu()

@@ -52,8 +52,8 @@ def test_workspace_size_shapes():
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
 
 
-def _cache(ptr=FAKE, slots=None):
-    return _lib.Cache(ptr, ptr, ptr, ptr, ptr, ptr, ptr, slots)
+def _cache(ptr=FAKE, slots=None, lgs=None):
+    return _lib.Cache(ptr, ptr, ptr, ptr, ptr, ptr, ptr, slots, ptr if lgs is None else lgs)
 
 
 def _prefill(lib, shape, N=2, T=128, cache=None, cu=FAKE, q=FAKE, ws=FAKE, ws_bytes=0, h0=None):
@@ -79,6 +79,8 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     assert b"aligned" in lib.gdn_cpr_last_error()
     assert _prefill(lib, s, h0=FAKE + 8) == _lib.GDN_ERR_INVALID_ARG
     assert _prefill(lib, s, cache=_cache(0)) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(lib, s, cache=_cache(lgs=0)) == _lib.GDN_ERR_INVALID_ARG
+    assert b"run_log_scale" in lib.gdn_cpr_last_error()
     assert _prefill(lib, s, N=-1) == _lib.GDN_ERR_INVALID_ARG
 
 
@@ -111,8 +113,29 @@ def test_decode_rejects_bad_arguments():
     assert dec(c=_cache(FAKE + 2)) == _lib.GDN_ERR_INVALID_ARG
     assert dec(c=_cache(FAKE, FAKE + 4)) == _lib.GDN_ERR_INVALID_ARG
     assert b"slot_index" in lib.gdn_cpr_last_error()
+    assert dec(c=_cache(lgs=0)) == _lib.GDN_ERR_INVALID_ARG
+    assert b"run_log_scale" in lib.gdn_cpr_last_error()
     assert dec(ws_bytes=16) == _lib.GDN_ERR_WORKSPACE
     assert dec(N=0) == _lib.GDN_OK
+
+
+def test_cache_state_rejects_bad_arguments():
+    lib = _lib_or_skip()
+    s = _shape()
+
+    def st(shape=s, N=2, c=_cache(), out=FAKE + 256):
+        return lib.gdn_cpr_cache_state(ctypes.byref(shape), N, ctypes.byref(c) if c is not None else None, out, None)
+
+    assert st(shape=_shape(dk=96)) == _lib.GDN_ERR_UNSUPPORTED
+    assert st(c=None) == _lib.GDN_ERR_INVALID_ARG
+    assert st(out=None) == _lib.GDN_ERR_INVALID_ARG
+    assert st(out=FAKE + 260) == _lib.GDN_ERR_INVALID_ARG
+    assert st(c=_cache(lgs=0)) == _lib.GDN_ERR_INVALID_ARG
+    assert b"run_log_scale" in lib.gdn_cpr_last_error()
+    assert st(out=FAKE) == _lib.GDN_ERR_INVALID_ARG  # aliases s_run
+    assert b"aliases" in lib.gdn_cpr_last_error()
+    assert st(N=-1) == _lib.GDN_ERR_INVALID_ARG
+    assert st(N=0) == _lib.GDN_OK
 
 
 def test_prefill_continue_rejects_bad_arguments():

@@ -16,7 +16,7 @@ import bitwise_invariant_gated_amd as gdn
 import oracle
 from gdn_synth import make_batch
 
-from gpu_util import DEV, DevBatch, as_f64, bits, note, prefill, torch_dtype
+from gpu_util import DEV, DevBatch, as_f64, bits, note, prefill, state_of, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,7 @@ def assert_cache_bitwise(c1, c2):
     assert np.array_equal(bits(c1.tail_len), bits(c2.tail_len))
     assert np.array_equal(bits(c1.s_bnd), bits(c2.s_bnd))
     assert np.array_equal(bits(c1.s_run), bits(c2.s_run))
+    assert np.array_equal(bits(c1.run_log_scale), bits(c2.run_log_scale))
     tl = c1.tail_len.cpu().numpy()
     for name in ("tail_k", "tail_v", "tail_g", "tail_beta"):
         a, b = bits(getattr(c1, name)), bits(getattr(c2, name))
@@ -150,4 +151,4 @@ def test_continuation_matches_oracle():
     torch.cuda.synchronize()
     o_ref, h_ref = oracle.recurrent_forward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0)
     assert float(np.max(np.abs(as_f64(o_seg) - o_ref))) <= 2e-2
-    assert float(np.max(np.abs(as_f64(c_seg.s_run) - h_ref))) <= 2e-2
+    assert float(np.max(np.abs(as_f64(state_of(db.shape, c_seg)) - h_ref))) <= 2e-2

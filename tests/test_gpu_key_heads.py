@@ -19,7 +19,8 @@ import bitwise_invariant_gated_amd as gdn
 import oracle
 from gdn_synth import make_batch
 
-from gpu_util import DEV, DevBatch, as_f64, bits, decode_rows, note, prefill, tol_for, torch_dtype
+from gpu_util import (DEV, DevBatch, as_f64, bits, decode_rows, note, prefill, shape_of, state_of, tol_for,
+                      torch_dtype)
 from test_gpu_continue import assert_cache_bitwise, run_segments
 from test_gpu_fwd_bwd import check_grads, run_fwd_bwd
 
@@ -50,7 +51,8 @@ def test_grouped_prefill_equals_repeated_heads_and_oracle(dtype, dk, dv, H, Hk):
     o_ref, h_ref = oracle.recurrent_forward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0)
     m = float(np.max(np.abs(o_ref)))
     assert float(np.max(np.abs(as_f64(o) - o_ref))) <= tol_for(b, m)
-    assert float(np.max(np.abs(as_f64(c.s_run) - h_ref))) <= tol_for(b, float(np.max(np.abs(h_ref))))
+    h = as_f64(state_of(shape_of(b), c))
+    assert float(np.max(np.abs(h - h_ref))) <= tol_for(b, float(np.max(np.abs(h_ref))))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -70,6 +72,7 @@ def test_grouped_prefill_equals_decode(dtype):
     ref = o_full[torch.from_numpy(rows.reshape(-1)).to(DEV)].view(m, len(pre), 6, 128)
     assert np.array_equal(bits(o_dec), bits(ref))
     assert np.array_equal(bits(c.s_run), bits(c_full.s_run))
+    assert np.array_equal(bits(c.run_log_scale), bits(c_full.run_log_scale))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

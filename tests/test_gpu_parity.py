@@ -12,7 +12,7 @@ import torch
 import oracle
 from gdn_synth import make_batch, workload
 
-from gpu_util import (DevBatch, as_f64, bits, decode_rows, note, prefill, tol_for)
+from gpu_util import (DevBatch, as_f64, bits, decode_rows, note, prefill, state_of, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,11 +21,11 @@ def _oracle(b):
     return oracle.recurrent_forward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0)
 
 
-def _check_vs_oracle(b, o, cache, seqs=None):
+def _check_vs_oracle(b, o, cache, shape):
     o_ref, h_ref = _oracle(b)
     tol_o = tol_for(b, float(np.max(np.abs(o_ref))) if o_ref.size else 1.0)
     err_o = float(np.max(np.abs(as_f64(o) - o_ref))) if o_ref.size else 0.0
-    s_run = as_f64(cache.s_run)
+    s_run = as_f64(state_of(shape, cache))
     tol_s = tol_for(b, float(np.max(np.abs(h_ref))) if h_ref.size else 1.0)
     err_s = float(np.max(np.abs(s_run - h_ref))) if h_ref.size else 0.0
     assert err_o <= tol_o, (err_o, tol_o)
@@ -35,6 +35,7 @@ def _check_vs_oracle(b, o, cache, seqs=None):
 
 def _cache_equal(c1, c2, tail_len):
     assert np.array_equal(bits(c1.s_run), bits(c2.s_run))
+    assert np.array_equal(bits(c1.run_log_scale), bits(c2.run_log_scale))
     assert np.array_equal(bits(c1.s_bnd), bits(c2.s_bnd))
     assert np.array_equal(bits(c1.tail_len), bits(c2.tail_len))
     tl = bits(c1.tail_len)
@@ -53,7 +54,7 @@ def test_tiny_f32_prefill_matches_oracle_and_decode_is_bitwise():
     db = DevBatch(b)
     o_p, c_p = prefill(db)
     torch.cuda.synchronize()
-    _check_vs_oracle(b, o_p, c_p)
+    _check_vs_oracle(b, o_p, c_p, db.shape)
     # decode the same 256 tokens from an empty prefill (zero-length sequence)
     b0 = b.truncate([0])
     db0 = DevBatch(b0)
@@ -75,7 +76,7 @@ def test_ragged_prefill_matches_oracle(dtype, dk, dv):
     db = DevBatch(b)
     o, c = prefill(db)
     torch.cuda.synchronize()
-    _check_vs_oracle(b, o, c)
+    _check_vs_oracle(b, o, c, db.shape)
     tl = bits(c.tail_len)
     for i, L in enumerate(RAGGED):
         assert np.all(tl[i] == L % 64)
@@ -118,6 +119,7 @@ def test_alone_equals_packed_bitwise():
         sl = b.seq_slice(i)
         assert np.array_equal(bits(oi), ob[sl]), i
         assert np.array_equal(bits(ci.s_run)[0], bits(c.s_run)[i]), i
+        assert np.array_equal(bits(ci.run_log_scale)[0], bits(c.run_log_scale)[i]), i
         assert np.array_equal(bits(ci.s_bnd)[0], bits(c.s_bnd)[i]), i
     # reversed batch order
     order = list(range(len(lens)))[::-1]
@@ -181,5 +183,5 @@ def test_prefill_5x2048_matches_oracle():
     db = DevBatch(b)
     o, c = prefill(db)
     torch.cuda.synchronize()
-    err_o, err_s = _check_vs_oracle(b, o, c)
+    err_o, err_s = _check_vs_oracle(b, o, c, db.shape)
     print(f"prefill_5x2048: max|o err| = {err_o:.3e}, max|state err| = {err_s:.3e}")

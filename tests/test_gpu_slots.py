@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 def pool_like(shape, rows, fill=3.0):
     c = gdn.alloc_cache(shape, rows)
-    for t in c.tensors()[:-1]:
+    for t in c.tensors():
         t.fill_(fill)
     c.tail_len.fill_(7)
     return c
@@ -41,6 +41,7 @@ def row_equal(pool, row, ref, i):
     assert np.array_equal(bits(pool.tail_len[row]), bits(ref.tail_len[i]))
     assert np.array_equal(bits(pool.s_bnd[row]), bits(ref.s_bnd[i]))
     assert np.array_equal(bits(pool.s_run[row]), bits(ref.s_run[i]))
+    assert np.array_equal(bits(pool.run_log_scale[row]), bits(ref.run_log_scale[i]))
     for name in ("tail_k", "tail_v", "tail_g", "tail_beta"):
         assert np.array_equal(bits(getattr(pool, name)[row])[:, :tl], bits(getattr(ref, name)[i])[:, :tl]), name
 
@@ -92,4 +93,5 @@ def test_slot_indexed_cache_matches_plain_cache(dtype):
     for r in set(range(8)) - set(slots):  # untouched rows
         assert int(pool.tail_len[r, 0]) == 7
         assert float(pool.s_run[r].min()) == 3.0 and float(pool.s_run[r].max()) == 3.0
+        assert float(pool.run_log_scale[r].min()) == 3.0 and float(pool.run_log_scale[r].max()) == 3.0
         assert float(pool.s_bnd[r].min()) == 3.0 and float(pool.s_bnd[r].max()) == 3.0

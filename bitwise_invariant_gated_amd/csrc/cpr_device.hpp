@@ -744,29 +744,32 @@ struct alignas(16) ChunkLdsB {
 
 // Stage one chunk (bf16 rows) into LDS: K and V row-major, g (into gam), beta.
 // Row t of k starts at k + (k_row0 + t * k_stride) * DK (likewise v); g and
-// beta at gb0 + t * gb_stride.
+// beta at gb0 + t * gb_stride.  Rows t >= n (a chunk shorter than the slot)
+// are identity padding: k = v = 0, g = beta = 0.
 template <int DK, int DV>
 __device__ __forceinline__ void stage_chunk_bf16(ChunkLdsB<DK, DV>& sm, const uint16_t* __restrict__ k,
                                                  size_t k_row0, size_t k_stride,
                                                  const uint16_t* __restrict__ v, size_t v_row0,
                                                  size_t v_stride, const uint16_t* __restrict__ g,
                                                  const uint16_t* __restrict__ beta, size_t gb0,
-                                                 size_t gb_stride) {
+                                                 size_t gb_stride, int n) {
   const int tid = threadIdx.x, nt = blockDim.x;
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   for (int idx = tid; idx < kChunk * DK / 8; idx += nt) {
     const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) =
-        *reinterpret_cast<const u32x4v*>(k + (k_row0 + (size_t)t * k_stride) * DK + i0);
+    u32x4v w = {0u, 0u, 0u, 0u};
+    if (t < n) w = *reinterpret_cast<const u32x4v*>(k + (k_row0 + (size_t)t * k_stride) * DK + i0);
+    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
   }
   for (int idx = tid; idx < kChunk * DV / 8; idx += nt) {
     const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) =
-        *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
+    u32x4v w = {0u, 0u, 0u, 0u};
+    if (t < n) w = *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
+    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) = w;
   }
   for (int t = tid; t < kChunk; t += nt) {
-    sm.gam[t] = Bf16::load(g, gb0 + (size_t)t * gb_stride);
-    sm.beta[t] = Bf16::load(beta, gb0 + (size_t)t * gb_stride);
+    sm.gam[t] = t < n ? Bf16::load(g, gb0 + (size_t)t * gb_stride) : 0.f;
+    sm.beta[t] = t < n ? Bf16::load(beta, gb0 + (size_t)t * gb_stride) : 0.f;
   }
   __syncthreads();
 }

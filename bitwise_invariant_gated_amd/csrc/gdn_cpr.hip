@@ -36,6 +36,13 @@ using namespace cpr;
 
 namespace {
 
+// C is the row count of the chunk machinery (chunk-product slots, MFMA tiles,
+// LDS arrays): 64.  The layer's chunk length Cl (the boundary and
+// resynchronisation period, 16, 32 or 64) is a runtime argument: a chunk of
+// Cl tokens fills the first Cl rows of a 64-row slot and the other rows are
+// identity padding (k = v = 0, g = beta = 0), which adds exact zeros to every
+// product and leaves the cumulative decay unchanged, so the real rows'
+// values are those of a Cl-row computation.
 constexpr int C = kChunk;
 constexpr int kChainCols = 32;  // state columns per boundary-chain work item
 
@@ -75,6 +82,7 @@ struct PrefillArgs {
   int32_t H;
   int32_t Hk;  // heads of q and k
   int32_t G;   // value heads per key head, H / Hk
+  int32_t Cl;  // chunk length
 };
 
 struct DecodeArgs {
@@ -100,6 +108,7 @@ struct DecodeArgs {
   int32_t H;
   int32_t Hk;  // heads of q and k
   int32_t G;   // value heads per key head, H / Hk
+  int32_t Cl;  // chunk length (rows per cache tail)
 };
 
 template <int DK, int DV>
@@ -140,7 +149,7 @@ __device__ __forceinline__ size_t kq_row(size_t tok, int h, int Hk, int G) { ret
 // varlen plan: exclusive prefix sums of full and of all chunks per sequence
 
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start, const int32_t* __restrict__ end,
-                                               int32_t N, int32_t* __restrict__ full_base,
+                                               int32_t N, int32_t Cl, int32_t* __restrict__ full_base,
                                                int32_t* __restrict__ all_base) {
   __shared__ int32_t sf[1024];
   __shared__ int32_t sa[1024];
@@ -156,8 +165,8 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start
     int nf = 0, na = 0;
     if (i < N) {
       const int L = end[i] - start[i];
-      nf = L / C;
-      na = (L + C - 1) / C;
+      nf = L / Cl;
+      na = (L + Cl - 1) / Cl;
     }
     sf[tid] = nf;
     sa[tid] = na;
@@ -200,19 +209,20 @@ __device__ __forceinline__ void stage_chunk(ChunkLds<DK, DV>& sm, const typename
                                             const typename D::T* __restrict__ v, size_t v_row0,
                                             size_t v_stride, const typename D::T* __restrict__ g,
                                             const typename D::T* __restrict__ beta, size_t gb0,
-                                            size_t gb_stride) {
+                                            size_t gb_stride, int n) {
+  // rows t >= n (a chunk shorter than the slot) are identity padding
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int idx = tid; idx < C * DK; idx += nt) {
     const int t = idx / DK, i = idx % DK;
-    sm.K[t][i] = D::load(k, (k_row0 + (size_t)t * k_stride) * DK + i);
+    sm.K[t][i] = t < n ? D::load(k, (k_row0 + (size_t)t * k_stride) * DK + i) : 0.f;
   }
   for (int idx = tid; idx < C * DV; idx += nt) {
     const int t = idx / DV, j = idx % DV;
-    sm.V[t][j] = D::load(v, (v_row0 + (size_t)t * v_stride) * DV + j);
+    sm.V[t][j] = t < n ? D::load(v, (v_row0 + (size_t)t * v_stride) * DV + j) : 0.f;
   }
   for (int t = tid; t < C; t += nt) {
-    sm.g[t] = D::load(g, gb0 + (size_t)t * gb_stride);
-    sm.beta[t] = D::load(beta, gb0 + (size_t)t * gb_stride);
+    sm.g[t] = t < n ? D::load(g, gb0 + (size_t)t * gb_stride) : 0.f;
+    sm.beta[t] = t < n ? D::load(beta, gb0 + (size_t)t * gb_stride) : 0.f;
   }
   __syncthreads();
 }
@@ -226,10 +236,10 @@ __global__ __launch_bounds__(256) void k_chunk_local_prefill(const PrefillArgs a
   if (f >= a.full_base[N]) return;
   const int i = find_seq(a.full_base, N, f);
   const int c = f - a.full_base[i];
-  const size_t tok0 = (size_t)a.start[i] + (size_t)c * C;
+  const size_t tok0 = (size_t)a.start[i] + (size_t)c * a.Cl;
   const size_t row0 = tok0 * H + h;  // row index into [T, H, ...]
   stage_chunk<D, DK, DV>(sm, (const T*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const T*)a.v, row0, H,
-                         (const T*)a.g, (const T*)a.beta, row0, H);
+                         (const T*)a.g, (const T*)a.beta, row0, H, a.Cl);
   const size_t slot = (size_t)f * H + h;
   float* P = (float*)(a.prod + slot * prod_slot_bytes(false, DK, DV));
   chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + slot);
@@ -242,9 +252,10 @@ __global__ __launch_bounds__(256) void k_chunk_local_resync(const DecodeArgs a) 
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
   const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  // tail rows of this (sequence, head): [C, DK], [C, DV], [C]
-  stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, ch * C, 1, (const T*)a.tail_v, ch * C, 1,
-                         (const T*)a.tail_g, (const T*)a.tail_beta, ch * C, 1);
+  // tail rows of this (sequence, head): [Cl, DK], [Cl, DV], [Cl]
+  const size_t tr = ch * a.Cl;
+  stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, tr, 1, (const T*)a.tail_v, tr, 1, (const T*)a.tail_g,
+                         (const T*)a.tail_beta, tr, 1, a.Cl);
   float* P = (float*)(a.prod + sh * prod_slot_bytes(false, DK, DV));
   chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + sh);
 }
@@ -258,10 +269,10 @@ __global__ __launch_bounds__(256, 3) void k_chunk_local_prefill_bf16(const Prefi
   if (f >= a.full_base[N]) return;
   const int i = find_seq(a.full_base, N, f);
   const int c = f - a.full_base[i];
-  const size_t tok0 = (size_t)a.start[i] + (size_t)c * C;
+  const size_t tok0 = (size_t)a.start[i] + (size_t)c * a.Cl;
   const size_t row0 = tok0 * H + h;
   stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const uint16_t*)a.v, row0,
-                           H, (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H);
+                           H, (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H, a.Cl);
   const size_t slot = (size_t)f * H + h;
   chunk_local_bf16<DK, DV>(sm, a.prod + slot * prod_slot_bytes(true, DK, DV), a.gamn + slot);
 }
@@ -272,8 +283,9 @@ __global__ __launch_bounds__(256, 3) void k_chunk_local_resync_bf16(const Decode
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
   const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, ch * C, 1, (const uint16_t*)a.tail_v, ch * C, 1,
-                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, ch * C, 1);
+  const size_t tr = ch * a.Cl;
+  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, tr, 1, (const uint16_t*)a.tail_v, tr, 1,
+                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, tr, 1, a.Cl);
   chunk_local_bf16<DK, DV>(sm, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn + sh);
 }
 
@@ -331,7 +343,8 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
   const int H = a.H;
   const int L = a.end[i] - a.start[i];
   if (a.skip_empty && L == 0) return;
-  const int nfull = L / C, nall = (L + C - 1) / C;
+  const int Cl = a.Cl;
+  const int nfull = L / Cl, nall = (L + Cl - 1) / Cl;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
   const size_t ch = cache_row(a.slot, i) * H + h;
@@ -346,10 +359,10 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
     if (c + 1 < nall) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
   }
   put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
-  if (L % C == 0) put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
+  if (L % Cl == 0) put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
   if (blockIdx.z == 0 && threadIdx.x == 0) {
-    a.tail_len[ch] = L % C;
-    if (L % C == 0 && a.lgs) a.lgs[ch] = 0.f;
+    a.tail_len[ch] = L % Cl;
+    if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
   }
 }
 
@@ -398,8 +411,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   const int H = a.H;
   const int L = a.end[i] - a.start[i];
   if (a.skip_empty && L == 0) return;
-  int nfull = L / C;
-  const int nall = (L + C - 1) / C;
+  const int Cl = a.Cl;
+  int nfull = L / Cl;
+  const int nall = (L + Cl - 1) / Cl;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
   const int abase = a.all_base[i];
@@ -497,10 +511,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   }
   store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
   if (a.all_chunks) return;
-  if (L % C == 0) store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
+  if (L % Cl == 0) store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
   if (blockIdx.z == 0 && tid == 0) {
-    a.tail_len[ch] = L % C;
-    if (L % C == 0 && a.lgs) a.lgs[ch] = 0.f;
+    a.tail_len[ch] = L % Cl;
+    if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
   }
 }
 
@@ -536,8 +550,9 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   const int i = find_seq(a.all_base, N, slot);
   const int c = slot - a.all_base[i];
   const int L = a.end[i] - a.start[i];
-  const int n = min(C, L - c * C);
-  const size_t tok0 = (size_t)a.start[i] + (size_t)c * C;
+  const int Cl = a.Cl;
+  const int n = min(Cl, L - c * Cl);
+  const size_t tok0 = (size_t)a.start[i] + (size_t)c * Cl;
   const int lane = threadIdx.x;
   const int col = blockIdx.z * kWave + lane;
   const size_t SS = (size_t)DK * DV;
@@ -583,8 +598,8 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   const T* vp = (const T*)a.v;
   scan_tokens<D, DK, DV>(s, kp, qp, vp, (T*)a.o, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col, lane,
                          c_l, b_l, renorm);
-  const int nall = (L + C - 1) / C;
-  if (c == nall - 1 && (L % C) != 0) {
+  const int nall = (L + Cl - 1) / Cl;
+  if (c == nall - 1 && (L % Cl) != 0) {
     // last, partial chunk: its end state is the running state (N with
     // log-scale lg, or the state itself when materialised), its tokens the tail
     const size_t ch = cache_row(a.slot, i) * H + h;
@@ -598,17 +613,17 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
       for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
       if (blockIdx.z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
     }
-    T* tv = (T*)a.tail_v + ch * C * DV;
+    T* tv = (T*)a.tail_v + ch * Cl * DV;
     for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
     if (blockIdx.z == 0) {
-      T* tk = (T*)a.tail_k + ch * C * DK;
+      T* tk = (T*)a.tail_k + ch * Cl * DK;
       for (int idx = lane; idx < n * DK; idx += kWave) {
         const int t = idx / DK, e = idx % DK;
         tk[idx] = kp[kq_row(tok0 + t, h, a.Hk, a.G) * DK + e];
       }
       if (lane < n) {
-        ((T*)a.tail_g)[ch * C + lane] = gp[(tok0 + lane) * H + h];
-        ((T*)a.tail_beta)[ch * C + lane] = bp[(tok0 + lane) * H + h];
+        ((T*)a.tail_g)[ch * Cl + lane] = gp[(tok0 + lane) * H + h];
+        ((T*)a.tail_beta)[ch * Cl + lane] = bp[(tok0 + lane) * H + h];
       }
     }
   }
@@ -627,7 +642,8 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   const int tl = a.tail_len[ch];
   const float lg = a.lgs[ch];
   __syncthreads();  // every wave has read tail_len and lgs before they are rewritten below
-  if ((unsigned)tl >= (unsigned)C) {  // not a valid cache: touch nothing
+  const int Cl = a.Cl;
+  if ((unsigned)tl >= (unsigned)Cl) {  // not a valid cache: touch nothing
     if (col == 0) a.flag[sh] = 0;
     return;
   }
@@ -651,14 +667,14 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
   D::store((T*)a.o, sh * DV + col, out);
   // append the token to the tail
-  T* tk = (T*)a.tail_k + (ch * C + tl) * DK;
+  T* tk = (T*)a.tail_k + (ch * Cl + tl) * DK;
   for (int e = col; e < DK; e += DV) tk[e] = kp[kr * DK + e];
-  ((T*)a.tail_v)[(ch * C + tl) * DV + col] = ((const T*)a.v)[sh * DV + col];
+  ((T*)a.tail_v)[(ch * Cl + tl) * DV + col] = ((const T*)a.v)[sh * DV + col];
   if (col == 0) {
-    ((T*)a.tail_g)[ch * C + tl] = ((const T*)a.g)[sh];
-    ((T*)a.tail_beta)[ch * C + tl] = ((const T*)a.beta)[sh];
+    ((T*)a.tail_g)[ch * Cl + tl] = ((const T*)a.g)[sh];
+    ((T*)a.tail_beta)[ch * Cl + tl] = ((const T*)a.beta)[sh];
   }
-  const bool full = (tl + 1 == C);
+  const bool full = (tl + 1 == Cl);
   if (!full) {
 #pragma unroll
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
@@ -718,6 +734,7 @@ struct ContArgs {
   int32_t H;
   int32_t Hk;  // heads of q and k
   int32_t G;   // value heads per key head, H / Hk
+  int32_t Cl;  // chunk length
 };
 
 template <class D, int DK, int DV>
@@ -732,7 +749,8 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   float lg = a.lgs[ch];
   __syncthreads();  // every wave has read tail_len and lgs before they are rewritten below
   const int L = a.cu[i + 1] - a.cu[i];
-  const int nh = ((unsigned)tl < (unsigned)C && tl > 0) ? min(C - tl, L) : 0;
+  const int Cl = a.Cl;
+  const int nh = ((unsigned)tl < (unsigned)Cl && tl > 0) ? min(Cl - tl, L) : 0;
   if (h == 0 && col == 0) a.body_start[i] = a.cu[i] + nh;
   if (col == 0) a.flag[sh] = 0;
   if (nh == 0) return;
@@ -761,7 +779,7 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
     const size_t kr = kq_row((size_t)(a.cu[i] + t), h, a.Hk, a.G);
     const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
     D::store((T*)a.o, row * DV + col, out);
-    const size_t tr = ch * C + tl + t;  // tail row
+    const size_t tr = ch * Cl + tl + t;  // tail row
     T* tk = (T*)a.tail_k + tr * DK;
     for (int e = col; e < DK; e += DV) tk[e] = kp[kr * DK + e];
     ((T*)a.tail_v)[tr * DV + col] = vp[row * DV + col];
@@ -770,7 +788,7 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
       ((T*)a.tail_beta)[tr] = bp[row];
     }
   }
-  const bool full = (tl + nh == C);
+  const bool full = (tl + nh == Cl);
   if (!full) {
 #pragma unroll
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
@@ -1192,6 +1210,7 @@ struct BwdArgs {
   int32_t H;
   int32_t Hk;  // heads of q and k
   int32_t G;   // value heads per key head, H / Hk
+  int32_t Cl;  // chunk length
 };
 
 template <int DK, int DV>
@@ -1217,15 +1236,15 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
   const int i = find_seq(a.all_base, a.N, slot);
   const int c = slot - a.all_base[i];
   const int L = a.cu[i + 1] - a.cu[i];
-  const int n = min(C, L - c * C);
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const int n = min(a.Cl, L - c * a.Cl);
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * a.Cl) * H + h;
   const int tid = threadIdx.x, wave = tid >> 6;
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* dop = (const T*)a.d_o;
   chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
   const ChunkScalars& cs = sm.cs;
-  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * C, h, a.Hk, a.G);
+  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
   auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
   auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
   auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
@@ -1303,7 +1322,7 @@ __global__ __launch_bounds__(DV * 4) void k_bwd_chain_f32(const BwdArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, H = a.H;
   const int tid = threadIdx.x, jb = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int L = a.cu[i + 1] - a.cu[i];
-  const int nall = (L + C - 1) / C;
+  const int nall = (L + a.Cl - 1) / a.Cl;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
   const int abase = a.all_base[i];
@@ -1372,8 +1391,8 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   const int i = find_seq(a.all_base, a.N, slot);
   const int c = slot - a.all_base[i];
   const int L = a.cu[i + 1] - a.cu[i];
-  const int n = min(C, L - c * C);
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * C) * H + h;
+  const int n = min(a.Cl, L - c * a.Cl);
+  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * a.Cl) * H + h;
   const int tid = threadIdx.x, wave = tid >> 6;
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
@@ -1381,7 +1400,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   const T* dop = (const T*)a.d_o;
   chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
   const ChunkScalars& cs = sm.cs;
-  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * C, h, a.Hk, a.G);
+  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
   auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
   auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
   auto Vx = [&](int t, int j) { return t < n ? D::load(vp, (row0 + (size_t)t * H) * DV + j) : 0.f; };
@@ -1670,8 +1689,8 @@ __device__ __forceinline__ bool slot_pos(const BwdArgs& a, SlotPos& p) {
   const int i = find_seq(a.all_base, a.N, slot);
   const int c = slot - a.all_base[i];
   const int L = a.cu[i + 1] - a.cu[i];
-  p.n = min(C, L - c * C);
-  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
+  p.n = min(a.Cl, L - c * a.Cl);
+  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * a.Cl;
   p.row0 = tok0 * H + h;
   p.kq0 = kq_row(tok0, h, a.Hk, a.G);
   p.sl = (size_t)slot * H + h;
@@ -1738,7 +1757,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_chain_bf16(const BwdArgs a) 
   const int jbg = blockIdx.z * (CB / 16), jb0 = jbg + wave * NT;
   const int H = a.H;
   const int L = a.cu[i + 1] - a.cu[i];
-  const int nall = (L + C - 1) / C;
+  const int nall = (L + a.Cl - 1) / a.Cl;
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
   const int abase = a.all_base[i];
@@ -1865,8 +1884,8 @@ bool shape_ok(const gdn_cpr_shape* s, std::string* why) {
     *why = "head dims must be 64 or 128";
     return false;
   }
-  if (s->chunk != C) {
-    *why = "chunk must be 64";
+  if (s->chunk != 16 && s->chunk != 32 && s->chunk != C) {
+    *why = "chunk must be 16, 32 or 64";
     return false;
   }
   if (s->dtype != GDN_DTYPE_F32 && s->dtype != GDN_DTYPE_BF16) {
@@ -1890,7 +1909,7 @@ struct PrefillLayout {
 
 PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   const size_t H = s.num_heads, DK = s.head_dim_k, DV = s.head_dim_v;
-  const size_t Fmax = (size_t)(T / C);
+  const size_t Fmax = (size_t)(T / s.chunk);
   const size_t Amax = Fmax + (size_t)N;
   PrefillLayout L;
   size_t off = 0;
@@ -1968,10 +1987,10 @@ void launch_chain_bf16(const PrefillArgs& a, hipStream_t st) {
 
 template <class D, int DK, int DV>
 gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const char* fn) {
-  const int Fmax = (int)(T / C);
+  const int Fmax = (int)(T / a.Cl);
   const int Amax = Fmax + a.N;
   mark(0, st);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.full_base, a.all_base);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.Cl, a.full_base, a.all_base);
   mark(1, st);
   constexpr bool kBf16 = std::is_same<D, Bf16>::value;
   if (Fmax > 0) {
@@ -2112,7 +2131,8 @@ struct CmpPrefillFn {
         hipLaunchKernelGGL((k_cmp_rec_prefill<D, DK, DV>), dim3(ca.N, ca.H, DV / kWave), dim3(kWave), 0, st, ca);
         return launch_status(fn);
       }
-      hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.full_base, pa.all_base);
+      hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.Cl, pa.full_base,
+                         pa.all_base);
       if (T > 0) hipLaunchKernelGGL((k_cmp_chunk_local_bf16<DK, DV>), dim3(Amax, ca.H), dim3(256), 0, st, ca);
       launch_chain_bf16<DK, DV>(pa, st);
       if (T > 0) hipLaunchKernelGGL((k_cmp_chunk_out_bf16<DK, DV>), dim3(Amax, ca.H), dim3(256), 0, st, ca);
@@ -2166,7 +2186,7 @@ struct FwdBwdLayout {
 FwdBwdLayout fwd_bwd_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   const size_t H = s.num_heads, DK = s.head_dim_k, DV = s.head_dim_v;
   const size_t esz = s.dtype == GDN_DTYPE_BF16 ? 2 : 4;
-  const size_t Amax = (size_t)(T / C) + (size_t)N;
+  const size_t Amax = (size_t)(T / s.chunk) + (size_t)N;
   FwdBwdLayout L;
   L.pre = prefill_layout(s, N, T);
   size_t off = L.pre.total;
@@ -2223,7 +2243,7 @@ struct FwdBwdFn {
     if (slot_bytes != want) return fail(GDN_ERR_HIP, "%s: internal slot size mismatch", fn);
     gdn_status r = run_prefill<D, DK, DV>(pa, T, st, fn);
     if (r != GDN_OK) return r;
-    const int Amax = (int)(T / C) + pa.N;
+    const int Amax = (int)(T / pa.Cl) + pa.N;
     if constexpr (kBf16) {
       if (T > 0) hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
       const long pairs = (long)pa.N * pa.H;
@@ -2341,6 +2361,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.H = shape->num_heads;
   a.Hk = key_heads(*shape);
   a.G = a.H / a.Hk;
+  a.Cl = shape->chunk;
   return dispatch<PrefillFn>(*shape, a, total_tokens, (hipStream_t)stream, fn);
 }
 
@@ -2401,6 +2422,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   a.H = shape->num_heads;
   a.Hk = key_heads(*shape);
   a.G = a.H / a.Hk;
+  a.Cl = shape->chunk;
   return dispatch<DecodeFn>(*shape, a, (hipStream_t)stream, fn);
 }
 
@@ -2466,6 +2488,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   ca.H = shape->num_heads;
   ca.Hk = key_heads(*shape);
   ca.G = ca.H / ca.Hk;
+  ca.Cl = shape->chunk;
   DecodeArgs da;
   memset(&da, 0, sizeof(da));
   da.s_bnd = cache->s_bnd;
@@ -2483,6 +2506,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   da.H = shape->num_heads;
   da.Hk = key_heads(*shape);
   da.G = da.H / da.Hk;
+  da.Cl = shape->chunk;
   da.slot = cache->slot_index;
   PrefillArgs pa;
   pa.q = q;
@@ -2516,6 +2540,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   pa.H = shape->num_heads;
   pa.Hk = key_heads(*shape);
   pa.G = pa.H / pa.Hk;
+  pa.Cl = shape->chunk;
   return dispatch<ContFn>(*shape, ca, da, pa, total_tokens, (hipStream_t)stream, fn);
 }
 
@@ -2591,6 +2616,7 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.H = shape->num_heads;
   pa.Hk = key_heads(*shape);
   pa.G = pa.H / pa.Hk;
+  pa.Cl = shape->chunk;
   BwdArgs ba;
   ba.q = q;
   ba.k = k;
@@ -2616,13 +2642,14 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   ba.H = shape->num_heads;
   ba.Hk = key_heads(*shape);
   ba.G = ba.H / ba.Hk;
+  ba.Cl = shape->chunk;
   return dispatch<FwdBwdFn>(*shape, pa, ba, total_tokens, L.slot, (hipStream_t)stream, fn);
 }
 
 extern "C" size_t gdn_cmp_workspace_size(const gdn_cpr_shape* shape, int32_t mode, int32_t num_seqs,
                                          int64_t total_tokens) {
   std::string why;
-  if (!shape_ok(shape, &why) || num_seqs < 0 || total_tokens < 0) return 0;
+  if (!shape_ok(shape, &why) || num_seqs < 0 || total_tokens < 0 || shape->chunk != C) return 0;
   if (mode == GDN_CMP_RECURRENT) return 256;
   if (mode == GDN_CMP_CHUNKWISE) return cmp_layout(*shape, num_seqs, total_tokens).total;
   return 0;
@@ -2635,6 +2662,7 @@ extern "C" gdn_status gdn_cmp_prefill(const gdn_cpr_shape* shape, int32_t mode, 
   const char* fn = "gdn_cmp_prefill";
   std::string why;
   if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (shape->chunk != C) return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take chunk = 64 only", fn);
   if (shape->dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take bf16 inputs", fn);
   if (mode != GDN_CMP_RECURRENT && mode != GDN_CMP_CHUNKWISE) return fail(GDN_ERR_INVALID_ARG, "%s: mode", fn);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
@@ -2697,6 +2725,7 @@ extern "C" gdn_status gdn_cmp_prefill(const gdn_cpr_shape* shape, int32_t mode, 
     pa.H = shape->num_heads;
     pa.Hk = key_heads(*shape);
     pa.G = pa.H / pa.Hk;
+    pa.Cl = shape->chunk;
   }
   return dispatch<CmpPrefillFn>(*shape, (int)mode, ca, pa, total_tokens, (hipStream_t)stream, fn);
 }
@@ -2707,6 +2736,7 @@ extern "C" gdn_status gdn_cmp_decode_step(const gdn_cpr_shape* shape, int32_t nu
   const char* fn = "gdn_cmp_decode_step";
   std::string why;
   if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (shape->chunk != C) return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take chunk = 64 only", fn);
   if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (num_seqs == 0) {
     g_last_error.clear();
@@ -2742,6 +2772,7 @@ extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int3
   const char* fn = "gdn_cmp_chunk_decode_step";
   std::string why;
   if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (shape->chunk != C) return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take chunk = 64 only", fn);
   if (shape->dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: the comparators take bf16 inputs", fn);
   if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
@@ -2793,6 +2824,7 @@ extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int3
   a.H = shape->num_heads;
   a.Hk = key_heads(*shape);
   a.G = a.H / a.Hk;
+  a.Cl = shape->chunk;
   return dispatch<CmpChunkDecodeFn>(*shape, a, (hipStream_t)stream, fn);
 }
 

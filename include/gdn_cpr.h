@@ -47,7 +47,13 @@
  *     rounded to nearest even.  States, dg, dbeta are always fp32.
  *   - g must be <= 0 (alpha in (0, 1]); beta is used as given.  Values are
  *     not checked on the device.
- *   - Supported shapes: d_k, d_v in {64, 128}; C = 64; H >= 1; H_k divides H.
+ *   - Supported shapes: d_k, d_v in {64, 128}; C in {16, 32, 64}; H >= 1;
+ *     H_k divides H.  The pages' layers use C = 64 (the chunk size of the
+ *     chunked kernels they name); other hybrid Gated DeltaNet layers may
+ *     resynchronise more often, so 16 and 32 are accepted: a chunk of C < 64
+ *     tokens is evaluated as a 64-row chunk whose rows past C are identity
+ *     steps (k = v = 0, g = beta = 0), which changes no real row's value.
+ *     The comparators (gdn_cmp_*) take C = 64 only.
  *   - Every pointer must be 16-byte aligned.
  *   - Errors detectable on the host (null or misaligned pointer, unsupported
  *     shape, workspace too small, negative sizes) return a status before any
@@ -88,7 +94,7 @@ typedef struct {
   int32_t num_heads;     /* H: value heads (v, g, beta, o, states, caches) */
   int32_t head_dim_k;    /* d_k */
   int32_t head_dim_v;    /* d_v */
-  int32_t chunk;         /* C, the boundary / resynchronisation period */
+  int32_t chunk;         /* C, the boundary / resynchronisation period: 16, 32 or 64 */
   int32_t dtype;         /* gdn_dtype of q, k, v, g, beta, o and the tail buffers */
   int32_t num_key_heads; /* H_k: heads of q and k; 0 means H.  H_k divides H and
                             value head h reads key head h / (H / H_k) */

@@ -29,10 +29,10 @@ def shape_of(b: Batch, C: int = 64) -> gdn.LayerShape:
 
 
 class DevBatch:
-    def __init__(self, b: Batch):
+    def __init__(self, b: Batch, C: int = 64):
         dt = torch_dtype(b)
         self.b = b
-        self.shape = shape_of(b)
+        self.shape = shape_of(b, C)
 
         def t(a):
             return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dt).contiguous()

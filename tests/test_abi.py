@@ -44,6 +44,11 @@ def test_workspace_size_shapes():
     assert n_pre > 5 * 16 * 32 * 128 * 128 * 4  # at least one fp32 boundary state per chunk
     assert n_dec > 256 * 16 * 4
     assert n_pre % 256 == 0 and n_dec % 256 == 0
+    # shorter chunks: more chunk slots and boundary states for the same tokens
+    n32 = lib.gdn_cpr_workspace_size(ctypes.byref(_shape(16, 128, 128, C=32)), 5, 10240, _lib.GDN_OP_PREFILL)
+    n16 = lib.gdn_cpr_workspace_size(ctypes.byref(_shape(16, 128, 128, C=16)), 5, 10240, _lib.GDN_OP_PREFILL)
+    assert n16 > n32 > n_pre
+    assert lib.gdn_cmp_workspace_size(ctypes.byref(_shape(16, 128, 128, C=32)), _lib.GDN_CMP_CHUNKWISE, 5, 10240) == 0
     bad = _shape(16, 96, 128)
     assert lib.gdn_cpr_workspace_size(ctypes.byref(bad), 5, 10240, _lib.GDN_OP_PREFILL) == 0
     assert lib.gdn_cpr_workspace_size(ctypes.byref(s), -1, 10240, _lib.GDN_OP_PREFILL) == 0
@@ -64,7 +69,7 @@ def _prefill(lib, shape, N=2, T=128, cache=None, cu=FAKE, q=FAKE, ws=FAKE, ws_by
 
 def test_prefill_rejects_unsupported_shapes():
     lib = _lib_or_skip()
-    for s in (_shape(dk=96), _shape(dv=32), _shape(C=32), _shape(H=0), _shape(dtype=7)):
+    for s in (_shape(dk=96), _shape(dv=32), _shape(C=48), _shape(C=128), _shape(H=0), _shape(dtype=7)):
         assert _prefill(lib, s) == _lib.GDN_ERR_UNSUPPORTED
         assert lib.gdn_cpr_last_error()
 
@@ -146,7 +151,7 @@ def test_prefill_continue_rejects_bad_arguments():
         return lib.gdn_cpr_prefill_continue(ctypes.byref(shape), N, T, q, FAKE, FAKE, FAKE, FAKE, cu,
                                             ctypes.byref(c), FAKE, ws, ws_bytes, None)
 
-    assert cont(shape=_shape(C=16)) == _lib.GDN_ERR_UNSUPPORTED
+    assert cont(shape=_shape(C=8)) == _lib.GDN_ERR_UNSUPPORTED
     assert cont(cu=None) == _lib.GDN_ERR_INVALID_ARG
     assert cont(q=FAKE + 2) == _lib.GDN_ERR_INVALID_ARG
     assert cont(c=_cache(0)) == _lib.GDN_ERR_INVALID_ARG

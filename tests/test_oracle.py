@@ -197,6 +197,46 @@ def test_chunk_boundaries_equal_recurrent_states():
         assert np.max(np.abs(bounds[0][c] - np.swapaxes(states[0][t], -1, -2))) < 1e-12
 
 
+def test_identity_padding_rows_leave_chunk_products_unchanged():
+    """A token with k = v = 0, g = beta = 0 is the identity step (alpha = 1, no
+    write), so padding a chunk of n < 64 tokens with such rows leaves the real
+    rows of W, U, K~ and Gamma_n, and the chunk's boundary map, unchanged.
+    This is the reading behind chunk lengths shorter than the 64-row slot."""
+    rng = np.random.default_rng(31)
+    for n in (16, 32, 47):
+        K = rng.standard_normal((n, 6))
+        K /= np.linalg.norm(K, axis=1, keepdims=True)
+        V = rng.standard_normal((n, 4))
+        g = -np.abs(rng.standard_normal(n)) * 0.2
+        beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(n)))
+        pad = 64 - n
+        Kp = np.vstack([K, np.zeros((pad, 6))])
+        Vp = np.vstack([V, np.zeros((pad, 4))])
+        gp = np.concatenate([g, np.zeros(pad)])
+        bp = np.concatenate([beta, np.zeros(pad)])
+        W, U, Kt, Gn, T, _, _ = oracle.chunk_products(K, V, g, beta)
+        Wp, Up, Ktp, Gnp, Tp, _, _ = oracle.chunk_products(Kp, Vp, gp, bp)
+        assert np.max(np.abs(Wp[:n] - W)) < 1e-13 and np.max(np.abs(Wp[n:])) == 0.0
+        assert np.max(np.abs(Up[:n] - U)) < 1e-13 and np.max(np.abs(Up[n:])) == 0.0
+        assert np.max(np.abs(Ktp[:n] - Kt)) < 1e-13 and np.max(np.abs(Ktp[n:])) == 0.0
+        assert abs(Gnp - Gn) < 1e-15
+        # the boundary map B' = Gamma_n B + (U - W B^T)^T K~ is the same
+        B = rng.standard_normal((4, 6))
+        Bn = Gn * B + (U - W @ B.T).T @ Kt
+        Bnp = Gnp * B + (Up - Wp @ B.T).T @ Ktp
+        assert np.max(np.abs(Bnp - Bn)) < 1e-13
+    # the recurrence: identity tokens after a sequence leave its final state as it is
+    b = _rand_problem(32, [40], H=1, dk=5, dv=3)
+    _, h = _run_rec(b)
+    z = np.zeros((24,) + b.q.shape[1:])
+    o2, h2 = orec.recurrent_forward(np.concatenate([b.q, z]), np.concatenate([b.k, z]),
+                                    np.concatenate([b.v, np.zeros((24,) + b.v.shape[1:])]),
+                                    np.concatenate([b.g, np.zeros((24,) + b.g.shape[1:])]),
+                                    np.concatenate([b.beta, np.zeros((24,) + b.beta.shape[1:])]),
+                                    np.array([0, 64], np.int32), b.h0)
+    assert np.array_equal(h2, h)
+
+
 def test_chunk_products_T_is_inverse():
     rng = np.random.default_rng(4)
     n, dk, dv = 10, 6, 4

@@ -90,6 +90,12 @@ def test_slot_indexed_cache_matches_plain_cache(dtype):
 
     for i, r in enumerate(slots):
         row_equal(pool, r, ref, i)
+    # the state written out through the row map equals the plain cache's
+    st_pool = gdn.gdn_cpr_cache_state(db.shape, pool)
+    st_ref = gdn.gdn_cpr_cache_state(db.shape, ref)
+    torch.cuda.synchronize()
+    assert st_pool.shape == st_ref.shape
+    assert np.array_equal(bits(st_pool), bits(st_ref))
     for r in set(range(8)) - set(slots):  # untouched rows
         assert int(pool.tail_len[r, 0]) == 7
         assert float(pool.s_run[r].min()) == 3.0 and float(pool.s_run[r].max()) == 3.0

@@ -519,15 +519,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
 }
 
 // decode resync, bf16 path: one wave per (sequence, head, 32 state columns),
-// operands straight from the decode workspace's product slot
+// the waves of a (sequence, head) in one work-group (so a step in which no
+// tail fills launches one small work-group per pair), operands straight from
+// the decode workspace's product slot
 constexpr int kResyncNT = 2;
+template <int DV>
+constexpr int kResyncWaves = DV / (16 * kResyncNT) < 4 ? DV / (16 * kResyncNT) : 4;
 
 template <int DK, int DV>
-__global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
+__global__ __launch_bounds__(kResyncWaves<DV> * 64) void k_chain_resync_bf16(const DecodeArgs a) {
   constexpr int NT = kResyncNT;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
-  const int jb0 = blockIdx.z * NT, lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int jb0 = (blockIdx.z * kResyncWaves<DV> + (threadIdx.x >> 6)) * NT;
   const size_t SS = (size_t)DK * DV;
   mfma::f32x4 S[DK / 16][NT];
   const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
@@ -535,7 +540,7 @@ __global__ __launch_bounds__(64) void k_chain_resync_bf16(const DecodeArgs a) {
   chain_step_bf16_global<DK, DV, NT>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb0, lane);
   store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
   store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
-  if (blockIdx.z == 0 && lane == 0 && a.lgs) a.lgs[ch] = 0.f;
+  if (blockIdx.z == 0 && threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -2020,7 +2025,8 @@ gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
   mark(1, st);
   if constexpr (std::is_same<D, Bf16>::value) {
     hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / (16 * kResyncNT)), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / (16 * kResyncNT) / kResyncWaves<DV>),
+                       dim3(64 * kResyncWaves<DV>), 0, st, a);
   } else {
     hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
     hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
@@ -2082,7 +2088,8 @@ struct ContFn {
     hipLaunchKernelGGL((k_cont_head<D, DK, DV>), dim3(ca.N, ca.H), dim3(DV), 0, st, ca);
     if constexpr (std::is_same<D, Bf16>::value) {
       hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
-      hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(da.N, da.H, DV / (16 * kResyncNT)), dim3(64), 0, st,
+      hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(da.N, da.H, DV / (16 * kResyncNT) / kResyncWaves<DV>),
+                         dim3(64 * kResyncWaves<DV>), 0, st,
                          da);
     } else {
       hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
@@ -2157,7 +2164,8 @@ struct CmpChunkDecodeFn {
     } else {
       hipLaunchKernelGGL((k_cmp_cdec_local_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
       hipLaunchKernelGGL((k_cmp_cdec_out_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
-      hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / (16 * kResyncNT)), dim3(64), 0, st, a);
+      hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / (16 * kResyncNT) / kResyncWaves<DV>),
+                       dim3(64 * kResyncWaves<DV>), 0, st, a);
       return launch_status(fn);
     }
   }

@@ -65,6 +65,13 @@ def measured_traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def stats(xs):
+    """mean, median, p90 and min of per-step HIP-event times (ms)"""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "min": round(float(a.min()), 5)}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -196,7 +203,7 @@ def main():
     # timed region 2: per-stage events (same work, one step at a time)
     dstep[0] = start_step  # decode tokens advance regardless; keep rows in range
     dstep[0] = args.warmup + args.steps
-    for _ in range(min(args.steps, 8)):
+    for _ in range(min(args.steps, 32)):
         if dstep[0] >= n_dec_tok:
             break
         step(True)
@@ -427,6 +434,9 @@ def main():
         "data": "synthetic (seeded GDN-shaped inputs; see gdn_synth)",
         "config": {"workload": "prefill 5x2048 tokens + decode 256 seqs x 1 token (2048-token prefix)",
                    "heads": H, "d_k": D, "d_v": D, "chunk": C, "state": "fp32"},
+        "timing_stats_ms": {"prefill": stats(prefill_ms), "scan": stats(scan_ms),
+                            "decode_token_step": stats(dstep_ms), "decode_call": stats(decode_ms),
+                            "samples": len(prefill_ms)},
         "prefill": {"ms": round(float(np.mean(prefill_ms)), 5),
                     "tokens_per_s": round(T / (float(np.mean(prefill_ms)) / 1e3), 1),
                     "stage_ms": {"chunk_products": round(float(np.mean(local_ms)), 5),

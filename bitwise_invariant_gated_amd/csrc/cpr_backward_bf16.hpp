@@ -315,8 +315,8 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
 }
 
 // ===========================================================================
-// state stage (256 threads): Dd, Delta, QB, dWn, dKt, dGamma_n
-template <int DK, int DV>
+// state stage (64 W threads): Dd, Delta, QB, dWn, dKt, dGamma_n
+template <int DK, int DV, int W>
 struct StateLds {
   static constexpr int kLK = DK + 8, kLV = DV + 8, kLX = C + 4, kLD = DV + 4, kLB = 32 + 4;
   uint16_t K[C][kLK];
@@ -327,7 +327,7 @@ struct StateLds {
   float De[C][kLD];
   float Bs[DK][kLB];  // 32 columns of B or dB', row-major
   bwd::ChunkScalars cs;
-  float red[256];
+  float red[64 * W];
 };
 
 // stage columns 32 jb .. 32 jb + 31 of a TL state (DK rows) into Bs
@@ -343,22 +343,24 @@ __device__ __forceinline__ void stage_cols(float (*Bs)[LB], const float* __restr
   }
 }
 
-template <int DK, int DV>
-__device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t* k, const uint16_t* v,
+template <int DK, int DV, int W>
+__device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint16_t* k, const uint16_t* v,
                                             const uint16_t* d_o, const uint16_t* gp, const uint16_t* bp,
                                             size_t row0, int H, size_t kq0, int Hk, int n,
                                             const float* __restrict__ B, uint8_t* __restrict__ slot) {
   typedef Slot<DK, DV> Sl;
-  typedef StateLds<DK, DV> Lds;
+  typedef StateLds<DK, DV, W> Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  constexpr int NI = DK / 64, NJ = DV / 64;
+  // wave w makes the 16-wide row / column tiles w, w + W, ...
+  static_assert((DK / 16) % W == 0 && (DV / 16) % W == 0, "tiles per wave");
+  constexpr int NI = DK / (16 * W), NJ = DV / (16 * W);
   const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
   const float* Ddlg = reinterpret_cast<const float*>(slot + Sl::oDdl);
   const float* dBp = reinterpret_cast<const float*>(slot + Sl::oDbp);
   stage_rows<DK>(sm.K, k, kq0, Hk, n);
   stage_rows<DV>(sm.V, v, row0, H, n);
   stage_rows<DV>(sm.dO, d_o, row0, H, n);
-  for (int idx = tid; idx < C * C / 4; idx += 256) {
+  for (int idx = tid; idx < C * C / 4; idx += 64 * W) {
     const int t = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
     *reinterpret_cast<f32x4*>(&sm.X[t][s4]) = *reinterpret_cast<const f32x4*>(Xg + (size_t)t * C + s4);
   }
@@ -367,14 +369,14 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
   float* Ddg = reinterpret_cast<float*>(slot + Sl::oDd);
   float* Deg = reinterpret_cast<float*>(slot + Sl::oDe);
   constexpr int NB = C / 16;
-  // Column tile jt = wave + 4 p: the dB' and B tiles of the column block are
+  // Column tile jt = wave + W p: the dB' and B tiles of the column block are
   // loaded once; the four row tiles accumulate together.
   //   Dd    = Ddl + Kt dB'
   //   KB    = K B                                   (kept in registers)
   //   Delta = X diag(beta) (V - diag(Gamma) KB)     (= X diag(beta) V - W B)
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
-    const int jt = wave + 4 * p;
+    const int jt = wave + W * p;
     f32x4 bD[DK / 16], bB[DK / 16];
 #pragma unroll
     for (int ib = 0; ib < DK / 16; ++ib) {
@@ -437,7 +439,7 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < NI; ++p) {
-      const int it = wave + 4 * p;
+      const int it = wave + W * p;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const f32x4 b = row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g);
@@ -456,8 +458,8 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
   for (int p = 0; p < NI; ++p)
 #pragma unroll
     for (int tm = 0; tm < C / 16; ++tm) {
-      st_rm(QBg, DK, 16 * tm, 16 * (wave + 4 * p), QB[p][tm], lane);
-      st_rm(DWg, DK, 16 * tm, 16 * (wave + 4 * p), DW[p][tm], lane);
+      st_rm(QBg, DK, 16 * tm, 16 * (wave + W * p), QB[p][tm], lane);
+      st_rm(DWg, DK, 16 * tm, 16 * (wave + W * p), DW[p][tm], lane);
       QB[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};  // reused for dKt
     }
   for (int jb = 0; jb < DV / 32; ++jb) {
@@ -465,7 +467,7 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < NI; ++p) {
-      const int it = wave + 4 * p;
+      const int it = wave + W * p;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const f32x4 b = row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g);
@@ -480,13 +482,13 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
 #pragma unroll
   for (int p = 0; p < NI; ++p)
 #pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) st_rm(KTg, DK, 16 * tm, 16 * (wave + 4 * p), QB[p][tm], lane);
+    for (int tm = 0; tm < C / 16; ++tm) st_rm(KTg, DK, 16 * tm, 16 * (wave + W * p), QB[p][tm], lane);
   // dGamma_n = <dB', B> (both in TL order), fixed order
   {
     float acc = 0.f;
     const f32x4* b4 = reinterpret_cast<const f32x4*>(B);
     const f32x4* d4 = reinterpret_cast<const f32x4*>(dBp);
-    for (int idx = tid; idx < DK * DV / 4; idx += 256) {
+    for (int idx = tid; idx < DK * DV / 4; idx += 64 * W) {
       const f32x4 x = b4[idx], y = d4[idx];
       acc = __builtin_fmaf(x[0], y[0], acc);
       acc = __builtin_fmaf(x[1], y[1], acc);
@@ -497,14 +499,14 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV>& sm, const uint16_t
     __syncthreads();
     if (tid == 0) {
       float s = 0.f;
-      for (int r = 0; r < 256; ++r) s += sm.red[r];
+      for (int r = 0; r < 64 * W; ++r) s += sm.red[r];
       *reinterpret_cast<float*>(slot + Sl::oDGn) = s;
     }
   }
 }
 
 // ===========================================================================
-// local gradients (256 threads): dq, dk, dv, dg, dbeta of the chunk's tokens
+// local gradients (64 W threads): dq, dk, dv, dg, dbeta of the chunk's tokens
 template <int DK, int DV>
 struct GradLds {
   static constexpr int kLK = DK + 8, kLV = DV + 8, kLX = C + 4;
@@ -521,7 +523,7 @@ struct GradLds {
   float rzP[C], czP[C], dbc[C], dbr[C], rzA[C], czA[C], dgo[C], de[C];
 };
 
-template <int DK, int DV>
+template <int DK, int DV, int W>
 // dq and dk go to rows kq0 + t Hk of [T, Hk, DK] in bf16 or, when the key
 // heads are shared (dq_part non-null), to the value head's rows row0 + t H of
 // fp32 [T, H, DK] partials that a later pass sums over the group.
@@ -535,7 +537,10 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   typedef Slot<DK, DV> Sl;
   typedef GradLds<DK, DV> Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  constexpr int NI = DK / 64, NJ = DV / 64;
+  // d-wide products: wave w makes the 16-wide tiles w, w + W, ...; C x C
+  // products: wave w < C / 16 makes row or column block w
+  static_assert((DK / 16) % W == 0 && (DV / 16) % W == 0 && W >= C / 16, "tiles per wave");
+  constexpr int NI = DK / (16 * W), NJ = DV / (16 * W);
   const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
   const float* Ddg = reinterpret_cast<const float*>(slot + Sl::oDd);
   const float* Deg = reinterpret_cast<const float*>(slot + Sl::oDe);
@@ -546,7 +551,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   stage_rows<DK>(sm.Q, q, kq0, Hk, n);
   stage_rows<DV>(sm.V, v, row0, H, n);
   stage_rows<DV>(sm.dO, d_o, row0, H, n);
-  for (int idx = tid; idx < C * C / 4; idx += 256) {
+  for (int idx = tid; idx < C * C / 4; idx += 64 * W) {
     const int t = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
     *reinterpret_cast<f32x4*>(&sm.X[t][s4]) = *reinterpret_cast<const f32x4*>(Xg + (size_t)t * C + s4);
   }
@@ -556,7 +561,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   constexpr int NB = C / 16;
   // dPD = (dO Delta^T) .* D (lower, diagonal included), Z_P = dPD .* QK^T;
   // wave w makes the tiles of column block w (rows tm >= w)
-  {
+  if (wave < NB) {
     const int tn = wave;
     f32x4 bde[DV / 16];
 #pragma unroll
@@ -600,7 +605,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   // dQ = diag(Gamma) QB + dPD K;  <QB, Q> per row
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
-    const int it = wave + 4 * p, i = 16 * it + lr;
+    const int it = wave + W * p, i = 16 * it + lr;
     float qb[NB][4];
 #pragma unroll
     for (int tm = 0; tm < NB; ++tm)
@@ -635,7 +640,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   // dV = diag(beta) X^T Dd
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
-    const int jt = wave + 4 * p;
+    const int jt = wave + W * p;
     f32x4 bd[NB], acc[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
@@ -659,7 +664,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   f32x4 TW[NI][NB];
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
-    const int it = wave + 4 * p;
+    const int it = wave + W * p;
     f32x4 bw[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
@@ -678,7 +683,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   }
   __syncthreads();  // Z_P sums done: M2 is free
   // dT = Dd V^T - dWn (diag(Gamma) K)^T; wave w makes row block w
-  {
+  if (wave < NB) {
     const int tm = wave;
     f32x4 ad[DV / 16], aw[DK / 16];
 #pragma unroll
@@ -716,10 +721,10 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
     sm.dbc[tid] = acc;
   }
   __syncthreads();
-  for (int idx = tid; idx < C * C; idx += 256) sm.M2[idx / C][idx % C] *= cs.beta[idx % C];  // dX
+  for (int idx = tid; idx < C * C; idx += 64 * W) sm.M2[idx / C][idx % C] *= cs.beta[idx % C];  // dX
   __syncthreads();
   // Y = dX X^T -> M3; wave w makes row block w
-  {
+  if (wave < NB) {
     const int tm = wave;
     f32x4 acc[NB];
 #pragma unroll
@@ -740,7 +745,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   // dA = -X^T Y (strict lower); dA .* D -> M2, Z_A = dA .* D .* G -> M3 after a
   // barrier; wave w makes the tiles of column block w
   f32x4 ZA[NB];
-  {
+  if (wave < NB) {
     const int tn = wave;
     f32x4 acc[NB], gk[NB];
 #pragma unroll
@@ -774,10 +779,12 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
       }
   }
   __syncthreads();  // Y no longer read
+  if (wave < NB) {
 #pragma unroll
-  for (int tm = 0; tm < NB; ++tm)
+    for (int tm = 0; tm < NB; ++tm)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * wave + lr] = ZA[tm][r];
+      for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * wave + lr] = ZA[tm][r];
+  }
   __syncthreads();
   if (tid < C) {
     float acc = 0.f;
@@ -793,7 +800,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   // dK = dPD^T Q + (dG + dG^T) K + diag(e) dKt + diag(Gamma) TW, dG = beta_t (dA .* D)
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
-    const int it = wave + 4 * p, i = 16 * it + lr;
+    const int it = wave + W * p, i = 16 * it + lr;
     float kt[NB][4];
 #pragma unroll
     for (int sb = 0; sb < NB; ++sb)

@@ -1713,24 +1713,31 @@ __global__ __launch_bounds__(256) void k_bwd_local_bf16(const BwdArgs a) {
                             a.ws + p.sl * Sl::bytes, a.gamn + p.sl);
 }
 
+// waves per work-group of the state and gradient stages: their d-wide
+// products split into 16-wide tiles over the waves, so two waves per SIMD
+// where d_k and d_v give 8 tiles each (the LDS holds one work-group per CU)
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_bwd_state_bf16(const BwdArgs a) {
+constexpr int kBwdWaves = (DK / 16) % 8 == 0 && (DV / 16) % 8 == 0 ? 8 : 4;
+
+template <int DK, int DV>
+__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_state_bf16(const BwdArgs a) {
   typedef bwdb::Slot<DK, DV> Sl;
-  __shared__ bwdb::StateLds<DK, DV> sm;
+  constexpr int W = kBwdWaves<DK, DV>;
+  __shared__ bwdb::StateLds<DK, DV, W> sm;
   SlotPos p;
   if (!slot_pos(a, p)) return;
-  bwdb::state_stage<DK, DV>(sm, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
+  bwdb::state_stage<DK, DV, W>(sm, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
                             (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
                             a.bnd + p.sl * DK * DV, a.ws + p.sl * Sl::bytes);
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_bwd_grads_bf16(const BwdArgs a) {
+__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_grads_bf16(const BwdArgs a) {
   typedef bwdb::Slot<DK, DV> Sl;
   __shared__ bwdb::GradLds<DK, DV> sm;
   SlotPos p;
   if (!slot_pos(a, p)) return;
-  bwdb::grad_stage<DK, DV>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  bwdb::grad_stage<DK, DV, kBwdWaves<DK, DV>>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.d_o, (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0,
                            a.Hk, p.n, a.ws + p.sl * Sl::bytes, (uint16_t*)a.dq, (uint16_t*)a.dk, a.dq_part,
                            a.dk_part, (uint16_t*)a.dv, a.dg, a.dbeta);
@@ -2261,8 +2268,8 @@ struct FwdBwdFn {
         hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 2, 1>), dim3(pa.N, pa.H, DV / 32), dim3(128), 0, st, ba);
       mark(5, st);
       if (T > 0) {
-        hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
-        hipLaunchKernelGGL((k_bwd_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+        hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
+        hipLaunchKernelGGL((k_bwd_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
         launch_key_head_sums(ba, T, st);
       }
       mark(6, st);

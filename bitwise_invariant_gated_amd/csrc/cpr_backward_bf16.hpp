@@ -149,7 +149,7 @@ __device__ __forceinline__ void lower_tile(int q, int& tm, int& tn) {
 }
 
 // ===========================================================================
-// local stage (256 threads): L, X, P, W, Kt and -W^T fragments, Ddl, R
+// local stage (64 W threads): L, X, P, W, Kt and -W^T fragments, Ddl, R
 template <int DK, int DV>
 struct LocalLds {
   static constexpr int kLK = DK + 8, kLV = DV + 8, kLA = C + 4;
@@ -162,7 +162,7 @@ struct LocalLds {
   bwd::ChunkScalars cs;
 };
 
-template <int DK, int DV>
+template <int DK, int DV, int W>
 __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t* q, const uint16_t* k,
                                             const uint16_t* d_o, const uint16_t* gp, const uint16_t* bp,
                                             size_t row0, int H, size_t kq0, int Hk, int n,
@@ -170,13 +170,15 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
   typedef Slot<DK, DV> Sl;
   typedef LocalLds<DK, DV> Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  // d-wide products: wave w makes the 16-wide tiles w, w + W, ...
+  static_assert((DK / 16) % W == 0 && (DV / 16) % W == 0 && W >= 4, "tiles per wave");
   stage_rows<DK>(sm.K, k, kq0, Hk, n);
   stage_rows<DK>(sm.Q, q, kq0, Hk, n);
   stage_rows<DV>(sm.dO, d_o, row0, H, n);
   bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
   const bwd::ChunkScalars& cs = sm.cs;
   // L (strictly lower) and P (lower, diagonal included) from the 10 lower tiles each
-  for (int q2 = wave; q2 < 20; q2 += 4) {
+  for (int q2 = wave; q2 < 20; q2 += W) {
     int tm, tn;
     lower_tile(q2 % 10, tm, tn);
     const bool isP = q2 >= 10;
@@ -195,7 +197,7 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
       }
     }
   }
-  for (int idx = tid; idx < C * C; idx += 256) {
+  for (int idx = tid; idx < C * C; idx += 64 * W) {
     const int t = idx / C, s = idx % C;
     if ((s >> 4) > (t >> 4)) sm.P[t][s] = 0.f;
   }
@@ -204,7 +206,7 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
     inverse_diag_blocks(sm.A, lane);
   } else {
     // Kt fragments (chain phase 1, the slot's first 16 KB): fragment (kb, tm)
-    for (int f = wave - 1; f < (DK / 32) * (C / 16); f += 3) {
+    for (int f = wave - 1; f < (DK / 32) * (C / 16); f += W - 1) {
       const int kb = f / (C / 16), tm = f % (C / 16), t = 16 * tm + lr;
       const u32x4 raw = frag_row(&sm.K[t][0], 32 * kb, g);
       const float et = cs.e[t];
@@ -217,14 +219,14 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
   }
   __syncthreads();
   inverse_below_diag(sm.A, wave, lane);
-  // W tiles (tm, it), it = wave + 4 p; X[t][s] = A[s][t] for s <= t.  The
+  // W tiles (tm, it), it = wave + W p; X[t][s] = A[s][t] for s <= t.  The
   // K column block is shared by the four row tiles, whose accumulations
   // interleave.
-  constexpr int NI = DK / 64, NJ = DV / 64, NB = C / 16;
+  constexpr int NI = DK / (16 * W), NJ = DV / (16 * W), NB = C / 16;
   f32x4 Wt[NI][NB];
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
-    const int it = wave + 4 * p;
+    const int it = wave + W * p;
 #pragma unroll
     for (int tm = 0; tm < NB; ++tm) Wt[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -254,11 +256,11 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
       *reinterpret_cast<u32x4*>(slot + Sl::oWNF + ((size_t)(kb * (DK / 16) + it) * 64 + lane) * 16) = out;
     }
   }
-  // Ddl = P^T dO, tiles (sb, jt), jt = wave + 4 p; P[t][s] = 0 for t < s
+  // Ddl = P^T dO, tiles (sb, jt), jt = wave + W p; P[t][s] = 0 for t < s
   float* Ddlg = reinterpret_cast<float*>(slot + Sl::oDdl);
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
-    const int jt = wave + 4 * p;
+    const int jt = wave + W * p;
     f32x4 acc[NB];
 #pragma unroll
     for (int sb = 0; sb < NB; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -285,7 +287,7 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
   float* Rg = reinterpret_cast<float*>(slot + Sl::oR);
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
-    const int it = wave + 4 * p;
+    const int it = wave + W * p;
     f32x4 acc[DV / 16];
 #pragma unroll
     for (int jt = 0; jt < DV / 16; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -307,7 +309,7 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
   }
   // X (row-major, zero above the diagonal) and Gamma_n
   float* Xg = reinterpret_cast<float*>(slot + Sl::oX);
-  for (int idx = tid; idx < C * C; idx += 256) {
+  for (int idx = tid; idx < C * C; idx += 64 * W) {
     const int t = idx / C, s = idx % C;
     Xg[idx] = (s <= t) ? sm.A[s][t] : 0.f;
   }

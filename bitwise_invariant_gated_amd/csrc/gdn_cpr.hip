@@ -1702,22 +1702,22 @@ __device__ __forceinline__ bool slot_pos(const BwdArgs& a, SlotPos& p) {
   return true;
 }
 
+// waves per work-group of the local, state and gradient stages: their
+// d-wide products split into 16-wide tiles over the waves, so two waves per
+// SIMD where d_k and d_v give 8 tiles each (the LDS holds one work-group per CU)
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_bwd_local_bf16(const BwdArgs a) {
+constexpr int kBwdWaves = (DK / 16) % 8 == 0 && (DV / 16) % 8 == 0 ? 8 : 4;
+
+template <int DK, int DV>
+__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_local_bf16(const BwdArgs a) {
   typedef bwdb::Slot<DK, DV> Sl;
   __shared__ bwdb::LocalLds<DK, DV> sm;
   SlotPos p;
   if (!slot_pos(a, p)) return;
-  bwdb::local_stage<DK, DV>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.d_o,
+  bwdb::local_stage<DK, DV, kBwdWaves<DK, DV>>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.d_o,
                             (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
                             a.ws + p.sl * Sl::bytes, a.gamn + p.sl);
 }
-
-// waves per work-group of the state and gradient stages: their d-wide
-// products split into 16-wide tiles over the waves, so two waves per SIMD
-// where d_k and d_v give 8 tiles each (the LDS holds one work-group per CU)
-template <int DK, int DV>
-constexpr int kBwdWaves = (DK / 16) % 8 == 0 && (DV / 16) % 8 == 0 ? 8 : 4;
 
 template <int DK, int DV>
 __global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_state_bf16(const BwdArgs a) {
@@ -2260,7 +2260,8 @@ struct FwdBwdFn {
     if (r != GDN_OK) return r;
     const int Amax = (int)(T / pa.Cl) + pa.N;
     if constexpr (kBf16) {
-      if (T > 0) hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+      if (T > 0)
+        hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
       const long pairs = (long)pa.N * pa.H;
       if (pairs * (DV / 64) >= 96)
         hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 4, 1>), dim3(pa.N, pa.H, DV / 64), dim3(256), 0, st, ba);

@@ -499,10 +499,12 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
     }
     sm.red[tid] = acc;
     __syncthreads();
-    if (tid == 0) {
+    if (tid < 64) {  // lane l sums red[W l .. W l + W - 1], then the lanes in order
+      float part = 0.f;
+      for (int r = 0; r < W; ++r) part += sm.red[W * tid + r];
       float s = 0.f;
-      for (int r = 0; r < 64 * W; ++r) s += sm.red[r];
-      *reinterpret_cast<float*>(slot + Sl::oDGn) = s;
+      for (int l = 0; l < 64; ++l) s += lane_bcast(part, l);
+      if (tid == 0) *reinterpret_cast<float*>(slot + Sl::oDGn) = s;
     }
   }
 }
@@ -522,7 +524,8 @@ struct GradLds {
   float M3[C][kLX];  // Y, then Z_A
   bwd::ChunkScalars cs;
   float pGO[C][DK / 16], pGW[C][DK / 16], pDE[C][DK / 16];  // per-row partial dot products
-  float rzP[C], czP[C], dbc[C], dbr[C], rzA[C], czA[C], dgo[C], de[C];
+  float rzP[C], czP[C], dbc[C], dbr[C], rzA[C], czA[C], dgo[C], de[C], dgam[C];
+  float sum_de;
 };
 
 template <int DK, int DV, int W>
@@ -562,36 +565,43 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
 
   constexpr int NB = C / 16;
   // dPD = (dO Delta^T) .* D (lower, diagonal included), Z_P = dPD .* QK^T;
-  // wave w makes the tiles of column block w (rows tm >= w)
-  if (wave < NB) {
-    const int tn = wave;
+  // wave w makes the tiles (w / NB + (W / NB) j, w % NB) (zero above the diagonal)
+  {
+    constexpr int NT2 = NB * NB / W;
+    const int tn = wave % NB;
     f32x4 bde[DV / 16];
 #pragma unroll
     for (int jb = 0; jb < DV / 16; ++jb) bde[jb] = row4_f(Deg, DV, 16 * tn + lr, 16 * jb, g);
-    f32x4 acc[NB], qk[NB];
+    f32x4 acc[NT2], qk[NT2];
 #pragma unroll
-    for (int tm = 0; tm < NB; ++tm) acc[tm] = qk[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT2; ++j) acc[j] = qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < DV / 16; ++jb)
 #pragma unroll
-      for (int tm = 0; tm < NB; ++tm)
-        if (tm >= tn) acc[tm] = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 16 * jb, g), bde[jb], acc[tm]);
+      for (int j = 0; j < NT2; ++j) {
+        const int tm = wave / NB + (W / NB) * j;
+        if (tm >= tn) acc[j] = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 16 * jb, g), bde[jb], acc[j]);
+      }
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb) {
       const u32x4 kf = frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g);
 #pragma unroll
-      for (int tm = 0; tm < NB; ++tm)
-        if (tm >= tn) qk[tm] = mma(frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g), kf, qk[tm]);
+      for (int j = 0; j < NT2; ++j) {
+        const int tm = wave / NB + (W / NB) * j;
+        if (tm >= tn) qk[j] = mma(frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g), kf, qk[j]);
+      }
     }
 #pragma unroll
-    for (int tm = 0; tm < NB; ++tm)
+    for (int j = 0; j < NT2; ++j) {
+      const int tm = wave / NB + (W / NB) * j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tm + 4 * g + r, s2 = 16 * tn + lr;
-        const float dpd = (tm >= tn && s2 <= t) ? acc[tm][r] * expf(cs.gam[t] - cs.gam[s2]) : 0.f;
+        const float dpd = (tm >= tn && s2 <= t) ? acc[j][r] * expf(cs.gam[t] - cs.gam[s2]) : 0.f;
         sm.dPD[t][s2] = dpd;
-        sm.M2[t][s2] = dpd * qk[tm][r];
+        sm.M2[t][s2] = dpd * qk[j][r];
       }
+    }
   }
   __syncthreads();
   if (tid < C) {
@@ -684,9 +694,11 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
       for (int r = 0; r < 4; ++r) TW[p][sb][r] = -cs.beta[16 * sb + 4 * g + r] * TW[p][sb][r];
   }
   __syncthreads();  // Z_P sums done: M2 is free
-  // dT = Dd V^T - dWn (diag(Gamma) K)^T; wave w makes row block w
-  if (wave < NB) {
-    const int tm = wave;
+  // dT = Dd V^T - dWn (diag(Gamma) K)^T; wave w makes row block w % NB,
+  // column blocks (w / NB) NT2 .. + NT2 - 1
+  {
+    constexpr int NT2 = NB * NB / W;
+    const int tm = wave % NB, tn0 = (wave / NB) * NT2;
     f32x4 ad[DV / 16], aw[DK / 16];
 #pragma unroll
     for (int jb = 0; jb < DV / 16; ++jb) ad[jb] = row4_f(Ddg, DV, 16 * tm + lr, 16 * jb, g);
@@ -695,26 +707,27 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
       const f32x4 w = row4_f(DWg, DK, 16 * tm + lr, 16 * ib, g);
       aw[ib] = f32x4{-w[0], -w[1], -w[2], -w[3]};
     }
-    f32x4 acc[NB];
+    f32x4 acc[NT2];
 #pragma unroll
-    for (int tn = 0; tn < NB; ++tn) acc[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NT2; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < DV / 16; ++jb)
 #pragma unroll
-      for (int tn = 0; tn < NB; ++tn)
-        acc[tn] = mma16(ad[jb], row4_bf(&sm.V[0][0], Lds::kLV, 16 * tn + lr, 16 * jb, g), acc[tn]);
+      for (int u = 0; u < NT2; ++u)
+        acc[u] = mma16(ad[jb], row4_bf(&sm.V[0][0], Lds::kLV, 16 * (tn0 + u) + lr, 16 * jb, g), acc[u]);
 #pragma unroll
     for (int ib = 0; ib < DK / 16; ++ib)
 #pragma unroll
-      for (int tn = 0; tn < NB; ++tn) {
+      for (int u = 0; u < NT2; ++u) {
+        const int tn = tn0 + u;
         const float gs = cs.Gam[16 * tn + lr];
         const f32x4 kk = row4_bf(&sm.K[0][0], Lds::kLK, 16 * tn + lr, 16 * ib, g);
-        acc[tn] = mma16(aw[ib], f32x4{gs * kk[0], gs * kk[1], gs * kk[2], gs * kk[3]}, acc[tn]);
+        acc[u] = mma16(aw[ib], f32x4{gs * kk[0], gs * kk[1], gs * kk[2], gs * kk[3]}, acc[u]);
       }
 #pragma unroll
-    for (int tn = 0; tn < NB; ++tn)
+    for (int u = 0; u < NT2; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.M2[16 * tm + 4 * g + r][16 * tn + lr] = acc[tn][r];
+      for (int r = 0; r < 4; ++r) sm.M2[16 * tm + 4 * g + r][16 * (tn0 + u) + lr] = acc[u][r];
   }
   __syncthreads();
   if (tid < C) {  // dbeta, column part: sum_t X[t][s] dT[t][s]
@@ -860,19 +873,26 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
     sm.de[tid] = c;
   }
   __syncthreads();
-  if (tid == 0) {
-    const float dGn = *reinterpret_cast<const float*>(slot + Sl::oDGn);
+  // each token's dgamma term and dbeta in parallel; one thread then forms the
+  // reverse cumulative sum (t = C - 1 down to 0) and the de e sum in order
+  if (tid < C) {
+    const int t = tid;
+    sm.dgam[t] = (sm.rzP[t] + sm.rzA[t]) - (sm.czP[t] + sm.czA[t]) + sm.dgo[t] * cs.Gam[t] - sm.de[t] * cs.e[t];
+    if (t < n) dbeta[row0 + (size_t)t * H] = sm.dbc[t] + sm.dbr[t];
+  } else if (tid == C) {
     float sum_de = 0.f;
     for (int t = 0; t < C; ++t) sum_de = __builtin_fmaf(sm.de[t], cs.e[t], sum_de);
+    sm.sum_de = sum_de;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float dGn = *reinterpret_cast<const float*>(slot + Sl::oDGn);
     float acc = 0.f;
     for (int t = C - 1; t >= 0; --t) {
-      float dgam = (sm.rzP[t] + sm.rzA[t]) - (sm.czP[t] + sm.czA[t]) + sm.dgo[t] * cs.Gam[t] - sm.de[t] * cs.e[t];
-      if (t == C - 1) dgam += dGn * cs.Gam[C - 1] + sum_de;
+      float dgam = sm.dgam[t];
+      if (t == C - 1) dgam += dGn * cs.Gam[C - 1] + sm.sum_de;
       acc += dgam;
-      if (t < n) {
-        dg[row0 + (size_t)t * H] = acc;
-        dbeta[row0 + (size_t)t * H] = sm.dbc[t] + sm.dbr[t];
-      }
+      if (t < n) dg[row0 + (size_t)t * H] = acc;
     }
   }
 }

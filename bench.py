@@ -294,6 +294,10 @@ def main():
     for _ in range(2):
         fwd_bwd()
     torch.cuda.synchronize()
+    # the bf16 call runs the backward local terms and reverse chain on a second
+    # stream beside the forward (see gdn_cpr_fwd_bwd): events 0 -> 4 span the
+    # forward, 0 -> 5 end when the reverse chain has joined, 5 -> 6 is the
+    # state and gradient stages
     fb_ms, fb_fwd, fb_bchain, fb_grads = [], [], [], []
     for _ in range(5):
         with fb_ev:
@@ -301,7 +305,7 @@ def main():
         torch.cuda.synchronize()
         fb_ms.append(fb_ev.events[0].elapsed_time(fb_ev.events[6]))
         fb_fwd.append(fb_ev.events[0].elapsed_time(fb_ev.events[4]))
-        fb_bchain.append(fb_ev.stage_ms(5))
+        fb_bchain.append(fb_ev.events[0].elapsed_time(fb_ev.events[5]))
         fb_grads.append(fb_ev.stage_ms(6))
     del ws_tr
 
@@ -456,9 +460,10 @@ def main():
                    "mean_over_64_steps_tokens_per_s": round(N_dec / (dec64_ms / 1e3), 1)},
         "fwd_bwd": {"workload": "1 x 10240 tokens", "ms": round(float(np.median(fb_ms)), 4),
                     "tokens_per_s": round(T4 / (float(np.median(fb_ms)) / 1e3), 1),
+                    "streams": 2,
                     "stage_ms": {"forward": round(float(np.median(fb_fwd)), 4),
-                                 "bwd_local_and_reverse_chain": round(float(np.median(fb_bchain)), 4),
-                                 "bwd_grads": round(float(np.median(fb_grads)), 4)}},
+                                 "to_reverse_chain_joined": round(float(np.median(fb_bchain)), 4),
+                                 "state_and_gradients": round(float(np.median(fb_grads)), 4)}},
         "continuation": {"workload": "256 cached sequences x 4 tokens in one gdn_cpr_prefill_continue call",
                          "ms": round(cont_ms, 5), "tokens_per_s": round(256 * n_tok / (cont_ms / 1e3), 1),
                          "four_decode_steps_ms": round(dec4_ms, 5),

@@ -1980,6 +1980,43 @@ gdn_status launch_status(const char* fn) {
   return GDN_OK;
 }
 
+// A second stream for the overlapped stages of gdn_cpr_fwd_bwd, one per
+// calling thread and device (created on first use at the default priority
+// and kept for the thread's lifetime), with the events that fork work onto
+// it and join it back.  Per thread, so that concurrent callers never wait on
+// each other's events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+// the side stream on the device of st, or nullptr if it cannot be made
+SideStream* side_stream(hipStream_t st) {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream tab[kMaxDevices];
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& x = tab[dev];
+  if (x.s) return &x;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  SideStream y;
+  bool ok = hipStreamCreateWithFlags(&y.s, hipStreamNonBlocking) == hipSuccess;
+  hipEvent_t* ev[2] = {&y.fork, &y.join};
+  for (int i = 0; i < 2 && ok; ++i) ok = hipEventCreateWithFlags(ev[i], hipEventDisableTiming) == hipSuccess;
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (!ok) {
+    for (int i = 0; i < 2; ++i)
+      if (*ev[i]) (void)hipEventDestroy(*ev[i]);
+    if (y.s) (void)hipStreamDestroy(y.s);
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  x = y;
+  return &x;
+}
+
 // bf16 boundary chain: the fewer (sequence, head) pairs, the more work-groups
 // per pair (the column split is bit-neutral)
 template <int DK, int DV>
@@ -2251,22 +2288,66 @@ struct FwdBwdFn {
     hipLaunchKernelGGL((k_key_head_sum<D, DK>), dim3(rows), dim3(DK), 0, st, ba.dk_part, (typename D::T*)ba.dk, ba.Hk,
                        ba.G);
   }
+  static void launch_bwd_chain_bf16(const BwdArgs& ba, hipStream_t st) {
+    const long pairs = (long)ba.N * ba.H;
+    if (pairs * (DV / 64) >= 96)
+      hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 4, 1>), dim3(ba.N, ba.H, DV / 64), dim3(256), 0, st, ba);
+    else
+      hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 2, 1>), dim3(ba.N, ba.H, DV / 32), dim3(128), 0, st, ba);
+  }
+  // bf16 path on two streams.  The backward's local terms and reverse chain
+  // read only the inputs, d_o, d_hT and the plan, so they run on the side
+  // stream beside the forward chunk products, boundary chain and in-chunk
+  // scan; the state and gradient stages, which need both chains, follow on
+  // the caller's stream after the join.  (Running the scan beside the state
+  // and gradient stages instead measured the same.)  Every kernel computes
+  // what it computes in the one-stream order, so the bits are the same.
+  static gdn_status run_overlapped(const PrefillArgs& pa, const BwdArgs& ba, int64_t T, hipStream_t st,
+                                   const SideStream& x, const char* fn) {
+    const int Fmax = (int)(T / pa.Cl), Amax = Fmax + pa.N;
+    auto ev = [&](hipError_t e) { return e == hipSuccess; };
+    mark(0, st);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.Cl, pa.full_base, pa.all_base);
+    mark(1, st);
+    if (!ev(hipEventRecord(x.fork, st)) || !ev(hipStreamWaitEvent(x.s, x.fork, 0)))
+      return fail(GDN_ERR_HIP, "%s: stream fork failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, x.s, ba);
+    launch_bwd_chain_bf16(ba, x.s);
+    if (!ev(hipEventRecord(x.join, x.s))) return fail(GDN_ERR_HIP, "%s: event record failed", fn);
+    if (Fmax > 0)
+      hipLaunchKernelGGL((k_chunk_local_prefill_bf16<DK, DV>), dim3(Fmax, pa.H), dim3(256), 0, st, pa);
+    mark(2, st);
+    if (pa.N > 0) launch_chain_bf16<DK, DV>(pa, st);
+    mark(3, st);
+    hipLaunchKernelGGL((k_scan<D, DK, DV>), dim3(Amax, pa.H, DV / kWave), dim3(kWave), 0, st, pa);
+    mark(4, st);
+    if (!ev(hipStreamWaitEvent(st, x.join, 0)))
+      return fail(GDN_ERR_HIP, "%s: stream join failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    mark(5, st);
+    hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
+    hipLaunchKernelGGL((k_bwd_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
+    launch_key_head_sums(ba, T, st);
+    mark(6, st);
+    return launch_status(fn);
+  }
   static gdn_status run(const PrefillArgs& pa, const BwdArgs& ba, int64_t T, size_t slot_bytes, hipStream_t st,
                         const char* fn) {
     constexpr bool kBf16 = std::is_same<D, Bf16>::value;
     const size_t want = kBf16 ? bwdb::Slot<DK, DV>::bytes : bwd::BwdSlot<DK, DV, sizeof(typename D::T)>::bytes;
     if (slot_bytes != want) return fail(GDN_ERR_HIP, "%s: internal slot size mismatch", fn);
+    if constexpr (kBf16) {
+      if (T > 0) {
+        // one stream only if the side stream cannot be made
+        if (const SideStream* x = side_stream(st)) return run_overlapped(pa, ba, T, st, *x, fn);
+      }
+    }
     gdn_status r = run_prefill<D, DK, DV>(pa, T, st, fn);
     if (r != GDN_OK) return r;
     const int Amax = (int)(T / pa.Cl) + pa.N;
     if constexpr (kBf16) {
       if (T > 0)
         hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
-      const long pairs = (long)pa.N * pa.H;
-      if (pairs * (DV / 64) >= 96)
-        hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 4, 1>), dim3(pa.N, pa.H, DV / 64), dim3(256), 0, st, ba);
-      else
-        hipLaunchKernelGGL((k_bwd_chain_bf16<DK, DV, 2, 1>), dim3(pa.N, pa.H, DV / 32), dim3(128), 0, st, ba);
+      launch_bwd_chain_bf16(ba, st);
       mark(5, st);
       if (T > 0) {
         hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);

@@ -249,6 +249,19 @@ gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t num_seqs, con
  *   dq, dk, dv        dtype, shaped like q, k, v
  *   dg, dbeta         [T, H] fp32
  *   dh0               [N, H, d_k, d_v] fp32, or NULL
+ * For bf16 inputs the call runs independent stages side by side on two
+ * streams: `stream` and a second stream that the library creates, at the
+ * default priority, the first time the calling thread calls it for that
+ * stream's device, and keeps for the thread's lifetime.  The backward's local
+ * terms and reverse chain run on the second stream beside the forward chunk
+ * products, chain and in-chunk scan on `stream`; the state and gradient
+ * stages follow on `stream`.  Events fork the work from `stream` and join it
+ * back, so everything the call does is ordered on `stream` as with one
+ * stream (also under graph capture, where the fork and join become graph
+ * edges; make the thread's first call outside a capture, since it creates
+ * the stream).  The bits do not depend on this: each kernel computes the
+ * same values in either order.  If the second stream cannot be created the
+ * call runs on `stream` alone.
  */
 gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                            const void* q, const void* k, const void* v, const void* g,
@@ -326,6 +339,9 @@ gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int32_t num_seq
  *                              4 in-chunk scan
  *   decode:                    1 per-token step, 2 resynchronisation
  *   fwd_bwd backward:          5 reverse boundary chain, 6 per-chunk gradients
+ * For bf16 fwd_bwd, whose backward local terms and reverse chain run on a
+ * second stream beside stages 2-4, event 5 is recorded once the reverse chain
+ * has joined `stream`; events 0 -> 6 span the whole call.
  * n_events is the array length; stages beyond it are not recorded.  Nothing
  * is allocated and nothing else changes.
  */

@@ -151,15 +151,12 @@ __device__ __forceinline__ size_t kq_row(size_t tok, int h, int Hk, int G) { ret
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start, const int32_t* __restrict__ end,
                                                int32_t N, int32_t Cl, int32_t* __restrict__ full_base,
                                                int32_t* __restrict__ all_base) {
-  __shared__ int32_t sf[1024];
-  __shared__ int32_t sa[1024];
-  __shared__ int32_t carry[2];
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    carry[0] = 0;
-    carry[1] = 0;
-  }
-  __syncthreads();
+  // 1024 sequences per pass: an inclusive scan inside each wave (shuffles),
+  // the 16 wave totals through LDS, and the running totals of earlier passes
+  // (integers, so the order of the sums does not matter)
+  __shared__ int32_t wf[16], wa[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cf = 0, ca = 0;
   for (int base = 0; base < N; base += 1024) {
     const int i = base + tid;
     int nf = 0, na = 0;
@@ -168,35 +165,40 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start
       nf = L / Cl;
       na = (L + Cl - 1) / Cl;
     }
-    sf[tid] = nf;
-    sa[tid] = na;
-    __syncthreads();
-    // Hillis-Steele inclusive scan (integers: order does not matter)
-    for (int off = 1; off < 1024; off <<= 1) {
-      int xf = 0, xa = 0;
-      if (tid >= off) {
-        xf = sf[tid - off];
-        xa = sa[tid - off];
+    int sf = nf, sa = na;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int xf = __shfl_up(sf, off), xa = __shfl_up(sa, off);
+      if (lane >= off) {
+        sf += xf;
+        sa += xa;
       }
-      __syncthreads();
-      sf[tid] += xf;
-      sa[tid] += xa;
-      __syncthreads();
+    }
+    if (lane == 63) {
+      wf[wave] = sf;
+      wa[wave] = sa;
+    }
+    __syncthreads();
+    int pf = 0, pa = 0, tf = 0, ta = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) {
+        pf += wf[w];
+        pa += wa[w];
+      }
+      tf += wf[w];
+      ta += wa[w];
     }
     if (i < N) {
-      full_base[i] = carry[0] + sf[tid] - nf;
-      all_base[i] = carry[1] + sa[tid] - na;
+      full_base[i] = cf + pf + sf - nf;
+      all_base[i] = ca + pa + sa - na;
     }
-    __syncthreads();
-    if (tid == 1023) {
-      carry[0] += sf[1023];
-      carry[1] += sa[1023];
-    }
-    __syncthreads();
+    cf += tf;
+    ca += ta;
+    __syncthreads();  // wf, wa are rewritten by the next pass
   }
   if (tid == 0) {
-    full_base[N] = carry[0];
-    all_base[N] = carry[1];
+    full_base[N] = cf;
+    all_base[N] = ca;
   }
 }
 

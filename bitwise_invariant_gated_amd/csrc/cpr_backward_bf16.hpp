@@ -738,67 +738,80 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   __syncthreads();
   for (int idx = tid; idx < C * C; idx += 64 * W) sm.M2[idx / C][idx % C] *= cs.beta[idx % C];  // dX
   __syncthreads();
-  // Y = dX X^T -> M3; wave w makes row block w
-  if (wave < NB) {
-    const int tm = wave;
-    f32x4 acc[NB];
+  // Y = dX X^T -> M3; wave w makes row block w % NB, column blocks
+  // tn_y(w, u): all of them (W = NB), or {h, NB - 1 - h} with h = w / NB
+  // (W = 2 NB), which gives every wave the same number of products
+  {
+    constexpr int NT2 = NB * NB / W;
+    const int tm = wave % NB, h = wave / NB;
+    auto tn_y = [&](int u) { return NT2 == NB ? u : (u == 0 ? h : NB - 1 - h); };
+    f32x4 acc[NT2];
 #pragma unroll
-    for (int tn = 0; tn < NB; ++tn) acc[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NT2; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
       const f32x4 a = row4_f(&sm.M2[0][0], Lds::kLX, 16 * tm + lr, 16 * rb, g);
 #pragma unroll
-      for (int tn = rb; tn < NB; ++tn)
-        acc[tn] = mma16(a, row4_f(&sm.X[0][0], Lds::kLX, 16 * tn + lr, 16 * rb, g), acc[tn]);
+      for (int u = 0; u < NT2; ++u) {
+        const int tn = tn_y(u);
+        if (tn >= rb) acc[u] = mma16(a, row4_f(&sm.X[0][0], Lds::kLX, 16 * tn + lr, 16 * rb, g), acc[u]);
+      }
     }
 #pragma unroll
-    for (int tn = 0; tn < NB; ++tn)
+    for (int u = 0; u < NT2; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * tn + lr] = acc[tn][r];
+      for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * tn_y(u) + lr] = acc[u][r];
   }
   __syncthreads();
   // dA = -X^T Y (strict lower); dA .* D -> M2, Z_A = dA .* D .* G -> M3 after a
-  // barrier; wave w makes the tiles of column block w
-  f32x4 ZA[NB];
-  if (wave < NB) {
-    const int tn = wave;
-    f32x4 acc[NB], gk[NB];
+  // barrier; wave w makes the tiles (w / NB + (W / NB) j, w % NB)
+  constexpr int NTA = NB * NB / W;
+  f32x4 ZA[NTA];
+  {
+    const int tn = wave % NB;
+    f32x4 acc[NTA], gk[NTA];
 #pragma unroll
-    for (int tm = 0; tm < NB; ++tm) acc[tm] = gk[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTA; ++j) acc[j] = gk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
       const f32x4 b = col4_f(&sm.M3[0][0], Lds::kLX, 16 * rb, 16 * tn + lr, g);
 #pragma unroll
-      for (int tm = 0; tm <= rb; ++tm)
-        if (tm >= tn) acc[tm] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * rb, 16 * tm + lr, g), b, acc[tm]);
+      for (int j = 0; j < NTA; ++j) {
+        const int tm = wave / NB + (W / NB) * j;
+        if (tm <= rb && tm >= tn) acc[j] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * rb, 16 * tm + lr, g), b, acc[j]);
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb) {
       const u32x4 kf = frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g);
 #pragma unroll
-      for (int tm = 0; tm < NB; ++tm)
-        if (tm >= tn) gk[tm] = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), kf, gk[tm]);
+      for (int j = 0; j < NTA; ++j) {
+        const int tm = wave / NB + (W / NB) * j;
+        if (tm >= tn) gk[j] = mma(frag_row(&sm.K[16 * tm + lr][0], 32 * kb, g), kf, gk[j]);
+      }
     }
 #pragma unroll
-    for (int tm = 0; tm < NB; ++tm)
+    for (int j = 0; j < NTA; ++j) {
+      const int tm = wave / NB + (W / NB) * j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tm + 4 * g + r, s2 = 16 * tn + lr;
         float dad = 0.f, z = 0.f;
         if (tm >= tn && s2 < t) {
-          dad = -acc[tm][r] * expf(cs.gam[t] - cs.gam[s2]);
-          z = dad * gk[tm][r];
+          dad = -acc[j][r] * expf(cs.gam[t] - cs.gam[s2]);
+          z = dad * gk[j][r];
         }
         sm.M2[t][s2] = dad;
-        ZA[tm][r] = z;
+        ZA[j][r] = z;
       }
+    }
   }
   __syncthreads();  // Y no longer read
-  if (wave < NB) {
 #pragma unroll
-    for (int tm = 0; tm < NB; ++tm)
+  for (int j = 0; j < NTA; ++j) {
+    const int tm = wave / NB + (W / NB) * j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * wave + lr] = ZA[tm][r];
+    for (int r = 0; r < 4; ++r) sm.M3[16 * tm + 4 * g + r][16 * (wave % NB) + lr] = ZA[j][r];
   }
   __syncthreads();
   if (tid < C) {

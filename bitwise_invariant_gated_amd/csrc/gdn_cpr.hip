@@ -11,7 +11,7 @@
 // Decode step:
 //   k_decode          per-token step on the running state (one work item per
 //                     sequence x head), tail append, resync flag
-//   k_chunk_local_resync / k_chain_resync
+//   k_resync_bf16 (bf16; fp32: k_chunk_local_resync, k_chain_resync)
 //                     for the (sequence, head) pairs whose tail just filled:
 //                     the same chunk products and boundary advance as prefill
 //                     over the C tail tokens, from the boundary state
@@ -279,17 +279,6 @@ __global__ __launch_bounds__(256, 3) void k_chunk_local_prefill_bf16(const Prefi
   chunk_local_bf16<DK, DV>(sm, a.prod + slot * prod_slot_bytes(true, DK, DV), a.gamn + slot);
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 3) void k_chunk_local_resync_bf16(const DecodeArgs a) {
-  __shared__ ChunkLdsB<DK, DV> sm;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
-  if (a.flag[sh] == 0) return;
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  const size_t tr = ch * a.Cl;
-  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, tr, 1, (const uint16_t*)a.tail_v, tr, 1,
-                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, tr, 1, a.Cl);
-  chunk_local_bf16<DK, DV>(sm, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn + sh);
-}
 
 // ---------------------------------------------------------------------------
 // boundary chain
@@ -520,10 +509,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   }
 }
 
-// decode resync, bf16 path: one wave per (sequence, head, 32 state columns),
-// the waves of a (sequence, head) in one work-group (so a step in which no
-// tail fills launches one small work-group per pair), operands straight from
-// the decode workspace's product slot
+// chain step of a filled tail, bf16 path, from a product slot the decode
+// workspace already holds (the chunkwise-everywhere comparator's decode):
+// one wave per (sequence, head, 32 state columns), the waves of a (sequence,
+// head) in one work-group
 constexpr int kResyncNT = 2;
 template <int DV>
 constexpr int kResyncWaves = DV / (16 * kResyncNT) < 4 ? DV / (16 * kResyncNT) : 4;
@@ -543,6 +532,40 @@ __global__ __launch_bounds__(kResyncWaves<DV> * 64) void k_chain_resync_bf16(con
   store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
   store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
   if (blockIdx.z == 0 && threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
+}
+
+// decode resync, bf16 path, in one launch: one work-group per (sequence,
+// head).  A pair whose tail filled forms the tail's chunk products into the
+// decode workspace's product slot (as the prefill's chunk-product kernel
+// does for a chunk) and then, wave w for state columns 32 w .. 32 w + 31,
+// takes the chain step from s_bnd with them (k_chain_resync_bf16's
+// arithmetic); every other pair exits at once, so a step in which no tail
+// fills costs one launch of early-exit work-groups.
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
+  constexpr int NT = kResyncNT, NW = DV / (16 * NT);
+  static_assert(NW <= 4, "the chain step's waves fit the work-group");
+  __shared__ ChunkLdsB<DK, DV> sm;
+  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  if (a.flag[sh] == 0) return;
+  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  const size_t tr = ch * a.Cl;
+  uint8_t* const prod = a.prod + sh * prod_slot_bytes(true, DK, DV);
+  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, tr, 1, (const uint16_t*)a.tail_v, tr, 1,
+                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, tr, 1, a.Cl);
+  chunk_local_bf16<DK, DV>(sm, prod, a.gamn + sh);
+  __syncthreads();  // the slot and Gamma_n, written by every wave, are read below
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < NW) {
+    const int jb0 = wave * NT;
+    const size_t SS = (size_t)DK * DV;
+    mfma::f32x4 S[DK / 16][NT];
+    load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * SS, jb0, lane);
+    chain_step_bf16_global<DK, DV, NT>(S, prod, a.gamn[sh], jb0, lane);
+    store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
+    store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
+  }
+  if (threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -2070,9 +2093,7 @@ gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
   hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(DV), 0, st, a);
   mark(1, st);
   if constexpr (std::is_same<D, Bf16>::value) {
-    hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(a.N, a.H, DV / (16 * kResyncNT) / kResyncWaves<DV>),
-                       dim3(64 * kResyncWaves<DV>), 0, st, a);
+    hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
     hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
@@ -2133,10 +2154,7 @@ struct ContFn {
                         const char* fn) {
     hipLaunchKernelGGL((k_cont_head<D, DK, DV>), dim3(ca.N, ca.H), dim3(DV), 0, st, ca);
     if constexpr (std::is_same<D, Bf16>::value) {
-      hipLaunchKernelGGL((k_chunk_local_resync_bf16<DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
-      hipLaunchKernelGGL((k_chain_resync_bf16<DK, DV>), dim3(da.N, da.H, DV / (16 * kResyncNT) / kResyncWaves<DV>),
-                         dim3(64 * kResyncWaves<DV>), 0, st,
-                         da);
+      hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
     } else {
       hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
       hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(da.N, da.H, DV / kChainCols), dim3(256), 0, st, da);

@@ -72,6 +72,68 @@ def stats(xs):
             "p90": round(float(np.percentile(a, 90)), 5), "min": round(float(a.min()), 5)}
 
 
+def _gfx_clock_from(data):
+    """First graphics-clock reading (MHz) in amd-smi or rocm-smi JSON output."""
+    import re
+    if isinstance(data, dict):
+        for key, val in data.items():
+            k = str(key).lower()
+            if k.startswith("gfx") and isinstance(val, dict):
+                clk = val.get("clk", val)
+                v = clk.get("value") if isinstance(clk, dict) else None
+                if isinstance(v, (int, float)) and v > 0:
+                    return float(v)
+            if k.startswith("sclk clock speed") and isinstance(val, str):
+                m = re.search(r"(\d+)\s*mhz", val.lower())
+                if m:
+                    return float(m.group(1))
+        for val in data.values():
+            r = _gfx_clock_from(val)
+            if r:
+                return r
+    elif isinstance(data, list):
+        for val in data:
+            r = _gfx_clock_from(val)
+            if r:
+                return r
+    return None
+
+
+def read_gfx_clock():
+    """(MHz, command) of GPU 0's current graphics clock from amd-smi, else
+    rocm-smi (child processes), or (None, None)."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            out = subprocess.run(cmd, capture_output=True, text=True, timeout=20).stdout
+            v = _gfx_clock_from(json.loads(out))
+        except Exception:
+            continue
+        if v:
+            return v, " ".join(cmd)
+    return None, None
+
+
+def clock_under_load(run, max_s=30.0):
+    """Read the graphics clock once while run() is issued back to back."""
+    import threading
+
+    import torch
+    res = []
+    th = threading.Thread(target=lambda: res.append(read_gfx_clock()), daemon=True)
+    th.start()
+    t_end = time.perf_counter() + max_s
+    n = 0
+    while th.is_alive() and time.perf_counter() < t_end:
+        run()
+        n += 1
+        if n % 32 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    return res[0] if res else (None, None)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -210,6 +272,11 @@ def main():
     ms_per_step = total_ms / args.steps
     toks = T + N_dec
     value = toks / (ms_per_step / 1e3)
+    log("graphics clock under the prefill (amd-smi)")
+    s0c = sets[0]
+    clk_mhz, clk_src = clock_under_load(
+        lambda: gdn.gdn_cpr_prefill(shape, s0c["q"], s0c["k"], s0c["v"], s0c["g"], s0c["beta"], s0c["cu"], None,
+                                    caches[0], outs[0], ws_pre))
 
     # ---- decode over 64 consecutive steps (one chunk: exactly one resync per
     # sequence) on a fresh copy of the 2,048-token-prefix cache
@@ -438,6 +505,7 @@ def main():
         "data": "synthetic (seeded GDN-shaped inputs; see gdn_synth)",
         "config": {"workload": "prefill 5x2048 tokens + decode 256 seqs x 1 token (2048-token prefix)",
                    "heads": H, "d_k": D, "d_v": D, "chunk": C, "state": "fp32"},
+        "gpu_clock_mhz": {"gfx_under_prefill": clk_mhz, "source": clk_src},
         "timing_stats_ms": {"prefill": stats(prefill_ms), "scan": stats(scan_ms),
                             "decode_token_step": stats(dstep_ms), "decode_call": stats(decode_ms),
                             "samples": len(prefill_ms)},

@@ -753,23 +753,44 @@ __device__ __forceinline__ void stage_chunk_bf16(ChunkLdsB<DK, DV>& sm, const ui
                                                  size_t v_stride, const uint16_t* __restrict__ g,
                                                  const uint16_t* __restrict__ beta, size_t gb0,
                                                  size_t gb_stride, int n) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+  // 256 threads (every caller's work-group): all of a thread's loads are
+  // issued before its first LDS write, so the staging costs one memory
+  // round trip rather than one per 16-byte piece
+  constexpr int NT = 256, MK = kChunk * DK / 8 / NT, MV = kChunk * DV / 8 / NT;
+  static_assert(MK * NT == kChunk * DK / 8 && MV * NT == kChunk * DV / 8 && kChunk <= NT, "staging split");
+  const int tid = threadIdx.x;
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  for (int idx = tid; idx < kChunk * DK / 8; idx += nt) {
-    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    u32x4v w = {0u, 0u, 0u, 0u};
-    if (t < n) w = *reinterpret_cast<const u32x4v*>(k + (k_row0 + (size_t)t * k_stride) * DK + i0);
-    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
+  // rows past n load row n - 1 (callers have n >= 1) and are zeroed after
+  // the loads, so no load sits behind a branch
+  const int last = n > 0 ? n - 1 : 0;
+  u32x4v wk[MK], wv[MV];
+#pragma unroll
+  for (int m = 0; m < MK; ++m) {
+    const int idx = tid + m * NT, t = min(idx / (DK / 8), last), i0 = (idx % (DK / 8)) * 8;
+    wk[m] = *reinterpret_cast<const u32x4v*>(k + (k_row0 + (size_t)t * k_stride) * DK + i0);
   }
-  for (int idx = tid; idx < kChunk * DV / 8; idx += nt) {
-    const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-    u32x4v w = {0u, 0u, 0u, 0u};
-    if (t < n) w = *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
-    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) = w;
+#pragma unroll
+  for (int m = 0; m < MV; ++m) {
+    const int idx = tid + m * NT, t = min(idx / (DV / 8), last), j0 = (idx % (DV / 8)) * 8;
+    wv[m] = *reinterpret_cast<const u32x4v*>(v + (v_row0 + (size_t)t * v_stride) * DV + j0);
   }
-  for (int t = tid; t < kChunk; t += nt) {
-    sm.gam[t] = t < n ? Bf16::load(g, gb0 + (size_t)t * gb_stride) : 0.f;
-    sm.beta[t] = t < n ? Bf16::load(beta, gb0 + (size_t)t * gb_stride) : 0.f;
+  const int tg = min(tid, last);
+  const float gl = Bf16::load(g, gb0 + (size_t)tg * gb_stride);
+  const float bl = Bf16::load(beta, gb0 + (size_t)tg * gb_stride);
+  const u32x4v zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int m = 0; m < MK; ++m) {
+    const int idx = tid + m * NT, t = idx / (DK / 8);
+    *reinterpret_cast<u32x4v*>(&sm.K[t][(idx % (DK / 8)) * 8]) = t < n ? wk[m] : zero;
+  }
+#pragma unroll
+  for (int m = 0; m < MV; ++m) {
+    const int idx = tid + m * NT, t = idx / (DV / 8);
+    *reinterpret_cast<u32x4v*>(&sm.V[t][(idx % (DV / 8)) * 8]) = t < n ? wv[m] : zero;
+  }
+  if (tid < kChunk) {
+    sm.gam[tid] = tid < n ? gl : 0.f;
+    sm.beta[tid] = tid < n ? bl : 0.f;
   }
   __syncthreads();
 }

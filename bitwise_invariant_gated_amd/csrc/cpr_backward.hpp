@@ -91,6 +91,31 @@ struct ChunkScalars {
   float g[C], beta[C], gam[C], Gam[C], e[C];
 };
 
+// gamma, Gamma, e from token tid's g and beta (threads tid < C; padding
+// tokens pass 0), loaded by the caller ahead of its other staging.
+__device__ __forceinline__ void chunk_scalars_from(ChunkScalars& cs, float g_t, float beta_t) {
+  const int tid = threadIdx.x;
+  if (tid < C) {
+    cs.g[tid] = g_t;
+    cs.beta[tid] = beta_t;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float acc = cs.g[0];
+    cs.gam[0] = acc;
+    for (int t = 1; t < C; ++t) {
+      acc = acc + cs.g[t];
+      cs.gam[t] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    cs.Gam[tid] = expf(cs.gam[tid]);
+    cs.e[tid] = expf(cs.gam[C - 1] - cs.gam[tid]);
+  }
+  __syncthreads();
+}
+
 // g, beta of the chunk's n real tokens (padding: 0), gamma, Gamma, e.
 template <class D>
 __device__ __forceinline__ void chunk_scalars(ChunkScalars& cs, const typename D::T* g, const typename D::T* beta,

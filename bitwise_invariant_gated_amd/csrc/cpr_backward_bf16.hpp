@@ -129,17 +129,62 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// rows t < n of a [T, H, D] bf16 tensor (row t at src + (row0 + t H) D) into
-// LDS; rows t >= n are zero
-template <int D, int LD>
-__device__ __forceinline__ void stage_rows(uint16_t (*dst)[LD], const uint16_t* __restrict__ src, size_t row0,
-                                           int H, int n) {
-  for (int idx = threadIdx.x; idx < C * D / 8; idx += blockDim.x) {
-    const int t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (t < n) w = *reinterpret_cast<const u32x4*>(src + (row0 + (size_t)t * H) * D + c8);
-    *reinterpret_cast<u32x4*>(&dst[t][c8]) = w;
+// Staging in two halves, so that a stage issues all of its global loads
+// before its first LDS write (one memory round trip, not one per piece).
+// Rows t < n of a [T, H, D] bf16 tensor (row t at src + (row0 + t H) D) over
+// NT threads; rows t >= n load row n - 1 (n >= 1) and are stored as zeros.
+template <int D, int NT>
+struct RowLoads {
+  static constexpr int M = C * D / 8 / NT;
+  static_assert(M * NT == C * D / 8, "rows split over the threads");
+  u32x4 w[M];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, size_t row0, int H, int n) {
+    const int last = n > 0 ? n - 1 : 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int idx = threadIdx.x + m * NT, t = min(idx / (D / 8), last), c8 = (idx % (D / 8)) * 8;
+      w[m] = *reinterpret_cast<const u32x4*>(src + (row0 + (size_t)t * H) * D + c8);
+    }
   }
+  template <int LD>
+  __device__ __forceinline__ void store(uint16_t (*dst)[LD], int n) const {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int idx = threadIdx.x + m * NT, t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&dst[t][c8]) = t < n ? w[m] : zero;
+    }
+  }
+};
+
+// The slot's X (C x C fp32, row-major) over NT threads.
+template <int NT>
+struct XLoads {
+  static constexpr int M = C * C / 4 / NT;
+  static_assert(M * NT == C * C / 4, "X split over the threads");
+  f32x4 w[M];
+  __device__ __forceinline__ void load(const float* __restrict__ Xg) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) w[m] = reinterpret_cast<const f32x4*>(Xg)[threadIdx.x + m * NT];
+  }
+  template <int LD>
+  __device__ __forceinline__ void store(float (*X)[LD]) const {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int idx = threadIdx.x + m * NT, t = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
+      *reinterpret_cast<f32x4*>(&X[t][s4]) = w[m];
+    }
+  }
+};
+
+// token threadIdx.x's g and beta (threads < C), 0 past the chunk's n tokens
+__device__ __forceinline__ void load_scalars(const uint16_t* gp, const uint16_t* bp, size_t row0, int H, int n,
+                                             float& g_t, float& b_t) {
+  const int last = n > 0 ? n - 1 : 0, t = min((int)threadIdx.x, last);
+  const float g = Bf16::load(gp, row0 + (size_t)t * H), b = Bf16::load(bp, row0 + (size_t)t * H);
+  const bool real = (int)threadIdx.x < n;
+  g_t = real ? g : 0.f;
+  b_t = real ? b : 0.f;
 }
 
 // tiles on or below the diagonal of a C x C matrix: index q in [0, 10)
@@ -172,10 +217,19 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   // d-wide products: wave w makes the 16-wide tiles w, w + W, ...
   static_assert((DK / 16) % W == 0 && (DV / 16) % W == 0 && W >= 4, "tiles per wave");
-  stage_rows<DK>(sm.K, k, kq0, Hk, n);
-  stage_rows<DK>(sm.Q, q, kq0, Hk, n);
-  stage_rows<DV>(sm.dO, d_o, row0, H, n);
-  bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
+  {
+    RowLoads<DK, 64 * W> rk, rq;
+    RowLoads<DV, 64 * W> rd;
+    float g_t, b_t;
+    rk.load(k, kq0, Hk, n);
+    rq.load(q, kq0, Hk, n);
+    rd.load(d_o, row0, H, n);
+    load_scalars(gp, bp, row0, H, n, g_t, b_t);
+    rk.store(sm.K, n);
+    rq.store(sm.Q, n);
+    rd.store(sm.dO, n);
+    bwd::chunk_scalars_from(sm.cs, g_t, b_t);  // synchronises
+  }
   const bwd::ChunkScalars& cs = sm.cs;
   // L (strictly lower) and P (lower, diagonal included) from the 10 lower tiles each
   for (int q2 = wave; q2 < 20; q2 += W) {
@@ -359,14 +413,22 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
   const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
   const float* Ddlg = reinterpret_cast<const float*>(slot + Sl::oDdl);
   const float* dBp = reinterpret_cast<const float*>(slot + Sl::oDbp);
-  stage_rows<DK>(sm.K, k, kq0, Hk, n);
-  stage_rows<DV>(sm.V, v, row0, H, n);
-  stage_rows<DV>(sm.dO, d_o, row0, H, n);
-  for (int idx = tid; idx < C * C / 4; idx += 64 * W) {
-    const int t = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
-    *reinterpret_cast<f32x4*>(&sm.X[t][s4]) = *reinterpret_cast<const f32x4*>(Xg + (size_t)t * C + s4);
+  {
+    RowLoads<DK, 64 * W> rk;
+    RowLoads<DV, 64 * W> rv, rd;
+    XLoads<64 * W> rx;
+    float g_t, b_t;
+    rk.load(k, kq0, Hk, n);
+    rv.load(v, row0, H, n);
+    rd.load(d_o, row0, H, n);
+    rx.load(Xg);
+    load_scalars(gp, bp, row0, H, n, g_t, b_t);
+    rk.store(sm.K, n);
+    rv.store(sm.V, n);
+    rd.store(sm.dO, n);
+    rx.store(sm.X);
+    bwd::chunk_scalars_from(sm.cs, g_t, b_t);  // synchronises
   }
-  bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
   const bwd::ChunkScalars& cs = sm.cs;
   float* Ddg = reinterpret_cast<float*>(slot + Sl::oDd);
   float* Deg = reinterpret_cast<float*>(slot + Sl::oDe);
@@ -552,15 +614,24 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   const float* QBg = reinterpret_cast<const float*>(slot + Sl::oQB);
   const float* DWg = reinterpret_cast<const float*>(slot + Sl::oDWn);
   const float* KTg = reinterpret_cast<const float*>(slot + Sl::oDKt);
-  stage_rows<DK>(sm.K, k, kq0, Hk, n);
-  stage_rows<DK>(sm.Q, q, kq0, Hk, n);
-  stage_rows<DV>(sm.V, v, row0, H, n);
-  stage_rows<DV>(sm.dO, d_o, row0, H, n);
-  for (int idx = tid; idx < C * C / 4; idx += 64 * W) {
-    const int t = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
-    *reinterpret_cast<f32x4*>(&sm.X[t][s4]) = *reinterpret_cast<const f32x4*>(Xg + (size_t)t * C + s4);
+  {
+    RowLoads<DK, 64 * W> rk, rq;
+    RowLoads<DV, 64 * W> rv, rd;
+    XLoads<64 * W> rx;
+    float g_t, b_t;
+    rk.load(k, kq0, Hk, n);
+    rq.load(q, kq0, Hk, n);
+    rv.load(v, row0, H, n);
+    rd.load(d_o, row0, H, n);
+    rx.load(Xg);
+    load_scalars(gp, bp, row0, H, n, g_t, b_t);
+    rk.store(sm.K, n);
+    rq.store(sm.Q, n);
+    rv.store(sm.V, n);
+    rd.store(sm.dO, n);
+    rx.store(sm.X);
+    bwd::chunk_scalars_from(sm.cs, g_t, b_t);  // synchronises
   }
-  bwd::chunk_scalars<Bf16>(sm.cs, gp, bp, row0, H, n);  // synchronises
   const bwd::ChunkScalars& cs = sm.cs;
 
   constexpr int NB = C / 16;

@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the graphics-clock reading (about a second of extra prefills), e.g. under a profiler")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run)")
@@ -272,11 +274,13 @@ def main():
     ms_per_step = total_ms / args.steps
     toks = T + N_dec
     value = toks / (ms_per_step / 1e3)
-    log("graphics clock under the prefill (amd-smi)")
-    s0c = sets[0]
-    clk_mhz, clk_src = clock_under_load(
-        lambda: gdn.gdn_cpr_prefill(shape, s0c["q"], s0c["k"], s0c["v"], s0c["g"], s0c["beta"], s0c["cu"], None,
-                                    caches[0], outs[0], ws_pre))
+    clk_mhz, clk_src = None, None
+    if not args.no_clock:
+        log("graphics clock under the prefill (amd-smi)")
+        s0c = sets[0]
+        clk_mhz, clk_src = clock_under_load(
+            lambda: gdn.gdn_cpr_prefill(shape, s0c["q"], s0c["k"], s0c["v"], s0c["g"], s0c["beta"], s0c["cu"], None,
+                                        caches[0], outs[0], ws_pre))
 
     # ---- decode over 64 consecutive steps (one chunk: exactly one resync per
     # sequence) on a fresh copy of the 2,048-token-prefix cache

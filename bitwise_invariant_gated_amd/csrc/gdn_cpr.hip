@@ -933,27 +933,8 @@ __global__ __launch_bounds__(256, 3) void k_cmp_chunk_local_bf16(const CmpArgs a
   const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
   const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
   const size_t row0 = tok0 * H + h, kq0 = kq_row(tok0, h, a.Hk, a.G);
-  const uint16_t* kp = (const uint16_t*)a.k;
-  const uint16_t* vp = (const uint16_t*)a.v;
-  const int tid = threadIdx.x;
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  for (int idx = tid; idx < C * DK / 8; idx += 256) {
-    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    u32x4v w = {0u, 0u, 0u, 0u};
-    if (t < n) w = *reinterpret_cast<const u32x4v*>(kp + (kq0 + (size_t)t * a.Hk) * DK + i0);
-    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
-  }
-  for (int idx = tid; idx < C * DV / 8; idx += 256) {
-    const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-    u32x4v w = {0u, 0u, 0u, 0u};
-    if (t < n) w = *reinterpret_cast<const u32x4v*>(vp + (row0 + (size_t)t * H) * DV + j0);
-    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) = w;
-  }
-  if (tid < C) {
-    sm.gam[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
-    sm.beta[tid] = tid < n ? Bf16::load((const uint16_t*)a.beta, row0 + (size_t)tid * H) : 0.f;
-  }
-  __syncthreads();
+  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, kq0, a.Hk, (const uint16_t*)a.v, row0, H,
+                           (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H, n);
   const size_t ps = (size_t)slot * H + h;
   chunk_local_bf16<DK, DV>(sm, a.prod + ps * Sl::bytes, a.gamn + ps);
 }

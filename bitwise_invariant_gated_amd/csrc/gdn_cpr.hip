@@ -1111,26 +1111,41 @@ __global__ __launch_bounds__(256, 3) void k_cmp_cdec_local_bf16(const DecodeArgs
   const uint16_t* kp = (const uint16_t*)a.k;
   const uint16_t* vp = (const uint16_t*)a.v;
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  for (int idx = tid; idx < C * DK / 8; idx += 256) {
-    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    u32x4v w = {0u, 0u, 0u, 0u};
-    if (t < tl) w = *reinterpret_cast<const u32x4v*>(tk + (ch * C + t) * DK + i0);
-    if (t == tl) w = *reinterpret_cast<const u32x4v*>(kp + kr * DK + i0);
-    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = w;
+  // rows t < tl from the tail, row tl the token, rows past it zero: every
+  // load is issued (rows past tl load the token again) before the LDS writes
+  constexpr int MK = C * DK / 8 / 256, MV = C * DV / 8 / 256;
+  u32x4v lk[MK], lv[MV];
+#pragma unroll
+  for (int m = 0; m < MK; ++m) {
+    const int idx = tid + 256 * m, t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
+    const uint16_t* src = t < tl ? tk + (ch * C + t) * DK : kp + kr * DK;
+    lk[m] = *reinterpret_cast<const u32x4v*>(src + i0);
   }
-  for (int idx = tid; idx < C * DV / 8; idx += 256) {
-    const int t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-    u32x4v w = {0u, 0u, 0u, 0u};
-    if (t < tl) w = *reinterpret_cast<const u32x4v*>(tv + (ch * C + t) * DV + j0);
-    if (t == tl) w = *reinterpret_cast<const u32x4v*>(vp + sh * DV + j0);
-    *reinterpret_cast<u32x4v*>(&sm.V[t][j0]) = w;
+#pragma unroll
+  for (int m = 0; m < MV; ++m) {
+    const int idx = tid + 256 * m, t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
+    const uint16_t* src = t < tl ? tv + (ch * C + t) * DV : vp + sh * DV;
+    lv[m] = *reinterpret_cast<const u32x4v*>(src + j0);
+  }
+  const int ts = min(tid, C - 1);
+  const uint16_t* gs = ts < tl ? (const uint16_t*)a.tail_g : (const uint16_t*)a.g;
+  const uint16_t* bs = ts < tl ? (const uint16_t*)a.tail_beta : (const uint16_t*)a.beta;
+  const size_t r = ts < tl ? ch * C + ts : sh;
+  const float gl = Bf16::load(gs, r), bl = Bf16::load(bs, r);
+  const u32x4v zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int m = 0; m < MK; ++m) {
+    const int idx = tid + 256 * m, t = idx / (DK / 8);
+    *reinterpret_cast<u32x4v*>(&sm.K[t][(idx % (DK / 8)) * 8]) = t <= tl ? lk[m] : zero;
+  }
+#pragma unroll
+  for (int m = 0; m < MV; ++m) {
+    const int idx = tid + 256 * m, t = idx / (DV / 8);
+    *reinterpret_cast<u32x4v*>(&sm.V[t][(idx % (DV / 8)) * 8]) = t <= tl ? lv[m] : zero;
   }
   if (tid < C) {
-    const uint16_t* gs = tid < tl ? (const uint16_t*)a.tail_g : (const uint16_t*)a.g;
-    const uint16_t* bs = tid < tl ? (const uint16_t*)a.tail_beta : (const uint16_t*)a.beta;
-    const size_t r = tid < tl ? ch * C + tid : sh;
-    sm.gam[tid] = tid <= tl ? Bf16::load(gs, r) : 0.f;
-    sm.beta[tid] = tid <= tl ? Bf16::load(bs, r) : 0.f;
+    sm.gam[tid] = tid <= tl ? gl : 0.f;
+    sm.beta[tid] = tid <= tl ? bl : 0.f;
   }
   __syncthreads();
   chunk_local_bf16<DK, DV>(sm, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn + sh);

@@ -677,12 +677,21 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
     if (col == 0) a.flag[sh] = 0;
     return;
   }
+  const T* kp = (const T*)a.k;
+  const T* qp = (const T*)a.q;
+  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
+  // the token's k, v, g, beta as stored, for the tail append at the end
+  // (loaded here, before any store, so the append needs no second read)
+  constexpr int KE = (DK + DV - 1) / DV;
+  T k_app[KE];
+#pragma unroll
+  for (int m = 0; m < KE; ++m) k_app[m] = col + m * DV < DK ? kp[kr * DK + col + m * DV] : T();
+  const T v_app = ((const T*)a.v)[sh * DV + col];
+  const T g_app = ((const T*)a.g)[sh], b_app = ((const T*)a.beta)[sh];
   float* R = a.s_run + ch * SS;
   float s[DK];
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
   bool ren;
   const float x = scale_advance(lg, D::load((const T*)a.g, sh), ren);
   float cs, rs;
@@ -693,16 +702,17 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   }
   const float bt = D::load((const T*)a.beta, sh);
   const float vv = D::load((const T*)a.v, sh * DV + col);
-  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
   const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
   D::store((T*)a.o, sh * DV + col, out);
   // append the token to the tail
   T* tk = (T*)a.tail_k + (ch * Cl + tl) * DK;
-  for (int e = col; e < DK; e += DV) tk[e] = kp[kr * DK + e];
-  ((T*)a.tail_v)[(ch * Cl + tl) * DV + col] = ((const T*)a.v)[sh * DV + col];
+#pragma unroll
+  for (int m = 0; m < KE; ++m)
+    if (col + m * DV < DK) tk[col + m * DV] = k_app[m];
+  ((T*)a.tail_v)[(ch * Cl + tl) * DV + col] = v_app;
   if (col == 0) {
-    ((T*)a.tail_g)[ch * Cl + tl] = ((const T*)a.g)[sh];
-    ((T*)a.tail_beta)[ch * Cl + tl] = ((const T*)a.beta)[sh];
+    ((T*)a.tail_g)[ch * Cl + tl] = g_app;
+    ((T*)a.tail_beta)[ch * Cl + tl] = b_app;
   }
   const bool full = (tl + 1 == Cl);
   if (!full) {

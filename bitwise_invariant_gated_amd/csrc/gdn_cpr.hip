@@ -803,8 +803,16 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   const T* vp = (const T*)a.v;
   const T* gp = (const T*)a.g;
   const T* bp = (const T*)a.beta;
+  constexpr int KE = (DK + DV - 1) / DV;
   for (int t = 0; t < nh; ++t) {
     const size_t row = (size_t)(a.cu[i] + t) * H + h;
+    const size_t kr = kq_row((size_t)(a.cu[i] + t), h, a.Hk, a.G);
+    // the token's k, v, g, beta as stored, for the tail append below (read
+    // before the output store, so the append needs no second read)
+    T k_app[KE];
+#pragma unroll
+    for (int m = 0; m < KE; ++m) k_app[m] = col + m * DV < DK ? kp[kr * DK + col + m * DV] : T();
+    const T v_app = vp[row * DV + col], g_app = gp[row], b_app = bp[row];
     bool ren;
     const float x = scale_advance(lg, D::load(gp, row), ren);
     float cs, rs;
@@ -816,16 +824,17 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
     lg = ren ? 0.f : x;
     const float bt = D::load(bp, row);
     const float vv = D::load(vp, row * DV + col);
-    const size_t kr = kq_row((size_t)(a.cu[i] + t), h, a.Hk, a.G);
     const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
     D::store((T*)a.o, row * DV + col, out);
     const size_t tr = ch * Cl + tl + t;  // tail row
     T* tk = (T*)a.tail_k + tr * DK;
-    for (int e = col; e < DK; e += DV) tk[e] = kp[kr * DK + e];
-    ((T*)a.tail_v)[tr * DV + col] = vp[row * DV + col];
+#pragma unroll
+    for (int m = 0; m < KE; ++m)
+      if (col + m * DV < DK) tk[col + m * DV] = k_app[m];
+    ((T*)a.tail_v)[tr * DV + col] = v_app;
     if (col == 0) {
-      ((T*)a.tail_g)[tr] = gp[row];
-      ((T*)a.tail_beta)[tr] = bp[row];
+      ((T*)a.tail_g)[tr] = g_app;
+      ((T*)a.tail_beta)[tr] = b_app;
     }
   }
   const bool full = (tl + nh == Cl);

@@ -386,18 +386,32 @@ struct StateLds {
   float red[64 * W];
 };
 
-// stage columns 32 jb .. 32 jb + 31 of a TL state (DK rows) into Bs
-template <int DK, int LB>
-__device__ __forceinline__ void stage_cols(float (*Bs)[LB], const float* __restrict__ T, int jb) {
-  for (int pc = threadIdx.x; pc < 2 * (DK / 16) * 64; pc += blockDim.x) {
-    const int tt = pc >> 6, l = pc & 63;
-    const int jt = 2 * jb + tt / (DK / 16), im = tt % (DK / 16);
-    const f32x4 v = tl4<DK>(T, im, jt, l);
-    const int c = l & 15, g = l >> 4;
+// Columns 32 jb .. 32 jb + 31 of a TL state (DK rows), over NT threads: load()
+// issues the reads into registers, store() writes them into Bs row-major, so
+// a block's reads can be in flight while the previous block is consumed.
+template <int DK, int NT>
+struct ColLoads {
+  static constexpr int M = 2 * (DK / 16) * 64 / NT;
+  static_assert(M * NT == 2 * (DK / 16) * 64, "columns split over the threads");
+  f32x4 w[M];
+  __device__ __forceinline__ void load(const float* __restrict__ T, int jb) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Bs[16 * im + 4 * g + r][16 * (jt - 2 * jb) + c] = v[r];
+    for (int m = 0; m < M; ++m) {
+      const int pc = threadIdx.x + m * NT, tt = pc >> 6, l = pc & 63;
+      w[m] = tl4<DK>(T, tt % (DK / 16), 2 * jb + tt / (DK / 16), l);
+    }
   }
-}
+  template <int LB>
+  __device__ __forceinline__ void store(float (*Bs)[LB]) const {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int pc = threadIdx.x + m * NT, tt = pc >> 6, l = pc & 63;
+      const int ct = tt / (DK / 16), im = tt % (DK / 16), c = l & 15, g = l >> 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Bs[16 * im + 4 * g + r][16 * ct + c] = w[m][r];
+    }
+  }
+};
 
 template <int DK, int DV, int W>
 __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint16_t* k, const uint16_t* v,
@@ -498,9 +512,12 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
   for (int p = 0; p < NI; ++p)
 #pragma unroll
     for (int tm = 0; tm < C / 16; ++tm) QB[p][tm] = DW[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  ColLoads<DK, 64 * W> cols;
+  cols.load(B, 0);
   for (int jb = 0; jb < DV / 32; ++jb) {
-    stage_cols<DK>(sm.Bs, B, jb);
+    cols.store(sm.Bs);
     __syncthreads();
+    cols.load(jb + 1 < DV / 32 ? B : dBp, jb + 1 < DV / 32 ? jb + 1 : 0);  // next block (or dB's first)
 #pragma unroll
     for (int p = 0; p < NI; ++p) {
       const int it = wave + W * p;
@@ -527,8 +544,9 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
       QB[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};  // reused for dKt
     }
   for (int jb = 0; jb < DV / 32; ++jb) {
-    stage_cols<DK>(sm.Bs, dBp, jb);
+    cols.store(sm.Bs);  // block jb of dB', loaded during the previous block's products
     __syncthreads();
+    if (jb + 1 < DV / 32) cols.load(dBp, jb + 1);
 #pragma unroll
     for (int p = 0; p < NI; ++p) {
       const int it = wave + W * p;

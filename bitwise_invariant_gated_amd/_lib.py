@@ -91,14 +91,14 @@ def load() -> ctypes.CDLL:
                                            ctypes.c_int32]
     lib.gdn_cpr_prefill.restype = ctypes.c_int
     lib.gdn_cpr_prefill.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
-                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cache), _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cache), _vp,
                                     _vp, ctypes.c_size_t, _vp]
     lib.gdn_cpr_decode_step.restype = ctypes.c_int
     lib.gdn_cpr_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, _vp, _vp, _vp, _vp,
-                                        _vp, ctypes.POINTER(Cache), _vp, _vp, ctypes.c_size_t, _vp]
+                                        _vp, ctypes.POINTER(Cache), _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.gdn_cpr_prefill_continue.restype = ctypes.c_int
     lib.gdn_cpr_prefill_continue.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
-                                             _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cache), _vp,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cache), _vp, _vp,
                                              _vp, ctypes.c_size_t, _vp]
     lib.gdn_cpr_fwd_bwd.restype = ctypes.c_int
     lib.gdn_cpr_fwd_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,

@@ -121,35 +121,38 @@ def _stream(stream) -> Optional[int]:
 
 
 def gdn_cpr_prefill(shape: LayerShape, q, k, v, g, beta, cu_seqlens, h0, cache: CprCache, o,
-                    workspace: torch.Tensor, stream=None) -> None:
+                    workspace: torch.Tensor, stream=None, hT=None) -> None:
+    """hT (optional, [N, H, d_k, d_v] fp32) receives every sequence's final state."""
     lib = _lib.load()
     N = int(cu_seqlens.numel()) - 1
     T = int(q.shape[0])
     cc = cache.c()
     _lib.check(lib.gdn_cpr_prefill(ctypes.byref(shape.c()), N, T, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                   _ptr(beta), _ptr(cu_seqlens), _ptr(h0), ctypes.byref(cc), _ptr(o),
-                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+                                   _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(hT), ctypes.byref(cc),
+                                   _ptr(o), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def gdn_cpr_decode_step(shape: LayerShape, q, k, v, g, beta, cache: CprCache, o,
-                        workspace: torch.Tensor, stream=None) -> None:
+                        workspace: torch.Tensor, stream=None, hT=None) -> None:
+    """hT (optional, [N, H, d_k, d_v] fp32) receives the state after the token."""
     lib = _lib.load()
     N = int(q.shape[0])
     cc = cache.c()
     _lib.check(lib.gdn_cpr_decode_step(ctypes.byref(shape.c()), N, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                       _ptr(beta), ctypes.byref(cc), _ptr(o), _ptr(workspace),
+                                       _ptr(beta), ctypes.byref(cc), _ptr(hT), _ptr(o), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
 
 
 def gdn_cpr_prefill_continue(shape: LayerShape, q, k, v, g, beta, cu_seqlens, cache: CprCache, o,
-                             workspace: torch.Tensor, stream=None) -> None:
+                             workspace: torch.Tensor, stream=None, hT=None) -> None:
+    """hT (optional, [N, H, d_k, d_v] fp32) receives every sequence's final state."""
     lib = _lib.load()
     N = int(cu_seqlens.numel()) - 1
     T = int(q.shape[0])
     cc = cache.c()
     _lib.check(lib.gdn_cpr_prefill_continue(ctypes.byref(shape.c()), N, T, _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(g), _ptr(beta), _ptr(cu_seqlens), ctypes.byref(cc),
-                                            _ptr(o), _ptr(workspace), workspace.numel(),
+                                            _ptr(hT), _ptr(o), _ptr(workspace), workspace.numel(),
                                             _stream(stream)))
 
 

@@ -2,21 +2,25 @@
 //
 // Every quantity that must round identically in prefill and decode is
 // computed by exactly one routine in this file:
-//   token_step        the per-token recurrence on one state column, on a
-//                     scaled running state (prefill's in-chunk scan and
-//                     decode both call it; token_step_dpp is the same
-//                     arithmetic with another operand delivery)
-//   chunk_local_f32   chunk products W, U, K~^T, Gamma_n of one chunk
-//                     (prefill's chunk pass and decode's resync call it)
-//   chain_step_f32    boundary advance S' = Gamma_n S + K~^T (U - W S)
-//                     (prefill's boundary chain and decode's resync call it)
+//   token_step        the per-token recurrence on one state column of the
+//                     scaled running state (with its scalars from
+//                     token_scale, step_factors and scale_after); the
+//                     prefill scan (scan_tokens), the decode step and the
+//                     continuation head all call this one function, each
+//                     delivering k and q to it the same way (DPP row
+//                     broadcast from a 16-byte slice per lane)
+//   chunk_local_bf16  chunk products W, U, K~^T, Gamma_n of one chunk
+//   chunk_local_f32   (prefill's chunk pass and decode's resync call them)
+//   chain_step_bf16   boundary advance S' = Gamma_n S + K~^T (U - W S)
+//   chain_step_f32    (prefill's boundary chain and decode's resync call them)
 // The pages that describe the method (IsoExec, section "Chunkwise-Parallel
 // Recurrent (CPR) Gated DeltaNet"; the Chinese page's section on a third way
 // for Gated DeltaNet) fix only the structure: boundary states by the chunk
 // form, then the recurrence inside every chunk from those boundaries, and
-// decode resynchronising every C tokens.  The rounding choices below are this
-// library's own; they are fixed (explicit FMAs, no contraction, fixed loop
-// orders) so that every caller reproduces them bit for bit.
+// decode resynchronising every C tokens, so that the three stages share one
+// rounding rhythm.  The rounding choices below are this library's own; they
+// are fixed (explicit FMAs, no contraction, fixed loop orders) so that every
+// caller reproduces them bit for bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,17 +33,11 @@ namespace cpr {
 constexpr int kChunk = 64;  // C
 constexpr int kWave = 64;
 
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-// Wave-uniform, read-only row pointer: loads through it become scalar loads
-// into SGPRs, which every lane's VALU instruction can read directly.
-typedef const __attribute__((address_space(4))) u32x8* UniformRow;
-
 // ---------------------------------------------------------------------------
 // storage dtypes
 
 struct Bf16 {
   typedef uint16_t T;
-  static constexpr int kRowGroup = 16;  // values per 32-byte scalar load
   __device__ static __forceinline__ float load(const T* p, size_t i) {
     return __uint_as_float((uint32_t)p[i] << 16);
   }
@@ -47,9 +45,6 @@ struct Bf16 {
   // fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32: branch
   // free, IEEE RNE for every non-NaN input; NaN stays NaN).
   __device__ static __forceinline__ uint16_t round(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-  __device__ static __forceinline__ float elem(const u32x8& w, int e) {
-    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
-  }
   // the element's bits as loaded, decoded later (load() = from_bits(load_bits()))
   __device__ static __forceinline__ uint32_t load_bits(const T* p, size_t i) { return p[i]; }
   __device__ static __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
@@ -57,20 +52,11 @@ struct Bf16 {
 
 struct F32 {
   typedef float T;
-  static constexpr int kRowGroup = 8;
   __device__ static __forceinline__ float load(const T* p, size_t i) { return p[i]; }
   __device__ static __forceinline__ void store(T* p, size_t i, float x) { p[i] = x; }
-  __device__ static __forceinline__ float elem(const u32x8& w, int e) { return __uint_as_float(w[e]); }
   __device__ static __forceinline__ uint32_t load_bits(const T* p, size_t i) { return __float_as_uint(p[i]); }
   __device__ static __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b); }
 };
-
-// Hides a pointer's value from the optimiser so that each use issues its own
-// scalar load (bounding SGPR live ranges instead of hoisting every load).
-__device__ __forceinline__ UniformRow fresh(UniformRow p) {
-  asm volatile("" : "+s"(p));
-  return p;
-}
 
 // Buffer resource over [base, base + bytes) for raw (unformatted) buffer
 // loads and stores: the address is the wave-uniform base plus a 32-bit
@@ -87,167 +73,19 @@ __device__ __forceinline__ float lane_bcast(float x, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// The plain per-token step (one state column per lane), used only by the
-// comparators that stand for the orders CPR replaces (recurrent everywhere,
-// and the recurrent decode of "native mixed" serving): the state is decayed
-// element by element at every token.  The CPR path uses token_step below.
+// Operand delivery of the per-token steps: DPP row broadcast.
 //
-// Lane j holds column j of S (S[i][j] = M[j][i], i = 0..DK-1) in s[].  With
-// k, q wave-uniform (scalar registers), the step is, in this exact order:
-//   pass A, i ascending:  s[i] = alpha * s[i];  p_(i mod 2) = fma(s[i], k[i], p_(i mod 2))
-//   p = p_0 + p_1;  u = beta * (v_j - p)
-//   pass B, i ascending:  s[i] = fma(k[i], u, s[i]);  o_(i mod 2) = fma(s[i], q[i], o_(i mod 2))
-//   return o_0 + o_1
-// which is M' = alpha M, p = M' k, u = beta (v - p), M = M' + u k^T, o = M q.
-template <class D, int DK>
-__device__ __forceinline__ float token_step_plain(float (&s)[DK], UniformRow krow, UniformRow qrow,
-                                            float alpha, float beta, float v) {
-  constexpr int G = D::kRowGroup;
-  static_assert(DK % G == 0, "key dim must be a multiple of the scalar load group");
-  float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-  for (int gi = 0; gi < DK / G; ++gi) {
-    const u32x8 w = *fresh(krow + gi);
-#pragma unroll
-    for (int e = 0; e < G; e += 2) {
-      const int i = gi * G + e;
-      s[i] = alpha * s[i];
-      p0 = __builtin_fmaf(s[i], D::elem(w, e), p0);
-      s[i + 1] = alpha * s[i + 1];
-      p1 = __builtin_fmaf(s[i + 1], D::elem(w, e + 1), p1);
-    }
-  }
-  const float u = beta * (v - (p0 + p1));
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-  for (int gi = 0; gi < DK / G; ++gi) {
-    const u32x8 w = *fresh(krow + gi);
-    const u32x8 x = *fresh(qrow + gi);
-#pragma unroll
-    for (int e = 0; e < G; e += 2) {
-      const int i = gi * G + e;
-      s[i] = __builtin_fmaf(D::elem(w, e), u, s[i]);
-      o0 = __builtin_fmaf(s[i], D::elem(x, e), o0);
-      s[i + 1] = __builtin_fmaf(D::elem(w, e + 1), u, s[i + 1]);
-      o1 = __builtin_fmaf(s[i + 1], D::elem(x, e + 1), o1);
-    }
-  }
-  return o0 + o1;
-}
-
-// alpha = exp(g); one definition for the scan and for decode.
-__device__ __forceinline__ float decay_of(float g) { return expf(g); }
-
-// ---------------------------------------------------------------------------
-// The CPR per-token step, on a scaled running state.
+// Every lane 16 r + c holds elements 8c .. 8c+7 of the token's k and q rows
+// (each 16-lane row of the wave holds a full copy; for d_k = 64 lanes c >= 8
+// repeat slot c - 8), and v_fmac_f32_dpp with row_newbcast:c reads element
+// 8c + e from lane c of the lane's own row.  So every lane (one state column)
+// sees every element of k and q without scalar loads, whose cache misses
+// stall the wave.
 //
-// Between chunk boundaries the running state is held as M = exp(lg) N: the
-// state registers (and the cache's s_run) hold N, and lg, one fp32 per
-// sequence and head, is the log of its scale.  A boundary state has lg = 0
-// and N = M.  Token t, with log-decay g, first advances the scale:
-//   x = lg + g                                        (one fp32 add)
-//   x >= kRenormLog:  c = exp(x), r = exp(-x), lg' = x
-//   x <  kRenormLog:  N = exp(x) N element by element, c = r = 1, lg' = 0
-// and then steps N with the scalars c and b = beta r:
-//   p = c (N k)      w = b (v - p)      (= u r with u = beta (v - p))
-//   N = N + w k^T    o = c (N q)
-// In exact arithmetic this is M' = alpha M = c N, p = M' k,
-// M = M' + u k^T = exp(lg') N and o = M q: the update of the pages'
-// recurrence.  The per-element decay multiply of the plain step becomes the
-// scalar c, so a state element costs three FMAs per token (N k, the update,
-// N q) instead of a multiply and three FMAs.  Renormalising keeps |N| within
-// a factor exp(-kRenormLog) of the state's scale, far inside fp32's range;
-// the decision depends only on the sequence's own log-decays since the last
-// boundary, so prefill and decode renormalise at the same tokens.
-//
-// Order (pinned): with k, q wave-uniform, lane j (state column j),
-//   b = beta * r   (per token)
-//   pass A, i ascending:  p_(i mod 4) = fma(N[i], k[i], p_(i mod 4))
-//   w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3)))
-//   pass B, i ascending:  N[i] = fma(k[i], w, N[i]);  o_(i mod 2) = fma(N[i], q[i], o_(i mod 2))
-//   o = c * (o_0 + o_1)
-constexpr float kRenormLog = -32.f;
-
-// log-scale after a token with log-decay g; renorm is set when it falls
-// below kRenormLog (the token then renormalises and the scale becomes 1)
-__device__ __forceinline__ float scale_advance(float lg, float g, bool& renorm) {
-  const float x = lg + g;
-  renorm = x < kRenormLog;
-  return x;
-}
-
-// the step's scalars for log-scale x: c = exp(x) (for a renormalising token,
-// the factor applied to N before a step with c = 1) and r = exp(-x) (1 when
-// renormalising)
-__device__ __forceinline__ void scale_factors(float x, bool renorm, float& c, float& r) {
-  c = expf(x);
-  r = renorm ? 1.f : expf(-x);
-}
-
-// N = c N before a renormalising token's step
-template <int DK>
-__device__ __forceinline__ void renormalise(float (&s)[DK], float c) {
-#pragma unroll
-  for (int i = 0; i < DK; ++i) s[i] = c * s[i];
-}
-
-// state element of a scaled running state: exp(lg) * n (exactly n when lg = 0)
-__device__ __forceinline__ float scale_of_log(float lg) { return expf(lg); }
-
-template <class D, int DK>
-__device__ __forceinline__ float token_step(float (&s)[DK], UniformRow krow, UniformRow qrow, float c, float b,
-                                            float v) {
-  constexpr int G = D::kRowGroup;
-  static_assert(DK % G == 0 && G % 4 == 0, "key dim must be a multiple of the scalar load group");
-  float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-  for (int gi = 0; gi < DK / G; ++gi) {
-    const u32x8 kw = *fresh(krow + gi);
-#pragma unroll
-    for (int e = 0; e < G; e += 4) {
-      const int i = gi * G + e;
-      p0 = __builtin_fmaf(s[i], D::elem(kw, e), p0);
-      p1 = __builtin_fmaf(s[i + 1], D::elem(kw, e + 1), p1);
-      p2 = __builtin_fmaf(s[i + 2], D::elem(kw, e + 2), p2);
-      p3 = __builtin_fmaf(s[i + 3], D::elem(kw, e + 3), p3);
-    }
-  }
-  const float w = b * (v - c * ((p0 + p1) + (p2 + p3)));
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-  for (int gi = 0; gi < DK / G; ++gi) {
-    const u32x8 kw = *fresh(krow + gi);
-    const u32x8 qw = *fresh(qrow + gi);
-#pragma unroll
-    for (int e = 0; e < G; e += 2) {
-      const int i = gi * G + e;
-      s[i] = __builtin_fmaf(D::elem(kw, e), w, s[i]);
-      o0 = __builtin_fmaf(s[i], D::elem(qw, e), o0);
-      s[i + 1] = __builtin_fmaf(D::elem(kw, e + 1), w, s[i + 1]);
-      o1 = __builtin_fmaf(s[i + 1], D::elem(qw, e + 1), o1);
-    }
-  }
-  return c * (o0 + o1);
-}
-
-// ---------------------------------------------------------------------------
-// The per-token steps with k and q delivered by DPP row broadcast.
-//
-// Used by the prefill scan (token_step_dpp) and the recurrent comparator
-// (token_step_plain_dpp).  Instead of scalar loads (whose cache misses
-// stall the wave), every lane 16 r + c vector-loads elements 8c .. 8c+7 of
-// the token's k and q rows (each 16-lane row holds a full copy) and
-// v_fmac_f32_dpp with row_newbcast:c reads element 8c + e from lane c of the
-// lane's own row.  The arithmetic is token_step's, operation for operation
-// and accumulator for accumulator (fma(a, b, c) = fma(b, a, c) exactly), so
-// both routines produce identical bits; the GPU tests compare prefill (this
-// routine) with decode (token_step) bit for bit.  The same holds for the
-// plain pair (token_step_plain_dpp / token_step_plain).
-//
-// Hazard: a DPP instruction must not read a VGPR written by a VALU
-// instruction in the two preceding cycles.  The converted k and q values are
-// passed through an s_nop 1 before each pass, and the build checks the ISA
-// for any remaining DPP-source write within two instructions.
+// Hazard: a DPP instruction must not read, as its DPP source, a VGPR written
+// by a VALU instruction in the two preceding cycles.  The unpacked k and q
+// values pass through an s_nop 1 before each pass, and the build checks the
+// ISA for any remaining DPP-source write within two instructions.
 #define CPR_FMAC_BCAST_CASE(N)                                                                  \
   if constexpr (I == N)                                                                          \
     asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"      \
@@ -275,13 +113,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Raw k and q elements 8c .. 8c+7 of one token (c = lane mod 16).
 template <class D>
 struct KQRaw {
-  uint32_t w[D::kRowGroup == 16 ? 8 : 16];  // k then q: 4 + 4 dwords (bf16) or 8 + 8 (fp32)
+  uint32_t w[sizeof(typename D::T) == 2 ? 8 : 16];  // k then q: 4 + 4 dwords (bf16) or 8 + 8 (fp32)
 };
 
+// this lane's 16-byte slot of a k or q row of DK elements
+template <int DK>
+__device__ __forceinline__ int kq_slot(int lane) {
+  return (lane & 15) & (DK / 8 - 1);  // lanes past the row repeat an in-bounds slot
+}
+
+// k and q of one token from plain row pointers (decode, continuation head)
 template <class D, int DK>
 __device__ __forceinline__ void load_kq(KQRaw<D>& r, const typename D::T* krow, const typename D::T* qrow, int lane) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  const int c = (lane & 15) & (DK / 8 - 1);  // lanes past the row repeat an in-bounds slot
+  const int c = kq_slot<DK>(lane);
   constexpr int n = sizeof(typename D::T) == 2 ? 1 : 2;  // 16-byte loads per 8 elements
 #pragma unroll
   for (int m = 0; m < n; ++m) {
@@ -313,9 +158,26 @@ __device__ __forceinline__ void unpack_kq(const KQRaw<D>& r, float (&kf)[8], flo
   }
 }
 
+// ---------------------------------------------------------------------------
+// The plain per-token step (one state column per lane), used only by the
+// comparators that stand for the orders CPR replaces (recurrent everywhere,
+// and the recurrent decode of "native mixed" serving): the state is decayed
+// element by element at every token.  The CPR path uses token_step below.
+//
+// Lane j holds column j of S (S[i][j] = M[j][i], i = 0..DK-1) in s[].  The
+// step is, in this exact order:
+//   pass A, i ascending:  s[i] = alpha * s[i];  p_(i mod 2) = fma(s[i], k[i], p_(i mod 2))
+//   p = p_0 + p_1;  u = beta * (v_j - p)
+//   pass B, i ascending:  s[i] = fma(k[i], u, s[i]);  o_(i mod 2) = fma(s[i], q[i], o_(i mod 2))
+//   return o_0 + o_1
+// which is M' = alpha M, p = M' k, u = beta (v - p), M = M' + u k^T, o = M q.
+
+// alpha = exp(g) (comparators)
+__device__ __forceinline__ float decay_of(float g) { return expf(g); }
+
 template <int DK>
-__device__ __forceinline__ float token_step_plain_dpp(float (&s)[DK], const float (&kf)[8], const float (&qf)[8],
-                                                      float alpha, float beta, float v) {
+__device__ __forceinline__ float token_step_plain(float (&s)[DK], const float (&kf)[8], const float (&qf)[8],
+                                                  float alpha, float beta, float v) {
   static_assert(DK % 16 == 0 && DK <= 128, "one 16-lane row holds the key row");
   asm volatile("s_nop 1" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
                "v"(kf[7]));
@@ -356,11 +218,83 @@ __device__ __forceinline__ float token_step_plain_dpp(float (&s)[DK], const floa
   return o0 + o1;
 }
 
-// token_step with k and q from DPP row broadcast (the prefill scan's delivery)
+// ---------------------------------------------------------------------------
+// The CPR per-token step, on a scaled running state.
+//
+// Between chunk boundaries the running state is held as M = exp(lg) N: the
+// state registers (and the cache's s_run) hold N, and lg, one fp32 per
+// sequence and head, is the log of its scale.  A boundary state has lg = 0
+// and N = M.  Token t, with log-decay g, first advances the scale
+// (token_scale):
+//   x = lg + g                                        (one fp32 add)
+//   renorm = x < kRenormLog
+// then takes its scalars (step_factors):
+//   c = exp(x),  b = beta * r  with  r = exp(-x)  (r = 1 when renorm)
+// and steps N (token_step):
+//   renorm:  N = c N element by element, then c = 1
+//   p = c (N k)      w = b (v - p)      (= u r with u = beta (v - p))
+//   N = N + w k^T    o = c (N q)
+// and the log-scale after the token is x, or 0 when renorm (scale_after).
+// In exact arithmetic this is M' = alpha M = c N, p = M' k,
+// M = M' + u k^T = exp(lg') N and o = M q: the update of the pages'
+// recurrence.  The per-element decay multiply of the plain step becomes the
+// scalar c, so a state element costs three FMAs per token (N k, the update,
+// N q) instead of a multiply and three FMAs.  Renormalising keeps |N| within
+// a factor exp(-kRenormLog) of the state's scale, far inside fp32's range;
+// the decision depends only on the sequence's own log-decays since the last
+// boundary, so prefill and decode renormalise at the same tokens.
+//
+// Order (pinned): lane j (state column j),
+//   pass A, i ascending:  p_(i mod 4) = fma(k[i], N[i], p_(i mod 4))
+//   w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3)))
+//   pass B, i ascending:  N[i] = fma(k[i], w, N[i]);  o_(i mod 2) = fma(q[i], N[i], o_(i mod 2))
+//   o = c * (o_0 + o_1)
+constexpr float kRenormLog = -32.f;
+
+struct TokenScale {
+  float x;      // lg + g
+  bool renorm;  // x < kRenormLog: the token renormalises
+};
+
+// the scale step of a token with log-decay g on a running state of log-scale lg
+__device__ __forceinline__ TokenScale token_scale(float lg, float g) {
+  const float x = lg + g;
+  return TokenScale{x, x < kRenormLog};
+}
+
+// log-scale of the running state after the token
+__device__ __forceinline__ float scale_after(TokenScale t) { return t.renorm ? 0.f : t.x; }
+
+// the token's step scalars: c = exp(x) (for a renormalising token, the factor
+// applied to N before a step with c = 1) and b = beta * r with r = exp(-x)
+// (r = 1 when renormalising)
+__device__ __forceinline__ void step_factors(TokenScale t, float beta, float& c, float& b) {
+  c = expf(t.x);
+  b = beta * (t.renorm ? 1.f : expf(-t.x));
+}
+
+// N = c N before a renormalising token's step
 template <int DK>
-__device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf)[8], const float (&qf)[8], float c,
-                                                float b, float v) {
+__device__ __forceinline__ void renormalise(float (&s)[DK], float c) {
+#pragma unroll
+  for (int i = 0; i < DK; ++i) s[i] = c * s[i];
+}
+
+// state element of a scaled running state: exp(lg) * n (exactly n when lg = 0)
+__device__ __forceinline__ float scale_of_log(float lg) { return expf(lg); }
+
+// The per-token step.  s: this lane's state column (N); kf, qf: this lane's
+// unpacked k and q elements 8c .. 8c+7 (DPP delivery above); c, b, renorm:
+// the token's scalars (step_factors, token_scale); v: the lane's value
+// element.  Returns the output element o.
+template <int DK>
+__device__ __forceinline__ float token_step(float (&s)[DK], const float (&kf)[8], const float (&qf)[8], float c,
+                                            float b, bool renorm, float v) {
   static_assert(DK % 16 == 0 && DK <= 128, "one 16-lane row holds the key row");
+  if (renorm) {
+    renormalise<DK>(s, c);
+    c = 1.f;
+  }
   asm volatile("s_nop 1" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
                "v"(kf[7]));
   float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
@@ -379,8 +313,8 @@ __device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf
   asm volatile("s_nop 1" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
                "v"(qf[7]));
   float o0 = 0.f, o1 = 0.f;
-  // software-pipelined as in token_step_plain_dpp: the updates of elements
-  // 2j, 2j+1 are followed by the output terms of elements 2j-2, 2j-1
+  // software-pipelined as in token_step_plain: the updates of elements 2j,
+  // 2j+1 are followed by the output terms of elements 2j-2, 2j-1
   static_for<0, DK / 2 + 1>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     if constexpr (j < DK / 2) {
@@ -397,16 +331,34 @@ __device__ __forceinline__ float token_step_dpp(float (&s)[DK], const float (&kf
   return c * (o0 + o1);
 }
 
+// One token of a single-token caller (decode, continuation head): the token's
+// k and q rows, g, beta and value element; the state column s (N) and the
+// log-scale lg are updated in place.  Returns the output element.
+template <class D, int DK>
+__device__ __forceinline__ float token_step_at(float (&s)[DK], float& lg, const typename D::T* krow,
+                                               const typename D::T* qrow, float g, float beta, float v, int lane) {
+  KQRaw<D> raw;
+  load_kq<D, DK>(raw, krow, qrow, lane);
+  const TokenScale ts = token_scale(lg, g);
+  float c, b;
+  step_factors(ts, beta, c, b);
+  float kf[8], qf[8];
+  unpack_kq<D>(raw, kf, qf);
+  const float out = token_step<DK>(s, kf, qf, c, b, ts.renorm, v);
+  lg = scale_after(ts);
+  return out;
+}
+
 // The CPR scan's loop over tokens t = 0 .. n-1 (n >= 1) of one stretch of a
 // sequence that starts on a chunk boundary: token t at row row0 + t * H of v
 // and o and at row kq0 + t * Hk of q and k; output o_t to column col of its
 // row of o; the state (N, from scale 1) updated in place.  Lane t holds token
-// t's step scalars c_l and b_l = beta r (scale_factors); bit t of renorm is
-// set when token t renormalises.  k, q and v of token t+1 are fetched as soon
-// as token t's have been unpacked; every fetch is issued (its index is
-// clamped to token n-1), so the wait before a token's first use of its
-// operands covers that token's loads only.  Rows are addressed as a
-// wave-uniform base plus a 32-bit lane offset (one VGPR per operand kind).
+// t's step scalars c_l and b_l (step_factors); bit t of renorm is set when
+// token t renormalises.  k, q and v of token t+1 are fetched as soon as
+// token t's have been unpacked; every fetch is issued (its index is clamped
+// to token n-1), so the wait before a token's first use of its operands
+// covers that token's loads only.  Rows are addressed as a wave-uniform base
+// plus a 32-bit lane offset (one VGPR per operand kind).
 template <class D, int DK, int DV>
 __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T* __restrict__ kp,
                                             const typename D::T* __restrict__ qp, const typename D::T* __restrict__ vp,
@@ -420,8 +372,7 @@ __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T*
   const BufRsrc rq = buf_rsrc(qp + kq0 * DK, (uint32_t)(n - 1) * kq_stride + DK * sizeof(T));
   const BufRsrc rv = buf_rsrc(vp + row0 * DV, (uint32_t)(n - 1) * v_stride + DV * sizeof(T));
   const BufRsrc ro = buf_rsrc(op + row0 * DV, (uint32_t)(n - 1) * v_stride + DV * sizeof(T));
-  // lanes past the row repeat an in-bounds slot
-  const uint32_t kq_off = (uint32_t)(((lane & 15) & (DK / 8 - 1)) * 8 * sizeof(T));
+  const uint32_t kq_off = (uint32_t)(kq_slot<DK>(lane) * 8 * sizeof(T));
   const uint32_t v_off = (uint32_t)(col * sizeof(T));
   KQRaw<D> raw;
   uint32_t vb;
@@ -452,12 +403,8 @@ __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T*
     asm volatile("" : "+v"(vbits));  // decode v here, not next to its load
     const float vcur = D::from_bits(vbits);
     fetch(t + 1);
-    float cs = lane_bcast(c_l, t);
-    if ((renorm >> t) & 1) {
-      renormalise<DK>(s, cs);
-      cs = 1.f;
-    }
-    const float out = token_step_dpp<DK>(s, kf, qf, cs, lane_bcast(b_l, t), vcur);
+    const float out =
+        token_step<DK>(s, kf, qf, lane_bcast(c_l, t), lane_bcast(b_l, t), (renorm >> t) & 1, vcur);
     if constexpr (sizeof(T) == 2)
       __builtin_amdgcn_raw_buffer_store_b16(D::round(out), ro, v_off, (uint32_t)t * v_stride, 0);
     else
@@ -491,7 +438,7 @@ __device__ __forceinline__ void scan_tokens_plain(float (&s)[DK], const typename
     asm volatile("" : "+v"(vbits));  // decode v here, not next to its load
     const float vcur = D::from_bits(vbits);
     fetch(rn, vn, t + 1);
-    const float out = token_step_plain_dpp<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
+    const float out = token_step_plain<DK>(s, kf, qf, lane_bcast(alpha_l, t), lane_bcast(beta_l, t), vcur);
     D::store(op + (row0 + (size_t)t * H) * DV, col, out);
   };
   fetch(r0, v0, 0);

@@ -24,6 +24,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -70,8 +71,8 @@ struct PrefillArgs {
   void* tail_g;
   void* tail_beta;
   int32_t* tail_len;
-  float* lgs;               // [rows, H] log-scale of s_run (the cache's run_log_scale), or null
-  int32_t run_materialize;  // 1: the partial last chunk writes the state exp(lg) N to s_run (no lgs)
+  float* lgs;  // [rows, H] log-scale of s_run (the cache's run_log_scale), or null
+  float* hT;   // [N, H, DK, DV] final state exp(lg) N of every sequence (batch order), or null
   void* o;
   int32_t* full_base;  // [N+1] prefix sums of full chunks per sequence
   int32_t* all_base;   // [N+1] prefix sums of all chunks (full + partial)
@@ -100,8 +101,9 @@ struct DecodeArgs {
   void* tail_beta;
   int32_t* tail_len;
   float* lgs;  // [rows, H] log-scale of s_run, or null (written 0 when s_run becomes a boundary)
+  float* hT;   // [N, H, DK, DV] state after the step (batch order), or null
   void* o;
-  int32_t* flag;  // [N*H] 1 = this pair resynchronises in this step
+  int32_t* flag;  // [N*H] bit 0: this pair resynchronises in this step; bit 1: the resync also writes hT
   uint8_t* prod;  // [N*H] chunk-product slots of prod_slot_bytes
   float* gamn;    // [N*H]
   int32_t N;
@@ -350,7 +352,10 @@ __global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
     if (c + 1 < nall) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
   }
   put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
-  if (L % Cl == 0) put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
+  if (L % Cl == 0) {
+    put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
+    if (a.hT) put_block<DK, DV, NB>(a.hT + sh * SS, sm, col0);
+  }
   if (blockIdx.z == 0 && threadIdx.x == 0) {
     a.tail_len[ch] = L % Cl;
     if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
@@ -371,6 +376,7 @@ __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   chain_step_f32<DK, NB>(sm);
   put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
   put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
+  if (a.hT && (a.flag[sh] & 2)) put_block<DK, DV, NB>(a.hT + sh * SS, sm, col0);
   if (blockIdx.z == 0 && threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
 }
 
@@ -502,7 +508,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const Prefill
   }
   store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
   if (a.all_chunks) return;
-  if (L % Cl == 0) store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
+  if (L % Cl == 0) {
+    store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
+    if (a.hT) store_state_tiles<DK, DV, NT>(a.hT + sh * SS, S, jb0, lane);
+  }
   if (blockIdx.z == 0 && tid == 0) {
     a.tail_len[ch] = L % Cl;
     if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
@@ -547,7 +556,8 @@ __global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
   static_assert(NW <= 4, "the chain step's waves fit the work-group");
   __shared__ ChunkLdsB<DK, DV> sm;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
-  if (a.flag[sh] == 0) return;
+  const int flag = a.flag[sh];
+  if (flag == 0) return;
   const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
   const size_t tr = ch * a.Cl;
   uint8_t* const prod = a.prod + sh * prod_slot_bytes(true, DK, DV);
@@ -564,6 +574,7 @@ __global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
     chain_step_bf16_global<DK, DV, NT>(S, prod, a.gamn[sh], jb0, lane);
     store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
     store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
+    if (a.hT && (flag & 2)) store_state_tiles<DK, DV, NT>(a.hT + sh * SS, S, jb0, lane);
   }
   if (threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
 }
@@ -606,23 +617,19 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
     g_l = D::load(gp, r);
     beta_l = D::load(bp, r);
   }
-  // log-scale of the running state after every token, in token order from
-  // the boundary (lg = 0); lane t keeps token t's
-  float lg = 0.f, x_l = 0.f;
-  bool ren_l = false;
+  // the scale steps of the chunk's tokens in token order from the boundary
+  // (lg = 0), lane t keeping token t's; then every lane takes its token's
+  // step scalars (the same helpers as the decode step)
+  float lg = 0.f;
+  TokenScale ts_l{0.f, false};
   for (int t = 0; t < n; ++t) {
-    bool ren;
-    const float x = scale_advance(lg, lane_bcast(g_l, t), ren);
-    if (lane == t) {
-      x_l = x;
-      ren_l = ren;
-    }
-    lg = ren ? 0.f : x;
+    const TokenScale ts = token_scale(lg, lane_bcast(g_l, t));
+    if (lane == t) ts_l = ts;
+    lg = scale_after(ts);
   }
-  float c_l, r_l;
-  scale_factors(x_l, ren_l, c_l, r_l);
-  const float b_l = beta_l * r_l;
-  const uint64_t renorm = __ballot(ren_l && lane < n);
+  float c_l, b_l;
+  step_factors(ts_l, beta_l, c_l, b_l);
+  const uint64_t renorm = __ballot(ts_l.renorm && lane < n);
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
@@ -634,14 +641,14 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
     // log-scale lg, or the state itself when materialised), its tokens the tail
     const size_t ch = cache_row(a.slot, i) * H + h;
     float* R = a.s_run + ch * SS;
-    if (a.run_materialize) {
+#pragma unroll
+    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+    if (blockIdx.z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
+    if (a.hT) {  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
+      float* F = a.hT + ((size_t)i * H + h) * SS;
       const float e = scale_of_log(lg);
 #pragma unroll
-      for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = e * s[ii];
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
-      if (blockIdx.z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
+      for (int ii = 0; ii < DK; ++ii) F[(size_t)ii * DV + col] = e * s[ii];
     }
     T* tv = (T*)a.tail_v + ch * Cl * DV;
     for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
@@ -692,17 +699,9 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   float s[DK];
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
-  bool ren;
-  const float x = scale_advance(lg, D::load((const T*)a.g, sh), ren);
-  float cs, rs;
-  scale_factors(x, ren, cs, rs);
-  if (ren) {
-    renormalise<DK>(s, cs);
-    cs = 1.f;
-  }
-  const float bt = D::load((const T*)a.beta, sh);
-  const float vv = D::load((const T*)a.v, sh * DV + col);
-  const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
+  float lg_next = lg;
+  const float out = token_step_at<D, DK>(s, lg_next, kp + kr * DK, qp + kr * DK, D::load(&g_app, 0),
+                                         D::load(&b_app, 0), D::load(&v_app, 0), col);
   D::store((T*)a.o, sh * DV + col, out);
   // append the token to the tail
   T* tk = (T*)a.tail_k + (ch * Cl + tl) * DK;
@@ -718,11 +717,17 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   if (!full) {
 #pragma unroll
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+    if (a.hT) {  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
+      float* F = a.hT + sh * SS;
+      const float e = scale_of_log(lg_next);
+#pragma unroll
+      for (int ii = 0; ii < DK; ++ii) F[(size_t)ii * DV + col] = e * s[ii];
+    }
   }
   if (col == 0) {
     a.tail_len[ch] = full ? 0 : tl + 1;
-    a.lgs[ch] = (full || ren) ? 0.f : x;  // a full tail resynchronises to a boundary (scale 1)
-    a.flag[sh] = full ? 1 : 0;
+    a.lgs[ch] = full ? 0.f : lg_next;  // a full tail resynchronises to a boundary (scale 1)
+    a.flag[sh] = full ? 3 : 0;         // the resync then also writes hT (if asked for)
   }
 }
 
@@ -767,8 +772,9 @@ struct ContArgs {
   void* tail_beta;
   int32_t* tail_len;
   float* lgs;  // [rows, H] log-scale of s_run
+  float* hT;   // [N, H, DK, DV] final state (batch order), or null
   void* o;
-  int32_t* flag;        // [N*H] 1 = this pair closes its chunk in the head
+  int32_t* flag;        // [N*H] as DecodeArgs::flag: bit 0 the head closes the chunk, bit 1 the resync writes hT
   int32_t* body_start;  // [N] first token row after the head
   int32_t N;
   int32_t H;
@@ -793,8 +799,16 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   const int nh = ((unsigned)tl < (unsigned)Cl && tl > 0) ? min(Cl - tl, L) : 0;
   if (h == 0 && col == 0) a.body_start[i] = a.cu[i] + nh;
   if (col == 0) a.flag[sh] = 0;
-  if (nh == 0) return;
   float* R = a.s_run + ch * SS;
+  if (L == 0) {  // nothing new: the final state is the cached one
+    if (a.hT) {
+      const float e = scale_of_log(lg);
+#pragma unroll
+      for (int ii = 0; ii < DK; ++ii) a.hT[sh * SS + (size_t)ii * DV + col] = e * R[(size_t)ii * DV + col];
+    }
+    return;
+  }
+  if (nh == 0) return;  // the body prefill writes the final state
   float s[DK];
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
@@ -813,18 +827,8 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
 #pragma unroll
     for (int m = 0; m < KE; ++m) k_app[m] = col + m * DV < DK ? kp[kr * DK + col + m * DV] : T();
     const T v_app = vp[row * DV + col], g_app = gp[row], b_app = bp[row];
-    bool ren;
-    const float x = scale_advance(lg, D::load(gp, row), ren);
-    float cs, rs;
-    scale_factors(x, ren, cs, rs);
-    if (ren) {
-      renormalise<DK>(s, cs);
-      cs = 1.f;
-    }
-    lg = ren ? 0.f : x;
-    const float bt = D::load(bp, row);
-    const float vv = D::load(vp, row * DV + col);
-    const float out = token_step<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), cs, bt * rs, vv);
+    const float out = token_step_at<D, DK>(s, lg, kp + kr * DK, qp + kr * DK, D::load(&g_app, 0),
+                                           D::load(&b_app, 0), D::load(&v_app, 0), col);
     D::store((T*)a.o, row * DV + col, out);
     const size_t tr = ch * Cl + tl + t;  // tail row
     T* tk = (T*)a.tail_k + tr * DK;
@@ -841,11 +845,17 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   if (!full) {
 #pragma unroll
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+    if (a.hT) {  // the head is the whole segment (nh == L): exp(lg) N is the final state
+      const float e = scale_of_log(lg);
+#pragma unroll
+      for (int ii = 0; ii < DK; ++ii) a.hT[sh * SS + (size_t)ii * DV + col] = e * s[ii];
+    }
   }
   if (col == 0) {
     a.tail_len[ch] = full ? 0 : tl + nh;
     a.lgs[ch] = full ? 0.f : lg;
-    a.flag[sh] = full ? 1 : 0;
+    // a closed chunk resynchronises; with no body after it, that boundary is the final state
+    a.flag[sh] = full ? (nh == L ? 3 : 1) : 0;
   }
 }
 
@@ -933,7 +943,11 @@ __global__ __launch_bounds__(DV) void k_cmp_rec_decode(const CmpArgs a) {
   const float bt = D::load((const T*)a.beta, sh);
   const float vv = D::load((const T*)a.v, sh * DV + col);
   const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
-  const float out = token_step_plain<D, DK>(s, (UniformRow)(kp + kr * DK), (UniformRow)(qp + kr * DK), alpha, bt, vv);
+  KQRaw<D> raw;
+  load_kq<D, DK>(raw, kp + kr * DK, qp + kr * DK, col);
+  float kf[8], qf[8];
+  unpack_kq<D>(raw, kf, qf);
+  const float out = token_step_plain<DK>(s, kf, qf, alpha, bt, vv);
   D::store((T*)a.o, sh * DV + col, out);
 #pragma unroll
   for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
@@ -2020,28 +2034,38 @@ gdn_status launch_status(const char* fn) {
   return GDN_OK;
 }
 
-// A second stream for the overlapped stages of gdn_cpr_fwd_bwd, one per
-// calling thread and device (created on first use at the default priority
-// and kept for the thread's lifetime), with the events that fork work onto
-// it and join it back.  Per thread, so that concurrent callers never wait on
-// each other's events.
+// A second stream for the overlapped stages of bf16 gdn_cpr_fwd_bwd, with the
+// events that fork work onto it and join it back.  Streams come from a
+// bounded pool per device (at most kSidePool, each created on first need at
+// the default priority and kept until the process ends): a call holds one
+// while it enqueues, so concurrent callers never share a stream's events,
+// and the number of streams stays bounded however many threads call.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
 
-// the side stream on the device of st, or nullptr if it cannot be made
-SideStream* side_stream(hipStream_t st) {
-  constexpr int kMaxDevices = 64;
-  thread_local SideStream tab[kMaxDevices];
-  hipDevice_t dev = 0;
-  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& x = tab[dev];
-  if (x.s) return &x;
+constexpr int kSidePool = 8;
+constexpr int kMaxDevices = 64;
+
+struct SidePool {
+  std::mutex m;
+  SideStream made[kSidePool];
+  bool busy[kSidePool] = {};
+  int n = 0;
+};
+
+SidePool& side_pool(int dev) {
+  static SidePool pools[kMaxDevices];
+  return pools[dev];
+}
+
+// creates a side stream and its events on device dev (the current device is
+// restored); false if any of them cannot be made
+bool make_side_stream(int dev, SideStream& y) {
   int cur = 0;
-  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
-  SideStream y;
+  if (hipGetDevice(&cur) != hipSuccess) return false;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return false;
   bool ok = hipStreamCreateWithFlags(&y.s, hipStreamNonBlocking) == hipSuccess;
   hipEvent_t* ev[2] = {&y.fork, &y.join};
   for (int i = 0; i < 2 && ok; ++i) ok = hipEventCreateWithFlags(ev[i], hipEventDisableTiming) == hipSuccess;
@@ -2051,11 +2075,49 @@ SideStream* side_stream(hipStream_t st) {
       if (*ev[i]) (void)hipEventDestroy(*ev[i]);
     if (y.s) (void)hipStreamDestroy(y.s);
     (void)hipGetLastError();
-    return nullptr;
+    y = SideStream{};
   }
-  x = y;
-  return &x;
+  return ok;
 }
+
+// A side stream on the device of st, held for the lease's lifetime; get()
+// is nullptr when none can be had (every pooled stream in use and the pool
+// full, or creation failed): the caller then runs on st alone.
+class SideLease {
+ public:
+  explicit SideLease(hipStream_t st) {
+    hipDevice_t dev = 0;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+      (void)hipGetLastError();
+      return;
+    }
+    SidePool& p = side_pool(dev);
+    std::lock_guard<std::mutex> lock(p.m);
+    for (int i = 0; i < p.n; ++i)
+      if (!p.busy[i]) {
+        take(p, i, dev);
+        return;
+      }
+    if (p.n < kSidePool && make_side_stream(dev, p.made[p.n])) take(p, p.n++, dev);
+  }
+  ~SideLease() {
+    if (slot_ < 0) return;
+    SidePool& p = side_pool(dev_);
+    std::lock_guard<std::mutex> lock(p.m);
+    p.busy[slot_] = false;
+  }
+  SideLease(const SideLease&) = delete;
+  SideLease& operator=(const SideLease&) = delete;
+  const SideStream* get() const { return slot_ < 0 ? nullptr : &side_pool(dev_).made[slot_]; }
+
+ private:
+  void take(SidePool& p, int i, int dev) {
+    p.busy[i] = true;
+    slot_ = i;
+    dev_ = dev;
+  }
+  int slot_ = -1, dev_ = 0;
+};
 
 // bf16 boundary chain: the fewer (sequence, head) pairs, the more work-groups
 // per pair (the column split is bit-neutral)
@@ -2072,6 +2134,11 @@ void launch_chain_bf16(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 4, 1>), dim3(a.N, a.H, DV / 64), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((k_chain_prefill_bf16<DK, DV, 2, 1>), dim3(a.N, a.H, DV / 32), dim3(128), 0, st, a);
+}
+
+template <int DK, int DV>
+void launch_resync_bf16(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
 }
 
 template <class D, int DK, int DV>
@@ -2108,7 +2175,7 @@ gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
   hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(DV), 0, st, a);
   mark(1, st);
   if constexpr (std::is_same<D, Bf16>::value) {
-    hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
+    launch_resync_bf16<DK, DV>(a, st);
   } else {
     hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
     hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
@@ -2169,7 +2236,7 @@ struct ContFn {
                         const char* fn) {
     hipLaunchKernelGGL((k_cont_head<D, DK, DV>), dim3(ca.N, ca.H), dim3(DV), 0, st, ca);
     if constexpr (std::is_same<D, Bf16>::value) {
-      hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
+      launch_resync_bf16<DK, DV>(da, st);
     } else {
       hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
       hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(da.N, da.H, DV / kChainCols), dim3(256), 0, st, da);
@@ -2372,8 +2439,9 @@ struct FwdBwdFn {
     if (slot_bytes != want) return fail(GDN_ERR_HIP, "%s: internal slot size mismatch", fn);
     if constexpr (kBf16) {
       if (T > 0) {
-        // one stream only if the side stream cannot be made
-        if (const SideStream* x = side_stream(st)) return run_overlapped(pa, ba, T, st, *x, fn);
+        // one stream only if no side stream can be had
+        SideLease lease(st);
+        if (const SideStream* x = lease.get()) return run_overlapped(pa, ba, T, st, *x, fn);
       }
     }
     gdn_status r = run_prefill<D, DK, DV>(pa, T, st, fn);
@@ -2423,7 +2491,7 @@ extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num
 
 extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                                       const void* q, const void* k, const void* v, const void* g,
-                                      const void* beta, const int32_t* cu_seqlens, const float* h0,
+                                      const void* beta, const int32_t* cu_seqlens, const float* h0, float* hT,
                                       const gdn_cpr_cache* cache_out, void* o, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_cpr_prefill";
@@ -2434,6 +2502,9 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   if (!cache_out) return fail(GDN_ERR_INVALID_ARG, "%s: cache_out is NULL", fn);
   CHECK_PTR(cu_seqlens, "cu_seqlens");
   CHECK_OPT_PTR(h0, "h0");
+  CHECK_OPT_PTR(hT, "hT");
+  if (hT && (hT == cache_out->s_bnd || hT == cache_out->s_run))
+    return fail(GDN_ERR_INVALID_ARG, "%s: hT aliases the cache", fn);
   CHECK_PTR(cache_out->s_bnd, "cache.s_bnd");
   CHECK_PTR(cache_out->s_run, "cache.s_run");
   CHECK_PTR(cache_out->tail_k, "cache.tail_k");
@@ -2461,7 +2532,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
   char* ws = (char*)workspace;
-  PrefillArgs a;
+  PrefillArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -2482,7 +2553,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.tail_beta = cache_out->tail_beta;
   a.tail_len = cache_out->tail_len;
   a.lgs = cache_out->run_log_scale;
-  a.run_materialize = 0;
+  a.hT = hT;
   a.o = o;
   a.full_base = (int32_t*)(ws + L.full_base);
   a.all_base = (int32_t*)(ws + L.all_base);
@@ -2499,7 +2570,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
 
 extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
                                           const void* k, const void* v, const void* g, const void* beta,
-                                          const gdn_cpr_cache* cache, void* o, void* workspace,
+                                          const gdn_cpr_cache* cache, float* hT, void* o, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_cpr_decode_step";
   std::string why;
@@ -2525,13 +2596,15 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   CHECK_PTR(cache->tail_len, "cache.tail_len");
   CHECK_PTR(cache->run_log_scale, "cache.run_log_scale");
   CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
+  CHECK_OPT_PTR(hT, "hT");
+  if (hT && (hT == cache->s_bnd || hT == cache->s_run)) return fail(GDN_ERR_INVALID_ARG, "%s: hT aliases the cache", fn);
   const DecodeLayout L = decode_layout(*shape, num_seqs);
   if (!workspace || workspace_bytes < L.total)
     return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
   char* ws = (char*)workspace;
-  DecodeArgs a;
+  DecodeArgs a{};
   a.slot = cache->slot_index;
   a.q = q;
   a.k = k;
@@ -2546,6 +2619,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   a.tail_beta = cache->tail_beta;
   a.tail_len = cache->tail_len;
   a.lgs = cache->run_log_scale;
+  a.hT = hT;
   a.o = o;
   a.flag = (int32_t*)(ws + L.flag);
   a.prod = (uint8_t*)(ws + L.prod);
@@ -2561,7 +2635,8 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
 extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                                                const void* q, const void* k, const void* v, const void* g,
                                                const void* beta, const int32_t* cu_seqlens, const gdn_cpr_cache* cache,
-                                               void* o, void* workspace, size_t workspace_bytes, void* stream) {
+                                               float* hT, void* o, void* workspace, size_t workspace_bytes,
+                                               void* stream) {
   const char* fn = "gdn_cpr_prefill_continue";
   std::string why;
   if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
@@ -2578,6 +2653,8 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   CHECK_PTR(cache->tail_len, "cache.tail_len");
   CHECK_PTR(cache->run_log_scale, "cache.run_log_scale");
   CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
+  CHECK_OPT_PTR(hT, "hT");
+  if (hT && (hT == cache->s_bnd || hT == cache->s_run)) return fail(GDN_ERR_INVALID_ARG, "%s: hT aliases the cache", fn);
   if (total_tokens > 0) {
     CHECK_PTR(q, "q");
     CHECK_PTR(k, "k");
@@ -2598,7 +2675,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   char* ws = (char*)workspace;
   char* wd = ws + L.dec_off;
   int32_t* body_start = (int32_t*)(ws + L.body_start);
-  ContArgs ca;
+  ContArgs ca{};
   ca.slot = cache->slot_index;
   ca.q = q;
   ca.k = k;
@@ -2613,6 +2690,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   ca.tail_beta = cache->tail_beta;
   ca.tail_len = cache->tail_len;
   ca.lgs = cache->run_log_scale;
+  ca.hT = hT;
   ca.o = o;
   ca.flag = (int32_t*)(wd + L.dec.flag);
   ca.body_start = body_start;
@@ -2621,7 +2699,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   ca.Hk = key_heads(*shape);
   ca.G = ca.H / ca.Hk;
   ca.Cl = shape->chunk;
-  DecodeArgs da;
+  DecodeArgs da{};
   memset(&da, 0, sizeof(da));
   da.s_bnd = cache->s_bnd;
   da.s_run = cache->s_run;
@@ -2631,6 +2709,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   da.tail_beta = cache->tail_beta;
   da.tail_len = cache->tail_len;
   da.lgs = cache->run_log_scale;
+  da.hT = hT;
   da.flag = ca.flag;
   da.prod = (uint8_t*)(wd + L.dec.prod);
   da.gamn = (float*)(wd + L.dec.gamn);
@@ -2640,7 +2719,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   da.G = da.H / da.Hk;
   da.Cl = shape->chunk;
   da.slot = cache->slot_index;
-  PrefillArgs pa;
+  PrefillArgs pa{};
   pa.q = q;
   pa.k = k;
   pa.v = v;
@@ -2661,7 +2740,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   pa.tail_beta = cache->tail_beta;
   pa.tail_len = cache->tail_len;
   pa.lgs = cache->run_log_scale;
-  pa.run_materialize = 0;
+  pa.hT = hT;
   pa.o = o;
   pa.full_base = (int32_t*)(ws + L.pre.full_base);
   pa.all_base = (int32_t*)(ws + L.pre.all_base);
@@ -2716,7 +2795,7 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
   char* ws = (char*)workspace;
-  PrefillArgs pa;
+  PrefillArgs pa{};
   pa.q = q;
   pa.k = k;
   pa.v = v;
@@ -2730,14 +2809,14 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.all_chunks = 0;
   pa.h0 = h0;
   pa.s_bnd = (float*)(ws + L.s_bnd);
-  pa.s_run = hT ? hT : (float*)(ws + L.s_run);
+  pa.s_run = (float*)(ws + L.s_run);
   pa.tail_k = ws + L.tail_k;
   pa.tail_v = ws + L.tail_v;
   pa.tail_g = ws + L.tail_g;
   pa.tail_beta = ws + L.tail_b;
   pa.tail_len = (int32_t*)(ws + L.tail_len);
   pa.lgs = nullptr;
-  pa.run_materialize = 1;  // hT is the final state itself
+  pa.hT = hT;
   pa.o = o;
   pa.full_base = (int32_t*)(ws + L.pre.full_base);
   pa.all_base = (int32_t*)(ws + L.pre.all_base);
@@ -2836,7 +2915,7 @@ extern "C" gdn_status gdn_cmp_prefill(const gdn_cpr_shape* shape, int32_t mode, 
   ca.H = shape->num_heads;
   ca.Hk = key_heads(*shape);
   ca.G = ca.H / ca.Hk;
-  PrefillArgs pa;
+  PrefillArgs pa{};
   memset(&pa, 0, sizeof(pa));
   if (mode == GDN_CMP_CHUNKWISE) {
     ca.all_base = (int32_t*)(ws + L.all_base);
@@ -2933,7 +3012,7 @@ extern "C" gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int3
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
   char* ws = (char*)workspace;
-  DecodeArgs a;
+  DecodeArgs a{};
   a.slot = cache->slot_index;
   a.q = q;
   a.k = k;
@@ -2990,15 +3069,24 @@ extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) 
 extern "C" const char* gdn_cpr_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" const char* gdn_cpr_numerics_id(void) {
-  return "gdn_cpr numerics v4: token step fp32 on a scaled running state M = exp(lg) N (lg += g, fp32; "
-         "lg < -32: N = exp(lg) N, lg = 0; c = exp(lg), r = exp(-lg); k dot as 4-way i mod 4 explicit-fma "
-         "chains summed (p0+p1)+(p2+p3), p = c dot; u = beta (v - p); w = u r; explicit-fma rank-1 update "
-         "N += w k^T; q dot 2-way even/odd, o = c dot); exp = ocml expf; gamma = left-to-right fp32 cumsum; "
+  return "gdn_cpr numerics v5: "
+         "per-token step (one routine for the prefill scan, decode and the continuation head; k and q by DPP "
+         "row broadcast) in fp32 on a scaled running state M = exp(lg) N: x = lg + g (fp32 add); "
+         "renorm = x < -32; c = exp(x); b = beta * r with r = exp(-x), r = 1 when renorm; renorm: N = c N, "
+         "c = 1; lg after the token = 0 when renorm, else x; lane j (state column j), "
+         "pass A, i ascending: p_(i mod 4) = fma(k[i], N[i], p_(i mod 4)); "
+         "w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3))); "
+         "pass B, i ascending: N[i] = fma(k[i], w, N[i]); o_(i mod 2) = fma(q[i], N[i], o_(i mod 2)); "
+         "o = c * (o_0 + o_1); "
+         "final state = exp(lg) * N elementwise; exp = ocml expf; "
+         "gamma = left-to-right fp32 cumsum of g; "
          "fp32 inputs: chunk products and boundary chain fp32 VALU with ascending explicit-fma sums and "
          "column-wise forward substitution; bf16 inputs: G, W^T, U and the boundary chain on "
          "v_mfma_f32_16x16x32_bf16 (k slots k0+4g+{0..3}, k0+16+4g+{0..3}; k steps ascending) with bf16 "
          "T diag(Gamma), T, K~, S, Delta operands and fp32 accumulation; (I+L)^-1 by 16x16 blocks: "
          "diagonal blocks by fp32 forward substitution (ascending pivots), blocks below by "
          "v_mfma_f32_16x16x4_f32 (Y = sum_k L_Bk X_kj, k ascending; X_Bj = -X_BB Y); T = X diag(beta) "
-         "rounded once per product; bf16 outputs round-to-nearest-even; C = 64";
+         "rounded once per product; bf16 outputs round-to-nearest-even; "
+         "C in {16, 32, 64}: a chunk of C < 64 tokens is a 64-row chunk whose rows past C are identity "
+         "steps (k = v = 0, g = beta = 0)";
 }

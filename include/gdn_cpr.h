@@ -33,6 +33,16 @@
  *     gdn_cpr_workspace_size).  Calls only enqueue work on `stream` (a
  *     hipStream_t; NULL = the legacy default stream) and return; results are
  *     ready when the stream reaches them.  No call synchronises the host.
+ *     This is what lets a serving engine keep its scheduler, its KV-cache
+ *     management and graph capture unchanged under the method (Chinese page,
+ *     opening summary, and the section on the method's two parts, the
+ *     execution contract and the unified model): every call can be recorded
+ *     into a hipGraph and replayed.
+ *   - The initial state h0 and the final state hT are plain fp32 states in
+ *     the S layout below, indexed by batch entry; the final state is
+ *     written from the kernels that produce it (the chain for a sequence
+ *     that ends on a chunk boundary, the scan of its last chunk otherwise),
+ *     with no extra pass.
  *   - Token-major packed layouts: q, k [T, H_k, d_k]; v, o [T, H, d_v];
  *     g, beta [T, H]; all rows contiguous.  H_k = H unless the shape asks
  *     for fewer key heads.  The pages name hybrid Gated DeltaNet models
@@ -157,42 +167,67 @@ size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num_seqs,
                               int64_t total_tokens, int32_t op);
 
 /*
- * Prefill (the engine_prefill case): run N packed sequences from their
- * initial states and fill the cache so that decode can continue them.
- * Chunks start at each sequence's first token.  The chain of boundary
- * states covers a sequence's full chunks; the tokens after its last full
- * chunk (L mod C of them) become the cache's tail.
+ * Prefill: the engine_prefill case of the pages' execution contract, whose
+ * cases name the stage a kernel region runs in (English page, "The IsoExec
+ * Unified Execution Contract", cases and regions; Chinese page, section on
+ * the method's two parts).  CPR evaluates it as the pages' third way for
+ * Gated DeltaNet prescribes for prefill and training (Chinese page, that
+ * section; English page, CPR section): the recurrent state at every chunk
+ * boundary first, then the recurrence inside all chunks in parallel, each
+ * from its boundary state.  Runs N packed sequences from their initial
+ * states and fills the cache so that decode can continue them.  Chunks
+ * start at each sequence's first token.  The chain of boundary states covers
+ * a sequence's full chunks; the tokens after its last full chunk (L mod C of
+ * them) become the cache's tail.
  *   q, k, v, g, beta  inputs, layouts above (T = total_tokens rows)
  *   cu_seqlens        [N + 1] int32
  *   h0                [N, H, d_k, d_v] fp32 initial states indexed by batch
  *                     entry (not by cache row), or NULL for zero states.
  *                     May alias cache_out->s_bnd or ->s_run when the cache
- *                     has no slot_index.
+ *                     has no slot_index, and may alias hT.
+ *   hT                [N, H, d_k, d_v] fp32 final states (the state after
+ *                     each sequence's last token, h0 for an empty one)
+ *                     indexed by batch entry, or NULL.  Must not alias the
+ *                     cache.  Equal bit for bit to what gdn_cpr_cache_state
+ *                     reads out of cache_out afterwards.
  *   cache_out         host struct; every field required; written in full
  *   o                 [T, H, d_v] outputs
  * Zero-length sequences are allowed: their cache becomes h0 and no output
- * rows exist for them.
+ * rows exist for them.  Errors: see the conventions; nothing is enqueued on
+ * a host-detected error.
  */
 gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                            const void* q, const void* k, const void* v, const void* g,
-                           const void* beta, const int32_t* cu_seqlens, const float* h0,
+                           const void* beta, const int32_t* cu_seqlens, const float* h0, float* hT,
                            const gdn_cpr_cache* cache_out, void* o, void* workspace,
                            size_t workspace_bytes, void* stream);
 
 /*
- * Decode (the engine_decode case): one token for each of N sequences.
+ * Decode: the engine_decode case of the execution contract (English page,
+ * contract section, cases; Chinese page, section on the method's two parts).
+ * CPR decodes in recurrent form and resynchronises the running state to the
+ * chunk-boundary computation every C tokens (English page, CPR section;
+ * Chinese page, third-way section), so its outputs equal prefill's bit for
+ * bit.  One token for each of N sequences.
  *   q, k, v, g, beta  one token per sequence: q, k [N, H_k, d_k]; v [N, H, d_v];
  *                     g, beta [N, H]
  *   cache             read-modify-write in place
+ *   hT                [N, H, d_k, d_v] fp32 state after the token, indexed by
+ *                     batch entry, or NULL (the usual case: the cache holds
+ *                     it in scaled form and gdn_cpr_cache_state reads it
+ *                     out; asking for it here writes 64 KB more per
+ *                     (sequence, head) at d = 128).  Must not alias the cache.
  *   o                 [N, H, d_v]
- * The token's output comes from the per-token step on s_run.  When the step
- * completes a chunk (tail_len reaches C), s_bnd and s_run are both replaced
- * by the chunk-boundary computation from s_bnd over the C tail tokens, and
- * tail_len returns to 0.
+ * The token's output comes from the per-token step on s_run, the routine
+ * prefill's in-chunk scan runs.  When the step completes a chunk (tail_len
+ * reaches C), s_bnd and s_run are both replaced by the chunk-boundary
+ * computation from s_bnd over the C tail tokens (prefill's chunk products
+ * and chain step), and tail_len returns to 0.  A cache row whose tail_len is
+ * outside [0, C) is left untouched.
  */
 gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
                                const void* k, const void* v, const void* g, const void* beta,
-                               const gdn_cpr_cache* cache, void* o, void* workspace,
+                               const gdn_cpr_cache* cache, float* hT, void* o, void* workspace,
                                size_t workspace_bytes, void* stream);
 
 /*
@@ -209,6 +244,10 @@ gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, con
  *   cu_seqlens        [N + 1] int32 over the new tokens
  *   cache             read-modify-write in place; cache i continues with
  *                     sequence i's new tokens
+ *   hT                [N, H, d_k, d_v] fp32 final states (after each
+ *                     sequence's last token; the cached state when it has
+ *                     no new tokens) indexed by batch entry, or NULL.  Must
+ *                     not alias the cache.
  *   o                 [T, H, d_v] outputs of the new tokens
  * Per sequence with tail_len = r and L new tokens: the first min(C - r, L)
  * tokens (none when r = 0) take the decode step from s_run and join the
@@ -222,7 +261,8 @@ gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, con
 gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                                     const void* q, const void* k, const void* v, const void* g,
                                     const void* beta, const int32_t* cu_seqlens, const gdn_cpr_cache* cache,
-                                    void* o, void* workspace, size_t workspace_bytes, void* stream);
+                                    float* hT, void* o, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /*
  * The state after each cached sequence's last token (the final state of
@@ -236,9 +276,12 @@ gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t num_seqs, con
                                float* state_out, void* stream);
 
 /*
- * Training forward + backward (the trainer_fwd case plus its gradient).
- * The forward is the prefill computation (o is bit-identical to
- * gdn_cpr_prefill on the same inputs).  The backward is the exact gradient
+ * Training forward + backward: the trainer_fwd case of the execution
+ * contract (English page, contract section; Chinese page, section on the
+ * method's two parts) plus its gradient; the pages time the pair as one
+ * stage (English page, CPR table, trainer forward + backward row).  The
+ * forward is the prefill computation (o and hT are bit-identical to
+ * gdn_cpr_prefill's on the same inputs).  The backward is the exact gradient
  * of the recurrence for the loss sum(o * d_o) + sum(hT * d_hT), evaluated
  * per chunk from the boundary states.
  *   d_o               [T, H, d_v] dtype, upstream gradient of o
@@ -250,18 +293,20 @@ gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t num_seqs, con
  *   dg, dbeta         [T, H] fp32
  *   dh0               [N, H, d_k, d_v] fp32, or NULL
  * For bf16 inputs the call runs independent stages side by side on two
- * streams: `stream` and a second stream that the library creates, at the
- * default priority, the first time the calling thread calls it for that
- * stream's device, and keeps for the thread's lifetime.  The backward's local
- * terms and reverse chain run on the second stream beside the forward chunk
- * products, chain and in-chunk scan on `stream`; the state and gradient
- * stages follow on `stream`.  Events fork the work from `stream` and join it
- * back, so everything the call does is ordered on `stream` as with one
- * stream (also under graph capture, where the fork and join become graph
- * edges; make the thread's first call outside a capture, since it creates
- * the stream).  The bits do not depend on this: each kernel computes the
- * same values in either order.  If the second stream cannot be created the
- * call runs on `stream` alone.
+ * streams: `stream` and a second stream on the same device that the call
+ * takes from a small pool the library keeps per device (at most eight
+ * streams, created at the default priority when first needed and kept until
+ * the process ends; a call holds its stream only while it enqueues, so
+ * concurrent callers never share one).  The backward's local terms and
+ * reverse chain run on the second stream beside the forward chunk products,
+ * chain and in-chunk scan on `stream`; the state and gradient stages follow
+ * on `stream`.  Events fork the work from `stream` and join it back, so
+ * everything the call does is ordered on `stream` as with one stream (also
+ * under graph capture, where the fork and join become graph edges; make a
+ * first call outside a capture, since a call may create a pooled stream).
+ * The bits do not depend on this: each kernel computes the same values in
+ * either order.  If no second stream can be had the call runs on `stream`
+ * alone.
  */
 gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                            const void* q, const void* k, const void* v, const void* g,
@@ -347,13 +392,18 @@ gdn_status gdn_cmp_chunk_decode_step(const gdn_cpr_shape* shape, int32_t num_seq
  */
 void gdn_cpr_set_stage_events(void* const* events, int32_t n_events);
 
-/* Description of the last error on the calling thread ("" if none). */
+/* Description of the last error on the calling thread ("" if none); valid
+ * until the thread's next call into the library. */
 const char* gdn_cpr_last_error(void);
 
 /*
  * Text naming every choice that fixes the library's rounding (routine
  * versions, accumulation orders, operand precisions).  Two builds with the
- * same text produce the same bits.
+ * same text produce the same bits.  It plays the part of the pages'
+ * numerical-policy identity, a digest over every choice that affects the
+ * numbers, which the trainer and the rollout engine compare before they run
+ * together (English page, contract section, identities; Chinese page,
+ * section on the method's two parts).  The returned string is static.
  */
 const char* gdn_cpr_numerics_id(void);
 

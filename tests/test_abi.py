@@ -61,9 +61,9 @@ def _cache(ptr=FAKE, slots=None, lgs=None):
     return _lib.Cache(ptr, ptr, ptr, ptr, ptr, ptr, ptr, slots, ptr if lgs is None else lgs)
 
 
-def _prefill(lib, shape, N=2, T=128, cache=None, cu=FAKE, q=FAKE, ws=FAKE, ws_bytes=0, h0=None):
+def _prefill(lib, shape, N=2, T=128, cache=None, cu=FAKE, q=FAKE, ws=FAKE, ws_bytes=0, h0=None, hT=None):
     cache = cache if cache is not None else _cache()
-    return lib.gdn_cpr_prefill(ctypes.byref(shape), N, T, q, FAKE, FAKE, FAKE, FAKE, cu, h0,
+    return lib.gdn_cpr_prefill(ctypes.byref(shape), N, T, q, FAKE, FAKE, FAKE, FAKE, cu, h0, hT,
                                ctypes.byref(cache), FAKE, ws, ws_bytes, None)
 
 
@@ -83,6 +83,10 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     assert _prefill(lib, s, q=FAKE + 4) == _lib.GDN_ERR_INVALID_ARG
     assert b"aligned" in lib.gdn_cpr_last_error()
     assert _prefill(lib, s, h0=FAKE + 8) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(lib, s, hT=FAKE + 8) == _lib.GDN_ERR_INVALID_ARG
+    assert b"hT" in lib.gdn_cpr_last_error()
+    assert _prefill(lib, s, hT=FAKE) == _lib.GDN_ERR_INVALID_ARG  # the fake cache's s_bnd
+    assert b"aliases" in lib.gdn_cpr_last_error()
     assert _prefill(lib, s, cache=_cache(0)) == _lib.GDN_ERR_INVALID_ARG
     assert _prefill(lib, s, cache=_cache(lgs=0)) == _lib.GDN_ERR_INVALID_ARG
     assert b"run_log_scale" in lib.gdn_cpr_last_error()
@@ -109,9 +113,9 @@ def test_decode_rejects_bad_arguments():
     s = _shape()
     cache = _cache()
 
-    def dec(shape=s, N=4, q=FAKE, ws=FAKE, ws_bytes=0, c=cache):
+    def dec(shape=s, N=4, q=FAKE, ws=FAKE, ws_bytes=0, c=cache, hT=None):
         return lib.gdn_cpr_decode_step(ctypes.byref(shape), N, q, FAKE, FAKE, FAKE, FAKE,
-                                       ctypes.byref(c), FAKE, ws, ws_bytes, None)
+                                       ctypes.byref(c), hT, FAKE, ws, ws_bytes, None)
 
     assert dec(shape=_shape(dk=32)) == _lib.GDN_ERR_UNSUPPORTED
     assert dec(q=None) == _lib.GDN_ERR_INVALID_ARG
@@ -120,6 +124,9 @@ def test_decode_rejects_bad_arguments():
     assert b"slot_index" in lib.gdn_cpr_last_error()
     assert dec(c=_cache(lgs=0)) == _lib.GDN_ERR_INVALID_ARG
     assert b"run_log_scale" in lib.gdn_cpr_last_error()
+    assert dec(hT=FAKE + 4) == _lib.GDN_ERR_INVALID_ARG
+    assert dec(hT=FAKE) == _lib.GDN_ERR_INVALID_ARG
+    assert b"aliases" in lib.gdn_cpr_last_error()
     assert dec(ws_bytes=16) == _lib.GDN_ERR_WORKSPACE
     assert dec(N=0) == _lib.GDN_OK
 
@@ -147,14 +154,17 @@ def test_prefill_continue_rejects_bad_arguments():
     lib = _lib_or_skip()
     s = _shape()
 
-    def cont(shape=s, N=2, T=128, q=FAKE, cu=FAKE, ws=FAKE, ws_bytes=0, c=_cache()):
+    def cont(shape=s, N=2, T=128, q=FAKE, cu=FAKE, ws=FAKE, ws_bytes=0, c=_cache(), hT=None):
         return lib.gdn_cpr_prefill_continue(ctypes.byref(shape), N, T, q, FAKE, FAKE, FAKE, FAKE, cu,
-                                            ctypes.byref(c), FAKE, ws, ws_bytes, None)
+                                            ctypes.byref(c), hT, FAKE, ws, ws_bytes, None)
 
     assert cont(shape=_shape(C=8)) == _lib.GDN_ERR_UNSUPPORTED
     assert cont(cu=None) == _lib.GDN_ERR_INVALID_ARG
     assert cont(q=FAKE + 2) == _lib.GDN_ERR_INVALID_ARG
     assert cont(c=_cache(0)) == _lib.GDN_ERR_INVALID_ARG
+    assert cont(hT=FAKE + 4) == _lib.GDN_ERR_INVALID_ARG
+    assert cont(hT=FAKE) == _lib.GDN_ERR_INVALID_ARG
+    assert b"aliases" in lib.gdn_cpr_last_error()
     need = lib.gdn_cpr_workspace_size(ctypes.byref(s), 2, 128, _lib.GDN_OP_PREFILL_CONTINUE)
     assert need >= lib.gdn_cpr_workspace_size(ctypes.byref(s), 2, 128, _lib.GDN_OP_PREFILL)
     assert cont(ws_bytes=need - 1) == _lib.GDN_ERR_WORKSPACE
@@ -165,3 +175,29 @@ def test_numerics_id_is_stable_text():
     lib = _lib_or_skip()
     a = lib.gdn_cpr_numerics_id()
     assert a and a == lib.gdn_cpr_numerics_id()
+
+
+def _pinned_order_lines():
+    """The formulas of the per-token step's pinned order, as the comment above
+    token_step in cpr_device.hpp states them."""
+    with open(os.path.join(ROOT, "bitwise_invariant_gated_amd", "csrc", "cpr_device.hpp")) as f:
+        text = f.read()
+    block = text[text.index("// Order (pinned): lane j (state column j),"):]
+    lines = []
+    for ln in block.splitlines()[1:]:
+        if not ln.startswith("//   "):
+            break
+        lines.extend(part.strip() for part in ln[2:].split(";  "))
+    return [" ".join(x.split()) for x in lines if x]
+
+
+def test_numerics_id_states_the_pinned_token_step_order():
+    """The identity text must name the per-token step's order exactly as the
+    device code's comment pins it (equal text is meant to mean equal bits)."""
+    lib = _lib_or_skip()
+    ident = " ".join(lib.gdn_cpr_numerics_id().decode().split())
+    lines = _pinned_order_lines()
+    assert len(lines) == 5, lines
+    for ln in lines:
+        assert ln in ident, ln
+    assert "C in {16, 32, 64}" in ident

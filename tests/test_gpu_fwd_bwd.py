@@ -2,9 +2,10 @@
 pinned by autograd and finite differences in test_oracle.py), the forward
 bit-identical to prefill, and reruns bit-identical.
 
-Tolerances per gradient tensor: fp32 inputs max|err| <= 1e-5 * max|ref|
-(relaxed to 1e-4 for dg, a sum over d_k*d_v*T terms); bf16 inputs
-max|err| <= 2e-2 * max(1, max|ref|).
+Tolerances per gradient tensor (the stated reading of the task's bounds for
+gradients): fp32 inputs max|err| <= 1e-5 * max|ref|; bf16 inputs
+max|err| <= 2e-2 * max(1, max|ref|).  Each test prints the measured
+max|err| / max|ref| per tensor.
 """
 
 import numpy as np
@@ -53,7 +54,7 @@ def check_grads(b, out, d_hT):
         m = float(np.max(np.abs(r))) if r.size else 0.0
         err = float(np.max(np.abs(got - r))) if r.size else 0.0
         if b.dtype == "f32":
-            tol = (1e-4 if n == "dg" else 1e-5) * m
+            tol = 1e-5 * m
         else:
             tol = 2e-2 * max(1.0, m)
         errs[n] = (err, tol, m)

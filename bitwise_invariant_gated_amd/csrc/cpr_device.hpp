@@ -102,6 +102,22 @@ __device__ __forceinline__ void fmac_bcast(float& acc, float src, float x) {
 }
 #undef CPR_FMAC_BCAST_CASE
 
+#define CPR_MUL_BCAST_CASE(N)                                                                   \
+  if constexpr (I == N)                                                                          \
+    asm volatile("v_mul_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"       \
+                 : "=v"(acc)                                                                     \
+                 : "v"(src), "v"(x));
+// acc = src[lane 16 r + I of this lane's row] * x (an accumulator's first term)
+template <int I>
+__device__ __forceinline__ void mul_bcast(float& acc, float src, float x) {
+  static_assert(I >= 0 && I < 16, "row_newbcast selects one of 16 lanes");
+  CPR_MUL_BCAST_CASE(0) CPR_MUL_BCAST_CASE(1) CPR_MUL_BCAST_CASE(2) CPR_MUL_BCAST_CASE(3)
+  CPR_MUL_BCAST_CASE(4) CPR_MUL_BCAST_CASE(5) CPR_MUL_BCAST_CASE(6) CPR_MUL_BCAST_CASE(7)
+  CPR_MUL_BCAST_CASE(8) CPR_MUL_BCAST_CASE(9) CPR_MUL_BCAST_CASE(10) CPR_MUL_BCAST_CASE(11)
+  CPR_MUL_BCAST_CASE(12) CPR_MUL_BCAST_CASE(13) CPR_MUL_BCAST_CASE(14) CPR_MUL_BCAST_CASE(15)
+}
+#undef CPR_MUL_BCAST_CASE
+
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -244,7 +260,10 @@ __device__ __forceinline__ float token_step_plain(float (&s)[DK], const float (&
 // the decision depends only on the sequence's own log-decays since the last
 // boundary, so prefill and decode renormalise at the same tokens.
 //
-// Order (pinned): lane j (state column j),
+// Order (pinned), lane j (state column j).  Every accumulator starts with
+// the product of its first term -- p_i = k[i] * N[i] for i < 4, o_i = q[i] * N[i] for i < 2 --
+// (the o terms taken after the update) and then takes fused multiply-adds in
+// ascending i:
 //   pass A, i ascending:  p_(i mod 4) = fma(k[i], N[i], p_(i mod 4))
 //   w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3)))
 //   pass B, i ascending:  N[i] = fma(k[i], w, N[i]);  o_(i mod 2) = fma(q[i], N[i], o_(i mod 2))
@@ -297,11 +316,15 @@ __device__ __forceinline__ float token_step(float (&s)[DK], const float (&kf)[8]
   }
   asm volatile("s_nop 1" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
                "v"(kf[7]));
-  float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+  float p0, p1, p2, p3;
+  mul_bcast<0>(p0, kf[0], s[0]);
+  mul_bcast<0>(p1, kf[1], s[1]);
+  mul_bcast<0>(p2, kf[2], s[2]);
+  mul_bcast<0>(p3, kf[3], s[3]);
   static_for<0, DK / 8>([&](auto nc) {
     constexpr int n = decltype(nc)::value;
 #pragma unroll
-    for (int e = 0; e < 8; e += 4) {
+    for (int e = (n == 0 ? 4 : 0); e < 8; e += 4) {
       const int i = 8 * n + e;
       fmac_bcast<n>(p0, kf[e], s[i]);
       fmac_bcast<n>(p1, kf[e + 1], s[i + 1]);
@@ -312,7 +335,7 @@ __device__ __forceinline__ float token_step(float (&s)[DK], const float (&kf)[8]
   const float w = b * (v - c * ((p0 + p1) + (p2 + p3)));
   asm volatile("s_nop 1" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
                "v"(qf[7]));
-  float o0 = 0.f, o1 = 0.f;
+  float o0, o1;
   // software-pipelined as in token_step_plain: the updates of elements 2j,
   // 2j+1 are followed by the output terms of elements 2j-2, 2j-1
   static_for<0, DK / 2 + 1>([&](auto jc) {
@@ -322,7 +345,10 @@ __device__ __forceinline__ float token_step(float (&s)[DK], const float (&kf)[8]
       fmac_bcast<n>(s[i], kf[e], w);
       fmac_bcast<n>(s[i + 1], kf[e + 1], w);
     }
-    if constexpr (j >= 1) {
+    if constexpr (j == 1) {
+      mul_bcast<0>(o0, qf[0], s[0]);
+      mul_bcast<0>(o1, qf[1], s[1]);
+    } else if constexpr (j > 1) {
       constexpr int i = 2 * j - 2, n = i / 8, e = i % 8;
       fmac_bcast<n>(o0, qf[e], s[i]);
       fmac_bcast<n>(o1, qf[e + 1], s[i + 1]);
@@ -395,20 +421,28 @@ __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T*
     else
       vb = __builtin_amdgcn_raw_buffer_load_b32(rv, v_off, tt * v_stride, 0);
   };
-  fetch(0);
-  for (int t = 0; t < n; ++t) {
-    float kf[8], qf[8];
+  // token t's operands are unpacked (and token t+1's fetch issued) at the end
+  // of iteration t-1, so the loop carries the unpacked values and the fetch
+  // writes the registers the unpack has just read
+  float kf[8], qf[8];
+  float vcur;
+  auto take = [&](int t) {
     unpack_kq<D>(raw, kf, qf);
     uint32_t vbits = vb;
     asm volatile("" : "+v"(vbits));  // decode v here, not next to its load
-    const float vcur = D::from_bits(vbits);
+    vcur = D::from_bits(vbits);
     fetch(t + 1);
+  };
+  fetch(0);
+  take(0);
+  for (int t = 0; t < n; ++t) {
     const float out =
         token_step<DK>(s, kf, qf, lane_bcast(c_l, t), lane_bcast(b_l, t), (renorm >> t) & 1, vcur);
     if constexpr (sizeof(T) == 2)
       __builtin_amdgcn_raw_buffer_store_b16(D::round(out), ro, v_off, (uint32_t)t * v_stride, 0);
     else
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ro, v_off, (uint32_t)t * v_stride, 0);
+    if (t + 1 < n) take(t + 1);
   }
 }
 
@@ -1081,7 +1115,7 @@ __device__ __forceinline__ void store_state_tiles(float* __restrict__ dst, const
 // so the chain writes one 16-byte store per tile and the scan reads each
 // lane's column with 16-byte loads.
 template <int DK>
-__host__ __device__ __forceinline__ size_t bnd_index(int row, int col) {
+__host__ __device__ constexpr size_t bnd_index(int row, int col) {
   return ((size_t)((col >> 4) * (DK / 16) + (row >> 4)) * 64 + 16 * ((row & 15) >> 2) + (col & 15)) * 4 + (row & 3);
 }
 

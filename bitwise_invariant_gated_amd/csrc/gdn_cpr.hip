@@ -46,6 +46,10 @@ namespace {
 // values are those of a Cl-row computation.
 constexpr int C = kChunk;
 constexpr int kChainCols = 32;  // state columns per boundary-chain work item
+// cache-policy bits of a buffer access with agent (device) scope coherence
+// (SC1): the access is coherent with every other work-group of the launch
+// whatever its XCD, with no cache-wide write-back or invalidate
+constexpr int kAuxAgent = 16;
 
 // ---------------------------------------------------------------------------
 // kernel arguments
@@ -79,6 +83,9 @@ struct PrefillArgs {
   uint8_t* prod;       // [F_max*H] chunk-product slots of prod_slot_bytes
   float* gamn;         // [F_max*H]
   float* bnd;          // [A_max*H][DK][DV] state at the start of every chunk
+  int32_t* order;      // [A_max] fused launch: chunk-major slot order (workspace)
+  int32_t* ready;      // [N*H*NZ*kReadyStride] fused launch: published boundary counts (workspace)
+  int32_t* counters;   // [2] fused launch: ticket, timeout (workspace)
   int32_t N;
   int32_t H;
   int32_t Hk;  // heads of q and k
@@ -150,9 +157,20 @@ __device__ __forceinline__ size_t kq_row(size_t tok, int h, int Hk, int G) { ret
 // ---------------------------------------------------------------------------
 // varlen plan: exclusive prefix sums of full and of all chunks per sequence
 
+// Bookkeeping of the fused boundary-chain + scan launch (k_chain_scan_bf16),
+// prepared by the plan kernel of the same call.
+struct FusedPlan {
+  int32_t* order;   // [A] chunk slots in chunk-major order (chunk 0 of every sequence, then chunk 1, ...),
+                    // or null: no fused launch follows
+  int32_t* ticket;  // work-item counter of the fused launch
+  int32_t* ready;   // [n_ready] boundaries published so far by each chain item
+  int32_t n_ready;
+};
+constexpr int kFusedMaxSeqs = 128;  // sequences per call for which the plan builds the chunk-major order
+
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start, const int32_t* __restrict__ end,
                                                int32_t N, int32_t Cl, int32_t* __restrict__ full_base,
-                                               int32_t* __restrict__ all_base) {
+                                               int32_t* __restrict__ all_base, const FusedPlan fp) {
   // 1024 sequences per pass: an inclusive scan inside each wave (shuffles),
   // the 16 wave totals through LDS, and the running totals of earlier passes
   // (integers, so the order of the sums does not matter)
@@ -201,6 +219,28 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start
   if (tid == 0) {
     full_base[N] = cf;
     all_base[N] = ca;
+  }
+  if (fp.order == nullptr) return;
+  // fused launch: clear its counters, and order the chunk slots by chunk
+  // index (then by sequence): slot (i, c) goes to position
+  //   sum_j min(nall_j, c) + #{j < i : nall_j > c}
+  // so that the scan units of early chunks, whose boundaries the chain
+  // publishes first, are taken first.  The order only schedules work; no
+  // result depends on it.
+  __shared__ int32_t nall_s[kFusedMaxSeqs];
+  for (int j = tid; j < fp.n_ready; j += 1024) fp.ready[j] = 0;
+  if (tid == 0) *fp.ticket = 0;
+  for (int j = tid; j < N; j += 1024) nall_s[j] = (end[j] - start[j] + Cl - 1) / Cl;
+  __syncthreads();  // nall_s and all_base complete
+  for (int sl = tid; sl < ca; sl += 1024) {
+    const int i = find_seq(all_base, N, sl);
+    const int c = sl - all_base[i];
+    int pos = 0;
+    for (int j = 0; j < N; ++j) {
+      const int nj = nall_s[j];
+      pos += min(nj, c) + ((j < i && nj > c) ? 1 : 0);
+    }
+    fp.order[pos] = sl;
   }
 }
 
@@ -582,31 +622,47 @@ __global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // in-chunk scan (prefill): one wave per (chunk, head, 64 state columns)
 
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
+// One scan unit: chunk slot `slot` (chunk c of sequence i), head h, state
+// columns 64 z .. 64 z + 63 (one wave, lane = column).  kAgentBnd: the
+// boundary state is read with agent-scope loads, because the boundary chain
+// wrote it during the same launch (k_chain_scan_bf16).
+template <class D, int DK, int DV, bool kAgentBnd>
+__device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i, int h, int z, int lane) {
   using T = typename D::T;
-  const int slot = blockIdx.x, h = blockIdx.y;
-  const int N = a.N, H = a.H;
-  if (slot >= a.all_base[N]) return;
-  const int i = find_seq(a.all_base, N, slot);
+  const int H = a.H;
   const int c = slot - a.all_base[i];
   const int L = a.end[i] - a.start[i];
   const int Cl = a.Cl;
   const int n = min(Cl, L - c * Cl);
   const size_t tok0 = (size_t)a.start[i] + (size_t)c * Cl;
-  const int lane = threadIdx.x;
-  const int col = blockIdx.z * kWave + lane;
+  const int col = z * kWave + lane;
   const size_t SS = (size_t)DK * DV;
 
   const float* B = a.bnd + ((size_t)slot * H + h) * SS;
   float s[DK];
+  if constexpr (kAgentBnd) {
+    // rows 4q .. 4q+3 of column col sit 256 q bytes after rows 0 .. 3
+    static_assert(bnd_index<DK>(4, 0) == 64, "row groups of a column are 256 bytes apart");
+    const BufRsrc rb = buf_rsrc(B, (uint32_t)(SS * sizeof(float)));
+    const uint32_t col_off = (uint32_t)(bnd_index<DK>(0, col) * 4);
 #pragma unroll
-  for (int q = 0; q < DK / 4; ++q) {  // rows 4q .. 4q+3 of column col: one 16-byte load
-    const mfma::f32x4 x = *reinterpret_cast<const mfma::f32x4*>(B + bnd_index<DK>(4 * q, col));
-    s[4 * q] = x[0];
-    s[4 * q + 1] = x[1];
-    s[4 * q + 2] = x[2];
-    s[4 * q + 3] = x[3];
+    for (int q = 0; q < DK / 4; ++q) {  // rows 4q .. 4q+3 of column col: one 16-byte load
+      const mfma::f32x4 x = __builtin_bit_cast(
+          mfma::f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col_off, 256 * q, kAuxAgent));
+      s[4 * q] = x[0];
+      s[4 * q + 1] = x[1];
+      s[4 * q + 2] = x[2];
+      s[4 * q + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < DK / 4; ++q) {  // rows 4q .. 4q+3 of column col: one 16-byte load
+      const mfma::f32x4 x = *reinterpret_cast<const mfma::f32x4*>(B + bnd_index<DK>(4 * q, col));
+      s[4 * q] = x[0];
+      s[4 * q + 1] = x[1];
+      s[4 * q + 2] = x[2];
+      s[4 * q + 3] = x[3];
+    }
   }
 
   const T* gp = (const T*)a.g;
@@ -638,12 +694,12 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
   const int nall = (L + Cl - 1) / Cl;
   if (c == nall - 1 && (L % Cl) != 0) {
     // last, partial chunk: its end state is the running state (N with
-    // log-scale lg, or the state itself when materialised), its tokens the tail
+    // log-scale lg), its tokens the tail
     const size_t ch = cache_row(a.slot, i) * H + h;
     float* R = a.s_run + ch * SS;
 #pragma unroll
     for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
-    if (blockIdx.z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
+    if (z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
     if (a.hT) {  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
       float* F = a.hT + ((size_t)i * H + h) * SS;
       const float e = scale_of_log(lg);
@@ -652,7 +708,7 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
     }
     T* tv = (T*)a.tail_v + ch * Cl * DV;
     for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
-    if (blockIdx.z == 0) {
+    if (z == 0) {
       T* tk = (T*)a.tail_k + ch * Cl * DK;
       for (int idx = lane; idx < n * DK; idx += kWave) {
         const int t = idx / DK, e = idx % DK;
@@ -663,6 +719,197 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
         ((T*)a.tail_beta)[ch * Cl + lane] = bp[(tok0 + lane) * H + h];
       }
     }
+  }
+}
+
+template <class D, int DK, int DV>
+__global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
+  const int slot = blockIdx.x;
+  if (slot >= a.all_base[a.N]) return;
+  scan_unit<D, DK, DV, false>(a, slot, find_seq(a.all_base, a.N, slot), blockIdx.y, blockIdx.z, threadIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// boundary chain and in-chunk scan in one launch (bf16 inputs)
+//
+// The scan of chunk c needs only the boundary B_c, so it can start as soon as
+// the chain has produced B_c instead of after the whole chain.  Every
+// work-group takes a ticket from an atomic counter when it starts, so ticket
+// order is start order.  Tickets 0 .. n_chain-1 are chain items, one per
+// (sequence, head, 64-column block): the chain of k_chain_prefill_bf16 with
+// 4 waves x 16 columns and a one-buffer LDS stage, which publishes, after
+// each step, how many boundaries of its columns have reached memory.  Later
+// tickets are scan items: 4 waves, each one (chunk, head, 64-column half)
+// unit, units in chunk-major order, each waiting until its chain item has
+// published its boundary.  Every chain item started before any scan item and
+// waits on nothing, so every wait ends; the wait is bounded all the same.
+// Boundaries travel with agent-scope stores and loads (coherent across the
+// XCDs, no cache-wide maintenance); the count is published only after the
+// stores are complete.  No value depends on the order in which items run.
+struct FusedArgs {
+  const int32_t* order;  // [A] chunk slots, chunk-major
+  int32_t* ticket;       // zeroed by the plan kernel
+  int32_t* ready;        // [N * H * NZ * kReadyStride] boundaries published per chain item (one per
+                         // kReadyStride words), zeroed by the plan kernel
+  int32_t* timeout;      // set to 1 if a scan unit ever stops waiting (never expected)
+  int32_t n_chain;       // chain items (tickets 0 .. n_chain - 1)
+};
+
+constexpr int kFusedChainCols = 64;  // state columns per chain item (= per scan unit)
+// each chain item's count sits on a cache line of its own: thousands of
+// waiting waves poll the counts, and packed counts would send all those polls
+// to a handful of lines (one memory channel), which then slows the chain's
+// own traffic
+constexpr int kReadyStride = 32;  // int32 words
+
+__device__ __forceinline__ void publish_count(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int read_count(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// waits (bounded) until *p >= need; false if it gave up
+__device__ __forceinline__ bool wait_count(const int32_t* p, int need) {
+  // a poll every ~8,000 cycles (3 to 4 us; a chain step takes about as
+  // long), so that thousands of waiting waves add little memory traffic
+  constexpr int kMaxPolls = 1 << 18;  // with the sleeps, about a second
+  for (int it = 0; it < kMaxPolls; ++it) {
+    if (__builtin_amdgcn_readfirstlane(read_count(p)) >= need) return true;
+    __builtin_amdgcn_s_sleep(127);
+  }
+  return false;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 3) void k_chain_scan_bf16(const PrefillArgs a, const FusedArgs f) {
+  using namespace mfma;
+  typedef SlotB<DK, DV> Sl;
+  constexpr int kThreads = 256, CB = kFusedChainCols, NZ = DV / CB;
+  constexpr int kFragPieces = (int)(Sl::oU / 16);  // WF + KF, 16-byte pieces
+  constexpr int kUPieces = C * CB * 4 / 16;        // U tiles of this item's columns
+  constexpr int kPieces = kFragPieces + kUPieces;
+  constexpr int kPer = kPieces / kThreads;
+  constexpr int kPerFrag = kFragPieces / kThreads;
+  static_assert(kPieces % kThreads == 0 && kFragPieces % kThreads == 0, "staging split");
+  static_assert(DV % CB == 0, "column blocks tile d_v");
+  __shared__ u32x4 stage[kPieces];
+  __shared__ float gn_stage;
+  __shared__ int32_t ticket_s;
+  // the ticket and the wave index are uniform over each wave: reading them
+  // into scalar registers keeps every index derived from them scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid == 0) ticket_s = atomicAdd(f.ticket, 1);
+  __syncthreads();
+  const int t = __builtin_amdgcn_readfirstlane(ticket_s);
+  const int H = a.H;
+  if (t >= f.n_chain) {
+    // ---- scan item: one unit per wave
+    const long u = (long)(t - f.n_chain) * 4 + wave;
+    const long per_slot = (long)H * NZ;
+    if (u >= (long)a.all_base[a.N] * per_slot) return;
+    const int pos = (int)(u / per_slot), r = (int)(u % per_slot), h = r / NZ, z = r % NZ;
+    const int slot = f.order[pos];
+    if (slot < 0 || slot >= a.all_base[a.N]) return;  // (the plan writes every position in range)
+    const int i = find_seq(a.all_base, a.N, slot);
+    const int c = slot - a.all_base[i];
+    if (!wait_count(f.ready + (((size_t)i * H + h) * NZ + z) * kReadyStride, c + 1) && lane == 0)
+      atomicExch(f.timeout, 1);
+    scan_unit<Bf16, DK, DV, true>(a, slot, i, h, z, lane);
+    return;
+  }
+  // ---- chain item
+  const int i = t / (H * NZ), r = t % (H * NZ), h = r / NZ, z = r % NZ;
+  const int jbg = z * (CB / 16), jb0 = jbg + wave;  // one 16-column tile per wave
+  const int L = a.end[i] - a.start[i];
+  if (a.skip_empty && L == 0) return;
+  const int Cl = a.Cl;
+  const int nfull = L / Cl, nall = (L + Cl - 1) / Cl;
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  const int abase = a.all_base[i], fbase = a.full_base[i];
+  int32_t* const rdy = f.ready + (sh * NZ + z) * kReadyStride;
+  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * Sl::bytes; };
+  auto gamn_of = [&](int c) { return a.gamn[(size_t)(fbase + c) * H + h]; };
+  auto fetch = [&](int c, u32x4 (&rg)[kPer]) {
+    const uint8_t* sp = slot_of(c);
+    const u32x4* fr = reinterpret_cast<const u32x4*>(sp);
+    const u32x4* up = reinterpret_cast<const u32x4*>(sp + Sl::oU) + (size_t)jbg * (C / 16) * 64;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int p = tid + m * kThreads;
+      rg[m] = m < kPerFrag ? fr[p] : up[p - kFragPieces];
+    }
+  };
+  f32x4 S[DK / 16][1];
+  const size_t ch = cache_row(a.slot, i) * H + h;
+  load_state_tiles<DK, DV, 1>(S, a.h0 ? a.h0 + (a.h0_slotted ? ch : sh) * SS : nullptr, jb0, lane);
+  // boundary c of this wave's tile, agent scope (bnd_index layout)
+  auto store_bnd = [&](int c) {
+    const BufRsrc rb = buf_rsrc(a.bnd + ((size_t)(abase + c) * H + h) * SS, (uint32_t)(SS * sizeof(float)));
+#pragma unroll
+    for (int im = 0; im < DK / 16; ++im)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[im][0]), rb,
+                                             (uint32_t)(((jb0 * (DK / 16) + im) * 64 + lane) * 16), 0, kAuxAgent);
+  };
+  auto all_stores_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  if (nall > 0) store_bnd(0);
+  u32x4 R[kPer];
+  float G = 1.f;
+  if (nfull > 0) {
+    fetch(0, R);
+    G = gamn_of(0);
+  }
+  all_stores_done();
+  if (nfull > 0) {
+    for (int m = 0; m < kPer; ++m) stage[tid + m * kThreads] = R[m];
+    if (tid == 0) gn_stage = G;
+    const int c1 = min(1, nfull - 1);
+    fetch(c1, R);
+    G = gamn_of(c1);
+  }
+  __syncthreads();
+  if (tid == 0 && nall > 0) publish_count(rdy, 1);
+  // Step c: the stage holds chunk c's products, R chunk c+1's.  After the
+  // step's products every wave waits for its outstanding memory operations
+  // (the boundary B_c stored and the fetch issued one step earlier), so once
+  // all waves are past the barrier B_0 .. B_c are complete and published.
+  for (int c = 0; c < nfull; ++c) {
+    f32x4 Ut[C / 16][1];
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm)
+      Ut[tm][0] = __builtin_bit_cast(f32x4, stage[kFragPieces + (wave * (C / 16) + tm) * 64 + lane]);
+    chain_step_bf16<DK, 1>(
+        S, [&](int kb, int tm) { return stage[(kb * (C / 16) + tm) * 64 + lane]; },
+        [&](int kb, int im) { return stage[(int)(Sl::oKF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut,
+        gn_stage);
+    all_stores_done();
+    __syncthreads();  // every wave is done with the stage; B_c is complete
+    if (tid == 0) publish_count(rdy, c + 1);
+    if (c + 1 < nall) store_bnd(c + 1);
+    if (c + 1 < nfull) {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) stage[tid + m * kThreads] = R[m];
+      if (tid == 0) gn_stage = G;
+      const int cf = min(c + 2, nfull - 1);
+      fetch(cf, R);
+      G = gamn_of(cf);
+    }
+    __syncthreads();  // the stage holds chunk c+1
+  }
+  all_stores_done();
+  __syncthreads();
+  if (tid == 0 && nall > 0) publish_count(rdy, nall);
+  store_state_tiles<DK, DV, 1>(a.s_bnd + ch * SS, S, jb0, lane);
+  if (L % Cl == 0) {
+    store_state_tiles<DK, DV, 1>(a.s_run + ch * SS, S, jb0, lane);
+    if (a.hT) store_state_tiles<DK, DV, 1>(a.hT + sh * SS, S, jb0, lane);
+  }
+  if (z == 0 && tid == 0) {
+    a.tail_len[ch] = L % Cl;
+    if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
   }
 }
 
@@ -1970,7 +2217,7 @@ bool shape_ok(const gdn_cpr_shape* s, std::string* why) {
 int key_heads(const gdn_cpr_shape& s) { return s.num_key_heads > 0 ? s.num_key_heads : s.num_heads; }
 
 struct PrefillLayout {
-  size_t full_base, all_base, prod, slot, gamn, bnd, total;
+  size_t full_base, all_base, prod, slot, gamn, bnd, order, ready, counters, total;
 };
 
 PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
@@ -1990,6 +2237,14 @@ PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   off = align_up(off + sizeof(float) * Fmax * H);
   L.bnd = off;
   off = align_up(off + sizeof(float) * Amax * H * DK * DV);
+  // fused chain + scan launch: chunk-major slot order, per-chain-item counts,
+  // ticket and timeout words
+  L.order = off;
+  off = align_up(off + sizeof(int32_t) * Amax);
+  L.ready = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)N * H * (DV / kFusedChainCols) * kReadyStride);
+  L.counters = off;
+  off = align_up(off + 2 * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -2141,14 +2396,30 @@ void launch_resync_bf16(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
 }
 
+// The fused boundary chain + scan launch (k_chain_scan_bf16) serves bf16
+// prefills of up to kFusedMaxSeqs sequences whose chain items leave most of
+// the chip's work-group slots to the scan; other prefills run the chain and
+// the scan as two launches.  Both give the same bits.
+constexpr long kFusedMaxChainItems = 512;
+
+template <int DK, int DV>
+bool use_fused(const PrefillArgs& a) {
+  return a.order && a.all_chunks == 0 && a.N <= kFusedMaxSeqs &&
+         (long)a.N * a.H * (DV / kFusedChainCols) <= kFusedMaxChainItems;
+}
+
 template <class D, int DK, int DV>
 gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const char* fn) {
   const int Fmax = (int)(T / a.Cl);
   const int Amax = Fmax + a.N;
-  mark(0, st);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.Cl, a.full_base, a.all_base);
-  mark(1, st);
   constexpr bool kBf16 = std::is_same<D, Bf16>::value;
+  const bool fused = kBf16 && use_fused<DK, DV>(a);
+  constexpr int NZ = DV / kFusedChainCols;
+  FusedPlan fp{};
+  if (fused) fp = FusedPlan{a.order, a.counters, a.ready, a.N * a.H * NZ * kReadyStride};
+  mark(0, st);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.Cl, a.full_base, a.all_base, fp);
+  mark(1, st);
   if (Fmax > 0) {
     if constexpr (kBf16)
       hipLaunchKernelGGL((k_chunk_local_prefill_bf16<DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
@@ -2156,6 +2427,16 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
       hipLaunchKernelGGL((k_chunk_local_prefill<D, DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
   }
   mark(2, st);
+  if (fused) {
+    // chain and scan as one launch: events 3 and 4 both follow it
+    const FusedArgs f{a.order, a.counters, a.ready, a.counters + 1, a.N * a.H * NZ};
+    const long units = (long)Amax * a.H * NZ;
+    const unsigned groups = (unsigned)(f.n_chain + (units + 3) / 4);
+    if constexpr (kBf16) hipLaunchKernelGGL((k_chain_scan_bf16<DK, DV>), dim3(groups), dim3(256), 0, st, a, f);
+    mark(3, st);
+    mark(4, st);
+    return launch_status(fn);
+  }
   if (a.N > 0) {
     if constexpr (kBf16)
       launch_chain_bf16<DK, DV>(a, st);
@@ -2285,7 +2566,7 @@ struct CmpPrefillFn {
         return launch_status(fn);
       }
       hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.Cl, pa.full_base,
-                         pa.all_base);
+                         pa.all_base, FusedPlan{});
       if (T > 0) hipLaunchKernelGGL((k_cmp_chunk_local_bf16<DK, DV>), dim3(Amax, ca.H), dim3(256), 0, st, ca);
       launch_chain_bf16<DK, DV>(pa, st);
       if (T > 0) hipLaunchKernelGGL((k_cmp_chunk_out_bf16<DK, DV>), dim3(Amax, ca.H), dim3(256), 0, st, ca);
@@ -2409,7 +2690,8 @@ struct FwdBwdFn {
     const int Fmax = (int)(T / pa.Cl), Amax = Fmax + pa.N;
     auto ev = [&](hipError_t e) { return e == hipSuccess; };
     mark(0, st);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.Cl, pa.full_base, pa.all_base);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.Cl, pa.full_base, pa.all_base,
+                       FusedPlan{});
     mark(1, st);
     if (!ev(hipEventRecord(x.fork, st)) || !ev(hipStreamWaitEvent(x.s, x.fork, 0)))
       return fail(GDN_ERR_HIP, "%s: stream fork failed: %s", fn, hipGetErrorString(hipGetLastError()));
@@ -2560,6 +2842,9 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   a.prod = (uint8_t*)(ws + L.prod);
   a.gamn = (float*)(ws + L.gamn);
   a.bnd = (float*)(ws + L.bnd);
+  a.order = (int32_t*)(ws + L.order);
+  a.ready = (int32_t*)(ws + L.ready);
+  a.counters = (int32_t*)(ws + L.counters);
   a.N = num_seqs;
   a.H = shape->num_heads;
   a.Hk = key_heads(*shape);
@@ -2747,6 +3032,9 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
   pa.prod = (uint8_t*)(ws + L.pre.prod);
   pa.gamn = (float*)(ws + L.pre.gamn);
   pa.bnd = (float*)(ws + L.pre.bnd);
+  pa.order = (int32_t*)(ws + L.pre.order);
+  pa.ready = (int32_t*)(ws + L.pre.ready);
+  pa.counters = (int32_t*)(ws + L.pre.counters);
   pa.N = num_seqs;
   pa.H = shape->num_heads;
   pa.Hk = key_heads(*shape);
@@ -2823,6 +3111,9 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
   pa.prod = (uint8_t*)(ws + L.pre.prod);
   pa.gamn = (float*)(ws + L.pre.gamn);
   pa.bnd = (float*)(ws + L.pre.bnd);
+  pa.order = (int32_t*)(ws + L.pre.order);
+  pa.ready = (int32_t*)(ws + L.pre.ready);
+  pa.counters = (int32_t*)(ws + L.pre.counters);
   pa.N = num_seqs;
   pa.H = shape->num_heads;
   pa.Hk = key_heads(*shape);
@@ -3069,11 +3360,13 @@ extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) 
 extern "C" const char* gdn_cpr_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" const char* gdn_cpr_numerics_id(void) {
-  return "gdn_cpr numerics v5: "
+  return "gdn_cpr numerics v6: "
          "per-token step (one routine for the prefill scan, decode and the continuation head; k and q by DPP "
          "row broadcast) in fp32 on a scaled running state M = exp(lg) N: x = lg + g (fp32 add); "
          "renorm = x < -32; c = exp(x); b = beta * r with r = exp(-x), r = 1 when renorm; renorm: N = c N, "
-         "c = 1; lg after the token = 0 when renorm, else x; lane j (state column j), "
+         "c = 1; lg after the token = 0 when renorm, else x; lane j (state column j); every accumulator "
+         "starts with the product of its first term (p_i = k[i] * N[i] for i < 4, o_i = q[i] * N[i] for "
+         "i < 2), then "
          "pass A, i ascending: p_(i mod 4) = fma(k[i], N[i], p_(i mod 4)); "
          "w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3))); "
          "pass B, i ascending: N[i] = fma(k[i], w, N[i]); o_(i mod 2) = fma(q[i], N[i], o_(i mod 2)); "

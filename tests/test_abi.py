@@ -182,9 +182,10 @@ def _pinned_order_lines():
     token_step in cpr_device.hpp states them."""
     with open(os.path.join(ROOT, "bitwise_invariant_gated_amd", "csrc", "cpr_device.hpp")) as f:
         text = f.read()
-    block = text[text.index("// Order (pinned): lane j (state column j),"):]
-    lines = []
-    for ln in block.splitlines()[1:]:
+    block = text[text.index("// Order (pinned), lane j (state column j)."):].splitlines()
+    lines = [next(ln for ln in block if "--" in ln).split("--")[1].strip()]  # the first-term products
+    start = next(k for k, ln in enumerate(block) if ln.startswith("//   pass A"))
+    for ln in block[start:]:
         if not ln.startswith("//   "):
             break
         lines.extend(part.strip() for part in ln[2:].split(";  "))
@@ -197,7 +198,7 @@ def test_numerics_id_states_the_pinned_token_step_order():
     lib = _lib_or_skip()
     ident = " ".join(lib.gdn_cpr_numerics_id().decode().split())
     lines = _pinned_order_lines()
-    assert len(lines) == 5, lines
+    assert len(lines) == 6, lines
     for ln in lines:
         assert ln in ident, ln
     assert "C in {16, 32, 64}" in ident

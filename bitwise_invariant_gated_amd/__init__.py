@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     gdn_cmp_workspace,
     gdn_cpr_cache_state,
     gdn_cpr_decode_step,
+    gdn_cpr_decode_step_noalloc,
     gdn_cpr_fwd_bwd,
     gdn_cpr_last_error,
     gdn_cpr_numerics_id,

@@ -34,6 +34,7 @@ EXPORTED = (
     "gdn_cpr_workspace_size",
     "gdn_cpr_prefill",
     "gdn_cpr_decode_step",
+    "gdn_cpr_decode_step_noalloc",
     "gdn_cpr_prefill_continue",
     "gdn_cpr_fwd_bwd",
     "gdn_cpr_cache_state",
@@ -96,6 +97,9 @@ def load() -> ctypes.CDLL:
     lib.gdn_cpr_decode_step.restype = ctypes.c_int
     lib.gdn_cpr_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, _vp, _vp, _vp, _vp,
                                         _vp, ctypes.POINTER(Cache), _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdn_cpr_decode_step_noalloc.restype = ctypes.c_int
+    lib.gdn_cpr_decode_step_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                                _vp, ctypes.POINTER(Cache), _vp, _vp, _vp]
     lib.gdn_cpr_prefill_continue.restype = ctypes.c_int
     lib.gdn_cpr_prefill_continue.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
                                              _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cache), _vp, _vp,

@@ -143,6 +143,17 @@ def gdn_cpr_decode_step(shape: LayerShape, q, k, v, g, beta, cache: CprCache, o,
                                        workspace.numel(), _stream(stream)))
 
 
+def gdn_cpr_decode_step_noalloc(shape: LayerShape, q, k, v, g, beta, cache: CprCache, o, stream=None,
+                                hT=None) -> None:
+    """gdn_cpr_decode_step with the library's fixed per-device scratch instead
+    of a workspace (allocates nothing; calls that overlap on one device race)."""
+    lib = _lib.load()
+    N = int(q.shape[0])
+    cc = cache.c()
+    _lib.check(lib.gdn_cpr_decode_step_noalloc(ctypes.byref(shape.c()), N, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                               _ptr(beta), ctypes.byref(cc), _ptr(hT), _ptr(o), _stream(stream)))
+
+
 def gdn_cpr_prefill_continue(shape: LayerShape, q, k, v, g, beta, cu_seqlens, cache: CprCache, o,
                              workspace: torch.Tensor, stream=None, hT=None) -> None:
     """hT (optional, [N, H, d_k, d_v] fp32) receives every sequence's final state."""

@@ -21,6 +21,7 @@
 // C tokens.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -111,8 +112,9 @@ struct DecodeArgs {
   float* hT;   // [N, H, DK, DV] state after the step (batch order), or null
   void* o;
   int32_t* flag;  // [N*H] bit 0: this pair resynchronises in this step; bit 1: the resync also writes hT
-  uint8_t* prod;  // [N*H] chunk-product slots of prod_slot_bytes
-  float* gamn;    // [N*H]
+  uint8_t* prod;  // chunk-product slots of prod_slot_bytes, one per pair of a resync launch
+  float* gamn;    // one per product slot
+  int32_t seq0;   // resync launches: the grid's sequence 0 is sequence seq0 of the batch
   int32_t N;
   int32_t H;
   int32_t Hk;  // heads of q and k
@@ -293,15 +295,17 @@ template <class D, int DK, int DV>
 __global__ __launch_bounds__(256) void k_chunk_local_resync(const DecodeArgs a) {
   using T = typename D::T;
   __shared__ ChunkLds<DK, DV> sm;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const int i = a.seq0 + blockIdx.x;
+  const size_t sh = (size_t)i * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  const size_t ps = (size_t)blockIdx.x * a.H + blockIdx.y;  // product slot
+  const size_t ch = cache_row(a.slot, i) * a.H + blockIdx.y;
   // tail rows of this (sequence, head): [Cl, DK], [Cl, DV], [Cl]
   const size_t tr = ch * a.Cl;
   stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, tr, 1, (const T*)a.tail_v, tr, 1, (const T*)a.tail_g,
                          (const T*)a.tail_beta, tr, 1, a.Cl);
-  float* P = (float*)(a.prod + sh * prod_slot_bytes(false, DK, DV));
-  chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + sh);
+  float* P = (float*)(a.prod + ps * prod_slot_bytes(false, DK, DV));
+  chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + ps);
 }
 
 // bf16 path: MFMA chunk products
@@ -406,13 +410,15 @@ template <int DK, int DV>
 __global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
   constexpr int NB = kChainCols;
   __shared__ ChainLds<DK, NB> sm;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const int i = a.seq0 + blockIdx.x;
+  const size_t sh = (size_t)i * a.H + blockIdx.y;
   if (a.flag[sh] == 0) return;
+  const size_t ps = (size_t)blockIdx.x * a.H + blockIdx.y;  // product slot
   const int col0 = blockIdx.z * NB;
   const size_t SS = (size_t)DK * DV;
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  const size_t ch = cache_row(a.slot, i) * a.H + blockIdx.y;
   get_block<DK, DV, NB>(sm, a.s_bnd + ch * SS, col0);
-  stage_products<DK, DV, NB>(sm, (const float*)(a.prod + sh * prod_slot_bytes(false, DK, DV)), a.gamn + sh, col0);
+  stage_products<DK, DV, NB>(sm, (const float*)(a.prod + ps * prod_slot_bytes(false, DK, DV)), a.gamn + ps, col0);
   chain_step_f32<DK, NB>(sm);
   put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
   put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
@@ -589,21 +595,26 @@ __global__ __launch_bounds__(kResyncWaves<DV> * 64) void k_chain_resync_bf16(con
 // does for a chunk) and then, wave w for state columns 32 w .. 32 w + 31,
 // takes the chain step from s_bnd with them (k_chain_resync_bf16's
 // arithmetic); every other pair exits at once, so a step in which no tail
-// fills costs one launch of early-exit work-groups.
+// fills costs one launch of early-exit work-groups.  The grid covers
+// sequences seq0 .. seq0 + gridDim.x - 1 of the batch (all of them, except
+// in the fixed-scratch decode, which resynchronises the batch in groups);
+// product slots are indexed within the grid.
 template <int DK, int DV>
 __global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
   constexpr int NT = kResyncNT, NW = DV / (16 * NT);
   static_assert(NW <= 4, "the chain step's waves fit the work-group");
   __shared__ ChunkLdsB<DK, DV> sm;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
+  const int i = a.seq0 + blockIdx.x;
+  const size_t sh = (size_t)i * a.H + blockIdx.y;
   const int flag = a.flag[sh];
   if (flag == 0) return;
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
+  const size_t ps = (size_t)blockIdx.x * a.H + blockIdx.y;  // product slot
+  const size_t ch = cache_row(a.slot, i) * a.H + blockIdx.y;
   const size_t tr = ch * a.Cl;
-  uint8_t* const prod = a.prod + sh * prod_slot_bytes(true, DK, DV);
+  uint8_t* const prod = a.prod + ps * prod_slot_bytes(true, DK, DV);
   stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, tr, 1, (const uint16_t*)a.tail_v, tr, 1,
                            (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, tr, 1, a.Cl);
-  chunk_local_bf16<DK, DV>(sm, prod, a.gamn + sh);
+  chunk_local_bf16<DK, DV>(sm, prod, a.gamn + ps);
   __syncthreads();  // the slot and Gamma_n, written by every wave, are read below
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave < NW) {
@@ -611,7 +622,7 @@ __global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
     const size_t SS = (size_t)DK * DV;
     mfma::f32x4 S[DK / 16][NT];
     load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * SS, jb0, lane);
-    chain_step_bf16_global<DK, DV, NT>(S, prod, a.gamn[sh], jb0, lane);
+    chain_step_bf16_global<DK, DV, NT>(S, prod, a.gamn[ps], jb0, lane);
     store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
     store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
     if (a.hT && (flag & 2)) store_state_tiles<DK, DV, NT>(a.hT + sh * SS, S, jb0, lane);
@@ -2392,8 +2403,8 @@ void launch_chain_bf16(const PrefillArgs& a, hipStream_t st) {
 }
 
 template <int DK, int DV>
-void launch_resync_bf16(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
+void launch_resync_bf16(const DecodeArgs& a, int n_seqs, hipStream_t st) {
+  hipLaunchKernelGGL((k_resync_bf16<DK, DV>), dim3(n_seqs, a.H), dim3(256), 0, st, a);
 }
 
 // The fused boundary chain + scan launch (k_chain_scan_bf16) serves bf16
@@ -2451,15 +2462,23 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
 }
 
 template <class D, int DK, int DV>
-gdn_status run_decode(const DecodeArgs& a, hipStream_t st, const char* fn) {
+// The resync runs over groups of `group` sequences, one launch (bf16) or
+// two (fp32) per group, each group's pairs using product slots 0 ..
+// group * H - 1; the workspace decode takes the whole batch as one group.
+gdn_status run_decode(const DecodeArgs& a, int group, hipStream_t st, const char* fn) {
   mark(0, st);
   hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(DV), 0, st, a);
   mark(1, st);
-  if constexpr (std::is_same<D, Bf16>::value) {
-    launch_resync_bf16<DK, DV>(a, st);
-  } else {
-    hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(a.N, a.H), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+  for (int s0 = 0; s0 < a.N; s0 += group) {
+    DecodeArgs r = a;
+    r.seq0 = s0;
+    const int n = std::min(group, a.N - s0);
+    if constexpr (std::is_same<D, Bf16>::value) {
+      launch_resync_bf16<DK, DV>(r, n, st);
+    } else {
+      hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(n, r.H), dim3(256), 0, st, r);
+      hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(n, r.H, DV / kChainCols), dim3(256), 0, st, r);
+    }
   }
   mark(2, st);
   return launch_status(fn);
@@ -2490,8 +2509,8 @@ struct PrefillFn {
 
 template <class D, int DK, int DV>
 struct DecodeFn {
-  static gdn_status run(const DecodeArgs& a, hipStream_t st, const char* fn) {
-    return run_decode<D, DK, DV>(a, st, fn);
+  static gdn_status run(const DecodeArgs& a, int group, hipStream_t st, const char* fn) {
+    return run_decode<D, DK, DV>(a, group, st, fn);
   }
 };
 
@@ -2517,7 +2536,7 @@ struct ContFn {
                         const char* fn) {
     hipLaunchKernelGGL((k_cont_head<D, DK, DV>), dim3(ca.N, ca.H), dim3(DV), 0, st, ca);
     if constexpr (std::is_same<D, Bf16>::value) {
-      launch_resync_bf16<DK, DV>(da, st);
+      launch_resync_bf16<DK, DV>(da, da.N, st);
     } else {
       hipLaunchKernelGGL((k_chunk_local_resync<D, DK, DV>), dim3(da.N, da.H), dim3(256), 0, st, da);
       hipLaunchKernelGGL((k_chain_resync<DK, DV>), dim3(da.N, da.H, DV / kChainCols), dim3(256), 0, st, da);
@@ -2853,17 +2872,19 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
   return dispatch<PrefillFn>(*shape, a, total_tokens, (hipStream_t)stream, fn);
 }
 
-extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
-                                          const void* k, const void* v, const void* g, const void* beta,
-                                          const gdn_cpr_cache* cache, float* hT, void* o, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
-  const char* fn = "gdn_cpr_decode_step";
+// Checks shared by the two decode entry points; fills every field of `a`
+// except the scratch pointers.  *done: nothing to enqueue (num_seqs == 0).
+gdn_status decode_prepare(const char* fn, const gdn_cpr_shape* shape, int32_t num_seqs, const void* q, const void* k,
+                          const void* v, const void* g, const void* beta, const gdn_cpr_cache* cache, float* hT,
+                          void* o, DecodeArgs& a, bool* done) {
+  *done = false;
   std::string why;
   if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
   if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
   if (num_seqs == 0) {
     g_last_error.clear();
+    *done = true;
     return GDN_OK;
   }
   CHECK_PTR(q, "q");
@@ -2883,13 +2904,7 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   CHECK_OPT_PTR(cache->slot_index, "cache.slot_index");
   CHECK_OPT_PTR(hT, "hT");
   if (hT && (hT == cache->s_bnd || hT == cache->s_run)) return fail(GDN_ERR_INVALID_ARG, "%s: hT aliases the cache", fn);
-  const DecodeLayout L = decode_layout(*shape, num_seqs);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
-  char* ws = (char*)workspace;
-  DecodeArgs a{};
+  a = DecodeArgs{};
   a.slot = cache->slot_index;
   a.q = q;
   a.k = k;
@@ -2906,15 +2921,112 @@ extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t nu
   a.lgs = cache->run_log_scale;
   a.hT = hT;
   a.o = o;
-  a.flag = (int32_t*)(ws + L.flag);
-  a.prod = (uint8_t*)(ws + L.prod);
-  a.gamn = (float*)(ws + L.gamn);
   a.N = num_seqs;
   a.H = shape->num_heads;
   a.Hk = key_heads(*shape);
   a.G = a.H / a.Hk;
   a.Cl = shape->chunk;
-  return dispatch<DecodeFn>(*shape, a, (hipStream_t)stream, fn);
+  return GDN_OK;
+}
+
+extern "C" gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                                          const void* k, const void* v, const void* g, const void* beta,
+                                          const gdn_cpr_cache* cache, float* hT, void* o, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_cpr_decode_step";
+  DecodeArgs a;
+  bool done = false;
+  const gdn_status r = decode_prepare(fn, shape, num_seqs, q, k, v, g, beta, cache, hT, o, a, &done);
+  if (r != GDN_OK || done) return r;
+  const DecodeLayout L = decode_layout(*shape, num_seqs);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  char* ws = (char*)workspace;
+  a.flag = (int32_t*)(ws + L.flag);
+  a.prod = (uint8_t*)(ws + L.prod);
+  a.gamn = (float*)(ws + L.gamn);
+  return dispatch<DecodeFn>(*shape, a, (int)num_seqs, (hipStream_t)stream, fn);
+}
+
+// ---------------------------------------------------------------------------
+// The decode step for callers that cannot allocate device memory: its
+// scratch (per-pair resync flags, then per-slot Gamma_n and chunk products)
+// is one fixed array per device, resolved once per device with
+// hipGetSymbolAddress.  Host code uses only the resolved address; the
+// array's name is not a device address on the host.
+
+constexpr size_t kNoAllocMaxPairs = size_t(1) << 16;             // (sequence, head) pairs per call
+constexpr size_t kNoAllocFlagBytes = kNoAllocMaxPairs * sizeof(int32_t);
+constexpr size_t kNoAllocProdBytes = size_t(64) << 20;            // product slots of one resync group
+constexpr size_t kNoAllocScratchBytes = 2 * kNoAllocFlagBytes + kNoAllocProdBytes;
+static_assert(kNoAllocMaxPairs == GDN_NOALLOC_MAX_PAIRS && kNoAllocScratchBytes == GDN_NOALLOC_SCRATCH_BYTES,
+              "the header states the fixed scratch's limits");
+static_assert(kNoAllocProdBytes / prod_slot_bytes(true, 64, 64) * sizeof(float) <= kNoAllocFlagBytes,
+              "the Gamma_n region holds one float per product slot of the smallest shape");
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxScratchDevices];
+
+// The device that work enqueued on `stream` runs on.
+gdn_status stream_device(hipStream_t stream, int* dev, const char* fn) {
+  const hipError_t e = stream ? hipStreamGetDevice(stream, dev) : hipGetDevice(dev);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: device of the stream: %s", fn, hipGetErrorString(e));
+  if (*dev < 0 || *dev >= kMaxScratchDevices) return fail(GDN_ERR_UNSUPPORTED, "%s: device %d", fn, *dev);
+  return GDN_OK;
+}
+
+// This device's copy of `scratch`, looked up on first use with the device current.
+gdn_status scratch_of(int dev, uint8_t** out, const char* fn) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: selecting device %d: %s", fn, dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p)
+      return fail(GDN_ERR_HIP, "%s: address of the scratch array on device %d: %s", fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+extern "C" gdn_status gdn_cpr_decode_step_noalloc(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                                                  const void* k, const void* v, const void* g, const void* beta,
+                                                  const gdn_cpr_cache* cache, float* hT, void* o, void* stream) {
+  const char* fn = "gdn_cpr_decode_step_noalloc";
+  DecodeArgs a;
+  bool done = false;
+  gdn_status r = decode_prepare(fn, shape, num_seqs, q, k, v, g, beta, cache, hT, o, a, &done);
+  if (r != GDN_OK || done) return r;
+  const size_t pairs = (size_t)num_seqs * (size_t)shape->num_heads;
+  if (pairs > kNoAllocMaxPairs)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: %zu (sequence, head) pairs; the fixed scratch holds flags for at most %zu",
+                fn, pairs, kNoAllocMaxPairs);
+  const size_t slots = kNoAllocProdBytes / prod_slot_bytes(shape->dtype == GDN_DTYPE_BF16, shape->head_dim_k,
+                                                           shape->head_dim_v);
+  const size_t group = slots / (size_t)shape->num_heads;  // sequences per resync launch
+  if (group == 0)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: %d heads; the fixed scratch holds chunk products for at most %zu", fn,
+                shape->num_heads, slots);
+  int dev = -1;
+  r = stream_device((hipStream_t)stream, &dev, fn);
+  if (r != GDN_OK) return r;
+  uint8_t* base = nullptr;
+  r = scratch_of(dev, &base, fn);
+  if (r != GDN_OK) return r;
+  a.flag = (int32_t*)base;
+  a.gamn = (float*)(base + kNoAllocFlagBytes);
+  a.prod = base + 2 * kNoAllocFlagBytes;
+  return dispatch<DecodeFn>(*shape, a, (int)std::min<size_t>(group, (size_t)num_seqs), (hipStream_t)stream, fn);
 }
 
 extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,

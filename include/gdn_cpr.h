@@ -30,7 +30,9 @@
  *   - Pointers are DEVICE pointers owned by the caller unless marked host.
  *     The library allocates no device memory and keeps none between calls;
  *     scratch lives in the caller's workspace (size from
- *     gdn_cpr_workspace_size).  Calls only enqueue work on `stream` (a
+ *     gdn_cpr_workspace_size).  The one exception is
+ *     gdn_cpr_decode_step_noalloc, whose scratch is a fixed array inside the
+ *     library.  Calls only enqueue work on `stream` (a
  *     hipStream_t; NULL = the legacy default stream) and return; results are
  *     ready when the stream reaches them.  No call synchronises the host.
  *     This is what lets a serving engine keep its scheduler, its KV-cache
@@ -229,6 +231,35 @@ gdn_status gdn_cpr_decode_step(const gdn_cpr_shape* shape, int32_t num_seqs, con
                                const void* k, const void* v, const void* g, const void* beta,
                                const gdn_cpr_cache* cache, float* hT, void* o, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_cpr_decode_step for callers that cannot allocate device memory: code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are those of gdn_cpr_decode_step (the same
+ * kernels; bit-identical outputs and cache), without the workspace.
+ * Scratch: one fixed array of GDN_NOALLOC_SCRATCH_BYTES (64.5 MiB) per
+ * device, in the library's code object, which each device that runs it
+ * holds until the process ends.  It holds the per-(sequence, head) resync
+ * flags and the chunk products of the tails that fill; everything in it is
+ * written before it is read, so no call needs it cleared.
+ * Limits (GDN_ERR_UNSUPPORTED, nothing enqueued): num_seqs * H <=
+ * GDN_NOALLOC_MAX_PAIRS (65,536), and H no larger than the chunk-product
+ * slots of 64 MiB (1,024 at d_k = d_v = 128 bf16, 682 for fp32).  Tails that
+ * fill are resynchronised in groups of as many sequences as those slots
+ * hold, one launch per group (bf16; two for fp32), so at large batches a
+ * step takes a few more launches than gdn_cpr_decode_step.
+ * Concurrency: every call on a device uses that device's one array, which
+ * keeps the last call's contents.  Calls that overlap on one device (on
+ * different streams, or from several threads) race; the caller orders them.
+ * The device is the stream's.  The first call on a device looks up the
+ * array's address there (hipGetSymbolAddress), with that device current:
+ * make it outside graph capture.
+ */
+#define GDN_NOALLOC_MAX_PAIRS 65536
+#define GDN_NOALLOC_SCRATCH_BYTES (2 * GDN_NOALLOC_MAX_PAIRS * 4 + (64 << 20))
+gdn_status gdn_cpr_decode_step_noalloc(const gdn_cpr_shape* shape, int32_t num_seqs, const void* q,
+                                       const void* k, const void* v, const void* g, const void* beta,
+                                       const gdn_cpr_cache* cache, float* hT, void* o, void* stream);
 
 /*
  * Prefill continued from a cache (serving: a further prompt segment, or

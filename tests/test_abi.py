@@ -131,6 +131,29 @@ def test_decode_rejects_bad_arguments():
     assert dec(N=0) == _lib.GDN_OK
 
 
+def test_noalloc_decode_rejects_bad_arguments_and_sizes():
+    lib = _lib_or_skip()
+    s = _shape()
+
+    def dec(shape=s, N=4, q=FAKE, c=_cache(), hT=None):
+        return lib.gdn_cpr_decode_step_noalloc(ctypes.byref(shape), N, q, FAKE, FAKE, FAKE, FAKE,
+                                               ctypes.byref(c), hT, FAKE, None)
+
+    assert dec(shape=_shape(dk=32)) == _lib.GDN_ERR_UNSUPPORTED
+    assert dec(q=None) == _lib.GDN_ERR_INVALID_ARG
+    assert dec(c=_cache(FAKE, FAKE + 4)) == _lib.GDN_ERR_INVALID_ARG
+    assert b"slot_index" in lib.gdn_cpr_last_error()
+    assert dec(hT=FAKE) == _lib.GDN_ERR_INVALID_ARG
+    assert b"aliases" in lib.gdn_cpr_last_error()
+    # the fixed scratch: flags for 65,536 (sequence, head) pairs ...
+    assert dec(N=32769) == _lib.GDN_ERR_UNSUPPORTED
+    assert b"pairs" in lib.gdn_cpr_last_error()
+    # ... and chunk products for 1,024 heads at d = 128 bf16 (64 KiB each)
+    assert dec(shape=_shape(H=1025, dk=128, dv=128), N=1) == _lib.GDN_ERR_UNSUPPORTED
+    assert b"heads" in lib.gdn_cpr_last_error()
+    assert dec(N=0) == _lib.GDN_OK
+
+
 def test_cache_state_rejects_bad_arguments():
     lib = _lib_or_skip()
     s = _shape()

@@ -84,8 +84,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
-            f"{LIB_NAME} is not built (expected at {LIB_PATH}); run __graft_entry__.build() "
-            "or python -m bitwise_invariant_gated_amd.build")
+            f"{LIB_NAME} is not built (expected at {LIB_PATH}); run python -m bitwise_invariant_gated_amd.build")
     lib = ctypes.CDLL(LIB_PATH)
     lib.gdn_cpr_workspace_size.restype = ctypes.c_size_t
     lib.gdn_cpr_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,

@@ -2461,10 +2461,10 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   return launch_status(fn);
 }
 
-template <class D, int DK, int DV>
 // The resync runs over groups of `group` sequences, one launch (bf16) or
 // two (fp32) per group, each group's pairs using product slots 0 ..
 // group * H - 1; the workspace decode takes the whole batch as one group.
+template <class D, int DK, int DV>
 gdn_status run_decode(const DecodeArgs& a, int group, hipStream_t st, const char* fn) {
   mark(0, st);
   hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(DV), 0, st, a);

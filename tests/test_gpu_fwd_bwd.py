@@ -2,7 +2,7 @@
 pinned by autograd and finite differences in test_oracle.py), the forward
 bit-identical to prefill, and reruns bit-identical.
 
-Tolerances per gradient tensor (the stated reading of the task's bounds for
+Tolerances per gradient tensor (the output tolerances carried over to the
 gradients): fp32 inputs max|err| <= 1e-5 * max|ref|; bf16 inputs
 max|err| <= 2e-2 * max(1, max|ref|).  Each test prints the measured
 max|err| / max|ref| per tensor.

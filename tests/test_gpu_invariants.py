@@ -1,5 +1,5 @@
 """GPU checks against what the recurrence itself fixes, with no oracle in the
-loop (the task's invariants, applied to the HIP path directly).
+loop (invariants of the update rule, applied to the HIP path directly).
 
 - Store and retrieve: with alpha = 1 (g = 0), beta = 1 and orthonormal keys,
   writing value v_j under key k_j and then querying with q = k_j returns v_j:
@@ -13,7 +13,7 @@ loop (the task's invariants, applied to the HIP path directly).
   M_t = exp(g_1 + ... + g_t) h0 and o_t = exp(g_1 + ... + g_t) M_0 q_t in
   closed form (evaluated here in fp64 from the same fp32 inputs).
 
-Tolerances: the task's, 1e-5 * max|o| for fp32 inputs and 2e-2 absolute for
+Tolerances: 1e-5 * max|o| for fp32 inputs and 2e-2 absolute for
 bf16 inputs.
 """
 

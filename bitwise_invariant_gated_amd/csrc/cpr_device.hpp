@@ -132,10 +132,34 @@ struct KQRaw {
   uint32_t w[sizeof(typename D::T) == 2 ? 8 : 16];  // k then q: 4 + 4 dwords (bf16) or 8 + 8 (fp32)
 };
 
-// this lane's 16-byte slot of a k or q row of DK elements
+// How a state column's keys sit on the lanes.  Up to d_k = 128 a lane holds
+// its column's whole key range and a wave covers 64 columns.  At d_k = 256
+// the keys of column j are split over lanes j and j + 32 (rows 0-1 of the
+// wave hold keys 0 .. 127, rows 2-3 keys 128 .. 255), a wave covers 32
+// columns, and the two halves' partial sums are combined across the lane
+// halves (halves_sum).
+template <int DK>
+struct KeySplit {
+  static constexpr int kParts = DK > 128 ? 2 : 1;
+  static constexpr int kKeys = DK / kParts;  // state elements per lane
+  static constexpr int kCols = 64 / kParts;  // state columns per wave
+  static_assert(DK % 16 == 0 && DK <= 256, "head dims up to 256");
+};
+
+// this lane's 16-byte slot of a k or q row of DK elements: elements 8c ..
+// 8c+7 of its half of the row, c = lane mod 16
 template <int DK>
 __device__ __forceinline__ int kq_slot(int lane) {
+  if constexpr (KeySplit<DK>::kParts == 2) return (lane & 15) + 16 * (lane >> 5);
   return (lane & 15) & (DK / 8 - 1);  // lanes past the row repeat an in-bounds slot
+}
+
+// x of lanes 0-31 plus x of lanes 32-63 (lane l pairs with l +- 32), the same
+// value in every lane: v_permlane32_swap exchanges the two lane halves, so
+// the two values meet in one fp32 add, which is exact in either order
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // k and q of one token from plain row pointers (decode, continuation head)
@@ -268,6 +292,11 @@ __device__ __forceinline__ float token_step_plain(float (&s)[DK], const float (&
 //   w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3)))
 //   pass B, i ascending:  N[i] = fma(k[i], w, N[i]);  o_(i mod 2) = fma(q[i], N[i], o_(i mod 2))
 //   o = c * (o_0 + o_1)
+//
+// At d_k = 256 (KeySplit) each lane runs these passes over its half of the
+// keys, i = 0 .. 127 of the half, with P = (p_0 + p_1) + (p_2 + p_3) and
+// O = o_0 + o_1 per half, and the halves meet in one add:
+//   w = b * (v - c * (P_lo + P_hi)),  o = c * (O_lo + O_hi).
 constexpr float kRenormLog = -32.f;
 
 struct TokenScale {
@@ -302,14 +331,15 @@ __device__ __forceinline__ void renormalise(float (&s)[DK], float c) {
 // state element of a scaled running state: exp(lg) * n (exactly n when lg = 0)
 __device__ __forceinline__ float scale_of_log(float lg) { return expf(lg); }
 
-// The per-token step.  s: this lane's state column (N); kf, qf: this lane's
-// unpacked k and q elements 8c .. 8c+7 (DPP delivery above); c, b, renorm:
-// the token's scalars (step_factors, token_scale); v: the lane's value
-// element.  Returns the output element o.
-template <int DK>
-__device__ __forceinline__ float token_step(float (&s)[DK], const float (&kf)[8], const float (&qf)[8], float c,
-                                            float b, bool renorm, float v) {
-  static_assert(DK % 16 == 0 && DK <= 128, "one 16-lane row holds the key row");
+// The per-token step.  s: this lane's state column (N; its half at
+// d_k = 256); kf, qf: this lane's unpacked k and q elements 8c .. 8c+7 (DPP
+// delivery above); c, b, renorm: the token's scalars (step_factors,
+// token_scale); v: the lane's value element.  Returns the output element o.
+template <int DKF>
+__device__ __forceinline__ float token_step(float (&s)[KeySplit<DKF>::kKeys], const float (&kf)[8],
+                                            const float (&qf)[8], float c, float b, bool renorm, float v) {
+  constexpr int DK = KeySplit<DKF>::kKeys;  // keys of this lane
+  static_assert(DK % 16 == 0 && DK <= 128, "one 16-lane row holds the lane's keys");
   if (renorm) {
     renormalise<DK>(s, c);
     c = 1.f;
@@ -332,7 +362,9 @@ __device__ __forceinline__ float token_step(float (&s)[DK], const float (&kf)[8]
       fmac_bcast<n>(p3, kf[e + 3], s[i + 3]);
     }
   });
-  const float w = b * (v - c * ((p0 + p1) + (p2 + p3)));
+  float P = (p0 + p1) + (p2 + p3);
+  if constexpr (KeySplit<DKF>::kParts == 2) P = halves_sum(P);
+  const float w = b * (v - c * P);
   asm volatile("s_nop 1" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
                "v"(qf[7]));
   float o0, o1;
@@ -354,14 +386,16 @@ __device__ __forceinline__ float token_step(float (&s)[DK], const float (&kf)[8]
       fmac_bcast<n>(o1, qf[e + 1], s[i + 1]);
     }
   });
-  return c * (o0 + o1);
+  float O = o0 + o1;
+  if constexpr (KeySplit<DKF>::kParts == 2) O = halves_sum(O);
+  return c * O;
 }
 
 // One token of a single-token caller (decode, continuation head): the token's
 // k and q rows, g, beta and value element; the state column s (N) and the
 // log-scale lg are updated in place.  Returns the output element.
 template <class D, int DK>
-__device__ __forceinline__ float token_step_at(float (&s)[DK], float& lg, const typename D::T* krow,
+__device__ __forceinline__ float token_step_at(float (&s)[KeySplit<DK>::kKeys], float& lg, const typename D::T* krow,
                                                const typename D::T* qrow, float g, float beta, float v, int lane) {
   KQRaw<D> raw;
   load_kq<D, DK>(raw, krow, qrow, lane);
@@ -384,9 +418,11 @@ __device__ __forceinline__ float token_step_at(float (&s)[DK], float& lg, const 
 // token t's have been unpacked; every fetch is issued (its index is clamped
 // to token n-1), so the wait before a token's first use of its operands
 // covers that token's loads only.  Rows are addressed as a wave-uniform base
-// plus a 32-bit lane offset (one VGPR per operand kind).
+// plus a 32-bit lane offset (one VGPR per operand kind).  At d_k = 256 the
+// lanes of the upper half hold the same columns' upper keys and store no
+// output.
 template <class D, int DK, int DV>
-__device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T* __restrict__ kp,
+__device__ __forceinline__ void scan_tokens(float (&s)[KeySplit<DK>::kKeys], const typename D::T* __restrict__ kp,
                                             const typename D::T* __restrict__ qp, const typename D::T* __restrict__ vp,
                                             typename D::T* __restrict__ op, size_t row0, int H, size_t kq0, int Hk,
                                             int n, int col, int lane, float c_l, float b_l, uint64_t renorm) {
@@ -438,10 +474,12 @@ __device__ __forceinline__ void scan_tokens(float (&s)[DK], const typename D::T*
   for (int t = 0; t < n; ++t) {
     const float out =
         token_step<DK>(s, kf, qf, lane_bcast(c_l, t), lane_bcast(b_l, t), (renorm >> t) & 1, vcur);
-    if constexpr (sizeof(T) == 2)
-      __builtin_amdgcn_raw_buffer_store_b16(D::round(out), ro, v_off, (uint32_t)t * v_stride, 0);
-    else
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ro, v_off, (uint32_t)t * v_stride, 0);
+    if (lane < KeySplit<DK>::kCols) {
+      if constexpr (sizeof(T) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(D::round(out), ro, v_off, (uint32_t)t * v_stride, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ro, v_off, (uint32_t)t * v_stride, 0);
+    }
     if (t + 1 < n) take(t + 1);
   }
 }

@@ -600,9 +600,10 @@ __global__ __launch_bounds__(kResyncWaves<DV> * 64) void k_chain_resync_bf16(con
 // in the fixed-scratch decode, which resynchronises the batch in groups);
 // product slots are indexed within the grid.
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
-  constexpr int NT = kResyncNT, NW = DV / (16 * NT);
-  static_assert(NW <= 4, "the chain step's waves fit the work-group");
+__global__ __launch_bounds__(256, DK > 128 ? 1 : 3) void k_resync_bf16(const DecodeArgs a) {
+  // 32 columns per wave pass (16 at d_k = 256, where a 16-column block's
+  // state is already 64 accumulator registers); four waves take the passes
+  constexpr int NT = DK > 128 ? 1 : kResyncNT, NW = DV / (16 * NT);
   __shared__ ChunkLdsB<DK, DV> sm;
   const int i = a.seq0 + blockIdx.x;
   const size_t sh = (size_t)i * a.H + blockIdx.y;
@@ -617,8 +618,8 @@ __global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
   chunk_local_bf16<DK, DV>(sm, prod, a.gamn + ps);
   __syncthreads();  // the slot and Gamma_n, written by every wave, are read below
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave < NW) {
-    const int jb0 = wave * NT;
+  for (int jw = wave; jw < NW; jw += 4) {
+    const int jb0 = jw * NT;
     const size_t SS = (size_t)DK * DV;
     mfma::f32x4 S[DK / 16][NT];
     load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * SS, jb0, lane);
@@ -631,33 +632,37 @@ __global__ __launch_bounds__(256, 3) void k_resync_bf16(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// in-chunk scan (prefill): one wave per (chunk, head, 64 state columns)
+// in-chunk scan (prefill): one wave per (chunk, head, 64 state columns; 32
+// at d_k = 256)
 
 // One scan unit: chunk slot `slot` (chunk c of sequence i), head h, state
-// columns 64 z .. 64 z + 63 (one wave, lane = column).  kAgentBnd: the
-// boundary state is read with agent-scope loads, because the boundary chain
-// wrote it during the same launch (k_chain_scan_bf16).
+// columns WC z .. WC z + WC - 1 (one wave; WC = KeySplit<DK>::kCols; lane =
+// column, and at d_k = 256 lanes j and j + 32 the two key halves of column
+// j).  kAgentBnd: the boundary state is read with agent-scope loads, because
+// the boundary chain wrote it during the same launch (k_chain_scan_bf16).
 template <class D, int DK, int DV, bool kAgentBnd>
 __device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i, int h, int z, int lane) {
   using T = typename D::T;
+  constexpr int KL = KeySplit<DK>::kKeys, WC = KeySplit<DK>::kCols;
   const int H = a.H;
   const int c = slot - a.all_base[i];
   const int L = a.end[i] - a.start[i];
   const int Cl = a.Cl;
   const int n = min(Cl, L - c * Cl);
   const size_t tok0 = (size_t)a.start[i] + (size_t)c * Cl;
-  const int col = z * kWave + lane;
+  const int col = z * WC + lane % WC;
+  const int k0 = (lane / WC) * KL;  // this lane's first key row
   const size_t SS = (size_t)DK * DV;
 
   const float* B = a.bnd + ((size_t)slot * H + h) * SS;
-  float s[DK];
+  float s[KL];
   if constexpr (kAgentBnd) {
     // rows 4q .. 4q+3 of column col sit 256 q bytes after rows 0 .. 3
-    static_assert(bnd_index<DK>(4, 0) == 64, "row groups of a column are 256 bytes apart");
+    static_assert(bnd_index<DK>(4, 0) == 64 && bnd_index<DK>(16, 0) == 256, "row groups 256 bytes apart");
     const BufRsrc rb = buf_rsrc(B, (uint32_t)(SS * sizeof(float)));
-    const uint32_t col_off = (uint32_t)(bnd_index<DK>(0, col) * 4);
+    const uint32_t col_off = (uint32_t)(bnd_index<DK>(k0, col) * 4);
 #pragma unroll
-    for (int q = 0; q < DK / 4; ++q) {  // rows 4q .. 4q+3 of column col: one 16-byte load
+    for (int q = 0; q < KL / 4; ++q) {  // rows k0 + 4q .. k0 + 4q+3 of column col: one 16-byte load
       const mfma::f32x4 x = __builtin_bit_cast(
           mfma::f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col_off, 256 * q, kAuxAgent));
       s[4 * q] = x[0];
@@ -667,8 +672,8 @@ __device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i,
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < DK / 4; ++q) {  // rows 4q .. 4q+3 of column col: one 16-byte load
-      const mfma::f32x4 x = *reinterpret_cast<const mfma::f32x4*>(B + bnd_index<DK>(4 * q, col));
+    for (int q = 0; q < KL / 4; ++q) {  // rows k0 + 4q .. k0 + 4q+3 of column col: one 16-byte load
+      const mfma::f32x4 x = *reinterpret_cast<const mfma::f32x4*>(B + bnd_index<DK>(k0 + 4 * q, col));
       s[4 * q] = x[0];
       s[4 * q + 1] = x[1];
       s[4 * q + 2] = x[2];
@@ -709,16 +714,17 @@ __device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i,
     const size_t ch = cache_row(a.slot, i) * H + h;
     float* R = a.s_run + ch * SS;
 #pragma unroll
-    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+    for (int ii = 0; ii < KL; ++ii) R[(size_t)ii * DV + k0 * DV + col] = s[ii];
     if (z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
     if (a.hT) {  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
       float* F = a.hT + ((size_t)i * H + h) * SS;
       const float e = scale_of_log(lg);
 #pragma unroll
-      for (int ii = 0; ii < DK; ++ii) F[(size_t)ii * DV + col] = e * s[ii];
+      for (int ii = 0; ii < KL; ++ii) F[(size_t)ii * DV + k0 * DV + col] = e * s[ii];
     }
     T* tv = (T*)a.tail_v + ch * Cl * DV;
-    for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
+    if (lane < WC)
+      for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
     if (z == 0) {
       T* tk = (T*)a.tail_k + ch * Cl * DK;
       for (int idx = lane; idx < n * DK; idx += kWave) {
@@ -794,7 +800,7 @@ __device__ __forceinline__ bool wait_count(const int32_t* p, int need) {
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 3) void k_chain_scan_bf16(const PrefillArgs a, const FusedArgs f) {
+__global__ __launch_bounds__(256, DK > 128 ? 2 : 3) void k_chain_scan_bf16(const PrefillArgs a, const FusedArgs f) {
   using namespace mfma;
   typedef SlotB<DK, DV> Sl;
   constexpr int kThreads = 256, CB = kFusedChainCols, NZ = DV / CB;
@@ -817,18 +823,20 @@ __global__ __launch_bounds__(256, 3) void k_chain_scan_bf16(const PrefillArgs a,
   const int t = __builtin_amdgcn_readfirstlane(ticket_s);
   const int H = a.H;
   if (t >= f.n_chain) {
-    // ---- scan item: one unit per wave
-    const long u = (long)(t - f.n_chain) * 4 + wave;
-    const long per_slot = (long)H * NZ;
-    if (u >= (long)a.all_base[a.N] * per_slot) return;
-    const int pos = (int)(u / per_slot), r = (int)(u % per_slot), h = r / NZ, z = r % NZ;
-    const int slot = f.order[pos];
-    if (slot < 0 || slot >= a.all_base[a.N]) return;  // (the plan writes every position in range)
-    const int i = find_seq(a.all_base, a.N, slot);
-    const int c = slot - a.all_base[i];
-    if (!wait_count(f.ready + (((size_t)i * H + h) * NZ + z) * kReadyStride, c + 1) && lane == 0)
-      atomicExch(f.timeout, 1);
-    scan_unit<Bf16, DK, DV, true>(a, slot, i, h, z, lane);
+    // ---- scan item: one unit per wave (launches at d_k = 256 have chain items only)
+    if constexpr (KeySplit<DK>::kParts == 1) {
+      const long u = (long)(t - f.n_chain) * 4 + wave;
+      const long per_slot = (long)H * NZ;
+      if (u >= (long)a.all_base[a.N] * per_slot) return;
+      const int pos = (int)(u / per_slot), r = (int)(u % per_slot), h = r / NZ, z = r % NZ;
+      const int slot = f.order[pos];
+      if (slot < 0 || slot >= a.all_base[a.N]) return;  // (the plan writes every position in range)
+      const int i = find_seq(a.all_base, a.N, slot);
+      const int c = slot - a.all_base[i];
+      if (!wait_count(f.ready + (((size_t)i * H + h) * NZ + z) * kReadyStride, c + 1) && lane == 0)
+        atomicExch(f.timeout, 1);
+      scan_unit<Bf16, DK, DV, true>(a, slot, i, h, z, lane);
+    }
     return;
   }
   // ---- chain item
@@ -925,21 +933,44 @@ __global__ __launch_bounds__(256, 3) void k_chain_scan_bf16(const PrefillArgs a,
 }
 
 // ---------------------------------------------------------------------------
-// decode: one work item per (sequence, head); DV threads, lane = state column
+// decode: one work-group per (sequence, head); a thread per state column (two
+// per column at d_k = 256, one per key half: ColumnLanes)
+
+// Where thread `tid` of a work-group of DV * kParts threads sits: its state
+// column, its first key row, and whether it writes the column's per-column
+// outputs (the lower key half does).
+template <int DK>
+struct ColumnLanes {
+  int lane, col, k0;
+  bool writer;
+  __device__ explicit ColumnLanes(int tid) {
+    constexpr int WC = KeySplit<DK>::kCols;
+    lane = tid & 63;
+    col = (tid >> 6) * WC + lane % WC;
+    k0 = (lane / WC) * KeySplit<DK>::kKeys;
+    writer = lane < WC;
+  }
+};
+
+template <int DK, int DV>
+constexpr int kColumnThreads = DV * KeySplit<DK>::kParts;
 
 template <class D, int DK, int DV>
-__global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
+__global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_decode(const DecodeArgs a) {
   using T = typename D::T;
+  constexpr int KL = KeySplit<DK>::kKeys, NTH = kColumnThreads<DK, DV>;
   const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
   const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  const int col = threadIdx.x;
+  const int tid = threadIdx.x;
+  const ColumnLanes<DK> cl(tid);
+  const int col = cl.col;
   const size_t SS = (size_t)DK * DV;
   const int tl = a.tail_len[ch];
   const float lg = a.lgs[ch];
   __syncthreads();  // every wave has read tail_len and lgs before they are rewritten below
   const int Cl = a.Cl;
   if ((unsigned)tl >= (unsigned)Cl) {  // not a valid cache: touch nothing
-    if (col == 0) a.flag[sh] = 0;
+    if (tid == 0) a.flag[sh] = 0;
     return;
   }
   const T* kp = (const T*)a.k;
@@ -947,42 +978,42 @@ __global__ __launch_bounds__(DV) void k_decode(const DecodeArgs a) {
   const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
   // the token's k, v, g, beta as stored, for the tail append at the end
   // (loaded here, before any store, so the append needs no second read)
-  constexpr int KE = (DK + DV - 1) / DV;
+  constexpr int KE = (DK + NTH - 1) / NTH;
   T k_app[KE];
 #pragma unroll
-  for (int m = 0; m < KE; ++m) k_app[m] = col + m * DV < DK ? kp[kr * DK + col + m * DV] : T();
+  for (int m = 0; m < KE; ++m) k_app[m] = tid + m * NTH < DK ? kp[kr * DK + tid + m * NTH] : T();
   const T v_app = ((const T*)a.v)[sh * DV + col];
   const T g_app = ((const T*)a.g)[sh], b_app = ((const T*)a.beta)[sh];
   float* R = a.s_run + ch * SS;
-  float s[DK];
+  float s[KL];
 #pragma unroll
-  for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
+  for (int ii = 0; ii < KL; ++ii) s[ii] = R[(size_t)ii * DV + cl.k0 * DV + col];
   float lg_next = lg;
   const float out = token_step_at<D, DK>(s, lg_next, kp + kr * DK, qp + kr * DK, D::load(&g_app, 0),
-                                         D::load(&b_app, 0), D::load(&v_app, 0), col);
-  D::store((T*)a.o, sh * DV + col, out);
+                                         D::load(&b_app, 0), D::load(&v_app, 0), cl.lane);
+  if (cl.writer) D::store((T*)a.o, sh * DV + col, out);
   // append the token to the tail
   T* tk = (T*)a.tail_k + (ch * Cl + tl) * DK;
 #pragma unroll
   for (int m = 0; m < KE; ++m)
-    if (col + m * DV < DK) tk[col + m * DV] = k_app[m];
-  ((T*)a.tail_v)[(ch * Cl + tl) * DV + col] = v_app;
-  if (col == 0) {
+    if (tid + m * NTH < DK) tk[tid + m * NTH] = k_app[m];
+  if (cl.writer) ((T*)a.tail_v)[(ch * Cl + tl) * DV + col] = v_app;
+  if (tid == 0) {
     ((T*)a.tail_g)[ch * Cl + tl] = g_app;
     ((T*)a.tail_beta)[ch * Cl + tl] = b_app;
   }
   const bool full = (tl + 1 == Cl);
   if (!full) {
 #pragma unroll
-    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+    for (int ii = 0; ii < KL; ++ii) R[(size_t)ii * DV + cl.k0 * DV + col] = s[ii];
     if (a.hT) {  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
       float* F = a.hT + sh * SS;
       const float e = scale_of_log(lg_next);
 #pragma unroll
-      for (int ii = 0; ii < DK; ++ii) F[(size_t)ii * DV + col] = e * s[ii];
+      for (int ii = 0; ii < KL; ++ii) F[(size_t)ii * DV + cl.k0 * DV + col] = e * s[ii];
     }
   }
-  if (col == 0) {
+  if (tid == 0) {
     a.tail_len[ch] = full ? 0 : tl + 1;
     a.lgs[ch] = full ? 0.f : lg_next;  // a full tail resynchronises to a boundary (scale 1)
     a.flag[sh] = full ? 3 : 0;         // the resync then also writes hT (if asked for)
@@ -1042,12 +1073,15 @@ struct ContArgs {
 };
 
 template <class D, int DK, int DV>
-__global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
+__global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_cont_head(const ContArgs a) {
   using T = typename D::T;
+  constexpr int KL = KeySplit<DK>::kKeys, NTH = kColumnThreads<DK, DV>;
   const int i = blockIdx.x, h = blockIdx.y, H = a.H;
   const size_t sh = (size_t)i * H + h;
   const size_t ch = cache_row(a.slot, i) * H + h;
-  const int col = threadIdx.x;
+  const int tid = threadIdx.x;
+  const ColumnLanes<DK> cl(tid);
+  const int col = cl.col;
   const size_t SS = (size_t)DK * DV;
   const int tl = a.tail_len[ch];
   float lg = a.lgs[ch];
@@ -1055,27 +1089,30 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   const int L = a.cu[i + 1] - a.cu[i];
   const int Cl = a.Cl;
   const int nh = ((unsigned)tl < (unsigned)Cl && tl > 0) ? min(Cl - tl, L) : 0;
-  if (h == 0 && col == 0) a.body_start[i] = a.cu[i] + nh;
-  if (col == 0) a.flag[sh] = 0;
+  if (h == 0 && tid == 0) a.body_start[i] = a.cu[i] + nh;
+  if (tid == 0) a.flag[sh] = 0;
   float* R = a.s_run + ch * SS;
   if (L == 0) {  // nothing new: the final state is the cached one
     if (a.hT) {
       const float e = scale_of_log(lg);
 #pragma unroll
-      for (int ii = 0; ii < DK; ++ii) a.hT[sh * SS + (size_t)ii * DV + col] = e * R[(size_t)ii * DV + col];
+      for (int ii = 0; ii < KL; ++ii) {
+        const size_t e_off = (size_t)ii * DV + cl.k0 * DV + col;
+        a.hT[sh * SS + e_off] = e * R[e_off];
+      }
     }
     return;
   }
   if (nh == 0) return;  // the body prefill writes the final state
-  float s[DK];
+  float s[KL];
 #pragma unroll
-  for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
+  for (int ii = 0; ii < KL; ++ii) s[ii] = R[(size_t)ii * DV + cl.k0 * DV + col];
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
   const T* gp = (const T*)a.g;
   const T* bp = (const T*)a.beta;
-  constexpr int KE = (DK + DV - 1) / DV;
+  constexpr int KE = (DK + NTH - 1) / NTH;
   for (int t = 0; t < nh; ++t) {
     const size_t row = (size_t)(a.cu[i] + t) * H + h;
     const size_t kr = kq_row((size_t)(a.cu[i] + t), h, a.Hk, a.G);
@@ -1083,18 +1120,18 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
     // before the output store, so the append needs no second read)
     T k_app[KE];
 #pragma unroll
-    for (int m = 0; m < KE; ++m) k_app[m] = col + m * DV < DK ? kp[kr * DK + col + m * DV] : T();
+    for (int m = 0; m < KE; ++m) k_app[m] = tid + m * NTH < DK ? kp[kr * DK + tid + m * NTH] : T();
     const T v_app = vp[row * DV + col], g_app = gp[row], b_app = bp[row];
     const float out = token_step_at<D, DK>(s, lg, kp + kr * DK, qp + kr * DK, D::load(&g_app, 0),
-                                           D::load(&b_app, 0), D::load(&v_app, 0), col);
-    D::store((T*)a.o, row * DV + col, out);
+                                           D::load(&b_app, 0), D::load(&v_app, 0), cl.lane);
+    if (cl.writer) D::store((T*)a.o, row * DV + col, out);
     const size_t tr = ch * Cl + tl + t;  // tail row
     T* tk = (T*)a.tail_k + tr * DK;
 #pragma unroll
     for (int m = 0; m < KE; ++m)
-      if (col + m * DV < DK) tk[col + m * DV] = k_app[m];
-    ((T*)a.tail_v)[tr * DV + col] = v_app;
-    if (col == 0) {
+      if (tid + m * NTH < DK) tk[tid + m * NTH] = k_app[m];
+    if (cl.writer) ((T*)a.tail_v)[tr * DV + col] = v_app;
+    if (tid == 0) {
       ((T*)a.tail_g)[tr] = g_app;
       ((T*)a.tail_beta)[tr] = b_app;
     }
@@ -1102,14 +1139,14 @@ __global__ __launch_bounds__(DV) void k_cont_head(const ContArgs a) {
   const bool full = (tl + nh == Cl);
   if (!full) {
 #pragma unroll
-    for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
+    for (int ii = 0; ii < KL; ++ii) R[(size_t)ii * DV + cl.k0 * DV + col] = s[ii];
     if (a.hT) {  // the head is the whole segment (nh == L): exp(lg) N is the final state
       const float e = scale_of_log(lg);
 #pragma unroll
-      for (int ii = 0; ii < DK; ++ii) a.hT[sh * SS + (size_t)ii * DV + col] = e * s[ii];
+      for (int ii = 0; ii < KL; ++ii) a.hT[sh * SS + (size_t)ii * DV + cl.k0 * DV + col] = e * s[ii];
     }
   }
-  if (col == 0) {
+  if (tid == 0) {
     a.tail_len[ch] = full ? 0 : tl + nh;
     a.lgs[ch] = full ? 0.f : lg;
     // a closed chunk resynchronises; with no body after it, that boundary is the final state
@@ -2195,7 +2232,9 @@ gdn_status fail(gdn_status st, const char* fmt, ...) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool shape_ok(const gdn_cpr_shape* s, std::string* why) {
+// wide_ok: the call serves d_k = d_v = 256 (bf16 prefill, decode,
+// continuation and the cache read-out; not fwd_bwd or the comparators)
+bool shape_ok(const gdn_cpr_shape* s, std::string* why, bool wide_ok = false) {
   if (!s) {
     *why = "shape is NULL";
     return false;
@@ -2204,8 +2243,17 @@ bool shape_ok(const gdn_cpr_shape* s, std::string* why) {
     *why = "num_heads must be >= 1";
     return false;
   }
-  if (!((s->head_dim_k == 64 || s->head_dim_k == 128) && (s->head_dim_v == 64 || s->head_dim_v == 128))) {
-    *why = "head dims must be 64 or 128";
+  const bool wide = s->head_dim_k == 256 && s->head_dim_v == 256;
+  if (!((s->head_dim_k == 64 || s->head_dim_k == 128) && (s->head_dim_v == 64 || s->head_dim_v == 128)) && !wide) {
+    *why = "head dims must be 64 or 128 (or both 256)";
+    return false;
+  }
+  if (wide && !wide_ok) {
+    *why = "head dims of 256 serve prefill, decode and continuation only";
+    return false;
+  }
+  if (wide && s->dtype != GDN_DTYPE_BF16) {
+    *why = "head dims of 256 take bf16 inputs";
     return false;
   }
   if (s->chunk != 16 && s->chunk != 32 && s->chunk != C) {
@@ -2415,7 +2463,7 @@ constexpr long kFusedMaxChainItems = 512;
 
 template <int DK, int DV>
 bool use_fused(const PrefillArgs& a) {
-  return a.order && a.all_chunks == 0 && a.N <= kFusedMaxSeqs &&
+  return KeySplit<DK>::kParts == 1 && a.order && a.all_chunks == 0 && a.N <= kFusedMaxSeqs &&
          (long)a.N * a.H * (DV / kFusedChainCols) <= kFusedMaxChainItems;
 }
 
@@ -2425,9 +2473,14 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   const int Amax = Fmax + a.N;
   constexpr bool kBf16 = std::is_same<D, Bf16>::value;
   const bool fused = kBf16 && use_fused<DK, DV>(a);
+  // at d_k = 256 the chain runs as the chain items of the fused kernel alone
+  // (its one-buffer stage fits the LDS where the two-buffer chain's does not),
+  // then the scan
+  constexpr bool kChainOnly = KeySplit<DK>::kParts > 1;
+  static_assert(!kChainOnly || kBf16, "d_k = 256 runs on the bf16 path");
   constexpr int NZ = DV / kFusedChainCols;
   FusedPlan fp{};
-  if (fused) fp = FusedPlan{a.order, a.counters, a.ready, a.N * a.H * NZ * kReadyStride};
+  if (fused || kChainOnly) fp = FusedPlan{a.order, a.counters, a.ready, a.N * a.H * NZ * kReadyStride};
   mark(0, st);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.Cl, a.full_base, a.all_base, fp);
   mark(1, st);
@@ -2449,14 +2502,18 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
     return launch_status(fn);
   }
   if (a.N > 0) {
-    if constexpr (kBf16)
+    if constexpr (kChainOnly) {
+      const FusedArgs f{a.order, a.counters, a.ready, a.counters + 1, a.N * a.H * NZ};
+      hipLaunchKernelGGL((k_chain_scan_bf16<DK, DV>), dim3(f.n_chain), dim3(256), 0, st, a, f);
+    } else if constexpr (kBf16) {
       launch_chain_bf16<DK, DV>(a, st);
-    else
+    } else {
       hipLaunchKernelGGL((k_chain_prefill<DK, DV>), dim3(a.N, a.H, DV / kChainCols), dim3(256), 0, st, a);
+    }
   }
   mark(3, st);
   if (Amax > 0 && T > 0)
-    hipLaunchKernelGGL((k_scan<D, DK, DV>), dim3(Amax, a.H, DV / kWave), dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL((k_scan<D, DK, DV>), dim3(Amax, a.H, DV / KeySplit<DK>::kCols), dim3(kWave), 0, st, a);
   mark(4, st);
   return launch_status(fn);
 }
@@ -2467,7 +2524,7 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
 template <class D, int DK, int DV>
 gdn_status run_decode(const DecodeArgs& a, int group, hipStream_t st, const char* fn) {
   mark(0, st);
-  hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(DV), 0, st, a);
+  hipLaunchKernelGGL((k_decode<D, DK, DV>), dim3(a.N, a.H), dim3(kColumnThreads<DK, DV>), 0, st, a);
   mark(1, st);
   for (int s0 = 0; s0 < a.N; s0 += group) {
     DecodeArgs r = a;
@@ -2484,10 +2541,17 @@ gdn_status run_decode(const DecodeArgs& a, int group, hipStream_t st, const char
   return launch_status(fn);
 }
 
+// Calls that also serve d_k = d_v = 256 on bf16 inputs (specialised below)
+template <template <class, int, int> class Fn>
+struct WideFn : std::false_type {};
+
 template <template <class, int, int> class Fn, class... Args>
 gdn_status dispatch(const gdn_cpr_shape& s, Args&&... args) {
   const bool bf = s.dtype == GDN_DTYPE_BF16;
   const int dk = s.head_dim_k, dv = s.head_dim_v;
+  if constexpr (WideFn<Fn>::value) {
+    if (bf && dk == 256 && dv == 256) return Fn<Bf16, 256, 256>::run(std::forward<Args>(args)...);
+  }
 #define GDN_CASE(DKv, DVv)                                                         \
   if (dk == DKv && dv == DVv)                                                      \
     return bf ? Fn<Bf16, DKv, DVv>::run(std::forward<Args>(args)...)               \
@@ -2534,7 +2598,7 @@ template <class D, int DK, int DV>
 struct ContFn {
   static gdn_status run(const ContArgs& ca, const DecodeArgs& da, const PrefillArgs& pa, int64_t T, hipStream_t st,
                         const char* fn) {
-    hipLaunchKernelGGL((k_cont_head<D, DK, DV>), dim3(ca.N, ca.H), dim3(DV), 0, st, ca);
+    hipLaunchKernelGGL((k_cont_head<D, DK, DV>), dim3(ca.N, ca.H), dim3(kColumnThreads<DK, DV>), 0, st, ca);
     if constexpr (std::is_same<D, Bf16>::value) {
       launch_resync_bf16<DK, DV>(da, da.N, st);
     } else {
@@ -2546,6 +2610,13 @@ struct ContFn {
     return run_prefill<D, DK, DV>(pa, T, st, fn);
   }
 };
+
+template <>
+struct WideFn<PrefillFn> : std::true_type {};
+template <>
+struct WideFn<DecodeFn> : std::true_type {};
+template <>
+struct WideFn<ContFn> : std::true_type {};
 
 // comparators: chunkwise layout = plan, one product slot and one boundary
 // state per (chunk slot incl. partial, head)
@@ -2782,7 +2853,7 @@ struct FwdBwdFn {
 extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num_seqs,
                                          int64_t total_tokens, int32_t op) {
   std::string why;
-  if (!shape_ok(shape, &why) || num_seqs < 0 || total_tokens < 0) return 0;
+  if (!shape_ok(shape, &why, op != GDN_OP_FWD_BWD) || num_seqs < 0 || total_tokens < 0) return 0;
   if (op == GDN_OP_PREFILL) return prefill_layout(*shape, num_seqs, total_tokens).total;
   if (op == GDN_OP_FWD_BWD) return fwd_bwd_layout(*shape, num_seqs, total_tokens).total;
   if (op == GDN_OP_DECODE) return decode_layout(*shape, num_seqs).total;
@@ -2797,7 +2868,7 @@ extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_se
                                       size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_cpr_prefill";
   std::string why;
-  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (!shape_ok(shape, &why, true)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (total_tokens > (int64_t)INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens", fn);
   if (!cache_out) return fail(GDN_ERR_INVALID_ARG, "%s: cache_out is NULL", fn);
@@ -2879,7 +2950,7 @@ gdn_status decode_prepare(const char* fn, const gdn_cpr_shape* shape, int32_t nu
                           void* o, DecodeArgs& a, bool* done) {
   *done = false;
   std::string why;
-  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (!shape_ok(shape, &why, true)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
   if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
   if (num_seqs == 0) {
@@ -3036,7 +3107,7 @@ extern "C" gdn_status gdn_cpr_prefill_continue(const gdn_cpr_shape* shape, int32
                                                void* stream) {
   const char* fn = "gdn_cpr_prefill_continue";
   std::string why;
-  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (!shape_ok(shape, &why, true)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (total_tokens > (int64_t)INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens", fn);
   if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
@@ -3446,7 +3517,7 @@ extern "C" gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t nu
                                           float* state_out, void* stream) {
   const char* fn = "gdn_cpr_cache_state";
   std::string why;
-  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (!shape_ok(shape, &why, true)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
   if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (!cache) return fail(GDN_ERR_INVALID_ARG, "%s: cache is NULL", fn);
   if (num_seqs == 0) {
@@ -3472,7 +3543,7 @@ extern "C" void gdn_cpr_set_stage_events(void* const* events, int32_t n_events) 
 extern "C" const char* gdn_cpr_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" const char* gdn_cpr_numerics_id(void) {
-  return "gdn_cpr numerics v6: "
+  return "gdn_cpr numerics v7: "
          "per-token step (one routine for the prefill scan, decode and the continuation head; k and q by DPP "
          "row broadcast) in fp32 on a scaled running state M = exp(lg) N: x = lg + g (fp32 add); "
          "renorm = x < -32; c = exp(x); b = beta * r with r = exp(-x), r = 1 when renorm; renorm: N = c N, "
@@ -3483,6 +3554,9 @@ extern "C" const char* gdn_cpr_numerics_id(void) {
          "w = b * (v - c * ((p_0 + p_1) + (p_2 + p_3))); "
          "pass B, i ascending: N[i] = fma(k[i], w, N[i]); o_(i mod 2) = fma(q[i], N[i], o_(i mod 2)); "
          "o = c * (o_0 + o_1); "
+         "d_k = 256 (bf16 inputs): lanes j and j + 32 hold keys 0..127 and 128..255 of column j and run the "
+         "passes over their half with P = (p_0 + p_1) + (p_2 + p_3) and O = o_0 + o_1 per half; "
+         "w = b * (v - c * (P_lo + P_hi)); o = c * (O_lo + O_hi); "
          "final state = exp(lg) * N elementwise; exp = ocml expf; "
          "gamma = left-to-right fp32 cumsum of g; "
          "fp32 inputs: chunk products and boundary chain fp32 VALU with ascending explicit-fma sums and "

@@ -54,6 +54,22 @@ def test_workspace_size_shapes():
     assert lib.gdn_cpr_workspace_size(ctypes.byref(s), -1, 10240, _lib.GDN_OP_PREFILL) == 0
 
 
+def test_head_dim_256_serves_bf16_prefill_decode_and_continuation_only():
+    lib = _lib_or_skip()
+    s = _shape(16, 256, 256)
+    for op in (_lib.GDN_OP_PREFILL, _lib.GDN_OP_DECODE, _lib.GDN_OP_PREFILL_CONTINUE):
+        assert lib.gdn_cpr_workspace_size(ctypes.byref(s), 4, 4096, op) > 0, op
+    assert lib.gdn_cpr_workspace_size(ctypes.byref(s), 4, 4096, _lib.GDN_OP_FWD_BWD) == 0
+    assert lib.gdn_cpr_workspace_size(ctypes.byref(_shape(16, 256, 256, dtype=_lib.GDN_DTYPE_F32)), 4, 4096,
+                                      _lib.GDN_OP_PREFILL) == 0
+    assert lib.gdn_cpr_workspace_size(ctypes.byref(_shape(16, 128, 256)), 4, 4096, _lib.GDN_OP_PREFILL) == 0
+    assert lib.gdn_cmp_workspace_size(ctypes.byref(s), _lib.GDN_CMP_CHUNKWISE, 4, 4096) == 0
+    # a d = 256 chunk-product slot: W and K~^T fragments in bf16, U in fp32 (128 KiB)
+    n1 = lib.gdn_cpr_workspace_size(ctypes.byref(s), 1, 0, _lib.GDN_OP_DECODE)
+    n2 = lib.gdn_cpr_workspace_size(ctypes.byref(s), 2, 0, _lib.GDN_OP_DECODE)
+    assert n2 - n1 >= 16 * 128 * 1024
+
+
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
 
 
@@ -69,7 +85,8 @@ def _prefill(lib, shape, N=2, T=128, cache=None, cu=FAKE, q=FAKE, ws=FAKE, ws_by
 
 def test_prefill_rejects_unsupported_shapes():
     lib = _lib_or_skip()
-    for s in (_shape(dk=96), _shape(dv=32), _shape(C=48), _shape(C=128), _shape(H=0), _shape(dtype=7)):
+    for s in (_shape(dk=96), _shape(dv=32), _shape(C=48), _shape(C=128), _shape(H=0), _shape(dtype=7),
+              _shape(dk=256), _shape(dk=256, dv=256, dtype=_lib.GDN_DTYPE_F32)):
         assert _prefill(lib, s) == _lib.GDN_ERR_UNSUPPORTED
         assert lib.gdn_cpr_last_error()
 
@@ -225,3 +242,8 @@ def test_numerics_id_states_the_pinned_token_step_order():
     for ln in lines:
         assert ln in ident, ln
     assert "C in {16, 32, 64}" in ident
+    # the key split at d_k = 256, as the device code's comment states it
+    with open(os.path.join(ROOT, "bitwise_invariant_gated_amd", "csrc", "cpr_device.hpp")) as f:
+        dev = " ".join(f.read().split())
+    for formula in ("w = b * (v - c * (P_lo + P_hi))", "o = c * (O_lo + O_hi)"):
+        assert formula in dev and formula in ident, formula

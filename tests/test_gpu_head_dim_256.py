@@ -1,0 +1,109 @@
+"""GPU: head dims d_k = d_v = 256 (bf16 prefill, decode and continuation).
+
+A state column's 256 keys are split over two lanes (keys 0..127 and
+128..255), whose partial sums meet in one add; the scan, decode and the
+continuation head all take that split, so the usual promises must hold:
+prefill within tolerance of the fp64 oracle, decode bit-equal to prefill
+across resynchronisations, a continued prefill bit-equal to one prefill,
+alone == packed, and the written-out final state hT bit-equal to the cache's
+read-out.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bitwise_invariant_gated_amd as gdn
+import oracle
+from gdn_synth import make_batch
+
+from gpu_util import DEV, DevBatch, as_f64, bits, decode_rows, note, prefill, state_of, tol_for
+from test_gpu_continue import assert_cache_bitwise, run_segments
+
+pytestmark = pytest.mark.gpu
+
+D = 256
+LENS = [0, 1, 31, 63, 64, 65, 130, 200]
+
+
+@pytest.mark.parametrize("C", [64, 32])
+def test_d256_prefill_matches_oracle(C):
+    note(f"d=256 prefill vs oracle C={C}")
+    b = make_batch(860 + C, LENS, 2, D, D, dtype="bf16", h0_std=0.1)
+    db = DevBatch(b, C)
+    o, c = prefill(db)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.recurrent_forward(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.h0)
+    err_o = float(np.max(np.abs(as_f64(o) - o_ref)))
+    h = as_f64(state_of(db.shape, c))
+    err_h = float(np.max(np.abs(h - h_ref)))
+    print(f"d=256 C={C}: max|o err| {err_o:.3e} (max|o| {np.max(np.abs(o_ref)):.3f}), max|state err| {err_h:.3e}")
+    assert err_o <= tol_for(b, float(np.max(np.abs(o_ref))))
+    assert err_h <= tol_for(b, float(np.max(np.abs(h_ref))))
+    tl = bits(c.tail_len)
+    for i, L in enumerate(LENS):
+        assert np.all(tl[i] == L % C), (i, L)
+
+
+def test_d256_decode_equals_prefill_bitwise():
+    note("d=256 decode == prefill")
+    full = np.array([140, 134, 200, 75, 96])
+    steps = 70  # every sequence crosses a chunk boundary while decoding
+    b = make_batch(870, list(full), 2, D, D, dtype="bf16", h0_std=0.1)
+    pre = full - steps
+    db = DevBatch(b)
+    o_full, c_full = prefill(db)
+    _, c_dec = prefill(DevBatch(b.truncate(list(pre))))
+    o_dec = decode_rows(db, pre, steps, c_dec)
+    torch.cuda.synchronize()
+    ob, od = bits(o_full), bits(o_dec)
+    for i, L in enumerate(full):
+        a = int(b.cu_seqlens[i])
+        assert np.array_equal(od[:, i], ob[a + pre[i]:a + L]), i
+    assert_cache_bitwise(c_full, c_dec)
+
+
+def test_d256_continuation_and_packing_bitwise():
+    note("d=256 continuation == one prefill; alone == packed")
+    segs = np.asarray([[40, 90], [64, 1], [0, 131], [63, 1], [10, 0]], np.int64)
+    lens = segs.sum(axis=1)
+    b = make_batch(871, list(lens), 2, D, D, dtype="bf16", h0_std=0.1)
+    db = DevBatch(b)
+    o_one, c_one = prefill(db)
+    o_seg, c_seg = run_segments(db, [segs[:, 0], segs[:, 1]])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o_seg), bits(o_one))
+    assert_cache_bitwise(c_one, c_seg)
+    ob = bits(o_one)
+    for i in range(len(lens)):
+        oi, ci = prefill(DevBatch(b.select([i])))
+        torch.cuda.synchronize()
+        a, e = int(b.cu_seqlens[i]), int(b.cu_seqlens[i + 1])
+        assert np.array_equal(bits(oi), ob[a:e]), i
+        assert np.array_equal(bits(state_of(db.shape, ci))[0], bits(state_of(db.shape, c_one))[i]), i
+
+
+def test_d256_final_state_outputs_equal_cache_state():
+    note("d=256 hT from prefill and decode")
+    lens = [63, 126, 130, 3]  # tails 63, 62, 2, 3: the two decode steps close the first two sequences' chunks
+    b = make_batch(872, [n + 2 for n in lens], 2, D, D, dtype="bf16", h0_std=0.1)
+    db = DevBatch(b)
+    dbp = DevBatch(b.truncate(lens))
+    N, H = b.num_seqs, b.num_heads
+    cache = gdn.alloc_cache(dbp.shape, N)
+    hT = torch.full((N, H, D, D), 7.0, dtype=torch.float32, device=DEV)
+    o = torch.empty((dbp.b.total_tokens, H, D), dtype=torch.bfloat16, device=DEV)
+    ws = gdn.alloc_workspace(dbp.shape, N, dbp.b.total_tokens, gdn.GDN_OP_PREFILL)
+    gdn.gdn_cpr_prefill(dbp.shape, dbp.q, dbp.k, dbp.v, dbp.g, dbp.beta, dbp.cu, dbp.h0, cache, o, ws, hT=hT)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(hT), bits(state_of(dbp.shape, cache)))
+    wsd = gdn.alloc_workspace(db.shape, N, 0, gdn.GDN_OP_DECODE)
+    base = b.cu_seqlens[:-1].astype(np.int64) + np.asarray(lens, np.int64)
+    for s in range(2):
+        rows = torch.from_numpy(base + s).to(DEV)
+        x = {n: getattr(db, n)[rows].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        od = torch.empty((N, H, D), dtype=torch.bfloat16, device=DEV)
+        hd = torch.full_like(hT, 7.0)
+        gdn.gdn_cpr_decode_step(db.shape, x["q"], x["k"], x["v"], x["g"], x["beta"], cache, od, wsd, hT=hd)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(hd), bits(state_of(db.shape, cache))), s

@@ -450,6 +450,70 @@ def main():
                         and torch.equal(c_cont.s_run.view(torch.int32), c_dec.s_run.view(torch.int32))
                         and torch.equal(c_cont.run_log_scale.view(torch.int32), c_dec.run_log_scale.view(torch.int32)))
 
+    # ---- head dim 256 (bf16): the 5 x 2,048 prefill at H = 16, and a decode
+    # step of 64 sequences x 16 heads from a 256-token prefix (no tail fills)
+    log("head dim 256: prefill 5 x 2,048 and a 64-sequence decode step")
+    D2, N2 = 256, 64
+    shape2 = gdn.LayerShape(H, D2, D2, C, torch.bfloat16)
+    s2 = to_dev(make_batch(210, [2048] * 5, H, D2, D2, "bf16"))
+    ws2 = gdn.alloc_workspace(shape2, N_pre, T, gdn.GDN_OP_PREFILL, dev)
+    c2 = gdn.alloc_cache(shape2, N_pre, dev)
+    o2 = torch.empty((T, H, D2), dtype=torch.bfloat16, device=dev)
+    run2 = lambda: gdn.gdn_cpr_prefill(shape2, s2["q"], s2["k"], s2["v"], s2["g"], s2["beta"], s2["cu"], None,
+                                       c2, o2, ws2)
+    run2()
+    torch.cuda.synchronize()
+    ta, tb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ta.record(stream)
+    for _ in range(5):
+        run2()
+    tb.record(stream)
+    torch.cuda.synchronize()
+    pre2_ms = ta.elapsed_time(tb) / 5
+    del ws2, c2, o2, s2
+    b2d = make_batch(211, [256 + 8] * N2, H, D2, D2, "bf16")
+    d2 = to_dev(b2d)
+    rows2 = (torch.from_numpy(b2d.cu_seqlens[:-1].astype(np.int64)).to(dev)[None, :]
+             + torch.arange(256, 264, device=dev)[:, None])
+    dec2 = {n: d2[n][rows2].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    p2 = to_dev(b2d.truncate([256] * N2))
+    c2d = gdn.alloc_cache(shape2, N2, dev)
+    ws2 = gdn.alloc_workspace(shape2, N2, 256 * N2, gdn.GDN_OP_PREFILL, dev)
+    o2 = torch.empty((256 * N2, H, D2), dtype=torch.bfloat16, device=dev)
+    gdn.gdn_cpr_prefill(shape2, p2["q"], p2["k"], p2["v"], p2["g"], p2["beta"], p2["cu"], None, c2d, o2, ws2)
+    del ws2, o2, p2, d2
+    ws2d = gdn.alloc_workspace(shape2, N2, 0, gdn.GDN_OP_DECODE, dev)
+    o2d = torch.empty((N2, H, D2), dtype=torch.bfloat16, device=dev)
+    dec2_call = lambda j: gdn.gdn_cpr_decode_step(shape2, dec2["q"][j], dec2["k"][j], dec2["v"][j], dec2["g"][j],
+                                                  dec2["beta"][j], c2d, o2d, ws2d)
+    dec2_call(0)
+    torch.cuda.synchronize()
+    ta.record(stream)
+    for j in range(1, 8):
+        dec2_call(j)
+    tb.record(stream)
+    torch.cuda.synchronize()
+    dec2_ms = ta.elapsed_time(tb) / 7
+    dec2_bytes = N2 * H * (2 * D2 * D2 * 4 + 2 * 4 + 3 * D2 * 2 + 2 * 2 + D2 * 2 + (2 * D2 + 2) * 2)
+    del c2d, ws2d, dec2
+    flops2 = 7.0 * D2 * D2 * T * H
+    head_dim_256 = {
+        "prefill": {"workload": "5 x 2048 tokens, H = 16, d_k = d_v = 256, bf16", "ms": round(pre2_ms, 4),
+                    "tokens_per_s": round(T / (pre2_ms / 1e3), 1),
+                    "roofline": {"what": "the whole prefill call against the scan's fp32 work (7 d^2 per token-head)",
+                                 "bound": "alu", "algorithmic_flop": flops2,
+                                 "achieved": round(flops2 / (pre2_ms / 1e3) / 1e12, 3), "peak": PEAK_F32,
+                                 "unit": "TFLOP/s",
+                                 "frac": round(flops2 / (pre2_ms / 1e3) / 1e12 / PEAK_F32, 4),
+                                 "frac_vs_nonpacked_issue_peak":
+                                     round(flops2 / (pre2_ms / 1e3) / 1e12 / PEAK_VALU_F32_NONPACKED, 4)}},
+        "decode": {"workload": "64 sequences x 1 token, H = 16, d_k = d_v = 256, 256-token prefix (no resync)",
+                   "ms": round(dec2_ms, 5), "tokens_per_s": round(N2 / (dec2_ms / 1e3), 1),
+                   "roofline": {"bound": "hbm", "algorithmic_bytes_per_call": dec2_bytes,
+                                "achieved": round(dec2_bytes / (dec2_ms / 1e3) / 1e9, 1), "peak": PEAK_HBM,
+                                "unit": "GB/s", "frac": round(dec2_bytes / (dec2_ms / 1e3) / 1e9 / PEAK_HBM, 4),
+                                "note": "whole decode call (the empty resync pass included)"}}}
+
     # ---- trainer forward + backward, 1 x 10,240 tokens
     log("fwd_bwd: 1 x 10,240 tokens")
     b_tr, _, _, _ = workload("train_1x10240")
@@ -675,6 +739,7 @@ def main():
                          "ms": round(cont_ms, 5), "tokens_per_s": round(256 * n_tok / (cont_ms / 1e3), 1),
                          "four_decode_steps_ms": round(dec4_ms, 5),
                          "equals_four_decode_steps_bitwise": cont_bitwise},
+        "head_dim_256": head_dim_256,
         "comparators": cmp_res,
         "parity": {"decode_o_equals_prefill_o_bitwise": parity_o,
                    "decode_state_equals_prefill_state_bitwise": parity_s},

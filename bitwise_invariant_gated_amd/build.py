@@ -62,7 +62,7 @@ def check_dpp_hazards(asm_text: str) -> list:
         parts = t.split(None, 1)
         op = parts[0]
         args = [a.strip() for a in parts[1].split(",")] if len(parts) > 1 else []
-        if op.startswith("v_fmac_f32_dpp") and len(args) >= 2:
+        if "_dpp" in op and len(args) >= 2:  # the DPP source is src0
             src = regs(args[1].split()[0])
             waits = 0
             for ws, wrote in reversed(recent):
@@ -84,8 +84,30 @@ def check_dpp_hazards(asm_text: str) -> list:
     return bad
 
 
+# kernels on the bf16 hot paths (prefill, decode, continuation, fwd_bwd), by
+# mangled-name fragment; register spills there cost a scratch set-up per
+# launch and memory traffic per spill, so the build rejects them
+HOT_KERNELS = ("k_scanIN3cpr4Bf16", "k_chain_scan_bf16", "k_decodeIN3cpr4Bf16", "k_resync_bf16",
+               "k_cont_headIN3cpr4Bf16", "k_chunk_local_prefill_bf16", "k_chain_prefill_bf16", "k_bwd_local_bf16",
+               "k_bwd_chain_bf16", "k_bwd_state_bf16", "k_bwd_grads_bf16", "k_plan")
+
+
+def check_spills(asm_text: str, hot=HOT_KERNELS) -> list:
+    """(kernel, spilled VGPRs) for every hot kernel whose metadata records
+    VGPR spills."""
+    import re
+    bad = []
+    for m in re.finditer(r"\.name:\s+(\S+)\n(.*?)\.wavefront_size", asm_text, re.S):
+        name, body = m.group(1), m.group(2)
+        sp = re.search(r"\.vgpr_spill_count:\s+(\d+)", body)
+        if sp and int(sp.group(1)) > 0 and any(h in name for h in hot):
+            bad.append((name, int(sp.group(1))))
+    return bad
+
+
 def check_isa(verbose: bool = True) -> None:
-    """Compile the device code to assembly and check the DPP hazard rule."""
+    """Compile the device code to assembly and check the DPP hazard rule and
+    that no hot kernel spills."""
     import tempfile
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "gdn_cpr.s")
@@ -101,8 +123,12 @@ def check_isa(verbose: bool = True) -> None:
     if bad:
         raise RuntimeError(f"DPP hazard in generated code ({len(bad)}): " + "; ".join(
             f"{fn} line {no}: {t}" for fn, no, t in bad[:5]))
+    spills = check_spills(text)
+    if spills:
+        raise RuntimeError("register spills in hot kernels: " + "; ".join(f"{n} ({k})" for n, k in spills))
     if verbose:
-        print(f"ISA check: {n_dpp} v_fmac_f32_dpp instructions, no VALU-write -> DPP-read hazard")
+        print(f"ISA check: {n_dpp} v_fmac_f32_dpp instructions, no VALU-write -> DPP-read hazard, "
+              "no spills in the hot kernels")
 
 
 def build(verbose: bool = True) -> str:

@@ -68,6 +68,30 @@ __device__ __forceinline__ BufRsrc buf_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// A lane's part of one state column of a [rows][DV] fp32 state at `base`:
+// rows k0 .. k0 + KL - 1 of column col, through one buffer resource, so the
+// lane offset is one VGPR and every row offset is a wave-uniform constant
+// (no 64-bit address per row).
+template <int KL, int DV>
+__device__ __forceinline__ void load_state_col(float (&s)[KL], const float* base, uint32_t bytes, int k0, int col) {
+  const BufRsrc r = buf_rsrc(base, bytes);
+  const uint32_t off = (uint32_t)(k0 * DV + col) * 4u;
+#pragma unroll
+  for (int ii = 0; ii < KL; ++ii)
+    s[ii] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, ii * DV * 4, 0));
+}
+
+// stores scale * s (scale = 1: s itself; the product is exact then)
+template <int KL, int DV>
+__device__ __forceinline__ void store_state_col(float* base, uint32_t bytes, const float (&s)[KL], int k0, int col,
+                                                float scale) {
+  const BufRsrc r = buf_rsrc(base, bytes);
+  const uint32_t off = (uint32_t)(k0 * DV + col) * 4u;
+#pragma unroll
+  for (int ii = 0; ii < KL; ++ii)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale * s[ii]), r, off, ii * DV * 4, 0);
+}
+
 __device__ __forceinline__ float lane_bcast(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }

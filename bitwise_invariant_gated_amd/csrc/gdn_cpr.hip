@@ -618,7 +618,7 @@ __global__ __launch_bounds__(256, DK > 128 ? 1 : 3) void k_resync_bf16(const Dec
   chunk_local_bf16<DK, DV>(sm, prod, a.gamn + ps);
   __syncthreads();  // the slot and Gamma_n, written by every wave, are read below
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int jw = wave; jw < NW; jw += 4) {
+  auto pass = [&](int jw) {
     const int jb0 = jw * NT;
     const size_t SS = (size_t)DK * DV;
     mfma::f32x4 S[DK / 16][NT];
@@ -627,6 +627,12 @@ __global__ __launch_bounds__(256, DK > 128 ? 1 : 3) void k_resync_bf16(const Dec
     store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
     store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
     if (a.hT && (flag & 2)) store_state_tiles<DK, DV, NT>(a.hT + sh * SS, S, jb0, lane);
+  };
+  if constexpr (NW <= 4) {
+    if (wave < NW) pass(wave);
+  } else {
+#pragma unroll 1
+    for (int jw = wave; jw < NW; jw += 4) pass(jw);
   }
   if (threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
 }
@@ -656,7 +662,7 @@ __device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i,
 
   const float* B = a.bnd + ((size_t)slot * H + h) * SS;
   float s[KL];
-  if constexpr (kAgentBnd) {
+  {
     // rows 4q .. 4q+3 of column col sit 256 q bytes after rows 0 .. 3
     static_assert(bnd_index<DK>(4, 0) == 64 && bnd_index<DK>(16, 0) == 256, "row groups 256 bytes apart");
     const BufRsrc rb = buf_rsrc(B, (uint32_t)(SS * sizeof(float)));
@@ -664,16 +670,7 @@ __device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i,
 #pragma unroll
     for (int q = 0; q < KL / 4; ++q) {  // rows k0 + 4q .. k0 + 4q+3 of column col: one 16-byte load
       const mfma::f32x4 x = __builtin_bit_cast(
-          mfma::f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col_off, 256 * q, kAuxAgent));
-      s[4 * q] = x[0];
-      s[4 * q + 1] = x[1];
-      s[4 * q + 2] = x[2];
-      s[4 * q + 3] = x[3];
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < KL / 4; ++q) {  // rows k0 + 4q .. k0 + 4q+3 of column col: one 16-byte load
-      const mfma::f32x4 x = *reinterpret_cast<const mfma::f32x4*>(B + bnd_index<DK>(k0 + 4 * q, col));
+          mfma::f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col_off, 256 * q, kAgentBnd ? kAuxAgent : 0));
       s[4 * q] = x[0];
       s[4 * q + 1] = x[1];
       s[4 * q + 2] = x[2];
@@ -713,15 +710,10 @@ __device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i,
     // log-scale lg), its tokens the tail
     const size_t ch = cache_row(a.slot, i) * H + h;
     float* R = a.s_run + ch * SS;
-#pragma unroll
-    for (int ii = 0; ii < KL; ++ii) R[(size_t)ii * DV + k0 * DV + col] = s[ii];
+    store_state_col<KL, DV>(R, (uint32_t)(SS * 4), s, k0, col, 1.f);
     if (z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
-    if (a.hT) {  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
-      float* F = a.hT + ((size_t)i * H + h) * SS;
-      const float e = scale_of_log(lg);
-#pragma unroll
-      for (int ii = 0; ii < KL; ++ii) F[(size_t)ii * DV + k0 * DV + col] = e * s[ii];
-    }
+    if (a.hT)  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
+      store_state_col<KL, DV>(a.hT + ((size_t)i * H + h) * SS, (uint32_t)(SS * 4), s, k0, col, scale_of_log(lg));
     T* tv = (T*)a.tail_v + ch * Cl * DV;
     if (lane < WC)
       for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
@@ -986,8 +978,7 @@ __global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_decode(const Deco
   const T g_app = ((const T*)a.g)[sh], b_app = ((const T*)a.beta)[sh];
   float* R = a.s_run + ch * SS;
   float s[KL];
-#pragma unroll
-  for (int ii = 0; ii < KL; ++ii) s[ii] = R[(size_t)ii * DV + cl.k0 * DV + col];
+  load_state_col<KL, DV>(s, R, (uint32_t)(SS * 4), cl.k0, col);
   float lg_next = lg;
   const float out = token_step_at<D, DK>(s, lg_next, kp + kr * DK, qp + kr * DK, D::load(&g_app, 0),
                                          D::load(&b_app, 0), D::load(&v_app, 0), cl.lane);
@@ -1004,14 +995,9 @@ __global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_decode(const Deco
   }
   const bool full = (tl + 1 == Cl);
   if (!full) {
-#pragma unroll
-    for (int ii = 0; ii < KL; ++ii) R[(size_t)ii * DV + cl.k0 * DV + col] = s[ii];
-    if (a.hT) {  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
-      float* F = a.hT + sh * SS;
-      const float e = scale_of_log(lg_next);
-#pragma unroll
-      for (int ii = 0; ii < KL; ++ii) F[(size_t)ii * DV + cl.k0 * DV + col] = e * s[ii];
-    }
+    store_state_col<KL, DV>(R, (uint32_t)(SS * 4), s, cl.k0, col, 1.f);
+    if (a.hT)  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
+      store_state_col<KL, DV>(a.hT + sh * SS, (uint32_t)(SS * 4), s, cl.k0, col, scale_of_log(lg_next));
   }
   if (tid == 0) {
     a.tail_len[ch] = full ? 0 : tl + 1;
@@ -1094,19 +1080,15 @@ __global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_cont_head(const C
   float* R = a.s_run + ch * SS;
   if (L == 0) {  // nothing new: the final state is the cached one
     if (a.hT) {
-      const float e = scale_of_log(lg);
-#pragma unroll
-      for (int ii = 0; ii < KL; ++ii) {
-        const size_t e_off = (size_t)ii * DV + cl.k0 * DV + col;
-        a.hT[sh * SS + e_off] = e * R[e_off];
-      }
+      float x[KL];
+      load_state_col<KL, DV>(x, R, (uint32_t)(SS * 4), cl.k0, col);
+      store_state_col<KL, DV>(a.hT + sh * SS, (uint32_t)(SS * 4), x, cl.k0, col, scale_of_log(lg));
     }
     return;
   }
   if (nh == 0) return;  // the body prefill writes the final state
   float s[KL];
-#pragma unroll
-  for (int ii = 0; ii < KL; ++ii) s[ii] = R[(size_t)ii * DV + cl.k0 * DV + col];
+  load_state_col<KL, DV>(s, R, (uint32_t)(SS * 4), cl.k0, col);
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
@@ -1138,13 +1120,9 @@ __global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_cont_head(const C
   }
   const bool full = (tl + nh == Cl);
   if (!full) {
-#pragma unroll
-    for (int ii = 0; ii < KL; ++ii) R[(size_t)ii * DV + cl.k0 * DV + col] = s[ii];
-    if (a.hT) {  // the head is the whole segment (nh == L): exp(lg) N is the final state
-      const float e = scale_of_log(lg);
-#pragma unroll
-      for (int ii = 0; ii < KL; ++ii) a.hT[sh * SS + (size_t)ii * DV + cl.k0 * DV + col] = e * s[ii];
-    }
+    store_state_col<KL, DV>(R, (uint32_t)(SS * 4), s, cl.k0, col, 1.f);
+    if (a.hT)  // the head is the whole segment (nh == L): exp(lg) N is the final state
+      store_state_col<KL, DV>(a.hT + sh * SS, (uint32_t)(SS * 4), s, cl.k0, col, scale_of_log(lg));
   }
   if (tid == 0) {
     a.tail_len[ch] = full ? 0 : tl + nh;

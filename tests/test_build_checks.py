@@ -1,7 +1,8 @@
-"""CPU checks of the build's ISA hazard checker (it must flag a DPP source
-written by a VALU instruction fewer than two wait states earlier)."""
+"""CPU checks of the build's ISA checks: the hazard checker must flag a DPP
+source written by a VALU instruction fewer than two wait states earlier, and
+the spill check must flag a hot kernel whose metadata records spills."""
 
-from bitwise_invariant_gated_amd.build import check_dpp_hazards
+from bitwise_invariant_gated_amd.build import check_dpp_hazards, check_spills
 
 
 def test_flags_valu_write_right_before_dpp_read():
@@ -48,3 +49,30 @@ def test_register_ranges_count_as_writes():
     v_fmac_f32_dpp v1, v5, v2 row_newbcast:0 row_mask:0xf bank_mask:0xf
 """
     assert len(check_dpp_hazards(asm)) == 1
+
+
+def test_flags_mul_dpp_too():
+    asm = """k:
+    v_lshlrev_b32_e32 v5, 16, v4
+    v_mul_f32_dpp v1, v5, v2 row_newbcast:0 row_mask:0xf bank_mask:0xf
+"""
+    assert len(check_dpp_hazards(asm)) == 1
+
+
+def test_spill_check_names_hot_kernels_only():
+    meta = """    .name:           _ZN12_GLOBAL__N_113k_resync_bf16ILi128ELi128EEEvNS_10DecodeArgsE
+    .private_segment_fixed_size: 224
+    .vgpr_count:     168
+    .vgpr_spill_count: 55
+    .wavefront_size: 64
+    .name:           _ZN12_GLOBAL__N_16k_scanIN3cpr3F32ELi128ELi128EEEvNS_11PrefillArgsE
+    .vgpr_count:     168
+    .vgpr_spill_count: 25
+    .wavefront_size: 64
+    .name:           _ZN12_GLOBAL__N_16k_scanIN3cpr4Bf16ELi128ELi128EEEvNS_11PrefillArgsE
+    .vgpr_count:     166
+    .vgpr_spill_count: 0
+    .wavefront_size: 64
+"""
+    bad = check_spills(meta)
+    assert [k for _, k in bad] == [55] and "k_resync_bf16" in bad[0][0]

@@ -60,6 +60,7 @@ CASES = [
     ("bf16", 128, 128, 16, 64, (80, 7)),   # 1,024 product slots: 64 sequences per resync group
     ("f32", 64, 64, 4, 64, (400, 3)),      # 1,365 slots: 341 sequences per group
     ("bf16", 128, 64, 4, 32, (20, 19)),    # one group, C = 32
+    ("bf16", 256, 256, 8, 64, (70, 5)),    # 512 slots of 128 KiB: 64 sequences per group
 ]
 
 

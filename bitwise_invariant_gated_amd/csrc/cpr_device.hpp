@@ -908,13 +908,24 @@ __device__ __forceinline__ void inverse_below_diag(float (*A)[LDA], int wave, in
 
 // Caller staged the chunk and synchronised; 256 threads.  Writes the slot
 // (SlotB layout) and *gamn.
-template <int DK, int DV>
+// kAux: the cache policy of the slot stores.  0: plain stores, for a slot
+// that a later launch reads.  Otherwise the buffer instructions' cache-policy
+// bits (and Gamma_n an atomic store) at agent scope, for a slot that another
+// work-group of the same launch reads, possibly on another XCD.
+template <int DK, int DV, int kAux = 0>
 __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t* __restrict__ slot,
                                                  float* __restrict__ gamn) {
   using namespace mfma;
   constexpr int C = kChunk;
   typedef SlotB<DK, DV> Sl;
   static_assert(DK % 32 == 0 && DV % 32 == 0, "head dims are multiples of 32");
+  const BufRsrc slot_r = buf_rsrc(slot, (uint32_t)Sl::bytes);
+  auto put = [&](size_t off, u32x4 x) {
+    if constexpr (kAux == 0)
+      *reinterpret_cast<u32x4*>(slot + off) = x;
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(x, slot_r, (uint32_t)off, 0, kAux);
+  };
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   // gamma = left-to-right fp32 cumsum of g (wave 0, in registers), while
@@ -977,7 +988,7 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
         const int r = 32 * kb + 16 * (w >> 1) + 4 * g + 2 * (w & 1);
         out[w] = pack2(sm.e[r] * __uint_as_float(raw[w] << 16), sm.e[r + 1] * __uint_as_float(raw[w] & 0xffff0000u));
       }
-      *reinterpret_cast<u32x4*>(slot + Sl::oKF + ((size_t)f * 64 + lane) * 16) = out;
+      put(Sl::oKF + ((size_t)f * 64 + lane) * 16, out);
     }
   }
   __syncthreads();
@@ -1029,7 +1040,7 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
       }
       const u32x4 out = {pack2(-acc[0][0], -acc[0][1]), pack2(-acc[0][2], -acc[0][3]), pack2(-acc[1][0], -acc[1][1]),
                          pack2(-acc[1][2], -acc[1][3])};
-      *reinterpret_cast<u32x4*>(slot + Sl::oWF + ((size_t)(p * (C / 16) + tm) * 64 + lane) * 16) = out;
+      put(Sl::oWF + ((size_t)(p * (C / 16) + tm) * 64 + lane) * 16, out);
     }
   }
   // U tiles (tm, jt), jt = 2 p, 2 p + 1
@@ -1051,10 +1062,15 @@ __device__ __forceinline__ void chunk_local_bf16(ChunkLdsB<DK, DV>& sm, uint8_t*
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<f32x4*>(slot + Sl::oU + ((size_t)((2 * p + h) * (C / 16) + tm) * 64 + lane) * 16) = acc[h];
+        put(Sl::oU + ((size_t)((2 * p + h) * (C / 16) + tm) * 64 + lane) * 16, __builtin_bit_cast(u32x4, acc[h]));
     }
   }
-  if (tid == 0) *gamn = sm.Gam[C - 1];
+  if (tid == 0) {
+    if constexpr (kAux == 0)
+      *gamn = sm.Gam[C - 1];
+    else
+      __hip_atomic_store(gamn, sm.Gam[C - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Boundary advance on the bf16 path for NT 16-column blocks of the state,

@@ -739,29 +739,37 @@ __global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// boundary chain and in-chunk scan in one launch (bf16 inputs)
+// chunk products, boundary chain and in-chunk scan in one launch (bf16 inputs)
 //
-// The scan of chunk c needs only the boundary B_c, so it can start as soon as
-// the chain has produced B_c instead of after the whole chain.  Every
-// work-group takes a ticket from an atomic counter when it starts, so ticket
-// order is start order.  Tickets 0 .. n_chain-1 are chain items, one per
-// (sequence, head, 64-column block): the chain of k_chain_prefill_bf16 with
-// 4 waves x 16 columns and a one-buffer LDS stage, which publishes, after
-// each step, how many boundaries of its columns have reached memory.  Later
-// tickets are scan items: 4 waves, each one (chunk, head, 64-column half)
-// unit, units in chunk-major order, each waiting until its chain item has
-// published its boundary.  Every chain item started before any scan item and
-// waits on nothing, so every wait ends; the wait is bounded all the same.
-// Boundaries travel with agent-scope stores and loads (coherent across the
-// XCDs, no cache-wide maintenance); the count is published only after the
+// The chain step of chunk c needs only chunk c's products, and the scan of
+// chunk c only the boundary B_c, so each can start as soon as its input is
+// in memory instead of after the whole stage before it.  Every work-group
+// takes a ticket from an atomic counter when it starts, so ticket order is
+// start order.  Tickets 0 .. n_cp-1 are chunk-product items, one per (chunk
+// slot in chunk-major order, head; partial chunks have none), which publish
+// a flag once their product slot has reached memory.  The next n_chain
+// tickets are chain items, one per (sequence, head, 64-column block): the
+// chain of k_chain_prefill_bf16 with 4 waves x 16 columns and a one-buffer
+// LDS stage, which waits for each chunk's flag before loading its products
+// and publishes, after each step, how many boundaries of its columns have
+// reached memory.  Later tickets are scan items: 4 waves, each one (chunk,
+// head, 64-column half) unit, units in chunk-major order, each waiting until
+// its chain item has published its boundary.  Every item waits only on items
+// with lower tickets, which started before it and never wait on it, so every
+// wait ends; the waits are bounded all the same.  Products and boundaries
+// travel with agent-scope stores and loads (coherent across the XCDs, no
+// cache-wide maintenance); a flag or count is published only after the
 // stores are complete.  No value depends on the order in which items run.
 struct FusedArgs {
   const int32_t* order;  // [A] chunk slots, chunk-major
   int32_t* ticket;       // zeroed by the plan kernel
   int32_t* ready;        // [N * H * NZ * kReadyStride] boundaries published per chain item (one per
                          // kReadyStride words), zeroed by the plan kernel
-  int32_t* timeout;      // set to 1 if a scan unit ever stops waiting (never expected)
-  int32_t n_chain;       // chain items (tickets 0 .. n_chain - 1)
+  int32_t* cp_ready;     // [F * H] 1 once a (full chunk, head)'s products are in memory (zeroed by the
+                         // plan kernel), or null: the products come from an earlier launch
+  int32_t* timeout;      // set to 1 if a wait ever gives up (never expected)
+  int32_t n_cp;          // chunk-product items (tickets 0 .. n_cp - 1)
+  int32_t n_chain;       // chain items (the next n_chain tickets)
 };
 
 constexpr int kFusedChainCols = 64;  // state columns per chain item (= per scan unit)
@@ -779,14 +787,17 @@ __device__ __forceinline__ int read_count(const int32_t* p) {
   return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// waits (bounded) until *p >= need; false if it gave up
+// waits (bounded) until *p >= need; false if it gave up.  The default polls
+// every ~8,000 cycles (3 to 4 us; a chain step takes about as long), so that
+// thousands of waiting scan waves add little memory traffic; the chain's wait
+// for chunk products (a few waves, on its critical path) polls every ~200
+// cycles.  Either way the bound is about a second.
+template <int kSleep = 127>
 __device__ __forceinline__ bool wait_count(const int32_t* p, int need) {
-  // a poll every ~8,000 cycles (3 to 4 us; a chain step takes about as
-  // long), so that thousands of waiting waves add little memory traffic
-  constexpr int kMaxPolls = 1 << 18;  // with the sleeps, about a second
+  constexpr int kMaxPolls = kSleep >= 127 ? 1 << 18 : 1 << 21;
   for (int it = 0; it < kMaxPolls; ++it) {
     if (__builtin_amdgcn_readfirstlane(read_count(p)) >= need) return true;
-    __builtin_amdgcn_s_sleep(127);
+    __builtin_amdgcn_s_sleep(kSleep);
   }
   return false;
 }
@@ -803,7 +814,12 @@ __global__ __launch_bounds__(256, DK > 128 ? 2 : 3) void k_chain_scan_bf16(const
   constexpr int kPerFrag = kFragPieces / kThreads;
   static_assert(kPieces % kThreads == 0 && kFragPieces % kThreads == 0, "staging split");
   static_assert(DV % CB == 0, "column blocks tile d_v");
-  __shared__ u32x4 stage[kPieces];
+  // one LDS block: a chain item's stage or a chunk-product item's arrays (at
+  // d_k = 256 the launch has chain items only)
+  constexpr bool kCP = KeySplit<DK>::kParts == 1;
+  constexpr size_t kStageBytes = (size_t)kPieces * 16, kCpBytes = kCP ? sizeof(ChunkLdsB<DK, DV>) : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStageBytes > kCpBytes ? kStageBytes : kCpBytes];
+  u32x4* const stage = reinterpret_cast<u32x4*>(lds);
   __shared__ float gn_stage;
   __shared__ int32_t ticket_s;
   // the ticket and the wave index are uniform over each wave: reading them
@@ -814,10 +830,33 @@ __global__ __launch_bounds__(256, DK > 128 ? 2 : 3) void k_chain_scan_bf16(const
   __syncthreads();
   const int t = __builtin_amdgcn_readfirstlane(ticket_s);
   const int H = a.H;
-  if (t >= f.n_chain) {
+  if (t < f.n_cp) {
+    // ---- chunk-product item: full chunk slot order[t / H], head t % H
+    if constexpr (kCP) {
+      const int pos = t / H, h = t % H;
+      if (pos >= a.all_base[a.N]) return;
+      const int slot = f.order[pos];
+      if (slot < 0 || slot >= a.all_base[a.N]) return;  // (the plan writes every position in range)
+      const int i = find_seq(a.all_base, a.N, slot);
+      const int c = slot - a.all_base[i];
+      if (c >= (a.end[i] - a.start[i]) / a.Cl) return;  // a partial chunk has no products
+      const size_t tok0 = (size_t)a.start[i] + (size_t)c * a.Cl;
+      const size_t row0 = tok0 * H + h;
+      ChunkLdsB<DK, DV>& sm = *reinterpret_cast<ChunkLdsB<DK, DV>*>(lds);
+      stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const uint16_t*)a.v,
+                               row0, H, (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H, a.Cl);
+      const size_t ps = (size_t)(a.full_base[i] + c) * H + h;
+      chunk_local_bf16<DK, DV, kAuxAgent>(sm, a.prod + ps * Sl::bytes, a.gamn + ps);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slot stores are complete
+      __syncthreads();                                  // and every wave's
+      if (tid == 0) publish_count(f.cp_ready + ps, 1);
+    }
+    return;
+  }
+  if (t >= f.n_cp + f.n_chain) {
     // ---- scan item: one unit per wave (launches at d_k = 256 have chain items only)
     if constexpr (KeySplit<DK>::kParts == 1) {
-      const long u = (long)(t - f.n_chain) * 4 + wave;
+      const long u = (long)(t - f.n_cp - f.n_chain) * 4 + wave;
       const long per_slot = (long)H * NZ;
       if (u >= (long)a.all_base[a.N] * per_slot) return;
       const int pos = (int)(u / per_slot), r = (int)(u % per_slot), h = r / NZ, z = r % NZ;
@@ -832,7 +871,8 @@ __global__ __launch_bounds__(256, DK > 128 ? 2 : 3) void k_chain_scan_bf16(const
     return;
   }
   // ---- chain item
-  const int i = t / (H * NZ), r = t % (H * NZ), h = r / NZ, z = r % NZ;
+  const int tc = t - f.n_cp;
+  const int i = tc / (H * NZ), r = tc % (H * NZ), h = r / NZ, z = r % NZ;
   const int jbg = z * (CB / 16), jb0 = jbg + wave;  // one 16-column tile per wave
   const int L = a.end[i] - a.start[i];
   if (a.skip_empty && L == 0) return;
@@ -843,15 +883,21 @@ __global__ __launch_bounds__(256, DK > 128 ? 2 : 3) void k_chain_scan_bf16(const
   const int abase = a.all_base[i], fbase = a.full_base[i];
   int32_t* const rdy = f.ready + (sh * NZ + z) * kReadyStride;
   auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * Sl::bytes; };
-  auto gamn_of = [&](int c) { return a.gamn[(size_t)(fbase + c) * H + h]; };
+  // chunk c's products, once its chunk-product item has published them; read
+  // at agent scope, since that item may have run on another XCD
+  auto gamn_of = [&](int c) {
+    return __hip_atomic_load(a.gamn + (size_t)(fbase + c) * H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   auto fetch = [&](int c, u32x4 (&rg)[kPer]) {
-    const uint8_t* sp = slot_of(c);
-    const u32x4* fr = reinterpret_cast<const u32x4*>(sp);
-    const u32x4* up = reinterpret_cast<const u32x4*>(sp + Sl::oU) + (size_t)jbg * (C / 16) * 64;
+    if (f.cp_ready && !wait_count<2>(f.cp_ready + (size_t)(fbase + c) * H + h, 1) && lane == 0)
+      atomicExch(f.timeout, 1);
+    const BufRsrc sr = buf_rsrc(slot_of(c), (uint32_t)Sl::bytes);
+    const uint32_t u0 = (uint32_t)(Sl::oU + (size_t)jbg * (C / 16) * 64 * 16);
 #pragma unroll
     for (int m = 0; m < kPer; ++m) {
       const int p = tid + m * kThreads;
-      rg[m] = m < kPerFrag ? fr[p] : up[p - kFragPieces];
+      const uint32_t off = m < kPerFrag ? (uint32_t)p * 16u : u0 + (uint32_t)(p - kFragPieces) * 16u;
+      rg[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, kAuxAgent));
     }
   };
   f32x4 S[DK / 16][1];
@@ -2274,12 +2320,12 @@ PrefillLayout prefill_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   off = align_up(off + sizeof(float) * Fmax * H);
   L.bnd = off;
   off = align_up(off + sizeof(float) * Amax * H * DK * DV);
-  // fused chain + scan launch: chunk-major slot order, per-chain-item counts,
-  // ticket and timeout words
+  // fused launch: chunk-major slot order, per-chain-item counts and
+  // chunk-product flags, ticket and timeout words
   L.order = off;
   off = align_up(off + sizeof(int32_t) * Amax);
-  L.ready = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)N * H * (DV / kFusedChainCols) * kReadyStride);
+  L.ready = off;  // then one chunk-product flag per (full chunk, head)
+  off = align_up(off + sizeof(int32_t) * ((size_t)N * H * (DV / kFusedChainCols) * kReadyStride + Fmax * H));
   L.counters = off;
   off = align_up(off + 2 * sizeof(int32_t));
   L.total = off;
@@ -2457,11 +2503,25 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   constexpr bool kChainOnly = KeySplit<DK>::kParts > 1;
   static_assert(!kChainOnly || kBf16, "d_k = 256 runs on the bf16 path");
   constexpr int NZ = DV / kFusedChainCols;
+  // the fused launch's counts: the chain items', then the chunk-product flags
+  const int n_counts = a.N * a.H * NZ * kReadyStride;
   FusedPlan fp{};
-  if (fused || kChainOnly) fp = FusedPlan{a.order, a.counters, a.ready, a.N * a.H * NZ * kReadyStride};
+  if (fused || kChainOnly) fp = FusedPlan{a.order, a.counters, a.ready, n_counts + (fused ? Fmax * a.H : 0)};
   mark(0, st);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.Cl, a.full_base, a.all_base, fp);
   mark(1, st);
+  if (fused) {
+    // chunk products, chain and scan as one launch: events 2, 3 and 4 follow it
+    const FusedArgs f{a.order, a.counters, a.ready, a.ready + n_counts, a.counters + 1, Amax * a.H,
+                      a.N * a.H * NZ};
+    const long units = (long)Amax * a.H * NZ;
+    const unsigned groups = (unsigned)(f.n_cp + f.n_chain + (units + 3) / 4);
+    if constexpr (kBf16) hipLaunchKernelGGL((k_chain_scan_bf16<DK, DV>), dim3(groups), dim3(256), 0, st, a, f);
+    mark(2, st);
+    mark(3, st);
+    mark(4, st);
+    return launch_status(fn);
+  }
   if (Fmax > 0) {
     if constexpr (kBf16)
       hipLaunchKernelGGL((k_chunk_local_prefill_bf16<DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
@@ -2469,19 +2529,9 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
       hipLaunchKernelGGL((k_chunk_local_prefill<D, DK, DV>), dim3(Fmax, a.H), dim3(256), 0, st, a);
   }
   mark(2, st);
-  if (fused) {
-    // chain and scan as one launch: events 3 and 4 both follow it
-    const FusedArgs f{a.order, a.counters, a.ready, a.counters + 1, a.N * a.H * NZ};
-    const long units = (long)Amax * a.H * NZ;
-    const unsigned groups = (unsigned)(f.n_chain + (units + 3) / 4);
-    if constexpr (kBf16) hipLaunchKernelGGL((k_chain_scan_bf16<DK, DV>), dim3(groups), dim3(256), 0, st, a, f);
-    mark(3, st);
-    mark(4, st);
-    return launch_status(fn);
-  }
   if (a.N > 0) {
     if constexpr (kChainOnly) {
-      const FusedArgs f{a.order, a.counters, a.ready, a.counters + 1, a.N * a.H * NZ};
+      const FusedArgs f{a.order, a.counters, a.ready, nullptr, a.counters + 1, 0, a.N * a.H * NZ};
       hipLaunchKernelGGL((k_chain_scan_bf16<DK, DV>), dim3(f.n_chain), dim3(256), 0, st, a, f);
     } else if constexpr (kBf16) {
       launch_chain_bf16<DK, DV>(a, st);

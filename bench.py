@@ -414,6 +414,40 @@ def main():
     torch.cuda.synchronize()
     dec64_ms = e2.elapsed_time(e3) / 64
 
+    # ---- the same decode call recorded in a HIP graph and replayed (as a
+    # serving loop would run it): a step in which no tail fills, then the
+    # replays' mean over a whole chunk (one resync per sequence)
+    log("decode: one call recorded in a graph, replayed")
+    c_gr = c64.clone()
+    x_gr = {n: dec64[n][0].clone() for n in dec64}
+    run_gr = lambda: gdn.gdn_cpr_decode_step(shape, x_gr["q"], x_gr["k"], x_gr["v"], x_gr["g"], x_gr["beta"], c_gr,
+                                             o_dec, ws_dec)
+    s_side = torch.cuda.Stream()
+    s_side.wait_stream(stream)
+    with torch.cuda.stream(s_side):
+        run_gr()
+    stream.wait_stream(s_side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_gr()
+    torch.cuda.synchronize()
+    graph.replay()  # the cache's tails now hold 2 tokens: the next 62 replays resync nothing
+    torch.cuda.synchronize()
+    e2.record(stream)
+    for _ in range(32):
+        graph.replay()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    dec_graph_ms = e2.elapsed_time(e3) / 32
+    e2.record(stream)
+    for _ in range(64):
+        graph.replay()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    dec_graph64_ms = e2.elapsed_time(e3) / 64
+    del graph, c_gr
+
     # ---- multi-token decode through the continuation call: 4 tokens for each
     # of the 256 cached sequences per call (from the cache after the 64-step
     # series), against 4 single-token decode steps on a copy of that cache
@@ -728,7 +762,11 @@ def main():
                                 "frac": round(dec_bytes / (float(np.mean(dstep_ms)) / 1e3) / 1e9 / PEAK_HBM, 4)},
                    "whole_call_GBps": round(dec_bytes / (dec_avg / 1e3) / 1e9, 1),
                    "mean_over_64_steps_ms": round(dec64_ms, 5),
-                   "mean_over_64_steps_tokens_per_s": round(N_dec / (dec64_ms / 1e3), 1)},
+                   "mean_over_64_steps_tokens_per_s": round(N_dec / (dec64_ms / 1e3), 1),
+                   "graph_replay": {"what": "one decode call captured in a HIP graph and replayed",
+                                    "ms_no_resync": round(dec_graph_ms, 5),
+                                    "mean_over_64_replays_ms": round(dec_graph64_ms, 5),
+                                    "no_resync_tokens_per_s": round(N_dec / (dec_graph_ms / 1e3), 1)}},
         "fwd_bwd": {"workload": "1 x 10240 tokens", "ms": round(float(np.median(fb_ms)), 4),
                     "tokens_per_s": round(T4 / (float(np.median(fb_ms)) / 1e3), 1),
                     "streams": 2,

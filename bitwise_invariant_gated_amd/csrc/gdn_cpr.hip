@@ -2484,11 +2484,14 @@ void launch_resync_bf16(const DecodeArgs& a, int n_seqs, hipStream_t st) {
 // the chip's work-group slots to the scan; other prefills run the chain and
 // the scan as two launches.  Both give the same bits.
 constexpr long kFusedMaxChainItems = 512;
+// and whose longest chain (at most T / C steps of a few microseconds) ends well
+// inside the bounded waits of its scan units (about a second)
+constexpr long kFusedMaxChainSteps = 1L << 16;
 
 template <int DK, int DV>
-bool use_fused(const PrefillArgs& a) {
+bool use_fused(const PrefillArgs& a, int64_t T) {
   return KeySplit<DK>::kParts == 1 && a.order && a.all_chunks == 0 && a.N <= kFusedMaxSeqs &&
-         (long)a.N * a.H * (DV / kFusedChainCols) <= kFusedMaxChainItems;
+         (long)a.N * a.H * (DV / kFusedChainCols) <= kFusedMaxChainItems && T / a.Cl <= kFusedMaxChainSteps;
 }
 
 template <class D, int DK, int DV>
@@ -2496,7 +2499,7 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   const int Fmax = (int)(T / a.Cl);
   const int Amax = Fmax + a.N;
   constexpr bool kBf16 = std::is_same<D, Bf16>::value;
-  const bool fused = kBf16 && use_fused<DK, DV>(a);
+  const bool fused = kBf16 && use_fused<DK, DV>(a, T);
   // at d_k = 256 the chain runs as the chain items of the fused kernel alone
   // (its one-buffer stage fits the LDS where the two-buffer chain's does not),
   // then the scan

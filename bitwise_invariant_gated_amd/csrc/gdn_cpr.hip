@@ -1,16 +1,22 @@
-// CPR Gated DeltaNet layer: HIP kernels for gfx950 and the C ABI (gdn_cpr.h).
+// CPR Gated DeltaNet layer for gfx950: host side and the C ABI (gdn_cpr.h).
+// The kernels live in prefill_kernels.hpp, decode_kernels.hpp,
+// comparator_kernels.hpp and backward_kernels.hpp.
 //
 // Prefill (per call, all on the caller's stream):
 //   k_plan            per-sequence chunk counts -> prefix sums (varlen plan)
-//   k_chunk_local     chunk products of every full chunk, all in parallel
-//   k_chain           boundary states: sequential over each sequence's full
-//                     chunks, parallel over sequences x heads x column blocks
-//   k_scan            per-token recurrence inside every chunk, all chunks in
-//                     parallel, each from its boundary state; writes o, the
-//                     final state and the decode tail
+//   k_chain_scan_bf16 bf16 batches of up to 128 sequences: one launch whose
+//                     work-groups are, in ticket order, the chunk products
+//                     of every full chunk, the boundary chains and the
+//                     in-chunk scans, each starting when its input is ready
+//   otherwise         k_chunk_local (chunk products of every full chunk, all
+//                     in parallel), k_chain (boundary states: sequential over
+//                     each sequence's full chunks, parallel over sequences x
+//                     heads x column blocks), k_scan (per-token recurrence
+//                     inside every chunk from its boundary state; writes o,
+//                     the final state and the decode tail)
 // Decode step:
-//   k_decode          per-token step on the running state (one work item per
-//                     sequence x head), tail append, resync flag
+//   k_decode          per-token step on the running state (one work-group
+//                     per sequence x head), tail append, resync flag
 //   k_resync_bf16 (bf16; fp32: k_chunk_local_resync, k_chain_resync)
 //                     for the (sequence, head) pairs whose tail just filled:
 //                     the same chunk products and boundary advance as prefill
@@ -30,2207 +36,9 @@
 #include <type_traits>
 
 #include "../../include/gdn_cpr.h"
-#include "cpr_backward.hpp"
-#include "cpr_backward_bf16.hpp"
-#include "cpr_device.hpp"
-
-using namespace cpr;
+#include "backward_kernels.hpp"
 
 namespace {
-
-// C is the row count of the chunk machinery (chunk-product slots, MFMA tiles,
-// LDS arrays): 64.  The layer's chunk length Cl (the boundary and
-// resynchronisation period, 16, 32 or 64) is a runtime argument: a chunk of
-// Cl tokens fills the first Cl rows of a 64-row slot and the other rows are
-// identity padding (k = v = 0, g = beta = 0), which adds exact zeros to every
-// product and leaves the cumulative decay unchanged, so the real rows'
-// values are those of a Cl-row computation.
-constexpr int C = kChunk;
-constexpr int kChainCols = 32;  // state columns per boundary-chain work item
-// cache-policy bits of a buffer access with agent (device) scope coherence
-// (SC1): the access is coherent with every other work-group of the launch
-// whatever its XCD, with no cache-wide write-back or invalidate
-constexpr int kAuxAgent = 16;
-
-// ---------------------------------------------------------------------------
-// kernel arguments
-
-struct PrefillArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* g;
-  const void* beta;
-  const int32_t* start;  // [N] first token row of each sequence
-  const int32_t* end;    // [N] one past its last token row (cu_seqlens + 1 for a plain prefill)
-  int32_t skip_empty;    // 1: a sequence with no tokens leaves its cache untouched
-  const int32_t* slot;   // [N] cache row of sequence i, or null (row i)
-  int32_t h0_slotted;    // 1: h0 is indexed by cache row (h0 = the cache's s_bnd)
-  int32_t all_chunks;    // 1 (comparator): products exist for every chunk slot, partial ones zero-padded;
-                         // the chain runs over all of them and writes only the final state to s_bnd
-  const float* h0;
-  float* s_bnd;
-  float* s_run;
-  void* tail_k;
-  void* tail_v;
-  void* tail_g;
-  void* tail_beta;
-  int32_t* tail_len;
-  float* lgs;  // [rows, H] log-scale of s_run (the cache's run_log_scale), or null
-  float* hT;   // [N, H, DK, DV] final state exp(lg) N of every sequence (batch order), or null
-  void* o;
-  int32_t* full_base;  // [N+1] prefix sums of full chunks per sequence
-  int32_t* all_base;   // [N+1] prefix sums of all chunks (full + partial)
-  uint8_t* prod;       // [F_max*H] chunk-product slots of prod_slot_bytes
-  float* gamn;         // [F_max*H]
-  float* bnd;          // [A_max*H][DK][DV] state at the start of every chunk
-  int32_t* order;      // [A_max] fused launch: chunk-major slot order (workspace)
-  int32_t* ready;      // [N*H*NZ*kReadyStride] fused launch: published boundary counts (workspace)
-  int32_t* counters;   // [2] fused launch: ticket, timeout (workspace)
-  int32_t N;
-  int32_t H;
-  int32_t Hk;  // heads of q and k
-  int32_t G;   // value heads per key head, H / Hk
-  int32_t Cl;  // chunk length
-};
-
-struct DecodeArgs {
-  const int32_t* slot;  // [N] cache row of sequence i, or null (row i)
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* g;
-  const void* beta;
-  float* s_bnd;
-  float* s_run;
-  void* tail_k;
-  void* tail_v;
-  void* tail_g;
-  void* tail_beta;
-  int32_t* tail_len;
-  float* lgs;  // [rows, H] log-scale of s_run, or null (written 0 when s_run becomes a boundary)
-  float* hT;   // [N, H, DK, DV] state after the step (batch order), or null
-  void* o;
-  int32_t* flag;  // [N*H] bit 0: this pair resynchronises in this step; bit 1: the resync also writes hT
-  uint8_t* prod;  // chunk-product slots of prod_slot_bytes, one per pair of a resync launch
-  float* gamn;    // one per product slot
-  int32_t seq0;   // resync launches: the grid's sequence 0 is sequence seq0 of the batch
-  int32_t N;
-  int32_t H;
-  int32_t Hk;  // heads of q and k
-  int32_t G;   // value heads per key head, H / Hk
-  int32_t Cl;  // chunk length (rows per cache tail)
-};
-
-template <int DK, int DV>
-__host__ __device__ constexpr size_t prod_floats() {
-  return (size_t)C * DK + (size_t)C * DV + (size_t)DK * C;
-}
-
-// bytes of one chunk-product slot: fp32 W, U, K~^T on the fp32 path; bf16
-// Wneg and K~^T plus fp32 U on the bf16 (MFMA) path
-__host__ __device__ constexpr size_t prod_slot_bytes(bool bf16, int DK, int DV) {
-  return bf16 ? (size_t)C * DK * 2 + (size_t)DK * C * 2 + (size_t)C * DV * 4
-              : ((size_t)C * DK + (size_t)C * DV + (size_t)DK * C) * 4;
-}
-
-// largest i in [0, N) with base[i] <= slot (slot < base[N] assumed)
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ base, int N, int slot) {
-  int lo = 0, hi = N;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (base[mid] <= slot)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
-// cache row of batch entry i (slot-indexed caches)
-__device__ __forceinline__ size_t cache_row(const int32_t* __restrict__ slot, int i) {
-  return slot ? (size_t)slot[i] : (size_t)i;
-}
-
-// row of q and k ([rows, Hk, d_k]) that value head h of token row tok reads:
-// key head h / G (value heads jG .. jG + G - 1 share key head j)
-__device__ __forceinline__ size_t kq_row(size_t tok, int h, int Hk, int G) { return tok * Hk + h / G; }
-
-// ---------------------------------------------------------------------------
-// varlen plan: exclusive prefix sums of full and of all chunks per sequence
-
-// Bookkeeping of the fused boundary-chain + scan launch (k_chain_scan_bf16),
-// prepared by the plan kernel of the same call.
-struct FusedPlan {
-  int32_t* order;   // [A] chunk slots in chunk-major order (chunk 0 of every sequence, then chunk 1, ...),
-                    // or null: no fused launch follows
-  int32_t* ticket;  // work-item counter of the fused launch
-  int32_t* ready;   // [n_ready] boundaries published so far by each chain item
-  int32_t n_ready;
-};
-constexpr int kFusedMaxSeqs = 128;  // sequences per call for which the plan builds the chunk-major order
-
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start, const int32_t* __restrict__ end,
-                                               int32_t N, int32_t Cl, int32_t* __restrict__ full_base,
-                                               int32_t* __restrict__ all_base, const FusedPlan fp) {
-  // 1024 sequences per pass: an inclusive scan inside each wave (shuffles),
-  // the 16 wave totals through LDS, and the running totals of earlier passes
-  // (integers, so the order of the sums does not matter)
-  __shared__ int32_t wf[16], wa[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int cf = 0, ca = 0;
-  for (int base = 0; base < N; base += 1024) {
-    const int i = base + tid;
-    int nf = 0, na = 0;
-    if (i < N) {
-      const int L = end[i] - start[i];
-      nf = L / Cl;
-      na = (L + Cl - 1) / Cl;
-    }
-    int sf = nf, sa = na;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int xf = __shfl_up(sf, off), xa = __shfl_up(sa, off);
-      if (lane >= off) {
-        sf += xf;
-        sa += xa;
-      }
-    }
-    if (lane == 63) {
-      wf[wave] = sf;
-      wa[wave] = sa;
-    }
-    __syncthreads();
-    int pf = 0, pa = 0, tf = 0, ta = 0;
-    for (int w = 0; w < 16; ++w) {
-      if (w < wave) {
-        pf += wf[w];
-        pa += wa[w];
-      }
-      tf += wf[w];
-      ta += wa[w];
-    }
-    if (i < N) {
-      full_base[i] = cf + pf + sf - nf;
-      all_base[i] = ca + pa + sa - na;
-    }
-    cf += tf;
-    ca += ta;
-    __syncthreads();  // wf, wa are rewritten by the next pass
-  }
-  if (tid == 0) {
-    full_base[N] = cf;
-    all_base[N] = ca;
-  }
-  if (fp.order == nullptr) return;
-  // fused launch: clear its counters, and order the chunk slots by chunk
-  // index (then by sequence): slot (i, c) goes to position
-  //   sum_j min(nall_j, c) + #{j < i : nall_j > c}
-  // so that the scan units of early chunks, whose boundaries the chain
-  // publishes first, are taken first.  The order only schedules work; no
-  // result depends on it.
-  __shared__ int32_t nall_s[kFusedMaxSeqs];
-  for (int j = tid; j < fp.n_ready; j += 1024) fp.ready[j] = 0;
-  if (tid == 0) *fp.ticket = 0;
-  for (int j = tid; j < N; j += 1024) nall_s[j] = (end[j] - start[j] + Cl - 1) / Cl;
-  __syncthreads();  // nall_s and all_base complete
-  for (int sl = tid; sl < ca; sl += 1024) {
-    const int i = find_seq(all_base, N, sl);
-    const int c = sl - all_base[i];
-    int pos = 0;
-    for (int j = 0; j < N; ++j) {
-      const int nj = nall_s[j];
-      pos += min(nj, c) + ((j < i && nj > c) ? 1 : 0);
-    }
-    fp.order[pos] = sl;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// chunk products
-
-template <class D, int DK, int DV>
-__device__ __forceinline__ void stage_chunk(ChunkLds<DK, DV>& sm, const typename D::T* __restrict__ k,
-                                            size_t k_row0, size_t k_stride,
-                                            const typename D::T* __restrict__ v, size_t v_row0,
-                                            size_t v_stride, const typename D::T* __restrict__ g,
-                                            const typename D::T* __restrict__ beta, size_t gb0,
-                                            size_t gb_stride, int n) {
-  // rows t >= n (a chunk shorter than the slot) are identity padding
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int idx = tid; idx < C * DK; idx += nt) {
-    const int t = idx / DK, i = idx % DK;
-    sm.K[t][i] = t < n ? D::load(k, (k_row0 + (size_t)t * k_stride) * DK + i) : 0.f;
-  }
-  for (int idx = tid; idx < C * DV; idx += nt) {
-    const int t = idx / DV, j = idx % DV;
-    sm.V[t][j] = t < n ? D::load(v, (v_row0 + (size_t)t * v_stride) * DV + j) : 0.f;
-  }
-  for (int t = tid; t < C; t += nt) {
-    sm.g[t] = t < n ? D::load(g, gb0 + (size_t)t * gb_stride) : 0.f;
-    sm.beta[t] = t < n ? D::load(beta, gb0 + (size_t)t * gb_stride) : 0.f;
-  }
-  __syncthreads();
-}
-
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(256) void k_chunk_local_prefill(const PrefillArgs a) {
-  using T = typename D::T;
-  __shared__ ChunkLds<DK, DV> sm;
-  const int f = blockIdx.x, h = blockIdx.y;
-  const int N = a.N, H = a.H;
-  if (f >= a.full_base[N]) return;
-  const int i = find_seq(a.full_base, N, f);
-  const int c = f - a.full_base[i];
-  const size_t tok0 = (size_t)a.start[i] + (size_t)c * a.Cl;
-  const size_t row0 = tok0 * H + h;  // row index into [T, H, ...]
-  stage_chunk<D, DK, DV>(sm, (const T*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const T*)a.v, row0, H,
-                         (const T*)a.g, (const T*)a.beta, row0, H, a.Cl);
-  const size_t slot = (size_t)f * H + h;
-  float* P = (float*)(a.prod + slot * prod_slot_bytes(false, DK, DV));
-  chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + slot);
-}
-
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(256) void k_chunk_local_resync(const DecodeArgs a) {
-  using T = typename D::T;
-  __shared__ ChunkLds<DK, DV> sm;
-  const int i = a.seq0 + blockIdx.x;
-  const size_t sh = (size_t)i * a.H + blockIdx.y;
-  if (a.flag[sh] == 0) return;
-  const size_t ps = (size_t)blockIdx.x * a.H + blockIdx.y;  // product slot
-  const size_t ch = cache_row(a.slot, i) * a.H + blockIdx.y;
-  // tail rows of this (sequence, head): [Cl, DK], [Cl, DV], [Cl]
-  const size_t tr = ch * a.Cl;
-  stage_chunk<D, DK, DV>(sm, (const T*)a.tail_k, tr, 1, (const T*)a.tail_v, tr, 1, (const T*)a.tail_g,
-                         (const T*)a.tail_beta, tr, 1, a.Cl);
-  float* P = (float*)(a.prod + ps * prod_slot_bytes(false, DK, DV));
-  chunk_local_f32<DK, DV>(sm, P, P + C * DK, P + C * DK + C * DV, a.gamn + ps);
-}
-
-// bf16 path: MFMA chunk products
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 3) void k_chunk_local_prefill_bf16(const PrefillArgs a) {
-  __shared__ ChunkLdsB<DK, DV> sm;
-  const int f = blockIdx.x, h = blockIdx.y;
-  const int N = a.N, H = a.H;
-  if (f >= a.full_base[N]) return;
-  const int i = find_seq(a.full_base, N, f);
-  const int c = f - a.full_base[i];
-  const size_t tok0 = (size_t)a.start[i] + (size_t)c * a.Cl;
-  const size_t row0 = tok0 * H + h;
-  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const uint16_t*)a.v, row0,
-                           H, (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H, a.Cl);
-  const size_t slot = (size_t)f * H + h;
-  chunk_local_bf16<DK, DV>(sm, a.prod + slot * prod_slot_bytes(true, DK, DV), a.gamn + slot);
-}
-
-
-// ---------------------------------------------------------------------------
-// boundary chain
-
-template <int DK, int DV, int NB>
-__device__ __forceinline__ void stage_products(ChainLds<DK, NB>& sm, const float* __restrict__ P,
-                                               const float* __restrict__ gamn, int col0) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const float* W = P;
-  const float* U = P + C * DK;
-  const float* KtT = P + C * DK + C * DV;
-  for (int idx = tid; idx < C * DK; idx += nt) (&sm.W[0][0])[idx] = W[idx];
-  for (int idx = tid; idx < DK * C; idx += nt) (&sm.KtT[0][0])[idx] = KtT[idx];
-  for (int idx = tid; idx < C * NB; idx += nt) {
-    const int t = idx / NB, j = idx % NB;
-    sm.U[t][j] = U[t * DV + col0 + j];
-  }
-  if (tid == 0) sm.gamn = *gamn;
-  __syncthreads();
-}
-
-template <int DK, int DV, int NB>
-__device__ __forceinline__ void put_block(float* __restrict__ dst, const ChainLds<DK, NB>& sm, int col0) {
-  for (int idx = threadIdx.x; idx < DK * NB; idx += blockDim.x) {
-    const int i = idx / NB, j = idx % NB;
-    dst[(size_t)i * DV + col0 + j] = sm.S[i][j];
-  }
-}
-
-// the same block into a boundary slot (accumulator-tile order, bnd_index)
-template <int DK, int DV, int NB>
-__device__ __forceinline__ void put_block_bnd(float* __restrict__ dst, const ChainLds<DK, NB>& sm, int col0) {
-  for (int idx = threadIdx.x; idx < DK * NB; idx += blockDim.x) {
-    const int i = idx / NB, j = idx % NB;
-    dst[bnd_index<DK>(i, col0 + j)] = sm.S[i][j];
-  }
-}
-
-template <int DK, int DV, int NB>
-__device__ __forceinline__ void get_block(ChainLds<DK, NB>& sm, const float* __restrict__ src, int col0) {
-  for (int idx = threadIdx.x; idx < DK * NB; idx += blockDim.x) {
-    const int i = idx / NB, j = idx % NB;
-    sm.S[i][j] = src ? src[(size_t)i * DV + col0 + j] : 0.f;
-  }
-  __syncthreads();
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_chain_prefill(const PrefillArgs a) {
-  constexpr int NB = kChainCols;
-  __shared__ ChainLds<DK, NB> sm;
-  const int i = blockIdx.x, h = blockIdx.y, col0 = blockIdx.z * NB;
-  const int H = a.H;
-  const int L = a.end[i] - a.start[i];
-  if (a.skip_empty && L == 0) return;
-  const int Cl = a.Cl;
-  const int nfull = L / Cl, nall = (L + Cl - 1) / Cl;
-  const size_t sh = (size_t)i * H + h;
-  const size_t SS = (size_t)DK * DV;
-  const size_t ch = cache_row(a.slot, i) * H + h;
-  get_block<DK, DV, NB>(sm, a.h0 ? a.h0 + (a.h0_slotted ? ch : sh) * SS : nullptr, col0);
-  const int abase = a.all_base[i], fbase = a.full_base[i];
-  if (nall > 0) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)abase * H + h) * SS, sm, col0);
-  for (int c = 0; c < nfull; ++c) {
-    const size_t slot = (size_t)(fbase + c) * H + h;
-    stage_products<DK, DV, NB>(sm, (const float*)(a.prod + slot * prod_slot_bytes(false, DK, DV)), a.gamn + slot,
-                               col0);
-    chain_step_f32<DK, NB>(sm);
-    if (c + 1 < nall) put_block_bnd<DK, DV, NB>(a.bnd + ((size_t)(abase + c + 1) * H + h) * SS, sm, col0);
-  }
-  put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
-  if (L % Cl == 0) {
-    put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
-    if (a.hT) put_block<DK, DV, NB>(a.hT + sh * SS, sm, col0);
-  }
-  if (blockIdx.z == 0 && threadIdx.x == 0) {
-    a.tail_len[ch] = L % Cl;
-    if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
-  }
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_chain_resync(const DecodeArgs a) {
-  constexpr int NB = kChainCols;
-  __shared__ ChainLds<DK, NB> sm;
-  const int i = a.seq0 + blockIdx.x;
-  const size_t sh = (size_t)i * a.H + blockIdx.y;
-  if (a.flag[sh] == 0) return;
-  const size_t ps = (size_t)blockIdx.x * a.H + blockIdx.y;  // product slot
-  const int col0 = blockIdx.z * NB;
-  const size_t SS = (size_t)DK * DV;
-  const size_t ch = cache_row(a.slot, i) * a.H + blockIdx.y;
-  get_block<DK, DV, NB>(sm, a.s_bnd + ch * SS, col0);
-  stage_products<DK, DV, NB>(sm, (const float*)(a.prod + ps * prod_slot_bytes(false, DK, DV)), a.gamn + ps, col0);
-  chain_step_f32<DK, NB>(sm);
-  put_block<DK, DV, NB>(a.s_bnd + ch * SS, sm, col0);
-  put_block<DK, DV, NB>(a.s_run + ch * SS, sm, col0);
-  if (a.hT && (a.flag[sh] & 2)) put_block<DK, DV, NB>(a.hT + sh * SS, sm, col0);
-  if (blockIdx.z == 0 && threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
-}
-
-// bf16 path: one work-group per (sequence, head, block of CB = WAVES * NT * 16
-// state columns); each wave keeps NT 16-column tiles of the state in MFMA
-// accumulator tiles for the whole chain.  A chunk's WF / KF fragments (shared
-// by the work-group) and the U tiles of its columns go through a two-buffer
-// LDS stage; the loads run two chunks ahead in registers, so each step only
-// waits on loads issued a full step earlier.  The column split is bit-neutral
-// (every state column's arithmetic depends only on that column), so the
-// launch picks WAVES and NT by the number of (sequence, head) pairs.
-template <int DK, int DV, int WAVES, int NT>
-__global__ __launch_bounds__(WAVES * 64) void k_chain_prefill_bf16(const PrefillArgs a) {
-  using namespace mfma;
-  typedef SlotB<DK, DV> Sl;
-  constexpr int kThreads = WAVES * 64;
-  constexpr int CB = WAVES * NT * 16;
-  constexpr int kFragPieces = (int)(Sl::oU / 16);  // WF + KF, 16-byte pieces
-  constexpr int kUPieces = C * CB * 4 / 16;        // U tiles of this block's columns
-  constexpr int kPieces = kFragPieces + kUPieces;
-  constexpr int kPer = kPieces / kThreads;
-  constexpr int kPerFrag = kFragPieces / kThreads;
-  static_assert(kPieces % kThreads == 0 && kFragPieces % kThreads == 0, "staging split");
-  static_assert(DV % CB == 0, "column blocks tile d_v");
-  __shared__ u32x4 stage[2][kPieces];
-  const int i = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int jbg = blockIdx.z * (CB / 16), jb0 = jbg + wave * NT;
-  const int H = a.H;
-  const int L = a.end[i] - a.start[i];
-  if (a.skip_empty && L == 0) return;
-  const int Cl = a.Cl;
-  int nfull = L / Cl;
-  const int nall = (L + Cl - 1) / Cl;
-  const size_t sh = (size_t)i * H + h;
-  const size_t SS = (size_t)DK * DV;
-  const int abase = a.all_base[i];
-  const int fbase = a.all_chunks ? abase : a.full_base[i];
-  if (a.all_chunks) nfull = nall;
-  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * Sl::bytes; };
-  auto gamn_of = [&](int c) { return a.gamn[(size_t)(fbase + c) * H + h]; };
-  // piece p of chunk c: WF/KF piece p, or U piece p - kFragPieces of this block's tiles
-  auto fetch = [&](int c, u32x4 (&r)[kPer]) {
-    const uint8_t* s = slot_of(c);
-    const u32x4* f = reinterpret_cast<const u32x4*>(s);
-    const u32x4* u = reinterpret_cast<const u32x4*>(s + Sl::oU) + (size_t)jbg * (C / 16) * 64;
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int p = tid + m * kThreads;
-      r[m] = m < kPerFrag ? f[p] : u[p - kFragPieces];
-    }
-  };
-  auto put = [&](int buf, const u32x4 (&r)[kPer]) {
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) stage[buf][tid + m * kThreads] = r[m];
-  };
-  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-
-  f32x4 S[DK / 16][NT];
-  const size_t ch = cache_row(a.slot, i) * H + h;
-  load_state_tiles<DK, DV, NT>(S, a.h0 ? a.h0 + (a.h0_slotted ? ch : sh) * SS : nullptr, jb0, lane);
-  if (nall > 0) store_bnd_tiles<DK, NT>(a.bnd + ((size_t)abase * H + h) * SS, S, jb0, lane);
-  // Gamma_n travels with its chunk: every thread loads it, thread 0 stages it
-  __shared__ float gn_stage[2];
-  u32x4 R0[kPer], R1[kPer];
-  float G0 = 1.f, G1 = 1.f;
-  if (nfull > 0) {
-    fetch(0, R0);
-    G0 = gamn_of(0);
-    put(0, R0);
-    if (tid == 0) gn_stage[0] = G0;
-    const int c1 = min(1, nfull - 1);
-    fetch(c1, R1);
-    G1 = gamn_of(c1);
-  }
-  __syncthreads();
-  // Step c: chunk c is in stage buffer P = c & 1; its registers RP are free
-  // and receive chunk c + 2 (clamped: the loads stay unconditional, so the
-  // compiler's wait counts cover exactly the loads a put needs); chunk c + 1
-  // sits in the other registers RQ and goes to the other buffer.  All steps
-  // but the last store their boundary unconditionally, for the same reason.
-  auto step = [&](auto par, auto is_last, int c) {
-    constexpr int P = decltype(par)::value;
-    constexpr bool kLast = decltype(is_last)::value;
-    u32x4(&RP)[kPer] = P ? R1 : R0;
-    u32x4(&RQ)[kPer] = P ? R0 : R1;
-    float& GP = P ? G1 : G0;
-    float& GQ = P ? G0 : G1;
-    if constexpr (!kLast) {
-      const int cf = min(c + 2, nfull - 1);
-      fetch(cf, RP);
-      GP = gamn_of(cf);
-    }
-    const u32x4* st = stage[P];
-    const float gn = gn_stage[P];
-    f32x4 Ut[C / 16][NT];
-#pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        Ut[tm][nt] = __builtin_bit_cast(f32x4, st[kFragPieces + ((wave * NT + nt) * (C / 16) + tm) * 64 + lane]);
-    chain_step_bf16<DK, NT>(
-        S, [&](int kb, int tm) { return st[(kb * (C / 16) + tm) * 64 + lane]; },
-        [&](int kb, int im) { return st[(int)(Sl::oKF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut, gn);
-    float* bnd_next = a.bnd + ((size_t)(abase + c + 1) * H + h) * SS;
-    if constexpr (kLast) {
-      if (c + 1 < nall) store_bnd_tiles<DK, NT>(bnd_next, S, jb0, lane);
-    } else {
-      store_bnd_tiles<DK, NT>(bnd_next, S, jb0, lane);
-      put(P ^ 1, RQ);
-      if (tid == 0) gn_stage[P ^ 1] = GQ;
-      barrier();
-    }
-  };
-  typedef std::integral_constant<int, 0> P0;
-  typedef std::integral_constant<int, 1> P1;
-  typedef std::integral_constant<bool, false> Mid;
-  typedef std::integral_constant<bool, true> Last;
-  int c = 0;
-  for (; c + 2 < nfull; c += 2) {
-    step(P0{}, Mid{}, c);
-    step(P1{}, Mid{}, c + 1);
-  }
-  if (c + 1 < nfull) {
-    step(P0{}, Mid{}, c);
-    step(P1{}, Last{}, c + 1);
-  } else if (c < nfull) {
-    step(P0{}, Last{}, c);
-  }
-  store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
-  if (a.all_chunks) return;
-  if (L % Cl == 0) {
-    store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
-    if (a.hT) store_state_tiles<DK, DV, NT>(a.hT + sh * SS, S, jb0, lane);
-  }
-  if (blockIdx.z == 0 && tid == 0) {
-    a.tail_len[ch] = L % Cl;
-    if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
-  }
-}
-
-// chain step of a filled tail, bf16 path, from a product slot the decode
-// workspace already holds (the chunkwise-everywhere comparator's decode):
-// one wave per (sequence, head, 32 state columns), the waves of a (sequence,
-// head) in one work-group
-constexpr int kResyncNT = 2;
-template <int DV>
-constexpr int kResyncWaves = DV / (16 * kResyncNT) < 4 ? DV / (16 * kResyncNT) : 4;
-
-template <int DK, int DV>
-__global__ __launch_bounds__(kResyncWaves<DV> * 64) void k_chain_resync_bf16(const DecodeArgs a) {
-  constexpr int NT = kResyncNT;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
-  if (a.flag[sh] == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int jb0 = (blockIdx.z * kResyncWaves<DV> + (threadIdx.x >> 6)) * NT;
-  const size_t SS = (size_t)DK * DV;
-  mfma::f32x4 S[DK / 16][NT];
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * SS, jb0, lane);
-  chain_step_bf16_global<DK, DV, NT>(S, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn[sh], jb0, lane);
-  store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
-  store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
-  if (blockIdx.z == 0 && threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
-}
-
-// decode resync, bf16 path, in one launch: one work-group per (sequence,
-// head).  A pair whose tail filled forms the tail's chunk products into the
-// decode workspace's product slot (as the prefill's chunk-product kernel
-// does for a chunk) and then, wave w for state columns 32 w .. 32 w + 31,
-// takes the chain step from s_bnd with them (k_chain_resync_bf16's
-// arithmetic); every other pair exits at once, so a step in which no tail
-// fills costs one launch of early-exit work-groups.  The grid covers
-// sequences seq0 .. seq0 + gridDim.x - 1 of the batch (all of them, except
-// in the fixed-scratch decode, which resynchronises the batch in groups);
-// product slots are indexed within the grid.
-template <int DK, int DV>
-__global__ __launch_bounds__(256, DK > 128 ? 1 : 3) void k_resync_bf16(const DecodeArgs a) {
-  // 32 columns per wave pass (16 at d_k = 256, where a 16-column block's
-  // state is already 64 accumulator registers); four waves take the passes
-  constexpr int NT = DK > 128 ? 1 : kResyncNT, NW = DV / (16 * NT);
-  __shared__ ChunkLdsB<DK, DV> sm;
-  const int i = a.seq0 + blockIdx.x;
-  const size_t sh = (size_t)i * a.H + blockIdx.y;
-  const int flag = a.flag[sh];
-  if (flag == 0) return;
-  const size_t ps = (size_t)blockIdx.x * a.H + blockIdx.y;  // product slot
-  const size_t ch = cache_row(a.slot, i) * a.H + blockIdx.y;
-  const size_t tr = ch * a.Cl;
-  uint8_t* const prod = a.prod + ps * prod_slot_bytes(true, DK, DV);
-  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.tail_k, tr, 1, (const uint16_t*)a.tail_v, tr, 1,
-                           (const uint16_t*)a.tail_g, (const uint16_t*)a.tail_beta, tr, 1, a.Cl);
-  chunk_local_bf16<DK, DV>(sm, prod, a.gamn + ps);
-  __syncthreads();  // the slot and Gamma_n, written by every wave, are read below
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  auto pass = [&](int jw) {
-    const int jb0 = jw * NT;
-    const size_t SS = (size_t)DK * DV;
-    mfma::f32x4 S[DK / 16][NT];
-    load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * SS, jb0, lane);
-    chain_step_bf16_global<DK, DV, NT>(S, prod, a.gamn[ps], jb0, lane);
-    store_state_tiles<DK, DV, NT>(a.s_bnd + ch * SS, S, jb0, lane);
-    store_state_tiles<DK, DV, NT>(a.s_run + ch * SS, S, jb0, lane);
-    if (a.hT && (flag & 2)) store_state_tiles<DK, DV, NT>(a.hT + sh * SS, S, jb0, lane);
-  };
-  if constexpr (NW <= 4) {
-    if (wave < NW) pass(wave);
-  } else {
-#pragma unroll 1
-    for (int jw = wave; jw < NW; jw += 4) pass(jw);
-  }
-  if (threadIdx.x == 0 && a.lgs) a.lgs[ch] = 0.f;
-}
-
-// ---------------------------------------------------------------------------
-// in-chunk scan (prefill): one wave per (chunk, head, 64 state columns; 32
-// at d_k = 256)
-
-// One scan unit: chunk slot `slot` (chunk c of sequence i), head h, state
-// columns WC z .. WC z + WC - 1 (one wave; WC = KeySplit<DK>::kCols; lane =
-// column, and at d_k = 256 lanes j and j + 32 the two key halves of column
-// j).  kAgentBnd: the boundary state is read with agent-scope loads, because
-// the boundary chain wrote it during the same launch (k_chain_scan_bf16).
-template <class D, int DK, int DV, bool kAgentBnd>
-__device__ __forceinline__ void scan_unit(const PrefillArgs& a, int slot, int i, int h, int z, int lane) {
-  using T = typename D::T;
-  constexpr int KL = KeySplit<DK>::kKeys, WC = KeySplit<DK>::kCols;
-  const int H = a.H;
-  const int c = slot - a.all_base[i];
-  const int L = a.end[i] - a.start[i];
-  const int Cl = a.Cl;
-  const int n = min(Cl, L - c * Cl);
-  const size_t tok0 = (size_t)a.start[i] + (size_t)c * Cl;
-  const int col = z * WC + lane % WC;
-  const int k0 = (lane / WC) * KL;  // this lane's first key row
-  const size_t SS = (size_t)DK * DV;
-
-  const float* B = a.bnd + ((size_t)slot * H + h) * SS;
-  float s[KL];
-  {
-    // rows 4q .. 4q+3 of column col sit 256 q bytes after rows 0 .. 3
-    static_assert(bnd_index<DK>(4, 0) == 64 && bnd_index<DK>(16, 0) == 256, "row groups 256 bytes apart");
-    const BufRsrc rb = buf_rsrc(B, (uint32_t)(SS * sizeof(float)));
-    const uint32_t col_off = (uint32_t)(bnd_index<DK>(k0, col) * 4);
-#pragma unroll
-    for (int q = 0; q < KL / 4; ++q) {  // rows k0 + 4q .. k0 + 4q+3 of column col: one 16-byte load
-      const mfma::f32x4 x = __builtin_bit_cast(
-          mfma::f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col_off, 256 * q, kAgentBnd ? kAuxAgent : 0));
-      s[4 * q] = x[0];
-      s[4 * q + 1] = x[1];
-      s[4 * q + 2] = x[2];
-      s[4 * q + 3] = x[3];
-    }
-  }
-
-  const T* gp = (const T*)a.g;
-  const T* bp = (const T*)a.beta;
-  float g_l = 0.f, beta_l = 0.f;
-  if (lane < n) {
-    const size_t r = (tok0 + lane) * H + h;
-    g_l = D::load(gp, r);
-    beta_l = D::load(bp, r);
-  }
-  // the scale steps of the chunk's tokens in token order from the boundary
-  // (lg = 0), lane t keeping token t's; then every lane takes its token's
-  // step scalars (the same helpers as the decode step)
-  float lg = 0.f;
-  TokenScale ts_l{0.f, false};
-  for (int t = 0; t < n; ++t) {
-    const TokenScale ts = token_scale(lg, lane_bcast(g_l, t));
-    if (lane == t) ts_l = ts;
-    lg = scale_after(ts);
-  }
-  float c_l, b_l;
-  step_factors(ts_l, beta_l, c_l, b_l);
-  const uint64_t renorm = __ballot(ts_l.renorm && lane < n);
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
-  const T* vp = (const T*)a.v;
-  scan_tokens<D, DK, DV>(s, kp, qp, vp, (T*)a.o, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col, lane,
-                         c_l, b_l, renorm);
-  const int nall = (L + Cl - 1) / Cl;
-  if (c == nall - 1 && (L % Cl) != 0) {
-    // last, partial chunk: its end state is the running state (N with
-    // log-scale lg), its tokens the tail
-    const size_t ch = cache_row(a.slot, i) * H + h;
-    float* R = a.s_run + ch * SS;
-    store_state_col<KL, DV>(R, (uint32_t)(SS * 4), s, k0, col, 1.f);
-    if (z == 0 && lane == 0 && a.lgs) a.lgs[ch] = lg;
-    if (a.hT)  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
-      store_state_col<KL, DV>(a.hT + ((size_t)i * H + h) * SS, (uint32_t)(SS * 4), s, k0, col, scale_of_log(lg));
-    T* tv = (T*)a.tail_v + ch * Cl * DV;
-    if (lane < WC)
-      for (int t = 0; t < n; ++t) tv[(size_t)t * DV + col] = vp[((tok0 + t) * H + h) * DV + col];
-    if (z == 0) {
-      T* tk = (T*)a.tail_k + ch * Cl * DK;
-      for (int idx = lane; idx < n * DK; idx += kWave) {
-        const int t = idx / DK, e = idx % DK;
-        tk[idx] = kp[kq_row(tok0 + t, h, a.Hk, a.G) * DK + e];
-      }
-      if (lane < n) {
-        ((T*)a.tail_g)[ch * Cl + lane] = gp[(tok0 + lane) * H + h];
-        ((T*)a.tail_beta)[ch * Cl + lane] = bp[(tok0 + lane) * H + h];
-      }
-    }
-  }
-}
-
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(64, 3) void k_scan(const PrefillArgs a) {
-  const int slot = blockIdx.x;
-  if (slot >= a.all_base[a.N]) return;
-  scan_unit<D, DK, DV, false>(a, slot, find_seq(a.all_base, a.N, slot), blockIdx.y, blockIdx.z, threadIdx.x);
-}
-
-// ---------------------------------------------------------------------------
-// chunk products, boundary chain and in-chunk scan in one launch (bf16 inputs)
-//
-// The chain step of chunk c needs only chunk c's products, and the scan of
-// chunk c only the boundary B_c, so each can start as soon as its input is
-// in memory instead of after the whole stage before it.  Every work-group
-// takes a ticket from an atomic counter when it starts, so ticket order is
-// start order.  Tickets 0 .. n_cp-1 are chunk-product items, one per (chunk
-// slot in chunk-major order, head; partial chunks have none), which publish
-// a flag once their product slot has reached memory.  The next n_chain
-// tickets are chain items, one per (sequence, head, 64-column block): the
-// chain of k_chain_prefill_bf16 with 4 waves x 16 columns and a one-buffer
-// LDS stage, which waits for each chunk's flag before loading its products
-// and publishes, after each step, how many boundaries of its columns have
-// reached memory.  Later tickets are scan items: 4 waves, each one (chunk,
-// head, 64-column half) unit, units in chunk-major order, each waiting until
-// its chain item has published its boundary.  Every item waits only on items
-// with lower tickets, which started before it and never wait on it, so every
-// wait ends; the waits are bounded all the same.  Products and boundaries
-// travel with agent-scope stores and loads (coherent across the XCDs, no
-// cache-wide maintenance); a flag or count is published only after the
-// stores are complete.  No value depends on the order in which items run.
-struct FusedArgs {
-  const int32_t* order;  // [A] chunk slots, chunk-major
-  int32_t* ticket;       // zeroed by the plan kernel
-  int32_t* ready;        // [N * H * NZ * kReadyStride] boundaries published per chain item (one per
-                         // kReadyStride words), zeroed by the plan kernel
-  int32_t* cp_ready;     // [F * H] 1 once a (full chunk, head)'s products are in memory (zeroed by the
-                         // plan kernel), or null: the products come from an earlier launch
-  int32_t* timeout;      // set to 1 if a wait ever gives up (never expected)
-  int32_t n_cp;          // chunk-product items (tickets 0 .. n_cp - 1)
-  int32_t n_chain;       // chain items (the next n_chain tickets)
-};
-
-constexpr int kFusedChainCols = 64;  // state columns per chain item (= per scan unit)
-// each chain item's count sits on a cache line of its own: thousands of
-// waiting waves poll the counts, and packed counts would send all those polls
-// to a handful of lines (one memory channel), which then slows the chain's
-// own traffic
-constexpr int kReadyStride = 32;  // int32 words
-
-__device__ __forceinline__ void publish_count(int32_t* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ int read_count(const int32_t* p) {
-  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// waits (bounded) until *p >= need; false if it gave up.  The default polls
-// every ~8,000 cycles (3 to 4 us; a chain step takes about as long), so that
-// thousands of waiting scan waves add little memory traffic; the chain's wait
-// for chunk products (a few waves, on its critical path) polls every ~200
-// cycles.  Either way the bound is about a second.
-template <int kSleep = 127>
-__device__ __forceinline__ bool wait_count(const int32_t* p, int need) {
-  constexpr int kMaxPolls = kSleep >= 127 ? 1 << 18 : 1 << 21;
-  for (int it = 0; it < kMaxPolls; ++it) {
-    if (__builtin_amdgcn_readfirstlane(read_count(p)) >= need) return true;
-    __builtin_amdgcn_s_sleep(kSleep);
-  }
-  return false;
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__(256, DK > 128 ? 2 : 3) void k_chain_scan_bf16(const PrefillArgs a, const FusedArgs f) {
-  using namespace mfma;
-  typedef SlotB<DK, DV> Sl;
-  constexpr int kThreads = 256, CB = kFusedChainCols, NZ = DV / CB;
-  constexpr int kFragPieces = (int)(Sl::oU / 16);  // WF + KF, 16-byte pieces
-  constexpr int kUPieces = C * CB * 4 / 16;        // U tiles of this item's columns
-  constexpr int kPieces = kFragPieces + kUPieces;
-  constexpr int kPer = kPieces / kThreads;
-  constexpr int kPerFrag = kFragPieces / kThreads;
-  static_assert(kPieces % kThreads == 0 && kFragPieces % kThreads == 0, "staging split");
-  static_assert(DV % CB == 0, "column blocks tile d_v");
-  // one LDS block: a chain item's stage or a chunk-product item's arrays (at
-  // d_k = 256 the launch has chain items only)
-  constexpr bool kCP = KeySplit<DK>::kParts == 1;
-  constexpr size_t kStageBytes = (size_t)kPieces * 16, kCpBytes = kCP ? sizeof(ChunkLdsB<DK, DV>) : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStageBytes > kCpBytes ? kStageBytes : kCpBytes];
-  u32x4* const stage = reinterpret_cast<u32x4*>(lds);
-  __shared__ float gn_stage;
-  __shared__ int32_t ticket_s;
-  // the ticket and the wave index are uniform over each wave: reading them
-  // into scalar registers keeps every index derived from them scalar
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid == 0) ticket_s = atomicAdd(f.ticket, 1);
-  __syncthreads();
-  const int t = __builtin_amdgcn_readfirstlane(ticket_s);
-  const int H = a.H;
-  if (t < f.n_cp) {
-    // ---- chunk-product item: full chunk slot order[t / H], head t % H
-    if constexpr (kCP) {
-      const int pos = t / H, h = t % H;
-      if (pos >= a.all_base[a.N]) return;
-      const int slot = f.order[pos];
-      if (slot < 0 || slot >= a.all_base[a.N]) return;  // (the plan writes every position in range)
-      const int i = find_seq(a.all_base, a.N, slot);
-      const int c = slot - a.all_base[i];
-      if (c >= (a.end[i] - a.start[i]) / a.Cl) return;  // a partial chunk has no products
-      const size_t tok0 = (size_t)a.start[i] + (size_t)c * a.Cl;
-      const size_t row0 = tok0 * H + h;
-      ChunkLdsB<DK, DV>& sm = *reinterpret_cast<ChunkLdsB<DK, DV>*>(lds);
-      stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, kq_row(tok0, h, a.Hk, a.G), a.Hk, (const uint16_t*)a.v,
-                               row0, H, (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H, a.Cl);
-      const size_t ps = (size_t)(a.full_base[i] + c) * H + h;
-      chunk_local_bf16<DK, DV, kAuxAgent>(sm, a.prod + ps * Sl::bytes, a.gamn + ps);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slot stores are complete
-      __syncthreads();                                  // and every wave's
-      if (tid == 0) publish_count(f.cp_ready + ps, 1);
-    }
-    return;
-  }
-  if (t >= f.n_cp + f.n_chain) {
-    // ---- scan item: one unit per wave (launches at d_k = 256 have chain items only)
-    if constexpr (KeySplit<DK>::kParts == 1) {
-      const long u = (long)(t - f.n_cp - f.n_chain) * 4 + wave;
-      const long per_slot = (long)H * NZ;
-      if (u >= (long)a.all_base[a.N] * per_slot) return;
-      const int pos = (int)(u / per_slot), r = (int)(u % per_slot), h = r / NZ, z = r % NZ;
-      const int slot = f.order[pos];
-      if (slot < 0 || slot >= a.all_base[a.N]) return;  // (the plan writes every position in range)
-      const int i = find_seq(a.all_base, a.N, slot);
-      const int c = slot - a.all_base[i];
-      if (!wait_count(f.ready + (((size_t)i * H + h) * NZ + z) * kReadyStride, c + 1) && lane == 0)
-        atomicExch(f.timeout, 1);
-      scan_unit<Bf16, DK, DV, true>(a, slot, i, h, z, lane);
-    }
-    return;
-  }
-  // ---- chain item
-  const int tc = t - f.n_cp;
-  const int i = tc / (H * NZ), r = tc % (H * NZ), h = r / NZ, z = r % NZ;
-  const int jbg = z * (CB / 16), jb0 = jbg + wave;  // one 16-column tile per wave
-  const int L = a.end[i] - a.start[i];
-  if (a.skip_empty && L == 0) return;
-  const int Cl = a.Cl;
-  const int nfull = L / Cl, nall = (L + Cl - 1) / Cl;
-  const size_t sh = (size_t)i * H + h;
-  const size_t SS = (size_t)DK * DV;
-  const int abase = a.all_base[i], fbase = a.full_base[i];
-  int32_t* const rdy = f.ready + (sh * NZ + z) * kReadyStride;
-  auto slot_of = [&](int c) { return a.prod + ((size_t)(fbase + c) * H + h) * Sl::bytes; };
-  // chunk c's products, once its chunk-product item has published them; read
-  // at agent scope, since that item may have run on another XCD
-  auto gamn_of = [&](int c) {
-    return __hip_atomic_load(a.gamn + (size_t)(fbase + c) * H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto fetch = [&](int c, u32x4 (&rg)[kPer]) {
-    if (f.cp_ready && !wait_count<2>(f.cp_ready + (size_t)(fbase + c) * H + h, 1) && lane == 0)
-      atomicExch(f.timeout, 1);
-    const BufRsrc sr = buf_rsrc(slot_of(c), (uint32_t)Sl::bytes);
-    const uint32_t u0 = (uint32_t)(Sl::oU + (size_t)jbg * (C / 16) * 64 * 16);
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int p = tid + m * kThreads;
-      const uint32_t off = m < kPerFrag ? (uint32_t)p * 16u : u0 + (uint32_t)(p - kFragPieces) * 16u;
-      rg[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, kAuxAgent));
-    }
-  };
-  f32x4 S[DK / 16][1];
-  const size_t ch = cache_row(a.slot, i) * H + h;
-  load_state_tiles<DK, DV, 1>(S, a.h0 ? a.h0 + (a.h0_slotted ? ch : sh) * SS : nullptr, jb0, lane);
-  // boundary c of this wave's tile, agent scope (bnd_index layout)
-  auto store_bnd = [&](int c) {
-    const BufRsrc rb = buf_rsrc(a.bnd + ((size_t)(abase + c) * H + h) * SS, (uint32_t)(SS * sizeof(float)));
-#pragma unroll
-    for (int im = 0; im < DK / 16; ++im)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[im][0]), rb,
-                                             (uint32_t)(((jb0 * (DK / 16) + im) * 64 + lane) * 16), 0, kAuxAgent);
-  };
-  auto all_stores_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  if (nall > 0) store_bnd(0);
-  u32x4 R[kPer];
-  float G = 1.f;
-  if (nfull > 0) {
-    fetch(0, R);
-    G = gamn_of(0);
-  }
-  all_stores_done();
-  if (nfull > 0) {
-    for (int m = 0; m < kPer; ++m) stage[tid + m * kThreads] = R[m];
-    if (tid == 0) gn_stage = G;
-    const int c1 = min(1, nfull - 1);
-    fetch(c1, R);
-    G = gamn_of(c1);
-  }
-  __syncthreads();
-  if (tid == 0 && nall > 0) publish_count(rdy, 1);
-  // Step c: the stage holds chunk c's products, R chunk c+1's.  After the
-  // step's products every wave waits for its outstanding memory operations
-  // (the boundary B_c stored and the fetch issued one step earlier), so once
-  // all waves are past the barrier B_0 .. B_c are complete and published.
-  for (int c = 0; c < nfull; ++c) {
-    f32x4 Ut[C / 16][1];
-#pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm)
-      Ut[tm][0] = __builtin_bit_cast(f32x4, stage[kFragPieces + (wave * (C / 16) + tm) * 64 + lane]);
-    chain_step_bf16<DK, 1>(
-        S, [&](int kb, int tm) { return stage[(kb * (C / 16) + tm) * 64 + lane]; },
-        [&](int kb, int im) { return stage[(int)(Sl::oKF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut,
-        gn_stage);
-    all_stores_done();
-    __syncthreads();  // every wave is done with the stage; B_c is complete
-    if (tid == 0) publish_count(rdy, c + 1);
-    if (c + 1 < nall) store_bnd(c + 1);
-    if (c + 1 < nfull) {
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) stage[tid + m * kThreads] = R[m];
-      if (tid == 0) gn_stage = G;
-      const int cf = min(c + 2, nfull - 1);
-      fetch(cf, R);
-      G = gamn_of(cf);
-    }
-    __syncthreads();  // the stage holds chunk c+1
-  }
-  all_stores_done();
-  __syncthreads();
-  if (tid == 0 && nall > 0) publish_count(rdy, nall);
-  store_state_tiles<DK, DV, 1>(a.s_bnd + ch * SS, S, jb0, lane);
-  if (L % Cl == 0) {
-    store_state_tiles<DK, DV, 1>(a.s_run + ch * SS, S, jb0, lane);
-    if (a.hT) store_state_tiles<DK, DV, 1>(a.hT + sh * SS, S, jb0, lane);
-  }
-  if (z == 0 && tid == 0) {
-    a.tail_len[ch] = L % Cl;
-    if (L % Cl == 0 && a.lgs) a.lgs[ch] = 0.f;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// decode: one work-group per (sequence, head); a thread per state column (two
-// per column at d_k = 256, one per key half: ColumnLanes)
-
-// Where thread `tid` of a work-group of DV * kParts threads sits: its state
-// column, its first key row, and whether it writes the column's per-column
-// outputs (the lower key half does).
-template <int DK>
-struct ColumnLanes {
-  int lane, col, k0;
-  bool writer;
-  __device__ explicit ColumnLanes(int tid) {
-    constexpr int WC = KeySplit<DK>::kCols;
-    lane = tid & 63;
-    col = (tid >> 6) * WC + lane % WC;
-    k0 = (lane / WC) * KeySplit<DK>::kKeys;
-    writer = lane < WC;
-  }
-};
-
-template <int DK, int DV>
-constexpr int kColumnThreads = DV * KeySplit<DK>::kParts;
-
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_decode(const DecodeArgs a) {
-  using T = typename D::T;
-  constexpr int KL = KeySplit<DK>::kKeys, NTH = kColumnThreads<DK, DV>;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  const int tid = threadIdx.x;
-  const ColumnLanes<DK> cl(tid);
-  const int col = cl.col;
-  const size_t SS = (size_t)DK * DV;
-  const int tl = a.tail_len[ch];
-  const float lg = a.lgs[ch];
-  __syncthreads();  // every wave has read tail_len and lgs before they are rewritten below
-  const int Cl = a.Cl;
-  if ((unsigned)tl >= (unsigned)Cl) {  // not a valid cache: touch nothing
-    if (tid == 0) a.flag[sh] = 0;
-    return;
-  }
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
-  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
-  // the token's k, v, g, beta as stored, for the tail append at the end
-  // (loaded here, before any store, so the append needs no second read)
-  constexpr int KE = (DK + NTH - 1) / NTH;
-  T k_app[KE];
-#pragma unroll
-  for (int m = 0; m < KE; ++m) k_app[m] = tid + m * NTH < DK ? kp[kr * DK + tid + m * NTH] : T();
-  const T v_app = ((const T*)a.v)[sh * DV + col];
-  const T g_app = ((const T*)a.g)[sh], b_app = ((const T*)a.beta)[sh];
-  float* R = a.s_run + ch * SS;
-  float s[KL];
-  load_state_col<KL, DV>(s, R, (uint32_t)(SS * 4), cl.k0, col);
-  float lg_next = lg;
-  const float out = token_step_at<D, DK>(s, lg_next, kp + kr * DK, qp + kr * DK, D::load(&g_app, 0),
-                                         D::load(&b_app, 0), D::load(&v_app, 0), cl.lane);
-  if (cl.writer) D::store((T*)a.o, sh * DV + col, out);
-  // append the token to the tail
-  T* tk = (T*)a.tail_k + (ch * Cl + tl) * DK;
-#pragma unroll
-  for (int m = 0; m < KE; ++m)
-    if (tid + m * NTH < DK) tk[tid + m * NTH] = k_app[m];
-  if (cl.writer) ((T*)a.tail_v)[(ch * Cl + tl) * DV + col] = v_app;
-  if (tid == 0) {
-    ((T*)a.tail_g)[ch * Cl + tl] = g_app;
-    ((T*)a.tail_beta)[ch * Cl + tl] = b_app;
-  }
-  const bool full = (tl + 1 == Cl);
-  if (!full) {
-    store_state_col<KL, DV>(R, (uint32_t)(SS * 4), s, cl.k0, col, 1.f);
-    if (a.hT)  // the state itself, exp(lg) N (gdn_cpr_cache_state's product)
-      store_state_col<KL, DV>(a.hT + sh * SS, (uint32_t)(SS * 4), s, cl.k0, col, scale_of_log(lg_next));
-  }
-  if (tid == 0) {
-    a.tail_len[ch] = full ? 0 : tl + 1;
-    a.lgs[ch] = full ? 0.f : lg_next;  // a full tail resynchronises to a boundary (scale 1)
-    a.flag[sh] = full ? 3 : 0;         // the resync then also writes hT (if asked for)
-  }
-}
-
-// ---------------------------------------------------------------------------
-// the running state of every (sequence, head) from its scaled form:
-// out = exp(lg) * s_run, row-major [d_k][d_v] (the same product the scan
-// uses when it writes a final state itself)
-
-__global__ __launch_bounds__(256) void k_cache_state(const float* __restrict__ s_run, const float* __restrict__ lgs,
-                                                    const int32_t* __restrict__ slot, float* __restrict__ out,
-                                                    int H, int SS4) {
-  const size_t sh = (size_t)blockIdx.x * H + blockIdx.y;
-  const size_t ch = cache_row(slot, blockIdx.x) * H + blockIdx.y;
-  const float e = scale_of_log(lgs[ch]);
-  const float4* src = reinterpret_cast<const float4*>(s_run) + ch * SS4;
-  float4* dst = reinterpret_cast<float4*>(out) + sh * SS4;
-  for (int i = threadIdx.x; i < SS4; i += 256) {
-    const float4 x = src[i];
-    dst[i] = make_float4(e * x.x, e * x.y, e * x.z, e * x.w);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// prefill continued from a cache: the head of each sequence (the tokens that
-// complete the cache's partial chunk) runs the decode step token by token;
-// the resynchronisation kernels then close that chunk, and the rest of the
-// sequence (which starts on a chunk boundary) goes through the prefill
-// kernels from the new boundary state.
-
-struct ContArgs {
-  const int32_t* slot;  // [N] cache row of sequence i, or null (row i)
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* g;
-  const void* beta;
-  const int32_t* cu;
-  float* s_run;
-  void* tail_k;
-  void* tail_v;
-  void* tail_g;
-  void* tail_beta;
-  int32_t* tail_len;
-  float* lgs;  // [rows, H] log-scale of s_run
-  float* hT;   // [N, H, DK, DV] final state (batch order), or null
-  void* o;
-  int32_t* flag;        // [N*H] as DecodeArgs::flag: bit 0 the head closes the chunk, bit 1 the resync writes hT
-  int32_t* body_start;  // [N] first token row after the head
-  int32_t N;
-  int32_t H;
-  int32_t Hk;  // heads of q and k
-  int32_t G;   // value heads per key head, H / Hk
-  int32_t Cl;  // chunk length
-};
-
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(DV * KeySplit<DK>::kParts) void k_cont_head(const ContArgs a) {
-  using T = typename D::T;
-  constexpr int KL = KeySplit<DK>::kKeys, NTH = kColumnThreads<DK, DV>;
-  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
-  const size_t sh = (size_t)i * H + h;
-  const size_t ch = cache_row(a.slot, i) * H + h;
-  const int tid = threadIdx.x;
-  const ColumnLanes<DK> cl(tid);
-  const int col = cl.col;
-  const size_t SS = (size_t)DK * DV;
-  const int tl = a.tail_len[ch];
-  float lg = a.lgs[ch];
-  __syncthreads();  // every wave has read tail_len and lgs before they are rewritten below
-  const int L = a.cu[i + 1] - a.cu[i];
-  const int Cl = a.Cl;
-  const int nh = ((unsigned)tl < (unsigned)Cl && tl > 0) ? min(Cl - tl, L) : 0;
-  if (h == 0 && tid == 0) a.body_start[i] = a.cu[i] + nh;
-  if (tid == 0) a.flag[sh] = 0;
-  float* R = a.s_run + ch * SS;
-  if (L == 0) {  // nothing new: the final state is the cached one
-    if (a.hT) {
-      float x[KL];
-      load_state_col<KL, DV>(x, R, (uint32_t)(SS * 4), cl.k0, col);
-      store_state_col<KL, DV>(a.hT + sh * SS, (uint32_t)(SS * 4), x, cl.k0, col, scale_of_log(lg));
-    }
-    return;
-  }
-  if (nh == 0) return;  // the body prefill writes the final state
-  float s[KL];
-  load_state_col<KL, DV>(s, R, (uint32_t)(SS * 4), cl.k0, col);
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
-  const T* vp = (const T*)a.v;
-  const T* gp = (const T*)a.g;
-  const T* bp = (const T*)a.beta;
-  constexpr int KE = (DK + NTH - 1) / NTH;
-  for (int t = 0; t < nh; ++t) {
-    const size_t row = (size_t)(a.cu[i] + t) * H + h;
-    const size_t kr = kq_row((size_t)(a.cu[i] + t), h, a.Hk, a.G);
-    // the token's k, v, g, beta as stored, for the tail append below (read
-    // before the output store, so the append needs no second read)
-    T k_app[KE];
-#pragma unroll
-    for (int m = 0; m < KE; ++m) k_app[m] = tid + m * NTH < DK ? kp[kr * DK + tid + m * NTH] : T();
-    const T v_app = vp[row * DV + col], g_app = gp[row], b_app = bp[row];
-    const float out = token_step_at<D, DK>(s, lg, kp + kr * DK, qp + kr * DK, D::load(&g_app, 0),
-                                           D::load(&b_app, 0), D::load(&v_app, 0), cl.lane);
-    if (cl.writer) D::store((T*)a.o, row * DV + col, out);
-    const size_t tr = ch * Cl + tl + t;  // tail row
-    T* tk = (T*)a.tail_k + tr * DK;
-#pragma unroll
-    for (int m = 0; m < KE; ++m)
-      if (tid + m * NTH < DK) tk[tid + m * NTH] = k_app[m];
-    if (cl.writer) ((T*)a.tail_v)[tr * DV + col] = v_app;
-    if (tid == 0) {
-      ((T*)a.tail_g)[tr] = g_app;
-      ((T*)a.tail_beta)[tr] = b_app;
-    }
-  }
-  const bool full = (tl + nh == Cl);
-  if (!full) {
-    store_state_col<KL, DV>(R, (uint32_t)(SS * 4), s, cl.k0, col, 1.f);
-    if (a.hT)  // the head is the whole segment (nh == L): exp(lg) N is the final state
-      store_state_col<KL, DV>(a.hT + sh * SS, (uint32_t)(SS * 4), s, cl.k0, col, scale_of_log(lg));
-  }
-  if (tid == 0) {
-    a.tail_len[ch] = full ? 0 : tl + nh;
-    a.lgs[ch] = full ? 0.f : lg;
-    // a closed chunk resynchronises; with no body after it, that boundary is the final state
-    a.flag[sh] = full ? (nh == L ? 3 : 1) : 0;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// comparators (not CPR): the two evaluation orders whose mismatch the pages
-// describe, built from this library's routines (English page, CPR section
-// and its table; Chinese page, third-way section):
-//   recurrent everywhere   the token step over each whole sequence, and the
-//                          same step for decode (no chunk boundaries)
-//   chunkwise everywhere   boundary states over every chunk (the last,
-//                          partial chunk zero-padded) and the outputs from the
-//                          chunk form O = diag(Gamma) Q B + (Q K^T .* D) Delta,
-//                          with no per-token scan
-// "Native mixed" serving is the chunkwise prefill followed by the recurrent
-// decode: both are exact in exact arithmetic, but they round differently.
-
-struct CmpArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* g;
-  const void* beta;
-  const int32_t* cu;
-  const float* h0;
-  float* state;  // [N, H, DK, DV] final state (prefill) / running state (decode)
-  void* o;
-  int32_t* all_base;
-  uint8_t* prod;
-  float* gamn;
-  float* bnd;
-  int32_t N;
-  int32_t H;
-  int32_t Hk;  // heads of q and k
-  int32_t G;   // value heads per key head, H / Hk
-};
-
-// recurrent prefill: one wave per (sequence, head, 64 state columns), the
-// scan's operand delivery (DPP row broadcast) over every token in order
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(64, 3) void k_cmp_rec_prefill(const CmpArgs a) {
-  using T = typename D::T;
-  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
-  const int lane = threadIdx.x, col = blockIdx.z * kWave + lane;
-  const int L = a.cu[i + 1] - a.cu[i];
-  const size_t sh = (size_t)i * H + h;
-  const size_t SS = (size_t)DK * DV;
-  float s[DK];
-#pragma unroll
-  for (int ii = 0; ii < DK; ++ii) s[ii] = a.h0 ? a.h0[sh * SS + (size_t)ii * DV + col] : 0.f;
-  const T* gp = (const T*)a.g;
-  const T* bp = (const T*)a.beta;
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
-  const T* vp = (const T*)a.v;
-  T* op = (T*)a.o;
-  for (int c0 = 0; c0 < L; c0 += kWave) {
-    const int n = min(kWave, L - c0);
-    const size_t tok0 = (size_t)a.cu[i] + c0;
-    float alpha_l = 1.f, beta_l = 0.f;
-    if (lane < n) {
-      const size_t r = (tok0 + lane) * H + h;
-      alpha_l = decay_of(D::load(gp, r));
-      beta_l = D::load(bp, r);
-    }
-    scan_tokens_plain<D, DK, DV>(s, kp, qp, vp, op, tok0 * H + h, H, kq_row(tok0, h, a.Hk, a.G), a.Hk, n, col,
-                                 lane, alpha_l, beta_l);
-  }
-#pragma unroll
-  for (int ii = 0; ii < DK; ++ii) a.state[sh * SS + (size_t)ii * DV + col] = s[ii];
-}
-
-// recurrent decode: the per-token step on the running state, nothing else
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(DV) void k_cmp_rec_decode(const CmpArgs a) {
-  using T = typename D::T;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
-  const int col = threadIdx.x;
-  float* R = a.state + sh * (size_t)DK * DV;
-  float s[DK];
-#pragma unroll
-  for (int ii = 0; ii < DK; ++ii) s[ii] = R[(size_t)ii * DV + col];
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
-  const float alpha = decay_of(D::load((const T*)a.g, sh));
-  const float bt = D::load((const T*)a.beta, sh);
-  const float vv = D::load((const T*)a.v, sh * DV + col);
-  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
-  KQRaw<D> raw;
-  load_kq<D, DK>(raw, kp + kr * DK, qp + kr * DK, col);
-  float kf[8], qf[8];
-  unpack_kq<D>(raw, kf, qf);
-  const float out = token_step_plain<DK>(s, kf, qf, alpha, bt, vv);
-  D::store((T*)a.o, sh * DV + col, out);
-#pragma unroll
-  for (int ii = 0; ii < DK; ++ii) R[(size_t)ii * DV + col] = s[ii];
-}
-
-// chunkwise: chunk products of every chunk slot, a partial chunk padded with
-// k = v = 0, g = beta = 0 (identity steps)
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 3) void k_cmp_chunk_local_bf16(const CmpArgs a) {
-  typedef SlotB<DK, DV> Sl;
-  __shared__ ChunkLdsB<DK, DV> sm;
-  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
-  if (slot >= a.all_base[a.N]) return;
-  const int i = find_seq(a.all_base, a.N, slot);
-  const int c = slot - a.all_base[i];
-  const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
-  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
-  const size_t row0 = tok0 * H + h, kq0 = kq_row(tok0, h, a.Hk, a.G);
-  stage_chunk_bf16<DK, DV>(sm, (const uint16_t*)a.k, kq0, a.Hk, (const uint16_t*)a.v, row0, H,
-                           (const uint16_t*)a.g, (const uint16_t*)a.beta, row0, H, n);
-  const size_t ps = (size_t)slot * H + h;
-  chunk_local_bf16<DK, DV>(sm, a.prod + ps * Sl::bytes, a.gamn + ps);
-}
-
-// chunkwise outputs: per (chunk slot, head), 4 waves x 32 state columns
-//   Delta = U + Wneg bf16(B)                       (as the chain's first phase)
-//   O     = diag(Gamma) (Q bf16(B)) + bf16(P) bf16(Delta),  P = (Q K^T) .* D
-template <int DK, int DV>
-struct CmpOutLds {
-  uint16_t Q[C][DK + 8];
-  uint16_t K[C][DK + 8];
-  uint16_t P[C][C + 8];
-  float g[C], gam[C], Gam[C];
-};
-
-// gamma, Gamma and P = bf16((Q K^T) .* D) of a chunk staged in sm (Q, K, g)
-template <int DK, int DV>
-__device__ __forceinline__ void cmp_out_prepare(CmpOutLds<DK, DV>& sm) {
-  using namespace mfma;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  if (tid == 0) {
-    float acc = sm.g[0];
-    sm.gam[0] = acc;
-    for (int t = 1; t < C; ++t) {
-      acc = acc + sm.g[t];
-      sm.gam[t] = acc;
-    }
-  }
-  __syncthreads();
-  if (tid < C) sm.Gam[tid] = expf(sm.gam[tid]);
-  for (int q2 = wave; q2 < 16; q2 += 4) {
-    const int tm = q2 >> 2, tn = q2 & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (tn <= tm) {
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb)
-        acc = mma(frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g), frag_row(&sm.K[16 * tn + lr][0], 32 * kb, g), acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tm + 4 * g + r, s2 = 16 * tn + lr;
-      sm.P[t][s2] = Bf16::round(s2 <= t ? acc[r] * expf(sm.gam[t] - sm.gam[s2]) : 0.f);
-    }
-  }
-  __syncthreads();
-}
-
-// Chunkwise outputs of the 16-row tiles tm0 <= tm < tm1 of one chunk, this
-// wave's DV / 4 state columns: S = the chunk's start state (accumulator
-// tiles), sl = its product slot.  out(row, column, value) receives each.
-template <int DK, int DV, class Out>
-__device__ __forceinline__ void cmp_out_rows(const CmpOutLds<DK, DV>& sm, const mfma::f32x4 (&S)[DK / 16][DV / 64],
-                                             const uint8_t* sl, int tm0, int tm1, Out&& out) {
-  using namespace mfma;
-  typedef SlotB<DK, DV> Sl;
-  constexpr int NT = DV / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4;
-  const int jb0 = wave * NT;
-  const u32x4* WF = reinterpret_cast<const u32x4*>(sl + Sl::oWF);
-  const f32x4* UT = reinterpret_cast<const f32x4*>(sl + Sl::oU);
-  u32x4 Sb[DK / 32][NT];
-#pragma unroll
-  for (int kb = 0; kb < DK / 32; ++kb)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) Sb[kb][nt] = frag_from_acc(S[2 * kb][nt], S[2 * kb + 1][nt]);
-  f32x4 Dl[C / 16][NT];
-#pragma unroll
-  for (int tm = 0; tm < C / 16; ++tm)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) Dl[tm][nt] = UT[((jb0 + nt) * (C / 16) + tm) * 64 + lane];
-#pragma unroll
-  for (int kb = 0; kb < DK / 32; ++kb)
-#pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) {
-      const u32x4 w = WF[(kb * (C / 16) + tm) * 64 + lane];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) Dl[tm][nt] = mma(w, Sb[kb][nt], Dl[tm][nt]);
-    }
-  u32x4 Db[C / 32][NT];
-#pragma unroll
-  for (int kb = 0; kb < C / 32; ++kb)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) Db[kb][nt] = frag_from_acc(Dl[2 * kb][nt], Dl[2 * kb + 1][nt]);
-#pragma unroll
-  for (int tm = 0; tm < C / 16; ++tm) {
-    if (tm < tm0 || tm >= tm1) continue;
-    f32x4 O[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
-      const u32x4 qf = frag_row(&sm.Q[16 * tm + lr][0], 32 * kb, g);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) O[nt] = mma(qf, Sb[kb][nt], O[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[nt][r] *= sm.Gam[16 * tm + 4 * g + r];
-#pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb) {
-      const u32x4 pf = frag_row(&sm.P[16 * tm + lr][0], 32 * kb, g);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) O[nt] = mma(pf, Db[kb][nt], O[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) out(16 * tm + 4 * g + r, 16 * (jb0 + nt) + lr, O[nt][r]);
-  }
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_cmp_chunk_out_bf16(const CmpArgs a) {
-  typedef SlotB<DK, DV> Sl;
-  constexpr int NT = DV / 64;  // 16-column tiles per wave
-  __shared__ CmpOutLds<DK, DV> sm;
-  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
-  if (slot >= a.all_base[a.N]) return;
-  const int i = find_seq(a.all_base, a.N, slot);
-  const int c = slot - a.all_base[i];
-  const int n = min(C, a.cu[i + 1] - a.cu[i] - c * C);
-  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * C;
-  const size_t row0 = tok0 * H + h, kq0 = kq_row(tok0, h, a.Hk, a.G);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint16_t* qp = (const uint16_t*)a.q;
-  const uint16_t* kp = (const uint16_t*)a.k;
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  for (int idx = tid; idx < C * DK / 8; idx += 256) {
-    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
-    if (t < n) {
-      wq = *reinterpret_cast<const u32x4v*>(qp + (kq0 + (size_t)t * a.Hk) * DK + i0);
-      wk = *reinterpret_cast<const u32x4v*>(kp + (kq0 + (size_t)t * a.Hk) * DK + i0);
-    }
-    *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
-    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
-  }
-  if (tid < C) sm.g[tid] = tid < n ? Bf16::load((const uint16_t*)a.g, row0 + (size_t)tid * H) : 0.f;
-  __syncthreads();
-  cmp_out_prepare(sm);
-  const size_t ps = (size_t)slot * H + h;
-  const float* B = a.bnd + ps * (size_t)DK * DV;
-  const int jb0 = wave * NT;
-  mfma::f32x4 S[DK / 16][NT];
-#pragma unroll
-  for (int im = 0; im < DK / 16; ++im)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      S[im][nt] = *reinterpret_cast<const mfma::f32x4*>(B + ((size_t)((jb0 + nt) * (DK / 16) + im) * 64 + lane) * 4);
-  uint16_t* op = (uint16_t*)a.o;
-  cmp_out_rows(sm, S, a.prod + ps * Sl::bytes, 0, C / 16, [&](int t, int col, float val) {
-    if (t < n) op[(row0 + (size_t)t * H) * DV + col] = Bf16::round(val);
-  });
-}
-
-// chunkwise-everywhere decode (comparator): every token recomputes the chunk
-// products of its partial chunk -- the cached tail, then the token, then zero
-// padding -- and takes its output from the chunk form on the cache's boundary
-// state, as the chunkwise prefill does for the same token.  When the token
-// completes the chunk, k_chain_resync_bf16 moves the boundary (s_run follows
-// it then; between boundaries this comparator leaves s_run alone).
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 3) void k_cmp_cdec_local_bf16(const DecodeArgs a) {
-  __shared__ ChunkLdsB<DK, DV> sm;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  const int tl = a.tail_len[ch];
-  if ((unsigned)tl >= (unsigned)C) return;
-  const int tid = threadIdx.x;
-  const size_t kr = kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G);
-  const uint16_t* tk = (const uint16_t*)a.tail_k;
-  const uint16_t* tv = (const uint16_t*)a.tail_v;
-  const uint16_t* kp = (const uint16_t*)a.k;
-  const uint16_t* vp = (const uint16_t*)a.v;
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  // rows t < tl from the tail, row tl the token, rows past it zero: every
-  // load is issued (rows past tl load the token again) before the LDS writes
-  constexpr int MK = C * DK / 8 / 256, MV = C * DV / 8 / 256;
-  u32x4v lk[MK], lv[MV];
-#pragma unroll
-  for (int m = 0; m < MK; ++m) {
-    const int idx = tid + 256 * m, t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    const uint16_t* src = t < tl ? tk + (ch * C + t) * DK : kp + kr * DK;
-    lk[m] = *reinterpret_cast<const u32x4v*>(src + i0);
-  }
-#pragma unroll
-  for (int m = 0; m < MV; ++m) {
-    const int idx = tid + 256 * m, t = idx / (DV / 8), j0 = (idx % (DV / 8)) * 8;
-    const uint16_t* src = t < tl ? tv + (ch * C + t) * DV : vp + sh * DV;
-    lv[m] = *reinterpret_cast<const u32x4v*>(src + j0);
-  }
-  const int ts = min(tid, C - 1);
-  const uint16_t* gs = ts < tl ? (const uint16_t*)a.tail_g : (const uint16_t*)a.g;
-  const uint16_t* bs = ts < tl ? (const uint16_t*)a.tail_beta : (const uint16_t*)a.beta;
-  const size_t r = ts < tl ? ch * C + ts : sh;
-  const float gl = Bf16::load(gs, r), bl = Bf16::load(bs, r);
-  const u32x4v zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int m = 0; m < MK; ++m) {
-    const int idx = tid + 256 * m, t = idx / (DK / 8);
-    *reinterpret_cast<u32x4v*>(&sm.K[t][(idx % (DK / 8)) * 8]) = t <= tl ? lk[m] : zero;
-  }
-#pragma unroll
-  for (int m = 0; m < MV; ++m) {
-    const int idx = tid + 256 * m, t = idx / (DV / 8);
-    *reinterpret_cast<u32x4v*>(&sm.V[t][(idx % (DV / 8)) * 8]) = t <= tl ? lv[m] : zero;
-  }
-  if (tid < C) {
-    sm.gam[tid] = tid <= tl ? gl : 0.f;
-    sm.beta[tid] = tid <= tl ? bl : 0.f;
-  }
-  __syncthreads();
-  chunk_local_bf16<DK, DV>(sm, a.prod + sh * prod_slot_bytes(true, DK, DV), a.gamn + sh);
-  // append the token to the tail (row tl of the tail is read by no kernel of this step)
-  uint16_t* wk = (uint16_t*)a.tail_k + (ch * C + tl) * DK;
-  uint16_t* wv = (uint16_t*)a.tail_v + (ch * C + tl) * DV;
-  for (int e = tid; e < DK; e += 256) wk[e] = kp[kr * DK + e];
-  for (int e = tid; e < DV; e += 256) wv[e] = vp[sh * DV + e];
-  if (tid == 0) {
-    ((uint16_t*)a.tail_g)[ch * C + tl] = ((const uint16_t*)a.g)[sh];
-    ((uint16_t*)a.tail_beta)[ch * C + tl] = ((const uint16_t*)a.beta)[sh];
-  }
-}
-
-// its output row, then tail_len and the resynchronisation flag
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_cmp_cdec_out_bf16(const DecodeArgs a) {
-  constexpr int NT = DV / 64;
-  __shared__ CmpOutLds<DK, DV> sm;
-  const size_t sh = (size_t)blockIdx.x * a.H + blockIdx.y;
-  const size_t ch = cache_row(a.slot, blockIdx.x) * a.H + blockIdx.y;
-  const int tl = a.tail_len[ch];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  __syncthreads();  // every wave has read tail_len before it is rewritten below
-  if ((unsigned)tl >= (unsigned)C) {
-    if (tid == 0) a.flag[sh] = 0;
-    return;
-  }
-  const uint16_t* tk = (const uint16_t*)a.tail_k;
-  const uint16_t* qp = (const uint16_t*)a.q;
-  const uint16_t* kp = (const uint16_t*)a.k;
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  for (int idx = tid; idx < C * DK / 8; idx += 256) {
-    const int t = idx / (DK / 8), i0 = (idx % (DK / 8)) * 8;
-    u32x4v wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
-    if (t < tl) wk = *reinterpret_cast<const u32x4v*>(tk + (ch * C + t) * DK + i0);
-    if (t == tl) {
-      wq = *reinterpret_cast<const u32x4v*>(qp + kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G) * DK + i0);
-      wk = *reinterpret_cast<const u32x4v*>(kp + kq_row(blockIdx.x, blockIdx.y, a.Hk, a.G) * DK + i0);
-    }
-    *reinterpret_cast<u32x4v*>(&sm.Q[t][i0]) = wq;
-    *reinterpret_cast<u32x4v*>(&sm.K[t][i0]) = wk;
-  }
-  if (tid < C)
-    sm.g[tid] = tid < tl ? Bf16::load((const uint16_t*)a.tail_g, ch * C + tid)
-                         : (tid == tl ? Bf16::load((const uint16_t*)a.g, sh) : 0.f);
-  __syncthreads();
-  cmp_out_prepare(sm);
-  mfma::f32x4 S[DK / 16][NT];
-  load_state_tiles<DK, DV, NT>(S, a.s_bnd + ch * (size_t)DK * DV, wave * NT, lane);
-  uint16_t* op = (uint16_t*)a.o;
-  cmp_out_rows(sm, S, a.prod + sh * prod_slot_bytes(true, DK, DV), tl / 16, tl / 16 + 1,
-               [&](int t, int col, float val) {
-                 if (t == tl) op[sh * DV + col] = Bf16::round(val);
-               });
-  if (tid == 0) {
-    const bool full = (tl + 1 == C);
-    a.tail_len[ch] = full ? 0 : tl + 1;
-    a.flag[sh] = full ? 1 : 0;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// backward (fwd_bwd): per-chunk local terms, reverse boundary chain, gradients
-
-struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* g;
-  const void* beta;
-  const void* d_o;
-  const int32_t* cu;
-  const int32_t* all_base;
-  const float* bnd;   // forward state at the start of every chunk slot
-  const float* d_hT;  // [N,H,DK,DV] or null
-  uint8_t* ws;        // [A_max*H] backward slots
-  float* gamn;        // [A_max*H]
-  void* dq;
-  void* dk;
-  void* dv;
-  float* dg;
-  float* dbeta;
-  float* dh0;
-  float* dq_part;  // [T, H, DK] fp32 per value head when key heads are shared, else null
-  float* dk_part;
-  int32_t N;
-  int32_t H;
-  int32_t Hk;  // heads of q and k
-  int32_t G;   // value heads per key head, H / Hk
-  int32_t Cl;  // chunk length
-};
-
-template <int DK, int DV>
-struct BwdLocalLds {
-  float At[C][C + 1];  // At[s][t] = A[t][s]
-  float X[C][C + 1];
-  float Pt[C][C + 1];  // Pt[s][t] = P[t][s]
-  float W[C][DK + 1];
-  float Dd[C][DV + 1];
-  bwd::ChunkScalars cs;
-};
-
-// B1: per chunk slot (full or partial) and head: X, W, Kt, -W^T, dDelta_local
-// = P^T dO and R = (diag(Gamma) Q)^T dO - W^T dDelta_local.
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
-  using namespace bwd;
-  using T = typename D::T;
-  typedef BwdSlot<DK, DV, sizeof(T)> Slot;
-  __shared__ BwdLocalLds<DK, DV> sm;
-  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
-  if (slot >= a.all_base[a.N]) return;
-  const int i = find_seq(a.all_base, a.N, slot);
-  const int c = slot - a.all_base[i];
-  const int L = a.cu[i + 1] - a.cu[i];
-  const int n = min(a.Cl, L - c * a.Cl);
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * a.Cl) * H + h;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
-  const T* dop = (const T*)a.d_o;
-  chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
-  const ChunkScalars& cs = sm.cs;
-  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
-  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
-  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
-  auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
-  uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
-
-  // A = strict lower(beta_t D G) and P = lower(QK^T .* D): 16 + 16 tiles
-  for (int q = 0; q < 8; ++q) {
-    const int id = wave * 8 + q, tl = id & 15, tm = tl >> 2, tn = tl & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (id < 16) {
-      acc = tile<DK>([&](int m, int k) { return Kx(m, k); }, [&](int k, int nn) { return Kx(nn, k); }, 16 * tm,
-                     16 * tn, acc);
-      tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) {
-        sm.At[s][t] = (s < t) ? (cs.beta[t] * expf(cs.gam[t] - cs.gam[s])) * v : 0.f;
-      });
-    } else {
-      acc = tile<DK>([&](int m, int k) { return Qx(m, k); }, [&](int k, int nn) { return Kx(nn, k); }, 16 * tm,
-                     16 * tn, acc);
-      tile_each(acc, 16 * tm, 16 * tn,
-                [&](int t, int s, float v) { sm.Pt[s][t] = (s <= t) ? v * expf(cs.gam[t] - cs.gam[s]) : 0.f; });
-    }
-  }
-  __syncthreads();
-  if (wave == 0) unit_lower_inverse<C + 1, C + 1>(sm.At, sm.X);
-  __syncthreads();
-  float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
-  constexpr int nW = 4 * (DK / 16), nD = 4 * (DV / 16);
-  for (int id = wave; id < nW + nD; id += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (id < nW) {
-      const int tm = id / (DK / 16), it = id % (DK / 16);
-      acc = tile<C>([&](int t, int r) { return sm.X[t][r] * (cs.beta[r] * cs.Gam[r]); },
-                    [&](int r, int e) { return Kx(r, e); }, 16 * tm, 16 * it, acc);
-      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.W[t][e] = v; });
-    } else {
-      const int u = id - nW, tm = u / (DV / 16), jt = u % (DV / 16);
-      acc = tile<C>([&](int t, int s) { return sm.Pt[t][s]; }, [&](int s, int j) { return dOx(s, j); }, 16 * tm,
-                    16 * jt, acc);
-      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.Dd[t][j] = v; });
-      *reinterpret_cast<f32x4*>(Dd + ((size_t)(jt * (C / 16) + tm) * 64 + (tid & 63)) * 4) = acc;
-    }
-  }
-  __syncthreads();
-  T* Kt = reinterpret_cast<T*>(ws + Slot::oKt);
-  T* WnT = reinterpret_cast<T*>(ws + Slot::oWnT);
-  float* Xs = reinterpret_cast<float*>(ws + Slot::oX);
-  for (int idx = tid; idx < C * DK; idx += 256) {
-    const int t = idx / DK, e = idx % DK;
-    D::store(Kt, idx, cs.e[t] * Kx(t, e));
-    D::store(WnT, (size_t)e * C + t, -sm.W[t][e]);
-  }
-  for (int idx = tid; idx < C * C; idx += 256) Xs[idx] = sm.X[idx / C][idx % C];
-  float* R = reinterpret_cast<float*>(ws + Slot::oR);
-  constexpr int nR = (DK / 16) * (DV / 16);
-  for (int id = wave; id < nR; id += 4) {
-    const int im = id / (DV / 16), jt = id % (DV / 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<C>([&](int e, int t) { return cs.Gam[t] * Qx(t, e); }, [&](int t, int j) { return dOx(t, j); },
-                  16 * im, 16 * jt, acc);
-    acc = tile<C>([&](int e, int t) { return -sm.W[t][e]; }, [&](int t, int j) { return sm.Dd[t][j]; }, 16 * im,
-                  16 * jt, acc);
-    *reinterpret_cast<f32x4*>(R + ((size_t)(jt * (DK / 16) + im) * 64 + (tid & 63)) * 4) = acc;
-  }
-  if (tid == 0) a.gamn[(size_t)slot * H + h] = cs.Gam[C - 1];
-}
-
-// B2 for fp32 inputs: the same reverse chain with fp32 operands on
-// v_mfma_f32_16x16x4_f32.  The k index of step m in a 16-row tile is
-// 16 tile + 4 g + m, so accumulator tiles (lane group g holds rows 4 g .. 4 g
-// + 3) are B operands as they stand.
-template <int DK, int DV>
-__global__ __launch_bounds__(DV * 4) void k_bwd_chain_f32(const BwdArgs a) {
-  using namespace bwd;
-  typedef BwdSlot<DK, DV, 4> Slot;
-  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
-  const int tid = threadIdx.x, jb = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int L = a.cu[i + 1] - a.cu[i];
-  const int nall = (L + a.Cl - 1) / a.Cl;
-  const size_t sh = (size_t)i * H + h;
-  const size_t SS = (size_t)DK * DV;
-  const int abase = a.all_base[i];
-  f32x4 S1[DK / 16][1];
-  load_state_tiles<DK, DV, 1>(S1, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
-  f32x4(&S)[DK / 16] = *reinterpret_cast<f32x4(*)[DK / 16]>(&S1);
-  for (int c = nall - 1; c >= 0; --c) {
-    const size_t sl = (size_t)(abase + c) * H + h;
-    uint8_t* ws = a.ws + sl * Slot::bytes;
-    store_state_tiles<DK, DV, 1>(reinterpret_cast<float*>(ws + Slot::oDbp), S1, jb, lane);
-    const float* Kt = reinterpret_cast<const float*>(ws + Slot::oKt);
-    const float* WnT = reinterpret_cast<const float*>(ws + Slot::oWnT);
-    const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
-    float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
-    f32x4 E[C / 16];
-#pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int it = 0; it < DK / 16; ++it)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mma4(Kt[(16 * tm + lr) * DK + 16 * it + 4 * g + m], S[it][m], acc);
-      E[tm] = acc;
-      f32x4* dd = reinterpret_cast<f32x4*>(Dd + ((size_t)(jb * (C / 16) + tm) * 64 + lane) * 4);
-      *dd = *dd + acc;
-    }
-    const float gn = a.gamn[sl];
-#pragma unroll
-    for (int im = 0; im < DK / 16; ++im) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(R + ((size_t)(jb * (DK / 16) + im) * 64 + lane) * 4);
-      f32x4 acc = {gn * S[im][0] + r[0], gn * S[im][1] + r[1], gn * S[im][2] + r[2], gn * S[im][3] + r[3]};
-#pragma unroll
-      for (int tm = 0; tm < C / 16; ++tm)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mma4(WnT[(16 * im + lr) * C + 16 * tm + 4 * g + m], E[tm][m], acc);
-      S[im] = acc;
-    }
-  }
-  if (a.dh0) store_state_tiles<DK, DV, 1>(a.dh0 + sh * SS, S1, jb, lane);
-}
-
-template <int DK, int DV>
-struct BwdGradLds {
-  static constexpr int DM = DK > DV ? DK : DV;
-  float N1[C][C + 1];   // G
-  float N2[C][C + 1];   // dT -> dX -> dA -> dG
-  float N3[C][C + 1];   // X
-  float N4[C][C + 1];   // dPD = (dO Delta^T) .* D, lower incl.
-  float N5[C][C + 1];   // Z_P, then Y, then dA D G
-  float M1[C][DM + 1];  // W -> dO B^T -> dW -> T^T dW
-  float M2[C][DM + 1];  // U -> Delta -> dKt
-  bwd::ChunkScalars cs;
-  float rzP[C], czP[C], dGamO[C], dGamW[C], de[C], dbc[C], dbr[C], rzA[C], czA[C];
-  float red[256];
-};
-
-// B3: per chunk slot and head: dq, dk, dv, dg, dbeta of the chunk's tokens.
-template <class D, int DK, int DV>
-__global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
-  using namespace bwd;
-  using T = typename D::T;
-  typedef BwdSlot<DK, DV, sizeof(T)> Slot;
-  __shared__ BwdGradLds<DK, DV> sm;
-  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
-  if (slot >= a.all_base[a.N]) return;
-  const int i = find_seq(a.all_base, a.N, slot);
-  const int c = slot - a.all_base[i];
-  const int L = a.cu[i + 1] - a.cu[i];
-  const int n = min(a.Cl, L - c * a.Cl);
-  const size_t row0 = ((size_t)a.cu[i] + (size_t)c * a.Cl) * H + h;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const T* kp = (const T*)a.k;
-  const T* qp = (const T*)a.q;
-  const T* vp = (const T*)a.v;
-  const T* dop = (const T*)a.d_o;
-  chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
-  const ChunkScalars& cs = sm.cs;
-  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
-  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
-  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
-  auto Vx = [&](int t, int j) { return t < n ? D::load(vp, (row0 + (size_t)t * H) * DV + j) : 0.f; };
-  auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
-  const uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
-  const float* Bst = a.bnd + ((size_t)slot * H + h) * DK * DV;
-  const float* dBp = reinterpret_cast<const float*>(ws + Slot::oDbp);
-  const float* Ddg = reinterpret_cast<const float*>(ws + Slot::oDd);
-  const float* Xs = reinterpret_cast<const float*>(ws + Slot::oX);
-  auto dDx = [&](int t, int j) { return Ddg[tile_index<C>(t, j)]; };
-  constexpr int nK = 4 * (DK / 16), nV = 4 * (DV / 16);
-
-  // G and X
-  for (int q = 0; q < 4; ++q) {
-    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<DK>([&](int m, int k) { return Kx(m, k); }, [&](int k, int nn) { return Kx(nn, k); }, 16 * tm, 16 * tn,
-                   acc);
-    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N1[t][s] = v; });
-  }
-  for (int idx = tid; idx < C * C; idx += 256) sm.N3[idx / C][idx % C] = Xs[idx];
-  __syncthreads();
-  // W = X diag(beta Gamma) K -> M1,  U = X diag(beta) V -> M2
-  for (int id = wave; id < nK + nV; id += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (id < nK) {
-      const int tm = id / (DK / 16), it = id % (DK / 16);
-      acc = tile<C>([&](int t, int r) { return sm.N3[t][r] * (cs.beta[r] * cs.Gam[r]); },
-                    [&](int r, int e) { return Kx(r, e); }, 16 * tm, 16 * it, acc);
-      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
-    } else {
-      const int u = id - nK, tm = u / (DV / 16), jt = u % (DV / 16);
-      acc = tile<C>([&](int t, int r) { return sm.N3[t][r] * cs.beta[r]; }, [&](int r, int j) { return Vx(r, j); },
-                    16 * tm, 16 * jt, acc);
-      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.M2[t][j] = v; });
-    }
-  }
-  __syncthreads();
-  // Delta = U - W B (in place in M2; every tile is read and written by one wave)
-  for (int id = wave; id < nV; id += 4) {
-    const int tm = id / (DV / 16), jt = id % (DV / 16);
-    f32x4 acc;
-    {
-      const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = sm.M2[16 * tm + 4 * g + r][16 * jt + lr];
-    }
-    acc = tile<DK>([&](int t, int e) { return -sm.M1[t][e]; }, [&](int e, int j) { return Bst[bnd_index<DK>(e, j)]; },
-                   16 * tm, 16 * jt, acc);
-    tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.M2[t][j] = v; });
-  }
-  __syncthreads();
-  // dP .* D (N4), Z_P = dPD .* QK (N5); dV = T^T dDelta
-  for (int q = 0; q < 4; ++q) {
-    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
-    f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
-    accP = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int s) { return sm.M2[s][j]; }, 16 * tm,
-                    16 * tn, accP);
-    accQ = tile<DK>([&](int t, int e) { return Qx(t, e); }, [&](int e, int s) { return Kx(s, e); }, 16 * tm, 16 * tn,
-                    accQ);
-    const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tm + 4 * g + r, s = 16 * tn + lr;
-      const float dpd = (s <= t) ? accP[r] * expf(cs.gam[t] - cs.gam[s]) : 0.f;
-      sm.N4[t][s] = dpd;
-      sm.N5[t][s] = dpd * accQ[r];
-    }
-  }
-  T* dvp = (T*)a.dv;
-  for (int id = wave; id < nV; id += 4) {
-    const int tm = id / (DV / 16), jt = id % (DV / 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<C>([&](int t, int s) { return sm.N3[s][t]; }, [&](int s, int j) { return dDx(s, j); }, 16 * tm,
-                  16 * jt, acc);
-    tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) {
-      if (t < n) D::store(dvp, (row0 + (size_t)t * H) * DV + j, cs.beta[t] * v);
-    });
-  }
-  __syncthreads();
-  // row / column sums of Z_P; dO B^T -> M1
-  if (tid < C) {
-    float acc = 0.f;
-    for (int s = 0; s < C; ++s) acc += sm.N5[tid][s];
-    sm.rzP[tid] = acc;
-  } else if (tid < 2 * C) {
-    const int s = tid - C;
-    float acc = 0.f;
-    for (int t = 0; t < C; ++t) acc += sm.N5[t][s];
-    sm.czP[s] = acc;
-  }
-  for (int id = wave; id < nK; id += 4) {
-    const int tm = id / (DK / 16), it = id % (DK / 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int e) { return Bst[bnd_index<DK>(e, j)]; },
-                   16 * tm, 16 * it, acc);
-    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
-  }
-  __syncthreads();
-  // dQ = diag(Gamma) dO B^T + dPD K;  dGamma (output part) = <dO B^T, Q> per row
-  T* dqp = (T*)a.dq;
-  for (int id = wave; id < nK; id += 4) {
-    const int tm = id / (DK / 16), it = id % (DK / 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<C>([&](int t, int s) { return sm.N4[t][s]; }, [&](int s, int e) { return Kx(s, e); }, 16 * tm, 16 * it,
-                  acc);
-    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
-      if (t < n) {
-        const float val = cs.Gam[t] * sm.M1[t][e] + v;
-        if (a.dq_part)
-          a.dq_part[(row0 + (size_t)t * H) * DK + e] = val;
-        else
-          D::store(dqp, (kq0 + (size_t)t * a.Hk) * DK + e, val);
-      }
-    });
-  }
-  if (tid < C) {
-    float acc = 0.f;
-    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M1[tid][e], Qx(tid, e), acc);
-    sm.dGamO[tid] = acc;
-  }
-  __syncthreads();
-  // dW = -dDelta B^T -> M1
-  for (int id = wave; id < nK; id += 4) {
-    const int tm = id / (DK / 16), it = id % (DK / 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int e) { return Bst[bnd_index<DK>(e, j)]; },
-                   16 * tm, 16 * it, acc);
-    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = -v; });
-  }
-  __syncthreads();
-  // T^T dW and dKt = Delta dB'^T (kept in registers), dT -> N2
-  f32x4 TW[(nK + 3) / 4], KW[(nK + 3) / 4];
-  for (int q = 0, id = wave; id < nK; id += 4, ++q) {
-    const int tm = id / (DK / 16), it = id % (DK / 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    TW[q] = tile<C>([&](int t, int s) { return cs.beta[t] * sm.N3[s][t]; }, [&](int s, int e) { return sm.M1[s][e]; },
-                    16 * tm, 16 * it, acc);
-    KW[q] = tile<DV>([&](int t, int j) { return sm.M2[t][j]; }, [&](int j, int e) { return dBp[(size_t)e * DV + j]; },
-                     16 * tm, 16 * it, acc);
-  }
-  for (int q = 0; q < 4; ++q) {
-    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int s) { return Vx(s, j); }, 16 * tm, 16 * tn,
-                   acc);
-    acc = tile<DK>([&](int t, int e) { return sm.M1[t][e]; }, [&](int e, int s) { return cs.Gam[s] * Kx(s, e); },
-                   16 * tm, 16 * tn, acc);
-    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N2[t][s] = v; });
-  }
-  __syncthreads();
-  for (int q = 0, id = wave; id < nK; id += 4, ++q) {
-    const int tm = id / (DK / 16), it = id % (DK / 16);
-    tile_each(TW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
-    tile_each(KW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M2[t][e] = v; });
-  }
-  __syncthreads();
-  // dGamma (W part), de, dbeta (column part)
-  if (tid < C) {
-    float acc = 0.f;
-    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M1[tid][e], Kx(tid, e), acc);
-    sm.dGamW[tid] = acc;
-  } else if (tid < 2 * C) {
-    const int t = tid - C;
-    float acc = 0.f;
-    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M2[t][e], Kx(t, e), acc);
-    sm.de[t] = acc;
-  } else if (tid < 3 * C) {
-    const int s = tid - 2 * C;
-    float acc = 0.f;
-    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(sm.N3[t][s], sm.N2[t][s], acc);
-    sm.dbc[s] = acc;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < C * C; idx += 256) sm.N2[idx / C][idx % C] *= sm.cs.beta[idx % C];  // dX
-  __syncthreads();
-  // Y = dX X^T -> N5
-  for (int q = 0; q < 4; ++q) {
-    const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<C>([&](int t, int r) { return sm.N2[t][r]; }, [&](int r, int s) { return sm.N3[s][r]; }, 16 * tm,
-                  16 * tn, acc);
-    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N5[t][s] = v; });
-  }
-  __syncthreads();
-  // dA = -X^T Y, strict lower -> N2
-  {
-    f32x4 accs[4];
-    for (int q = 0; q < 4; ++q) {
-      const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      accs[q] = tile<C>([&](int t, int r) { return sm.N3[r][t]; }, [&](int r, int s) { return sm.N5[r][s]; }, 16 * tm,
-                        16 * tn, acc);
-    }
-    __syncthreads();
-    for (int q = 0; q < 4; ++q) {
-      const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
-      tile_each(accs[q], 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N2[t][s] = (s < t) ? -v : 0.f; });
-    }
-  }
-  __syncthreads();
-  // dA D G -> N5, dG = dA beta_t D -> N2
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int t = idx / C, s = idx % C;
-    const float dA = sm.N2[t][s];
-    float zb = 0.f, dG = 0.f;
-    if (s < t) {
-      const float Dv = expf(cs.gam[t] - cs.gam[s]);
-      zb = dA * Dv * sm.N1[t][s];
-      dG = dA * cs.beta[t] * Dv;
-    }
-    sm.N5[t][s] = zb;
-    sm.N2[t][s] = dG;
-  }
-  __syncthreads();
-  if (tid < C) {
-    float acc = 0.f;
-    for (int s = 0; s < C; ++s) acc += sm.N5[tid][s];
-    sm.dbr[tid] = acc;
-    sm.rzA[tid] = cs.beta[tid] * acc;
-  } else if (tid < 2 * C) {
-    const int s = tid - C;
-    float acc = 0.f;
-    for (int t = 0; t < C; ++t) acc = __builtin_fmaf(cs.beta[t], sm.N5[t][s], acc);
-    sm.czA[s] = acc;
-  }
-  {
-    float acc = 0.f;
-    for (int idx = tid; idx < DK * DV; idx += 256)
-      acc = __builtin_fmaf(dBp[idx], Bst[bnd_index<DK>(idx / DV, idx % DV)], acc);
-    sm.red[tid] = acc;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float dGn = 0.f;
-    for (int r = 0; r < 256; ++r) dGn += sm.red[r];
-    float sum_de = 0.f;
-    for (int t = 0; t < C; ++t) sum_de = __builtin_fmaf(sm.de[t], cs.e[t], sum_de);
-    float acc = 0.f;
-    for (int t = C - 1; t >= 0; --t) {
-      float dgam = (sm.rzP[t] + sm.rzA[t]) - (sm.czP[t] + sm.czA[t]) + (sm.dGamO[t] + sm.dGamW[t]) * cs.Gam[t] -
-                   sm.de[t] * cs.e[t];
-      if (t == C - 1) dgam += dGn * cs.Gam[C - 1] + sum_de;
-      acc += dgam;
-      if (t < n) {
-        a.dg[row0 + (size_t)t * H] = acc;
-        a.dbeta[row0 + (size_t)t * H] = sm.dbc[t] + sm.dbr[t];
-      }
-    }
-  }
-  // dK = dPD^T Q + (dG + dG^T) K + diag(e) dKt + diag(Gamma) T^T dW
-  T* dkp = (T*)a.dk;
-  for (int id = wave; id < nK; id += 4) {
-    const int tm = id / (DK / 16), it = id % (DK / 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile<C>([&](int t, int s) { return sm.N4[s][t]; }, [&](int s, int e) { return Qx(s, e); }, 16 * tm, 16 * it,
-                  acc);
-    acc = tile<C>([&](int t, int s) { return sm.N2[t][s] + sm.N2[s][t]; }, [&](int s, int e) { return Kx(s, e); },
-                  16 * tm, 16 * it, acc);
-    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
-      if (t < n) {
-        const float val = v + cs.e[t] * sm.M2[t][e] + cs.Gam[t] * sm.M1[t][e];
-        if (a.dk_part)
-          a.dk_part[(row0 + (size_t)t * H) * DK + e] = val;
-        else
-          D::store(dkp, (kq0 + (size_t)t * a.Hk) * DK + e, val);
-      }
-    });
-  }
-}
-
-// ---------------------------------------------------------------------------
-// backward, bf16 path: local stage, reverse chain, state stage, gradients
-// (cpr_backward_bf16.hpp); one work-group per (chunk slot, head) except the chain
-
-struct SlotPos {
-  int n;        // real tokens of the chunk
-  size_t row0;  // row of its first token in [T, H, ...]
-  size_t kq0;   // its row in [T, Hk, DK] (q, k)
-  size_t sl;    // slot * H + h
-};
-
-__device__ __forceinline__ bool slot_pos(const BwdArgs& a, SlotPos& p) {
-  const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
-  if (slot >= a.all_base[a.N]) return false;
-  const int i = find_seq(a.all_base, a.N, slot);
-  const int c = slot - a.all_base[i];
-  const int L = a.cu[i + 1] - a.cu[i];
-  p.n = min(a.Cl, L - c * a.Cl);
-  const size_t tok0 = (size_t)a.cu[i] + (size_t)c * a.Cl;
-  p.row0 = tok0 * H + h;
-  p.kq0 = kq_row(tok0, h, a.Hk, a.G);
-  p.sl = (size_t)slot * H + h;
-  return true;
-}
-
-// waves per work-group of the local, state and gradient stages: their
-// d-wide products split into 16-wide tiles over the waves, so two waves per
-// SIMD where d_k and d_v give 8 tiles each (the LDS holds one work-group per CU)
-template <int DK, int DV>
-constexpr int kBwdWaves = (DK / 16) % 8 == 0 && (DV / 16) % 8 == 0 ? 8 : 4;
-
-template <int DK, int DV>
-__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_local_bf16(const BwdArgs a) {
-  typedef bwdb::Slot<DK, DV> Sl;
-  __shared__ bwdb::LocalLds<DK, DV> sm;
-  SlotPos p;
-  if (!slot_pos(a, p)) return;
-  bwdb::local_stage<DK, DV, kBwdWaves<DK, DV>>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.d_o,
-                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
-                            a.ws + p.sl * Sl::bytes, a.gamn + p.sl);
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_state_bf16(const BwdArgs a) {
-  typedef bwdb::Slot<DK, DV> Sl;
-  constexpr int W = kBwdWaves<DK, DV>;
-  __shared__ bwdb::StateLds<DK, DV, W> sm;
-  SlotPos p;
-  if (!slot_pos(a, p)) return;
-  bwdb::state_stage<DK, DV, W>(sm, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
-                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
-                            a.bnd + p.sl * DK * DV, a.ws + p.sl * Sl::bytes);
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_grads_bf16(const BwdArgs a) {
-  typedef bwdb::Slot<DK, DV> Sl;
-  __shared__ bwdb::GradLds<DK, DV> sm;
-  SlotPos p;
-  if (!slot_pos(a, p)) return;
-  bwdb::grad_stage<DK, DV, kBwdWaves<DK, DV>>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.d_o, (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0,
-                           a.Hk, p.n, a.ws + p.sl * Sl::bytes, (uint16_t*)a.dq, (uint16_t*)a.dk, a.dq_part,
-                           a.dk_part, (uint16_t*)a.dv, a.dg, a.dbeta);
-}
-
-// Reverse chain, bf16 path: the forward chain's structure run from the last
-// chunk to the first.  Per chunk (dS = adjoint of the chunk's end state):
-//   store dB' = dS;  E = Kt bf16(dS);  dS = fma(Gamma_n, dS, R) + (-W^T) bf16(E)
-// Work-groups own CB = WAVES * NT * 16 state columns; the chunk's Kt / -W^T
-// fragments and its R tiles for those columns go through a two-buffer LDS
-// stage with loads two chunks ahead.
-template <int DK, int DV, int WAVES, int NT>
-__global__ __launch_bounds__(WAVES * 64) void k_bwd_chain_bf16(const BwdArgs a) {
-  using namespace mfma;
-  typedef bwdb::Slot<DK, DV> Sl;
-  constexpr int kThreads = WAVES * 64;
-  constexpr int CB = WAVES * NT * 16;
-  constexpr int kFragPieces = (int)(Sl::oR / 16);
-  constexpr int kRPieces = DK * CB * 4 / 16;
-  constexpr int kPieces = kFragPieces + kRPieces;
-  constexpr int kPer = kPieces / kThreads;
-  constexpr int kPerFrag = kFragPieces / kThreads;
-  static_assert(kPieces % kThreads == 0 && kFragPieces % kThreads == 0, "staging split");
-  static_assert(DV % CB == 0, "column blocks tile d_v");
-  __shared__ u32x4 stage[2][kPieces];
-  __shared__ float gn_stage[2];
-  const int i = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int jbg = blockIdx.z * (CB / 16), jb0 = jbg + wave * NT;
-  const int H = a.H;
-  const int L = a.cu[i + 1] - a.cu[i];
-  const int nall = (L + a.Cl - 1) / a.Cl;
-  const size_t sh = (size_t)i * H + h;
-  const size_t SS = (size_t)DK * DV;
-  const int abase = a.all_base[i];
-  // step u visits chunk nall - 1 - u
-  auto slot_of = [&](int u) { return a.ws + ((size_t)(abase + nall - 1 - u) * H + h) * Sl::bytes; };
-  auto gamn_of = [&](int u) { return a.gamn[(size_t)(abase + nall - 1 - u) * H + h]; };
-  auto fetch = [&](int u, u32x4 (&r)[kPer]) {
-    const uint8_t* s = slot_of(u);
-    const u32x4* f = reinterpret_cast<const u32x4*>(s);
-    const u32x4* rr = reinterpret_cast<const u32x4*>(s + Sl::oR) + (size_t)jbg * (DK / 16) * 64;
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int p = tid + m * kThreads;
-      r[m] = m < kPerFrag ? f[p] : rr[p - kFragPieces];
-    }
-  };
-  auto put = [&](int buf, const u32x4 (&r)[kPer]) {
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) stage[buf][tid + m * kThreads] = r[m];
-  };
-  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-
-  f32x4 S[DK / 16][NT];
-  load_state_tiles<DK, DV, NT>(S, a.d_hT ? a.d_hT + sh * SS : nullptr, jb0, lane);
-  u32x4 R0[kPer], R1[kPer];
-  float G0 = 1.f, G1 = 1.f;
-  if (nall > 0) {
-    fetch(0, R0);
-    G0 = gamn_of(0);
-    put(0, R0);
-    if (tid == 0) gn_stage[0] = G0;
-    const int u1 = min(1, nall - 1);
-    fetch(u1, R1);
-    G1 = gamn_of(u1);
-  }
-  __syncthreads();
-  auto step = [&](auto par, auto is_last, int u) {
-    constexpr int P = decltype(par)::value;
-    constexpr bool kLast = decltype(is_last)::value;
-    u32x4(&RP)[kPer] = P ? R1 : R0;
-    u32x4(&RQ)[kPer] = P ? R0 : R1;
-    float& GP = P ? G1 : G0;
-    float& GQ = P ? G0 : G1;
-    if constexpr (!kLast) {
-      const int uf = min(u + 2, nall - 1);
-      fetch(uf, RP);
-      GP = gamn_of(uf);
-    }
-    const u32x4* st = stage[P];
-    const float gn = gn_stage[P];
-    store_bnd_tiles<DK, NT>(reinterpret_cast<float*>(slot_of(u) + Sl::oDbp), S, jb0, lane);
-    f32x4 Ut[C / 16][NT];
-#pragma unroll
-    for (int tm = 0; tm < C / 16; ++tm)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) Ut[tm][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    chain_step_bf16_init<DK, NT>(
-        S, [&](int kb, int tm) { return st[(kb * (C / 16) + tm) * 64 + lane]; },
-        [&](int kb, int im) { return st[(int)(Sl::oWNF / 16) + (kb * (DK / 16) + im) * 64 + lane]; }, Ut,
-        [&](int im, int nt, const f32x4& x) {
-          const f32x4 r =
-              __builtin_bit_cast(f32x4, st[kFragPieces + ((wave * NT + nt) * (DK / 16) + im) * 64 + lane]);
-          return f32x4{__builtin_fmaf(gn, x[0], r[0]), __builtin_fmaf(gn, x[1], r[1]), __builtin_fmaf(gn, x[2], r[2]),
-                       __builtin_fmaf(gn, x[3], r[3])};
-        });
-    if constexpr (!kLast) {
-      put(P ^ 1, RQ);
-      if (tid == 0) gn_stage[P ^ 1] = GQ;
-      barrier();
-    }
-  };
-  typedef std::integral_constant<int, 0> P0;
-  typedef std::integral_constant<int, 1> P1;
-  typedef std::integral_constant<bool, false> Mid;
-  typedef std::integral_constant<bool, true> Last;
-  int u = 0;
-  for (; u + 2 < nall; u += 2) {
-    step(P0{}, Mid{}, u);
-    step(P1{}, Mid{}, u + 1);
-  }
-  if (u + 1 < nall) {
-    step(P0{}, Mid{}, u);
-    step(P1{}, Last{}, u + 1);
-  } else if (u < nall) {
-    step(P0{}, Last{}, u);
-  }
-  if (a.dh0) store_state_tiles<DK, DV, NT>(a.dh0 + sh * SS, S, jb0, lane);
-}
 
 // ---------------------------------------------------------------------------
 // host side

@@ -37,6 +37,7 @@ METRIC = "GDN layer tokens/s (prefill 5x2048, decode 256x1) + bitwise prefill/de
 PEAK_F32 = 157.3
 PEAK_VALU_F32_NONPACKED = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PEAK_MFMA_F32 = 157.3
+PEAK_MFMA_BF16 = 2500.0  # dense
 PEAK_HBM = 8000.0  # GB/s
 
 
@@ -58,6 +59,29 @@ def bwd_state_grads_flop(C: int, dk: int, dv: int) -> int:
     grads += nb * nb * (dv // 16 + dk // 16) * tile                    # dT
     grads += nb * nb * (dk // 16) * tile                               # (dG + dG^T) K
     grads += nb * tri * tile + sum((i + 1) * (nb - i) for i in range(nb)) * tile  # dX X^T, X^T Y
+    grads += 2 * tri * (dk // 16) * tile                               # Q K^T, K K^T
+    return state + grads
+
+
+def bwd_state_grads_bf16_exec_flop(C: int, dk: int, dv: int) -> int:
+    """bf16 MFMA flops the state and gradient stages execute for one chunk-head.
+    A product with an fp32 operand runs as bf16 hi/lo parts: three products
+    (hi hi, hi lo, lo hi) when both operands are fp32, two when the other is
+    the layer's bf16 k, q, v or dO; Q K^T and K K^T take one.  Over the same
+    tiles as `bwd_state_grads_flop` (the instruction counters of one fwd_bwd
+    call record the same count: 44,072,960 at C = 64, d = 128)."""
+    nb = C // 16
+    tile = 2 * 16 * 16 * 16
+    tri = nb * (nb + 1) // 2
+    tri_y = sum((i + 1) * (nb - i) for i in range(nb))
+    # K dB', K B, dO B^T: 2 each; Dd B^T, Delta dB'^T: 3 each; X diag(beta) (.): 3
+    state = (2 + 2 + 2 + 3 + 3) * 2 * C * dk * dv + 3 * tri * (dv // 16) * tile
+    grads = (2 * tri * (dv // 16) + 2 * tri * (dk // 16)) * tile        # dO Delta^T, dPD K
+    grads += (3 * tri * (dv // 16) + 3 * tri * (dk // 16)) * tile       # X^T Dd, X^T dWn
+    grads += 2 * tri * (dk // 16) * tile                               # dPD^T Q
+    grads += 2 * nb * nb * (dv // 16 + dk // 16) * tile                # Dd V^T, dWn K^T
+    grads += 2 * nb * nb * (dk // 16) * tile                           # (dG + dG^T) K
+    grads += 3 * (nb * tri + tri_y) * tile                             # dX X^T, X^T Y
     grads += 2 * tri * (dk // 16) * tile                               # Q K^T, K K^T
     return state + grads
 
@@ -715,10 +739,16 @@ def main():
     fb_flop_ch = bwd_state_grads_flop(C, D, D)
     fb_flop = fb_flop_ch * n_chunk_heads
     fb_t = float(np.median(fb_grads))
+    fb_exec_ch = bwd_state_grads_bf16_exec_flop(C, D, D)
     fb_roofline = {"kernels": "k_bwd_state_bf16 + k_bwd_grads_bf16", "bound": "mfma",
                    "achieved": round(fb_flop / (fb_t / 1e3) / 1e12, 3), "peak": PEAK_MFMA_F32, "unit": "TFLOP/s",
                    "frac": round(fb_flop / (fb_t / 1e3) / 1e12 / PEAK_MFMA_F32, 4),
-                   "algorithmic_flop_per_chunk_head": fb_flop_ch, "chunk_heads": n_chunk_heads}
+                   "algorithmic_flop_per_chunk_head": fb_flop_ch, "chunk_heads": n_chunk_heads,
+                   "note": "fp32-class products taken as bf16 hi/lo parts on the bf16 MFMA; the fraction above is "
+                           "the algorithmic fp32 work against the fp32 MFMA peak",
+                   "executed_bf16_flop_per_chunk_head": fb_exec_ch,
+                   "executed_bf16_tflops": round(fb_exec_ch * n_chunk_heads / (fb_t / 1e3) / 1e12, 2),
+                   "executed_bf16_frac": round(fb_exec_ch * n_chunk_heads / (fb_t / 1e3) / 1e12 / PEAK_MFMA_BF16, 4)}
     dec_avg = float(np.mean(decode_ms))
     # per (sequence, head): state read + write, log-scale read + write, q/k/v, g/beta, o, tail append
     dec_bytes = N_dec * H * (2 * D * D * 4 + 2 * 4 + 3 * D * 2 + 2 * 2 + D * 2 + (2 * D + 2) * 2)

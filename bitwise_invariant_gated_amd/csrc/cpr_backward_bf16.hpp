@@ -11,12 +11,12 @@
 //     Ddl = P^T dO,  R = (diag(Gamma) Q)^T dO - W^T Ddl
 //   reverse chain   dB = Gamma_n dB' + R + (-W^T) Kt dB'   (bf16 operands)
 //   state     (after it)
-//     Dd = Ddl + Kt dB',  Delta = X diag(beta) (V - diag(Gamma) K B)  (= X diag(beta) V - W B)
+//     Dd = Ddl + diag(e) (K dB'),  Delta = X diag(beta) (V - diag(Gamma) K B)  (= X diag(beta) V - W B)
 //     QB = dO B^T,  dWn = Dd B^T (= -dW),  dKt = Delta dB'^T,  dGamma_n = <dB', B>
 //   local gradients
 //     dPD = (dO Delta^T) .* D,  dQ = diag(Gamma) QB + dPD K
 //     dV = diag(beta) X^T Dd,  TW = T^T dW = -diag(beta) X^T dWn
-//     dT = Dd V^T - dWn (diag(Gamma) K)^T,  dX = dT diag(beta)
+//     dT = Dd V^T - (dWn K^T) diag(Gamma),  dX = dT diag(beta)
 //     dA = -X^T (dX X^T) (strict lower),  dG = dA .* beta_t D
 //     dK = dPD^T Q + (dG + dG^T) K + diag(e) dKt + diag(Gamma) TW
 //     dbeta = colsum(X .* dT) + rowsum(dA .* D .* G)
@@ -25,11 +25,13 @@
 //       Z = dPD .* QK + beta_t dA .* D .* G,  dGamma_out = <QB, Q> per row,
 //       dGamma_W = <TW, K> per row,  de = <dKt, K> per row
 //     dg = reverse cumsum of dgamma.
-// Products run on v_mfma_f32_16x16x4_f32 (fp32 operands; step m of a
-// 16-wide k block contracts index 4 g + m in lane group g) except G and
-// Q K^T (exact bf16 operands, v_mfma_f32_16x16x32_bf16) and the reverse
-// chain (bf16 operands, as the forward chain).  Every reduction has a fixed
-// order, so reruns give identical bits.
+// Products with an fp32 operand run on v_mfma_f32_16x16x16_bf16 with that
+// operand split into bf16 hi + lo parts (three products per 16-wide k block,
+// two where the other operand is the layer's bf16 k, q, v or dO; mma16s
+// below); G and Q K^T take their exact bf16 operands on
+// v_mfma_f32_16x16x32_bf16, the reverse chain bf16 operands as the forward
+// chain, and the inverse's blocks below the diagonal the forward's fp32
+// routine.  Every reduction has a fixed order, so reruns give identical bits.
 #pragma once
 
 #include "cpr_backward.hpp"
@@ -64,20 +66,60 @@ struct Slot {
 // ---------------------------------------------------------------------------
 // operand helpers (lane l = 16 g + c)
 
-__device__ __forceinline__ f32x4 mma16(const f32x4& a, const f32x4& b, f32x4 acc) {
-  acc = mma4(a[0], b[0], acc);
-  acc = mma4(a[1], b[1], acc);
-  acc = mma4(a[2], b[2], acc);
-  return mma4(a[3], b[3], acc);
+
+// fp32 products at the bf16 MFMA rate.  A lane's operand x (four values of a
+// 16-wide k block: lane 16 g + c holds index 4 g + {0..3}) is split as x = hi + lo with
+// hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in fp32), which holds x
+// to about 2^-17 |x|; a product then takes hi*hi + hi*lo + lo*hi, in that
+// order, on v_mfma_f32_16x16x16_bf16 (the dropped lo*lo term is about 2^-17
+// of the product).  An operand that is already bf16 (the layer's k, q, v,
+// dO) has lo = 0 and takes two terms.  One bf16 MFMA of k = 16 stands for
+// four fp32 ones and costs a quarter of one of them.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Split4 {
+  s16x4 hi, lo;
+};
+
+__device__ __forceinline__ Split4 split4(const f32x4& x) {
+  const uint32_t h0 = pack2(x[0], x[1]), h1 = pack2(x[2], x[3]);
+  const uint32_t l0 = pack2(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xffff0000u));
+  const uint32_t l1 = pack2(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xffff0000u));
+  return Split4{__builtin_bit_cast(s16x4, u32x2{h0, h1}), __builtin_bit_cast(s16x4, u32x2{l0, l1})};
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_k16(s16x4 a, s16x4 b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma16s(const Split4& a, const Split4& b, f32x4 acc) {
+  acc = mfma_bf16_k16(a.hi, b.hi, acc);
+  acc = mfma_bf16_k16(a.hi, b.lo, acc);
+  return mfma_bf16_k16(a.lo, b.hi, acc);
+}
+
+// a exact in bf16
+__device__ __forceinline__ f32x4 mma16s(s16x4 a, const Split4& b, f32x4 acc) {
+  acc = mfma_bf16_k16(a, b.hi, acc);
+  return mfma_bf16_k16(a, b.lo, acc);
+}
+
+// b exact in bf16
+__device__ __forceinline__ f32x4 mma16s(const Split4& a, s16x4 b, f32x4 acc) {
+  acc = mfma_bf16_k16(a.hi, b, acc);
+  return mfma_bf16_k16(a.lo, b, acc);
 }
 
 __device__ __forceinline__ float bfv(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-// M[r][k0 + 4 g + {0..3}] of a row-major bf16 matrix (8-byte aligned rows)
-__device__ __forceinline__ f32x4 row4_bf(const uint16_t* M, int ld, int r, int k0, int g) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(M + (size_t)r * ld + k0 + 4 * g);
-  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
-               __uint_as_float(w[1] & 0xffff0000u)};
+// the bits of M[r][k0 + 4 g + {0..3}] of a row-major bf16 matrix (8-byte aligned rows)
+__device__ __forceinline__ s16x4 row4_bits(const uint16_t* M, int ld, int r, int k0, int g) {
+  return __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(M + (size_t)r * ld + k0 + 4 * g));
+}
+
+// the bits of M[k0 + 4 g + {0..3}][col] of a row-major bf16 matrix
+__device__ __forceinline__ s16x4 col4_bits(const uint16_t* M, int ld, int k0, int col, int g) {
+  const uint16_t* p = M + (size_t)(k0 + 4 * g) * ld + col;
+  return s16x4{(short)p[0], (short)p[ld], (short)p[2 * ld], (short)p[3 * ld]};
 }
 
 // M[k0 + 4 g + {0..3}][col] of a row-major bf16 matrix
@@ -285,7 +327,7 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
     for (int tm = 0; tm < NB; ++tm) Wt[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sb = 0; sb < NB; ++sb) {
-      const f32x4 b = col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, 16 * it + lr, g);
+      const s16x4 b = col4_bits(&sm.K[0][0], Lds::kLK, 16 * sb, 16 * it + lr, g);
       f32x4 bg;
 #pragma unroll
       for (int m = 0; m < 4; ++m) bg[m] = cs.beta[16 * sb + 4 * g + m] * cs.Gam[16 * sb + 4 * g + m];
@@ -298,7 +340,7 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
           const int s = 16 * sb + 4 * g + m;
           a[m] = (s <= t) ? sm.A[s][t] * bg[m] : 0.f;
         }
-        Wt[p][tm] = mma16(a, b, Wt[p][tm]);
+        Wt[p][tm] = mma16s(split4(a), b, Wt[p][tm]);
       }
     }
     // -W^T fragments (chain phase 2): fragment (kb, it)
@@ -320,13 +362,13 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
     for (int sb = 0; sb < NB; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
-      const f32x4 b = col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g);
+      const s16x4 b = col4_bits(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g);
 #pragma unroll
       for (int sb = 0; sb <= tb; ++sb) {
         f32x4 a;
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[m] = sm.P[16 * tb + 4 * g + m][16 * sb + lr];
-        acc[sb] = mma16(a, b, acc[sb]);
+        acc[sb] = mma16s(split4(a), b, acc[sb]);
       }
     }
 #pragma unroll
@@ -351,11 +393,11 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
 #pragma unroll
       for (int m = 0; m < 4; ++m) a[m] *= cs.Gam[16 * tb + 4 * g + m];
       const f32x4& w = Wt[p][tb];
-      const f32x4 wn = {-w[0], -w[1], -w[2], -w[3]};
+      const Split4 as = split4(a), wn = split4(f32x4{-w[0], -w[1], -w[2], -w[3]});
 #pragma unroll
       for (int jt = 0; jt < DV / 16; ++jt) {
-        acc[jt] = mma16(a, col4_bf(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g), acc[jt]);
-        acc[jt] = mma16(wn, tl4<C>(sm.Ddl, tb, jt, lane), acc[jt]);
+        acc[jt] = mma16s(as, col4_bits(&sm.dO[0][0], Lds::kLV, 16 * tb, 16 * jt + lr, g), acc[jt]);
+        acc[jt] = mma16s(wn, split4(tl4<C>(sm.Ddl, tb, jt, lane)), acc[jt]);
       }
     }
 #pragma unroll
@@ -427,6 +469,15 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
   const float* Xg = reinterpret_cast<const float*>(slot + Sl::oX);
   const float* Ddlg = reinterpret_cast<const float*>(slot + Sl::oDdl);
   const float* dBp = reinterpret_cast<const float*>(slot + Sl::oDbp);
+  constexpr int NB = C / 16;
+  // the first column tile's dB', B and Ddl tiles are loaded with the staging
+  // (a barrier waits only for LDS, so they stay in flight across it)
+  f32x4 d0[DK / 16], b0[DK / 16], l0[NB];
+#pragma unroll
+  for (int ib = 0; ib < DK / 16; ++ib) {
+    d0[ib] = tl4<DK>(dBp, ib, wave, lane);
+    b0[ib] = tl4<DK>(B, ib, wave, lane);
+  }
   {
     RowLoads<DK, 64 * W> rk;
     RowLoads<DV, 64 * W> rv, rd;
@@ -437,6 +488,8 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
     rd.load(d_o, row0, H, n);
     rx.load(Xg);
     load_scalars(gp, bp, row0, H, n, g_t, b_t);
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) l0[tm] = tl4<C>(Ddlg, tm, wave, lane);
     rk.store(sm.K, n);
     rv.store(sm.V, n);
     rd.store(sm.dO, n);
@@ -446,38 +499,47 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
   const bwd::ChunkScalars& cs = sm.cs;
   float* Ddg = reinterpret_cast<float*>(slot + Sl::oDd);
   float* Deg = reinterpret_cast<float*>(slot + Sl::oDe);
-  constexpr int NB = C / 16;
   // Column tile jt = wave + W p: the dB' and B tiles of the column block are
   // loaded once; the four row tiles accumulate together.
   //   Dd    = Ddl + Kt dB'
   //   KB    = K B                                   (kept in registers)
   //   Delta = X diag(beta) (V - diag(Gamma) KB)     (= X diag(beta) V - W B)
+  // the QB phase's first 32 columns of B
+  ColLoads<DK, 64 * W> cols;
+  cols.load(B, 0);
+  // <dB', B>: this lane's share (the tiles it loads below, p, ib, element
+  // ascending), summed over the threads at the end in a fixed order
+  float gdot = 0.f;
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
     const int jt = wave + W * p;
-    f32x4 bD[DK / 16], bB[DK / 16];
+    Split4 bD[DK / 16], bB[DK / 16];
 #pragma unroll
     for (int ib = 0; ib < DK / 16; ++ib) {
-      bD[ib] = tl4<DK>(dBp, ib, jt, lane);
-      bB[ib] = tl4<DK>(B, ib, jt, lane);
-    }
-    f32x4 dd[NB], kb[NB];
+      const f32x4 d = p == 0 ? d0[ib] : tl4<DK>(dBp, ib, jt, lane), b = p == 0 ? b0[ib] : tl4<DK>(B, ib, jt, lane);
 #pragma unroll
-    for (int tm = 0; tm < NB; ++tm) {
-      dd[tm] = tl4<C>(Ddlg, tm, jt, lane);
-      kb[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) gdot = __builtin_fmaf(b[r], d[r], gdot);
+      bD[ib] = split4(d);
+      bB[ib] = split4(b);
     }
+    // Kt dB' as diag(e) (K dB'): K is exact in bf16
+    f32x4 kd[NB], kb[NB];
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm) kd[tm] = kb[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ib = 0; ib < DK / 16; ++ib)
 #pragma unroll
       for (int tm = 0; tm < NB; ++tm) {
-        const f32x4 a = row4_bf(&sm.K[0][0], Lds::kLK, 16 * tm + lr, 16 * ib, g);
-        const float et = cs.e[16 * tm + lr];
-        dd[tm] = mma16(f32x4{et * a[0], et * a[1], et * a[2], et * a[3]}, bD[ib], dd[tm]);
-        kb[tm] = mma16(a, bB[ib], kb[tm]);
+        const s16x4 a = row4_bits(&sm.K[0][0], Lds::kLK, 16 * tm + lr, 16 * ib, g);
+        kd[tm] = mma16s(a, bD[ib], kd[tm]);
+        kb[tm] = mma16s(a, bB[ib], kb[tm]);
       }
+    f32x4 dd[NB];
 #pragma unroll
     for (int tm = 0; tm < NB; ++tm) {
+      const f32x4 ddl = p == 0 ? l0[tm] : tl4<C>(Ddlg, tm, jt, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dd[tm][r] = __builtin_fmaf(cs.e[16 * tm + 4 * g + r], kd[tm][r], ddl[r]);
       st_rm(&sm.Dd[0][0], Lds::kLD, 16 * tm, 16 * jt, dd[tm], lane);
       st_rm(Ddg, DV, 16 * tm, 16 * jt, dd[tm], lane);
     }
@@ -491,12 +553,13 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
       f32x4 b;
 #pragma unroll
       for (int m = 0; m < 4; ++m) b[m] = __builtin_fmaf(-cs.Gam[16 * sb + 4 * g + m], kb[sb][m], v[m]);
+      const Split4 bs = split4(b);
 #pragma unroll
       for (int tm = sb; tm < NB; ++tm) {
         f32x4 a = row4_f(&sm.X[0][0], Lds::kLX, 16 * tm + lr, 16 * sb, g);
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[m] *= cs.beta[16 * sb + 4 * g + m];
-        de[tm] = mma16(a, b, de[tm]);
+        de[tm] = mma16s(split4(a), bs, de[tm]);
       }
     }
 #pragma unroll
@@ -505,6 +568,7 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
       st_rm(Deg, DV, 16 * tm, 16 * jt, de[tm], lane);
     }
   }
+  sm.red[tid] = gdot;
   __syncthreads();
   // QB = dO B^T and dWn = Dd B^T, then dKt = Delta dB'^T, 32 columns of B / dB' at a time
   f32x4 QB[NI][C / 16], DW[NI][C / 16];
@@ -512,8 +576,6 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
   for (int p = 0; p < NI; ++p)
 #pragma unroll
     for (int tm = 0; tm < C / 16; ++tm) QB[p][tm] = DW[p][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  ColLoads<DK, 64 * W> cols;
-  cols.load(B, 0);
   for (int jb = 0; jb < DV / 32; ++jb) {
     cols.store(sm.Bs);
     __syncthreads();
@@ -523,11 +585,12 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
       const int it = wave + W * p;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 b = row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g);
+        const Split4 b = split4(row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g));
 #pragma unroll
         for (int tm = 0; tm < C / 16; ++tm) {
-          QB[p][tm] = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 32 * jb + 16 * kk, g), b, QB[p][tm]);
-          DW[p][tm] = mma16(row4_f(&sm.Dd[0][0], Lds::kLD, 16 * tm + lr, 32 * jb + 16 * kk, g), b, DW[p][tm]);
+          QB[p][tm] = mma16s(row4_bits(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 32 * jb + 16 * kk, g), b, QB[p][tm]);
+          DW[p][tm] =
+              mma16s(split4(row4_f(&sm.Dd[0][0], Lds::kLD, 16 * tm + lr, 32 * jb + 16 * kk, g)), b, DW[p][tm]);
         }
       }
     }
@@ -552,10 +615,11 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
       const int it = wave + W * p;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 b = row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g);
+        const Split4 b = split4(row4_f(&sm.Bs[0][0], Lds::kLB, 16 * it + lr, 16 * kk, g));
 #pragma unroll
         for (int tm = 0; tm < C / 16; ++tm)
-          QB[p][tm] = mma16(row4_f(&sm.De[0][0], Lds::kLD, 16 * tm + lr, 32 * jb + 16 * kk, g), b, QB[p][tm]);
+          QB[p][tm] =
+              mma16s(split4(row4_f(&sm.De[0][0], Lds::kLD, 16 * tm + lr, 32 * jb + 16 * kk, g)), b, QB[p][tm]);
       }
     }
     __syncthreads();
@@ -565,20 +629,9 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
   for (int p = 0; p < NI; ++p)
 #pragma unroll
     for (int tm = 0; tm < C / 16; ++tm) st_rm(KTg, DK, 16 * tm, 16 * (wave + W * p), QB[p][tm], lane);
-  // dGamma_n = <dB', B> (both in TL order), fixed order
+  // dGamma_n = <dB', B> from the threads' shares (written to red before the
+  // barriers above), in a fixed order
   {
-    float acc = 0.f;
-    const f32x4* b4 = reinterpret_cast<const f32x4*>(B);
-    const f32x4* d4 = reinterpret_cast<const f32x4*>(dBp);
-    for (int idx = tid; idx < DK * DV / 4; idx += 64 * W) {
-      const f32x4 x = b4[idx], y = d4[idx];
-      acc = __builtin_fmaf(x[0], y[0], acc);
-      acc = __builtin_fmaf(x[1], y[1], acc);
-      acc = __builtin_fmaf(x[2], y[2], acc);
-      acc = __builtin_fmaf(x[3], y[3], acc);
-    }
-    sm.red[tid] = acc;
-    __syncthreads();
     if (tid < 64) {  // lane l sums red[W l .. W l + W - 1], then the lanes in order
       float part = 0.f;
       for (int r = 0; r < W; ++r) part += sm.red[W * tid + r];
@@ -632,6 +685,12 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   const float* QBg = reinterpret_cast<const float*>(slot + Sl::oQB);
   const float* DWg = reinterpret_cast<const float*>(slot + Sl::oDWn);
   const float* KTg = reinterpret_cast<const float*>(slot + Sl::oDKt);
+  constexpr int NB = C / 16;
+  // Every global operand is loaded one phase ahead of its use (a barrier
+  // waits only for LDS, so the loads stay in flight across it).
+  const float dGn = *reinterpret_cast<const float*>(slot + Sl::oDGn);
+  const int tn_p = wave % NB;  // the dPD phase's column block
+  f32x4 bde_raw[DV / 16];
   {
     RowLoads<DK, 64 * W> rk, rq;
     RowLoads<DV, 64 * W> rv, rd;
@@ -643,6 +702,8 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
     rd.load(d_o, row0, H, n);
     rx.load(Xg);
     load_scalars(gp, bp, row0, H, n, g_t, b_t);
+#pragma unroll
+    for (int jb = 0; jb < DV / 16; ++jb) bde_raw[jb] = row4_f(Deg, DV, 16 * tn_p + lr, 16 * jb, g);
     rk.store(sm.K, n);
     rq.store(sm.Q, n);
     rv.store(sm.V, n);
@@ -652,15 +713,32 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   }
   const bwd::ChunkScalars& cs = sm.cs;
 
-  constexpr int NB = C / 16;
+  // the next phase's operands: QB (dQ), Dd and dWn columns (dV, TW)
+  float qb[NI][NB][4];
+  f32x4 bd_raw[NJ][NB], bw_raw[NI][NB];
+#pragma unroll
+  for (int p = 0; p < NI; ++p)
+#pragma unroll
+    for (int tm = 0; tm < NB; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qb[p][tm][r] = QBg[(size_t)(16 * tm + 4 * g + r) * DK + 16 * (wave + W * p) + lr];
+#pragma unroll
+  for (int p = 0; p < NJ; ++p)
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) bd_raw[p][tb] = col4_f(Ddg, DV, 16 * tb, 16 * (wave + W * p) + lr, g);
+#pragma unroll
+  for (int p = 0; p < NI; ++p)
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) bw_raw[p][tb] = col4_f(DWg, DK, 16 * tb, 16 * (wave + W * p) + lr, g);
+
   // dPD = (dO Delta^T) .* D (lower, diagonal included), Z_P = dPD .* QK^T;
   // wave w makes the tiles (w / NB + (W / NB) j, w % NB) (zero above the diagonal)
   {
     constexpr int NT2 = NB * NB / W;
-    const int tn = wave % NB;
-    f32x4 bde[DV / 16];
+    const int tn = tn_p;
+    Split4 bde[DV / 16];
 #pragma unroll
-    for (int jb = 0; jb < DV / 16; ++jb) bde[jb] = row4_f(Deg, DV, 16 * tn + lr, 16 * jb, g);
+    for (int jb = 0; jb < DV / 16; ++jb) bde[jb] = split4(bde_raw[jb]);
     f32x4 acc[NT2], qk[NT2];
 #pragma unroll
     for (int j = 0; j < NT2; ++j) acc[j] = qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -669,7 +747,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
 #pragma unroll
       for (int j = 0; j < NT2; ++j) {
         const int tm = wave / NB + (W / NB) * j;
-        if (tm >= tn) acc[j] = mma16(row4_bf(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 16 * jb, g), bde[jb], acc[j]);
+        if (tm >= tn) acc[j] = mma16s(row4_bits(&sm.dO[0][0], Lds::kLV, 16 * tm + lr, 16 * jb, g), bde[jb], acc[j]);
       }
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb) {
@@ -703,34 +781,35 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
     for (int t = 0; t < C; ++t) acc += sm.M2[t][s2];
     sm.czP[s2] = acc;
   }
+  // the dT phase's rows of Dd and dWn (row block wave % NB)
+  f32x4 ad_raw[DV / 16], aw_raw[DK / 16];
+#pragma unroll
+  for (int jb = 0; jb < DV / 16; ++jb) ad_raw[jb] = row4_f(Ddg, DV, 16 * (wave % NB) + lr, 16 * jb, g);
+#pragma unroll
+  for (int ib = 0; ib < DK / 16; ++ib) aw_raw[ib] = row4_f(DWg, DK, 16 * (wave % NB) + lr, 16 * ib, g);
   // dQ = diag(Gamma) QB + dPD K;  <QB, Q> per row
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
     const int it = wave + W * p, i = 16 * it + lr;
-    float qb[NB][4];
-#pragma unroll
-    for (int tm = 0; tm < NB; ++tm)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) qb[tm][r] = QBg[(size_t)(16 * tm + 4 * g + r) * DK + i];
     f32x4 acc[NB];
 #pragma unroll
     for (int tm = 0; tm < NB; ++tm) acc[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sb = 0; sb < NB; ++sb) {
-      const f32x4 b = col4_bf(&sm.K[0][0], Lds::kLK, 16 * sb, i, g);
+      const s16x4 b = col4_bits(&sm.K[0][0], Lds::kLK, 16 * sb, i, g);
 #pragma unroll
       for (int tm = sb; tm < NB; ++tm)
-        acc[tm] = mma16(row4_f(&sm.dPD[0][0], Lds::kLX, 16 * tm + lr, 16 * sb, g), b, acc[tm]);
+        acc[tm] = mma16s(split4(row4_f(&sm.dPD[0][0], Lds::kLX, 16 * tm + lr, 16 * sb, g)), b, acc[tm]);
     }
 #pragma unroll
     for (int tm = 0; tm < NB; ++tm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tm + 4 * g + r;
-        const float part = sum16(qb[tm][r] * bfv(sm.Q[t][i]));
+        const float part = sum16(qb[p][tm][r] * bfv(sm.Q[t][i]));
         if (lr == 0) sm.pGO[t][it] = part;
         if (t < n) {
-          const float val = __builtin_fmaf(cs.Gam[t], qb[tm][r], acc[tm][r]);
+          const float val = __builtin_fmaf(cs.Gam[t], qb[p][tm][r], acc[tm][r]);
           if (dq_part)
             dq_part[(row0 + (size_t)t * H) * DK + i] = val;
           else
@@ -742,17 +821,18 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
     const int jt = wave + W * p;
-    f32x4 bd[NB], acc[NB];
+    Split4 bd[NB];
+    f32x4 acc[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
-      bd[tb] = col4_f(Ddg, DV, 16 * tb, 16 * jt + lr, g);
+      bd[tb] = split4(bd_raw[p][tb]);
       acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
       for (int sb = 0; sb <= tb; ++sb)
-        acc[sb] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), bd[tb], acc[sb]);
+        acc[sb] = mma16s(split4(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g)), bd[tb], acc[sb]);
 #pragma unroll
     for (int sb = 0; sb < NB; ++sb)
 #pragma unroll
@@ -766,57 +846,60 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
     const int it = wave + W * p;
-    f32x4 bw[NB];
+    Split4 bw[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
-      bw[tb] = col4_f(DWg, DK, 16 * tb, 16 * it + lr, g);
+      bw[tb] = split4(bw_raw[p][tb]);
       TW[p][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
       for (int sb = 0; sb <= tb; ++sb)
-        TW[p][sb] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), bw[tb], TW[p][sb]);
+        TW[p][sb] = mma16s(split4(col4_f(&sm.X[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g)), bw[tb], TW[p][sb]);
 #pragma unroll
     for (int sb = 0; sb < NB; ++sb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) TW[p][sb][r] = -cs.beta[16 * sb + 4 * g + r] * TW[p][sb][r];
   }
   __syncthreads();  // Z_P sums done: M2 is free
-  // dT = Dd V^T - dWn (diag(Gamma) K)^T; wave w makes row block w % NB,
+  // the dK phase's dKt values
+  float kt[NI][NB][4];
+#pragma unroll
+  for (int p = 0; p < NI; ++p)
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kt[p][sb][r] = KTg[(size_t)(16 * sb + 4 * g + r) * DK + 16 * (wave + W * p) + lr];
+  // dT = Dd V^T - (dWn K^T) diag(Gamma); wave w makes row block w % NB,
   // column blocks (w / NB) NT2 .. + NT2 - 1
   {
     constexpr int NT2 = NB * NB / W;
     const int tm = wave % NB, tn0 = (wave / NB) * NT2;
-    f32x4 ad[DV / 16], aw[DK / 16];
+    f32x4 acc[NT2], acw[NT2];
 #pragma unroll
-    for (int jb = 0; jb < DV / 16; ++jb) ad[jb] = row4_f(Ddg, DV, 16 * tm + lr, 16 * jb, g);
+    for (int u = 0; u < NT2; ++u) acc[u] = acw[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ib = 0; ib < DK / 16; ++ib) {
-      const f32x4 w = row4_f(DWg, DK, 16 * tm + lr, 16 * ib, g);
-      aw[ib] = f32x4{-w[0], -w[1], -w[2], -w[3]};
-    }
-    f32x4 acc[NT2];
-#pragma unroll
-    for (int u = 0; u < NT2; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jb = 0; jb < DV / 16; ++jb)
+    for (int jb = 0; jb < DV / 16; ++jb) {
+      const Split4 ad = split4(ad_raw[jb]);
 #pragma unroll
       for (int u = 0; u < NT2; ++u)
-        acc[u] = mma16(ad[jb], row4_bf(&sm.V[0][0], Lds::kLV, 16 * (tn0 + u) + lr, 16 * jb, g), acc[u]);
+        acc[u] = mma16s(ad, row4_bits(&sm.V[0][0], Lds::kLV, 16 * (tn0 + u) + lr, 16 * jb, g), acc[u]);
+    }
 #pragma unroll
-    for (int ib = 0; ib < DK / 16; ++ib)
+    for (int ib = 0; ib < DK / 16; ++ib) {
+      const Split4 aw = split4(aw_raw[ib]);
 #pragma unroll
-      for (int u = 0; u < NT2; ++u) {
-        const int tn = tn0 + u;
-        const float gs = cs.Gam[16 * tn + lr];
-        const f32x4 kk = row4_bf(&sm.K[0][0], Lds::kLK, 16 * tn + lr, 16 * ib, g);
-        acc[u] = mma16(aw[ib], f32x4{gs * kk[0], gs * kk[1], gs * kk[2], gs * kk[3]}, acc[u]);
-      }
+      for (int u = 0; u < NT2; ++u)
+        acw[u] = mma16s(aw, row4_bits(&sm.K[0][0], Lds::kLK, 16 * (tn0 + u) + lr, 16 * ib, g), acw[u]);
+    }
 #pragma unroll
-    for (int u = 0; u < NT2; ++u)
+    for (int u = 0; u < NT2; ++u) {
+      const float gs = cs.Gam[16 * (tn0 + u) + lr];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.M2[16 * tm + 4 * g + r][16 * (tn0 + u) + lr] = acc[u][r];
+      for (int r = 0; r < 4; ++r)
+        sm.M2[16 * tm + 4 * g + r][16 * (tn0 + u) + lr] = __builtin_fmaf(-gs, acw[u][r], acc[u][r]);
+    }
   }
   __syncthreads();
   if (tid < C) {  // dbeta, column part: sum_t X[t][s] dT[t][s]
@@ -839,11 +922,11 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
     for (int u = 0; u < NT2; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const f32x4 a = row4_f(&sm.M2[0][0], Lds::kLX, 16 * tm + lr, 16 * rb, g);
+      const Split4 a = split4(row4_f(&sm.M2[0][0], Lds::kLX, 16 * tm + lr, 16 * rb, g));
 #pragma unroll
       for (int u = 0; u < NT2; ++u) {
         const int tn = tn_y(u);
-        if (tn >= rb) acc[u] = mma16(a, row4_f(&sm.X[0][0], Lds::kLX, 16 * tn + lr, 16 * rb, g), acc[u]);
+        if (tn >= rb) acc[u] = mma16s(a, split4(row4_f(&sm.X[0][0], Lds::kLX, 16 * tn + lr, 16 * rb, g)), acc[u]);
       }
     }
 #pragma unroll
@@ -863,11 +946,12 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
     for (int j = 0; j < NTA; ++j) acc[j] = gk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const f32x4 b = col4_f(&sm.M3[0][0], Lds::kLX, 16 * rb, 16 * tn + lr, g);
+      const Split4 b = split4(col4_f(&sm.M3[0][0], Lds::kLX, 16 * rb, 16 * tn + lr, g));
 #pragma unroll
       for (int j = 0; j < NTA; ++j) {
         const int tm = wave / NB + (W / NB) * j;
-        if (tm <= rb && tm >= tn) acc[j] = mma16(col4_f(&sm.X[0][0], Lds::kLX, 16 * rb, 16 * tm + lr, g), b, acc[j]);
+        if (tm <= rb && tm >= tn)
+          acc[j] = mma16s(split4(col4_f(&sm.X[0][0], Lds::kLX, 16 * rb, 16 * tm + lr, g)), b, acc[j]);
       }
     }
 #pragma unroll
@@ -918,28 +1002,24 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
 #pragma unroll
   for (int p = 0; p < NI; ++p) {
     const int it = wave + W * p, i = 16 * it + lr;
-    float kt[NB][4];
-#pragma unroll
-    for (int sb = 0; sb < NB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) kt[sb][r] = KTg[(size_t)(16 * sb + 4 * g + r) * DK + i];
     f32x4 acc[NB];
 #pragma unroll
     for (int sb = 0; sb < NB; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
-      const f32x4 bq = col4_bf(&sm.Q[0][0], Lds::kLK, 16 * tb, i, g);
-      const f32x4 bk = col4_bf(&sm.K[0][0], Lds::kLK, 16 * tb, i, g);
+      const s16x4 bq = col4_bits(&sm.Q[0][0], Lds::kLK, 16 * tb, i, g);
+      const s16x4 bk = col4_bits(&sm.K[0][0], Lds::kLK, 16 * tb, i, g);
 #pragma unroll
       for (int sb = 0; sb < NB; ++sb) {
-        if (sb <= tb) acc[sb] = mma16(col4_f(&sm.dPD[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g), bq, acc[sb]);
+        if (sb <= tb)
+          acc[sb] = mma16s(split4(col4_f(&sm.dPD[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g)), bq, acc[sb]);
         const f32x4 lo = row4_f(&sm.M2[0][0], Lds::kLX, 16 * sb + lr, 16 * tb, g);   // dA D [s][t]
         const f32x4 hi = col4_f(&sm.M2[0][0], Lds::kLX, 16 * tb, 16 * sb + lr, g);  // dA D [t][s]
         const float bs = cs.beta[16 * sb + lr];
         f32x4 a;
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[m] = __builtin_fmaf(bs, lo[m], cs.beta[16 * tb + 4 * g + m] * hi[m]);
-        acc[sb] = mma16(a, bk, acc[sb]);
+        acc[sb] = mma16s(split4(a), bk, acc[sb]);
       }
     }
 #pragma unroll
@@ -949,12 +1029,12 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
         const int s2 = 16 * sb + 4 * g + r;
         const float ks = bfv(sm.K[s2][i]);
         const float tw = TW[p][sb][r];
-        const float pw = sum16(tw * ks), pe = sum16(kt[sb][r] * ks);
+        const float pw = sum16(tw * ks), pe = sum16(kt[p][sb][r] * ks);
         if (lr == 0) {
           sm.pGW[s2][it] = pw;
           sm.pDE[s2][it] = pe;
         }
-        const float val = acc[sb][r] + cs.e[s2] * kt[sb][r] + cs.Gam[s2] * tw;
+        const float val = acc[sb][r] + cs.e[s2] * kt[p][sb][r] + cs.Gam[s2] * tw;
         if (s2 < n) {
           if (dk_part)
             dk_part[(row0 + (size_t)s2 * H) * DK + i] = val;
@@ -988,15 +1068,16 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   }
   __syncthreads();
   if (tid == 0) {
-    const float dGn = *reinterpret_cast<const float*>(slot + Sl::oDGn);
     float acc = 0.f;
     for (int t = C - 1; t >= 0; --t) {
       float dgam = sm.dgam[t];
       if (t == C - 1) dgam += dGn * cs.Gam[C - 1] + sm.sum_de;
       acc += dgam;
-      if (t < n) dg[row0 + (size_t)t * H] = acc;
+      sm.dgam[t] = acc;
     }
   }
+  __syncthreads();
+  if (tid < n) dg[row0 + (size_t)tid * H] = sm.dgam[tid];
 }
 
 }  // namespace bwdb

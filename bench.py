@@ -554,6 +554,37 @@ def main():
     dec2_ms = ta.elapsed_time(tb) / 7
     dec2_bytes = N2 * H * (2 * D2 * D2 * 4 + 2 * 4 + 3 * D2 * 2 + 2 * 2 + D2 * 2 + (2 * D2 + 2) * 2)
     del c2d, ws2d, dec2
+    # fwd_bwd at d = 256 on the trainer shape: the prefill's forward, the
+    # fp32-product backward kernels and the bf16-operand reverse chain
+    log("head dim 256: fwd_bwd 1 x 10,240")
+    b2t = make_batch(212, [10240], H, D2, D2, "bf16", with_do=True)
+    t2 = to_dev(b2t)
+    t2_do = torch.from_numpy(b2t.d_o).to(dev).to(torch.bfloat16)
+    T2 = b2t.total_tokens
+    ws2f = gdn.alloc_workspace(shape2, 1, T2, gdn.GDN_OP_FWD_BWD, dev)
+    o2f = torch.empty((T2, H, D2), dtype=torch.bfloat16, device=dev)
+    g2f = [torch.empty((T2, H, D2), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    dg2f, db2f = (torch.empty((T2, H), dtype=torch.float32, device=dev) for _ in range(2))
+    fb2_ev = gdn.StageEvents(7)
+
+    def fb2():
+        gdn.gdn_cpr_fwd_bwd(shape2, t2["q"], t2["k"], t2["v"], t2["g"], t2["beta"], t2["cu"], None, t2_do, None,
+                            o2f, None, g2f[0], g2f[1], g2f[2], dg2f, db2f, None, ws2f)
+
+    fb2()
+    torch.cuda.synchronize()
+    fb2_ms, fb2_fwd, fb2_grads = [], [], []
+    for _ in range(3):
+        with fb2_ev:
+            fb2()
+        torch.cuda.synchronize()
+        fb2_ms.append(fb2_ev.events[0].elapsed_time(fb2_ev.events[6]))
+        fb2_fwd.append(fb2_ev.events[0].elapsed_time(fb2_ev.events[4]))
+        fb2_grads.append(fb2_ev.stage_ms(6))
+    del ws2f, o2f, g2f, dg2f, db2f, t2, t2_do
+    fb2_t = float(np.median(fb2_ms))
+    fb2_g = float(np.median(fb2_grads))
+    fb2_flop = bwd_state_grads_flop(C, D2, D2) * (T2 // C) * H
     flops2 = 7.0 * D2 * D2 * T * H
     head_dim_256 = {
         "prefill": {"workload": "5 x 2048 tokens, H = 16, d_k = d_v = 256, bf16", "ms": round(pre2_ms, 4),
@@ -570,7 +601,18 @@ def main():
                    "roofline": {"bound": "hbm", "algorithmic_bytes_per_call": dec2_bytes,
                                 "achieved": round(dec2_bytes / (dec2_ms / 1e3) / 1e9, 1), "peak": PEAK_HBM,
                                 "unit": "GB/s", "frac": round(dec2_bytes / (dec2_ms / 1e3) / 1e9 / PEAK_HBM, 4),
-                                "note": "whole decode call (the empty resync pass included)"}}}
+                                "note": "whole decode call (the empty resync pass included)"}},
+        "fwd_bwd": {"workload": "1 x 10240 tokens, H = 16, d_k = d_v = 256, bf16", "ms": round(fb2_t, 4),
+                    "tokens_per_s": round(T2 / (fb2_t / 1e3), 1),
+                    "stage_ms": {"forward": round(float(np.median(fb2_fwd)), 4),
+                                 "local_and_reverse_chain": round(float(np.median(fb2_ms)) - float(np.median(fb2_fwd))
+                                                                  - fb2_g, 4),
+                                 "state_and_gradients": round(fb2_g, 4)},
+                    "roofline": {"what": "the state and gradient kernel (k_bwd_grads, fp32 MFMA) against the "
+                                         "chunk-form gradient's products over their nonzero tiles",
+                                 "bound": "mfma", "algorithmic_flop": fb2_flop,
+                                 "achieved": round(fb2_flop / (fb2_g / 1e3) / 1e12, 3), "peak": PEAK_MFMA_F32,
+                                 "unit": "TFLOP/s", "frac": round(fb2_flop / (fb2_g / 1e3) / 1e12 / PEAK_MFMA_F32, 4)}}}
 
     # ---- trainer forward + backward, 1 x 10,240 tokens
     log("fwd_bwd: 1 x 10,240 tokens")

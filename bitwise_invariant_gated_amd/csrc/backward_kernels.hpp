@@ -42,13 +42,22 @@ struct BwdArgs {
   int32_t Cl;  // chunk length
 };
 
+// the slot's scratch for a kernel's C x d arrays when d > 128 (their stores
+// are complete before the barrier, so other waves read them after it)
+template <bool kWide>
+__device__ __forceinline__ void sync_scratch() {
+  if constexpr (kWide) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 template <int DK, int DV>
 struct BwdLocalLds {
+  static constexpr bool kWide = DK > 128 || DV > 128;  // W and Dd in the slot's scratch
   float At[C][C + 1];  // At[s][t] = A[t][s]
   float X[C][C + 1];
   float Pt[C][C + 1];  // Pt[s][t] = P[t][s]
-  float W[C][DK + 1];
-  float Dd[C][DV + 1];
+  float W[C][kWide ? 1 : DK + 1];
+  float Dd[C][kWide ? 1 : DV + 1];
   bwd::ChunkScalars cs;
 };
 
@@ -78,6 +87,12 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
   auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
   auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
   uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
+  // W [C][DK] and Dd [C][DV]: in the LDS, or in the slot's scratch when d > 128
+  constexpr bool kWide = Slot::kWide;
+  float* const scr = reinterpret_cast<float*>(ws + Slot::oScr);
+  float* const Wm = kWide ? scr : &sm.W[0][0];
+  float* const Dm = kWide ? scr + Slot::kArr / 4 : &sm.Dd[0][0];
+  constexpr int LW = kWide ? DK : DK + 1, LDd = kWide ? DV : DV + 1;
 
   // A = strict lower(beta_t D G) and P = lower(QK^T .* D): 16 + 16 tiles
   for (int q = 0; q < 8; ++q) {
@@ -107,23 +122,23 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
       const int tm = id / (DK / 16), it = id % (DK / 16);
       acc = tile<C>([&](int t, int r) { return sm.X[t][r] * (cs.beta[r] * cs.Gam[r]); },
                     [&](int r, int e) { return Kx(r, e); }, 16 * tm, 16 * it, acc);
-      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.W[t][e] = v; });
+      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { Wm[t * LW + e] = v; });
     } else {
       const int u = id - nW, tm = u / (DV / 16), jt = u % (DV / 16);
       acc = tile<C>([&](int t, int s) { return sm.Pt[t][s]; }, [&](int s, int j) { return dOx(s, j); }, 16 * tm,
                     16 * jt, acc);
-      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.Dd[t][j] = v; });
+      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { Dm[t * LDd + j] = v; });
       *reinterpret_cast<f32x4*>(Dd + ((size_t)(jt * (C / 16) + tm) * 64 + (tid & 63)) * 4) = acc;
     }
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   T* Kt = reinterpret_cast<T*>(ws + Slot::oKt);
   T* WnT = reinterpret_cast<T*>(ws + Slot::oWnT);
   float* Xs = reinterpret_cast<float*>(ws + Slot::oX);
   for (int idx = tid; idx < C * DK; idx += 256) {
     const int t = idx / DK, e = idx % DK;
     D::store(Kt, idx, cs.e[t] * Kx(t, e));
-    D::store(WnT, (size_t)e * C + t, -sm.W[t][e]);
+    D::store(WnT, (size_t)e * C + t, -Wm[t * LW + e]);
   }
   for (int idx = tid; idx < C * C; idx += 256) Xs[idx] = sm.X[idx / C][idx % C];
   float* R = reinterpret_cast<float*>(ws + Slot::oR);
@@ -133,8 +148,8 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = tile<C>([&](int e, int t) { return cs.Gam[t] * Qx(t, e); }, [&](int t, int j) { return dOx(t, j); },
                   16 * im, 16 * jt, acc);
-    acc = tile<C>([&](int e, int t) { return -sm.W[t][e]; }, [&](int t, int j) { return sm.Dd[t][j]; }, 16 * im,
-                  16 * jt, acc);
+    acc = tile<C>([&](int e, int t) { return -Wm[t * LW + e]; }, [&](int t, int j) { return Dm[t * LDd + j]; },
+                  16 * im, 16 * jt, acc);
     *reinterpret_cast<f32x4*>(R + ((size_t)(jt * (DK / 16) + im) * 64 + (tid & 63)) * 4) = acc;
   }
   if (tid == 0) a.gamn[(size_t)slot * H + h] = cs.Gam[C - 1];
@@ -193,16 +208,74 @@ __global__ __launch_bounds__(DV * 4) void k_bwd_chain_f32(const BwdArgs a) {
   if (a.dh0) store_state_tiles<DK, DV, 1>(a.dh0 + sh * SS, S1, jb, lane);
 }
 
+// B2 for bf16 inputs at d_k = d_v = 256 (the slot of the kernels above, Kt
+// and -W^T in bf16): the same step with each product on
+// v_mfma_f32_16x16x16_bf16, Kt or -W^T exact as the A operand and the fp32
+// adjoint (or E) split into bf16 hi + lo parts as the B operand (two products
+// per 16-wide k block; the accumulator tiles are B operands as they stand).
+// Work-groups of 4 waves own 64 state columns, a wave 16 of them.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_bwd_chain_wide(const BwdArgs a) {
+  using namespace bwd;
+  typedef BwdSlot<DK, DV, 2> Slot;
+  const int i = blockIdx.x, h = blockIdx.y, H = a.H;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int jb = blockIdx.z * 4 + (tid >> 6);
+  const int L = a.cu[i + 1] - a.cu[i];
+  const int nall = (L + a.Cl - 1) / a.Cl;
+  const size_t sh = (size_t)i * H + h;
+  const size_t SS = (size_t)DK * DV;
+  const int abase = a.all_base[i];
+  f32x4 S1[DK / 16][1];
+  load_state_tiles<DK, DV, 1>(S1, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  for (int c = nall - 1; c >= 0; --c) {
+    const size_t sl = (size_t)(abase + c) * H + h;
+    uint8_t* ws = a.ws + sl * Slot::bytes;
+    store_state_tiles<DK, DV, 1>(reinterpret_cast<float*>(ws + Slot::oDbp), S1, jb, lane);
+    const uint16_t* Kt = reinterpret_cast<const uint16_t*>(ws + Slot::oKt);    // [C][DK]
+    const uint16_t* WnT = reinterpret_cast<const uint16_t*>(ws + Slot::oWnT);  // [DK][C]
+    const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
+    float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
+    bwdb::Split4 Sp[DK / 16];
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) Sp[it] = bwdb::split4(S1[it][0]);
+    bwdb::Split4 Ep[C / 16];
+#pragma unroll
+    for (int tm = 0; tm < C / 16; ++tm) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int it = 0; it < DK / 16; ++it)
+        acc = bwdb::mma16s(bwdb::row4_bits(Kt, DK, 16 * tm + lr, 16 * it, g), Sp[it], acc);
+      Ep[tm] = bwdb::split4(acc);
+      f32x4* dd = reinterpret_cast<f32x4*>(Dd + ((size_t)(jb * (C / 16) + tm) * 64 + lane) * 4);
+      *dd = *dd + acc;
+    }
+    const float gn = a.gamn[sl];
+#pragma unroll
+    for (int im = 0; im < DK / 16; ++im) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(R + ((size_t)(jb * (DK / 16) + im) * 64 + lane) * 4);
+      f32x4 acc = {__builtin_fmaf(gn, S1[im][0][0], r[0]), __builtin_fmaf(gn, S1[im][0][1], r[1]),
+                   __builtin_fmaf(gn, S1[im][0][2], r[2]), __builtin_fmaf(gn, S1[im][0][3], r[3])};
+#pragma unroll
+      for (int tm = 0; tm < C / 16; ++tm)
+        acc = bwdb::mma16s(bwdb::row4_bits(WnT, C, 16 * im + lr, 16 * tm, g), Ep[tm], acc);
+      S1[im][0] = acc;
+    }
+  }
+  if (a.dh0) store_state_tiles<DK, DV, 1>(a.dh0 + sh * SS, S1, jb, lane);
+}
+
 template <int DK, int DV>
 struct BwdGradLds {
   static constexpr int DM = DK > DV ? DK : DV;
-  float N1[C][C + 1];   // G
+  static constexpr bool kWide = DK > 128 || DV > 128;  // N1, M1 and M2 in the slot's scratch
+  float N1[C][kWide ? 1 : C + 1];  // G
   float N2[C][C + 1];   // dT -> dX -> dA -> dG
   float N3[C][C + 1];   // X
   float N4[C][C + 1];   // dPD = (dO Delta^T) .* D, lower incl.
   float N5[C][C + 1];   // Z_P, then Y, then dA D G
-  float M1[C][DM + 1];  // W -> dO B^T -> dW -> T^T dW
-  float M2[C][DM + 1];  // U -> Delta -> dKt
+  float M1[C][kWide ? 1 : DM + 1];  // W -> dO B^T -> dW -> T^T dW
+  float M2[C][kWide ? 1 : DM + 1];  // U -> Delta -> dKt
   bwd::ChunkScalars cs;
   float rzP[C], czP[C], dGamO[C], dGamW[C], de[C], dbc[C], dbr[C], rzA[C], czA[C];
   float red[256];
@@ -241,6 +314,21 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   const float* Xs = reinterpret_cast<const float*>(ws + Slot::oX);
   auto dDx = [&](int t, int j) { return Ddg[tile_index<C>(t, j)]; };
   constexpr int nK = 4 * (DK / 16), nV = 4 * (DV / 16);
+  // the C x d arrays: W, dO B^T, dW, T^T dW share the LDS array M1 and U ->
+  // Delta, dKt share M2; when d > 128 each has a region of the slot's scratch
+  constexpr bool kWide = Slot::kWide;
+  constexpr int LM = kWide ? Slot::DM : Slot::DM + 1;
+  float* const scr = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + Slot::oScr);
+  constexpr size_t kA = Slot::kArr / 4;
+  float* const mW = kWide ? scr : &sm.M1[0][0];
+  float* const mU = kWide ? scr + kA : &sm.M2[0][0];
+  float* const mQB = kWide ? scr + 2 * kA : &sm.M1[0][0];
+  float* const mdW = kWide ? scr + 3 * kA : &sm.M1[0][0];
+  float* const mTW = kWide ? scr + 4 * kA : &sm.M1[0][0];
+  float* const mKt = kWide ? scr + 5 * kA : &sm.M2[0][0];
+  // G (C x C) as well, so that two work-groups fit a CU's LDS
+  float* const nG = kWide ? scr + 6 * kA : &sm.N1[0][0];
+  constexpr int LG = kWide ? C : C + 1;
 
   // G and X
   for (int q = 0; q < 4; ++q) {
@@ -248,10 +336,10 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = tile<DK>([&](int m, int k) { return Kx(m, k); }, [&](int k, int nn) { return Kx(nn, k); }, 16 * tm, 16 * tn,
                    acc);
-    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N1[t][s] = v; });
+    tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { nG[t * LG + s] = v; });
   }
   for (int idx = tid; idx < C * C; idx += 256) sm.N3[idx / C][idx % C] = Xs[idx];
-  __syncthreads();
+  sync_scratch<kWide>();
   // W = X diag(beta Gamma) K -> M1,  U = X diag(beta) V -> M2
   for (int id = wave; id < nK + nV; id += 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -259,15 +347,15 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
       const int tm = id / (DK / 16), it = id % (DK / 16);
       acc = tile<C>([&](int t, int r) { return sm.N3[t][r] * (cs.beta[r] * cs.Gam[r]); },
                     [&](int r, int e) { return Kx(r, e); }, 16 * tm, 16 * it, acc);
-      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
+      tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { mW[t * LM + e] = v; });
     } else {
       const int u = id - nK, tm = u / (DV / 16), jt = u % (DV / 16);
       acc = tile<C>([&](int t, int r) { return sm.N3[t][r] * cs.beta[r]; }, [&](int r, int j) { return Vx(r, j); },
                     16 * tm, 16 * jt, acc);
-      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.M2[t][j] = v; });
+      tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { mU[t * LM + j] = v; });
     }
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // Delta = U - W B (in place in M2; every tile is read and written by one wave)
   for (int id = wave; id < nV; id += 4) {
     const int tm = id / (DV / 16), jt = id % (DV / 16);
@@ -275,18 +363,18 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     {
       const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = sm.M2[16 * tm + 4 * g + r][16 * jt + lr];
+      for (int r = 0; r < 4; ++r) acc[r] = mU[(16 * tm + 4 * g + r) * LM + 16 * jt + lr];
     }
-    acc = tile<DK>([&](int t, int e) { return -sm.M1[t][e]; }, [&](int e, int j) { return Bst[bnd_index<DK>(e, j)]; },
+    acc = tile<DK>([&](int t, int e) { return -mW[t * LM + e]; }, [&](int e, int j) { return Bst[bnd_index<DK>(e, j)]; },
                    16 * tm, 16 * jt, acc);
-    tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { sm.M2[t][j] = v; });
+    tile_each(acc, 16 * tm, 16 * jt, [&](int t, int j, float v) { mU[t * LM + j] = v; });
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // dP .* D (N4), Z_P = dPD .* QK (N5); dV = T^T dDelta
   for (int q = 0; q < 4; ++q) {
     const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
     f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
-    accP = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int s) { return sm.M2[s][j]; }, 16 * tm,
+    accP = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int s) { return mU[s * LM + j]; }, 16 * tm,
                     16 * tn, accP);
     accQ = tile<DK>([&](int t, int e) { return Qx(t, e); }, [&](int e, int s) { return Kx(s, e); }, 16 * tm, 16 * tn,
                     accQ);
@@ -309,7 +397,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
       if (t < n) D::store(dvp, (row0 + (size_t)t * H) * DV + j, cs.beta[t] * v);
     });
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // row / column sums of Z_P; dO B^T -> M1
   if (tid < C) {
     float acc = 0.f;
@@ -326,9 +414,9 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = tile<DV>([&](int t, int j) { return dOx(t, j); }, [&](int j, int e) { return Bst[bnd_index<DK>(e, j)]; },
                    16 * tm, 16 * it, acc);
-    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
+    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { mQB[t * LM + e] = v; });
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // dQ = diag(Gamma) dO B^T + dPD K;  dGamma (output part) = <dO B^T, Q> per row
   T* dqp = (T*)a.dq;
   for (int id = wave; id < nK; id += 4) {
@@ -338,7 +426,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
                   acc);
     tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
       if (t < n) {
-        const float val = cs.Gam[t] * sm.M1[t][e] + v;
+        const float val = cs.Gam[t] * mQB[t * LM + e] + v;
         if (a.dq_part)
           a.dq_part[(row0 + (size_t)t * H) * DK + e] = val;
         else
@@ -348,27 +436,27 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   }
   if (tid < C) {
     float acc = 0.f;
-    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M1[tid][e], Qx(tid, e), acc);
+    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(mQB[tid * LM + e], Qx(tid, e), acc);
     sm.dGamO[tid] = acc;
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // dW = -dDelta B^T -> M1
   for (int id = wave; id < nK; id += 4) {
     const int tm = id / (DK / 16), it = id % (DK / 16);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int e) { return Bst[bnd_index<DK>(e, j)]; },
                    16 * tm, 16 * it, acc);
-    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = -v; });
+    tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) { mdW[t * LM + e] = -v; });
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // T^T dW and dKt = Delta dB'^T (kept in registers), dT -> N2
   f32x4 TW[(nK + 3) / 4], KW[(nK + 3) / 4];
   for (int q = 0, id = wave; id < nK; id += 4, ++q) {
     const int tm = id / (DK / 16), it = id % (DK / 16);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    TW[q] = tile<C>([&](int t, int s) { return cs.beta[t] * sm.N3[s][t]; }, [&](int s, int e) { return sm.M1[s][e]; },
-                    16 * tm, 16 * it, acc);
-    KW[q] = tile<DV>([&](int t, int j) { return sm.M2[t][j]; }, [&](int j, int e) { return dBp[(size_t)e * DV + j]; },
+    TW[q] = tile<C>([&](int t, int s) { return cs.beta[t] * sm.N3[s][t]; },
+                    [&](int s, int e) { return mdW[s * LM + e]; }, 16 * tm, 16 * it, acc);
+    KW[q] = tile<DV>([&](int t, int j) { return mU[t * LM + j]; }, [&](int j, int e) { return dBp[(size_t)e * DV + j]; },
                      16 * tm, 16 * it, acc);
   }
   for (int q = 0; q < 4; ++q) {
@@ -376,26 +464,26 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = tile<DV>([&](int t, int j) { return dDx(t, j); }, [&](int j, int s) { return Vx(s, j); }, 16 * tm, 16 * tn,
                    acc);
-    acc = tile<DK>([&](int t, int e) { return sm.M1[t][e]; }, [&](int e, int s) { return cs.Gam[s] * Kx(s, e); },
+    acc = tile<DK>([&](int t, int e) { return mdW[t * LM + e]; }, [&](int e, int s) { return cs.Gam[s] * Kx(s, e); },
                    16 * tm, 16 * tn, acc);
     tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N2[t][s] = v; });
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   for (int q = 0, id = wave; id < nK; id += 4, ++q) {
     const int tm = id / (DK / 16), it = id % (DK / 16);
-    tile_each(TW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M1[t][e] = v; });
-    tile_each(KW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { sm.M2[t][e] = v; });
+    tile_each(TW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { mTW[t * LM + e] = v; });
+    tile_each(KW[q], 16 * tm, 16 * it, [&](int t, int e, float v) { mKt[t * LM + e] = v; });
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // dGamma (W part), de, dbeta (column part)
   if (tid < C) {
     float acc = 0.f;
-    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M1[tid][e], Kx(tid, e), acc);
+    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(mTW[tid * LM + e], Kx(tid, e), acc);
     sm.dGamW[tid] = acc;
   } else if (tid < 2 * C) {
     const int t = tid - C;
     float acc = 0.f;
-    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(sm.M2[t][e], Kx(t, e), acc);
+    for (int e = 0; e < DK; ++e) acc = __builtin_fmaf(mKt[t * LM + e], Kx(t, e), acc);
     sm.de[t] = acc;
   } else if (tid < 3 * C) {
     const int s = tid - 2 * C;
@@ -403,9 +491,9 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     for (int t = 0; t < C; ++t) acc = __builtin_fmaf(sm.N3[t][s], sm.N2[t][s], acc);
     sm.dbc[s] = acc;
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   for (int idx = tid; idx < C * C; idx += 256) sm.N2[idx / C][idx % C] *= sm.cs.beta[idx % C];  // dX
-  __syncthreads();
+  sync_scratch<kWide>();
   // Y = dX X^T -> N5
   for (int q = 0; q < 4; ++q) {
     const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
@@ -414,7 +502,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
                   16 * tn, acc);
     tile_each(acc, 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N5[t][s] = v; });
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // dA = -X^T Y, strict lower -> N2
   {
     f32x4 accs[4];
@@ -424,13 +512,13 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
       accs[q] = tile<C>([&](int t, int r) { return sm.N3[r][t]; }, [&](int r, int s) { return sm.N5[r][s]; }, 16 * tm,
                         16 * tn, acc);
     }
-    __syncthreads();
+    sync_scratch<kWide>();
     for (int q = 0; q < 4; ++q) {
       const int tl = wave * 4 + q, tm = tl >> 2, tn = tl & 3;
       tile_each(accs[q], 16 * tm, 16 * tn, [&](int t, int s, float v) { sm.N2[t][s] = (s < t) ? -v : 0.f; });
     }
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   // dA D G -> N5, dG = dA beta_t D -> N2
   for (int idx = tid; idx < C * C; idx += 256) {
     const int t = idx / C, s = idx % C;
@@ -438,13 +526,13 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
     float zb = 0.f, dG = 0.f;
     if (s < t) {
       const float Dv = expf(cs.gam[t] - cs.gam[s]);
-      zb = dA * Dv * sm.N1[t][s];
+      zb = dA * Dv * nG[t * LG + s];
       dG = dA * cs.beta[t] * Dv;
     }
     sm.N5[t][s] = zb;
     sm.N2[t][s] = dG;
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   if (tid < C) {
     float acc = 0.f;
     for (int s = 0; s < C; ++s) acc += sm.N5[tid][s];
@@ -462,7 +550,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
       acc = __builtin_fmaf(dBp[idx], Bst[bnd_index<DK>(idx / DV, idx % DV)], acc);
     sm.red[tid] = acc;
   }
-  __syncthreads();
+  sync_scratch<kWide>();
   if (tid == 0) {
     float dGn = 0.f;
     for (int r = 0; r < 256; ++r) dGn += sm.red[r];
@@ -491,7 +579,7 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
                   16 * tm, 16 * it, acc);
     tile_each(acc, 16 * tm, 16 * it, [&](int t, int e, float v) {
       if (t < n) {
-        const float val = v + cs.e[t] * sm.M2[t][e] + cs.Gam[t] * sm.M1[t][e];
+        const float val = v + cs.e[t] * mKt[t * LM + e] + cs.Gam[t] * mTW[t * LM + e];
         if (a.dk_part)
           a.dk_part[(row0 + (size_t)t * H) * DK + e] = val;
         else

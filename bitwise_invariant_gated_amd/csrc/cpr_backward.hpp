@@ -82,8 +82,17 @@ struct BwdSlot {
   static constexpr size_t kDd = (size_t)C * DV * 4;   // dDelta, fp32 tiles
   static constexpr size_t kX = (size_t)C * C * 4;     // X, fp32 [C][C]
   static constexpr size_t kDbp = (size_t)DK * DV * 4; // dB', fp32 [DK][DV]
+  // d > 128 (bf16 inputs at d_k = d_v = 256): the C x d fp32 arrays of the
+  // local and gradient kernels (and the gradient kernel's G) do not fit the
+  // LDS and live here instead, one region of C x max(DK, DV) per array, each
+  // written once per launch
+  static constexpr bool kWide = DK > 128 || DV > 128;
+  static constexpr int DM = DK > DV ? DK : DV;
+  static constexpr size_t kArr = (size_t)C * DM * 4;
+  static constexpr int kArrays = 7;
+  static constexpr size_t kScr = kWide ? kArrays * kArr : 0;
   static constexpr size_t oKt = 0, oWnT = oKt + kKt, oR = oWnT + kWnT, oDd = oR + kR, oX = oDd + kDd,
-                          oDbp = oX + kX, bytes = oDbp + kDbp;
+                          oDbp = oX + kX, oScr = oDbp + kDbp, bytes = oScr + kScr;
 };
 
 // Chunk scalars shared by the two per-chunk kernels.

@@ -65,7 +65,7 @@ gdn_status fail(gdn_status st, const char* fmt, ...) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // wide_ok: the call serves d_k = d_v = 256 (bf16 prefill, decode,
-// continuation and the cache read-out; not fwd_bwd or the comparators)
+// continuation, fwd_bwd and the cache read-out; not the comparators)
 bool shape_ok(const gdn_cpr_shape* s, std::string* why, bool wide_ok = false) {
   if (!s) {
     *why = "shape is NULL";
@@ -81,7 +81,7 @@ bool shape_ok(const gdn_cpr_shape* s, std::string* why, bool wide_ok = false) {
     return false;
   }
   if (wide && !wide_ok) {
-    *why = "head dims of 256 serve prefill, decode and continuation only";
+    *why = "head dims of 256 serve prefill, decode, continuation and fwd_bwd only";
     return false;
   }
   if (wide && s->dtype != GDN_DTYPE_BF16) {
@@ -571,12 +571,13 @@ FwdBwdLayout fwd_bwd_layout(const gdn_cpr_shape& s, int32_t N, int64_t T) {
   off = align_up(off + NH * 4);
   L.bgamn = off;
   off = align_up(off + Amax * H * 4);
-  if (s.dtype == GDN_DTYPE_BF16)  // bwdb::Slot
+  const bool wide = DK > 128 || DV > 128;
+  if (s.dtype == GDN_DTYPE_BF16 && !wide)  // bwdb::Slot
     L.slot = 2 * (size_t)C * DK * 2 + 2 * DK * DV * 4 + (size_t)C * C * 4 + 3 * (size_t)C * DK * 4 +
              3 * (size_t)C * DV * 4 + 256;
-  else
+  else  // bwd::BwdSlot (fp32 inputs, and bf16 at d = 256 with its scratch arrays)
     L.slot = (size_t)C * DK * esz + DK * (size_t)C * esz + DK * DV * 4 + (size_t)C * DV * 4 + (size_t)C * C * 4 +
-             DK * DV * 4;
+             DK * DV * 4 + (wide ? 7 * (size_t)C * std::max(DK, DV) * 4 : 0);
   L.bslots = off;
   off = align_up(off + Amax * H * L.slot);
   L.dq_part = L.dk_part = 0;
@@ -646,9 +647,14 @@ struct FwdBwdFn {
   static gdn_status run(const PrefillArgs& pa, const BwdArgs& ba, int64_t T, size_t slot_bytes, hipStream_t st,
                         const char* fn) {
     constexpr bool kBf16 = std::is_same<D, Bf16>::value;
-    const size_t want = kBf16 ? bwdb::Slot<DK, DV>::bytes : bwd::BwdSlot<DK, DV, sizeof(typename D::T)>::bytes;
+    // d_k = d_v = 256 (bf16 only) runs the fp32-product kernels with their C x d
+    // arrays in the slot and the bf16-operand reverse chain
+    constexpr bool kWide = DK > 128 || DV > 128;
+    static_assert(!kWide || kBf16, "d = 256 takes bf16 inputs");
+    const size_t want = kBf16 && !kWide ? bwdb::Slot<DK, DV>::bytes
+                                        : bwd::BwdSlot<DK, DV, sizeof(typename D::T)>::bytes;
     if (slot_bytes != want) return fail(GDN_ERR_HIP, "%s: internal slot size mismatch", fn);
-    if constexpr (kBf16) {
+    if constexpr (kBf16 && !kWide) {
       if (T > 0) {
         // one stream only if no side stream can be had
         SideLease lease(st);
@@ -658,7 +664,16 @@ struct FwdBwdFn {
     gdn_status r = run_prefill<D, DK, DV>(pa, T, st, fn);
     if (r != GDN_OK) return r;
     const int Amax = (int)(T / pa.Cl) + pa.N;
-    if constexpr (kBf16) {
+    if constexpr (kWide) {
+      if (T > 0) hipLaunchKernelGGL((k_bwd_local<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+      hipLaunchKernelGGL((k_bwd_chain_wide<DK, DV>), dim3(pa.N, pa.H, DV / 64), dim3(256), 0, st, ba);
+      mark(5, st);
+      if (T > 0) {
+        hipLaunchKernelGGL((k_bwd_grads<D, DK, DV>), dim3(Amax, pa.H), dim3(256), 0, st, ba);
+        launch_key_head_sums(ba, T, st);
+      }
+      mark(6, st);
+    } else if constexpr (kBf16) {
       if (T > 0)
         hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
       launch_bwd_chain_bf16(ba, st);
@@ -684,6 +699,9 @@ struct FwdBwdFn {
   }
 };
 
+template <>
+struct WideFn<FwdBwdFn> : std::true_type {};
+
 }  // namespace
 
 // ===========================================================================
@@ -692,7 +710,7 @@ struct FwdBwdFn {
 extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num_seqs,
                                          int64_t total_tokens, int32_t op) {
   std::string why;
-  if (!shape_ok(shape, &why, op != GDN_OP_FWD_BWD) || num_seqs < 0 || total_tokens < 0) return 0;
+  if (!shape_ok(shape, &why, true) || num_seqs < 0 || total_tokens < 0) return 0;
   if (op == GDN_OP_PREFILL) return prefill_layout(*shape, num_seqs, total_tokens).total;
   if (op == GDN_OP_FWD_BWD) return fwd_bwd_layout(*shape, num_seqs, total_tokens).total;
   if (op == GDN_OP_DECODE) return decode_layout(*shape, num_seqs).total;
@@ -1073,7 +1091,7 @@ extern "C" gdn_status gdn_cpr_fwd_bwd(const gdn_cpr_shape* shape, int32_t num_se
                                       void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_cpr_fwd_bwd";
   std::string why;
-  if (!shape_ok(shape, &why)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (!shape_ok(shape, &why, true)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
   if (total_tokens > (int64_t)INT32_MAX / 2) return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens", fn);
   CHECK_PTR(cu_seqlens, "cu_seqlens");

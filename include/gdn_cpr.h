@@ -67,12 +67,14 @@
  *     steps (k = v = 0, g = beta = 0), which changes no real row's value.
  *     The comparators (gdn_cmp_*) take C = 64 only.
  *   - d_k = d_v = 256 is accepted for bf16 inputs by gdn_cpr_prefill,
- *     gdn_cpr_decode_step(_noalloc), gdn_cpr_prefill_continue and
- *     gdn_cpr_cache_state (the pages give no layer dimensions, so heads
- *     wider than their shapes are served too).  A state column's
- *     256 keys are then split over two lanes whose partial dot products meet
- *     in one add (order in gdn_cpr_numerics_id); prefill and decode still
- *     agree bit for bit.  fwd_bwd and the comparators take 64 and 128 only.
+ *     gdn_cpr_decode_step(_noalloc), gdn_cpr_prefill_continue,
+ *     gdn_cpr_cache_state and gdn_cpr_fwd_bwd (the pages give no layer
+ *     dimensions, so heads wider than their shapes are served too).  A state
+ *     column's 256 keys are then split over two lanes whose partial dot
+ *     products meet in one add (order in gdn_cpr_numerics_id); prefill and
+ *     decode still agree bit for bit.  fwd_bwd's forward at 256 is the
+ *     prefill; its backward takes fp32 products and a larger workspace
+ *     (gdn_cpr_workspace_size).  The comparators take 64 and 128 only.
  *   - Every pointer must be 16-byte aligned.
  *   - Errors detectable on the host (null or misaligned pointer, unsupported
  *     shape, workspace too small, negative sizes) return a status before any

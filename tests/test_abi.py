@@ -54,12 +54,17 @@ def test_workspace_size_shapes():
     assert lib.gdn_cpr_workspace_size(ctypes.byref(s), -1, 10240, _lib.GDN_OP_PREFILL) == 0
 
 
-def test_head_dim_256_serves_bf16_prefill_decode_and_continuation_only():
+def test_head_dim_256_serves_bf16_prefill_decode_continuation_and_fwd_bwd_only():
     lib = _lib_or_skip()
     s = _shape(16, 256, 256)
-    for op in (_lib.GDN_OP_PREFILL, _lib.GDN_OP_DECODE, _lib.GDN_OP_PREFILL_CONTINUE):
+    for op in (_lib.GDN_OP_PREFILL, _lib.GDN_OP_DECODE, _lib.GDN_OP_PREFILL_CONTINUE, _lib.GDN_OP_FWD_BWD):
         assert lib.gdn_cpr_workspace_size(ctypes.byref(s), 4, 4096, op) > 0, op
-    assert lib.gdn_cpr_workspace_size(ctypes.byref(s), 4, 4096, _lib.GDN_OP_FWD_BWD) == 0
+    # fwd_bwd at d = 256: per (chunk slot, head) Kt and -W^T (bf16), R, dDelta,
+    # X, dB' and seven C x 256 fp32 arrays of the local and gradient kernels
+    f1 = lib.gdn_cpr_workspace_size(ctypes.byref(s), 1, 64, _lib.GDN_OP_FWD_BWD)
+    f2 = lib.gdn_cpr_workspace_size(ctypes.byref(s), 1, 128, _lib.GDN_OP_FWD_BWD)
+    slot = 2 * 64 * 256 * 2 + 2 * 256 * 256 * 4 + 64 * 256 * 4 + 64 * 64 * 4 + 7 * 64 * 256 * 4
+    assert f2 - f1 >= 16 * slot
     assert lib.gdn_cpr_workspace_size(ctypes.byref(_shape(16, 256, 256, dtype=_lib.GDN_DTYPE_F32)), 4, 4096,
                                       _lib.GDN_OP_PREFILL) == 0
     assert lib.gdn_cpr_workspace_size(ctypes.byref(_shape(16, 128, 256)), 4, 4096, _lib.GDN_OP_PREFILL) == 0

@@ -1,4 +1,4 @@
-"""GPU: head dims d_k = d_v = 256 (bf16 prefill, decode and continuation).
+"""GPU: head dims d_k = d_v = 256 (bf16 prefill, decode, continuation and fwd_bwd).
 
 A state column's 256 keys are split over two lanes (keys 0..127 and
 128..255), whose partial sums meet in one add; the scan, decode and the
@@ -107,3 +107,43 @@ def test_d256_final_state_outputs_equal_cache_state():
         gdn.gdn_cpr_decode_step(db.shape, x["q"], x["k"], x["v"], x["g"], x["beta"], cache, od, wsd, hT=hd)
         torch.cuda.synchronize()
         assert np.array_equal(bits(hd), bits(state_of(db.shape, cache))), s
+
+
+def test_d256_fwd_bwd_matches_oracle():
+    """fwd_bwd at d = 256: the forward bit-equal to prefill (outputs and hT),
+    the gradients within the bf16 tolerance of the oracle's analytic backward
+    (d_hT given, h0 given), on ragged lengths including empty and partial
+    chunks."""
+    from test_gpu_fwd_bwd import check_grads, run_fwd_bwd
+    note("d=256 fwd_bwd vs oracle")
+    lens = [1, 63, 64, 65, 130, 0, 200]
+    b = make_batch(880, lens, 2, D, D, dtype="bf16", h0_std=0.1, with_do=True)
+    rng = np.random.default_rng(9)
+    d_hT = rng.standard_normal((len(lens), 2, D, D)).astype(np.float32)
+    db = DevBatch(b)
+    out = run_fwd_bwd(db, d_hT)
+    o_p, c_p = prefill(db)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out["o"]), bits(o_p))
+    assert np.array_equal(bits(out["hT"]), bits(state_of(db.shape, c_p)))
+    errs = check_grads(b, out, d_hT)
+    print("d=256 fwd_bwd:", {n: f"{e[0]:.2e}/{e[2]:.2e}" for n, e in errs.items()})
+
+
+def test_d256_fwd_bwd_rerun_identical_and_zero_upstream():
+    """Reruns give identical bits; dO = 0 and no d_hT give exactly zero
+    gradients."""
+    from test_gpu_fwd_bwd import NAMES, run_fwd_bwd
+    note("d=256 fwd_bwd rerun, zero upstream")
+    b = make_batch(881, [150, 64, 17], 2, D, D, dtype="bf16", h0_std=0.1, with_do=True)
+    db = DevBatch(b)
+    out1 = run_fwd_bwd(db)
+    out2 = run_fwd_bwd(db)
+    torch.cuda.synchronize()
+    for n in ("o", "hT") + NAMES:
+        assert np.array_equal(bits(out1[n]), bits(out2[n])), n
+    b.d_o[:] = 0.0
+    out0 = run_fwd_bwd(DevBatch(b))
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert float(torch.max(torch.abs(out0[n].float()))) == 0.0, n

@@ -498,12 +498,19 @@ __device__ __forceinline__ void scan_tokens(float (&s)[KeySplit<DK>::kKeys], con
   for (int t = 0; t < n; ++t) {
     const float out =
         token_step<DK>(s, kf, qf, lane_bcast(c_l, t), lane_bcast(b_l, t), (renorm >> t) & 1, vcur);
-    if (lane < KeySplit<DK>::kCols) {
+    auto store = [&] {
       if constexpr (sizeof(T) == 2)
         __builtin_amdgcn_raw_buffer_store_b16(D::round(out), ro, v_off, (uint32_t)t * v_stride, 0);
       else
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ro, v_off, (uint32_t)t * v_stride, 0);
-    }
+    };
+    // with one lane per column every lane stores, with no branch around the
+    // store, so the wait before the next token's operands can leave the
+    // store in flight (a store under an exec branch makes it wait for all)
+    if constexpr (KeySplit<DK>::kParts == 1)
+      store();
+    else if (lane < KeySplit<DK>::kCols)
+      store();
     if (t + 1 < n) take(t + 1);
   }
 }

@@ -147,3 +147,33 @@ def test_d256_fwd_bwd_rerun_identical_and_zero_upstream():
     torch.cuda.synchronize()
     for n in NAMES:
         assert float(torch.max(torch.abs(out0[n].float()))) == 0.0, n
+
+
+def test_d256_fwd_bwd_shared_key_heads_and_short_chunks():
+    """d = 256 fwd_bwd with key heads shared by pairs of value heads: dq, dk
+    (group sums) against the oracle, the rest bit-equal to the run with each
+    key head repeated; and with C = 32 (identity-padded rows): forward ==
+    prefill bitwise, gradients against the oracle."""
+    from test_gpu_fwd_bwd import check_grads, run_fwd_bwd
+    from test_gpu_key_heads import repeated
+    note("d=256 fwd_bwd shared key heads, C=32")
+    lens = [1, 64, 130, 0, 97]
+    b = make_batch(882, lens, 4, D, D, dtype="bf16", h0_std=0.1, with_do=True, num_key_heads=2)
+    d_hT = np.random.default_rng(10).standard_normal((len(lens), 4, D, D)).astype(np.float32)
+    out = run_fwd_bwd(DevBatch(b), d_hT)
+    out_r = run_fwd_bwd(DevBatch(repeated(b)), d_hT)
+    torch.cuda.synchronize()
+    errs = check_grads(b, out, d_hT)
+    print("d=256 grouped:", {n: f"{e[0]:.2e}/{e[2]:.2e}" for n, e in errs.items()})
+    for n in ("o", "hT", "dv", "dg", "dbeta", "dh0"):
+        assert np.array_equal(bits(out[n]), bits(out_r[n])), n
+    lens = [1, 31, 32, 33, 100]
+    b = make_batch(883, lens, 2, D, D, dtype="bf16", h0_std=0.1, with_do=True)
+    db = DevBatch(b, 32)
+    out = run_fwd_bwd(db)
+    o_p, c_p = prefill(db)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out["o"]), bits(o_p))
+    assert np.array_equal(bits(out["hT"]), bits(state_of(db.shape, c_p)))
+    errs = check_grads(b, out, None)
+    print("d=256 C=32:", {n: f"{e[0]:.2e}/{e[2]:.2e}" for n, e in errs.items()})

@@ -213,11 +213,20 @@ __global__ __launch_bounds__(DV * 4) void k_bwd_chain_f32(const BwdArgs a) {
 // v_mfma_f32_16x16x16_bf16, Kt or -W^T exact as the A operand and the fp32
 // adjoint (or E) split into bf16 hi + lo parts as the B operand (two products
 // per 16-wide k block; the accumulator tiles are B operands as they stand).
-// Work-groups of 4 waves own 64 state columns, a wave 16 of them.
+// Work-groups of 4 waves own 64 state columns, a wave 16 of them.  Each
+// chunk's Kt and -W^T (64 KiB) pass through the LDS: they are fetched into
+// registers with 16-byte loads one chunk ahead and written to the LDS at the
+// start of the chunk's step.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void k_bwd_chain_wide(const BwdArgs a) {
   using namespace bwd;
+  using mfma::u32x4;
   typedef BwdSlot<DK, DV, 2> Slot;
+  constexpr int kLK = DK + 8, kLC = C + 8;  // LDS rows (bf16), padded against bank conflicts
+  constexpr int kPieces = (int)((Slot::kKt + Slot::kWnT) / 16), kPer = kPieces / 256;
+  static_assert(kPer * 256 == kPieces && Slot::oWnT == Slot::kKt, "Kt and -W^T are adjacent, split over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[C][kLK];
+  __shared__ __attribute__((aligned(16))) uint16_t sWn[DK][kLC];
   const int i = blockIdx.x, h = blockIdx.y, H = a.H;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int jb = blockIdx.z * 4 + (tid >> 6);
@@ -226,14 +235,37 @@ __global__ __launch_bounds__(256) void k_bwd_chain_wide(const BwdArgs a) {
   const size_t sh = (size_t)i * H + h;
   const size_t SS = (size_t)DK * DV;
   const int abase = a.all_base[i];
+  auto slot_of = [&](int c) { return a.ws + ((size_t)(abase + c) * H + h) * Slot::bytes; };
+  // piece p (16 bytes) of the slot's Kt (then -W^T) bytes
+  u32x4 pre[kPer];
+  auto fetch = [&](int c) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(slot_of(c) + Slot::oKt);
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) pre[m] = src[tid + 256 * m];
+  };
+  auto stage = [&] {
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int p = tid + 256 * m;
+      if (p < (int)(Slot::kKt / 16)) {
+        const int r = p / (DK / 8), c8 = (p % (DK / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&sKt[r][c8]) = pre[m];
+      } else {
+        const int q = p - (int)(Slot::kKt / 16), r = q / (C / 8), c8 = (q % (C / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&sWn[r][c8]) = pre[m];
+      }
+    }
+  };
   f32x4 S1[DK / 16][1];
   load_state_tiles<DK, DV, 1>(S1, a.d_hT ? a.d_hT + sh * SS : nullptr, jb, lane);
+  if (nall > 0) fetch(nall - 1);
   for (int c = nall - 1; c >= 0; --c) {
-    const size_t sl = (size_t)(abase + c) * H + h;
-    uint8_t* ws = a.ws + sl * Slot::bytes;
+    uint8_t* ws = slot_of(c);
+    __syncthreads();  // the previous chunk's LDS operands are no longer read
+    stage();
+    __syncthreads();
+    if (c > 0) fetch(c - 1);
     store_state_tiles<DK, DV, 1>(reinterpret_cast<float*>(ws + Slot::oDbp), S1, jb, lane);
-    const uint16_t* Kt = reinterpret_cast<const uint16_t*>(ws + Slot::oKt);    // [C][DK]
-    const uint16_t* WnT = reinterpret_cast<const uint16_t*>(ws + Slot::oWnT);  // [DK][C]
     const float* R = reinterpret_cast<const float*>(ws + Slot::oR);
     float* Dd = reinterpret_cast<float*>(ws + Slot::oDd);
     bwdb::Split4 Sp[DK / 16];
@@ -245,12 +277,12 @@ __global__ __launch_bounds__(256) void k_bwd_chain_wide(const BwdArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int it = 0; it < DK / 16; ++it)
-        acc = bwdb::mma16s(bwdb::row4_bits(Kt, DK, 16 * tm + lr, 16 * it, g), Sp[it], acc);
+        acc = bwdb::mma16s(bwdb::row4_bits(&sKt[0][0], kLK, 16 * tm + lr, 16 * it, g), Sp[it], acc);
       Ep[tm] = bwdb::split4(acc);
       f32x4* dd = reinterpret_cast<f32x4*>(Dd + ((size_t)(jb * (C / 16) + tm) * 64 + lane) * 4);
       *dd = *dd + acc;
     }
-    const float gn = a.gamn[sl];
+    const float gn = a.gamn[(size_t)(abase + c) * H + h];
 #pragma unroll
     for (int im = 0; im < DK / 16; ++im) {
       const f32x4 r = *reinterpret_cast<const f32x4*>(R + ((size_t)(jb * (DK / 16) + im) * 64 + lane) * 4);
@@ -258,7 +290,7 @@ __global__ __launch_bounds__(256) void k_bwd_chain_wide(const BwdArgs a) {
                    __builtin_fmaf(gn, S1[im][0][2], r[2]), __builtin_fmaf(gn, S1[im][0][3], r[3])};
 #pragma unroll
       for (int tm = 0; tm < C / 16; ++tm)
-        acc = bwdb::mma16s(bwdb::row4_bits(WnT, C, 16 * im + lr, 16 * tm, g), Ep[tm], acc);
+        acc = bwdb::mma16s(bwdb::row4_bits(&sWn[0][0], kLC, 16 * im + lr, 16 * tm, g), Ep[tm], acc);
       S1[im][0] = acc;
     }
   }

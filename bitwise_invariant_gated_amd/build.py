@@ -89,7 +89,7 @@ def check_dpp_hazards(asm_text: str) -> list:
 # launch and memory traffic per spill, so the build rejects them
 HOT_KERNELS = ("k_scanIN3cpr4Bf16", "k_chain_scan_bf16", "k_decodeIN3cpr4Bf16", "k_resync_bf16",
                "k_cont_headIN3cpr4Bf16", "k_chunk_local_prefill_bf16", "k_chain_prefill_bf16", "k_bwd_local_bf16",
-               "k_bwd_chain_bf16", "k_bwd_state_bf16", "k_bwd_grads_bf16", "k_plan")
+               "k_bwd_chain_bf16", "k_bwd_state_grads_bf16", "k_plan")
 
 
 def check_spills(asm_text: str, hot=HOT_KERNELS) -> list:

@@ -42,8 +42,9 @@ struct BwdArgs {
   int32_t Cl;  // chunk length
 };
 
-// the slot's scratch for a kernel's C x d arrays when d > 128 (their stores
-// are complete before the barrier, so other waves read them after it)
+// Barrier after writes to the slot's scratch (the C x d arrays of the local
+// and gradient kernels when d > 128): each wave waits for its stores to
+// complete first, so every wave of the work-group reads them after it.
 template <bool kWide>
 __device__ __forceinline__ void sync_scratch() {
   if constexpr (kWide) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -663,28 +664,26 @@ __global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_local_bf16(con
                             a.ws + p.sl * Sl::bytes, a.gamn + p.sl);
 }
 
+// The state and gradient stages of one (chunk slot, head) in one work-group,
+// the state stage's slot results (Dd, Delta, QB, dWn, dKt, dGamma_n) read back
+// by the gradient stage once every wave's stores are complete.
 template <int DK, int DV>
-__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_state_bf16(const BwdArgs a) {
+__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_state_grads_bf16(const BwdArgs a) {
   typedef bwdb::Slot<DK, DV> Sl;
   constexpr int W = kBwdWaves<DK, DV>;
-  __shared__ bwdb::StateLds<DK, DV, W> sm;
+  __shared__ bwdb::StateGradLds<DK, DV, W> sm;
   SlotPos p;
   if (!slot_pos(a, p)) return;
+  uint8_t* slot = a.ws + p.sl * Sl::bytes;
   bwdb::state_stage<DK, DV, W>(sm, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.d_o,
-                            (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
-                            a.bnd + p.sl * DK * DV, a.ws + p.sl * Sl::bytes);
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__((kBwdWaves<DK, DV> * 64)) void k_bwd_grads_bf16(const BwdArgs a) {
-  typedef bwdb::Slot<DK, DV> Sl;
-  __shared__ bwdb::GradLds<DK, DV> sm;
-  SlotPos p;
-  if (!slot_pos(a, p)) return;
-  bwdb::grad_stage<DK, DV, kBwdWaves<DK, DV>>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.d_o, (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0,
-                           a.Hk, p.n, a.ws + p.sl * Sl::bytes, (uint16_t*)a.dq, (uint16_t*)a.dk, a.dq_part,
-                           a.dk_part, (uint16_t*)a.dv, a.dg, a.dbeta);
+                               (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H, p.kq0, a.Hk, p.n,
+                               a.bnd + p.sl * DK * DV, slot);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  bwdb::grad_stage<DK, DV, W>(sm, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                              (const uint16_t*)a.d_o, (const uint16_t*)a.g, (const uint16_t*)a.beta, p.row0, a.H,
+                              p.kq0, a.Hk, p.n, slot, (uint16_t*)a.dq, (uint16_t*)a.dk, a.dq_part, a.dk_part,
+                              (uint16_t*)a.dv, a.dg, a.dbeta);
 }
 
 // Reverse chain, bf16 path: the forward chain's structure run from the last

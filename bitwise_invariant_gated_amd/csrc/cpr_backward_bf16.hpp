@@ -414,20 +414,7 @@ __device__ __forceinline__ void local_stage(LocalLds<DK, DV>& sm, const uint16_t
 
 // ===========================================================================
 // state stage (64 W threads): Dd, Delta, QB, dWn, dKt, dGamma_n
-template <int DK, int DV, int W>
-struct StateLds {
-  static constexpr int kLK = DK + 8, kLV = DV + 8, kLX = C + 4, kLD = DV + 4, kLB = 32 + 4;
-  uint16_t K[C][kLK];
-  uint16_t V[C][kLV];
-  uint16_t dO[C][kLV];
-  float X[C][kLX];
-  float Dd[C][kLD];
-  float De[C][kLD];
-  float Bs[DK][kLB];  // 32 columns of B or dB', row-major
-  bwd::ChunkScalars cs;
-  float red[64 * W];
-};
-
+//
 // Columns 32 jb .. 32 jb + 31 of a TL state (DK rows), over NT threads: load()
 // issues the reads into registers, store() writes them into Bs row-major, so
 // a block's reads can be in flight while the previous block is consumed.
@@ -455,13 +442,13 @@ struct ColLoads {
   }
 };
 
-template <int DK, int DV, int W>
-__device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint16_t* k, const uint16_t* v,
+template <int DK, int DV, int W, class SM>
+__device__ __forceinline__ void state_stage(SM& sm, const uint16_t* k, const uint16_t* v,
                                             const uint16_t* d_o, const uint16_t* gp, const uint16_t* bp,
                                             size_t row0, int H, size_t kq0, int Hk, int n,
                                             const float* __restrict__ B, uint8_t* __restrict__ slot) {
   typedef Slot<DK, DV> Sl;
-  typedef StateLds<DK, DV, W> Lds;
+  typedef SM Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   // wave w makes the 16-wide row / column tiles w, w + W, ...
   static_assert((DK / 16) % W == 0 && (DV / 16) % W == 0, "tiles per wave");
@@ -644,28 +631,43 @@ __device__ __forceinline__ void state_stage(StateLds<DK, DV, W>& sm, const uint1
 
 // ===========================================================================
 // local gradients (64 W threads): dq, dk, dv, dg, dbeta of the chunk's tokens
-template <int DK, int DV>
-struct GradLds {
-  static constexpr int kLK = DK + 8, kLV = DV + 8, kLX = C + 4;
+// The state and gradient stages of one (chunk slot, head) in one work-group:
+// K, V, dO, X and the chunk scalars, staged by the state stage, stay in the
+// LDS for the gradient stage; the two stages' other arrays share the rest.
+template <int DK, int DV, int W>
+struct StateGradLds {
+  static constexpr int kLK = DK + 8, kLV = DV + 8, kLX = C + 4, kLD = DV + 4, kLB = 32 + 4;
   uint16_t K[C][kLK];
-  uint16_t Q[C][kLK];
   uint16_t V[C][kLV];
   uint16_t dO[C][kLV];
   float X[C][kLX];
-  float dPD[C][kLX];
-  float M2[C][kLX];  // Z_P, then dT -> dX, then dA .* D
-  float M3[C][kLX];  // Y, then Z_A
   bwd::ChunkScalars cs;
-  float pGO[C][DK / 16], pGW[C][DK / 16], pDE[C][DK / 16];  // per-row partial dot products
-  float rzP[C], czP[C], dbc[C], dbr[C], rzA[C], czA[C], dgo[C], de[C], dgam[C];
-  float sum_de;
+  union alignas(16) {
+    struct {  // state stage
+      float Dd[C][kLD];
+      float De[C][kLD];
+      float Bs[DK][kLB];
+      float red[64 * W];
+    };
+    struct {  // gradient stage
+      uint16_t Q[C][kLK];
+      float dPD[C][kLX];
+      float M2[C][kLX];
+      float M3[C][kLX];
+      float pGO[C][DK / 16], pGW[C][DK / 16], pDE[C][DK / 16];
+      float rzP[C], czP[C], dbc[C], dbr[C], rzA[C], czA[C], dgo[C], de[C], dgam[C];
+      float sum_de;
+    };
+  };
 };
 
-template <int DK, int DV, int W>
+// K, V, dO, X and the chunk scalars are already in the LDS (the state stage
+// of the same work-group put them there); only Q is loaded.
+template <int DK, int DV, int W, class SM>
 // dq and dk go to rows kq0 + t Hk of [T, Hk, DK] in bf16 or, when the key
 // heads are shared (dq_part non-null), to the value head's rows row0 + t H of
 // fp32 [T, H, DK] partials that a later pass sums over the group.
-__device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* q, const uint16_t* k,
+__device__ __forceinline__ void grad_stage(SM& sm, const uint16_t* q, const uint16_t* k,
                                            const uint16_t* v, const uint16_t* d_o, const uint16_t* gp,
                                            const uint16_t* bp, size_t row0, int H, size_t kq0, int Hk, int n,
                                            const uint8_t* __restrict__ slot, uint16_t* __restrict__ dq,
@@ -673,7 +675,7 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
                                            float* __restrict__ dk_part, uint16_t* __restrict__ dv,
                                            float* __restrict__ dg, float* __restrict__ dbeta) {
   typedef Slot<DK, DV> Sl;
-  typedef GradLds<DK, DV> Lds;
+  typedef SM Lds;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   // d-wide products: wave w makes the 16-wide tiles w, w + W, ...; C x C
   // products: wave w < C / 16 makes row or column block w
@@ -692,24 +694,12 @@ __device__ __forceinline__ void grad_stage(GradLds<DK, DV>& sm, const uint16_t* 
   const int tn_p = wave % NB;  // the dPD phase's column block
   f32x4 bde_raw[DV / 16];
   {
-    RowLoads<DK, 64 * W> rk, rq;
-    RowLoads<DV, 64 * W> rv, rd;
-    XLoads<64 * W> rx;
-    float g_t, b_t;
-    rk.load(k, kq0, Hk, n);
+    RowLoads<DK, 64 * W> rq;
     rq.load(q, kq0, Hk, n);
-    rv.load(v, row0, H, n);
-    rd.load(d_o, row0, H, n);
-    rx.load(Xg);
-    load_scalars(gp, bp, row0, H, n, g_t, b_t);
 #pragma unroll
     for (int jb = 0; jb < DV / 16; ++jb) bde_raw[jb] = row4_f(Deg, DV, 16 * tn_p + lr, 16 * jb, g);
-    rk.store(sm.K, n);
     rq.store(sm.Q, n);
-    rv.store(sm.V, n);
-    rd.store(sm.dO, n);
-    rx.store(sm.X);
-    bwd::chunk_scalars_from(sm.cs, g_t, b_t);  // synchronises
+    __syncthreads();
   }
   const bwd::ChunkScalars& cs = sm.cs;
 

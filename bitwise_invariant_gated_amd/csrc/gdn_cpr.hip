@@ -638,8 +638,7 @@ struct FwdBwdFn {
     if (!ev(hipStreamWaitEvent(st, x.join, 0)))
       return fail(GDN_ERR_HIP, "%s: stream join failed: %s", fn, hipGetErrorString(hipGetLastError()));
     mark(5, st);
-    hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
-    hipLaunchKernelGGL((k_bwd_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
+    hipLaunchKernelGGL((k_bwd_state_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
     launch_key_head_sums(ba, T, st);
     mark(6, st);
     return launch_status(fn);
@@ -679,8 +678,8 @@ struct FwdBwdFn {
       launch_bwd_chain_bf16(ba, st);
       mark(5, st);
       if (T > 0) {
-        hipLaunchKernelGGL((k_bwd_state_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
-        hipLaunchKernelGGL((k_bwd_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
+        hipLaunchKernelGGL((k_bwd_state_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0,
+                           st, ba);
         launch_key_head_sums(ba, T, st);
       }
       mark(6, st);

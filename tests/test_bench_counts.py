@@ -3,10 +3,12 @@ the MFMA instruction counters of one fwd_bwd call (1 x 10,240 tokens, 16
 heads, d = 128, C = 64: 2,560 chunk-heads), as recorded in
 profiles/prefill_5x2048_decode_256x1_counters.md:
   - the algorithmic products over their nonzero 16 x 16 tiles, 19,365,888
-    flops per chunk-head (the fp32-MFMA build: SQ_INSTS_VALU_MFMA_MOPS_F32);
-  - the bf16 MFMA flops the hi/lo split build executes, 44,072,960 per
-    chunk-head (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / 2,560: state
-    27,131,904, gradients 16,941,056)."""
+    flops per chunk-head (what the stages executed when their products ran on
+    fp32 MFMA, SQ_INSTS_VALU_MFMA_MOPS_F32 x 512 / 2,560);
+  - the bf16 MFMA flops they execute with the fp32-operand products split
+    into bf16 hi/lo parts, 44,072,960 per chunk-head
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / 2,560: state 27,131,904,
+    gradients 16,941,056)."""
 
 import os
 import sys

@@ -610,11 +610,11 @@ struct FwdBwdFn {
   }
   // bf16 path on two streams.  The backward's local terms and reverse chain
   // read only the inputs, d_o, d_hT and the plan, so they run on the side
-  // stream beside the forward chunk products, boundary chain and in-chunk
-  // scan; the state and gradient stages, which need both chains, follow on
-  // the caller's stream after the join.  (Running the scan beside the state
-  // and gradient stages instead measured the same.)  Every kernel computes
-  // what it computes in the one-stream order, so the bits are the same.
+  // stream beside the forward boundary chain and in-chunk scan (after the
+  // forward's chunk products); the state and gradient stages, which need both
+  // chains, follow on the caller's stream after the join.  Every kernel
+  // computes what it computes in the one-stream order, so the bits are the
+  // same.
   static gdn_status run_overlapped(const PrefillArgs& pa, const BwdArgs& ba, int64_t T, hipStream_t st,
                                    const SideStream& x, const char* fn) {
     const int Fmax = (int)(T / pa.Cl), Amax = Fmax + pa.N;
@@ -623,14 +623,17 @@ struct FwdBwdFn {
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.Cl, pa.full_base, pa.all_base,
                        FusedPlan{});
     mark(1, st);
+    // the forward's chunk products first, on the whole chip: launched beside
+    // the backward's local stage, whose work-groups take a CU each, they would
+    // wait for CUs to free up and delay the forward chain behind them
+    if (Fmax > 0)
+      hipLaunchKernelGGL((k_chunk_local_prefill_bf16<DK, DV>), dim3(Fmax, pa.H), dim3(256), 0, st, pa);
+    mark(2, st);
     if (!ev(hipEventRecord(x.fork, st)) || !ev(hipStreamWaitEvent(x.s, x.fork, 0)))
       return fail(GDN_ERR_HIP, "%s: stream fork failed: %s", fn, hipGetErrorString(hipGetLastError()));
     hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, x.s, ba);
     launch_bwd_chain_bf16(ba, x.s);
     if (!ev(hipEventRecord(x.join, x.s))) return fail(GDN_ERR_HIP, "%s: event record failed", fn);
-    if (Fmax > 0)
-      hipLaunchKernelGGL((k_chunk_local_prefill_bf16<DK, DV>), dim3(Fmax, pa.H), dim3(256), 0, st, pa);
-    mark(2, st);
     if (pa.N > 0) launch_chain_bf16<DK, DV>(pa, st);
     mark(3, st);
     hipLaunchKernelGGL((k_scan<D, DK, DV>), dim3(Amax, pa.H, DV / kWave), dim3(kWave), 0, st, pa);

@@ -337,10 +337,10 @@ gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t num_seqs, con
  * takes from a small pool the library keeps per device (at most eight
  * streams, created at the default priority when first needed and kept until
  * the process ends; a call holds its stream only while it enqueues, so
- * concurrent callers never share one).  The backward's local terms and
- * reverse chain run on the second stream beside the forward chunk products,
- * chain and in-chunk scan on `stream`; the state and gradient stages follow
- * on `stream`.  Events fork the work from `stream` and join it back, so
+ * concurrent callers never share one).  After the forward's chunk products,
+ * the backward's local terms and reverse chain run on the second stream
+ * beside the forward chain and in-chunk scan on `stream`; the state and
+ * gradient stages follow on `stream`.  Events fork the work from `stream` and join it back, so
  * everything the call does is ordered on `stream` as with one stream (also
  * under graph capture, where the fork and join become graph edges; make a
  * first call outside a capture, since a call may create a pooled stream).

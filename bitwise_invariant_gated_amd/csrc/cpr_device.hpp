@@ -142,6 +142,104 @@ __device__ __forceinline__ void mul_bcast(float& acc, float src, float x) {
 }
 #undef CPR_MUL_BCAST_CASE
 
+// The two passes of token_step as asm statements of 16 keys each.  They hold
+// the same DPP multiply-adds, in the same order, as one statement per
+// instruction would, but the compiler brackets every inline-asm statement
+// that reads a register another one wrote since its last own instruction
+// with an s_nop (it cannot see that no 16-bit destination select is
+// involved), which cost one issue slot per four multiply-adds.  Within a
+// statement no instruction reads, as its DPP source, a register written in
+// the statement (the sources are k and q), and an accumulator or state
+// element is read at the earliest four instructions after it is written.
+#define CPR_DPP(OP, A, S, X, N) #OP " %" #A ", %" #S ", %" #X " row_newbcast:" #N " row_mask:0xf bank_mask:0xf\n"
+// pass A, keys 8N .. 8N+7: p_(e mod 4) += k[8N+e] * N[8N+e]; operands
+// %0..%3 p_0..p_3, %4..%11 k elements 0..7 of the lane's slot, S0..S7 the keys' N
+#define CPR_PA_GROUP(N, S0, S1, S2, S3, S4, S5, S6, S7)                                               \
+  CPR_DPP(v_fmac_f32_dpp, 0, 4, S0, N) CPR_DPP(v_fmac_f32_dpp, 1, 5, S1, N)                              \
+  CPR_DPP(v_fmac_f32_dpp, 2, 6, S2, N) CPR_DPP(v_fmac_f32_dpp, 3, 7, S3, N)                              \
+  CPR_DPP(v_fmac_f32_dpp, 0, 8, S4, N) CPR_DPP(v_fmac_f32_dpp, 1, 9, S5, N)                              \
+  CPR_DPP(v_fmac_f32_dpp, 2, 10, S6, N) CPR_DPP(v_fmac_f32_dpp, 3, 11, S7, N)
+// keys 0 .. 7: the first four terms start the accumulators
+#define CPR_PA_FIRST                                                                                     \
+  CPR_DPP(v_mul_f32_dpp, 0, 4, 12, 0) CPR_DPP(v_mul_f32_dpp, 1, 5, 13, 0)                                \
+  CPR_DPP(v_mul_f32_dpp, 2, 6, 14, 0) CPR_DPP(v_mul_f32_dpp, 3, 7, 15, 0)                                \
+  CPR_DPP(v_fmac_f32_dpp, 0, 8, 16, 0) CPR_DPP(v_fmac_f32_dpp, 1, 9, 17, 0)                              \
+  CPR_DPP(v_fmac_f32_dpp, 2, 10, 18, 0) CPR_DPP(v_fmac_f32_dpp, 3, 11, 19, 0)
+#define CPR_PA_IN(B)                                                                                     \
+  "v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]), "v"(kf[7]),        \
+      "v"(s[16 * B]), "v"(s[16 * B + 1]), "v"(s[16 * B + 2]), "v"(s[16 * B + 3]), "v"(s[16 * B + 4]),    \
+      "v"(s[16 * B + 5]), "v"(s[16 * B + 6]), "v"(s[16 * B + 7]), "v"(s[16 * B + 8]), "v"(s[16 * B + 9]), \
+      "v"(s[16 * B + 10]), "v"(s[16 * B + 11]), "v"(s[16 * B + 12]), "v"(s[16 * B + 13]),                \
+      "v"(s[16 * B + 14]), "v"(s[16 * B + 15])
+#define CPR_PA_CASE(B, N0, N1)                                                                           \
+  if constexpr (I == B)                                                                                  \
+    asm volatile(CPR_PA_GROUP(N0, 12, 13, 14, 15, 16, 17, 18, 19) CPR_PA_GROUP(N1, 20, 21, 22, 23, 24, 25, 26, 27) \
+                 : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3])                                        \
+                 : CPR_PA_IN(B));
+// pass A over keys 16 I .. 16 I + 15 (the accumulators start at I = 0)
+template <int I, int DK>
+__device__ __forceinline__ void pass_a_keys16(float (&p)[4], const float (&kf)[8], const float (&s)[DK]) {
+  static_assert(I >= 0 && I < 8 && 16 * I + 16 <= DK, "16-key groups of at most 128 keys");
+  if constexpr (I == 0)
+    asm volatile(CPR_PA_FIRST CPR_PA_GROUP(1, 20, 21, 22, 23, 24, 25, 26, 27)
+                 : "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3])
+                 : CPR_PA_IN(0));
+  CPR_PA_CASE(1, 2, 3) CPR_PA_CASE(2, 4, 5) CPR_PA_CASE(3, 6, 7) CPR_PA_CASE(4, 8, 9)
+  CPR_PA_CASE(5, 10, 11) CPR_PA_CASE(6, 12, 13) CPR_PA_CASE(7, 14, 15)
+}
+#undef CPR_PA_CASE
+#undef CPR_PA_IN
+#undef CPR_PA_FIRST
+#undef CPR_PA_GROUP
+
+// pass B over keys 8 I .. 8 I + 7: for each pair of keys the update
+// N[i] += k[i] w, N[i+1] += k[i+1] w, then the output terms of the pair
+// before it, o_0 += q[i-2] N[i-2], o_1 += q[i-1] N[i-1].  Operands: %0..%7
+// the keys' N, %8 %9 o_0 o_1, %10 %11 N of the two keys before the group,
+// %12..%19 k, %20..%27 q elements 0..7 of the lane's slot, %28 w.
+#define CPR_PB_U(A, K, N) CPR_DPP(v_fmac_f32_dpp, A, K, 28, N)
+#define CPR_PB_O(A, Q, S, N) CPR_DPP(v_fmac_f32_dpp, A, Q, S, N)
+#define CPR_PB_REST(N)                                                                                   \
+  CPR_PB_U(2, 14, N) CPR_PB_U(3, 15, N) CPR_PB_O(8, 20, 0, N) CPR_PB_O(9, 21, 1, N)                      \
+  CPR_PB_U(4, 16, N) CPR_PB_U(5, 17, N) CPR_PB_O(8, 22, 2, N) CPR_PB_O(9, 23, 3, N)                      \
+  CPR_PB_U(6, 18, N) CPR_PB_U(7, 19, N) CPR_PB_O(8, 24, 4, N) CPR_PB_O(9, 25, 5, N)
+#define CPR_PB_OUT(I)                                                                                    \
+  "+v"(s[8 * I]), "+v"(s[8 * I + 1]), "+v"(s[8 * I + 2]), "+v"(s[8 * I + 3]), "+v"(s[8 * I + 4]),        \
+      "+v"(s[8 * I + 5]), "+v"(s[8 * I + 6]), "+v"(s[8 * I + 7])
+#define CPR_PB_IN                                                                                        \
+  "v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]), "v"(kf[7]),        \
+      "v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]), "v"(w)
+#define CPR_PB_CASE(N, NP)                                                                               \
+  if constexpr (I == N)                                                                                  \
+    asm volatile(CPR_PB_U(0, 12, N) CPR_PB_U(1, 13, N) CPR_PB_O(8, 26, 10, NP) CPR_PB_O(9, 27, 11, NP)     \
+                     CPR_PB_REST(N)                                                                      \
+                 : CPR_PB_OUT(N), "+v"(o[0]), "+v"(o[1])                                                  \
+                 : "v"(s[8 * N - 2]), "v"(s[8 * N - 1]), CPR_PB_IN);
+template <int I, int DK>
+__device__ __forceinline__ void pass_b_keys8(float (&s)[DK], float (&o)[2], const float (&kf)[8], const float (&qf)[8],
+                                             float w) {
+  static_assert(I >= 0 && I < 16 && 8 * I + 8 <= DK, "8-key groups of at most 128 keys");
+  // keys 0, 1 have no pair before them; keys 2, 3's output terms start o_0,
+  // o_1 (%10 %11 are unused here; any live registers serve)
+  if constexpr (I == 0)
+    asm volatile(CPR_PB_U(0, 12, 0) CPR_PB_U(1, 13, 0) CPR_PB_U(2, 14, 0) CPR_PB_U(3, 15, 0)
+                     CPR_DPP(v_mul_f32_dpp, 8, 20, 0, 0) CPR_DPP(v_mul_f32_dpp, 9, 21, 1, 0)
+                         CPR_PB_U(4, 16, 0) CPR_PB_U(5, 17, 0) CPR_PB_O(8, 22, 2, 0) CPR_PB_O(9, 23, 3, 0)
+                             CPR_PB_U(6, 18, 0) CPR_PB_U(7, 19, 0) CPR_PB_O(8, 24, 4, 0) CPR_PB_O(9, 25, 5, 0)
+                 : CPR_PB_OUT(0), "=&v"(o[0]), "=&v"(o[1])
+                 : "v"(s[8]), "v"(s[9]), CPR_PB_IN);
+  CPR_PB_CASE(1, 0) CPR_PB_CASE(2, 1) CPR_PB_CASE(3, 2) CPR_PB_CASE(4, 3) CPR_PB_CASE(5, 4)
+  CPR_PB_CASE(6, 5) CPR_PB_CASE(7, 6) CPR_PB_CASE(8, 7) CPR_PB_CASE(9, 8) CPR_PB_CASE(10, 9)
+  CPR_PB_CASE(11, 10) CPR_PB_CASE(12, 11) CPR_PB_CASE(13, 12) CPR_PB_CASE(14, 13) CPR_PB_CASE(15, 14)
+}
+#undef CPR_PB_CASE
+#undef CPR_PB_IN
+#undef CPR_PB_OUT
+#undef CPR_PB_REST
+#undef CPR_PB_O
+#undef CPR_PB_U
+#undef CPR_DPP
+
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -370,47 +468,20 @@ __device__ __forceinline__ float token_step(float (&s)[KeySplit<DKF>::kKeys], co
   }
   asm volatile("s_nop 1" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
                "v"(kf[7]));
-  float p0, p1, p2, p3;
-  mul_bcast<0>(p0, kf[0], s[0]);
-  mul_bcast<0>(p1, kf[1], s[1]);
-  mul_bcast<0>(p2, kf[2], s[2]);
-  mul_bcast<0>(p3, kf[3], s[3]);
-  static_for<0, DK / 8>([&](auto nc) {
-    constexpr int n = decltype(nc)::value;
-#pragma unroll
-    for (int e = (n == 0 ? 4 : 0); e < 8; e += 4) {
-      const int i = 8 * n + e;
-      fmac_bcast<n>(p0, kf[e], s[i]);
-      fmac_bcast<n>(p1, kf[e + 1], s[i + 1]);
-      fmac_bcast<n>(p2, kf[e + 2], s[i + 2]);
-      fmac_bcast<n>(p3, kf[e + 3], s[i + 3]);
-    }
-  });
-  float P = (p0 + p1) + (p2 + p3);
+  float p[4];
+  static_for<0, DK / 16>([&](auto bc) { pass_a_keys16<decltype(bc)::value, DK>(p, kf, s); });
+  float P = (p[0] + p[1]) + (p[2] + p[3]);
   if constexpr (KeySplit<DKF>::kParts == 2) P = halves_sum(P);
   const float w = b * (v - c * P);
   asm volatile("s_nop 1" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
                "v"(qf[7]));
-  float o0, o1;
+  float o[2];
   // software-pipelined as in token_step_plain: the updates of elements 2j,
   // 2j+1 are followed by the output terms of elements 2j-2, 2j-1
-  static_for<0, DK / 2 + 1>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    if constexpr (j < DK / 2) {
-      constexpr int i = 2 * j, n = i / 8, e = i % 8;
-      fmac_bcast<n>(s[i], kf[e], w);
-      fmac_bcast<n>(s[i + 1], kf[e + 1], w);
-    }
-    if constexpr (j == 1) {
-      mul_bcast<0>(o0, qf[0], s[0]);
-      mul_bcast<0>(o1, qf[1], s[1]);
-    } else if constexpr (j > 1) {
-      constexpr int i = 2 * j - 2, n = i / 8, e = i % 8;
-      fmac_bcast<n>(o0, qf[e], s[i]);
-      fmac_bcast<n>(o1, qf[e + 1], s[i + 1]);
-    }
-  });
-  float O = o0 + o1;
+  static_for<0, DK / 8>([&](auto bc) { pass_b_keys8<decltype(bc)::value, DK>(s, o, kf, qf, w); });
+  fmac_bcast<DK / 8 - 1>(o[0], qf[6], s[DK - 2]);
+  fmac_bcast<DK / 8 - 1>(o[1], qf[7], s[DK - 1]);
+  float O = o[0] + o[1];
   if constexpr (KeySplit<DKF>::kParts == 2) O = halves_sum(O);
   return c * O;
 }
@@ -491,6 +562,13 @@ __device__ __forceinline__ void scan_tokens(float (&s)[KeySplit<DK>::kKeys], con
     uint32_t vbits = vb;
     asm volatile("" : "+v"(vbits));  // decode v here, not next to its load
     vcur = D::from_bits(vbits);
+    // the next fetch is issued after the unpack, so that its registers are
+    // not live beside both tokens' raw words (before the first token the
+    // compiler would otherwise issue both fetches back to back)
+    asm volatile("" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]),
+                 "v"(kf[7]), "v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
+                 "v"(qf[7])
+                 : "memory");
     fetch(t + 1);
   };
   fetch(0);

@@ -192,50 +192,60 @@ __device__ __forceinline__ void pass_a_keys16(float (&p)[4], const float (&kf)[8
 #undef CPR_PA_FIRST
 #undef CPR_PA_GROUP
 
-// pass B over keys 8 I .. 8 I + 7: for each pair of keys the update
+// pass B over keys 16 I .. 16 I + 15: for each pair of keys the update
 // N[i] += k[i] w, N[i+1] += k[i+1] w, then the output terms of the pair
-// before it, o_0 += q[i-2] N[i-2], o_1 += q[i-1] N[i-1].  Operands: %0..%7
-// the keys' N, %8 %9 o_0 o_1, %10 %11 N of the two keys before the group,
-// %12..%19 k, %20..%27 q elements 0..7 of the lane's slot, %28 w.
-#define CPR_PB_U(A, K, N) CPR_DPP(v_fmac_f32_dpp, A, K, 28, N)
+// before it, o_0 += q[i-2] N[i-2], o_1 += q[i-1] N[i-1].  Operands: %0..%15
+// the keys' N, %16 %17 o_0 o_1, %18 %19 N of the two keys before the group,
+// %20..%27 k, %28..%35 q elements 0..7 of the lane's slot, %36 w.
+#define CPR_PB_U(A, K, N) CPR_DPP(v_fmac_f32_dpp, A, K, 36, N)
 #define CPR_PB_O(A, Q, S, N) CPR_DPP(v_fmac_f32_dpp, A, Q, S, N)
-#define CPR_PB_REST(N)                                                                                   \
-  CPR_PB_U(2, 14, N) CPR_PB_U(3, 15, N) CPR_PB_O(8, 20, 0, N) CPR_PB_O(9, 21, 1, N)                      \
-  CPR_PB_U(4, 16, N) CPR_PB_U(5, 17, N) CPR_PB_O(8, 22, 2, N) CPR_PB_O(9, 23, 3, N)                      \
-  CPR_PB_U(6, 18, N) CPR_PB_U(7, 19, N) CPR_PB_O(8, 24, 4, N) CPR_PB_O(9, 25, 5, N)
-#define CPR_PB_OUT(I)                                                                                    \
-  "+v"(s[8 * I]), "+v"(s[8 * I + 1]), "+v"(s[8 * I + 2]), "+v"(s[8 * I + 3]), "+v"(s[8 * I + 4]),        \
-      "+v"(s[8 * I + 5]), "+v"(s[8 * I + 6]), "+v"(s[8 * I + 7])
+#define CPR_PB_TAIL(N0, N1)                                                                              \
+  CPR_PB_U(2, 22, N0) CPR_PB_U(3, 23, N0) CPR_PB_O(16, 28, 0, N0) CPR_PB_O(17, 29, 1, N0)               \
+  CPR_PB_U(4, 24, N0) CPR_PB_U(5, 25, N0) CPR_PB_O(16, 30, 2, N0) CPR_PB_O(17, 31, 3, N0)               \
+  CPR_PB_U(6, 26, N0) CPR_PB_U(7, 27, N0) CPR_PB_O(16, 32, 4, N0) CPR_PB_O(17, 33, 5, N0)               \
+  CPR_PB_U(8, 20, N1) CPR_PB_U(9, 21, N1) CPR_PB_O(16, 34, 6, N0) CPR_PB_O(17, 35, 7, N0)               \
+  CPR_PB_U(10, 22, N1) CPR_PB_U(11, 23, N1) CPR_PB_O(16, 28, 8, N1) CPR_PB_O(17, 29, 9, N1)             \
+  CPR_PB_U(12, 24, N1) CPR_PB_U(13, 25, N1) CPR_PB_O(16, 30, 10, N1) CPR_PB_O(17, 31, 11, N1)           \
+  CPR_PB_U(14, 26, N1) CPR_PB_U(15, 27, N1) CPR_PB_O(16, 32, 12, N1) CPR_PB_O(17, 33, 13, N1)
+#define CPR_PB_OUT(B)                                                                                    \
+  "+v"(s[16 * B]), "+v"(s[16 * B + 1]), "+v"(s[16 * B + 2]), "+v"(s[16 * B + 3]), "+v"(s[16 * B + 4]),   \
+      "+v"(s[16 * B + 5]), "+v"(s[16 * B + 6]), "+v"(s[16 * B + 7]), "+v"(s[16 * B + 8]),                \
+      "+v"(s[16 * B + 9]), "+v"(s[16 * B + 10]), "+v"(s[16 * B + 11]), "+v"(s[16 * B + 12]),             \
+      "+v"(s[16 * B + 13]), "+v"(s[16 * B + 14]), "+v"(s[16 * B + 15])
 #define CPR_PB_IN                                                                                        \
   "v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]), "v"(kf[7]),        \
       "v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]), "v"(w)
-#define CPR_PB_CASE(N, NP)                                                                               \
-  if constexpr (I == N)                                                                                  \
-    asm volatile(CPR_PB_U(0, 12, N) CPR_PB_U(1, 13, N) CPR_PB_O(8, 26, 10, NP) CPR_PB_O(9, 27, 11, NP)     \
-                     CPR_PB_REST(N)                                                                      \
-                 : CPR_PB_OUT(N), "+v"(o[0]), "+v"(o[1])                                                  \
-                 : "v"(s[8 * N - 2]), "v"(s[8 * N - 1]), CPR_PB_IN);
+#define CPR_PB_CASE(B, NP, N0, N1)                                                                       \
+  if constexpr (I == B)                                                                                  \
+    asm volatile(CPR_PB_U(0, 20, N0) CPR_PB_U(1, 21, N0) CPR_PB_O(16, 34, 18, NP) CPR_PB_O(17, 35, 19, NP) \
+                     CPR_PB_TAIL(N0, N1)                                                                 \
+                 : CPR_PB_OUT(B), "+v"(o[0]), "+v"(o[1])                                                  \
+                 : "v"(s[16 * B - 2]), "v"(s[16 * B - 1]), CPR_PB_IN);
 template <int I, int DK>
-__device__ __forceinline__ void pass_b_keys8(float (&s)[DK], float (&o)[2], const float (&kf)[8], const float (&qf)[8],
-                                             float w) {
-  static_assert(I >= 0 && I < 16 && 8 * I + 8 <= DK, "8-key groups of at most 128 keys");
-  // keys 0, 1 have no pair before them; keys 2, 3's output terms start o_0,
-  // o_1 (%10 %11 are unused here; any live registers serve)
+__device__ __forceinline__ void pass_b_keys16(float (&s)[DK], float (&o)[2], const float (&kf)[8], const float (&qf)[8],
+                                              float w) {
+  static_assert(I >= 0 && I < 8 && 16 * I + 16 <= DK, "16-key groups of at most 128 keys");
+  // keys 0, 1 have no pair before them; keys 2, 3's output terms start o_0, o_1
+  // (%18 %19 are unused here)
   if constexpr (I == 0)
-    asm volatile(CPR_PB_U(0, 12, 0) CPR_PB_U(1, 13, 0) CPR_PB_U(2, 14, 0) CPR_PB_U(3, 15, 0)
-                     CPR_DPP(v_mul_f32_dpp, 8, 20, 0, 0) CPR_DPP(v_mul_f32_dpp, 9, 21, 1, 0)
-                         CPR_PB_U(4, 16, 0) CPR_PB_U(5, 17, 0) CPR_PB_O(8, 22, 2, 0) CPR_PB_O(9, 23, 3, 0)
-                             CPR_PB_U(6, 18, 0) CPR_PB_U(7, 19, 0) CPR_PB_O(8, 24, 4, 0) CPR_PB_O(9, 25, 5, 0)
+    asm volatile(CPR_PB_U(0, 20, 0) CPR_PB_U(1, 21, 0) CPR_PB_U(2, 22, 0) CPR_PB_U(3, 23, 0)
+                     CPR_DPP(v_mul_f32_dpp, 16, 28, 0, 0) CPR_DPP(v_mul_f32_dpp, 17, 29, 1, 0)
+                         CPR_PB_U(4, 24, 0) CPR_PB_U(5, 25, 0) CPR_PB_O(16, 30, 2, 0) CPR_PB_O(17, 31, 3, 0)
+                             CPR_PB_U(6, 26, 0) CPR_PB_U(7, 27, 0) CPR_PB_O(16, 32, 4, 0) CPR_PB_O(17, 33, 5, 0)
+                                 CPR_PB_U(8, 20, 1) CPR_PB_U(9, 21, 1) CPR_PB_O(16, 34, 6, 0) CPR_PB_O(17, 35, 7, 0)
+                                     CPR_PB_U(10, 22, 1) CPR_PB_U(11, 23, 1) CPR_PB_O(16, 28, 8, 1)
+                                         CPR_PB_O(17, 29, 9, 1) CPR_PB_U(12, 24, 1) CPR_PB_U(13, 25, 1)
+                                             CPR_PB_O(16, 30, 10, 1) CPR_PB_O(17, 31, 11, 1) CPR_PB_U(14, 26, 1)
+                                                 CPR_PB_U(15, 27, 1) CPR_PB_O(16, 32, 12, 1) CPR_PB_O(17, 33, 13, 1)
                  : CPR_PB_OUT(0), "=&v"(o[0]), "=&v"(o[1])
-                 : "v"(s[8]), "v"(s[9]), CPR_PB_IN);
-  CPR_PB_CASE(1, 0) CPR_PB_CASE(2, 1) CPR_PB_CASE(3, 2) CPR_PB_CASE(4, 3) CPR_PB_CASE(5, 4)
-  CPR_PB_CASE(6, 5) CPR_PB_CASE(7, 6) CPR_PB_CASE(8, 7) CPR_PB_CASE(9, 8) CPR_PB_CASE(10, 9)
-  CPR_PB_CASE(11, 10) CPR_PB_CASE(12, 11) CPR_PB_CASE(13, 12) CPR_PB_CASE(14, 13) CPR_PB_CASE(15, 14)
+                 : "v"(kf[0]), "v"(kf[1]), CPR_PB_IN);
+  CPR_PB_CASE(1, 1, 2, 3) CPR_PB_CASE(2, 3, 4, 5) CPR_PB_CASE(3, 5, 6, 7) CPR_PB_CASE(4, 7, 8, 9)
+  CPR_PB_CASE(5, 9, 10, 11) CPR_PB_CASE(6, 11, 12, 13) CPR_PB_CASE(7, 13, 14, 15)
 }
 #undef CPR_PB_CASE
 #undef CPR_PB_IN
 #undef CPR_PB_OUT
-#undef CPR_PB_REST
+#undef CPR_PB_TAIL
 #undef CPR_PB_O
 #undef CPR_PB_U
 #undef CPR_DPP
@@ -478,7 +488,7 @@ __device__ __forceinline__ float token_step(float (&s)[KeySplit<DKF>::kKeys], co
   float o[2];
   // software-pipelined as in token_step_plain: the updates of elements 2j,
   // 2j+1 are followed by the output terms of elements 2j-2, 2j-1
-  static_for<0, DK / 8>([&](auto bc) { pass_b_keys8<decltype(bc)::value, DK>(s, o, kf, qf, w); });
+  static_for<0, DK / 16>([&](auto bc) { pass_b_keys16<decltype(bc)::value, DK>(s, o, kf, qf, w); });
   fmac_bcast<DK / 8 - 1>(o[0], qf[6], s[DK - 2]);
   fmac_bcast<DK / 8 - 1>(o[1], qf[7], s[DK - 1]);
   float O = o[0] + o[1];
@@ -514,8 +524,8 @@ __device__ __forceinline__ float token_step_at(float (&s)[KeySplit<DK>::kKeys], 
 // to token n-1), so the wait before a token's first use of its operands
 // covers that token's loads only.  Rows are addressed as a wave-uniform base
 // plus a 32-bit lane offset (one VGPR per operand kind).  At d_k = 256 the
-// lanes of the upper half hold the same columns' upper keys and store no
-// output.
+// lanes of the upper half hold the same columns' upper keys and store the
+// same outputs as the lower half.
 template <class D, int DK, int DV>
 __device__ __forceinline__ void scan_tokens(float (&s)[KeySplit<DK>::kKeys], const typename D::T* __restrict__ kp,
                                             const typename D::T* __restrict__ qp, const typename D::T* __restrict__ vp,
@@ -582,13 +592,12 @@ __device__ __forceinline__ void scan_tokens(float (&s)[KeySplit<DK>::kKeys], con
       else
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ro, v_off, (uint32_t)t * v_stride, 0);
     };
-    // with one lane per column every lane stores, with no branch around the
-    // store, so the wait before the next token's operands can leave the
-    // store in flight (a store under an exec branch makes it wait for all)
-    if constexpr (KeySplit<DK>::kParts == 1)
-      store();
-    else if (lane < KeySplit<DK>::kCols)
-      store();
+    // every lane stores, with no branch around the store, so the wait
+    // before the next token's operands can leave the store in flight (a
+    // store under an exec branch makes it wait for all).  At d_k = 256 the
+    // two lanes of a column hold the same bits (halves_sum adds the lower
+    // half to the upper in both) and store them to the same address.
+    store();
     if (t + 1 < n) take(t + 1);
   }
 }

@@ -635,10 +635,12 @@ def main():
     for _ in range(2):
         fwd_bwd()
     torch.cuda.synchronize()
-    # the bf16 call runs the backward local terms and reverse chain on a second
-    # stream beside the forward (see gdn_cpr_fwd_bwd): events 0 -> 4 span the
-    # forward, 0 -> 5 end when the reverse chain has joined, 5 -> 6 is the
-    # state and gradient stages
+    # the bf16 call runs the backward local terms, reverse chain and state and
+    # gradient stages on a second stream beside the forward (see
+    # gdn_cpr_fwd_bwd): events 0 -> 4 span the forward, 0 -> 5 end when the
+    # reverse chain and the forward chain are both done (event 5 is recorded on
+    # the second stream), 5 -> 6 is the state and gradient stages (and the
+    # join back)
     fb_ms, fb_fwd, fb_bchain, fb_grads = [], [], [], []
     for _ in range(5):
         with fb_ev:

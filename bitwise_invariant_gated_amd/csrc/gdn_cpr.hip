@@ -188,7 +188,7 @@ gdn_status launch_status(const char* fn) {
 // and the number of streams stays bounded however many threads call.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, fchain = nullptr;
 };
 
 constexpr int kSidePool = 8;
@@ -213,11 +213,11 @@ bool make_side_stream(int dev, SideStream& y) {
   if (hipGetDevice(&cur) != hipSuccess) return false;
   if (cur != dev && hipSetDevice(dev) != hipSuccess) return false;
   bool ok = hipStreamCreateWithFlags(&y.s, hipStreamNonBlocking) == hipSuccess;
-  hipEvent_t* ev[2] = {&y.fork, &y.join};
-  for (int i = 0; i < 2 && ok; ++i) ok = hipEventCreateWithFlags(ev[i], hipEventDisableTiming) == hipSuccess;
+  hipEvent_t* ev[3] = {&y.fork, &y.join, &y.fchain};
+  for (int i = 0; i < 3 && ok; ++i) ok = hipEventCreateWithFlags(ev[i], hipEventDisableTiming) == hipSuccess;
   if (cur != dev) (void)hipSetDevice(cur);
   if (!ok) {
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 3; ++i)
       if (*ev[i]) (void)hipEventDestroy(*ev[i]);
     if (y.s) (void)hipStreamDestroy(y.s);
     (void)hipGetLastError();
@@ -633,15 +633,22 @@ struct FwdBwdFn {
       return fail(GDN_ERR_HIP, "%s: stream fork failed: %s", fn, hipGetErrorString(hipGetLastError()));
     hipLaunchKernelGGL((k_bwd_local_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, x.s, ba);
     launch_bwd_chain_bf16(ba, x.s);
-    if (!ev(hipEventRecord(x.join, x.s))) return fail(GDN_ERR_HIP, "%s: event record failed", fn);
     if (pa.N > 0) launch_chain_bf16<DK, DV>(pa, st);
     mark(3, st);
+    // the forward boundary states are complete here; the state and gradient
+    // stages need them and the reverse chain's, not the scan's outputs, so they
+    // follow the reverse chain on the side stream and take CUs as the scan's
+    // waves drain (the event is recorded before the side stream waits on it)
+    if (!ev(hipEventRecord(x.fchain, st)))
+      return fail(GDN_ERR_HIP, "%s: event record failed: %s", fn, hipGetErrorString(hipGetLastError()));
     hipLaunchKernelGGL((k_scan<D, DK, DV>), dim3(Amax, pa.H, DV / kWave), dim3(kWave), 0, st, pa);
     mark(4, st);
-    if (!ev(hipStreamWaitEvent(st, x.join, 0)))
+    if (!ev(hipStreamWaitEvent(x.s, x.fchain, 0)))
+      return fail(GDN_ERR_HIP, "%s: stream wait failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    mark(5, x.s);
+    hipLaunchKernelGGL((k_bwd_state_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, x.s, ba);
+    if (!ev(hipEventRecord(x.join, x.s)) || !ev(hipStreamWaitEvent(st, x.join, 0)))
       return fail(GDN_ERR_HIP, "%s: stream join failed: %s", fn, hipGetErrorString(hipGetLastError()));
-    mark(5, st);
-    hipLaunchKernelGGL((k_bwd_state_grads_bf16<DK, DV>), dim3(Amax, pa.H), dim3(kBwdWaves<DK, DV> * 64), 0, st, ba);
     launch_key_head_sums(ba, T, st);
     mark(6, st);
     return launch_status(fn);

@@ -340,7 +340,9 @@ gdn_status gdn_cpr_cache_state(const gdn_cpr_shape* shape, int32_t num_seqs, con
  * concurrent callers never share one).  After the forward's chunk products,
  * the backward's local terms and reverse chain run on the second stream
  * beside the forward chain and in-chunk scan on `stream`; the state and
- * gradient stages follow on `stream`.  Events fork the work from `stream` and join it back, so
+ * gradient stages follow the reverse chain on the second stream once the
+ * forward chain is done (they do not read the scan's outputs), beside the
+ * rest of the scan.  Events fork the work from `stream` and join it back, so
  * everything the call does is ordered on `stream` as with one stream (also
  * under graph capture, where the fork and join become graph edges; make a
  * first call outside a capture, since a call may create a pooled stream).

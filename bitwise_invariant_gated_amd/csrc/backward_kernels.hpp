@@ -51,7 +51,7 @@ __device__ __forceinline__ void sync_scratch() {
   __syncthreads();
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool kStage = false>
 struct BwdLocalLds {
   static constexpr bool kWide = DK > 128 || DV > 128;  // W and Dd in the slot's scratch
   float At[C][C + 1];  // At[s][t] = A[t][s]
@@ -60,6 +60,11 @@ struct BwdLocalLds {
   float W[C][kWide ? 1 : DK + 1];
   float Dd[C][kWide ? 1 : DV + 1];
   bwd::ChunkScalars cs;
+  // kStage (bf16 inputs, d > 128): the chunk's K, Q and dO rows, which every
+  // product reads, as bf16 bits (rows past the chunk's tokens are zero)
+  alignas(16) uint16_t Ks[kStage ? C : 1][kStage ? DK + 8 : 1];
+  alignas(16) uint16_t Qs[kStage ? C : 1][kStage ? DK + 8 : 1];
+  alignas(16) uint16_t dOs[kStage ? C : 1][kStage ? DV + 8 : 1];
 };
 
 // B1: per chunk slot (full or partial) and head: X, W, Kt, -W^T, dDelta_local
@@ -69,7 +74,12 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
   using namespace bwd;
   using T = typename D::T;
   typedef BwdSlot<DK, DV, sizeof(T)> Slot;
-  __shared__ BwdLocalLds<DK, DV> sm;
+  constexpr bool kWide = Slot::kWide;
+  // d > 128 on bf16 inputs: the LDS has room for the chunk's K, Q and dO
+  // (about 150 KB with the C x C arrays, one work-group per CU), which the
+  // products would otherwise fetch element by element from global memory
+  constexpr bool kStage = kWide && std::is_same<D, Bf16>::value;
+  __shared__ BwdLocalLds<DK, DV, kStage> sm;
   const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
   if (slot >= a.all_base[a.N]) return;
   const int i = find_seq(a.all_base, a.N, slot);
@@ -81,15 +91,45 @@ __global__ __launch_bounds__(256) void k_bwd_local(const BwdArgs a) {
   const T* kp = (const T*)a.k;
   const T* qp = (const T*)a.q;
   const T* dop = (const T*)a.d_o;
+  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
+  if constexpr (kStage) {
+    // 16-byte pieces (8 elements); chunk_scalars' barriers publish them
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v zero = {0u, 0u, 0u, 0u};
+    for (int idx = tid; idx < C * (DK / 8); idx += 256) {
+      const int t = idx / (DK / 8), m = idx % (DK / 8);
+      u32x4v kv = zero, qv = zero;
+      if (t < n) {  // rows past the chunk's tokens are not read
+        const size_t off = (kq0 + (size_t)t * a.Hk) * DK + 8 * m;
+        kv = *reinterpret_cast<const u32x4v*>(kp + off);
+        qv = *reinterpret_cast<const u32x4v*>(qp + off);
+      }
+      *reinterpret_cast<u32x4v*>(&sm.Ks[t][8 * m]) = kv;
+      *reinterpret_cast<u32x4v*>(&sm.Qs[t][8 * m]) = qv;
+    }
+    for (int idx = tid; idx < C * (DV / 8); idx += 256) {
+      const int t = idx / (DV / 8), m = idx % (DV / 8);
+      u32x4v dv = zero;
+      if (t < n) dv = *reinterpret_cast<const u32x4v*>(dop + (row0 + (size_t)t * H) * DV + 8 * m);
+      *reinterpret_cast<u32x4v*>(&sm.dOs[t][8 * m]) = dv;
+    }
+  }
   chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
   const ChunkScalars& cs = sm.cs;
-  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
-  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
-  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
-  auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
+  auto Kx = [&](int t, int e) {
+    if constexpr (kStage) return __uint_as_float((uint32_t)sm.Ks[t][e] << 16);
+    else return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f;
+  };
+  auto Qx = [&](int t, int e) {
+    if constexpr (kStage) return __uint_as_float((uint32_t)sm.Qs[t][e] << 16);
+    else return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f;
+  };
+  auto dOx = [&](int t, int j) {
+    if constexpr (kStage) return __uint_as_float((uint32_t)sm.dOs[t][j] << 16);
+    else return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f;
+  };
   uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;
   // W [C][DK] and Dd [C][DV]: in the LDS, or in the slot's scratch when d > 128
-  constexpr bool kWide = Slot::kWide;
   float* const scr = reinterpret_cast<float*>(ws + Slot::oScr);
   float* const Wm = kWide ? scr : &sm.W[0][0];
   float* const Dm = kWide ? scr + Slot::kArr / 4 : &sm.Dd[0][0];
@@ -298,7 +338,7 @@ __global__ __launch_bounds__(256) void k_bwd_chain_wide(const BwdArgs a) {
   if (a.dh0) store_state_tiles<DK, DV, 1>(a.dh0 + sh * SS, S1, jb, lane);
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool kStage = false>
 struct BwdGradLds {
   static constexpr int DM = DK > DV ? DK : DV;
   static constexpr bool kWide = DK > 128 || DV > 128;  // N1, M1 and M2 in the slot's scratch
@@ -312,6 +352,10 @@ struct BwdGradLds {
   bwd::ChunkScalars cs;
   float rzP[C], czP[C], dGamO[C], dGamW[C], de[C], dbc[C], dbr[C], rzA[C], czA[C];
   float red[256];
+  // kStage (bf16 inputs, d > 128): the chunk's K and Q rows as bf16 bits
+  // (rows past the chunk's tokens are zero)
+  alignas(16) uint16_t Ks[kStage ? C : 1][kStage ? DK + 8 : 1];
+  alignas(16) uint16_t Qs[kStage ? C : 1][kStage ? DK + 8 : 1];
 };
 
 // B3: per chunk slot and head: dq, dk, dv, dg, dbeta of the chunk's tokens.
@@ -320,7 +364,11 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   using namespace bwd;
   using T = typename D::T;
   typedef BwdSlot<DK, DV, sizeof(T)> Slot;
-  __shared__ BwdGradLds<DK, DV> sm;
+  // d > 128 on bf16 inputs: the chunk's K and Q, the most-read operands, in
+  // the LDS (about 140 KB with the C x C arrays, one work-group per CU)
+  // instead of element by element from global memory
+  constexpr bool kStage = Slot::kWide && std::is_same<D, Bf16>::value;
+  __shared__ BwdGradLds<DK, DV, kStage> sm;
   const int slot = blockIdx.x, h = blockIdx.y, H = a.H;
   if (slot >= a.all_base[a.N]) return;
   const int i = find_seq(a.all_base, a.N, slot);
@@ -333,11 +381,32 @@ __global__ __launch_bounds__(256) void k_bwd_grads(const BwdArgs a) {
   const T* qp = (const T*)a.q;
   const T* vp = (const T*)a.v;
   const T* dop = (const T*)a.d_o;
+  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
+  if constexpr (kStage) {
+    // 16-byte pieces (8 elements); chunk_scalars' barriers publish them
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    for (int idx = tid; idx < C * (DK / 8); idx += 256) {
+      const int t = idx / (DK / 8), m = idx % (DK / 8);
+      u32x4v kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+      if (t < n) {  // rows past the chunk's tokens are not read
+        const size_t off = (kq0 + (size_t)t * a.Hk) * DK + 8 * m;
+        kv = *reinterpret_cast<const u32x4v*>(kp + off);
+        qv = *reinterpret_cast<const u32x4v*>(qp + off);
+      }
+      *reinterpret_cast<u32x4v*>(&sm.Ks[t][8 * m]) = kv;
+      *reinterpret_cast<u32x4v*>(&sm.Qs[t][8 * m]) = qv;
+    }
+  }
   chunk_scalars<D>(sm.cs, (const T*)a.g, (const T*)a.beta, row0, H, n);
   const ChunkScalars& cs = sm.cs;
-  const size_t kq0 = kq_row((size_t)a.cu[i] + (size_t)c * a.Cl, h, a.Hk, a.G);
-  auto Kx = [&](int t, int e) { return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
-  auto Qx = [&](int t, int e) { return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f; };
+  auto Kx = [&](int t, int e) {
+    if constexpr (kStage) return __uint_as_float((uint32_t)sm.Ks[t][e] << 16);
+    else return t < n ? D::load(kp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f;
+  };
+  auto Qx = [&](int t, int e) {
+    if constexpr (kStage) return __uint_as_float((uint32_t)sm.Qs[t][e] << 16);
+    else return t < n ? D::load(qp, (kq0 + (size_t)t * a.Hk) * DK + e) : 0.f;
+  };
   auto Vx = [&](int t, int j) { return t < n ? D::load(vp, (row0 + (size_t)t * H) * DV + j) : 0.f; };
   auto dOx = [&](int t, int j) { return t < n ? D::load(dop, (row0 + (size_t)t * H) * DV + j) : 0.f; };
   const uint8_t* ws = a.ws + ((size_t)slot * H + h) * Slot::bytes;

@@ -76,3 +76,33 @@ def test_spill_check_names_hot_kernels_only():
 """
     bad = check_spills(meta)
     assert [k for _, k in bad] == [55] and "k_resync_bf16" in bad[0][0]
+
+
+def test_reads_inline_asm_blocks():
+    # several instructions in one inline-asm statement are emitted between
+    # ASMSTART / ASMEND markers without indentation; a DPP source written by
+    # the statement before, or by the instruction before within the
+    # statement, is a hazard either way
+    before = """k:
+	v_lshlrev_b32_e32 v5, 16, v4
+	;;#ASMSTART
+v_fmac_f32_dpp v1, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf
+v_fmac_f32_dpp v3, v6, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf
+	;;#ASMEND
+"""
+    within = """k:
+	;;#ASMSTART
+v_fmac_f32_dpp v5, v7, v2 row_newbcast:0 row_mask:0xf bank_mask:0xf
+v_fmac_f32_dpp v1, v5, v2 row_newbcast:1 row_mask:0xf bank_mask:0xf
+	;;#ASMEND
+"""
+    clean = """k:
+	;;#ASMSTART
+v_fmac_f32_dpp v1, v5, v2 row_newbcast:0 row_mask:0xf bank_mask:0xf
+v_fmac_f32_dpp v3, v6, v1 row_newbcast:0 row_mask:0xf bank_mask:0xf
+v_fmac_f32_dpp v1, v5, v8 row_newbcast:1 row_mask:0xf bank_mask:0xf
+	;;#ASMEND
+"""
+    assert len(check_dpp_hazards(before)) == 1
+    assert len(check_dpp_hazards(within)) == 1
+    assert check_dpp_hazards(clean) == []

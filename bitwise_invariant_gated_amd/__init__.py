@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     gdn_cpr_numerics_id,
     gdn_cpr_prefill,
     gdn_cpr_prefill_continue,
+    gdn_cpr_wait_status,
     gdn_cpr_workspace_size,
 )
 from ._lib import (  # noqa: F401

@@ -38,6 +38,7 @@ EXPORTED = (
     "gdn_cpr_prefill_continue",
     "gdn_cpr_fwd_bwd",
     "gdn_cpr_cache_state",
+    "gdn_cpr_wait_status",
     "gdn_cpr_set_stage_events",
     "gdn_cpr_last_error",
     "gdn_cpr_numerics_id",
@@ -107,6 +108,9 @@ def load() -> ctypes.CDLL:
     lib.gdn_cpr_fwd_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdn_cpr_wait_status.restype = ctypes.c_int
+    lib.gdn_cpr_wait_status.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64, _vp,
+                                        ctypes.c_size_t, _vp, _vp]
     lib.gdn_cpr_cache_state.restype = ctypes.c_int
     lib.gdn_cpr_cache_state.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.POINTER(Cache), _vp, _vp]
     lib.gdn_cmp_workspace_size.restype = ctypes.c_size_t

@@ -96,6 +96,19 @@ def gdn_cpr_cache_state(shape: LayerShape, cache: CprCache, num_seqs: Optional[i
     return out
 
 
+def gdn_cpr_wait_status(shape: LayerShape, num_seqs: int, total_tokens: int, workspace: torch.Tensor,
+                        status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The wait status of the last prefill / continuation / fwd_bwd call on `workspace`
+    (called with that call's sizes) as a one-element int32 device tensor (or into
+    `status`): 0 if every bounded wait ended normally, 1 if one gave up."""
+    lib = _lib.load()
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    _lib.check(lib.gdn_cpr_wait_status(ctypes.byref(shape.c()), num_seqs, total_tokens, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream)))
+    return status
+
+
 def gdn_cpr_workspace_size(shape: LayerShape, num_seqs: int, total_tokens: int, op: int) -> int:
     return int(_lib.load().gdn_cpr_workspace_size(ctypes.byref(shape.c()), num_seqs, total_tokens, op))
 

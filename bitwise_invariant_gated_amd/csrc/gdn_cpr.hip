@@ -316,7 +316,7 @@ gdn_status run_prefill(const PrefillArgs& a, int64_t T, hipStream_t st, const ch
   constexpr int NZ = DV / kFusedChainCols;
   // the fused launch's counts: the chain items', then the chunk-product flags
   const int n_counts = a.N * a.H * NZ * kReadyStride;
-  FusedPlan fp{};
+  FusedPlan fp{nullptr, a.counters, nullptr, 0};  // the plan clears the timeout word either way
   if (fused || kChainOnly) fp = FusedPlan{a.order, a.counters, a.ready, n_counts + (fused ? Fmax * a.H : 0)};
   mark(0, st);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, a.start, a.end, a.N, a.Cl, a.full_base, a.all_base, fp);
@@ -621,7 +621,7 @@ struct FwdBwdFn {
     auto ev = [&](hipError_t e) { return e == hipSuccess; };
     mark(0, st);
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, pa.start, pa.end, pa.N, pa.Cl, pa.full_base, pa.all_base,
-                       FusedPlan{});
+                       FusedPlan{nullptr, pa.counters, nullptr, 0});
     mark(1, st);
     // the forward's chunk products first, on the whole chip: launched beside
     // the backward's local stage, whose work-groups take a CU each, they would
@@ -725,6 +725,28 @@ extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num
   if (op == GDN_OP_DECODE) return decode_layout(*shape, num_seqs).total;
   if (op == GDN_OP_PREFILL_CONTINUE) return cont_layout(*shape, num_seqs, total_tokens).total;
   return 0;
+}
+
+extern "C" gdn_status gdn_cpr_wait_status(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                                          const void* workspace, size_t workspace_bytes, int32_t* status,
+                                          void* stream) {
+  const char* fn = "gdn_cpr_wait_status";
+  std::string why;
+  if (!shape_ok(shape, &why, true)) return fail(GDN_ERR_UNSUPPORTED, "%s: %s", fn, why.c_str());
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative size", fn);
+  CHECK_PTR(status, "status");
+  // prefill, continuation and fwd_bwd place the prefill layout at the start
+  // of their workspace: the timeout word follows the fused launch's ticket
+  const PrefillLayout L = prefill_layout(*shape, num_seqs, total_tokens);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(GDN_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  const char* word = (const char*)workspace + L.counters + sizeof(int32_t);
+  if (hipMemcpyAsync(status, word, sizeof(int32_t), hipMemcpyDeviceToDevice, (hipStream_t)stream) != hipSuccess)
+    return fail(GDN_ERR_HIP, "%s: copy failed: %s", fn, hipGetErrorString(hipGetLastError()));
+  g_last_error.clear();
+  return GDN_OK;
 }
 
 extern "C" gdn_status gdn_cpr_prefill(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,

@@ -144,7 +144,8 @@ __device__ __forceinline__ size_t kq_row(size_t tok, int h, int Hk, int G) { ret
 struct FusedPlan {
   int32_t* order;   // [A] chunk slots in chunk-major order (chunk 0 of every sequence, then chunk 1, ...),
                     // or null: no fused launch follows
-  int32_t* ticket;  // work-item counter of the fused launch
+  int32_t* ticket;  // [2] work-item counter of the fused launch, then its wait-timeout word
+                    // (cleared by every plan that is given them, fused launch or not)
   int32_t* ready;   // [n_ready] boundaries published so far by each chain item
   int32_t n_ready;
 };
@@ -202,6 +203,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ start
     full_base[N] = cf;
     all_base[N] = ca;
   }
+  if (tid == 0 && fp.ticket) fp.ticket[1] = 0;  // no wait of this call has given up (yet)
   if (fp.order == nullptr) return;
   // fused launch: clear its counters, and order the chunk slots by chunk
   // index (then by sequence): slot (i, c) goes to position

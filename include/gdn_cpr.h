@@ -82,6 +82,13 @@
  *     failures return GDN_ERR_HIP.  A malformed cu_seqlens (not
  *     non-decreasing, or not ending at T) is the caller's error and is not
  *     detected.
+ *   - A bf16 prefill of up to 128 sequences runs its chunk products, chain
+ *     and scan as one launch in which work-groups wait for results of other
+ *     work-groups of the same launch.  Every such wait is on work that
+ *     started earlier and is bounded (about a second of polling); none is
+ *     expected to give up.  If one does, that call's outputs are not valid,
+ *     and gdn_cpr_wait_status (below) reports it without a host
+ *     synchronisation.
  */
 #ifndef GDN_CPR_H
 #define GDN_CPR_H
@@ -176,6 +183,22 @@ typedef struct {
  */
 size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num_seqs,
                               int64_t total_tokens, int32_t op);
+
+/*
+ * Wait status of the most recent gdn_cpr_prefill, gdn_cpr_prefill_continue
+ * or gdn_cpr_fwd_bwd call that used `workspace`, called with that call's
+ * shape, num_seqs and total_tokens: enqueues on `stream` a copy of one
+ * int32 into `status` (device memory, 16-byte aligned), 0 if every bounded
+ * wait of that call ended with its data published and 1 if one gave up (see
+ * the conventions above).  Stream-ordered like the calls; the host reads
+ * the value once the stream has reached it.  For callers that check a
+ * result without synchronising the device, e.g. a service's health check.
+ * After a call with num_seqs = 0 (which enqueues nothing) the word is that
+ * of the call before.  Errors: see the conventions.
+ */
+gdn_status gdn_cpr_wait_status(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                               const void* workspace, size_t workspace_bytes, int32_t* status,
+                               void* stream);
 
 /*
  * Prefill: the engine_prefill case of the pages' execution contract, whose

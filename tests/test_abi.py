@@ -252,3 +252,22 @@ def test_numerics_id_states_the_pinned_token_step_order():
         dev = " ".join(f.read().split())
     for formula in ("w = b * (v - c * (P_lo + P_hi))", "o = c * (O_lo + O_hi)"):
         assert formula in dev and formula in ident, formula
+
+
+def test_wait_status_rejects_bad_arguments():
+    lib = _lib_or_skip()
+    s = _shape()
+    need = lib.gdn_cpr_workspace_size(ctypes.byref(s), 2, 300, _lib.GDN_OP_PREFILL)
+
+    def ws(shape=s, N=2, T=300, w=FAKE + 4096, nbytes=need, status=FAKE + 256):
+        return lib.gdn_cpr_wait_status(ctypes.byref(shape), N, T, w, nbytes, status, None)
+
+    assert ws(shape=_shape(dk=96)) == _lib.GDN_ERR_UNSUPPORTED
+    assert ws(N=-1) == _lib.GDN_ERR_INVALID_ARG
+    assert ws(T=-1) == _lib.GDN_ERR_INVALID_ARG
+    assert ws(status=None) == _lib.GDN_ERR_INVALID_ARG
+    assert ws(status=FAKE + 260) == _lib.GDN_ERR_INVALID_ARG
+    assert ws(w=None) == _lib.GDN_ERR_WORKSPACE
+    assert ws(nbytes=need - 1) == _lib.GDN_ERR_WORKSPACE
+    assert b"workspace" in lib.gdn_cpr_last_error()
+    assert ws(w=FAKE + 4100) == _lib.GDN_ERR_INVALID_ARG

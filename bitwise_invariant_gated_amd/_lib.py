@@ -39,6 +39,7 @@ EXPORTED = (
     "gdn_cpr_fwd_bwd",
     "gdn_cpr_cache_state",
     "gdn_cpr_wait_status",
+    "gdn_cpr_debug_set_wait_polls",
     "gdn_cpr_set_stage_events",
     "gdn_cpr_last_error",
     "gdn_cpr_numerics_id",
@@ -108,6 +109,8 @@ def load() -> ctypes.CDLL:
     lib.gdn_cpr_fwd_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdn_cpr_debug_set_wait_polls.restype = ctypes.c_int
+    lib.gdn_cpr_debug_set_wait_polls.argtypes = [ctypes.c_int32]
     lib.gdn_cpr_wait_status.restype = ctypes.c_int
     lib.gdn_cpr_wait_status.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int64, _vp,
                                         ctypes.c_size_t, _vp, _vp]

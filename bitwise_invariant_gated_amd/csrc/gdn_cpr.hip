@@ -727,6 +727,15 @@ extern "C" size_t gdn_cpr_workspace_size(const gdn_cpr_shape* shape, int32_t num
   return 0;
 }
 
+extern "C" gdn_status gdn_cpr_debug_set_wait_polls(int32_t polls) {
+  const char* fn = "gdn_cpr_debug_set_wait_polls";
+  if (polls < 0) return fail(GDN_ERR_INVALID_ARG, "%s: negative poll count", fn);
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_wait_polls), &polls, sizeof(polls)) != hipSuccess)
+    return fail(GDN_ERR_HIP, "%s: %s", fn, hipGetErrorString(hipGetLastError()));
+  g_last_error.clear();
+  return GDN_OK;
+}
+
 extern "C" gdn_status gdn_cpr_wait_status(const gdn_cpr_shape* shape, int32_t num_seqs, int64_t total_tokens,
                                           const void* workspace, size_t workspace_bytes, int32_t* status,
                                           void* stream) {

@@ -769,6 +769,11 @@ __device__ __forceinline__ int read_count(const int32_t* p) {
   return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Test hook: a positive value replaces the waits' poll bound (so that a test
+// can make them give up while every work-group still exits); 0, the
+// default, keeps it.  Set by gdn_cpr_debug_set_wait_polls.
+__device__ int32_t g_wait_polls = 0;
+
 // waits (bounded) until *p >= need; false if it gave up.  The default polls
 // every ~8,000 cycles (3 to 4 us; a chain step takes about as long), so that
 // thousands of waiting scan waves add little memory traffic; the chain's wait
@@ -777,9 +782,12 @@ __device__ __forceinline__ int read_count(const int32_t* p) {
 template <int kSleep = 127>
 __device__ __forceinline__ bool wait_count(const int32_t* p, int need) {
   constexpr int kMaxPolls = kSleep >= 127 ? 1 << 18 : 1 << 21;
-  for (int it = 0; it < kMaxPolls; ++it) {
-    if (__builtin_amdgcn_readfirstlane(read_count(p)) >= need) return true;
+  if (__builtin_amdgcn_readfirstlane(read_count(p)) >= need) return true;  // no wait: no further load
+  const int32_t over = g_wait_polls;
+  const int polls = over > 0 ? min((int)over, kMaxPolls) : kMaxPolls;
+  for (int it = 1; it < polls; ++it) {
     __builtin_amdgcn_s_sleep(kSleep);
+    if (__builtin_amdgcn_readfirstlane(read_count(p)) >= need) return true;
   }
   return false;
 }

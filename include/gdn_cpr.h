@@ -201,6 +201,17 @@ gdn_status gdn_cpr_wait_status(const gdn_cpr_shape* shape, int32_t num_seqs, int
                                void* stream);
 
 /*
+ * Test hook for the failure path above: a positive `polls` bounds every
+ * such wait at that many polls instead of about a second's worth, so that
+ * a test can make waits give up (the call's outputs are then not valid, but
+ * every work-group still finishes); 0 restores the default.  Applies to the
+ * current device, synchronously, to calls enqueued afterwards; not for use
+ * beside other work on the device.  Errors: GDN_ERR_INVALID_ARG for a
+ * negative count, GDN_ERR_HIP if the copy fails.
+ */
+gdn_status gdn_cpr_debug_set_wait_polls(int32_t polls);
+
+/*
  * Prefill: the engine_prefill case of the pages' execution contract, whose
  * cases name the stage a kernel region runs in (English page, "The IsoExec
  * Unified Execution Contract", cases and regions; Chinese page, section on

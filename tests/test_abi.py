@@ -271,3 +271,8 @@ def test_wait_status_rejects_bad_arguments():
     assert ws(nbytes=need - 1) == _lib.GDN_ERR_WORKSPACE
     assert b"workspace" in lib.gdn_cpr_last_error()
     assert ws(w=FAKE + 4100) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_debug_wait_polls_rejects_a_negative_count():
+    lib = _lib_or_skip()
+    assert lib.gdn_cpr_debug_set_wait_polls(-1) == _lib.GDN_ERR_INVALID_ARG

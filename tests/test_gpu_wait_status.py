@@ -62,3 +62,36 @@ def test_fwd_bwd_wait_status_is_zero():
     gdn.gdn_cpr_fwd_bwd(db.shape, db.q, db.k, db.v, db.g, db.beta, db.cu, None, db.d_o, None, o, None,
                         dq, dk, dv, dg, db_, None, ws)
     assert _status(db.shape, N, T, ws) == 0
+
+
+def test_waits_that_give_up_set_the_status_and_the_next_call_recovers():
+    # the test hook bounds every wait at one poll: scan units that start
+    # before their boundary is published (and chain items before their chunk
+    # products) give up, so the call's outputs are not valid, but every
+    # work-group still finishes; the status must say so, and a normal call
+    # afterwards on the same workspace must read 0 and reproduce the bits
+    note("forced wait give-up: status 1, then a normal call reads 0")
+    from bitwise_invariant_gated_amd import _lib
+    lib = _lib.load()
+    b = make_batch(1704, [1024] * 5, 4, 128, 128, dtype="bf16")
+    db = DevBatch(b)
+    N, T = b.num_seqs, b.total_tokens
+    ws = gdn.alloc_workspace(db.shape, N, T, gdn.GDN_OP_PREFILL)
+
+    def run():
+        cache = gdn.alloc_cache(db.shape, N)
+        o = torch.empty((T, 4, 128), dtype=torch_dtype(b), device=DEV)
+        gdn.gdn_cpr_prefill(db.shape, db.q, db.k, db.v, db.g, db.beta, db.cu, None, cache, o, ws)
+        return o
+
+    ref = run()
+    assert _status(db.shape, N, T, ws) == 0
+    try:
+        _lib.check(lib.gdn_cpr_debug_set_wait_polls(1))
+        run()
+        assert _status(db.shape, N, T, ws) == 1
+    finally:
+        _lib.check(lib.gdn_cpr_debug_set_wait_polls(0))
+    again = run()
+    assert _status(db.shape, N, T, ws) == 0
+    assert torch.equal(again.view(torch.int16), ref.view(torch.int16))
